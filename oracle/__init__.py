@@ -1,0 +1,282 @@
+"""Oracle for the MoE expert grouped GEMM: plain fp64 CPU reference.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the library never
+does.  It shares no code with the HIP path and imports nothing from it.
+
+Everything here works on numpy arrays of the raw stored bits:
+  * bf16 tensors as ``uint16`` arrays,
+  * MXFP8 (E4M3) codes as ``uint8`` [rows, cols],
+  * MXFP4 (E2M1) codes as ``uint8`` [rows, cols/2], even column in the low
+    nibble (the byte layout of ``float4_e2m1fn_x2`` named in the PR page
+    "[Megatron-LM] feat: add grouped gemm fp4 support, ...", section "Changes"),
+  * E8M0 scales as ``uint8`` [rows, cols/32], one per 32 consecutive elements.
+
+The arithmetic lives in ``oracle.c`` (binary64 loops over experts, rows and
+the reduction index); this module only marshals arrays and composes the
+steps in the order the pages give them:
+
+  FC1 -> SwiGLU -> (bf16) -> MXFP4 quantise -> FC2      (blog "Enabling
+  DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with Primus", section
+  "MegaMoE: fusing communication into the grouped GEMM": SwiGLU sits between
+  the two grouped GEMMs; the FC1 weight is [experts, 2I, H], gate then up).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+BF16, E4M3, E2M1 = 0, 1, 2          # operand encodings (oracle's own numbering)
+EPI_NONE, EPI_SWIGLU, EPI_SWIGLU_MXFP4 = 0, 1, 2
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, compiling it first only if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        p, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.orc_bf16_value.restype = dbl
+        L.orc_bf16_value.argtypes = [ctypes.c_uint16]
+        L.orc_e4m3_value.restype = dbl
+        L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_value.restype = dbl
+        L.orc_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_value.restype = dbl
+        L.orc_e8m0_value.argtypes = [ctypes.c_uint8]
+        L.orc_round_bf16.restype = ctypes.c_uint16
+        L.orc_round_bf16.argtypes = [dbl]
+        L.orc_decode.restype = None
+        L.orc_decode.argtypes = [i32, p, p, i64, i64, p]
+        L.orc_round_bf16_array.restype = None
+        L.orc_round_bf16_array.argtypes = [p, i64, p]
+        L.orc_round_f32_array.restype = None
+        L.orc_round_f32_array.argtypes = [p, i64, p]
+        L.orc_mx_quantize.restype = i32
+        L.orc_mx_quantize.argtypes = [p, i64, i64, i32, i32, p, p]
+        L.orc_fwd_rows.restype = i32
+        L.orc_fwd_rows.argtypes = [i32, p, p, p, p, p, i64, i64, i64, i64, i32, p, i64, p]
+        L.orc_dgrad_rows.restype = i32
+        L.orc_dgrad_rows.argtypes = [p, p, p, i64, i64, i64, i64, i32, p, i64, p]
+        L.orc_wgrad_rows.restype = i32
+        L.orc_wgrad_rows.argtypes = [p, p, p, i64, i64, i64, i64, p, p, i64, p]
+        L.orc_swiglu.restype = None
+        L.orc_swiglu.argtypes = [p, i64, i64, p]
+        L.orc_threads.restype = i32
+        L.orc_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def threads() -> int:
+    return lib().orc_threads()
+
+
+# ------------------------------------------------------------------ formats
+def bf16_value(bits: int) -> float:
+    return lib().orc_bf16_value(int(bits))
+
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(int(code))
+
+
+def e2m1_value(nibble: int) -> float:
+    return lib().orc_e2m1_value(int(nibble))
+
+
+def e8m0_value(code: int) -> float:
+    return lib().orc_e8m0_value(int(code))
+
+
+def decode(dtype: int, data: np.ndarray, scale: np.ndarray | None, rows: int, cols: int) -> np.ndarray:
+    """Exact binary64 values of a stored [rows, cols] matrix."""
+    if dtype == BF16:
+        data = _c(data, np.uint16)
+    else:
+        data = _c(data, np.uint8)
+        scale = _c(scale, np.uint8)
+    out = np.empty((rows, cols), np.float64)
+    lib().orc_decode(dtype, _ptr(data), _ptr(scale), rows, cols, _ptr(out))
+    return out
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round binary64 values to bf16 bit patterns (nearest, ties to even)."""
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_round_bf16_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def round_f32(x: np.ndarray) -> np.ndarray:
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.float32)
+    lib().orc_round_f32_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    bits = _c(bits, np.uint16)
+    return decode(BF16, bits.reshape(1, -1), None, 1, bits.size).reshape(bits.shape)
+
+
+def mx_quantize(x_bits: np.ndarray, dtype: int, axis: int = 1):
+    """OCP-MX quantise a bf16 matrix; returns (codes, scales)."""
+    x_bits = _c(x_bits, np.uint16)
+    rows, cols = x_bits.shape
+    if axis == 1:
+        qshape = (rows, cols) if dtype == E4M3 else (rows, cols // 2)
+        sshape = (rows, cols // 32)
+    else:
+        qshape = (rows, cols) if dtype == E4M3 else (rows // 2, cols)
+        sshape = (rows // 32, cols)
+    q = np.zeros(qshape, np.uint8)
+    s = np.zeros(sshape, np.uint8)
+    rc = lib().orc_mx_quantize(_ptr(x_bits), rows, cols, dtype, axis, _ptr(q), _ptr(s))
+    if rc:
+        raise ValueError("orc_mx_quantize: bad arguments")
+    return q, s
+
+
+def mx_dequantize(dtype: int, q: np.ndarray, s: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    return decode(dtype, q, s, rows, cols)
+
+
+def swiglu(c: np.ndarray) -> np.ndarray:
+    c = _c(c, np.float64)
+    n, N = c.shape
+    h = np.empty((n, N // 2), np.float64)
+    lib().orc_swiglu(_ptr(c), n, N, _ptr(h))
+    return h
+
+
+# ------------------------------------------------------------------ GEMMs
+def _operand(dtype, x):
+    return _c(x, np.uint16 if dtype == BF16 else np.uint8)
+
+
+def fwd_rows(dtype, a, a_scale, b, b_scale, group_lens, N, K, trans_b, rows):
+    """Unrounded binary64 C[rows, :] = A_g[rows] @ B_g for each row's expert."""
+    lens = _c(group_lens, np.int64)
+    rows = _c(rows, np.int64)
+    a, b = _operand(dtype, a), _operand(dtype, b)
+    a_scale, b_scale = _c(a_scale, np.uint8), _c(b_scale, np.uint8)
+    out = np.empty((rows.size, N), np.float64)
+    M = int(lens.sum())
+    rc = lib().orc_fwd_rows(dtype, _ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale),
+                            _ptr(lens), lens.size, M, N, K, int(trans_b),
+                            _ptr(rows), rows.size, _ptr(out))
+    if rc:
+        raise ValueError("orc_fwd_rows: a requested row belongs to no expert")
+    return out
+
+
+def dgrad_rows(dy, b, group_lens, N, K, trans_b, rows):
+    """Unrounded dX[rows, :] = dY[rows] @ B_g^T (bf16 operands)."""
+    lens = _c(group_lens, np.int64)
+    rows = _c(rows, np.int64)
+    dy, b = _c(dy, np.uint16), _c(b, np.uint16)
+    out = np.empty((rows.size, K), np.float64)
+    rc = lib().orc_dgrad_rows(_ptr(dy), _ptr(b), _ptr(lens), lens.size, int(lens.sum()),
+                              N, K, int(trans_b), _ptr(rows), rows.size, _ptr(out))
+    if rc:
+        raise ValueError("orc_dgrad_rows: a requested row belongs to no expert")
+    return out
+
+
+def wgrad_rows(a, dy, group_lens, N, K, gs, ks):
+    """Unrounded D_g[k, :] = sum over expert g's rows of A[r, k] * dY[r, :]."""
+    lens = _c(group_lens, np.int64)
+    gs, ks = _c(gs, np.int64), _c(ks, np.int64)
+    a, dy = _c(a, np.uint16), _c(dy, np.uint16)
+    out = np.empty((gs.size, N), np.float64)
+    rc = lib().orc_wgrad_rows(_ptr(a), _ptr(dy), _ptr(lens), lens.size, int(lens.sum()),
+                              N, K, _ptr(gs), _ptr(ks), gs.size, _ptr(out))
+    if rc:
+        raise ValueError("orc_wgrad_rows: bad (expert, k) pair")
+    return out
+
+
+# ------------------------------------------------------------------ composed ops
+def grouped_fwd(dtype, a, a_scale, b, b_scale, group_lens, N, K, trans_b, epilogue, rows):
+    """Forward with its epilogue, for the listed rows.
+
+    Returns a dict:
+      "exact": binary64 result before the final rounding ([n, N] or [n, N/2]),
+      "bf16":  uint16 bits of the bf16 output (NONE, SWIGLU, and the bf16 SwiGLU
+               value that SWIGLU_MXFP4 quantises),
+      "q", "s": MXFP4 codes [n, N/4] and scales [n, N/64] (SWIGLU_MXFP4 only).
+    """
+    c = fwd_rows(dtype, a, a_scale, b, b_scale, group_lens, N, K, trans_b, rows)
+    if epilogue == EPI_NONE:
+        return {"exact": c, "bf16": round_bf16(c)}
+    h = swiglu(c)
+    hb = round_bf16(h)
+    out = {"exact": h, "bf16": hb}
+    if epilogue == EPI_SWIGLU_MXFP4:
+        out["q"], out["s"] = mx_quantize(hb, E2M1, axis=1)
+    return out
+
+
+def wgrad_accumulate(main_grad_in: np.ndarray, d_exact: np.ndarray, accumulate: bool) -> np.ndarray:
+    """fp32 result of main_grad (+)= D, one rounding of the exact sum."""
+    base = main_grad_in.astype(np.float64) if accumulate else 0.0
+    return round_f32(base + d_exact)
+
+
+def mlp_mxfp4_rows(x_bits, w1q, w1s, w2q, w2s, group_lens, H, I, rows):
+    """Expert MLP FC1 -> SwiGLU -> FC2 in MXFP4 for the listed rows.
+
+    x_bits: bf16 [M, H]; w1q/w1s: FC1 weight [G, 2I, H] as MXFP4 codes/scales;
+    w2q/w2s: FC2 weight [G, H, I].  The activations are quantised along H
+    (FC1) and along I (FC2) in blocks of 32, from bf16 values.
+    Returns dict with "h_q", "h_s" (FC2 input), "exact" (binary64 FC2 output,
+    before rounding) and "bf16".
+    """
+    rows = _c(rows, np.int64)
+    xr = np.ascontiguousarray(x_bits[rows])
+    xq, xs = mx_quantize(xr, E2M1, axis=1)
+    # quantisation is row-local, so quantising only the listed rows is exact;
+    # the GEMM helper indexes A by global row, so scatter into a sparse holder
+    lens = _c(group_lens, np.int64)
+    local_lens, local_rows = _local_groups(lens, rows)
+    c1 = fwd_rows(E2M1, xq, xs, w1q, w1s, local_lens, 2 * I, H, 1, local_rows)
+    h = swiglu(c1)
+    hb = round_bf16(h)
+    hq, hs = mx_quantize(hb, E2M1, axis=1)
+    c2 = fwd_rows(E2M1, hq, hs, w2q, w2s, local_lens, H, I, 1, local_rows)
+    return {"h_bf16": hb, "h_q": hq, "h_s": hs, "exact": c2, "bf16": round_bf16(c2)}
+
+
+def _local_groups(lens: np.ndarray, rows: np.ndarray):
+    """Re-index sorted-by-expert sample rows as a compact ragged batch.
+
+    Row i of the compact batch is global row rows[i]; the compact expert
+    lengths count how many sample rows fall in each expert, so the compact
+    batch keeps every row's expert.  Requires rows sorted ascending.
+    """
+    if np.any(np.diff(rows) < 0):
+        raise ValueError("rows must be sorted")
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    g_of = np.searchsorted(offs, rows, side="right") - 1
+    if np.any(rows >= offs[-1]) or np.any(rows < 0):
+        raise ValueError("row outside every expert")
+    local = np.bincount(g_of, minlength=lens.size).astype(np.int64)
+    return local, np.arange(rows.size, dtype=np.int64)

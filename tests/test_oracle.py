@@ -1,0 +1,430 @@
+"""Pins for the oracle: every check here compares it with something other than
+itself -- a library routine (torch's float8 decoders and fp32->fp8/bf16
+conversions, numpy's dense matmul and integer matmul), closed forms of the OCP
+element formats, exact arithmetic on integer or power-of-two inputs,
+invariants of the grouped GEMM, and hand-worked quantisation fixtures under
+tests/golden/.  CPU only.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import GOLDEN
+
+BF16, E4M3, E2M1 = 0, 1, 2
+
+
+def bf16_of(x):
+    """Exact bf16 bits of float values that are representable in bf16."""
+    t = torch.tensor(np.asarray(x, np.float32))
+    b = t.to(torch.bfloat16)
+    assert torch.equal(b.float(), t), "value not representable in bf16"
+    return b.view(torch.int16).numpy().view(np.uint16)
+
+
+def rand_bf16(shape, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * std).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------------ decoding
+def test_bf16_decode_all_patterns(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = orc.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+    assert (np.signbit(mine) == np.signbit(ref)).all()
+
+
+def test_e4m3_decode_matches_torch(orc):
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mine = np.array([orc.e4m3_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert (np.isnan(mine) == nan).all()
+    assert (mine[~nan] == ref[~nan]).all()
+    assert (np.signbit(mine[~nan]) == np.signbit(ref[~nan])).all()
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+
+
+def test_e8m0_decode_matches_torch(orc):
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    mine = np.array([orc.e8m0_value(c) for c in range(256)])
+    assert np.isnan(mine[255]) and np.isnan(ref[255])
+    assert (mine[:255] == ref[:255]).all()
+
+
+def _read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                c, v = line.split()
+                rows.append((int(c, 16), float(v)))
+    return rows
+
+
+def test_e2m1_decode_golden(orc):
+    rows = _read_table("e2m1_values.txt")
+    assert len(rows) == 16
+    for code, val in rows:
+        got = orc.e2m1_value(code)
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), (code, got, val)
+
+
+def test_e4m3_decode_golden(orc):
+    for code, val in _read_table("e4m3_selected.txt"):
+        got = orc.e4m3_value(code)
+        if math.isnan(val):
+            assert math.isnan(got)
+        else:
+            assert got == val and math.copysign(1, got) == math.copysign(1, val), (code, got, val)
+
+
+# ------------------------------------------------------------------ rounding
+def test_round_bf16_matches_torch_on_fp32_inputs(orc):
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(200000, generator=g) * torch.exp2(torch.randint(-140, 120, (200000,), generator=g).float())
+    x = torch.cat([x, torch.tensor([0.0, -0.0, 3.4e38, -3.4e38, 1e-45, 2.0 ** -133, 2.0 ** -134])])
+    ref = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    mine = orc.round_bf16(x.double().numpy())
+    assert (mine == ref).all()
+
+
+def test_round_bf16_ties_and_single_rounding(orc):
+    one_ulp = 2.0 ** -7
+    # exact midpoints round to the even neighbour
+    assert orc.round_bf16(np.array([1.0 + one_ulp / 2]))[0] == 0x3F80          # -> 1.0
+    assert orc.round_bf16(np.array([1.0 + 3 * one_ulp / 2]))[0] == 0x3F82      # -> 1+2ulp
+    # just above a midpoint by less than an fp32 ulp: a double rounding through
+    # fp32 would land on the midpoint and then go to even; one rounding goes up
+    x = 1.0 + one_ulp / 2 + 2.0 ** -40
+    assert orc.round_bf16(np.array([x]))[0] == 0x3F81
+    # overflow and signed zero
+    assert orc.round_bf16(np.array([1e39]))[0] == 0x7F80
+    assert orc.round_bf16(np.array([-0.0]))[0] == 0x8000
+
+
+# ------------------------------------------------------------------ quantiser
+def _golden_quant_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "quantize_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            fmt, vals, e, codes = [p.strip() for p in line.split("|")]
+            cases.append((fmt, [float(v) for v in vals.split()], int(e),
+                          [int(c, 16) for c in codes.split()]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_quant_cases(), ids=lambda c: c[0] + "_" + str(c[2]))
+def test_quantize_golden_cases(orc, case):
+    fmt, vals, E, codes = case
+    assert len(vals) == 32 and len(codes) == 32
+    x = bf16_of(vals).reshape(1, 32)
+    dt = E4M3 if fmt == "e4m3" else E2M1
+    q, s = orc.mx_quantize(x, dt, axis=1)
+    assert s[0, 0] == E
+    if dt == E4M3:
+        assert list(q[0]) == codes
+    else:
+        unpacked = [(int(q[0, i // 2]) >> (4 * (i & 1))) & 15 for i in range(32)]
+        assert unpacked == codes
+
+
+def _scale_exponent(vals):
+    """Block scale from the closed form, floor(log2 amax) via exact frexp."""
+    amax = np.abs(vals).max(axis=-1)
+    _, e = np.frexp(amax)
+    return e - 1
+
+
+def test_quantize_e4m3_elements_match_torch(orc):
+    # torch's fp32 -> float8_e4m3fn conversion rounds to nearest-even and does
+    # not saturate, so clamp to +-448 before handing it the scaled values
+    x = rand_bf16((256, 256), seed=11)
+    xv = orc.bf16_to_f64(x)
+    # outliers and tiny values to reach saturation and subnormals
+    x2 = rand_bf16((64, 256), seed=12, std=1e-3)
+    x = np.concatenate([x, x2], axis=0)
+    xv = orc.bf16_to_f64(x)
+    q, s = orc.mx_quantize(x, E4M3, axis=1)
+    blocks = xv.reshape(-1, 32)
+    scale = np.exp2(s.reshape(-1).astype(np.float64) - 127.0)
+    scaled = np.clip(blocks / scale[:, None], -448.0, 448.0)
+    ref = torch.from_numpy(scaled.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (q.reshape(-1, 32) == ref).all()
+    # the scale: floor(log2 amax) - 8 + 127, from numpy's frexp
+    assert (s.reshape(-1) == np.clip(_scale_exponent(blocks) - 8 + 127, 0, 254)).all()
+
+
+def test_quantize_roundtrip_exact_on_representable(orc):
+    # blocks whose elements are grid values times 2^k and whose largest
+    # magnitude is the grid maximum's exponent: dequant(quant(v)) == v
+    rng = np.random.default_rng(5)
+    for dt, grid, top in ((E4M3, [orc.e4m3_value(c) for c in range(0x7F)], 1.75 * 256),
+                          (E2M1, [orc.e2m1_value(c) for c in range(8)], 6.0)):
+        grid = np.array(grid)
+        rows = []
+        for k in range(-20, 21, 4):
+            v = rng.choice(grid[grid >= 0.015625 if dt == E4M3 else grid >= 0], size=32)
+            v *= rng.choice([-1.0, 1.0], size=32)
+            v[rng.integers(32)] = top
+            rows.append(v * 2.0 ** k)
+        vals = np.array(rows)
+        x = bf16_of(vals)
+        q, s = orc.mx_quantize(x, dt, axis=1)
+        back = orc.mx_dequantize(dt, q, s, *vals.shape)
+        assert (back == vals).all()
+
+
+def test_quantize_axis0_equals_axis1_of_transpose(orc):
+    x = rand_bf16((64, 96), seed=3)
+    for dt in (E4M3, E2M1):
+        q0, s0 = orc.mx_quantize(x, dt, axis=0)
+        q1, s1 = orc.mx_quantize(np.ascontiguousarray(x.T), dt, axis=1)
+        assert (s0 == s1.T).all()
+        if dt == E4M3:
+            assert (q0 == q1.T).all()
+        else:
+            lo0, hi0 = q0 & 15, q0 >> 4          # rows 2i, 2i+1
+            lo1, hi1 = q1 & 15, q1 >> 4          # cols 2i, 2i+1
+            assert (lo0 == lo1.T).all() and (hi0 == hi1.T).all()
+
+
+def test_quantize_scale_power_of_two_invariance(orc):
+    # multiplying a block by 2^j shifts its scale byte by j and keeps its codes
+    x = rand_bf16((32, 64), seed=9)
+    xv = orc.bf16_to_f64(x)
+    for dt in (E4M3, E2M1):
+        q, s = orc.mx_quantize(x, dt)
+        q3, s3 = orc.mx_quantize(bf16_of(xv * 8.0), dt)
+        assert (q3 == q).all() and (s3.astype(int) == s.astype(int) + 3).all()
+
+
+def test_e2m1_packing_low_nibble_is_even_column(orc):
+    vals = np.zeros(32)
+    vals[0], vals[1] = 1.0, 6.0          # scale 2^0 (amax 6): codes 2 and 7
+    q, s = orc.mx_quantize(bf16_of(vals).reshape(1, 32), E2M1)
+    assert s[0, 0] == 127 and q[0, 0] == 0x72
+
+
+# ------------------------------------------------------------------ SwiGLU
+def test_swiglu_closed_forms(orc):
+    c = np.array([[0.0, 1.0, 40.0, -40.0, 2.0, 3.0, 1.0, 0.5]])
+    h = orc.swiglu(c)
+    assert h.shape == (1, 4)
+    assert h[0, 0] == 0.0                                    # silu(0) = 0
+    assert h[0, 1] == pytest.approx(3.0 / (1 + math.exp(-1.0)), rel=1e-15)  # gate first
+    assert h[0, 2] == pytest.approx(40.0, rel=1e-15)         # silu(x) -> x
+    assert abs(h[0, 3]) < 1e-15                              # silu(-x) -> 0
+    # swapping the halves changes the result: gate/up order matters
+    assert orc.swiglu(c[:, [4, 5, 6, 7, 0, 1, 2, 3]])[0, 1] != h[0, 1]
+
+
+# ------------------------------------------------------------------ GEMMs
+def _setup(G, lens, K, N, seed, trans_b=0, integer=False):
+    M = int(sum(lens))
+    if integer:
+        rng = np.random.default_rng(seed)
+        av = rng.integers(-4, 5, size=(M, K)).astype(np.float64)
+        bv = rng.integers(-4, 5, size=(G, K, N)).astype(np.float64)
+        a, b = bf16_of(av), bf16_of(bv)
+    else:
+        a = rand_bf16((M, K), seed)
+        b = rand_bf16((G, K, N), seed + 1)
+    if trans_b:
+        b = np.ascontiguousarray(b.transpose(0, 2, 1))
+    return M, a, b
+
+
+def test_fwd_single_expert_equals_dense_numpy(orc):
+    lens = np.array([37])
+    M, a, b = _setup(1, lens, 48, 20, seed=1)
+    got = orc.fwd_rows(BF16, a, None, b, None, lens, 20, 48, 0, np.arange(M))
+    ref = orc.bf16_to_f64(a) @ orc.bf16_to_f64(b)[0]
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("trans_b", [0, 1])
+def test_fwd_integer_inputs_exact(orc, trans_b):
+    lens = np.array([5, 0, 7, 1, 0, 3])
+    G, K, N = 6, 32, 12
+    M, a, b = _setup(G, lens, K, N, seed=2, trans_b=trans_b, integer=True)
+    got = orc.fwd_rows(BF16, a, None, b, None, lens, N, K, trans_b, np.arange(M))
+    ai = orc.bf16_to_f64(a).astype(np.int64)
+    bi = orc.bf16_to_f64(b).astype(np.int64)
+    if trans_b:
+        bi = bi.transpose(0, 2, 1)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    for g in range(G):
+        ref = ai[offs[g]:offs[g + 1]] @ bi[g]
+        assert (got[offs[g]:offs[g + 1]] == ref).all()
+
+
+def test_fwd_scaled_identity_maps_rows_to_experts(orc):
+    # B_g = 2^(g+1) I: every output row is its A row times its expert's factor,
+    # so any wrong row -> expert assignment shows up exactly
+    lens = np.array([3, 0, 4, 2])
+    G, K = 4, 16
+    M = int(lens.sum())
+    a = rand_bf16((M, K), seed=4)
+    bv = np.stack([np.eye(K) * 2.0 ** (g + 1) for g in range(G)])
+    got = orc.fwd_rows(BF16, a, None, bf16_of(bv), None, lens, K, K, 0, np.arange(M))
+    expert = np.repeat(np.arange(G), lens)
+    assert (got == orc.bf16_to_f64(a) * (2.0 ** (expert + 1))[:, None]).all()
+
+
+def test_fwd_row_sampling_and_rejects_uncovered_rows(orc):
+    lens = np.array([4, 0, 5])
+    M, a, b = _setup(3, lens, 32, 8, seed=6)
+    full = orc.fwd_rows(BF16, a, None, b, None, lens, 8, 32, 0, np.arange(M))
+    some = orc.fwd_rows(BF16, a, None, b, None, lens, 8, 32, 0, np.array([8, 0, 4]))
+    assert (some == full[[8, 0, 4]]).all()
+    with pytest.raises(ValueError):
+        orc.fwd_rows(BF16, a, None, b, None, lens, 8, 32, 0, np.array([M]))
+
+
+def test_adjoint_identity_fwd_dgrad_wgrad(orc):
+    # <dY, A B> = <dY B^T, A> = <A^T dY, B> summed over experts
+    lens = np.array([6, 0, 9, 3])
+    G, K, N = 4, 32, 24
+    M, a, b = _setup(G, lens, K, N, seed=8)
+    dy = rand_bf16((M, N), seed=10)
+    rows = np.arange(M)
+    av, bv, dyv = orc.bf16_to_f64(a), orc.bf16_to_f64(b), orc.bf16_to_f64(dy)
+    c = orc.fwd_rows(BF16, a, None, b, None, lens, N, K, 0, rows)
+    dx = orc.dgrad_rows(dy, b, lens, N, K, 0, rows)
+    gs = np.repeat(np.arange(G), K)
+    ks = np.tile(np.arange(K), G)
+    dw = orc.wgrad_rows(a, dy, lens, N, K, gs, ks).reshape(G, K, N)
+    t1 = (dyv * c).sum()
+    t2 = (dx * av).sum()
+    t3 = (dw * bv).sum()
+    assert t1 == pytest.approx(t2, rel=1e-12) and t1 == pytest.approx(t3, rel=1e-12)
+    assert (dw[1] == 0).all()                        # empty expert
+
+
+def test_dgrad_layouts_agree_and_match_numpy(orc):
+    lens = np.array([7, 2, 0, 5])
+    G, K, N = 4, 40, 16
+    M, a, b = _setup(G, lens, K, N, seed=12)
+    dy = rand_bf16((M, N), seed=13)
+    rows = np.arange(M)
+    d0 = orc.dgrad_rows(dy, b, lens, N, K, 0, rows)
+    d1 = orc.dgrad_rows(dy, np.ascontiguousarray(b.transpose(0, 2, 1)), lens, N, K, 1, rows)
+    assert np.allclose(d0, d1, rtol=1e-13, atol=1e-14)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    bv, dyv = orc.bf16_to_f64(b), orc.bf16_to_f64(dy)
+    for g in range(G):
+        ref = dyv[offs[g]:offs[g + 1]] @ bv[g].T
+        assert np.allclose(d0[offs[g]:offs[g + 1]], ref, rtol=1e-13, atol=1e-14)
+
+
+def test_wgrad_sum_over_experts_is_dense_atdy(orc):
+    lens = np.array([5, 0, 11, 1])
+    G, K, N = 4, 24, 20
+    M, a, _ = _setup(G, lens, K, N, seed=14)
+    dy = rand_bf16((M, N), seed=15)
+    gs = np.repeat(np.arange(G), K)
+    ks = np.tile(np.arange(K), G)
+    dw = orc.wgrad_rows(a, dy, lens, N, K, gs, ks).reshape(G, K, N)
+    ref = orc.bf16_to_f64(a).T @ orc.bf16_to_f64(dy)
+    assert np.allclose(dw.sum(0), ref, rtol=1e-12, atol=1e-13)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    g = 2
+    refg = orc.bf16_to_f64(a)[offs[g]:offs[g + 1]].T @ orc.bf16_to_f64(dy)[offs[g]:offs[g + 1]]
+    assert np.allclose(dw[g], refg, rtol=1e-12, atol=1e-13)
+
+
+def test_wgrad_accumulate_rounds_once(orc):
+    base = np.array([1.0, 1.0, -2.0], np.float32)
+    d = np.array([2.0 ** -24, 2.0 ** -24 + 2.0 ** -50, 0.0])
+    out = orc.wgrad_accumulate(base, d, accumulate=True)
+    # 1 + 2^-24 is an exact fp32 midpoint -> even (1.0); a hair above -> up
+    assert out[0] == np.float32(1.0)
+    assert out[1] == np.nextafter(np.float32(1.0), np.float32(2.0))
+    assert out[2] == np.float32(-2.0)
+    assert (orc.wgrad_accumulate(base, d, accumulate=False) == d.astype(np.float32)).all()
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E2M1])
+def test_mx_fwd_matches_dense_on_decoded_values(orc, fmt):
+    rng = np.random.default_rng(21 + fmt)
+    lens = np.array([9, 0, 4])
+    G, K, N = 3, 64, 16
+    M = int(lens.sum())
+    cols = K if fmt == E4M3 else K // 2
+    a = rng.integers(0, 256, size=(M, cols), dtype=np.uint8)
+    b = rng.integers(0, 256, size=(G, N, cols), dtype=np.uint8)
+    if fmt == E4M3:                                  # avoid the NaN codes
+        a[(a & 0x7F) == 0x7F] -= 1
+        b[(b & 0x7F) == 0x7F] -= 1
+    as_ = rng.integers(120, 135, size=(M, K // 32), dtype=np.uint8)
+    bs = rng.integers(120, 135, size=(G, N, K // 32), dtype=np.uint8)
+    got = orc.fwd_rows(fmt, a, as_, b, bs, lens, N, K, 1, np.arange(M))
+    # independent decode: per-code tables (pinned above) times 2^(E-127)
+    if fmt == E4M3:
+        tab = np.array([orc.e4m3_value(c) for c in range(256)])
+        av, bvv = tab[a], tab[b]
+    else:
+        tab = np.array([orc.e2m1_value(c) for c in range(16)])
+        av = np.stack([tab[a & 15], tab[a >> 4]], axis=-1).reshape(M, K)
+        bvv = np.stack([tab[b & 15], tab[b >> 4]], axis=-1).reshape(G, N, K)
+    av = av * np.repeat(np.exp2(as_.astype(float) - 127), 32, axis=1)
+    bvv = bvv * np.repeat(np.exp2(bs.astype(float) - 127), 32, axis=2)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    for g in range(G):
+        ref = av[offs[g]:offs[g + 1]] @ bvv[g].T
+        assert np.allclose(got[offs[g]:offs[g + 1]], ref, rtol=1e-13, atol=0)
+    # one scale byte up doubles exactly the products that use that block
+    as2 = as_.copy()
+    as2[:, 1] += 1
+    got2 = orc.fwd_rows(fmt, a, as2, b, bs, lens, N, K, 1, np.arange(M))
+    half = av.copy()
+    half[:, 32:] *= 2
+    for g in range(G):
+        ref = half[offs[g]:offs[g + 1]] @ bvv[g].T
+        assert np.allclose(got2[offs[g]:offs[g + 1]], ref, rtol=1e-13, atol=0)
+
+
+def test_epilogue_composition(orc):
+    lens = np.array([3, 4])
+    G, K, N = 2, 32, 64
+    M, a, b = _setup(G, lens, K, N, seed=30)
+    rows = np.arange(M)
+    r = orc.grouped_fwd(BF16, a, None, b, None, lens, N, K, 0, orc.EPI_SWIGLU_MXFP4, rows)
+    c = orc.fwd_rows(BF16, a, None, b, None, lens, N, K, 0, rows)
+    g, u = c[:, :N // 2], c[:, N // 2:]
+    assert np.allclose(r["exact"], g / (1 + np.exp(-g)) * u, rtol=1e-14, atol=0)
+    assert r["q"].shape == (M, N // 4) and r["s"].shape == (M, N // 64)
+
+
+def test_mlp_row_sampling_matches_full(orc):
+    rng = np.random.default_rng(40)
+    lens = np.array([5, 0, 6, 3])
+    G, H, I = 4, 64, 32
+    M = int(lens.sum())
+    x = rand_bf16((M, H), seed=41)
+    w1 = rand_bf16((G * 2 * I, H), seed=42)
+    w2 = rand_bf16((G * H, I), seed=43)
+    w1q, w1s = orc.mx_quantize(w1, E2M1)
+    w2q, w2s = orc.mx_quantize(w2, E2M1)
+    w1q, w1s = w1q.reshape(G, 2 * I, H // 2), w1s.reshape(G, 2 * I, H // 32)
+    w2q, w2s = w2q.reshape(G, H, I // 2), w2s.reshape(G, H, I // 32)
+    full = orc.mlp_mxfp4_rows(x, w1q, w1s, w2q, w2s, lens, H, I, np.arange(M))
+    pick = np.sort(rng.choice(M, size=6, replace=False))
+    some = orc.mlp_mxfp4_rows(x, w1q, w1s, w2q, w2s, lens, H, I, pick)
+    assert (some["exact"] == full["exact"][pick]).all()
+    # and it equals the step-by-step chain over all rows
+    xq, xs = orc.mx_quantize(x, E2M1)
+    c1 = orc.fwd_rows(E2M1, xq, xs, w1q, w1s, lens, 2 * I, H, 1, np.arange(M))
+    hq, hs = orc.mx_quantize(orc.round_bf16(orc.swiglu(c1)), E2M1)
+    c2 = orc.fwd_rows(E2M1, hq, hs, w2q, w2s, lens, H, I, 1, np.arange(M))
+    assert (c2 == full["exact"]).all()
