@@ -1,0 +1,359 @@
+"""Benchmark of the MoE expert grouped GEMM on one MI355X.
+
+Headline (the JSON line's `value`): BF16 grouped GEMM forward of a
+DeepSeek-V4-Flash-like MoE FC1 layer -- 256 experts, 8192 tokens routed top-6
+(49152 rows, imbalanced seeded routing with empty and tiny experts),
+hidden K = 4096, N = 4096 ([gate | up] for intermediate 2048), weights
+[experts, K, N], fused SwiGLU epilogue to [49152, 2048] -- in TFLOP/s of
+useful FLOPs (2 * sum(group_lens) * K * N per step).  A step is one call of
+pt_grouped_gemm_fwd with inputs resident in HBM.
+
+`per_config` adds the other workloads (measured the same way, not part of
+`value`): the tiny 4-expert case, BF16 dgrad and wgrad into an fp32
+main_grad at the same shape, MXFP8 forward and its quantise kernel at a
+GPT-OSS-20B-like shape, and the MXFP4 expert MLP (quantise -> FC1 + SwiGLU +
+MXFP4 epilogue -> FC2).
+
+`cpu_baseline` times the oracle (fp64 CPU reference) on a bounded sample of
+the headline workload's rows on this host; its outputs also give a parity
+check of the same GPU output.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import moe_expert_grouped_gemm_amd as ptm  # noqa: E402
+from moe_expert_grouped_gemm_amd import synth  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2516.6, "mxfp8": 5033.2, "mxfp4": 10066.3}   # dense MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "grouped-GEMM TFLOP/s (useful FLOPs) + % of dtype MFMA peak, BF16/MXFP8/MXFP4"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_expert_grouped_gemm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("src_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, stream):
+    """Warm up, then time exactly `steps` calls: wall clock between two
+    device synchronisations, and each launch between HIP events on the
+    stream the kernels run on."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per = np.array([s.elapsed_time(e) for s, e in evs])
+    return wall_ms / steps, per
+
+
+def roofline(flops, nbytes, seconds, dtype):
+    t_mfma = flops / (PEAK_TFLOPS[dtype] * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        ach = nbytes / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    ach = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_TFLOPS[dtype], 4)}
+
+
+def summary(name, dtype, flops, nbytes, per_ms, extra=None):
+    sec = float(np.median(per_ms)) * 1e-3
+    d = {"workload": name, "dtype": dtype,
+         "ms_median": round(float(np.median(per_ms)), 4),
+         "ms_p10": round(float(np.percentile(per_ms, 10)), 4),
+         "ms_p90": round(float(np.percentile(per_ms, 90)), 4),
+         "useful_tflops": round(flops / sec / 1e12, 2) if flops else None,
+         "pct_mfma_peak": round(100 * flops / sec / 1e12 / PEAK_TFLOPS[dtype], 2) if flops else None,
+         "algorithmic_gbs": round(nbytes / sec / 1e9, 1),
+         "roofline": roofline(flops, nbytes, sec, dtype) if flops else
+         {"bound": "hbm", "achieved": round(nbytes / sec / 1e9, 1), "peak": PEAK_HBM_GBS,
+          "unit": "GB/s", "frac": round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 4)}}
+    if extra:
+        d.update(extra)
+    return d
+
+
+# ------------------------------------------------------------------ workloads
+def fc1_inputs(dev):
+    lens = synth.lens_topk_gaussian(8192, 256, 6, seed=1)
+    G, M, K, N = 256, int(lens.sum()), 4096, 4096
+    a = synth.randn_bf16((M, K), seed=101, std=K ** -0.5, device=dev)
+    b = synth.randn_bf16((G, K, N), seed=101 + 1000, std=K ** -0.5, device=dev)
+    return lens, G, M, K, N, a, b
+
+
+def bytes_weights(lens, per_expert):
+    return int((lens > 0).sum()) * per_expert
+
+
+def cpu_baseline(lens, a, b, out, K, N, min_s=10.0, max_s=30.0):
+    """Oracle (fp64) over whole experts' rows of the headline workload until
+    about min_s seconds of CPU work; returns the baseline record and the
+    parity of the GPU output on those rows."""
+    import oracle
+    offs = synth.offsets(lens)
+    rng = np.random.default_rng(7)
+    order = [g for g in rng.permutation(len(lens)) if lens[g] > 0]
+    done_flops, t_used, errs, rows_done, experts = 0.0, 0.0, [], 0, 0
+    for g in order:
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        rows = np.arange(r0, r1)
+        if rows.size > 64:
+            rows = np.sort(rng.choice(rows, size=64, replace=False))
+        a_rows = synth.bf16_bits(a[torch.as_tensor(rows, device=a.device)])
+        bg = synth.bf16_bits(b[g:g + 1])
+        t0 = time.perf_counter()
+        res = oracle.grouped_fwd(oracle.BF16, a_rows, None, bg, None, np.array([rows.size]), N, K, 0,
+                                 oracle.EPI_SWIGLU, np.arange(rows.size))
+        t_used += time.perf_counter() - t0
+        done_flops += 2.0 * rows.size * K * N
+        rows_done += rows.size
+        experts += 1
+        got = (out[torch.as_tensor(rows, device=out.device)].view(torch.int16).cpu().numpy()
+               .view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        ref = res["exact"]
+        floor = float(np.sqrt(np.mean(ref * ref)))
+        errs.append(float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), floor))))
+        if t_used >= min_s or t_used >= max_s:
+            break
+    rec = {"value": round(done_flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+           "kind": "oracle",
+           "sample": f"{rows_done} rows (<=64 per expert) of {experts} experts of the headline "
+                     f"workload, fwd + SwiGLU in fp64, {t_used:.1f} s"}
+    return rec, max(errs)
+
+
+def bench_fc1(dev, stream, steps, warmup):
+    lens, G, M, K, N, a, b = fc1_inputs(dev)
+    out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
+    lens_d = torch.as_tensor(lens, device=dev)
+
+    def step():
+        ptm.pt_grouped_gemm_fwd(a, None, b, None, out, None, lens_d, None, G, M, N, K,
+                                ptm.PT_BF16, 0, ptm.PT_EPI_SWIGLU, stream=stream)
+
+    ms_step, per = time_launches(step, steps, warmup, stream)
+    flops = 2.0 * M * K * N
+    nbytes = bytes_weights(lens, K * N * 2) + M * K * 2 + M * (N // 2) * 2
+    return dict(lens=lens, G=G, M=M, K=K, N=N, a=a, b=b, out=out, lens_d=lens_d,
+                ms_step=ms_step, per=per, flops=flops, nbytes=nbytes)
+
+
+def bench_cfg0(dev, stream, iters):
+    lens = synth.lens_multinomial(256, 4, seed=0, n_empty=1)
+    G, M, K, N = 4, int(lens.sum()), 128, 256
+    a = synth.randn_bf16((M, K), seed=100, std=K ** -0.5, device=dev)
+    b = synth.randn_bf16((G, K, N), seed=101, std=K ** -0.5, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    lens_d = torch.as_tensor(lens, device=dev)
+    _, per = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
+        a, None, b, None, out, None, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, ptm.PT_EPI_NONE,
+        stream=stream), iters, 10, stream)
+    flops = 2.0 * M * K * N
+    nbytes = bytes_weights(lens, K * N * 2) + M * K * 2 + M * N * 2
+    return summary("tiny BF16 fwd, 4 experts, M=256, K=128, N=256", "bf16", flops, nbytes, per)
+
+
+def bench_cfg2(dev, stream, iters, fc1):
+    lens, G, M, K, N, a, b = fc1["lens"], fc1["G"], fc1["M"], fc1["K"], fc1["N"], fc1["a"], fc1["b"]
+    lens_d = fc1["lens_d"]
+    dy = synth.randn_bf16((M, N), seed=102, std=1e-2, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    _, per_d = time_launches(lambda: ptm.pt_grouped_gemm_dgrad(
+        dy, None, b, None, dx, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, stream=stream), iters, 2, stream)
+    flops = 2.0 * M * K * N
+    d = summary("BF16 dgrad, 256 experts, M=49152, K=N=4096", "bf16", flops,
+                bytes_weights(lens, K * N * 2) + M * N * 2 + M * K * 2, per_d)
+    del dx
+    g = torch.Generator(device=dev)
+    g.manual_seed(103)
+    mg = torch.randn((G, K, N), generator=g, device=dev, dtype=torch.float32).mul_(1e-3)
+    _, per_w = time_launches(lambda: ptm.pt_grouped_gemm_wgrad(
+        a, None, dy, None, mg, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, 1, stream=stream), iters, 2, stream)
+    w = summary("BF16 wgrad accumulated into fp32 main_grad [256, 4096, 4096]", "bf16", flops,
+                bytes_weights(lens, K * N * 4 * 2) + M * K * 2 + M * N * 2, per_w)
+    del mg, dy
+    torch.cuda.empty_cache()
+    return d, w
+
+
+def bench_cfg3(dev, stream, iters):
+    lens = synth.lens_zipf_distinct(16384, 32, 4, 1.1, seed=3)
+    G, M, K, N = 32, int(lens.sum()), 2880, 5760
+    x = synth.randn_bf16((M, K), seed=104, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    w = synth.randn_bf16((G * N, K), seed=104 + 1000, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    aq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    bq = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
+    bs = torch.empty((G * N, K // 32), dtype=torch.uint8, device=dev)
+    ptm.pt_mx_quantize(w, bq, bs, G * N, K, ptm.PT_MXFP8_E4M3, 1, stream=stream)
+    del w
+    _, per_q = time_launches(lambda: ptm.pt_mx_quantize(x, aq, as_, M, K, ptm.PT_MXFP8_E4M3, 1, stream=stream),
+                             iters, 3, stream)
+    q = summary("MXFP8 quantise of A [65536, 2880]", "mxfp8", 0, M * K * 2 + M * K + M * K // 32, per_q)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    lens_d = torch.as_tensor(lens, device=dev)
+    _, per = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
+        aq, as_, bq, bs, out, None, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, 1, ptm.PT_EPI_NONE,
+        stream=stream), iters, 3, stream)
+    flops = 2.0 * M * K * N
+    nbytes = bytes_weights(lens, N * K + N * K // 32) + M * K + M * K // 32 + M * N * 2
+    f = summary("MXFP8 fwd, 32 experts (Zipf 1.1), M=65536, K=2880, N=5760", "mxfp8", flops, nbytes, per,
+                {"group_lens_min_median_max": [int(lens.min()), int(np.median(lens)), int(lens.max())]})
+    return f, q
+
+
+def bench_cfg4(dev, stream, iters, lens):
+    G, M, H, I = 256, int(lens.sum()), 4096, 2048
+    x = synth.randn_bf16((M, H), seed=105, device=dev)
+    w1q = torch.empty((G * 2 * I, H // 2), dtype=torch.uint8, device=dev)
+    w1s = torch.empty((G * 2 * I, H // 32), dtype=torch.uint8, device=dev)
+    w2q = torch.empty((G * H, I // 2), dtype=torch.uint8, device=dev)
+    w2s = torch.empty((G * H, I // 32), dtype=torch.uint8, device=dev)
+    for rows, cols, q, s, seed in ((G * 2 * I, H, w1q, w1s, 1105), (G * H, I, w2q, w2s, 2105)):
+        wb = synth.randn_bf16((rows, cols), seed=seed, device=dev)
+        ptm.pt_mx_quantize(wb, q, s, rows, cols, ptm.PT_MXFP4_E2M1, 1, stream=stream)
+        del wb
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    xq = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M, H // 32), dtype=torch.uint8, device=dev)
+    hq = torch.empty((M, I // 2), dtype=torch.uint8, device=dev)
+    hs = torch.empty((M, I // 32), dtype=torch.uint8, device=dev)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    lens_d = torch.as_tensor(lens, device=dev)
+
+    def mlp():
+        ptm.pt_mx_quantize(x, xq, xs, M, H, ptm.PT_MXFP4_E2M1, 1, stream=stream)
+        ptm.pt_grouped_gemm_fwd(xq, xs, w1q, w1s, hq, hs, lens_d, None, G, M, 2 * I, H,
+                                ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_SWIGLU_MXFP4, stream=stream)
+        ptm.pt_grouped_gemm_fwd(hq, hs, w2q, w2s, out, None, lens_d, None, G, M, H, I,
+                                ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_NONE, stream=stream)
+
+    _, per = time_launches(mlp, iters, 3, stream)
+    flops = 2.0 * M * H * 2 * I + 2.0 * M * I * H
+    ne = int((lens > 0).sum())
+    nbytes = (ne * (2 * I * H // 2 + 2 * I * H // 32 + H * I // 2 + H * I // 32)
+              + M * H * 2 + 2 * (M * I // 2 + M * I // 32) + M * H * 2)
+    return summary("MXFP4 expert MLP quantise -> FC1 + SwiGLU + MXFP4 -> FC2, 256 experts, M=49152, "
+                   "H=4096, I=2048", "mxfp4", flops, nbytes, per)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--headline-only", action="store_true", help="skip per_config workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="comma list of per_config keys to run")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(this library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ptm.load()
+    stream = torch.cuda.current_stream()
+
+    log("headline: BF16 FC1 + SwiGLU, 256 experts, M=49152, K=N=4096")
+    fc1 = bench_fc1(dev, stream, args.steps, args.warmup)
+    kern_ms = float(np.mean(fc1["per"]))
+    sec = kern_ms * 1e-3
+    value = fc1["flops"] / (fc1["ms_step"] * 1e-3) / 1e12
+    roof = roofline(fc1["flops"], fc1["nbytes"], sec, "bf16")
+    roof["traffic"] = measured_traffic("fc1_bf16_swiglu")
+    lens = fc1["lens"]
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(fc1["ms_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded routing and N(0,1/K) bf16 tensors; no trained weights)",
+        "config": {"workload": "BF16 MoE FC1 forward + fused SwiGLU, DeepSeek-V4-Flash-like layer",
+                   "experts": 256, "tokens": 8192, "top_k": 6, "rows": int(fc1["M"]),
+                   "K": 4096, "N": 4096, "out": [int(fc1["M"]), 2048], "weight_layout": "[G,K,N]",
+                   "group_lens_min_p10_median_max": [int(lens.min()), int(np.percentile(lens, 10)),
+                                                     int(np.median(lens)), int(lens.max())],
+                   "empty_experts": int((lens == 0).sum())},
+        "pct_mfma_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
+        "kernel_ms_mean": round(kern_ms, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a sample of the headline workload")
+        rec, err = cpu_baseline(lens, fc1["a"], fc1["b"], fc1["out"], fc1["K"], fc1["N"])
+        line["cpu_baseline"] = rec
+        line["parity_sample_max_floored_rel_err"] = round(err, 6)
+    if not args.headline_only:
+        per = {}
+        want = set(args.only.split(",")) if args.only else None
+        iters = max(5, min(args.steps, 20))
+        if want is None or "cfg0" in want:
+            log("per_config: tiny")
+            per["cfg0_tiny_bf16_fwd"] = bench_cfg0(dev, stream, 50)
+        if want is None or "cfg2" in want:
+            log("per_config: dgrad / wgrad")
+            per["cfg2_bf16_dgrad"], per["cfg2_bf16_wgrad"] = bench_cfg2(dev, stream, iters, fc1)
+        b_keep_lens = fc1["lens"]
+        for k in ("a", "b", "out"):
+            fc1.pop(k)
+        torch.cuda.empty_cache()
+        if want is None or "cfg3" in want:
+            log("per_config: MXFP8")
+            per["cfg3_mxfp8_fwd"], per["cfg3_mxfp8_quantize_A"] = bench_cfg3(dev, stream, iters)
+            torch.cuda.empty_cache()
+        if want is None or "cfg4" in want:
+            log("per_config: MXFP4 MLP")
+            per["cfg4_mxfp4_mlp"] = bench_cfg4(dev, stream, iters, b_keep_lens)
+        line["per_config"] = per
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

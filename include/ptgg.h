@@ -1,0 +1,202 @@
+/*
+ * ptgg.h -- C ABI of the MoE expert grouped GEMM library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation: the tokens routed to the experts of a Mixture-of-Experts
+ * layer arrive sorted by expert, so expert g owns a contiguous run of
+ * group_lens[g] rows of the activation matrix, and every expert multiplies
+ * its own rows by its own weight matrix.  All experts are issued as ONE
+ * kernel over the ragged batch instead of one small GEMM per expert (blog
+ * "Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with
+ * Primus", section "Expert parallelism: DeepEP and the grouped GEMM", and
+ * its optimisation-ladder table, rung "Turbo grouped GEMM").
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named a, b, dy, out, dx, main_grad, q, scales, group_lens,
+ *    group_offs and workspace are DEVICE pointers on the current HIP device.
+ *    The library never dereferences them on the host, never allocates, never
+ *    frees and never synchronises; the caller owns every buffer and keeps it
+ *    alive until the work queued on `stream` has finished.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is only enqueued; calls return immediately.
+ *  - Row ranges: expert g owns rows [offs[g], offs[g] + group_lens[g]) of the
+ *    row-indexed operands, where offs = group_offs (int64[G+1]) when given,
+ *    else the exclusive prefix sum of group_lens computed on the device.
+ *    group_lens are int64, >= 0, and come from the router on the device; the
+ *    host never reads them.  Experts with zero rows are allowed anywhere.
+ *    Device code clamps every range into [0, M], so malformed lengths never
+ *    cause an out-of-bounds access; it records them instead in the optional
+ *    error word (see pt_read_error_flags).
+ *  - Element types (pt_dtype):
+ *      PT_BF16         bfloat16, row-major.
+ *      PT_MXFP8_E4M3   OCP-MX: one E4M3 byte per element + one E8M0 scale
+ *                      byte per 32 consecutive elements along the reduction
+ *                      dimension K.
+ *      PT_MXFP4_E2M1   OCP-MX: E2M1 codes packed two per byte (even element
+ *                      in the low nibble, the float4_e2m1fn_x2 layout named
+ *                      in the PR page "[Megatron-LM] feat: add grouped gemm
+ *                      fp4 support, skip cache trans weight and santize
+ *                      code", section "Changes") + one E8M0 scale per 32.
+ *    For MX operands the scales form a row-major [rows, K/32] byte matrix.
+ *  - Accumulation is in fp32 on the matrix cores; outputs are rounded once
+ *    (bf16 round-to-nearest-even, or fp32 for main_grad).
+ *  - Return value: a pt_status.  On any error nothing is launched.
+ */
+#ifndef PTGG_H
+#define PTGG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PT_OK = 0,
+    PT_ERR_INVALID_ARG = 1,  /* NULL required pointer, negative or inconsistent size */
+    PT_ERR_UNSUPPORTED = 2,  /* dtype/layout/epilogue combination, too many experts, not gfx950 */
+    PT_ERR_MISALIGNED = 3,   /* pointer or leading dimension not 16-byte aligned */
+    PT_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
+    PT_ERR_HIP = 5           /* a HIP runtime call failed */
+} pt_status;
+
+typedef enum {
+    PT_BF16 = 0,
+    PT_MXFP8_E4M3 = 1,
+    PT_MXFP4_E2M1 = 2
+} pt_dtype;
+
+typedef enum {
+    PT_EPI_NONE = 0,         /* out = bf16(C), [M, N]                               */
+    PT_EPI_SWIGLU = 1,       /* out = bf16(silu(C[:, :N/2]) * C[:, N/2:]), [M, N/2] */
+    PT_EPI_SWIGLU_MXFP4 = 2  /* SWIGLU's bf16 value, then MXFP4-quantised along its
+                                columns: out = codes [M, N/4] bytes,
+                                out_scale = E8M0 [M, N/64]                         */
+} pt_epilogue;
+
+typedef enum {
+    PT_OP_FWD = 0,
+    PT_OP_DGRAD = 1,
+    PT_OP_WGRAD = 2
+} pt_op;
+
+/* Largest expert count one call accepts. */
+#define PT_MAX_GROUPS 1024
+
+/*
+ * Grouped forward: for every expert g and each of its rows r,
+ *     C[r, :] = A[r, :] . B_g            (B_g is K x N)
+ * followed by the epilogue.  This is the FC1/FC2 expert GEMM; the SwiGLU
+ * epilogue takes the FC1 output as [gate | up] halves, gate first, since the
+ * FC1 weight stacks gate and up projections (blog "Enabling DeepSeek-V4-Flash
+ * Training on AMD Instinct MI355X GPUs with Primus", section "MegaMoE: fusing
+ * communication into the grouped GEMM", weight w1 [g, 2I, H] "gate + up", with
+ * SwiGLU between the two grouped GEMMs; Primus-Turbo README, "What's New":
+ * expert MLP with SwiGLU folded into the grouped GEMM).
+ *
+ *  a          [M, K]   activations (bf16 / E4M3 bytes / packed E2M1 [M, K/2])
+ *  a_scale    [M, K/32] E8M0, MX only (else NULL)
+ *  b          trans_b = 0: [G, K, N] (bf16 only); trans_b = 1: [G, N, K], the
+ *             [experts, out, in] weight layout (required for MX)
+ *  b_scale    [G, N, K/32] E8M0, MX only
+ *  out        see pt_epilogue; rows outside every expert are not written
+ *  out_scale  [M, N/64] E8M0 for PT_EPI_SWIGLU_MXFP4, else NULL
+ *  Requirements: K % 8 == 0 (bf16) or K % 32 == 0 (MX); N % 8 == 0 (bf16,
+ *  trans_b = 0); N even for SWIGLU, N % 128 == 0 for SWIGLU_MXFP4.
+ *  workspace  optional (may be NULL); if given and >= 4 bytes its first
+ *             32-bit word receives the sticky device error bits.
+ */
+int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale,
+                        const void *b, const uint8_t *b_scale,
+                        void *out, uint8_t *out_scale,
+                        const int64_t *group_lens, const int64_t *group_offs,
+                        int64_t G, int64_t M, int64_t N, int64_t K,
+                        int dtype, int trans_b, int epilogue,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Grouped data gradient: for every expert g and each of its rows r,
+ *     dX[r, k] = sum_n dY[r, n] * B_g[k, n]
+ * (the grouped GEMM's backward flow, PR page "[Megatron-LM] feat: add grouped
+ * gemm fp4 support, ...", Copilot overview: the grouped linear returns to the
+ * standard grouped GEMM backward).
+ *  dy  [M, N] bf16;  b as in pt_grouped_gemm_fwd (trans_b selects [G,K,N] or
+ *  [G,N,K]);  dx  [M, K] bf16.  dtype must be PT_BF16 (MX backward returns
+ *  PT_ERR_UNSUPPORTED; the scale arguments must then be NULL).
+ *  Requirements: N % 8 == 0 and K % 8 == 0.
+ */
+int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale,
+                          const void *b, const uint8_t *b_scale, void *dx,
+                          const int64_t *group_lens, const int64_t *group_offs,
+                          int64_t G, int64_t M, int64_t N, int64_t K,
+                          int dtype, int trans_b,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Grouped weight gradient, accumulated into an fp32 main_grad (PR page
+ * "[Megatron-LM] feat: add grouped gemm fp4 support, ...", section "Changes":
+ * the weight gradient is always accumulated into weight.main_grad and the
+ * weight is flagged as having its gradient added):
+ *     D_g[k, n] = sum over expert g's rows r of A[r, k] * dY[r, n]
+ *     main_grad[g] = (accumulate ? main_grad[g] : 0) + D_g     (fp32, RNE)
+ * The reduction length is the expert's own row count.
+ *  a  [M, K] bf16;  dy  [M, N] bf16;
+ *  main_grad  trans_out = 0: [G, K, N];  trans_out = 1: [G, N, K]  (fp32)
+ *  An expert with no rows leaves its main_grad slice untouched when
+ *  accumulating and writes zeros when not.
+ *  workspace: pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ...) bytes (may be
+ *  0, in which case workspace may be NULL).
+ *  Requirements: K % 8 == 0, N % 8 == 0; dtype PT_BF16.
+ */
+int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
+                          const void *dy, const uint8_t *dy_scale,
+                          float *main_grad,
+                          const int64_t *group_lens, const int64_t *group_offs,
+                          int64_t G, int64_t M, int64_t N, int64_t K,
+                          int dtype, int trans_out, int accumulate,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * OCP-MX quantisation of a bf16 matrix x [rows, cols], one block per 32
+ * consecutive elements along the columns (axis = 1; the only axis served):
+ *   E = clamp(floor(log2(max|v|)) - emax + 127, 0, 254)   (E = 0 for an
+ *       all-zero block; emax = 8 for E4M3, 2 for E2M1)
+ *   code_i = nearest element-format value to v_i / 2^(E-127), ties to even,
+ *            magnitudes beyond the format's maximum saturate, sign kept.
+ * (MX weight buffers of the PR page "[Megatron-LM] feat: add grouped gemm fp4
+ * support, ...", section "Changes"; the Primus-Turbo README lists MXFP8 and
+ * MXFP4 grouped GEMMs under "What's New".)
+ *  q       E4M3: [rows, cols] bytes;  E2M1: [rows, cols/2] bytes (even column
+ *          in the low nibble)
+ *  scales  [rows, cols/32] E8M0 bytes
+ *  dtype   PT_MXFP8_E4M3 or PT_MXFP4_E2M1.  Requirements: cols % 32 == 0.
+ *  NaN/Inf inputs are outside the contract (no fault; results unspecified).
+ */
+int pt_mx_quantize(const void *x, void *q, uint8_t *scales,
+                   int64_t rows, int64_t cols, int dtype, int axis, void *stream);
+
+/* Bytes of workspace `op` needs for these sizes (0 when none). */
+size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N,
+                                      int64_t K, int dtype);
+
+/*
+ * Sticky device error bits recorded in the first word of a workspace by the
+ * grouped GEMM kernels (bit 0: a negative group length; bit 1: an expert
+ * range outside [0, M] was clamped; bit 2: the lengths do not sum to M).
+ * The caller zeroes the word before the calls it wants to check.  This call
+ * synchronises `stream` and copies the word to *flags (host pointer).
+ */
+int pt_read_error_flags(const void *workspace, void *stream, uint32_t *flags);
+
+/* Human-readable name of a pt_status. */
+const char *pt_status_string(int status);
+
+/* Library version string. */
+const char *pt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTGG_H */

@@ -1,0 +1,162 @@
+"""MoE expert grouped GEMM for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/ptgg.h`` (``libptgg.so``,
+built in-tree by ``build.py``).  Each ``pt_*`` function here has the C
+function's name and argument order; it only turns torch tensors into device
+pointers, picks the current HIP stream and raises on a non-zero status.
+Every step of the computation runs in the library's HIP kernels: there is no
+fallback path, and using the package without the built library or without a
+GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+__all__ = [
+    "PT_BF16", "PT_MXFP8_E4M3", "PT_MXFP4_E2M1",
+    "PT_EPI_NONE", "PT_EPI_SWIGLU", "PT_EPI_SWIGLU_MXFP4",
+    "PT_OP_FWD", "PT_OP_DGRAD", "PT_OP_WGRAD",
+    "load", "lib_path", "PtggError",
+    "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_wgrad",
+    "pt_mx_quantize", "pt_grouped_gemm_workspace_size", "pt_read_error_flags",
+    "pt_status_string", "pt_version",
+]
+
+PT_BF16, PT_MXFP8_E4M3, PT_MXFP4_E2M1 = 0, 1, 2
+PT_EPI_NONE, PT_EPI_SWIGLU, PT_EPI_SWIGLU_MXFP4 = 0, 1, 2
+PT_OP_FWD, PT_OP_DGRAD, PT_OP_WGRAD = 0, 1, 2
+
+EXPORTS = (
+    "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_wgrad",
+    "pt_mx_quantize", "pt_grouped_gemm_workspace_size", "pt_read_error_flags",
+    "pt_status_string", "pt_version",
+)
+
+_lib = None
+
+
+class PtggError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {pt_status_string(status)} ({status})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def load(require_gpu: bool = True):
+    """Load libptgg.so (building it first only if it has not been built)."""
+    global _lib
+    if require_gpu and not torch.cuda.is_available():
+        raise RuntimeError("moe_expert_grouped_gemm_amd needs a gfx950 GPU; none is visible")
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    L = ctypes.CDLL(_build.LIB)
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.pt_grouped_gemm_fwd.restype = i32
+    L.pt_grouped_gemm_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
+    L.pt_grouped_gemm_dgrad.restype = i32
+    L.pt_grouped_gemm_dgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, p, sz, p]
+    L.pt_grouped_gemm_wgrad.restype = i32
+    L.pt_grouped_gemm_wgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
+    L.pt_mx_quantize.restype = i32
+    L.pt_mx_quantize.argtypes = [p, p, p, i64, i64, i32, i32, p]
+    L.pt_grouped_gemm_workspace_size.restype = sz
+    L.pt_grouped_gemm_workspace_size.argtypes = [i32, i64, i64, i64, i64, i32]
+    L.pt_read_error_flags.restype = i32
+    L.pt_read_error_flags.argtypes = [p, p, ctypes.POINTER(ctypes.c_uint32)]
+    L.pt_status_string.restype = ctypes.c_char_p
+    L.pt_status_string.argtypes = [i32]
+    L.pt_version.restype = ctypes.c_char_p
+    L.pt_version.argtypes = []
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return t.data_ptr()
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, status):
+    if status != 0:
+        raise PtggError(fn, status)
+
+
+def pt_grouped_gemm_fwd(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs,
+                        G, M, N, K, dtype, trans_b, epilogue, workspace=None, stream=None):
+    L = load()
+    _check("pt_grouped_gemm_fwd", L.pt_grouped_gemm_fwd(
+        _ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), _ptr(out), _ptr(out_scale),
+        _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_b, epilogue,
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def pt_grouped_gemm_dgrad(dy, dy_scale, b, b_scale, dx, group_lens, group_offs,
+                          G, M, N, K, dtype, trans_b, workspace=None, stream=None):
+    L = load()
+    _check("pt_grouped_gemm_dgrad", L.pt_grouped_gemm_dgrad(
+        _ptr(dy), _ptr(dy_scale), _ptr(b), _ptr(b_scale), _ptr(dx),
+        _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_b,
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def pt_grouped_gemm_wgrad(a, a_scale, dy, dy_scale, main_grad, group_lens, group_offs,
+                          G, M, N, K, dtype, trans_out, accumulate, workspace=None, stream=None):
+    L = load()
+    _check("pt_grouped_gemm_wgrad", L.pt_grouped_gemm_wgrad(
+        _ptr(a), _ptr(a_scale), _ptr(dy), _ptr(dy_scale), _ptr(main_grad),
+        _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_out, accumulate,
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def pt_mx_quantize(x, q, scales, rows, cols, dtype, axis=1, stream=None):
+    L = load()
+    _check("pt_mx_quantize", L.pt_mx_quantize(
+        _ptr(x), _ptr(q), _ptr(scales), rows, cols, dtype, axis, _stream(stream)))
+
+
+def pt_grouped_gemm_workspace_size(op, G, M, N, K, dtype) -> int:
+    return int(load(require_gpu=False).pt_grouped_gemm_workspace_size(op, G, M, N, K, dtype))
+
+
+def pt_read_error_flags(workspace, stream=None) -> int:
+    L = load()
+    flags = ctypes.c_uint32(0)
+    _check("pt_read_error_flags", L.pt_read_error_flags(_ptr(workspace), _stream(stream), ctypes.byref(flags)))
+    return int(flags.value)
+
+
+def pt_status_string(status: int) -> str:
+    return load(require_gpu=False).pt_status_string(int(status)).decode()
+
+
+def pt_version() -> str:
+    return load(require_gpu=False).pt_version().decode()

@@ -1,0 +1,260 @@
+// api.cpp -- the C ABI (include/ptgg.h): host-side argument checks and
+// dispatch to the gfx950 kernels.  Nothing here reads device memory,
+// allocates or synchronises (except pt_read_error_flags, a test helper).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/ptgg.h"
+#include "launch.hpp"
+
+namespace ptgg {
+
+int device_cus()
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+namespace {
+
+// 1 when the current device is gfx950, 0 otherwise (cached per device).
+bool device_is_gfx950()
+{
+    static int state[64] = {0};  // 0 unknown, 1 yes, 2 no
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    std::lock_guard<std::mutex> lock(mu);
+    if (state[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+        state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return state[dev] == 1;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_groups(const int64_t *lens, int64_t G, int64_t M)
+{
+    if (!lens || G < 1 || M < 0) return PT_ERR_INVALID_ARG;
+    if (G > PT_MAX_GROUPS) return PT_ERR_UNSUPPORTED;
+    if (M > (int64_t)INT32_MAX / 2) return PT_ERR_UNSUPPORTED;
+    return PT_OK;
+}
+
+uint32_t *error_word(void *ws, size_t bytes) { return (ws && bytes >= 4) ? (uint32_t *)ws : nullptr; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PT_OK : PT_ERR_HIP; }
+
+}  // namespace
+}  // namespace ptgg
+
+using namespace ptgg;
+
+extern "C" {
+
+int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale,
+                        void *out, uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs,
+                        int64_t G, int64_t M, int64_t N, int64_t K, int dtype, int trans_b, int epilogue,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = check_groups(group_lens, G, M);
+    if (st) return st;
+    if (N < 1 || K < 1 || N > INT32_MAX / 4 || K > INT32_MAX / 4) return PT_ERR_INVALID_ARG;
+    if (M > 0 && (!a || !b || !out)) return PT_ERR_INVALID_ARG;
+    if (epilogue < PT_EPI_NONE || epilogue > PT_EPI_SWIGLU_MXFP4) return PT_ERR_UNSUPPORTED;
+    if (trans_b != 0 && trans_b != 1) return PT_ERR_INVALID_ARG;
+    if (epilogue == PT_EPI_SWIGLU && N % 16) return PT_ERR_UNSUPPORTED;
+    if (epilogue == PT_EPI_SWIGLU_MXFP4 && !out_scale) return PT_ERR_INVALID_ARG;
+    if (epilogue == PT_EPI_SWIGLU_MXFP4 && N % 64) return PT_ERR_UNSUPPORTED;
+    if (epilogue != PT_EPI_SWIGLU_MXFP4 && out_scale) return PT_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    const int ep = epilogue == PT_EPI_SWIGLU ? kEpiSwiglu : epilogue == PT_EPI_SWIGLU_MXFP4 ? kEpiSwigluMxfp4 : kEpiNone;
+    const int64_t Nc = epilogue == PT_EPI_NONE ? N : N / 2;   // columns per expert tile
+    const int64_t ldo = epilogue == PT_EPI_NONE ? N : epilogue == PT_EPI_SWIGLU ? N / 2 : N / 4;
+    if (dtype == PT_BF16) {
+        if (a_scale || b_scale) return PT_ERR_INVALID_ARG;
+        if (K % 8) return PT_ERR_UNSUPPORTED;
+        if (!trans_b && N % 8) return PT_ERR_UNSUPPORTED;
+        Bf16Params p = {};
+        p.a = (const uint16_t *)a;
+        p.b = (const uint16_t *)b;
+        p.out = out;
+        p.out_scale = out_scale;
+        p.lens = group_lens;
+        p.offs = group_offs;
+        p.err = error_word(workspace, workspace_bytes);
+        p.G = (int)G;
+        p.M = M;
+        p.Kred = (int)K;
+        p.Nout = (int)N;
+        p.lda = (int)K;
+        p.ldb = trans_b ? (int)K : (int)N;
+        p.b_gstride = N * K;
+        p.ldo = (int)ldo;
+        p.tilesN = (int)((Nc + (epilogue == PT_EPI_NONE ? bf16_tile_n() : bf16_tile_n() / 2) - 1) /
+                         (epilogue == PT_EPI_NONE ? bf16_tile_n() : bf16_tile_n() / 2));
+        if (M == 0) return PT_OK;
+        return hip_status(launch_bf16(p, trans_b ? kFwdKContig : kFwdNContig, ep, s));
+    }
+    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) {
+        if (!trans_b) return PT_ERR_UNSUPPORTED;           // scales run along K
+        if (K % 32) return PT_ERR_UNSUPPORTED;
+        if (M > 0 && (!a_scale || !b_scale)) return PT_ERR_INVALID_ARG;
+        MxParams p = {};
+        p.a = (const uint8_t *)a;
+        p.as = a_scale;
+        p.b = (const uint8_t *)b;
+        p.bs = b_scale;
+        p.out = out;
+        p.out_scale = out_scale;
+        p.lens = group_lens;
+        p.offs = group_offs;
+        p.err = error_word(workspace, workspace_bytes);
+        p.G = (int)G;
+        p.M = M;
+        p.N = (int)N;
+        p.K = (int)K;
+        p.ldo = (int)ldo;
+        const int tn = epilogue == PT_EPI_NONE ? mx_tile_n() : mx_tile_n() / 2;
+        p.tilesN = (int)((Nc + tn - 1) / tn);
+        if (M == 0) return PT_OK;
+        return hip_status(launch_mx(p, dtype == PT_MXFP8_E4M3 ? 0 : 1, ep, s));
+    }
+    return PT_ERR_UNSUPPORTED;
+}
+
+int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b, const uint8_t *b_scale, void *dx,
+                          const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M, int64_t N,
+                          int64_t K, int dtype, int trans_b, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = check_groups(group_lens, G, M);
+    if (st) return st;
+    if (N < 1 || K < 1 || N > INT32_MAX / 4 || K > INT32_MAX / 4) return PT_ERR_INVALID_ARG;
+    if (M > 0 && (!dy || !b || !dx)) return PT_ERR_INVALID_ARG;
+    if (trans_b != 0 && trans_b != 1) return PT_ERR_INVALID_ARG;
+    if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
+    if (dy_scale || b_scale) return PT_ERR_INVALID_ARG;
+    if (N % 8 || K % 8) return PT_ERR_UNSUPPORTED;
+    if (!aligned16(dy) || !aligned16(b) || !aligned16(dx)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    // dX[r, k] = sum_n dY[r, n] B[k, n]: reduction over n, output columns k.
+    Bf16Params p = {};
+    p.a = (const uint16_t *)dy;
+    p.b = (const uint16_t *)b;
+    p.out = dx;
+    p.lens = group_lens;
+    p.offs = group_offs;
+    p.err = error_word(workspace, workspace_bytes);
+    p.G = (int)G;
+    p.M = M;
+    p.Kred = (int)N;
+    p.Nout = (int)K;
+    p.lda = (int)N;
+    p.ldb = trans_b ? (int)K : (int)N;   // [G,K,N]: row k holds n contiguous
+    p.b_gstride = N * K;
+    p.ldo = (int)K;
+    p.tilesN = (int)((K + bf16_tile_n() - 1) / bf16_tile_n());
+    if (M == 0) return PT_OK;
+    return hip_status(launch_bf16(p, trans_b ? kFwdNContig : kFwdKContig, kEpiNone, (hipStream_t)stream));
+}
+
+int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy, const uint8_t *dy_scale,
+                          float *main_grad, const int64_t *group_lens, const int64_t *group_offs, int64_t G,
+                          int64_t M, int64_t N, int64_t K, int dtype, int trans_out, int accumulate,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = check_groups(group_lens, G, M);
+    if (st) return st;
+    if (N < 8 || K < 8 || N > INT32_MAX / 4 || K > INT32_MAX / 4) return PT_ERR_INVALID_ARG;
+    if (!main_grad || (M > 0 && (!a || !dy))) return PT_ERR_INVALID_ARG;
+    if (trans_out != 0 && trans_out != 1) return PT_ERR_INVALID_ARG;
+    if (accumulate != 0 && accumulate != 1) return PT_ERR_INVALID_ARG;
+    if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
+    if (a_scale || dy_scale) return PT_ERR_INVALID_ARG;
+    if (N % 8 || K % 8) return PT_ERR_UNSUPPORTED;
+    if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    Bf16Params p = {};
+    // trans_out = 0: D[k, n] = sum_r A[r, k] dY[r, n];  1: D^T[n, k] with the
+    // operands swapped
+    p.a = (const uint16_t *)(trans_out ? dy : a);
+    p.b = (const uint16_t *)(trans_out ? a : dy);
+    p.lda = (int)(trans_out ? N : K);
+    p.ldb = (int)(trans_out ? K : N);
+    p.Mout = (int)(trans_out ? N : K);
+    p.Nout = (int)(trans_out ? K : N);
+    p.out = main_grad;
+    p.ldo = p.Nout;
+    p.o_gstride = N * K;
+    p.lens = group_lens;
+    p.offs = group_offs;
+    p.err = error_word(workspace, workspace_bytes);
+    p.G = (int)G;
+    p.M = M;
+    p.tilesM = (p.Mout + bf16_tile_m() - 1) / bf16_tile_m();
+    p.tilesN = (p.Nout + bf16_tile_n() - 1) / bf16_tile_n();
+    p.accumulate = accumulate;
+    if (M == 0 && accumulate) return PT_OK;
+    return hip_status(launch_bf16(p, kWgrad, kEpiNone, (hipStream_t)stream));
+}
+
+int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_t cols, int dtype, int axis,
+                   void *stream)
+{
+    if (rows < 0 || cols < 0) return PT_ERR_INVALID_ARG;
+    if (axis != 1) return PT_ERR_UNSUPPORTED;
+    if (dtype != PT_MXFP8_E4M3 && dtype != PT_MXFP4_E2M1) return PT_ERR_UNSUPPORTED;
+    if (cols % 32) return PT_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0) return PT_OK;
+    if (!x || !q || !scales) return PT_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    return hip_status(launch_quantize((const uint16_t *)x, (uint8_t *)q, scales, rows, cols,
+                                      dtype == PT_MXFP8_E4M3 ? 0 : 1, (hipStream_t)stream));
+}
+
+size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, int64_t K, int dtype)
+{
+    (void)op; (void)G; (void)M; (void)N; (void)K; (void)dtype;
+    return 256;   // the error word, rounded up to one allocation granule
+}
+
+int pt_read_error_flags(const void *workspace, void *stream, uint32_t *flags)
+{
+    if (!workspace || !flags) return PT_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipStreamSynchronize(s) != hipSuccess) return PT_ERR_HIP;
+    if (hipMemcpy(flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return PT_ERR_HIP;
+    return PT_OK;
+}
+
+const char *pt_status_string(int status)
+{
+    switch (status) {
+    case PT_OK: return "PT_OK";
+    case PT_ERR_INVALID_ARG: return "PT_ERR_INVALID_ARG";
+    case PT_ERR_UNSUPPORTED: return "PT_ERR_UNSUPPORTED";
+    case PT_ERR_MISALIGNED: return "PT_ERR_MISALIGNED";
+    case PT_ERR_WORKSPACE: return "PT_ERR_WORKSPACE";
+    case PT_ERR_HIP: return "PT_ERR_HIP";
+    default: return "PT_ERR_UNKNOWN";
+    }
+}
+
+const char *pt_version(void) { return "ptgg 0.1.0 (gfx950)"; }
+
+}  // extern "C"

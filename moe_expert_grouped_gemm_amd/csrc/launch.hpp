@@ -1,0 +1,66 @@
+// launch.hpp -- internal launcher interface between the C ABI and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ptgg {
+
+// C[m, j] = sum_q A[m, q] * Bop(j, q) per expert (forward and dgrad), or
+// D[i, j] = sum over the expert's rows r of A[r, i] * B[r, j] (wgrad).
+struct Bf16Params {
+    const uint16_t *a;
+    const uint16_t *b;
+    void *out;
+    uint8_t *out_scale;  // SwiGLU -> MXFP4 epilogue only
+    const int64_t *lens;
+    const int64_t *offs;
+    uint32_t *err;
+    int G;
+    int64_t M;
+    int Kred;          // fwd/dgrad: reduction length
+    int Nout;          // output columns before the epilogue
+    int Mout;          // wgrad: output rows per expert
+    int lda, ldb;      // leading dimensions (elements)
+    int64_t b_gstride; // fwd/dgrad: elements between experts' weight matrices
+    int ldo;           // output leading dimension (elements)
+    int64_t o_gstride; // wgrad: elements between experts' main_grad slices
+    int tilesN;
+    int tilesM;        // wgrad only
+    int accumulate;    // wgrad only
+};
+
+enum Bf16Kind { kFwdKContig = 0, kFwdNContig = 1, kWgrad = 2 };
+enum Epi { kEpiNone = 0, kEpiSwiglu = 1, kEpiSwigluMxfp4 = 2 };
+
+hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s);
+int bf16_tile_m();
+int bf16_tile_n();
+
+struct MxParams {
+    const uint8_t *a;        // [M, K] codes (E4M3) or [M, K/2] (E2M1)
+    const uint8_t *as;       // [M, K/32]
+    const uint8_t *b;        // [G, N, K(/2)]
+    const uint8_t *bs;       // [G, N, K/32]
+    void *out;
+    uint8_t *out_scale;
+    const int64_t *lens;
+    const int64_t *offs;
+    uint32_t *err;
+    int G;
+    int64_t M;
+    int N, K;
+    int ldo;                 // output row stride (elements for bf16, bytes for MXFP4)
+    int tilesN;
+};
+
+hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);
+int mx_tile_m();
+int mx_tile_n();
+
+hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales,
+                           int64_t rows, int64_t cols, int fmt, hipStream_t s);
+
+// Number of compute units of the current device (cached per device).
+int device_cus();
+
+}  // namespace ptgg
