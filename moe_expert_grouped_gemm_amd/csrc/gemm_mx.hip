@@ -87,8 +87,15 @@ __device__ __forceinline__ void store_stage(const Stage &st, uint8_t *s)
     *(uintx2 *)(s + TILE_A + TILE_B + threadIdx.x * SC_STRIDE) = st.sc;
 }
 
-// One k-step of 2 x 2 blocks of 32 x 32 per wave.  MFMA step s covers scale
-// blocks 2s and 2s+1 of the k-step: lane half h = l >> 5 takes block 2s + h.
+// One k-step of 2 x 2 blocks of 32 x 32 per wave.  MFMA step s covers the 64
+// values of scale blocks 2s and 2s+1 of the k-step; lane half h = l >> 5
+// supplies the E8M0 byte of block 2s + h.  Which operand bytes that scale
+// multiplies depends on the element width (measured on gfx950):
+//  - E2M1: the lane's 16 bytes (32 values) all belong to the lane's own
+//    scale, so lane half h holds block 2s + h whole;
+//  - E4M3: bytes 0-15 of BOTH lane halves take half 0's scale and bytes
+//    16-31 take half 1's, so lane half h holds values 16h..16h+15 of block
+//    2s in bytes 0-15 and values 16h..16h+15 of block 2s+1 in bytes 16-31.
 template <int FMT>
 __device__ __forceinline__ void mma_stage(floatx16 (&acc)[2][2], const uint8_t *s, int wm, int wn,
                                           int nvalid_bi)
@@ -106,20 +113,22 @@ __device__ __forceinline__ void mma_stage(floatx16 (&acc)[2][2], const uint8_t *
 #pragma unroll
     for (int st = 0; st < F::blocks / 2; ++st) {
         const int blk = 2 * st + h;                 // scale block of this lane
-        const int off = blk * F::bytes_per_lane;    // byte offset in the row slice
+        // byte offsets (in the row's k-step slice) of the lane's two 16-byte halves
+        const int off_lo = FMT == 0 ? 64 * st + 16 * h : 16 * blk;
+        const int off_hi = 64 * st + 32 + 16 * h;  // E4M3 only
         intx8 af[2], bf[2];
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi) {
-            const uint8_t *p = sA + (wm * 64 + bi * 32 + r) * LDS_STRIDE + off;
-            intx4 lo = *(const intx4 *)p;
-            intx4 hi = F::bytes_per_lane == 32 ? *(const intx4 *)(p + 16) : intx4{0, 0, 0, 0};
+            const uint8_t *p = sA + (wm * 64 + bi * 32 + r) * LDS_STRIDE;
+            intx4 lo = *(const intx4 *)(p + off_lo);
+            intx4 hi = FMT == 0 ? *(const intx4 *)(p + off_hi) : intx4{0, 0, 0, 0};
             af[bi] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
         for (int bj = 0; bj < 2; ++bj) {
-            const uint8_t *p = sB + (wn * 64 + bj * 32 + r) * LDS_STRIDE + off;
-            intx4 lo = *(const intx4 *)p;
-            intx4 hi = F::bytes_per_lane == 32 ? *(const intx4 *)(p + 16) : intx4{0, 0, 0, 0};
+            const uint8_t *p = sB + (wn * 64 + bj * 32 + r) * LDS_STRIDE;
+            intx4 lo = *(const intx4 *)(p + off_lo);
+            intx4 hi = FMT == 0 ? *(const intx4 *)(p + off_hi) : intx4{0, 0, 0, 0};
             bf[bj] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
         int as[2], bs[2];
