@@ -289,6 +289,9 @@ def main():
     ap.add_argument("--headline-only", action="store_true", help="skip per_config workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None, help="comma list of per_config keys to run")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB --steps times "
+                         "(reference kernel for calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -301,6 +304,14 @@ def main():
     torch.cuda.set_device(dev)
     ptm.load()
     stream = torch.cuda.current_stream()
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        _, per = time_launches(lambda: dst.copy_(src), args.steps, args.warmup, stream)
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                          "ms_mean": float(np.mean(per)), "gbs": 2 * n / (np.mean(per) * 1e-3) / 1e9}))
+        return
 
     log("headline: BF16 FC1 + SwiGLU, 256 experts, M=49152, K=N=4096")
     fc1 = bench_fc1(dev, stream, args.steps, args.warmup)
