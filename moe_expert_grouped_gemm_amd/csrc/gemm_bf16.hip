@@ -1,19 +1,35 @@
 // gemm_bf16.hip -- BF16 grouped GEMM for gfx950: forward (with optional fused
-// SwiGLU epilogue), data gradient and variable-length weight gradient.
+// SwiGLU / SwiGLU->MXFP4 epilogue), data gradient and variable-length weight
+// gradient.
 //
 // One persistent kernel walks the ragged batch: every workgroup builds the
 // expert/tile table in LDS from the device-resident group lengths, then takes
-// linear tile ids in an XCD-aware order.  Tiles are BM x BN outputs; the
-// reduction runs in BK-deep steps staged through double-buffered LDS and fed
-// to v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
+// linear tile ids in an XCD-aware order.  Tiles are 128 x 256 outputs; the
+// reduction runs in 32-deep steps through an NSTAGE-deep ring of LDS buffers
+// filled by direct buffer->LDS loads (buffer_load_dwordx4 ... lds), so several
+// steps of operand traffic are in flight while the matrix cores work on the
+// oldest one.  Each operand of a tile gets a buffer resource whose record
+// bound is exactly the expert's slice, a fixed 32-bit offset per lane and a
+// scalar offset that advances one step per k-step: issuing a stage costs no
+// vector ALU work, and rows past an expert's end read as zeros.  The last,
+// partial k-step (if any) gives every lane an explicit bound check instead.
+//
+// Operands are kept in LDS in the layout they have in memory:
+//  - reduction-contiguous ([row][k]): 16-byte chunks XOR-swizzled by row,
+//    read with ds_read_b128;
+//  - column-contiguous ([k][col]): 16-byte chunks XOR-swizzled by k, read
+//    with the gfx950 transposing ds_read_b64_tr_b16, which hands every lane
+//    four consecutive k values of one column.
+// Fragment reads are issued as inline asm with immediate offsets from
+// per-lane bases computed once: the compiler cannot tell them apart from
+// reads of the LDS still being filled by the in-flight direct loads and would
+// otherwise wait for every outstanding load before each of them.
 //
 //  forward / dgrad:  C[m, j] = sum_q A[m, q] * Bop(j, q), m in one expert's
-//                    rows.  Bop is read either reduction-contiguous ([j][q])
-//                    or column-contiguous ([q][j], transposed on the way into
-//                    LDS).
+//                    rows; A is reduction-contiguous, Bop either layout.
 //  wgrad:            D[i, j] = sum over the expert's rows r of A[r, i] * B[r, j];
-//                    both operands are read row-by-row (transposed into LDS)
-//                    and the result is added into the fp32 main_grad once.
+//                    both operands column-contiguous; the result is added
+//                    into the fp32 main_grad once per element.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
@@ -22,111 +38,298 @@ namespace ptgg {
 
 namespace {
 
-constexpr int BM = kTileM, BN = kTileN, BK = 64;
-constexpr int LDS_STRIDE = BK + 8;                  // bf16 per LDS row: 144 B
-constexpr int TILE_A = BM * LDS_STRIDE;             // elements
-constexpr int TILE_B = BN * LDS_STRIDE;
-constexpr int STAGE = TILE_A + TILE_B;
-constexpr int GEMM_LDS_BYTES = 2 * STAGE * 2;       // two stages of bf16
+constexpr int BM = 128, BN = 256, BK = 32;
+constexpr int NSTAGE = 3;
+constexpr int A_BYTES = BM * BK * 2;               // 8 KiB per stage
+constexpr int B_BYTES = BN * BK * 2;               // 16 KiB per stage
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
+constexpr int A_LOADS = A_BYTES / 16 / kThreads;   // 16-byte loads per thread per stage
+constexpr int B_LOADS = B_BYTES / 16 / kThreads;
+constexpr int LOADS = A_LOADS + B_LOADS;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;       // raw buffer, 32-bit data format
+constexpr uint32_t kOOB = 0x80000000u;             // offset past every record bound
 
-struct Frag {
-    uintx4 v[4];
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait for the oldest in-flight stage when `after` younger stages (of LOADS
+// loads per thread each) may stay outstanding.
+__device__ __forceinline__ void wait_stage(int after)
+{
+    static_assert(NSTAGE <= 6, "extend wait_stage");
+    switch (after) {
+    case 4: wait_vmcnt<(NSTAGE > 5 ? 4 : 0) * LOADS>(); break;
+    case 3: wait_vmcnt<(NSTAGE > 4 ? 3 : 0) * LOADS>(); break;
+    case 2: wait_vmcnt<(NSTAGE > 3 ? 2 : 0) * LOADS>(); break;
+    case 1: wait_vmcnt<LOADS>(); break;
+    default: wait_vmcnt<0>(); break;
+    }
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without the memory fence of __syncthreads() (which would
+// wait for every outstanding load, draining the ring); the empty asm keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+template <int OFF>
+__device__ __forceinline__ bf16x8 ldsr_b128(uint32_t addr)
+{
+    bf16x8 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ uintx2 ldsr_tr(uint32_t addr)
+{
+    uintx2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+__device__ __forceinline__ bf16x8 join(uintx2 lo, uintx2 hi)
+{
+    return __builtin_bit_cast(bf16x8, uintx4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Wait for all issued LDS reads; the fragments pass through the asm so no
+// use of them can be scheduled before the wait.
+__device__ __forceinline__ void frag_wait(bf16x8 (&a)[2], bf16x8 (&b)[4])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+// One 16-byte direct load per lane into LDS (lane i lands at lds + 16 i) from
+// byte voff + soff of a buffer of `bytes` bytes at `base`; offsets at or past
+// the bound read zeros.  Kept a plain function: the buffer-resource type is
+// device-only, and inside templates clang's host pass would silently discard
+// every kernel that reaches it.
+__device__ __forceinline__ void dma16(const void *base, uint32_t bytes, uint8_t *lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (lds_void *)lds, 16, voff, soff, 0, 0);
+}
+
+// One operand's direct-load state for a tile: NL 16-byte loads per thread
+// per stage at voff[i] + kt * kstep (bytes) inside the buffer `rsrc`.
+template <int NL>
+struct Dma {
+    const void *base;
+    uint32_t bytes;
+    uint32_t voff[NL];
+    uint32_t kstep;
 };
 
-// -------------------------------------------------------------- loaders
-// Reduction-contiguous operand: 128 tile rows x 64 reduction values, four
-// 16-byte chunks per thread.  Row index r maps to a source row via `rowptr`.
-template <class RowPtr>
-__device__ __forceinline__ void load_kcontig(Frag &f, RowPtr rowptr, int k0, int Kred)
+// Issue one stage of an operand: slot i of this thread lands at LDS byte
+// lds_off + (i * 256 + thread) * 16.
+template <int NL>
+__device__ __forceinline__ void issue(uint8_t *smem, const Dma<NL> &d, uint32_t lds_off, uint32_t soff,
+                                      const uint32_t (&voff)[NL], int wave)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int c = threadIdx.x + i * kThreads;
-        int r = c >> 3, kc = c & 7;
-        int k = k0 + kc * 8;
-        if (k < Kred)
-            f.v[i] = *(const uintx4 *)(rowptr(r) + k);
-        else
-            f.v[i] = uintx4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < NL; ++i)
+        dma16(d.base, d.bytes, smem + lds_off + (i * kThreads + wave * kWave) * 16, voff[i], soff);
 }
 
-__device__ __forceinline__ void store_kcontig(const Frag &f, uint16_t *s)
+// ---- slot geometry.  Reduction-contiguous operand with R rows: LDS [R][32]
+// bf16 (64-byte rows of four 16-byte chunks), chunk c of row r at position
+// c ^ ((r >> 2) & 3).  Column-contiguous operand with R columns: LDS [32][R]
+// (rows of R*2 bytes), chunk c of row k at position c ^ ((k & 3) << 2).
+__device__ __forceinline__ int kpos(int r, int c) { return c ^ ((r >> 2) & 3); }
+__device__ __forceinline__ int npos(int k, int c) { return c ^ ((k & 3) << 2); }
+
+// slot s of a reduction-contiguous stage: tile row and source chunk
+__device__ __forceinline__ void kslot(int s, int &r, int &c) { r = s >> 2; c = kpos(r, s & 3); }
+// slot s of a column-contiguous stage with R columns: k row and source chunk
+template <int R>
+__device__ __forceinline__ void nslot(int s, int &k, int &c) { k = s / (R / 8); c = npos(k, s % (R / 8)); }
+
+// Tile column c (0..255) -> logical output column.  With SwiGLU a tile covers
+// 128 consecutive outputs j: within each wave's 128 columns, blocks 0-1 are
+// gate columns j and blocks 2-3 the matching up columns I + j.
+template <int EPI>
+__device__ __forceinline__ int col_of(int nt, int c, int Nout)
 {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int c = threadIdx.x + i * kThreads;
-        int r = c >> 3, kc = c & 7;
-        *(uintx4 *)(s + r * LDS_STRIDE + kc * 8) = f.v[i];
-    }
+    if (EPI == kEpiNone) return nt * BN + c;
+    const int I = Nout >> 1;
+    const int w = c >> 7, cc = c & 127;
+    const int j = nt * (BN / 2) + w * 64 + (cc & 63);
+    return cc >= 64 ? I + j : j;
 }
 
-// Column-contiguous operand: the source is [reduction][columns]; each thread
-// reads 4 reduction rows x 8 columns (four 16-byte loads) and writes the
-// transposed 8 x 4 block, so LDS holds [column][reduction] like the other
-// operand.  colptr(q, c8) returns the source address of reduction index q,
-// tile columns c8..c8+7, or nullptr when the row is outside the reduction.
-template <class ColPtr>
-__device__ __forceinline__ void load_ncontig(Frag &f, ColPtr colptr, int q0)
+// Clamp an 8-column chunk start into the valid range of its half.
+template <int EPI>
+__device__ __forceinline__ int clamp8(int n, int Nout)
 {
-    const int kb = threadIdx.x & 15, nb = threadIdx.x >> 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint16_t *src = colptr(q0 + kb * 4 + i, nb * 8);
-        f.v[i] = src ? *(const uintx4 *)src : uintx4{0u, 0u, 0u, 0u};
-    }
+    if (EPI == kEpiNone) return min(n, Nout - 8);
+    const int I = Nout >> 1;
+    return n < I ? min(n, I - 8) : min(n, Nout - 8);
 }
 
-__device__ __forceinline__ void store_ncontig(const Frag &f, uint16_t *s)
+// ------------------------------------------------------------------ epilogue
+// Wave (wm, wn) holds rows wm*64 + bi*32 + .., columns wn*128 + bj*32 + lane%32.
+__device__ __forceinline__ int e_row(int wm, int bi, int reg)
 {
-    const int kb = threadIdx.x & 15, nb = threadIdx.x >> 4;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        uint32_t r0 = f.v[0][d], r1 = f.v[1][d], r2 = f.v[2][d], r3 = f.v[3][d];
-        uintx2 lo, hi;
-        lo[0] = (r0 & 0xFFFFu) | (r1 << 16);
-        lo[1] = (r2 & 0xFFFFu) | (r3 << 16);
-        hi[0] = (r0 >> 16) | (r1 & 0xFFFF0000u);
-        hi[1] = (r2 >> 16) | (r3 & 0xFFFF0000u);
-        *(uintx2 *)(s + (nb * 8 + 2 * d) * LDS_STRIDE + kb * 4) = lo;
-        *(uintx2 *)(s + (nb * 8 + 2 * d + 1) * LDS_STRIDE + kb * 4) = hi;
-    }
+    return wm * 64 + bi * 32 + (reg >> 2) * 8 + ((threadIdx.x & 63) >> 5) * 4 + (reg & 3);
 }
 
-// -------------------------------------------------------------- MFMA step
-// Wave (wm, wn) owns the 64 x 64 sub-tile at (wm*64, wn*64): 2 x 2 blocks of
-// 32 x 32.  Lane l supplies row (l & 31) of A and column (l & 31) of B with 8
-// reduction values at offset (l >> 5) * 8 of each 16-deep step.
-__device__ __forceinline__ void mma_stage(floatx16 (&acc)[2][2], const uint16_t *sA,
-                                          const uint16_t *sB, int wm, int wn, int nvalid_bi)
+template <int EPI>
+__device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], const Bf16Params &p, int64_t row0,
+                                          int m0, int rows, int nt, int wm, int wn)
 {
     const int lane = threadIdx.x & 63;
-    const int r = lane & 31, kh = (lane >> 5) * 8;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8 af[2], bf[2];
+    if (EPI == kEpiNone) {
+        uint16_t *o = (uint16_t *)p.out + row0 * p.ldo;
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi)
-            af[bi] = *(const bf16x8 *)(sA + (wm * 64 + bi * 32 + r) * LDS_STRIDE + ks * 16 + kh);
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
-            bf[bj] = *(const bf16x8 *)(sB + (wn * 64 + bj * 32 + r) * LDS_STRIDE + ks * 16 + kh);
+            for (int bj = 0; bj < 4; ++bj) {
+                const int n = nt * BN + wn * 128 + bj * 32 + (lane & 31);
+                if (n >= p.Nout) continue;
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
-            if (bi < nvalid_bi) {
-#pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + e_row(wm, bi, r);
+                    if (m < rows) o[(int64_t)m * p.ldo + n] = (uint16_t)bf16_rne(acc[bi][bj][r]);
+                }
             }
+    } else if (EPI == kEpiSwiglu) {
+        uint16_t *o = (uint16_t *)p.out + row0 * p.ldo;
+        const int I = p.Nout >> 1;
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) {
+            const int j = nt * (BN / 2) + wn * 64 + bj * 32 + (lane & 31);
+            if (j >= I) continue;
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + e_row(wm, bi, r);
+                    if (m < rows)
+                        o[(int64_t)m * p.ldo + j] = (uint16_t)bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r]));
+                }
+        }
+    } else {
+        // SwiGLU value rounded to bf16, then one MXFP4 block per 32 outputs:
+        // the 32 lanes of a half-wave hold 32 consecutive j of one row.
+        uint8_t *o = (uint8_t *)p.out + row0 * p.ldo;
+        uint8_t *os = p.out_scale + row0 * (p.Nout / 64);
+        const int I = p.Nout >> 1;
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) {
+            const int j = nt * (BN / 2) + wn * 64 + bj * 32 + (lane & 31);
+            const bool jvalid = j < I;          // uniform over a half-wave (I % 32 == 0)
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + e_row(wm, bi, r);
+                    const uint32_t hb = bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r]));
+                    uint32_t amax = hb & 0x7FFFu;
+#pragma unroll
+                    for (int d = 1; d < 32; d <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, d, 64));
+                    const uint32_t E = mx_scale_byte<2>(amax);
+                    const uint32_t code = mx_encode<1>(hb, E);
+                    const uint32_t nb = (uint32_t)__shfl_xor((int)code, 1, 64);
+                    if (jvalid && m < rows) {
+                        if ((lane & 1) == 0) o[(int64_t)m * p.ldo + (j >> 1)] = (uint8_t)(code | (nb << 4));
+                        if ((lane & 31) == 0) os[(int64_t)m * (p.Nout / 64) + (j >> 5)] = (uint8_t)E;
+                    }
+                }
         }
     }
 }
 
+// Issue stage kt of both operands into ring slot kt % NSTAGE.  Full k-steps
+// advance the scalar offset; the partial last step bounds every lane.
+template <int KIND>
+__device__ __forceinline__ void issue_stage(uint8_t *smem, const Dma<A_LOADS> &da, const Dma<B_LOADS> &db, int kt,
+                                            int nfull, int Kred, int wave)
+{
+    const int tid = threadIdx.x;
+    const uint32_t st = (uint32_t)(kt % NSTAGE) * STAGE_BYTES;
+    if (kt < nfull) {
+        issue(smem, da, st, kt * da.kstep, da.voff, wave);
+        issue(smem, db, st + A_BYTES, kt * db.kstep, db.voff, wave);
+        return;
+    }
+    uint32_t va[A_LOADS], vb[B_LOADS];
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+        int x, c;
+        bool ok;
+        if (KIND == kWgrad) { nslot<BM>(i * kThreads + tid, x, c); ok = k0 + x < Kred; }
+        else { kslot(i * kThreads + tid, x, c); ok = k0 + c * 8 < Kred; }
+        va[i] = ok ? da.voff[i] + kt * da.kstep : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+        int x, c;
+        bool ok;
+        if (KIND == kFwdKContig) { kslot(i * kThreads + tid, x, c); ok = k0 + c * 8 < Kred; }
+        else { nslot<BN>(i * kThreads + tid, x, c); ok = k0 + x < Kred; }
+        vb[i] = ok ? db.voff[i] + kt * db.kstep : kOOB;
+    }
+    issue(smem, da, st, 0u, va, wave);
+    issue(smem, db, st + A_BYTES, 0u, vb, wave);
+}
+
+// Fragments of k-step KS of one stage at LDS byte address `so`: A rows
+// (wm*64 + bi*32 ..) and B columns (wn*128 + bj*32 ..) of this wave, from the
+// per-lane bases computed once per kernel.
+template <int KIND, int KS>
+__device__ __forceinline__ void load_frags(uint32_t so, const uint32_t (&aK)[2], const uint32_t (&aN)[2],
+                                           const uint32_t (&bK)[2], const uint32_t (&bN)[4],
+                                           bf16x8 (&af)[2], bf16x8 (&bfr)[4])
+{
+    constexpr int AO = KS * 16 * BM * 2, AJ = 4 * BM * 2;           // column-contiguous A
+    constexpr int BO = A_BYTES + KS * 16 * BN * 2, BJ = 4 * BN * 2;  // column-contiguous B
+    if constexpr (KIND == kWgrad) {
+        af[0] = join(ldsr_tr<AO>(so + aN[0]), ldsr_tr<AO + AJ>(so + aN[0]));
+        af[1] = join(ldsr_tr<AO>(so + aN[1]), ldsr_tr<AO + AJ>(so + aN[1]));
+    } else {
+        af[0] = ldsr_b128<0>(so + aK[KS]);
+        af[1] = ldsr_b128<32 * 64>(so + aK[KS]);
+    }
+    if constexpr (KIND == kFwdKContig) {
+        bfr[0] = ldsr_b128<A_BYTES + 0 * 32 * 64>(so + bK[KS]);
+        bfr[1] = ldsr_b128<A_BYTES + 1 * 32 * 64>(so + bK[KS]);
+        bfr[2] = ldsr_b128<A_BYTES + 2 * 32 * 64>(so + bK[KS]);
+        bfr[3] = ldsr_b128<A_BYTES + 3 * 32 * 64>(so + bK[KS]);
+    } else {
+        bfr[0] = join(ldsr_tr<BO>(so + bN[0]), ldsr_tr<BO + BJ>(so + bN[0]));
+        bfr[1] = join(ldsr_tr<BO>(so + bN[1]), ldsr_tr<BO + BJ>(so + bN[1]));
+        bfr[2] = join(ldsr_tr<BO>(so + bN[2]), ldsr_tr<BO + BJ>(so + bN[2]));
+        bfr[3] = join(ldsr_tr<BO>(so + bN[3]), ldsr_tr<BO + BJ>(so + bN[3]));
+    }
+}
+
+// ------------------------------------------------------------------ kernel
 template <int KIND, int EPI>
 __global__ __launch_bounds__(kThreads) void gg_bf16_kernel(Bf16Params p)
 {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    uint16_t *stage0 = (uint16_t *)smem;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     GroupTable tab;
     tab.G = p.G;
     int *tb = (int *)(smem + GEMM_LDS_BYTES);
@@ -141,14 +344,43 @@ __global__ __launch_bounds__(kThreads) void gg_bf16_kernel(Bf16Params p)
                                   TilesWgrad{p.tilesM * p.tilesN, p.accumulate}, p.err, s_scan);
     else
         total = build_group_table(tab, p.lens, p.offs, p.G, p.M, TilesFwd{BM, p.tilesN}, p.err, s_scan);
+    total = __builtin_amdgcn_readfirstlane(total);
 
-    const int wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t lds0 = lds_addr(smem);
+
+    // ---- per-lane LDS read bases (fixed for the kernel)
+    const int r32 = lane & 31, h = lane >> 5, g16 = (lane >> 4) & 1, s16 = lane & 15;
+    uint32_t aK[2], bK[2], aN[2], bN[4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int ra = wm * 64 + r32, rb = wn * 128 + r32;
+        aK[ks] = ra * 64 + kpos(ra, 2 * ks + h) * 16;
+        bK[ks] = rb * 64 + kpos(rb, 2 * ks + h) * 16;
+    }
+    {
+        const int krow = h * 8 + (s16 >> 2);                 // k & 3 == (s16 >> 2) & 3
+        const int lo = 8 * (s16 & 1);                        // byte offset inside the chunk
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+            const int col = wm * 64 + bi * 32 + 16 * g16 + 4 * (s16 & 3);
+            aN[bi] = krow * (BM * 2) + npos(krow, col >> 3) * 16 + lo;
+        }
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const int col = wn * 128 + bj * 32 + 16 * g16 + 4 * (s16 & 3);
+            bN[bj] = krow * (BN * 2) + npos(krow, col >> 3) * 16 + lo;
+        }
+    }
 
     for (int tile = xcd_logical_id(); tile < total; tile += gridDim.x) {
-        const int g = find_group(tab, tile);
-        const int local = tile - tab.tile0[g];
-        const int row0 = tab.row0[g], rows = tab.rows[g];
+        const int g = __builtin_amdgcn_readfirstlane(find_group(tab, tile));
+        const int local = tile - __builtin_amdgcn_readfirstlane(tab.tile0[g]);
+        const int row0 = __builtin_amdgcn_readfirstlane(tab.row0[g]);
+        const int rows = __builtin_amdgcn_readfirstlane(tab.rows[g]);
         int mt, nt;
         if (KIND == kWgrad) {
             mt = local / p.tilesN;
@@ -159,101 +391,127 @@ __global__ __launch_bounds__(kThreads) void gg_bf16_kernel(Bf16Params p)
             mt = local % tm;
         }
         const int m0 = mt * BM;
-
-        floatx16 acc[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-        // operand address functors
-        const uint16_t *Arow = p.a + (int64_t)row0 * p.lda;
-        const uint16_t *Bg = (KIND == kWgrad) ? p.b + (int64_t)row0 * p.ldb : p.b + (int64_t)g * p.b_gstride;
         const int Kred = (KIND == kWgrad) ? rows : p.Kred;
-        const int nk = (Kred + BK - 1) / BK;
+        const int nk = (Kred + BK - 1) / BK, nfull = Kred / BK;
         int nvalid_bi = 2;
         if (KIND != kWgrad) {
-            const int vr = min(BM, rows - m0) - wm * 64;   // valid rows in this wave
+            const int vr = min(BM, rows - m0) - wm * 64;
             nvalid_bi = vr <= 0 ? 0 : (vr > 32 ? 2 : 1);
         }
 
-        auto a_rowptr = [&](int r) { return Arow + (int64_t)min(m0 + r, rows - 1) * p.lda; };
-        auto b_rowptr = [&](int c) {
-            int n = clamp_col<EPI>(map_col<EPI>(nt, c, p.Nout), p.Nout, 1);
-            return Bg + (int64_t)n * p.ldb;
-        };
-        auto b_colptr = [&](int q, int c8) -> const uint16_t * {
-            if (q >= Kred) return nullptr;
-            int n = clamp_col<EPI>(map_col<EPI>(nt, c8, p.Nout), p.Nout, 8);
-            return Bg + (int64_t)q * p.ldb + n;
-        };
-        // wgrad: A operand columns are the output rows i
-        auto wa_colptr = [&](int q, int c8) -> const uint16_t * {
-            if (q >= rows) return nullptr;
-            int i = min(m0 + c8, p.Mout - 8);
-            return Arow + (int64_t)q * p.lda + i;
-        };
-        auto wb_colptr = [&](int q, int c8) -> const uint16_t * {
-            if (q >= rows) return nullptr;
-            int n = min(nt * BN + c8, p.Nout - 8);
-            return Bg + (int64_t)q * p.ldb + n;
-        };
-
-        Frag fa, fb;
-        auto load = [&](int kt) {
-            const int k0 = kt * BK;
-            if (KIND == kWgrad) {
-                load_ncontig(fa, wa_colptr, k0);
-                load_ncontig(fb, wb_colptr, k0);
-            } else {
-                load_kcontig(fa, a_rowptr, k0, Kred);
-                if (KIND == kFwdKContig)
-                    load_kcontig(fb, b_rowptr, k0, Kred);
-                else
-                    load_ncontig(fb, b_colptr, k0);
+        // ---- operand buffers and per-lane offsets for this tile
+        Dma<A_LOADS> da;
+        Dma<B_LOADS> db;
+        const uint16_t *Arow = p.a + (int64_t)row0 * p.lda;
+        if (KIND == kWgrad) {
+            // A operand: [token][i] slice of the expert, columns m0.. of A
+            da.base = Arow;
+            da.bytes = (uint32_t)rows * p.lda * 2;
+            da.kstep = BK * p.lda * 2;
+#pragma unroll
+            for (int i = 0; i < A_LOADS; ++i) {
+                int k, c;
+                nslot<BM>(i * kThreads + tid, k, c);
+                da.voff[i] = (uint32_t)(k * p.lda + min(m0 + c * 8, p.Mout - 8)) * 2;
             }
-        };
-        auto store = [&](uint16_t *st) {
-            if (KIND == kWgrad) {
-                store_ncontig(fa, st);
-                store_ncontig(fb, st + TILE_A);
-            } else {
-                store_kcontig(fa, st);
-                if (KIND == kFwdKContig)
-                    store_kcontig(fb, st + TILE_A);
-                else
-                    store_ncontig(fb, st + TILE_A);
+            const uint16_t *Brow = p.b + (int64_t)row0 * p.ldb;
+            db.base = Brow;
+            db.bytes = (uint32_t)rows * p.ldb * 2;
+            db.kstep = BK * p.ldb * 2;
+#pragma unroll
+            for (int i = 0; i < B_LOADS; ++i) {
+                int k, c;
+                nslot<BN>(i * kThreads + tid, k, c);
+                db.voff[i] = (uint32_t)(k * p.ldb + min(nt * BN + c * 8, p.Nout - 8)) * 2;
             }
-        };
-
-        if (nk > 0) {
-            load(0);
-            store(stage0);
+        } else {
+            // A operand: the expert's rows; rows past its end fall outside the bound
+            da.base = Arow;
+            da.bytes = (uint32_t)rows * p.lda * 2;
+            da.kstep = BK * 2;
+#pragma unroll
+            for (int i = 0; i < A_LOADS; ++i) {
+                int r, c;
+                kslot(i * kThreads + tid, r, c);
+                da.voff[i] = (uint32_t)((m0 + r) * p.lda + c * 8) * 2;
+            }
+            const uint16_t *Bg = p.b + (int64_t)g * p.b_gstride;
+            if (KIND == kFwdKContig) {
+                db.base = Bg;
+            db.bytes = (uint32_t)p.Nout * p.ldb * 2;
+                db.kstep = BK * 2;
+#pragma unroll
+                for (int i = 0; i < B_LOADS; ++i) {
+                    int r, c;
+                    kslot(i * kThreads + tid, r, c);
+                    int n = col_of<EPI>(nt, r, p.Nout);
+                    n = EPI == kEpiNone ? min(n, p.Nout - 1) : clamp8<EPI>(n & ~7, p.Nout) + (n & 7);
+                    db.voff[i] = (uint32_t)(n * p.ldb + c * 8) * 2;
+                }
+            } else {
+                db.base = Bg;
+            db.bytes = (uint32_t)Kred * p.ldb * 2;
+                db.kstep = BK * p.ldb * 2;
+#pragma unroll
+                for (int i = 0; i < B_LOADS; ++i) {
+                    int k, c;
+                    nslot<BN>(i * kThreads + tid, k, c);
+                    const int n = clamp8<EPI>(col_of<EPI>(nt, c * 8, p.Nout), p.Nout);
+                    db.voff[i] = (uint32_t)(k * p.ldb + n) * 2;
+                }
+            }
         }
-        __syncthreads();
+
+        floatx16 acc[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        auto mma = [&](const bf16x8 (&af)[2], const bf16x8 (&bfr)[4]) {
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+                if (bi < nvalid_bi) {
+#pragma unroll
+                    for (int bj = 0; bj < 4; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bfr[bj], acc[bi][bj], 0, 0, 0);
+                }
+        };
+
+#pragma unroll
+        for (int s = 0; s < NSTAGE - 1; ++s)
+            if (s < nk) issue_stage<KIND>(smem, da, db, s, nfull, Kred, wave);
+
         for (int kt = 0; kt < nk; ++kt) {
-            uint16_t *cur = stage0 + (kt & 1) * STAGE;
-            uint16_t *nxt = stage0 + ((kt + 1) & 1) * STAGE;
-            if (kt + 1 < nk) load(kt + 1);
-            mma_stage(acc, cur, cur + TILE_A, wm, wn, nvalid_bi);
-            if (kt + 1 < nk) store(nxt);
-            __syncthreads();
+            wait_stage(min(NSTAGE - 2, nk - 1 - kt));    // stage kt landed (own loads)
+            barrier();                                   // ... everyone's; slot of kt-1 free
+            if (kt + NSTAGE - 1 < nk) issue_stage<KIND>(smem, da, db, kt + NSTAGE - 1, nfull, Kred, wave);
+            static_assert(BK == 32, "two k-steps per stage");
+            const uint32_t so = lds0 + (uint32_t)(kt % NSTAGE) * STAGE_BYTES;
+            bf16x8 a0[2], b0[4], a1[2], b1[4];
+            load_frags<KIND, 0>(so, aK, aN, bK, bN, a0, b0);
+            frag_wait(a0, b0);
+            load_frags<KIND, 1>(so, aK, aN, bK, bN, a1, b1);   // in flight during step 0
+            mma(a0, b0);
+            frag_wait(a1, b1);
+            mma(a1, b1);
         }
+        wait_lgkm0();
+        barrier();                                       // LDS free for the next tile
 
-        // ------------------------------------------------------ epilogue
         if (KIND == kWgrad) {
             float *og = (float *)p.out + (int64_t)g * p.o_gstride;
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-                for (int bj = 0; bj < 2; ++bj) {
-                    const int n = nt * BN + acc_col(wn, bj);
+                for (int bj = 0; bj < 4; ++bj) {
+                    const int n = nt * BN + wn * 128 + bj * 32 + (lane & 31);
                     if (n >= p.Nout) continue;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int i = m0 + acc_row(wm, bi, r);
+                        const int i = m0 + e_row(wm, bi, r);
                         if (i < p.Mout) {
                             float *dst = og + (int64_t)i * p.ldo + n;
                             float v = acc[bi][bj][r];
@@ -263,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void gg_bf16_kernel(Bf16Params p)
                     }
                 }
         } else {
-            store_tile<EPI>(acc, p.out, p.out_scale, row0, m0, rows, nt, p.Nout, p.ldo);
+            store_out<EPI>(acc, p, row0, m0, rows, nt, wm, wn);
         }
     }
 }
@@ -274,18 +532,15 @@ hipError_t launch_one(const Bf16Params &p, hipStream_t s)
     const int lds = GEMM_LDS_BYTES + table_bytes(p.G);
     auto kern = gg_bf16_kernel<KIND, EPI>;
     static int configured_lds = 0;
-    static int occupancy = 0;
     if (configured_lds < lds) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         configured_lds = lds;
-        occupancy = 0;
     }
     int occ = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, lds);
     if (e != hipSuccess) return e;
     if (occ < 1) occ = 1;
-    (void)occupancy;
     int64_t tiles_max;
     if (KIND == kWgrad)
         tiles_max = (int64_t)p.G * p.tilesM * p.tilesN;
