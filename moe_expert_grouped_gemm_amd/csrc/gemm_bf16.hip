@@ -30,6 +30,8 @@
 //  wgrad:            D[i, j] = sum over the expert's rows r of A[r, i] * B[r, j];
 //                    both operands column-contiguous; the result is added
 //                    into the fp32 main_grad once per element.
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
@@ -39,11 +41,9 @@ namespace ptgg {
 namespace {
 
 constexpr int BM = 128, BN = 256, BK = 32;
-constexpr int NSTAGE = 3;
 constexpr int A_BYTES = BM * BK * 2;               // 8 KiB per stage
 constexpr int B_BYTES = BN * BK * 2;               // 16 KiB per stage
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
 constexpr int A_LOADS = A_BYTES / 16 / kThreads;   // 16-byte loads per thread per stage
 constexpr int B_LOADS = B_BYTES / 16 / kThreads;
 constexpr int LOADS = A_LOADS + B_LOADS;
@@ -61,14 +61,16 @@ __device__ __forceinline__ void wait_vmcnt()
 }
 
 // Wait for the oldest in-flight stage when `after` younger stages (of LOADS
-// loads per thread each) may stay outstanding.
+// loads per thread each; at most NSTAGE - 1) may stay outstanding.
+template <int NSTAGE>
 __device__ __forceinline__ void wait_stage(int after)
 {
-    static_assert(NSTAGE <= 6, "extend wait_stage");
+    static_assert(NSTAGE >= 2 && NSTAGE <= 6, "extend wait_stage");
     switch (after) {
-    case 4: wait_vmcnt<(NSTAGE > 5 ? 4 : 0) * LOADS>(); break;
-    case 3: wait_vmcnt<(NSTAGE > 4 ? 3 : 0) * LOADS>(); break;
-    case 2: wait_vmcnt<(NSTAGE > 3 ? 2 : 0) * LOADS>(); break;
+    case 5: wait_vmcnt<(NSTAGE > 5 ? 5 : NSTAGE - 1) * LOADS>(); break;
+    case 4: wait_vmcnt<(NSTAGE > 4 ? 4 : NSTAGE - 1) * LOADS>(); break;
+    case 3: wait_vmcnt<(NSTAGE > 3 ? 3 : NSTAGE - 1) * LOADS>(); break;
+    case 2: wait_vmcnt<(NSTAGE > 2 ? 2 : NSTAGE - 1) * LOADS>(); break;
     case 1: wait_vmcnt<LOADS>(); break;
     default: wait_vmcnt<0>(); break;
     }
@@ -262,7 +264,7 @@ __device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], const Bf1
 
 // Issue stage kt of both operands into ring slot kt % NSTAGE.  Full k-steps
 // advance the scalar offset; the partial last step bounds every lane.
-template <int KIND>
+template <int KIND, int NSTAGE>
 __device__ __forceinline__ void issue_stage(uint8_t *smem, const Dma<A_LOADS> &da, const Dma<B_LOADS> &db, int kt,
                                             int nfull, int Kred, int wave)
 {
@@ -326,9 +328,10 @@ __device__ __forceinline__ void load_frags(uint32_t so, const uint32_t (&aK)[2],
 }
 
 // ------------------------------------------------------------------ kernel
-template <int KIND, int EPI>
-__global__ __launch_bounds__(kThreads) void gg_bf16_kernel(Bf16Params p)
+template <int KIND, int EPI, int NSTAGE>
+__global__ __launch_bounds__(kThreads, 2) void gg_bf16_kernel(Bf16Params p)
 {
+    constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     GroupTable tab;
     tab.G = p.G;
@@ -480,23 +483,37 @@ __global__ __launch_bounds__(kThreads) void gg_bf16_kernel(Bf16Params p)
                 }
         };
 
+        // Schedule per k-step kt (two 16-deep MFMA steps per stage):
+        //   read step-1 fragments of kt | MFMA step 0 of kt
+        //   wait for stage kt+1, barrier (kt fully read by every wave)
+        //   load stage kt+NSTAGE into kt's slot
+        //   read step-0 fragments of kt+1 | MFMA step 1 of kt
+        // so LDS reads overlap MFMAs and NSTAGE-1 stages stay in flight.
+        static_assert(BK == 32, "two k-steps per stage");
 #pragma unroll
-        for (int s = 0; s < NSTAGE - 1; ++s)
-            if (s < nk) issue_stage<KIND>(smem, da, db, s, nfull, Kred, wave);
-
-        for (int kt = 0; kt < nk; ++kt) {
-            wait_stage(min(NSTAGE - 2, nk - 1 - kt));    // stage kt landed (own loads)
-            barrier();                                   // ... everyone's; slot of kt-1 free
-            if (kt + NSTAGE - 1 < nk) issue_stage<KIND>(smem, da, db, kt + NSTAGE - 1, nfull, Kred, wave);
-            static_assert(BK == 32, "two k-steps per stage");
-            const uint32_t so = lds0 + (uint32_t)(kt % NSTAGE) * STAGE_BYTES;
-            bf16x8 a0[2], b0[4], a1[2], b1[4];
-            load_frags<KIND, 0>(so, aK, aN, bK, bN, a0, b0);
+        for (int s = 0; s < NSTAGE; ++s)
+            if (s < nk) issue_stage<KIND, NSTAGE>(smem, da, db, s, nfull, Kred, wave);
+        bf16x8 a0[2], b0[4], a1[2], b1[4];
+        if (nk > 0) {
+            wait_stage<NSTAGE>(min(NSTAGE - 1, nk - 1));
+            barrier();
+            load_frags<KIND, 0>(lds0, aK, aN, bK, bN, a0, b0);
             frag_wait(a0, b0);
-            load_frags<KIND, 1>(so, aK, aN, bK, bN, a1, b1);   // in flight during step 0
+        }
+        int slot = 0;
+        for (int kt = 0; kt < nk; ++kt) {
+            const uint32_t so = lds0 + (uint32_t)slot * STAGE_BYTES;
+            load_frags<KIND, 1>(so, aK, aN, bK, bN, a1, b1);
             mma(a0, b0);
+            const int nslot_ = slot + 1 == NSTAGE ? 0 : slot + 1;
+            if (kt + 1 < nk) wait_stage<NSTAGE>(min(NSTAGE - 2, nk - 2 - kt));
             frag_wait(a1, b1);
+            barrier();
+            if (kt + NSTAGE < nk) issue_stage<KIND, NSTAGE>(smem, da, db, kt + NSTAGE, nfull, Kred, wave);
+            if (kt + 1 < nk) load_frags<KIND, 0>(lds0 + (uint32_t)nslot_ * STAGE_BYTES, aK, aN, bK, bN, a0, b0);
             mma(a1, b1);
+            if (kt + 1 < nk) frag_wait(a0, b0);
+            slot = nslot_;
         }
         wait_lgkm0();
         barrier();                                       // LDS free for the next tile
@@ -526,11 +543,23 @@ __global__ __launch_bounds__(kThreads) void gg_bf16_kernel(Bf16Params p)
     }
 }
 
-template <int KIND, int EPI>
+// Ring depth: a tuning knob (3..5 stages of 24 KiB); PTGG_NSTAGE overrides
+// the default for experiments.  Results do not depend on it.
+int ring_depth()
+{
+    static int depth = [] {
+        const char *e = getenv("PTGG_NSTAGE");
+        int d = e ? atoi(e) : 3;
+        return (d >= 3 && d <= 5) ? d : 3;
+    }();
+    return depth;
+}
+
+template <int KIND, int EPI, int NSTAGE>
 hipError_t launch_one(const Bf16Params &p, hipStream_t s)
 {
-    const int lds = GEMM_LDS_BYTES + table_bytes(p.G);
-    auto kern = gg_bf16_kernel<KIND, EPI>;
+    const int lds = NSTAGE * STAGE_BYTES + table_bytes(p.G);
+    auto kern = gg_bf16_kernel<KIND, EPI, NSTAGE>;
     static int configured_lds = 0;
     if (configured_lds < lds) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -554,6 +583,16 @@ hipError_t launch_one(const Bf16Params &p, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int KIND, int EPI>
+hipError_t launch_depth(const Bf16Params &p, hipStream_t s)
+{
+    switch (ring_depth()) {
+    case 4: return launch_one<KIND, EPI, 4>(p, s);
+    case 5: return launch_one<KIND, EPI, 5>(p, s);
+    default: return launch_one<KIND, EPI, 3>(p, s);
+    }
+}
+
 }  // namespace
 
 int bf16_tile_m() { return BM; }
@@ -561,15 +600,15 @@ int bf16_tile_n() { return BN; }
 
 hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s)
 {
-    if (kind == kWgrad) return launch_one<kWgrad, kEpiNone>(p, s);
+    if (kind == kWgrad) return launch_depth<kWgrad, kEpiNone>(p, s);
     if (kind == kFwdKContig) {
-        if (epi == kEpiSwiglu) return launch_one<kFwdKContig, kEpiSwiglu>(p, s);
-        if (epi == kEpiSwigluMxfp4) return launch_one<kFwdKContig, kEpiSwigluMxfp4>(p, s);
-        return launch_one<kFwdKContig, kEpiNone>(p, s);
+        if (epi == kEpiSwiglu) return launch_depth<kFwdKContig, kEpiSwiglu>(p, s);
+        if (epi == kEpiSwigluMxfp4) return launch_depth<kFwdKContig, kEpiSwigluMxfp4>(p, s);
+        return launch_depth<kFwdKContig, kEpiNone>(p, s);
     }
-    if (epi == kEpiSwiglu) return launch_one<kFwdNContig, kEpiSwiglu>(p, s);
-    if (epi == kEpiSwigluMxfp4) return launch_one<kFwdNContig, kEpiSwigluMxfp4>(p, s);
-    return launch_one<kFwdNContig, kEpiNone>(p, s);
+    if (epi == kEpiSwiglu) return launch_depth<kFwdNContig, kEpiSwiglu>(p, s);
+    if (epi == kEpiSwigluMxfp4) return launch_depth<kFwdNContig, kEpiSwigluMxfp4>(p, s);
+    return launch_depth<kFwdNContig, kEpiNone>(p, s);
 }
 
 }  // namespace ptgg
