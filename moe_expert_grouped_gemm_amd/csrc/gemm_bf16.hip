@@ -465,13 +465,31 @@ __global__ __launch_bounds__(kThreads, 2) void gg_bf16_kernel(Bf16Params p)
             }
         }
 
+        // Accumulators start at zero, or for an accumulating wgrad at the
+        // main_grad tile itself: its loads go out before the operand
+        // prologue and overlap it, and the tile ends with plain stores.
         floatx16 acc[2][4];
+        if (KIND == kWgrad && p.accumulate) {
+            const float *og = (const float *)p.out + (int64_t)g * p.o_gstride;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int bj = 0; bj < 4; ++bj) {
+                    const int n = nt * BN + wn * 128 + bj * 32 + (lane & 31);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = m0 + e_row(wm, bi, r);
+                        acc[bi][bj][r] = (n < p.Nout && i < p.Mout) ? og[(int64_t)i * p.ldo + n] : 0.0f;
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        }
 
         auto mma = [&](const bf16x8 (&af)[2], const bf16x8 (&bfr)[4]) {
 #pragma unroll
@@ -519,6 +537,11 @@ __global__ __launch_bounds__(kThreads, 2) void gg_bf16_kernel(Bf16Params p)
         barrier();                                       // LDS free for the next tile
 
         if (KIND == kWgrad) {
+            // Nothing is outstanding here; saying so explicitly keeps the
+            // compiler from waiting for every earlier store before each one
+            // (vmcnt counts stores too) when it cannot prove the seeded
+            // accumulators have arrived.
+            wait_vmcnt<0>();
             float *og = (float *)p.out + (int64_t)g * p.o_gstride;
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
@@ -529,12 +552,7 @@ __global__ __launch_bounds__(kThreads, 2) void gg_bf16_kernel(Bf16Params p)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int i = m0 + e_row(wm, bi, r);
-                        if (i < p.Mout) {
-                            float *dst = og + (int64_t)i * p.ldo + n;
-                            float v = acc[bi][bj][r];
-                            if (p.accumulate) v = *dst + v;
-                            *dst = v;
-                        }
+                        if (i < p.Mout) og[(int64_t)i * p.ldo + n] = acc[bi][bj][r];
                     }
                 }
         } else {
