@@ -38,6 +38,10 @@
  *                      fp4 support, skip cache trans weight and santize
  *                      code", section "Changes") + one E8M0 scale per 32.
  *    For MX operands the scales form a row-major [rows, K/32] byte matrix.
+ *  - Size limits: the kernels address operands with 32-bit byte offsets, so
+ *    each of A (or dY), one expert's weight matrix, and the whole scale
+ *    tensors must stay below 2 GiB; larger problems get PT_ERR_UNSUPPORTED
+ *    (split them along M or N).
  *  - Accumulation is in fp32 on the matrix cores; outputs are rounded once
  *    (bf16 round-to-nearest-even, or fp32 for main_grad).
  *  - Return value: a pt_status.  On any error nothing is launched.
@@ -103,7 +107,8 @@ typedef enum {
  *  out        see pt_epilogue; rows outside every expert are not written
  *  out_scale  [M, N/64] E8M0 for PT_EPI_SWIGLU_MXFP4, else NULL
  *  Requirements: K % 8 == 0 (bf16) or K % 32 == 0 (MX); N % 8 == 0 (bf16,
- *  trans_b = 0); N even for SWIGLU, N % 128 == 0 for SWIGLU_MXFP4.
+ *  trans_b = 0); N % 16 == 0 for SWIGLU, N % 64 == 0 for SWIGLU_MXFP4;
+ *  a_scale and b_scale 4-byte aligned (else PT_ERR_MISALIGNED).
  *  workspace  optional (may be NULL); if given and >= 4 bytes its first
  *             32-bit word receives the sticky device error bits.
  */

@@ -44,6 +44,11 @@ bool device_is_gfx950()
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+// The kernels address each operand with 32-bit byte offsets (buffer
+// resources whose out-of-range offsets start at 2^31).
+bool fits31(int64_t bytes) { return bytes < ((int64_t)1 << 31); }
 
 int check_groups(const int64_t *lens, int64_t G, int64_t M)
 {
@@ -89,6 +94,7 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
         if (a_scale || b_scale) return PT_ERR_INVALID_ARG;
         if (K % 8) return PT_ERR_UNSUPPORTED;
         if (!trans_b && N % 8) return PT_ERR_UNSUPPORTED;
+        if (!fits31(M * K * 2) || !fits31(N * K * 2)) return PT_ERR_UNSUPPORTED;
         Bf16Params p = {};
         p.a = (const uint16_t *)a;
         p.b = (const uint16_t *)b;
@@ -114,6 +120,9 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
         if (!trans_b) return PT_ERR_UNSUPPORTED;           // scales run along K
         if (K % 32) return PT_ERR_UNSUPPORTED;
         if (M > 0 && (!a_scale || !b_scale)) return PT_ERR_INVALID_ARG;
+        if (!aligned4(a_scale) || !aligned4(b_scale)) return PT_ERR_MISALIGNED;
+        const int64_t kb = dtype == PT_MXFP8_E4M3 ? K : K / 2;      // code bytes per row
+        if (!fits31(M * kb) || !fits31(N * kb) || !fits31(G * N * (K / 32) + 4)) return PT_ERR_UNSUPPORTED;
         MxParams p = {};
         p.a = (const uint8_t *)a;
         p.as = a_scale;
@@ -149,6 +158,7 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
     if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
     if (dy_scale || b_scale) return PT_ERR_INVALID_ARG;
     if (N % 8 || K % 8) return PT_ERR_UNSUPPORTED;
+    if (!fits31(M * N * 2) || !fits31(N * K * 2)) return PT_ERR_UNSUPPORTED;
     if (!aligned16(dy) || !aligned16(b) || !aligned16(dx)) return PT_ERR_MISALIGNED;
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
     // dX[r, k] = sum_n dY[r, n] B[k, n]: reduction over n, output columns k.
@@ -186,6 +196,7 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
     if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
     if (a_scale || dy_scale) return PT_ERR_INVALID_ARG;
     if (N % 8 || K % 8) return PT_ERR_UNSUPPORTED;
+    if (!fits31(M * K * 2) || !fits31(M * N * 2)) return PT_ERR_UNSUPPORTED;
     if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad)) return PT_ERR_MISALIGNED;
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
     Bf16Params p = {};

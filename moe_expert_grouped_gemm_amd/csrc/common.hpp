@@ -159,7 +159,7 @@ struct TilesWgrad {        // wgrad: the whole output of active experts
 };
 
 template <class Tiles>
-__device__ int build_group_table(GroupTable &t, const int64_t *lens, const int64_t *offs,
+__device__ __forceinline__ int build_group_table(GroupTable &t, const int64_t *lens, const int64_t *offs,
                                  int G, int64_t M, Tiles tiles, uint32_t *err, int *s_scratch)
 {
     const int tid = threadIdx.x;

@@ -32,33 +32,13 @@
 //                    into the fp32 main_grad once per element.
 #include <stdlib.h>
 
-#include "common.hpp"
-#include "epilogue.hpp"
-#include "launch.hpp"
+#include "pipeline.hpp"
 
 namespace ptgg {
 
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 32;
-constexpr int A_BYTES = BM * BK * 2;               // 8 KiB per stage
-constexpr int B_BYTES = BN * BK * 2;               // 16 KiB per stage
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int A_LOADS = A_BYTES / 16 / kThreads;   // 16-byte loads per thread per stage
-constexpr int B_LOADS = B_BYTES / 16 / kThreads;
-constexpr int LOADS = A_LOADS + B_LOADS;
-constexpr uint32_t kRsrcWord3 = 0x00020000u;       // raw buffer, 32-bit data format
-constexpr uint32_t kOOB = 0x80000000u;             // offset past every record bound
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Wait until at most N of this wave's vector-memory operations are pending.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
+constexpr int BK = ROW_BYTES / 2;                  // bf16 reduction depth of a stage
 
 // Wait for the oldest in-flight stage when `after` younger stages (of LOADS
 // loads per thread each; at most NSTAGE - 1) may stay outstanding.
@@ -75,29 +55,11 @@ __device__ __forceinline__ void wait_stage(int after)
     default: wait_vmcnt<0>(); break;
     }
 }
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// Workgroup barrier without the memory fence of __syncthreads() (which would
-// wait for every outstanding load, draining the ring); the empty asm keeps
-// the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
-}
 
 template <int OFF>
 __device__ __forceinline__ bf16x8 ldsr_b128(uint32_t addr)
 {
-    bf16x8 v;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-    return v;
+    return __builtin_bit_cast(bf16x8, ldsr_u128<OFF>(addr));
 }
 template <int OFF>
 __device__ __forceinline__ uintx2 ldsr_tr(uint32_t addr)
@@ -118,149 +80,13 @@ __device__ __forceinline__ void frag_wait(bf16x8 (&a)[2], bf16x8 (&b)[4])
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, (int)kRsrcWord3);
-}
-
-// One 16-byte direct load per lane into LDS (lane i lands at lds + 16 i) from
-// byte voff + soff of a buffer of `bytes` bytes at `base`; offsets at or past
-// the bound read zeros.  Kept a plain function: the buffer-resource type is
-// device-only, and inside templates clang's host pass would silently discard
-// every kernel that reaches it.
-__device__ __forceinline__ void dma16(const void *base, uint32_t bytes, uint8_t *lds, uint32_t voff, uint32_t soff)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (lds_void *)lds, 16, voff, soff, 0, 0);
-}
-
-// One operand's direct-load state for a tile: NL 16-byte loads per thread
-// per stage at voff[i] + kt * kstep (bytes) inside the buffer `rsrc`.
-template <int NL>
-struct Dma {
-    const void *base;
-    uint32_t bytes;
-    uint32_t voff[NL];
-    uint32_t kstep;
-};
-
-// Issue one stage of an operand: slot i of this thread lands at LDS byte
-// lds_off + (i * 256 + thread) * 16.
-template <int NL>
-__device__ __forceinline__ void issue(uint8_t *smem, const Dma<NL> &d, uint32_t lds_off, uint32_t soff,
-                                      const uint32_t (&voff)[NL], int wave)
-{
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-        dma16(d.base, d.bytes, smem + lds_off + (i * kThreads + wave * kWave) * 16, voff[i], soff);
-}
-
-// ---- slot geometry.  Reduction-contiguous operand with R rows: LDS [R][32]
-// bf16 (64-byte rows of four 16-byte chunks), chunk c of row r at position
-// c ^ ((r >> 2) & 3).  Column-contiguous operand with R columns: LDS [32][R]
-// (rows of R*2 bytes), chunk c of row k at position c ^ ((k & 3) << 2).
-__device__ __forceinline__ int kpos(int r, int c) { return c ^ ((r >> 2) & 3); }
+// Column-contiguous operand with R columns in one stage: LDS [32][R] (rows of
+// R*2 bytes), chunk c of k-row k at position c ^ ((k & 3) << 2), read with the
+// transposing ds_read_b64_tr_b16.
 __device__ __forceinline__ int npos(int k, int c) { return c ^ ((k & 3) << 2); }
-
-// slot s of a reduction-contiguous stage: tile row and source chunk
-__device__ __forceinline__ void kslot(int s, int &r, int &c) { r = s >> 2; c = kpos(r, s & 3); }
 // slot s of a column-contiguous stage with R columns: k row and source chunk
 template <int R>
 __device__ __forceinline__ void nslot(int s, int &k, int &c) { k = s / (R / 8); c = npos(k, s % (R / 8)); }
-
-// Tile column c (0..255) -> logical output column.  With SwiGLU a tile covers
-// 128 consecutive outputs j: within each wave's 128 columns, blocks 0-1 are
-// gate columns j and blocks 2-3 the matching up columns I + j.
-template <int EPI>
-__device__ __forceinline__ int col_of(int nt, int c, int Nout)
-{
-    if (EPI == kEpiNone) return nt * BN + c;
-    const int I = Nout >> 1;
-    const int w = c >> 7, cc = c & 127;
-    const int j = nt * (BN / 2) + w * 64 + (cc & 63);
-    return cc >= 64 ? I + j : j;
-}
-
-// Clamp an 8-column chunk start into the valid range of its half.
-template <int EPI>
-__device__ __forceinline__ int clamp8(int n, int Nout)
-{
-    if (EPI == kEpiNone) return min(n, Nout - 8);
-    const int I = Nout >> 1;
-    return n < I ? min(n, I - 8) : min(n, Nout - 8);
-}
-
-// ------------------------------------------------------------------ epilogue
-// Wave (wm, wn) holds rows wm*64 + bi*32 + .., columns wn*128 + bj*32 + lane%32.
-__device__ __forceinline__ int e_row(int wm, int bi, int reg)
-{
-    return wm * 64 + bi * 32 + (reg >> 2) * 8 + ((threadIdx.x & 63) >> 5) * 4 + (reg & 3);
-}
-
-template <int EPI>
-__device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], const Bf16Params &p, int64_t row0,
-                                          int m0, int rows, int nt, int wm, int wn)
-{
-    const int lane = threadIdx.x & 63;
-    if (EPI == kEpiNone) {
-        uint16_t *o = (uint16_t *)p.out + row0 * p.ldo;
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < 4; ++bj) {
-                const int n = nt * BN + wn * 128 + bj * 32 + (lane & 31);
-                if (n >= p.Nout) continue;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + e_row(wm, bi, r);
-                    if (m < rows) o[(int64_t)m * p.ldo + n] = (uint16_t)bf16_rne(acc[bi][bj][r]);
-                }
-            }
-    } else if (EPI == kEpiSwiglu) {
-        uint16_t *o = (uint16_t *)p.out + row0 * p.ldo;
-        const int I = p.Nout >> 1;
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj) {
-            const int j = nt * (BN / 2) + wn * 64 + bj * 32 + (lane & 31);
-            if (j >= I) continue;
-#pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + e_row(wm, bi, r);
-                    if (m < rows)
-                        o[(int64_t)m * p.ldo + j] = (uint16_t)bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r]));
-                }
-        }
-    } else {
-        // SwiGLU value rounded to bf16, then one MXFP4 block per 32 outputs:
-        // the 32 lanes of a half-wave hold 32 consecutive j of one row.
-        uint8_t *o = (uint8_t *)p.out + row0 * p.ldo;
-        uint8_t *os = p.out_scale + row0 * (p.Nout / 64);
-        const int I = p.Nout >> 1;
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj) {
-            const int j = nt * (BN / 2) + wn * 64 + bj * 32 + (lane & 31);
-            const bool jvalid = j < I;          // uniform over a half-wave (I % 32 == 0)
-#pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + e_row(wm, bi, r);
-                    const uint32_t hb = bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r]));
-                    uint32_t amax = hb & 0x7FFFu;
-#pragma unroll
-                    for (int d = 1; d < 32; d <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, d, 64));
-                    const uint32_t E = mx_scale_byte<2>(amax);
-                    const uint32_t code = mx_encode<1>(hb, E);
-                    const uint32_t nb = (uint32_t)__shfl_xor((int)code, 1, 64);
-                    if (jvalid && m < rows) {
-                        if ((lane & 1) == 0) o[(int64_t)m * p.ldo + (j >> 1)] = (uint8_t)(code | (nb << 4));
-                        if ((lane & 31) == 0) os[(int64_t)m * (p.Nout / 64) + (j >> 5)] = (uint8_t)E;
-                    }
-                }
-        }
-    }
-}
 
 // Issue stage kt of both operands into ring slot kt % NSTAGE.  Full k-steps
 // advance the scalar offset; the partial last step bounds every lane.
@@ -556,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 2) void gg_bf16_kernel(Bf16Params p)
                     }
                 }
         } else {
-            store_out<EPI>(acc, p, row0, m0, rows, nt, wm, wn);
+            store_out<EPI>(acc, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wm, wn);
         }
     }
 }
@@ -593,10 +419,7 @@ hipError_t launch_one(const Bf16Params &p, hipStream_t s)
         tiles_max = (int64_t)p.G * p.tilesM * p.tilesN;
     else
         tiles_max = (p.M / BM + p.G) * (int64_t)p.tilesN;
-    int64_t grid = (int64_t)device_cus() * occ;
-    if (tiles_max < grid) grid = tiles_max;
-    if (grid >= 8) grid = grid / 8 * 8;
-    if (grid < 1) grid = 1;
+    const int64_t grid = persistent_grid(occ, tiles_max);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, p);
     return hipGetLastError();
 }

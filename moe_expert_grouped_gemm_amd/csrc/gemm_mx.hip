@@ -1,159 +1,200 @@
 // gemm_mx.hip -- OCP-MX grouped GEMM forward for gfx950 (MXFP8 E4M3 and
 // MXFP4 E2M1 operands, one E8M0 scale per 32 values along K).
 //
-// Same persistent ragged-batch schedule as the BF16 kernel.  Both operands are
-// K-contiguous (activations [M, K], weights [G, N, K], the [experts, out, in]
-// layout).  Each 128-byte slice of a row per k-step (128 E4M3 or 256 E2M1
-// values) is staged through double-buffered LDS together with its 4 or 8
-// scale bytes, and fed to v_mfma_scale_f32_32x32x64_f8f6f4: lane l supplies
-// row (l & 31) with the 32 values of one scale block and that block's E8M0
-// byte, so the block scales are applied inside the matrix core and the fp32
-// accumulator receives exactly-scaled products.
-#include "common.hpp"
-#include "epilogue.hpp"
-#include "launch.hpp"
+// Same persistent ragged-batch schedule, tile shape and LDS ring as the BF16
+// kernel: both operands are K-contiguous (activations [M, K], weights
+// [G, N, K], the [experts, out, in] layout), and every stage of the ring holds
+// 64 code bytes of each of the tile's 128 A rows and 256 B rows (64 E4M3 or
+// 128 E2M1 values), filled by direct buffer->LDS loads.  The products run on
+// v_mfma_scale_f32_32x32x64_f8f6f4, which applies one E8M0 byte per lane to
+// the 32 values of a block inside the matrix core, so the fp32 accumulator
+// receives exactly scaled products.
+//
+// A stage's fragments are the same LDS bytes for both element widths: lane l
+// of a wave reads the 16-byte chunks h and 2 + h (h = l >> 5) of its row.
+//  - E2M1: each chunk is one 32-value block, and one MFMA per chunk consumes
+//    it (two MFMA steps of 64 values per stage); lane half h supplies the
+//    scale of block 2s + h of step s.
+//  - E4M3: one MFMA consumes the whole stage.  Bytes 0-15 of every lane take
+//    the scale supplied by lane half 0 and bytes 16-31 the one supplied by
+//    lane half 1 (measured on gfx950), so lane half h holds values
+//    16h..16h+15 of block 0 (chunk h) in bytes 0-15 and the same values of
+//    block 1 (chunk 2 + h) in bytes 16-31, and supplies block h's scale.
+//
+// Scale bytes bypass LDS: every lane loads the bytes of its own rows for a
+// stage into registers when the stage's operand loads are issued, three
+// stages ahead, so the k-loop is unrolled by the ring depth to keep each
+// slot's registers and LDS offsets static.  Stages past the end are still
+// issued, with offsets past every bound (zeros, no memory traffic), so that
+// every wait in the loop has the same count.
+#include "pipeline.hpp"
 
 namespace ptgg {
 
 namespace {
 
-constexpr int BM = kTileM, BN = kTileN;
-constexpr int BKB = 128;                       // code bytes per row per k-step
-constexpr int LDS_STRIDE = BKB + 16;           // 144 B rows (conflict-free 16-B reads)
-constexpr int SC_STRIDE = 8;                   // scale bytes per row per k-step (<= 8 blocks)
-constexpr int TILE_A = BM * LDS_STRIDE;
-constexpr int TILE_B = BN * LDS_STRIDE;
-constexpr int TILE_AS = BM * SC_STRIDE;
-constexpr int TILE_BS = BN * SC_STRIDE;
-constexpr int STAGE = TILE_A + TILE_B + TILE_AS + TILE_BS;
-constexpr int GEMM_LDS_BYTES = 2 * STAGE;
+constexpr int NSTAGE = 3;
+typedef unsigned int uintx8 __attribute__((ext_vector_type(8)));
 
-// FMT 0: E4M3 (one byte per value, 128 values per k-step, 4 scale blocks)
-// FMT 1: E2M1 (two values per byte, 256 values per k-step, 8 scale blocks)
-template <int FMT>
-struct Fmt {
-    static constexpr int vals_per_byte = FMT == 0 ? 1 : 2;
-    static constexpr int blocks = BKB * vals_per_byte / 32;   // scale blocks per k-step
-    static constexpr int mfma_fmt = FMT == 0 ? 0 : 4;         // cbsz/blgp operand format
-    static constexpr int bytes_per_lane = 32 / vals_per_byte; // one scale block
+// How a lane fetches its scale bytes for one stage.  Every load is one
+// aligned 32-bit word; the bytes are extracted where they are used.  (Byte or
+// 16-bit loads would leave narrow values in the loop-carried registers, and
+// the masking copies the compiler then adds at the loop back-edge each wait
+// for their load.)
+enum ScaleMode {
+    kScE4M3 = 0,      // the word holding byte 2*kt + h of the row
+    kScE2M1Word = 1,  // K % 128 == 0: the word of bytes 4*kt .. 4*kt + 3
+    kScE2M1Span = 2,  // any K: lane half h loads aligned word h of the two
+                      // that cover bytes 4*kt .. 4*kt + 3; the halves swap
+                      // words and realign them
+};
+template <int SCM>
+struct Sc {
+    static constexpr int regs = 6;                    // 2 A rows + 4 B rows per lane
+    static constexpr int per_stage = LOADS + regs;    // vector-memory ops per stage
 };
 
-struct Stage {
-    uintx4 a[4], b[4];
-    uintx2 sc;          // this thread's row of scale bytes (A rows, then B rows)
+template <int V>
+struct IC { static constexpr int value = V; };
+
+__device__ __forceinline__ uint32_t ld_u32(const void *base, uint32_t bytes, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(base, bytes), voff, soff, 0);
+}
+
+// Scale rows of this lane for a tile: A rows bi = 0, 1 and B rows bj = 0..3,
+// as byte offsets from the start of the scale tensors (both 4-byte aligned);
+// the record bounds are the tensors' sizes rounded up to whole words, so an
+// aligned word never reaches past the page of the tensor's last byte.
+struct ScRows {
+    const uint8_t *a;
+    const uint8_t *b;
+    uint32_t abytes, bbytes;
+    uint32_t row[6];
 };
 
-template <int FMT>
-__device__ __forceinline__ void load_stage(Stage &st, const uint8_t *Ab, const uint8_t *Asb,
-                                           const uint8_t *Bb, const uint8_t *Bsb, int m0, int rows,
-                                           int n0, int N, int Kb, int KS, int kt)
+// E4M3: byte of the row that lane half h needs for stage kt.  The partial
+// last stage (kt == nfull) holds block 0 only, and block 1's lanes take its
+// byte: a finite scale for codes that are all zero.
+__device__ __forceinline__ uint32_t e4m3_byte(int kt, int nfull, int h)
 {
-    using F = Fmt<FMT>;
-    const int kb0 = kt * BKB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = threadIdx.x + i * kThreads;
-        const int r = c >> 3, kc = c & 7;
-        const int k = kb0 + kc * 16;
-        const bool kv = k < Kb;
-        const int ar = min(m0 + r, rows - 1);
-        const int br = min(n0 + r, N - 1);
-        st.a[i] = kv ? *(const uintx4 *)(Ab + (int64_t)ar * Kb + k) : uintx4{0u, 0u, 0u, 0u};
-        st.b[i] = kv ? *(const uintx4 *)(Bb + (int64_t)br * Kb + k) : uintx4{0u, 0u, 0u, 0u};
-    }
-    // scales: thread t < 128 loads A row t, t >= 128 loads B row t - 128
-    const int t = threadIdx.x;
-    const uint8_t *srow = t < BM ? Asb + (int64_t)min(m0 + t, rows - 1) * KS
-                                 : Bsb + (int64_t)min(n0 + t - BM, N - 1) * KS;
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int j = 0; j < F::blocks; ++j) {
-        const int blk = kt * F::blocks + j;
-        const uint32_t v = blk < KS ? (uint32_t)srow[blk] : 0u;
-        w[j >> 2] |= v << (8 * (j & 3));
-    }
-    st.sc = uintx2{w[0], w[1]};
+    return 2u * kt + ((kt == nfull) ? 0u : (uint32_t)h);
 }
 
-__device__ __forceinline__ void store_stage(const Stage &st, uint8_t *s)
+// Load this lane's scale words of stage kt (a dummy stage past the end reads
+// zeros without touching memory).
+template <int SCM>
+__device__ __forceinline__ void load_scales(uint32_t (&sc)[6], const ScRows &sr, int kt, int nk, int nfull, int h)
 {
+    const uint32_t soff = kt >= nk ? kOOB : 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = threadIdx.x + i * kThreads;
-        const int r = c >> 3, kc = c & 7;
-        *(uintx4 *)(s + r * LDS_STRIDE + kc * 16) = st.a[i];
-        *(uintx4 *)(s + TILE_A + r * LDS_STRIDE + kc * 16) = st.b[i];
+    for (int i = 0; i < 6; ++i) {
+        const uint8_t *base = i < 2 ? sr.a : sr.b;
+        const uint32_t bytes = i < 2 ? sr.abytes : sr.bbytes;
+        uint32_t a;
+        if constexpr (SCM == kScE4M3) a = (sr.row[i] + e4m3_byte(kt, nfull, h)) & ~3u;
+        else if constexpr (SCM == kScE2M1Word) a = sr.row[i] + 4u * kt;
+        else a = ((sr.row[i] + 4u * kt) & ~3u) + 4u * h;
+        sc[i] = ld_u32(base, bytes, a, soff);
     }
-    *(uintx2 *)(s + TILE_A + TILE_B + threadIdx.x * SC_STRIDE) = st.sc;
 }
 
-// One k-step of 2 x 2 blocks of 32 x 32 per wave.  MFMA step s covers the 64
-// values of scale blocks 2s and 2s+1 of the k-step; lane half h = l >> 5
-// supplies the E8M0 byte of block 2s + h.  Which operand bytes that scale
-// multiplies depends on the element width (measured on gfx950):
-//  - E2M1: the lane's 16 bytes (32 values) all belong to the lane's own
-//    scale, so lane half h holds block 2s + h whole;
-//  - E4M3: bytes 0-15 of BOTH lane halves take half 0's scale and bytes
-//    16-31 take half 1's, so lane half h holds values 16h..16h+15 of block
-//    2s in bytes 0-15 and values 16h..16h+15 of block 2s+1 in bytes 16-31.
-template <int FMT>
-__device__ __forceinline__ void mma_stage(floatx16 (&acc)[2][2], const uint8_t *s, int wm, int wn,
-                                          int nvalid_bi)
+// Per-stage scale words: E4M3 the lane's byte at bits 0-7; E2M1 the row's
+// four bytes of the stage in order, those of missing blocks in a partial
+// last stage cleared (a finite scale for codes that are all zero).
+template <int SCM>
+__device__ __forceinline__ void scale_words(const uint32_t (&sc)[6], uint32_t (&w)[6], const ScRows &sr, int kt,
+                                            int nfull, int nb_last, int h)
 {
-    using F = Fmt<FMT>;
-    const int lane = threadIdx.x & 63;
-    const int r = lane & 31, h = lane >> 5;
-    const uint8_t *sA = s, *sB = s + TILE_A;
-    const uint8_t *sAs = s + TILE_A + TILE_B, *sBs = sAs + TILE_AS;
-    uintx2 ascale[2], bscale[2];
+    const uint32_t keep = (kt == nfull) ? (1u << (8 * nb_last)) - 1u : 0xFFFFFFFFu;
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) ascale[bi] = *(const uintx2 *)(sAs + (wm * 64 + bi * 32 + r) * SC_STRIDE);
-#pragma unroll
-    for (int bj = 0; bj < 2; ++bj) bscale[bj] = *(const uintx2 *)(sBs + (wn * 64 + bj * 32 + r) * SC_STRIDE);
-#pragma unroll
-    for (int st = 0; st < F::blocks / 2; ++st) {
-        const int blk = 2 * st + h;                 // scale block of this lane
-        // byte offsets (in the row's k-step slice) of the lane's two 16-byte halves
-        const int off_lo = FMT == 0 ? 64 * st + 16 * h : 16 * blk;
-        const int off_hi = 64 * st + 32 + 16 * h;  // E4M3 only
-        intx8 af[2], bf[2];
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
-            const uint8_t *p = sA + (wm * 64 + bi * 32 + r) * LDS_STRIDE;
-            intx4 lo = *(const intx4 *)(p + off_lo);
-            intx4 hi = FMT == 0 ? *(const intx4 *)(p + off_hi) : intx4{0, 0, 0, 0};
-            af[bi] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj) {
-            const uint8_t *p = sB + (wn * 64 + bj * 32 + r) * LDS_STRIDE;
-            intx4 lo = *(const intx4 *)(p + off_lo);
-            intx4 hi = FMT == 0 ? *(const intx4 *)(p + off_hi) : intx4{0, 0, 0, 0};
-            bf[bj] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        int as[2], bs[2];
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi) as[bi] = (int)((ascale[bi][blk >> 2] >> (8 * (blk & 3))) & 0xFFu);
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj) bs[bj] = (int)((bscale[bj][blk >> 2] >> (8 * (blk & 3))) & 0xFFu);
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
-            if (bi < nvalid_bi) {
-#pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[bi], bf[bj], acc[bi][bj], F::mfma_fmt, F::mfma_fmt, 0, as[bi], 0, bs[bj]);
-            }
+    for (int i = 0; i < 6; ++i) {
+        if constexpr (SCM == kScE4M3) {
+            w[i] = __builtin_amdgcn_ubfe(sc[i], ((sr.row[i] + e4m3_byte(kt, nfull, h)) & 3u) * 8u, 8u);
+        } else if constexpr (SCM == kScE2M1Word) {
+            w[i] = sc[i];
+        } else {
+            const auto r = __builtin_amdgcn_permlane32_swap(sc[i], sc[i], false, false);
+            w[i] = __builtin_amdgcn_alignbyte(r[1], r[0], (sr.row[i] + 4u * kt) & 3u) & keep;
         }
     }
 }
 
-template <int FMT, int EPI>
-__global__ __launch_bounds__(kThreads) void gg_mx_kernel(MxParams p)
+// Scale operand of row slot i (A rows 0-1, B rows 2-5) for MFMA step s.
+template <int SCM>
+__device__ __forceinline__ int scale_of(const uint32_t (&w)[6], int i, int s, uint32_t sh)
 {
-    using F = Fmt<FMT>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    uint8_t *stage0 = (uint8_t *)smem;
+    if constexpr (SCM == kScE4M3) return (int)w[i];
+    else return (int)__builtin_amdgcn_ubfe(w[i], sh + 16u * s, 8u);
+}
+
+// Direct-load state of one tile.  Slot i * 256 + t of a stage (thread t,
+// load i) holds chunk c = (t & 3) ^ ((t >> 4) & 3) of tile row i * 64 + t / 4,
+// so a thread's loads share one chunk and one 32-bit offset per operand; the
+// rows of loads 1.. sit at wave-uniform distances from load 0's, passed as
+// scalar offsets.
+struct Ops {
+    const uint8_t *a;
+    const uint8_t *b;
+    uint32_t abytes, bbytes;
+    uint32_t avoff, bvoff;          // load 0 of this thread, chunk included
+    uint32_t adelta;                // A rows of load 1: + 64 rows
+    uint32_t bdelta[B_LOADS];       // B rows of loads 0..3
+    uint32_t chunk;                 // byte offset of the chunk inside a stage row
+};
+
+// Issue the operand loads of stage kt into LDS byte offset st.  Branch-free,
+// so that every path issues the same loads and the compiler's own waits for
+// the scale registers see the true number of loads in flight: in a partial
+// last stage a thread whose chunk lies at or past the row length, and every
+// thread of a stage past the end, gets an offset past the bound.
+__device__ __forceinline__ void issue_stage(uint8_t *smem, const Ops &o, uint32_t st, int kt, int nk, int Kb,
+                                            int wave)
+{
+    const int k0 = kt * ROW_BYTES;
+    const int room = kt < nk ? Kb - k0 : 0;              // bytes left in each row from k0
+    const bool ok = (int)o.chunk < room;
+    const uint32_t va = ok ? o.avoff + k0 : kOOB, vb = ok ? o.bvoff + k0 : kOOB;
+    uint8_t *lds = smem + st + wave * kWave * 16;
+    dma16(o.a, o.abytes, lds, va, 0u);
+    dma16(o.a, o.abytes, lds + kThreads * 16, va, o.adelta);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) dma16(o.b, o.bbytes, lds + A_BYTES + i * kThreads * 16, vb, o.bdelta[i]);
+}
+
+__device__ __forceinline__ intx8 cat8(uintx4 lo, uintx4 hi)
+{
+    return __builtin_bit_cast(intx8, uintx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+__device__ __forceinline__ intx8 pad8(uintx4 lo) { return cat8(lo, uintx4{0u, 0u, 0u, 0u}); }
+
+// Wait for all issued LDS reads; the fragments pass through the asm so no
+// use of them can be scheduled before the wait.
+__device__ __forceinline__ void frag_wait(uintx4 (&a)[2], uintx4 (&b)[4])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+__device__ __forceinline__ void frag_wait(uintx4 (&a)[2][2], uintx4 (&b)[2][4], int j0)
+{
+    if (j0 == 0)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(b[0][0]), "+v"(b[0][1]),
+                       "+v"(b[1][0]), "+v"(b[1][1]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b[0][2]), "+v"(b[0][3]), "+v"(b[1][2]), "+v"(b[1][3]));
+}
+
+// ------------------------------------------------------------------ kernel
+// FMT 0: E4M3 (64 values per row per stage); FMT 1: E2M1 (128 values).
+template <int FMT, int EPI, int SCM>
+__global__ __launch_bounds__(kThreads, 2) void gg_mx_kernel(MxParams p)
+{
+    static_assert(NSTAGE == 3, "the k-loop below is unrolled for three slots");
+    constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;
+    constexpr int MF = FMT == 0 ? 0 : 4;                  // operand format code of the scaled MFMA
+    constexpr int RB = 32 * ROW_BYTES;                    // LDS bytes of 32 rows
+    using S = Sc<SCM>;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     GroupTable tab;
     tab.G = p.G;
     int *tb = (int *)(smem + GEMM_LDS_BYTES);
@@ -161,90 +202,246 @@ __global__ __launch_bounds__(kThreads) void gg_mx_kernel(MxParams p)
     tab.rows = tb + p.G;
     tab.tile0 = tb + 2 * p.G;
     int *s_scan = tab.tile0 + p.G + 1;
-    const int total = build_group_table(tab, p.lens, p.offs, p.G, p.M, TilesFwd{BM, p.tilesN}, p.err, s_scan);
+    int total = build_group_table(tab, p.lens, p.offs, p.G, p.M, TilesFwd{BM, p.tilesN}, p.err, s_scan);
+    total = __builtin_amdgcn_readfirstlane(total);
 
-    const int wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int Kb = p.K / F::vals_per_byte;     // code bytes per row
-    const int KS = p.K / 32;                   // scale bytes per row
-    const int nk = (Kb + BKB - 1) / BKB;
+    const uint32_t lds0 = lds_addr(smem);
+    const int r32 = lane & 31, h = lane >> 5;
+    const uint32_t sh = 8u * h;
+
+    const int Kb = FMT == 0 ? p.K : p.K / 2;              // code bytes per row
+    const int KS = p.K / 32;                               // scale bytes per row
+    const int nk = (Kb + ROW_BYTES - 1) / ROW_BYTES, nfull = Kb / ROW_BYTES;
+    const int nb_last = (Kb - nfull * ROW_BYTES) / 16;     // blocks of the partial stage (E2M1)
+
+    // per-lane LDS read bases: chunks h and 2 + h of the lane's first A / B row
+    uint32_t aK[2], bK[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int ra = wm * 64 + r32, rb = wn * 128 + r32;
+        aK[c] = lds0 + ra * ROW_BYTES + kpos(ra, 2 * c + h) * 16;
+        bK[c] = lds0 + A_BYTES + rb * ROW_BYTES + kpos(rb, 2 * c + h) * 16;
+    }
 
     for (int tile = xcd_logical_id(); tile < total; tile += gridDim.x) {
-        const int g = find_group(tab, tile);
-        const int local = tile - tab.tile0[g];
-        const int row0 = tab.row0[g], rows = tab.rows[g];
+        const int g = __builtin_amdgcn_readfirstlane(find_group(tab, tile));
+        const int local = tile - __builtin_amdgcn_readfirstlane(tab.tile0[g]);
+        const int row0 = __builtin_amdgcn_readfirstlane(tab.row0[g]);
+        const int rows = __builtin_amdgcn_readfirstlane(tab.rows[g]);
         const int tm = (rows + BM - 1) / BM;
         const int nt = local / tm, mt = local % tm;
         const int m0 = mt * BM;
         const int vr = min(BM, rows - m0) - wm * 64;
         const int nvalid_bi = vr <= 0 ? 0 : (vr > 32 ? 2 : 1);
 
-        floatx16 acc[2][2];
+        // ---- operand buffers and per-thread offsets for this tile.  A rows
+        // past the expert's end and B rows past N fall outside the record
+        // bounds and read zeros; with SwiGLU, gate rows past N/2 read up rows
+        // whose outputs are never stored.
+        Ops o;
+        o.a = p.a + (int64_t)row0 * Kb;
+        o.abytes = (uint32_t)rows * Kb;
+        o.b = p.b + (int64_t)g * p.N * Kb;
+        o.bbytes = (uint32_t)p.N * Kb;
+        o.chunk = (uint32_t)(((tid & 3) ^ ((tid >> 4) & 3)) * 16);
+        o.avoff = (uint32_t)(m0 + (tid >> 2)) * Kb + o.chunk;
+        o.adelta = 64u * Kb;
+        if (EPI == kEpiNone) {
+            o.bvoff = (uint32_t)(nt * BN + (tid >> 2)) * Kb + o.chunk;
+#pragma unroll
+            for (int i = 0; i < B_LOADS; ++i) o.bdelta[i] = (uint32_t)(i * 64) * Kb;
+        } else {
+            // tile rows 0-63 / 64-127 / 128-191 / 192-255: gate j, up I + j,
+            // gate j + 64, up I + j + 64, with j = nt * 128 + row % 64
+            const int I = p.N >> 1;
+            o.bvoff = (uint32_t)(nt * (BN / 2) + (tid >> 2)) * Kb + o.chunk;
+            o.bdelta[0] = 0u;
+            o.bdelta[1] = (uint32_t)I * Kb;
+            o.bdelta[2] = 64u * Kb;
+            o.bdelta[3] = (uint32_t)(I + 64) * Kb;
+        }
+        ScRows sr;
+        sr.a = p.as;
+        sr.abytes = (uint32_t)((p.M * KS + 3) & ~3ll);
+        sr.b = p.bs;
+        sr.bbytes = (uint32_t)(((int64_t)p.G * p.N * KS + 3) & ~3ll);
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+            sr.row[bi] = (uint32_t)((row0 + min(m0 + wm * 64 + bi * 32 + r32, rows - 1)) * KS);
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+            sr.row[2 + bj] =
+                (uint32_t)((g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)) * KS);
+
+        floatx16 acc[2][4];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-        const uint8_t *Ab = p.a + (int64_t)row0 * Kb;
-        const uint8_t *Asb = p.as + (int64_t)row0 * KS;
-        const uint8_t *Bb = p.b + (int64_t)g * p.N * Kb;
-        const uint8_t *Bsb = p.bs + (int64_t)g * p.N * KS;
-        // B rows of this tile: for SwiGLU the tile's 128 rows are 64 gate rows
-        // and the 64 matching up rows, interleaved per wave (see map_col)
-        Stage st;
-        auto load = [&](int kt) {
-            if (EPI == kEpiNone) {
-                load_stage<FMT>(st, Ab, Asb, Bb, Bsb, m0, rows, nt * BN, p.N, Kb, KS, kt);
-            } else {
-                // gather: B row c of the tile is weight row map_col(nt, c)
-                const int kb0 = kt * BKB;
+        // The explicit waits below count a stage's loads (operands, then
+        // scales) as one group in program order; a compiler fence after each
+        // group keeps the scheduler from moving loads of different stages
+        // past one another.
+        uint32_t sc[NSTAGE][S::regs];
+        // prologue: stages 0 .. NSTAGE-1 (dummies past the end)
+        issue_stage(smem, o, 0 * STAGE_BYTES, 0, nk, Kb, wave);
+        load_scales<SCM>(sc[0], sr, 0, nk, nfull, h);
+        asm volatile("" ::: "memory");
+        issue_stage(smem, o, 1 * STAGE_BYTES, 1, nk, Kb, wave);
+        load_scales<SCM>(sc[1], sr, 1, nk, nfull, h);
+        asm volatile("" ::: "memory");
+        issue_stage(smem, o, 2 * STAGE_BYTES, 2, nk, Kb, wave);
+        load_scales<SCM>(sc[2], sr, 2, nk, nfull, h);
+        asm volatile("" ::: "memory");
+        wait_vmcnt<(NSTAGE - 1) * S::per_stage>();
+        barrier();
+
+        // Fragments: fa[c][bi] / fb[c][bj] hold chunk (c == 0 ? h : 2 + h) of
+        // the lane's rows.  E2M1 runs one MFMA step per chunk; E4M3 one MFMA
+        // over both chunks, split by B blocks (0-1, then 2-3).  Registers are
+        // refilled as soon as the last MFMA reading them has been issued.
+        uintx4 fa[2][2], fb[2][4];
+        if constexpr (FMT == 1) {
+            fa[0][0] = ldsr_u128<0>(aK[0]);
+            fa[0][1] = ldsr_u128<RB>(aK[0]);
+            fb[0][0] = ldsr_u128<0 * RB>(bK[0]);
+            fb[0][1] = ldsr_u128<1 * RB>(bK[0]);
+            fb[0][2] = ldsr_u128<2 * RB>(bK[0]);
+            fb[0][3] = ldsr_u128<3 * RB>(bK[0]);
+            frag_wait(fa[0], fb[0]);
+        } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int c = threadIdx.x + i * kThreads;
-                    const int r = c >> 3, kc = c & 7;
-                    const int k = kb0 + kc * 16;
-                    const bool kv = k < Kb;
-                    const int ar = min(m0 + r, rows - 1);
-                    const int br = clamp_col<EPI>(map_col<EPI>(nt, r, p.N), p.N, 1);
-                    st.a[i] = kv ? *(const uintx4 *)(Ab + (int64_t)ar * Kb + k) : uintx4{0u, 0u, 0u, 0u};
-                    st.b[i] = kv ? *(const uintx4 *)(Bb + (int64_t)br * Kb + k) : uintx4{0u, 0u, 0u, 0u};
-                }
-                const int t = threadIdx.x;
-                const uint8_t *srow = t < BM ? Asb + (int64_t)min(m0 + t, rows - 1) * KS
-                                             : Bsb + (int64_t)clamp_col<EPI>(map_col<EPI>(nt, t - BM, p.N), p.N, 1) * KS;
-                uint32_t w[2] = {0u, 0u};
-#pragma unroll
-                for (int j = 0; j < F::blocks; ++j) {
-                    const int blk = kt * F::blocks + j;
-                    const uint32_t v = blk < KS ? (uint32_t)srow[blk] : 0u;
-                    w[j >> 2] |= v << (8 * (j & 3));
-                }
-                st.sc = uintx2{w[0], w[1]};
+            for (int c = 0; c < 2; ++c) {
+                fa[c][0] = ldsr_u128<0>(aK[c]);
+                fa[c][1] = ldsr_u128<RB>(aK[c]);
+                fb[c][0] = ldsr_u128<0>(bK[c]);
+                fb[c][1] = ldsr_u128<RB>(bK[c]);
             }
+            frag_wait(fa, fb, 0);
+        }
+
+        auto mfma = [&](int bi, int bj, intx8 a, intx8 b, const uint32_t (&w)[S::regs], int s) {
+            acc[bi][bj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                a, b, acc[bi][bj], MF, MF, 0, scale_of<SCM>(w, bi, s, sh), 0, scale_of<SCM>(w, 2 + bj, s, sh));
         };
 
-        load(0);
-        store_stage(st, stage0);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            uint8_t *cur = stage0 + (kt & 1) * STAGE;
-            uint8_t *nxt = stage0 + ((kt + 1) & 1) * STAGE;
-            if (kt + 1 < nk) load(kt + 1);
-            mma_stage<FMT>(acc, cur, wm, wn, nvalid_bi);
-            if (kt + 1 < nk) store_stage(st, nxt);
-            __syncthreads();
+        int kt0 = 0;
+        auto step = [&](auto PC) {
+            constexpr int P = decltype(PC)::value;          // ring slot of stage kt
+            constexpr int SO = P * STAGE_BYTES, SN = ((P + 1) % NSTAGE) * STAGE_BYTES;
+            const int kt = kt0 + P;
+            uint32_t w[S::regs];
+            scale_words<SCM>(sc[P], w, sr, kt, nfull, nb_last, h);
+            if constexpr (FMT == 1) {
+                // read chunk 2 + h of stage kt | MFMA step 0
+                uintx4 ga[2], gb[4];
+                ga[0] = ldsr_u128<SO>(aK[1]);
+                ga[1] = ldsr_u128<SO + RB>(aK[1]);
+                gb[0] = ldsr_u128<SO + 0 * RB>(bK[1]);
+                gb[1] = ldsr_u128<SO + 1 * RB>(bK[1]);
+                gb[2] = ldsr_u128<SO + 2 * RB>(bK[1]);
+                gb[3] = ldsr_u128<SO + 3 * RB>(bK[1]);
+#pragma unroll
+                for (int bi = 0; bi < 2; ++bi)
+                    if (bi < nvalid_bi) {
+#pragma unroll
+                        for (int bj = 0; bj < 4; ++bj) mfma(bi, bj, pad8(fa[0][bi]), pad8(fb[0][bj]), w, 0);
+                    }
+                // stage kt+1 landed and every wave is done with slot P
+                wait_vmcnt<(NSTAGE - 2) * S::per_stage>();
+                frag_wait(ga, gb);
+                barrier();
+                issue_stage(smem, o, SO, kt + NSTAGE, nk, Kb, wave);
+                // read chunk h of stage kt+1 | MFMA step 1
+                fa[0][0] = ldsr_u128<SN>(aK[0]);
+                fa[0][1] = ldsr_u128<SN + RB>(aK[0]);
+                fb[0][0] = ldsr_u128<SN + 0 * RB>(bK[0]);
+                fb[0][1] = ldsr_u128<SN + 1 * RB>(bK[0]);
+                fb[0][2] = ldsr_u128<SN + 2 * RB>(bK[0]);
+                fb[0][3] = ldsr_u128<SN + 3 * RB>(bK[0]);
+#pragma unroll
+                for (int bi = 0; bi < 2; ++bi)
+                    if (bi < nvalid_bi) {
+#pragma unroll
+                        for (int bj = 0; bj < 4; ++bj) mfma(bi, bj, pad8(ga[bi]), pad8(gb[bj]), w, 1);
+                    }
+                load_scales<SCM>(sc[P], sr, kt + NSTAGE, nk, nfull, h);
+                asm volatile("" ::: "memory");
+                frag_wait(fa[0], fb[0]);
+            } else {
+                // read B blocks 2-3 of stage kt | MFMA on B blocks 0-1
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    fb[c][2] = ldsr_u128<SO + 2 * RB>(bK[c]);
+                    fb[c][3] = ldsr_u128<SO + 3 * RB>(bK[c]);
+                }
+#pragma unroll
+                for (int bi = 0; bi < 2; ++bi)
+                    if (bi < nvalid_bi) {
+#pragma unroll
+                        for (int bj = 0; bj < 2; ++bj)
+                            mfma(bi, bj, cat8(fa[0][bi], fa[1][bi]), cat8(fb[0][bj], fb[1][bj]), w, 0);
+                    }
+                wait_vmcnt<(NSTAGE - 2) * S::per_stage>();
+                frag_wait(fa, fb, 2);
+                barrier();
+                issue_stage(smem, o, SO, kt + NSTAGE, nk, Kb, wave);
+                // read B blocks 0-1 of stage kt+1 | MFMA on B blocks 2-3 | read A of stage kt+1
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    fb[c][0] = ldsr_u128<SN>(bK[c]);
+                    fb[c][1] = ldsr_u128<SN + RB>(bK[c]);
+                }
+#pragma unroll
+                for (int bi = 0; bi < 2; ++bi)
+                    if (bi < nvalid_bi) {
+#pragma unroll
+                        for (int bj = 2; bj < 4; ++bj)
+                            mfma(bi, bj, cat8(fa[0][bi], fa[1][bi]), cat8(fb[0][bj], fb[1][bj]), w, 0);
+                    }
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    fa[c][0] = ldsr_u128<SN>(aK[c]);
+                    fa[c][1] = ldsr_u128<SN + RB>(aK[c]);
+                }
+                load_scales<SCM>(sc[P], sr, kt + NSTAGE, nk, nfull, h);
+                asm volatile("" ::: "memory");
+                frag_wait(fa, fb, 0);
+            }
+        };
+        // Whole rounds of the three slots, then the last one or two stages.
+        // The loop has no early exit: the compiler's own waits for the scale
+        // registers assume every path it can see, and an exit taken between
+        // slots would show it a way back to the loop head past the other
+        // slots' loads.
+        for (; kt0 + NSTAGE <= nk; kt0 += NSTAGE) {
+            step(IC<0>{});
+            step(IC<1>{});
+            step(IC<2>{});
         }
-        store_tile<EPI>(acc, p.out, p.out_scale, row0, m0, rows, nt, p.N, p.ldo);
+        if (kt0 < nk) {
+            step(IC<0>{});
+            if (kt0 + 1 < nk) step(IC<1>{});
+        }
+        // drain the dummy stages still in flight before the slots are reused
+        wait_vmcnt<0>();
+        barrier();
+        store_out<EPI>(acc, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn);
     }
 }
 
-template <int FMT, int EPI>
+template <int FMT, int EPI, int SCM>
 hipError_t launch_one(const MxParams &p, hipStream_t s)
 {
-    const int lds = GEMM_LDS_BYTES + table_bytes(p.G);
-    auto kern = gg_mx_kernel<FMT, EPI>;
+    const int lds = NSTAGE * STAGE_BYTES + table_bytes(p.G);
+    auto kern = gg_mx_kernel<FMT, EPI, SCM>;
     static int configured_lds = 0;
     if (configured_lds < lds) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -254,14 +451,18 @@ hipError_t launch_one(const MxParams &p, hipStream_t s)
     int occ = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, lds);
     if (e != hipSuccess) return e;
-    if (occ < 1) occ = 1;
     const int64_t tiles_max = (p.M / BM + p.G) * (int64_t)p.tilesN;
-    int64_t grid = (int64_t)device_cus() * occ;
-    if (tiles_max < grid) grid = tiles_max;
-    if (grid >= 8) grid = grid / 8 * 8;
-    if (grid < 1) grid = 1;
+    const int64_t grid = persistent_grid(occ, tiles_max);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, p);
     return hipGetLastError();
+}
+
+template <int FMT, int SCM>
+hipError_t launch_epi(const MxParams &p, int epi, hipStream_t s)
+{
+    if (epi == kEpiSwiglu) return launch_one<FMT, kEpiSwiglu, SCM>(p, s);
+    if (epi == kEpiSwigluMxfp4) return launch_one<FMT, kEpiSwigluMxfp4, SCM>(p, s);
+    return launch_one<FMT, kEpiNone, SCM>(p, s);
 }
 
 }  // namespace
@@ -271,14 +472,9 @@ int mx_tile_n() { return BN; }
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s)
 {
-    if (fmt == 0) {
-        if (epi == kEpiSwiglu) return launch_one<0, kEpiSwiglu>(p, s);
-        if (epi == kEpiSwigluMxfp4) return launch_one<0, kEpiSwigluMxfp4>(p, s);
-        return launch_one<0, kEpiNone>(p, s);
-    }
-    if (epi == kEpiSwiglu) return launch_one<1, kEpiSwiglu>(p, s);
-    if (epi == kEpiSwigluMxfp4) return launch_one<1, kEpiSwigluMxfp4>(p, s);
-    return launch_one<1, kEpiNone>(p, s);
+    if (fmt == 0) return launch_epi<0, kScE4M3>(p, epi, s);
+    if (p.K % 128 == 0) return launch_epi<1, kScE2M1Word>(p, epi, s);
+    return launch_epi<1, kScE2M1Span>(p, epi, s);
 }
 
 }  // namespace ptgg

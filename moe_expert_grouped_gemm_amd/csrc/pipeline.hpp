@@ -1,0 +1,232 @@
+// pipeline.hpp -- pieces shared by the gfx950 grouped-GEMM mainloops (BF16
+// and OCP-MX): the LDS ring filled by direct buffer->LDS loads, its waits and
+// barrier, the swizzled geometry of a reduction-contiguous operand in LDS,
+// the SwiGLU column map of a tile and the output epilogues.
+//
+// Tiles are 128 x 256 outputs computed by four waves in a 2 x 2 layout, each
+// wave owning 64 x 128 outputs as 2 x 4 blocks of 32 x 32 (the result layout
+// of the 32x32 MFMAs: lane l, register r holds row (r/4)*8 + (l/32)*4 + r%4
+// and column l%32 of its block).  Every stage of the ring carries 64 bytes of
+// each operand row along the reduction (32 BF16, 64 E4M3 or 128 E2M1 values).
+#pragma once
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ptgg {
+namespace {
+
+constexpr int BM = 128, BN = 256;
+constexpr int ROW_BYTES = 64;                      // per operand row per stage
+constexpr int A_BYTES = BM * ROW_BYTES;            // 8 KiB per stage
+constexpr int B_BYTES = BN * ROW_BYTES;            // 16 KiB per stage
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int A_LOADS = A_BYTES / 16 / kThreads;   // 16-byte loads per thread per stage
+constexpr int B_LOADS = B_BYTES / 16 / kThreads;
+constexpr int LOADS = A_LOADS + B_LOADS;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;       // raw buffer, 32-bit data format
+constexpr uint32_t kOOB = 0x80000000u;             // offset past every record bound
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without the memory fence of __syncthreads() (which would
+// wait for every outstanding load, draining the ring); the empty asm keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+// 16-byte LDS read at addr + OFF, issued as inline asm: the compiler cannot
+// tell it apart from reads of LDS still being filled by the in-flight direct
+// loads and would otherwise wait for every outstanding load before it.
+template <int OFF>
+__device__ __forceinline__ uintx4 ldsr_u128(uint32_t addr)
+{
+    uintx4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+// One 16-byte direct load per lane into LDS (lane i lands at lds + 16 i) from
+// byte voff + soff of a buffer of `bytes` bytes at `base`; offsets at or past
+// the bound read zeros.  Kept a plain function: the buffer-resource type is
+// device-only, and inside templates clang's host pass would silently discard
+// every kernel that reaches it.
+__device__ __forceinline__ void dma16(const void *base, uint32_t bytes, uint8_t *lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (lds_void *)lds, 16, voff, soff, 0, 0);
+}
+
+// One operand's direct-load state for a tile: NL 16-byte loads per thread
+// per stage at voff[i] + kt * kstep (bytes) inside the buffer at `base`.
+template <int NL>
+struct Dma {
+    const void *base;
+    uint32_t bytes;
+    uint32_t voff[NL];
+    uint32_t kstep;
+};
+
+// Issue one stage of an operand: slot i of this thread lands at LDS byte
+// lds_off + (i * 256 + thread) * 16.
+template <int NL>
+__device__ __forceinline__ void issue(uint8_t *smem, const Dma<NL> &d, uint32_t lds_off, uint32_t soff,
+                                      const uint32_t (&voff)[NL], int wave)
+{
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+        dma16(d.base, d.bytes, smem + lds_off + (i * kThreads + wave * kWave) * 16, voff[i], soff);
+}
+
+// Reduction-contiguous operand with R rows in one stage: LDS [R][64 bytes],
+// chunk c (16 bytes) of row r at position c ^ ((r >> 2) & 3), so the 16-byte
+// fragment reads of 32 consecutive rows spread over all banks.
+__device__ __forceinline__ int kpos(int r, int c) { return c ^ ((r >> 2) & 3); }
+// slot s of such a stage: tile row and source chunk
+__device__ __forceinline__ void kslot(int s, int &r, int &c) { r = s >> 2; c = kpos(r, s & 3); }
+
+// Tile column c (0..255) -> logical output column.  With SwiGLU a tile covers
+// 128 consecutive outputs j: within each wave's 128 columns, blocks 0-1 are
+// gate columns j and blocks 2-3 the matching up columns I + j, so one lane
+// holds both factors of its outputs.
+template <int EPI>
+__device__ __forceinline__ int col_of(int nt, int c, int Nout)
+{
+    if (EPI == kEpiNone) return nt * BN + c;
+    const int I = Nout >> 1;
+    const int w = c >> 7, cc = c & 127;
+    const int j = nt * (BN / 2) + w * 64 + (cc & 63);
+    return cc >= 64 ? I + j : j;
+}
+
+// Clamp an 8-column chunk start into the valid range of its half.
+template <int EPI>
+__device__ __forceinline__ int clamp8(int n, int Nout)
+{
+    if (EPI == kEpiNone) return min(n, Nout - 8);
+    const int I = Nout >> 1;
+    return n < I ? min(n, I - 8) : min(n, Nout - 8);
+}
+
+// Clamp a single column into the valid range of its half.
+template <int EPI>
+__device__ __forceinline__ int clamp1(int n, int Nout)
+{
+    if (EPI == kEpiNone) return min(n, Nout - 1);
+    const int I = Nout >> 1;
+    return n < I ? min(n, I - 1) : min(n, Nout - 1);
+}
+
+// Wave (wm, wn) holds rows wm*64 + bi*32 + .., columns wn*128 + bj*32 + lane%32.
+__device__ __forceinline__ int e_row(int wm, int bi, int reg)
+{
+    return wm * 64 + bi * 32 + (reg >> 2) * 8 + ((threadIdx.x & 63) >> 5) * 4 + (reg & 3);
+}
+
+// Stores rows [m0, m0 + 128) of one expert (global row row0 + m), masked to
+// m < rows.  Output layouts:
+//   kEpiNone:        bf16 out[M, ldo], columns nt*256 + c < Nout
+//   kEpiSwiglu:      bf16 out[M, ldo], outputs j < Nout/2
+//   kEpiSwigluMxfp4: codes out[M, ldo bytes] (two per byte, low nibble the
+//                    even output), scales out_scale[M, Nout/64]; requires
+//                    (Nout/2) % 32 == 0
+template <int EPI>
+__device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], void *out, uint8_t *out_scale, int ldo,
+                                          int Nout, int64_t row0, int m0, int rows, int nt, int wm, int wn)
+{
+    const int lane = threadIdx.x & 63;
+    if (EPI == kEpiNone) {
+        uint16_t *o = (uint16_t *)out + row0 * ldo;
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+                const int n = nt * BN + wn * 128 + bj * 32 + (lane & 31);
+                if (n >= Nout) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + e_row(wm, bi, r);
+                    if (m < rows) o[(int64_t)m * ldo + n] = (uint16_t)bf16_rne(acc[bi][bj][r]);
+                }
+            }
+    } else if (EPI == kEpiSwiglu) {
+        uint16_t *o = (uint16_t *)out + row0 * ldo;
+        const int I = Nout >> 1;
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) {
+            const int j = nt * (BN / 2) + wn * 64 + bj * 32 + (lane & 31);
+            if (j >= I) continue;
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + e_row(wm, bi, r);
+                    if (m < rows)
+                        o[(int64_t)m * ldo + j] = (uint16_t)bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r]));
+                }
+        }
+    } else {
+        // SwiGLU value rounded to bf16, then one MXFP4 block per 32 outputs:
+        // the 32 lanes of a half-wave hold 32 consecutive j of one row.
+        uint8_t *o = (uint8_t *)out + row0 * ldo;
+        uint8_t *os = out_scale + row0 * (Nout / 64);
+        const int I = Nout >> 1;
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) {
+            const int j = nt * (BN / 2) + wn * 64 + bj * 32 + (lane & 31);
+            const bool jvalid = j < I;          // uniform over a half-wave (I % 32 == 0)
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + e_row(wm, bi, r);
+                    const uint32_t hb = bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r]));
+                    uint32_t amax = hb & 0x7FFFu;
+#pragma unroll
+                    for (int d = 1; d < 32; d <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, d, 64));
+                    const uint32_t E = mx_scale_byte<2>(amax);
+                    const uint32_t code = mx_encode<1>(hb, E);
+                    const uint32_t nb = (uint32_t)__shfl_xor((int)code, 1, 64);
+                    if (jvalid && m < rows) {
+                        if ((lane & 1) == 0) o[(int64_t)m * ldo + (j >> 1)] = (uint8_t)(code | (nb << 4));
+                        if ((lane & 31) == 0) os[(int64_t)m * (Nout / 64) + (j >> 5)] = (uint8_t)E;
+                    }
+                }
+        }
+    }
+}
+
+// Grid of a persistent launch: enough workgroups to fill every CU at the
+// kernel's occupancy, never more than there are tiles, a multiple of the 8
+// XCDs when possible.
+inline int64_t persistent_grid(int occ, int64_t tiles_max)
+{
+    int64_t grid = (int64_t)device_cus() * (occ < 1 ? 1 : occ);
+    if (tiles_max < grid) grid = tiles_max;
+    if (grid >= 8) grid = grid / 8 * 8;
+    return grid < 1 ? 1 : grid;
+}
+
+}  // namespace
+}  // namespace ptgg
