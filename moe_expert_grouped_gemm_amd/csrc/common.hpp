@@ -121,10 +121,12 @@ struct GroupTable {
 };
 
 // Bytes of LDS the table needs for G experts.
-__host__ __device__ constexpr int table_bytes(int G) { return 4 * (3 * G + 1) + 16; }
+// (3G + 1 ints, then scan scratch for up to 8 waves)
+__host__ __device__ constexpr int table_bytes(int G) { return 4 * (3 * G + 1) + 32; }
 
-// Exclusive scan over v (one value per thread) across the 256-thread block;
+// Exclusive scan over v (one value per thread) across the NT-thread block;
 // returns this thread's exclusive prefix and writes the block total to *total.
+template <int NT = kThreads>
 __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int *total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -138,7 +140,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int *tot
     __syncthreads();
     int before = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) {
+    for (int w = 0; w < NT / kWave; ++w) {
         int s = s_wave[w];
         before += (w < wave) ? s : 0;
         all += s;
@@ -158,12 +160,12 @@ struct TilesWgrad {        // wgrad: the whole output of active experts
     __device__ int operator()(int rows) const { return (rows > 0 || !accumulate) ? ntiles : 0; }
 };
 
-template <class Tiles>
+template <class Tiles, int NT = kThreads>
 __device__ __forceinline__ int build_group_table(GroupTable &t, const int64_t *lens, const int64_t *offs,
                                  int G, int64_t M, Tiles tiles, uint32_t *err, int *s_scratch)
 {
     const int tid = threadIdx.x;
-    const int per = (G + kThreads - 1) / kThreads;
+    const int per = (G + NT - 1) / NT;
     const int g0 = tid * per;
     uint32_t flags = 0;
     // pass 1: clamped lengths and (if no offsets) their prefix
@@ -179,7 +181,7 @@ __device__ __forceinline__ int build_group_table(GroupTable &t, const int64_t *l
         }
     }
     int total_rows;
-    int pre = block_exclusive_scan(sum, s_scratch, &total_rows);
+    int pre = block_exclusive_scan<NT>(sum, s_scratch, &total_rows);
     for (int i = 0; i < per; ++i) {
         int g = g0 + i;
         if (g < G) {
@@ -199,7 +201,7 @@ __device__ __forceinline__ int build_group_table(GroupTable &t, const int64_t *l
         if (g < G) tsum += tiles(t.rows[g]);
     }
     int total_tiles;
-    int tpre = block_exclusive_scan(tsum, s_scratch, &total_tiles);
+    int tpre = block_exclusive_scan<NT>(tsum, s_scratch, &total_tiles);
     for (int i = 0; i < per; ++i) {
         int g = g0 + i;
         if (g < G) {

@@ -27,6 +27,8 @@
 // slot's registers and LDS offsets static.  Stages past the end are still
 // issued, with offsets past every bound (zeros, no memory traffic), so that
 // every wait in the loop has the same count.
+#include <stdlib.h>
+
 #include "pipeline.hpp"
 
 namespace ptgg {
@@ -437,6 +439,400 @@ __global__ __launch_bounds__(kThreads, 2) void gg_mx_kernel(MxParams p)
     }
 }
 
+// ====================================================================== wide
+// The main MX kernel: one workgroup of 8 waves per CU (still two waves per
+// SIMD), 256 x 256 tiles (wave (wm, wn), wm = 0..3, owns 64 x 128 outputs as
+// before) and 128 code bytes of every operand row per stage, so that each
+// direct load fetches whole 128-byte lines (64-byte half lines stream from
+// L2 at roughly half the rate) and a tile moves a third fewer operand bytes
+// per product than 128 x 256.  Two 64 KiB ring slots: the loads of stage
+// kt+1 go out at the start of stage kt and land while it computes.
+//
+// LDS rows are 128 bytes, chunk c (16 bytes) of row r at position
+// c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows hit 8
+// different bank groups.  A lane reads chunks 2j + h of its rows; with the
+// row's base 128-byte aligned, the address of chunk 2j + h is
+// base ^ (j << 5) for a per-lane base that folds in h and r & 7.
+//
+// Per stage a row holds 4 scale blocks (E4M3) or 8 (E2M1, K % 256 == 0).
+constexpr int WBM = 256, WBN = 256, WROW = 128, WTHREADS = 512;
+constexpr int WA_BYTES = WBM * WROW;                   // 32 KiB
+constexpr int WSTAGE = WA_BYTES + WBN * WROW;          // 64 KiB
+constexpr int W_LOADS = WA_BYTES / 16 / WTHREADS;      // per operand per thread per stage (4)
+
+enum WideScale {
+    kWE4M3Word = 0,   // E4M3, K % 128 == 0: the word of bytes 4kt .. 4kt+3
+    kWE4M3Span = 1,   // E4M3, other K: two words exchanged between lane halves
+    kWE2M1Pair = 2,   // E2M1, K % 256 == 0: words 8kt and 8kt+4, one per lane half, exchanged
+};
+
+// Load this lane's scale word of each of its 6 rows for stage kt.
+template <int WSC>
+__device__ __forceinline__ void wload_scales(uint32_t (&sc)[6], const ScRows &sr, int kt, int nk, int h)
+{
+    const uint32_t soff = kt >= nk ? kOOB : 0u;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        const uint8_t *base = i < 2 ? sr.a : sr.b;
+        const uint32_t bytes = i < 2 ? sr.abytes : sr.bbytes;
+        uint32_t a;
+        if constexpr (WSC == kWE4M3Word) a = sr.row[i] + 4u * kt;
+        else if constexpr (WSC == kWE4M3Span) a = ((sr.row[i] + 4u * kt) & ~3u) + 4u * h;
+        else a = sr.row[i] + 8u * kt + 4u * h;
+        sc[i] = ld_u32(base, bytes, a, soff);
+    }
+}
+
+// Stage scale words, one per row: E4M3 the row's 4 bytes of the stage in
+// order (missing blocks of a partial last stage cleared), so step s of lane
+// half h takes byte 2s + h; E2M1 the 4 bytes this lane half uses, in step
+// order (bytes h, 2 + h, 4 + h, 6 + h of the row's 8, picked by v_perm_b32).
+template <int WSC>
+__device__ __forceinline__ void wscale_words(const uint32_t (&sc)[6], uint32_t (&w)[6], const ScRows &sr, int kt,
+                                             int nfull, int nb_last, int h)
+{
+    const uint32_t keep = (kt == nfull) ? (1u << (8 * nb_last)) - 1u : 0xFFFFFFFFu;
+    const uint32_t sel = h ? 0x07050301u : 0x06040200u;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        if constexpr (WSC == kWE4M3Word) {
+            w[i] = sc[i];
+        } else if constexpr (WSC == kWE4M3Span) {
+            const auto r = __builtin_amdgcn_permlane32_swap(sc[i], sc[i], false, false);
+            w[i] = __builtin_amdgcn_alignbyte(r[1], r[0], (sr.row[i] + 4u * kt) & 3u) & keep;
+        } else {
+            const auto r = __builtin_amdgcn_permlane32_swap(sc[i], sc[i], false, false);
+            w[i] = __builtin_amdgcn_perm(r[1], r[0], sel);
+        }
+    }
+}
+
+// Scale operand of row slot i for MFMA step s of a stage.
+template <int WSC>
+__device__ __forceinline__ int wscale_of(const uint32_t (&w)[6], int i, int s, uint32_t sh)
+{
+    if constexpr (WSC == kWE2M1Pair) return (int)__builtin_amdgcn_ubfe(w[i], 8u * s, 8u);
+    else return (int)__builtin_amdgcn_ubfe(w[i], sh + 16u * s, 8u);
+}
+
+struct WOps {
+    const uint8_t *a;
+    const uint8_t *b;
+    uint32_t abytes, bbytes;
+    uint32_t avoff, bvoff;          // load 0 of this thread, chunk included
+    uint32_t adelta[W_LOADS];       // row distances of loads 0..3 (bytes)
+    uint32_t bdelta[W_LOADS];
+    uint32_t chunk;
+};
+
+// Issue the operand loads of stage kt into ring slot st (branch-free: a
+// thread whose chunk lies past the row length in a partial last stage, and
+// every thread of a stage past the end, gets an offset past the bound).
+__device__ __forceinline__ void wissue_stage(uint8_t *smem, const WOps &o, uint32_t st, int kt, int nk, int Kb,
+                                             int wave)
+{
+    const int k0 = kt * WROW;
+    const int room = kt < nk ? Kb - k0 : 0;
+    const bool ok = (int)o.chunk < room;
+    const uint32_t va = ok ? o.avoff + k0 : kOOB, vb = ok ? o.bvoff + k0 : kOOB;
+    uint8_t *lds = smem + st + wave * kWave * 16;
+#pragma unroll
+    for (int i = 0; i < W_LOADS; ++i) dma16(o.a, o.abytes, lds + i * WTHREADS * 16, va, o.adelta[i]);
+#pragma unroll
+    for (int i = 0; i < W_LOADS; ++i) dma16(o.b, o.bbytes, lds + WA_BYTES + i * WTHREADS * 16, vb, o.bdelta[i]);
+}
+
+// 16-byte LDS read at a run-time address plus immediate OFF (bi / bj rows).
+template <int OFF>
+__device__ __forceinline__ uintx4 wld(uint32_t addr)
+{
+    return ldsr_u128<OFF>(addr);
+}
+
+template <int FMT, int EPI, int WSC>
+__global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
+{
+    constexpr int GEMM_LDS_BYTES = 2 * WSTAGE;
+    constexpr int MF = FMT == 0 ? 0 : 4;
+    constexpr int RB = 32 * WROW;                           // LDS bytes of 32 rows (bi / bj step)
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    GroupTable tab;
+    tab.G = p.G;
+    int *tb = (int *)(smem + GEMM_LDS_BYTES);
+    tab.row0 = tb;
+    tab.rows = tb + p.G;
+    tab.tile0 = tb + 2 * p.G;
+    int *s_scan = tab.tile0 + p.G + 1;
+    int total = build_group_table<TilesFwd, WTHREADS>(tab, p.lens, p.offs, p.G, p.M, TilesFwd{WBM, p.tilesN}, p.err,
+                                                      s_scan);
+    total = __builtin_amdgcn_readfirstlane(total);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t lds0 = lds_addr(smem);
+    const int r32 = lane & 31, h = lane >> 5;
+    const uint32_t sh = 8u * h;
+
+    const int Kb = FMT == 0 ? p.K : p.K / 2;
+    const int KS = p.K / 32;
+    const int nk = (Kb + WROW - 1) / WROW, nfull = Kb / WROW;
+    const int nb_last = (Kb - nfull * WROW) / 32;           // E4M3 blocks of the partial stage
+
+    // per-lane fragment bases (slot 0 / 1): chunk 2j + h of the lane's first
+    // A row / B row is at base ^ (j << 5)
+    uint32_t aB[2], bB[2];
+    {
+        const uint32_t y = (uint32_t)((h ^ (r32 & 7)) & 1) * 16u | (uint32_t)((r32 & 6) << 4);
+        const uint32_t ra = (uint32_t)(wm * 64 + r32), rb = (uint32_t)(wn * 128 + r32);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            aB[s] = lds0 + s * WSTAGE + ra * WROW + y;
+            bB[s] = lds0 + s * WSTAGE + WA_BYTES + rb * WROW + y;
+        }
+    }
+
+    for (int tile = xcd_logical_id(); tile < total; tile += gridDim.x) {
+        const int g = __builtin_amdgcn_readfirstlane(find_group(tab, tile));
+        const int local = tile - __builtin_amdgcn_readfirstlane(tab.tile0[g]);
+        const int row0 = __builtin_amdgcn_readfirstlane(tab.row0[g]);
+        const int rows = __builtin_amdgcn_readfirstlane(tab.rows[g]);
+        const int tm = (rows + WBM - 1) / WBM;
+        const int nt = local / tm, mt = local % tm;
+        const int m0 = mt * WBM;
+        const int vr = min(WBM, rows - m0) - wm * 64;
+        const int nvalid_bi = vr <= 0 ? 0 : (vr > 32 ? 2 : 1);
+
+        // ---- operand loads: slot i * 512 + t holds chunk c = (t & 7) ^ ((t >> 3) & 7)
+        // of tile row i * 64 + t / 8
+        WOps o;
+        o.a = p.a + (int64_t)row0 * Kb;
+        o.abytes = (uint32_t)rows * Kb;
+        o.b = p.b + (int64_t)g * p.N * Kb;
+        o.bbytes = (uint32_t)p.N * Kb;
+        o.chunk = (uint32_t)(((tid & 7) ^ ((tid >> 3) & 7)) * 16);
+        o.avoff = (uint32_t)(m0 + (tid >> 3)) * Kb + o.chunk;
+#pragma unroll
+        for (int i = 0; i < W_LOADS; ++i) o.adelta[i] = (uint32_t)(i * 64) * Kb;
+        if (EPI == kEpiNone) {
+            o.bvoff = (uint32_t)(nt * WBN + (tid >> 3)) * Kb + o.chunk;
+#pragma unroll
+            for (int i = 0; i < W_LOADS; ++i) o.bdelta[i] = (uint32_t)(i * 64) * Kb;
+        } else {
+            // tile rows 0-63 / 64-127 / 128-191 / 192-255: gate j, up I + j,
+            // gate j + 64, up I + j + 64, with j = nt * 128 + row % 64
+            const int I = p.N >> 1;
+            o.bvoff = (uint32_t)(nt * (WBN / 2) + (tid >> 3)) * Kb + o.chunk;
+            o.bdelta[0] = 0u;
+            o.bdelta[1] = (uint32_t)I * Kb;
+            o.bdelta[2] = 64u * Kb;
+            o.bdelta[3] = (uint32_t)(I + 64) * Kb;
+        }
+        ScRows sr;
+        sr.a = p.as;
+        sr.abytes = (uint32_t)((p.M * KS + 3) & ~3ll);
+        sr.b = p.bs;
+        sr.bbytes = (uint32_t)(((int64_t)p.G * p.N * KS + 3) & ~3ll);
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+            sr.row[bi] = (uint32_t)((row0 + min(m0 + wm * 64 + bi * 32 + r32, rows - 1)) * KS);
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+            sr.row[2 + bj] =
+                (uint32_t)((g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)) * KS);
+
+        floatx16 acc[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        auto mfma = [&](int bi, int bj, intx8 a, intx8 b, const uint32_t (&w)[6], int s) {
+            acc[bi][bj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                a, b, acc[bi][bj], MF, MF, 0, wscale_of<WSC>(w, bi, s, sh), 0, wscale_of<WSC>(w, 2 + bj, s, sh));
+        };
+
+        // prologue: stage 0 (the loads of each stage form one group in program order)
+        uint32_t sc[2][6];
+        wissue_stage(smem, o, 0, 0, nk, Kb, wave);
+        wload_scales<WSC>(sc[0], sr, 0, nk, h);
+        asm volatile("" ::: "memory");
+        wait_vmcnt<0>();
+        barrier();
+
+        // Fragments.  E2M1: f*[s & 1] hold chunk 2s + h for MFMA step s (A 2 x,
+        // B 4 x 16 bytes).  E4M3: step s uses chunks 4s + h and 4s + 2 + h;
+        // A of the current step sits in ea, B blocks 0-1 / 2-3 in eb[0] / eb[1].
+        uintx4 fa[2][2], fb[2][4];          // E2M1
+        uintx4 ea[2][2], eb[2][2][2];       // E4M3 A [chunk][block], B [half][chunk][block]
+        auto rdA = [&](uintx4 (&x)[2], uint32_t addr) {
+            x[0] = wld<0>(addr);
+            x[1] = wld<RB>(addr);
+        };
+        if constexpr (FMT == 1) {
+            rdA(fa[0], aB[0]);
+            fb[0][0] = wld<0 * RB>(bB[0]);
+            fb[0][1] = wld<1 * RB>(bB[0]);
+            fb[0][2] = wld<2 * RB>(bB[0]);
+            fb[0][3] = wld<3 * RB>(bB[0]);
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fb[0][0]), "+v"(fb[0][1]),
+                         "+v"(fb[0][2]), "+v"(fb[0][3]));
+        } else {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                rdA(ea[c], aB[0] ^ (uint32_t)(c << 5));
+                eb[0][c][0] = wld<0>(bB[0] ^ (uint32_t)(c << 5));
+                eb[0][c][1] = wld<RB>(bB[0] ^ (uint32_t)(c << 5));
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ea[0][0]), "+v"(ea[0][1]), "+v"(ea[1][0]), "+v"(ea[1][1]),
+                         "+v"(eb[0][0][0]), "+v"(eb[0][0][1]), "+v"(eb[0][1][0]), "+v"(eb[0][1][1]));
+        }
+
+        int kt0 = 0;
+        auto stage = [&](auto PC) {
+            constexpr int P = decltype(PC)::value;          // ring slot of stage kt
+            constexpr int Q = P ^ 1;
+            const int kt = kt0 + P;
+            uint32_t w[6];
+            wscale_words<WSC>(sc[P], w, sr, kt, nfull, nb_last, h);
+            // the next stage's loads go to the other slot, free since the barrier
+            wissue_stage(smem, o, Q * WSTAGE, kt + 1, nk, Kb, wave);
+            wload_scales<WSC>(sc[Q], sr, kt + 1, nk, h);
+            asm volatile("" ::: "memory");
+            if constexpr (FMT == 1) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int cur = s & 1, nxt = cur ^ 1;
+                    if (s < 3) {
+                        const uint32_t xa = aB[P] ^ (uint32_t)((s + 1) << 5), xb = bB[P] ^ (uint32_t)((s + 1) << 5);
+                        rdA(fa[nxt], xa);
+                        fb[nxt][0] = wld<0 * RB>(xb);
+                        fb[nxt][1] = wld<1 * RB>(xb);
+                        fb[nxt][2] = wld<2 * RB>(xb);
+                        fb[nxt][3] = wld<3 * RB>(xb);
+                    }
+#pragma unroll
+                    for (int bi = 0; bi < 2; ++bi)
+                        if (bi < nvalid_bi) {
+#pragma unroll
+                            for (int bj = 0; bj < 4; ++bj) mfma(bi, bj, pad8(fa[cur][bi]), pad8(fb[cur][bj]), w, s);
+                        }
+                    if (s < 3)
+                        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[nxt][0]), "+v"(fa[nxt][1]), "+v"(fb[nxt][0]),
+                                     "+v"(fb[nxt][1]), "+v"(fb[nxt][2]), "+v"(fb[nxt][3]));
+                }
+            } else {
+                // substeps: (step 0, B 0-1), (0, 2-3), (1, 0-1), (1, 2-3).  One A
+                // buffer: step 1's A is read once the last MFMA on step 0's A
+                // has been issued.
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int s = q >> 1, half = q & 1;
+                    // read ahead: B half 1 of step s, or B half 0 of step 1
+                    if (q == 0 || q == 2) {
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            const uint32_t xb = bB[P] ^ (uint32_t)((2 * s + c) << 5);
+                            eb[1][c][0] = wld<2 * RB>(xb);
+                            eb[1][c][1] = wld<3 * RB>(xb);
+                        }
+                    } else if (q == 1) {
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            const uint32_t xb = bB[P] ^ (uint32_t)((2 + c) << 5);
+                            eb[0][c][0] = wld<0>(xb);
+                            eb[0][c][1] = wld<RB>(xb);
+                        }
+                    }
+#pragma unroll
+                    for (int bi = 0; bi < 2; ++bi)
+                        if (bi < nvalid_bi) {
+#pragma unroll
+                            for (int k = 0; k < 2; ++k)
+                                mfma(bi, 2 * half + k, cat8(ea[0][bi], ea[1][bi]), cat8(eb[half][0][k], eb[half][1][k]),
+                                     w, s);
+                        }
+                    if (q == 1) {
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) rdA(ea[c], aB[P] ^ (uint32_t)((2 + c) << 5));
+                    }
+                    if (q == 0 || q == 2)
+                        asm volatile("s_waitcnt lgkmcnt(0)"
+                                     : "+v"(eb[1][0][0]), "+v"(eb[1][0][1]), "+v"(eb[1][1][0]), "+v"(eb[1][1][1]));
+                    else if (q == 1)
+                        asm volatile("s_waitcnt lgkmcnt(0)"
+                                     : "+v"(ea[0][0]), "+v"(ea[0][1]), "+v"(ea[1][0]), "+v"(ea[1][1]),
+                                       "+v"(eb[0][0][0]), "+v"(eb[0][0][1]), "+v"(eb[0][1][0]), "+v"(eb[0][1][1]));
+                }
+            }
+            // stage kt+1 landed for this wave; after the barrier for all waves,
+            // and every wave is done reading slot P
+            wait_vmcnt<0>();
+            barrier();
+            if (kt + 1 < nk) {
+                if constexpr (FMT == 1) {
+                    rdA(fa[0], aB[Q]);
+                    fb[0][0] = wld<0 * RB>(bB[Q]);
+                    fb[0][1] = wld<1 * RB>(bB[Q]);
+                    fb[0][2] = wld<2 * RB>(bB[Q]);
+                    fb[0][3] = wld<3 * RB>(bB[Q]);
+                    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fb[0][0]),
+                                 "+v"(fb[0][1]), "+v"(fb[0][2]), "+v"(fb[0][3]));
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        rdA(ea[c], aB[Q] ^ (uint32_t)(c << 5));
+                        eb[0][c][0] = wld<0>(bB[Q] ^ (uint32_t)(c << 5));
+                        eb[0][c][1] = wld<RB>(bB[Q] ^ (uint32_t)(c << 5));
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)"
+                                 : "+v"(ea[0][0]), "+v"(ea[0][1]), "+v"(ea[1][0]), "+v"(ea[1][1]),
+                                   "+v"(eb[0][0][0]), "+v"(eb[0][0][1]), "+v"(eb[0][1][0]), "+v"(eb[0][1][1]));
+                }
+            }
+        };
+        // whole pairs of slots, then the last stage; no early exit (see the
+        // 128 x 256 kernel)
+        for (; kt0 + 2 <= nk; kt0 += 2) {
+            stage(IC<0>{});
+            stage(IC<1>{});
+        }
+        if (kt0 < nk) stage(IC<0>{});
+        store_out<EPI>(acc, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn);
+    }
+}
+
+template <int FMT, int EPI, int WSC>
+hipError_t launch_wide(const MxParams &p, hipStream_t s)
+{
+    const int lds = 2 * WSTAGE + table_bytes(p.G);
+    auto kern = gg_mx_wide_kernel<FMT, EPI, WSC>;
+    static int configured_lds = 0;
+    if (configured_lds < lds) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        configured_lds = lds;
+    }
+    int occ = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, WTHREADS, lds);
+    if (e != hipSuccess) return e;
+    const int64_t tiles_max = (p.M / WBM + p.G) * (int64_t)p.tilesN;
+    const int64_t grid = persistent_grid(occ, tiles_max);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WTHREADS), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int FMT, int WSC>
+hipError_t launch_wide_epi(const MxParams &p, int epi, hipStream_t s)
+{
+    if (epi == kEpiSwiglu) return launch_wide<FMT, kEpiSwiglu, WSC>(p, s);
+    if (epi == kEpiSwigluMxfp4) return launch_wide<FMT, kEpiSwigluMxfp4, WSC>(p, s);
+    return launch_wide<FMT, kEpiNone, WSC>(p, s);
+}
+
 template <int FMT, int EPI, int SCM>
 hipError_t launch_one(const MxParams &p, hipStream_t s)
 {
@@ -470,9 +866,28 @@ hipError_t launch_epi(const MxParams &p, int epi, hipStream_t s)
 int mx_tile_m() { return BM; }
 int mx_tile_n() { return BN; }
 
+// Which MX mainloop runs: PTGG_MX_TILE=128 forces the 128 x 256 kernel
+// wherever it applies (a tuning knob for experiments; results do not depend
+// on it).
+bool mx_force_narrow()
+{
+    static const bool narrow = [] {
+        const char *e = getenv("PTGG_MX_TILE");
+        return e && atoi(e) == 128;
+    }();
+    return narrow;
+}
+
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s)
 {
-    if (fmt == 0) return launch_epi<0, kScE4M3>(p, epi, s);
+    if (fmt == 1 && mx_force_narrow())
+        return p.K % 128 == 0 ? launch_epi<1, kScE2M1Word>(p, epi, s) : launch_epi<1, kScE2M1Span>(p, epi, s);
+    if (fmt == 0) {
+        if (p.K % 128 == 0) return launch_wide_epi<0, kWE4M3Word>(p, epi, s);
+        return launch_wide_epi<0, kWE4M3Span>(p, epi, s);
+    }
+    if (p.K % 256 == 0) return launch_wide_epi<1, kWE2M1Pair>(p, epi, s);
+    // E2M1 whose stage of 8 scale blocks would not start on a word
     if (p.K % 128 == 0) return launch_epi<1, kScE2M1Word>(p, epi, s);
     return launch_epi<1, kScE2M1Span>(p, epi, s);
 }
