@@ -106,8 +106,9 @@ typedef enum {
  *  b_scale    [G, N, K/32] E8M0, MX only
  *  out        see pt_epilogue; rows outside every expert are not written
  *  out_scale  [M, N/64] E8M0 for PT_EPI_SWIGLU_MXFP4, else NULL
- *  Requirements: K % 8 == 0 (bf16) or K % 32 == 0 (MX); N % 8 == 0 (bf16,
- *  trans_b = 0); N % 16 == 0 for SWIGLU, N % 64 == 0 for SWIGLU_MXFP4;
+ *  Requirements: K % 8 == 0 (bf16) or K % 32 == 0 (MX); N % 8 == 0 (bf16
+ *  with trans_b = 0, and MX); N % 16 == 0 for SWIGLU, N % 64 == 0 for
+ *  SWIGLU_MXFP4;
  *  a_scale and b_scale 4-byte aligned (else PT_ERR_MISALIGNED).
  *  workspace  optional (may be NULL); if given and >= 4 bytes its first
  *             32-bit word receives the sticky device error bits.

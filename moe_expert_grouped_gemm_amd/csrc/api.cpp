@@ -118,6 +118,7 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
     }
     if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) {
         if (!trans_b) return PT_ERR_UNSUPPORTED;           // scales run along K
+        if (N % 8) return PT_ERR_UNSUPPORTED;              // outputs leave in 16-byte chunks
         if (K % 32) return PT_ERR_UNSUPPORTED;
         if (M > 0 && (!a_scale || !b_scale)) return PT_ERR_INVALID_ARG;
         if (!aligned4(a_scale) || !aligned4(b_scale)) return PT_ERR_MISALIGNED;

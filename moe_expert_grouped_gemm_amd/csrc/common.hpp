@@ -35,9 +35,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float f)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return bits_f32(h << 16); }
 
+// silu(gate) * up = gate / (1 + e^-gate) * up, with the hardware reciprocal
+// (1 ulp) instead of an IEEE division; 1/inf = 0 gives the limit for very
+// negative gates.
 __device__ __forceinline__ float silu_mul(float gate, float up)
 {
-    return gate / (1.0f + __expf(-gate)) * up;
+    return gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
 }
 
 // ------------------------------------------------------------------ MX encode

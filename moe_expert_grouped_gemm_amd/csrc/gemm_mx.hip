@@ -549,10 +549,18 @@ __device__ __forceinline__ uintx4 wld(uint32_t addr)
     return ldsr_u128<OFF>(addr);
 }
 
+// LDS of the ring or of the epilogue tile, whichever is larger; the group
+// table follows it.
+template <int EPI>
+constexpr int wide_lds_bytes()
+{
+    return 2 * WSTAGE > epi_lds_bytes<EPI, 4>() ? 2 * WSTAGE : epi_lds_bytes<EPI, 4>();
+}
+
 template <int FMT, int EPI, int WSC>
 __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
 {
-    constexpr int GEMM_LDS_BYTES = 2 * WSTAGE;
+    constexpr int GEMM_LDS_BYTES = wide_lds_bytes<EPI>();
     constexpr int MF = FMT == 0 ? 0 : 4;
     constexpr int RB = 32 * WROW;                           // LDS bytes of 32 rows (bi / bj step)
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -801,14 +809,14 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             stage(IC<1>{});
         }
         if (kt0 < nk) stage(IC<0>{});
-        store_out<EPI>(acc, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn);
+        store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn);
     }
 }
 
 template <int FMT, int EPI, int WSC>
 hipError_t launch_wide(const MxParams &p, hipStream_t s)
 {
-    const int lds = 2 * WSTAGE + table_bytes(p.G);
+    const int lds = wide_lds_bytes<EPI>() + table_bytes(p.G);
     auto kern = gg_mx_wide_kernel<FMT, EPI, WSC>;
     static int configured_lds = 0;
     if (configured_lds < lds) {

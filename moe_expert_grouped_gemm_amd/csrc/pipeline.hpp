@@ -217,6 +217,98 @@ __device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], void *out
     }
 }
 
+// Epilogue through LDS, for a tile of 64 * NWM rows computed by NWM x 2
+// waves (the ring is idle by then).  Phase 1: every wave writes its results
+// as bf16 (after SwiGLU when asked) into a row-major LDS tile whose rows are
+// padded by 16 bytes, so the two lane halves (rows 4 apart) of a 2-byte
+// write land on different banks.  Phase 2: whole rows leave as 16-byte
+// stores, or, for MXFP4, each thread encodes one 32-value block held in its
+// own registers (amax, shared E8M0 byte, codes) and stores its 16 code bytes
+// and its scale byte.  Tile columns: kEpiNone 256 (nt * 256 + c), SwiGLU 128
+// outputs (nt * 128 + c, c = wn * 64 + bj * 32 + lane % 32).
+template <int EPI>
+__host__ __device__ constexpr int epi_row_bytes() { return (EPI == kEpiNone ? BN : BN / 2) * 2 + 16; }
+template <int EPI, int NWM>
+__host__ __device__ constexpr int epi_lds_bytes() { return 64 * NWM * epi_row_bytes<EPI>(); }
+
+template <int EPI, int NWM>
+__device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[2][4], uint8_t *smem, void *out,
+                                               uint8_t *out_scale, int ldo, int Nout, int64_t row0, int m0, int rows,
+                                               int nt, int wm, int wn)
+{
+    constexpr int TR = 64 * NWM;                           // tile rows
+    constexpr int OC = EPI == kEpiNone ? BN : BN / 2;      // output columns of the tile
+    constexpr int RS = epi_row_bytes<EPI>();
+    constexpr int NT = NWM * 2 * kWave;
+    const int lane = threadIdx.x & 63;
+    if (EPI == kEpiNone) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+                const int c = wn * 128 + bj * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    *(uint16_t *)(smem + e_row(wm, bi, r) * RS + c * 2) = (uint16_t)bf16_rne(acc[bi][bj][r]);
+            }
+    } else {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj) {
+                const int c = wn * 64 + bj * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    *(uint16_t *)(smem + e_row(wm, bi, r) * RS + c * 2) =
+                        (uint16_t)bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r]));
+            }
+    }
+    __syncthreads();
+    const int ncols = EPI == kEpiNone ? Nout : Nout / 2;   // valid output columns (multiple of 8)
+    if (EPI != kEpiSwigluMxfp4) {
+        constexpr int CPR = OC / 8;                        // 16-byte chunks per row
+        uint16_t *o = (uint16_t *)out + row0 * ldo;
+        for (int i = threadIdx.x; i < TR * CPR; i += NT) {
+            const int r = i / CPR, c = i % CPR;
+            const int col = nt * OC + c * 8;
+            if (m0 + r < rows && col < ncols)
+                *(uintx4 *)(o + (int64_t)(m0 + r) * ldo + col) = *(const uintx4 *)(smem + r * RS + c * 16);
+        }
+    } else {
+        constexpr int BPR = OC / 32;                       // MXFP4 blocks per row
+        uint8_t *o = (uint8_t *)out + row0 * ldo;
+        uint8_t *os = out_scale + row0 * (Nout / 64);
+        for (int i = threadIdx.x; i < TR * BPR; i += NT) {
+            const int r = i / BPR, b = i % BPR;
+            const int j0 = nt * OC + b * 32;
+            if (m0 + r >= rows || j0 >= ncols) continue;
+            uintx4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = *(const uintx4 *)(smem + r * RS + b * 64 + q * 16);
+            uint32_t amax = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) amax = max(amax, max(v[q][e] & 0x7FFFu, (v[q][e] >> 16) & 0x7FFFu));
+            const uint32_t E = mx_scale_byte<2>(amax);
+            uint32_t packed[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    w |= mx_encode<1>(v[q][e] & 0xFFFFu, E) << (8 * e);
+                    w |= mx_encode<1>(v[q][e] >> 16, E) << (8 * e + 4);
+                }
+                packed[q] = w;
+            }
+            *(uintx4 *)(o + (int64_t)(m0 + r) * ldo + (j0 >> 1)) = uintx4{packed[0], packed[1], packed[2], packed[3]};
+            os[(int64_t)(m0 + r) * (Nout / 64) + (j0 >> 5)] = (uint8_t)E;
+        }
+    }
+    __syncthreads();
+}
+
 // Grid of a persistent launch: enough workgroups to fill every CU at the
 // kernel's occupancy, never more than there are tiles, a multiple of the 8
 // XCDs when possible.
