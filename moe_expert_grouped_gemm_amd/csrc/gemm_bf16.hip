@@ -40,6 +40,9 @@ namespace {
 
 constexpr int BK = ROW_BYTES / 2;                  // bf16 reduction depth of a stage
 
+template <int V>
+struct IC { static constexpr int value = V; };
+
 // Wait for the oldest in-flight stage when `after` younger stages (of LOADS
 // loads per thread each; at most NSTAGE - 1) may stay outstanding.
 template <int NSTAGE>
@@ -434,13 +437,371 @@ hipError_t launch_depth(const Bf16Params &p, hipStream_t s)
     }
 }
 
+// ====================================================================== wide
+// The main BF16 kernel: one workgroup of 8 waves per CU (two waves per SIMD)
+// computes 256 x 256 tiles; wave (wm, wn), wm = 0..3, owns 64 x 128 outputs
+// as 2 x 4 blocks of 32 x 32.  A stage carries 64 values of the reduction
+// (four 16-deep MFMA steps): 128-byte rows of a reduction-contiguous operand
+// or 64 rows of 512 bytes of a column-contiguous one, so every direct load
+// fetches whole lines, and a tile moves a third fewer operand bytes per
+// product than 128 x 256.  Two ring slots per operand; the loads of stage
+// kt+1 go out at the start of stage kt and land while it computes.  LDS:
+// [A slot 0 | A slot 1 | B slot 0 | B slot 1], 32 KiB each, so slot and k-step
+// offsets fit the 16-bit immediates of the fragment reads.
+//  - reduction-contiguous: [256 rows][128 B], chunk c of row r at position
+//    c ^ (r & 7); the chunk 2j + h a lane reads is at base ^ (j << 5);
+//  - column-contiguous: [64 k][512 B], chunk c of k-row k at c ^ ((k & 3) << 2),
+//    read with ds_read_b64_tr_b16 (four k values of one column per lane).
+constexpr int WBM = 256, WBN = 256, WTHREADS = 512;
+constexpr int WSLOT = 32768;                           // one operand's stage
+constexpr int WB_REGION = 2 * WSLOT;                   // B slots start here
+constexpr int WRING = 4 * WSLOT;
+constexpr int W_LOADS = WSLOT / 16 / WTHREADS;         // per operand per thread per stage (4)
+constexpr int WK = 64;                                 // reduction values per stage
+
+template <int EPI>
+constexpr int wide_lds_bytes()
+{
+    return WRING > epi_lds_bytes<EPI, 4>() ? WRING : epi_lds_bytes<EPI, 4>();
+}
+
+// One operand's loads of a tile: W_LOADS per thread per stage, all at one
+// per-thread offset plus wave-uniform distances; stage kt starts kt * kstep
+// bytes further on.  `chunk` (reduction-contiguous only) is the byte offset
+// of the thread's chunk inside a stage row, for the partial last stage.
+struct WOp {
+    const void *base;
+    uint32_t bytes;
+    uint32_t voff;
+    uint32_t delta[W_LOADS];
+    uint32_t kstep;
+    int chunk;
+};
+
+// Issue one operand's loads of stage kt into LDS at `lds` (slot base).
+// Branch-free: a stage past the end, and in a partial last stage a chunk of
+// a reduction-contiguous row at or past the reduction length, get an offset
+// past the bound; rows of a column-contiguous stage past the reduction
+// length lie past the operand's bound already.
+template <bool KCONTIG>
+__device__ __forceinline__ void wissue(uint8_t *lds, const WOp &o, int kt, int nk, int Kred, int wave)
+{
+    bool ok = kt < nk;
+    if (KCONTIG) ok = ok && kt * WK + o.chunk / 2 < Kred;
+    const uint32_t v = ok ? o.voff + (uint32_t)kt * o.kstep : kOOB;
+    uint8_t *d = lds + wave * kWave * 16;
+#pragma unroll
+    for (int i = 0; i < W_LOADS; ++i) dma16(o.base, o.bytes, d + i * WTHREADS * 16, v, o.delta[i]);
+}
+
+__device__ __forceinline__ void wfrag_wait(bf16x8 (&a)[2], bf16x8 (&b)[4]) { frag_wait(a, b); }
+
+template <int KIND, int EPI>
+__global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
+{
+    constexpr int LDS_BYTES = wide_lds_bytes<EPI>();
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    GroupTable tab;
+    tab.G = p.G;
+    int *tb = (int *)(smem + LDS_BYTES);
+    tab.row0 = tb;
+    tab.rows = tb + p.G;
+    tab.tile0 = tb + 2 * p.G;
+    int *s_scan = tab.tile0 + p.G + 1;
+    int total;
+    if (KIND == kWgrad)
+        total = build_group_table<TilesWgrad, WTHREADS>(tab, p.lens, p.offs, p.G, p.M,
+                                                        TilesWgrad{p.tilesM * p.tilesN, p.accumulate}, p.err, s_scan);
+    else
+        total = build_group_table<TilesFwd, WTHREADS>(tab, p.lens, p.offs, p.G, p.M, TilesFwd{WBM, p.tilesN}, p.err,
+                                                      s_scan);
+    total = __builtin_amdgcn_readfirstlane(total);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t lds0 = lds_addr(smem);
+    const int r32 = lane & 31, h = lane >> 5, g16 = (lane >> 4) & 1, s16 = lane & 15;
+
+    // ---- per-lane fragment bases (slot 0; slot 1 is + WSLOT by immediate)
+    // reduction-contiguous: chunk 2j + h of the lane's first row at base ^ (j << 5)
+    const uint32_t y = (uint32_t)((h ^ (r32 & 7)) & 1) * 16u | (uint32_t)((r32 & 6) << 4);
+    const uint32_t aK = lds0 + (uint32_t)(wm * 64 + r32) * 128u + y;
+    const uint32_t bK = lds0 + WB_REGION + (uint32_t)(wn * 128 + r32) * 128u + y;
+    // column-contiguous: transposing reads of k-rows h*8 + s16/4 (+4), columns
+    // 16 g16 + 4 (s16 & 3) of each 32-column block
+    uint32_t aN[2], bN[4];
+    {
+        const int krow = h * 8 + (s16 >> 2);
+        const int lo = 8 * (s16 & 1);
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+            const int col = wm * 64 + bi * 32 + 16 * g16 + 4 * (s16 & 3);
+            aN[bi] = lds0 + krow * 512 + npos(krow, col >> 3) * 16 + lo;
+        }
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const int col = wn * 128 + bj * 32 + 16 * g16 + 4 * (s16 & 3);
+            bN[bj] = lds0 + WB_REGION + krow * 512 + npos(krow, col >> 3) * 16 + lo;
+        }
+    }
+    // ---- per-thread load slots: reduction-contiguous row i*64 + t/8, chunk
+    // (t & 7) ^ ((t >> 3) & 7); column-contiguous k-row i*16 + t/32, chunk
+    // (t & 31) ^ (((t >> 5) & 3) << 2)
+    const int kc_row = tid >> 3, kc_chunk = (tid & 7) ^ ((tid >> 3) & 7);
+    const int nc_row = tid >> 5, nc_chunk = (tid & 31) ^ (((tid >> 5) & 3) << 2);
+
+    for (int tile = xcd_logical_id(); tile < total; tile += gridDim.x) {
+        const int g = __builtin_amdgcn_readfirstlane(find_group(tab, tile));
+        const int local = tile - __builtin_amdgcn_readfirstlane(tab.tile0[g]);
+        const int row0 = __builtin_amdgcn_readfirstlane(tab.row0[g]);
+        const int rows = __builtin_amdgcn_readfirstlane(tab.rows[g]);
+        int mt, nt;
+        if (KIND == kWgrad) {
+            mt = local / p.tilesN;
+            nt = local % p.tilesN;
+        } else {
+            const int tm = (rows + WBM - 1) / WBM;
+            nt = local / tm;
+            mt = local % tm;
+        }
+        const int m0 = mt * WBM;
+        const int Kred = (KIND == kWgrad) ? rows : p.Kred;
+        const int nk = (Kred + WK - 1) / WK;
+        int nvalid_bi = 2;
+        if (KIND != kWgrad) {
+            const int vr = min(WBM, rows - m0) - wm * 64;
+            nvalid_bi = vr <= 0 ? 0 : (vr > 32 ? 2 : 1);
+        }
+
+        WOp oa, ob;
+        if (KIND == kWgrad) {
+            // [token][i] and [token][j] slices of the expert: column-contiguous
+            oa.base = p.a + (int64_t)row0 * p.lda;
+            oa.bytes = (uint32_t)rows * p.lda * 2;
+            oa.voff = (uint32_t)(nc_row * p.lda + min(m0 + nc_chunk * 8, p.Mout - 8)) * 2;
+            ob.base = p.b + (int64_t)row0 * p.ldb;
+            ob.bytes = (uint32_t)rows * p.ldb * 2;
+            ob.voff = (uint32_t)(nc_row * p.ldb + min(nt * WBN + nc_chunk * 8, p.Nout - 8)) * 2;
+#pragma unroll
+            for (int i = 0; i < W_LOADS; ++i) {
+                oa.delta[i] = (uint32_t)(i * 16 * p.lda) * 2;
+                ob.delta[i] = (uint32_t)(i * 16 * p.ldb) * 2;
+            }
+            oa.kstep = (uint32_t)WK * p.lda * 2;
+            ob.kstep = (uint32_t)WK * p.ldb * 2;
+        } else {
+            // A: the expert's rows, reduction-contiguous; rows past its end read zeros
+            oa.base = p.a + (int64_t)row0 * p.lda;
+            oa.bytes = (uint32_t)rows * p.lda * 2;
+            oa.voff = (uint32_t)(m0 + kc_row) * p.lda * 2 + kc_chunk * 16;
+#pragma unroll
+            for (int i = 0; i < W_LOADS; ++i) oa.delta[i] = (uint32_t)(i * 64 * p.lda) * 2;
+            oa.kstep = WK * 2;
+            oa.chunk = kc_chunk * 16;
+            const uint16_t *Bg = p.b + (int64_t)g * p.b_gstride;
+            ob.base = Bg;
+            if (KIND == kFwdKContig) {
+                // tile rows i*64 + t/8: B rows col_of(i*64 + t/8); with SwiGLU
+                // the 64-row groups are gate j, up I+j, gate j+64, up I+j+64
+                ob.bytes = (uint32_t)p.Nout * p.ldb * 2;
+                const int n0 = col_of<EPI>(nt, kc_row, p.Nout);
+                ob.voff = (uint32_t)n0 * p.ldb * 2 + kc_chunk * 16;
+#pragma unroll
+                for (int i = 0; i < W_LOADS; ++i)
+                    ob.delta[i] = (uint32_t)(col_of<EPI>(nt, i * 64, p.Nout) - col_of<EPI>(nt, 0, p.Nout)) * p.ldb * 2;
+                ob.kstep = WK * 2;
+                ob.chunk = kc_chunk * 16;
+            } else {
+                ob.bytes = (uint32_t)p.Kred * p.ldb * 2;
+                const int n = clamp8<EPI>(col_of<EPI>(nt, nc_chunk * 8, p.Nout), p.Nout);
+                ob.voff = (uint32_t)(nc_row * p.ldb + n) * 2;
+#pragma unroll
+                for (int i = 0; i < W_LOADS; ++i) ob.delta[i] = (uint32_t)(i * 16 * p.ldb) * 2;
+                ob.kstep = (uint32_t)WK * p.ldb * 2;
+            }
+        }
+
+        // Accumulators start at zero, or for an accumulating wgrad at the
+        // main_grad tile itself (loads overlap the operand prologue).
+        floatx16 acc[2][4];
+        if (KIND == kWgrad && p.accumulate) {
+            const float *og = (const float *)p.out + (int64_t)g * p.o_gstride;
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) {
+                    const int n = nt * WBN + wn * 128 + bj * 32 + (lane & 31);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = m0 + e_row(wm, bi, r);
+                        acc[bi][bj][r] = (n < p.Nout && i < p.Mout) ? og[(int64_t)i * p.ldo + n] : 0.0f;
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        }
+
+        auto issue_stage = [&](int kt, int slot) {
+            wissue<KIND != kWgrad>(smem + slot * WSLOT, oa, kt, nk, Kred, wave);
+            wissue<KIND == kFwdKContig>(smem + WB_REGION + slot * WSLOT, ob, kt, nk, Kred, wave);
+        };
+        // fragments of k-step KS of slot P
+        auto rd = [&](auto KSC, auto PC, bf16x8 (&af)[2], bf16x8 (&bf)[4]) {
+            constexpr int KS = decltype(KSC)::value, P = decltype(PC)::value;
+            constexpr int SO = P * WSLOT;
+            constexpr int NO = SO + KS * 16 * 512, NJ = 4 * 512;     // column-contiguous k-step, +4 k-rows
+            if constexpr (KIND == kWgrad) {
+                af[0] = join(ldsr_tr<NO>(aN[0]), ldsr_tr<NO + NJ>(aN[0]));
+                af[1] = join(ldsr_tr<NO>(aN[1]), ldsr_tr<NO + NJ>(aN[1]));
+            } else {
+                const uint32_t x = aK ^ (uint32_t)(KS << 5);
+                af[0] = ldsr_b128<SO>(x);
+                af[1] = ldsr_b128<SO + 32 * 128>(x);
+            }
+            if constexpr (KIND == kFwdKContig) {
+                const uint32_t x = bK ^ (uint32_t)(KS << 5);
+                bf[0] = ldsr_b128<SO + 0 * 32 * 128>(x);
+                bf[1] = ldsr_b128<SO + 1 * 32 * 128>(x);
+                bf[2] = ldsr_b128<SO + 2 * 32 * 128>(x);
+                bf[3] = ldsr_b128<SO + 3 * 32 * 128>(x);
+            } else {
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) bf[bj] = join(ldsr_tr<NO>(bN[bj]), ldsr_tr<NO + NJ>(bN[bj]));
+            }
+        };
+        auto mma = [&](const bf16x8 (&af)[2], const bf16x8 (&bf)[4]) {
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+                if (bi < nvalid_bi) {
+#pragma unroll
+                    for (int bj = 0; bj < 4; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
+                }
+        };
+
+        // prologue: stage 0
+        issue_stage(0, 0);
+        wait_vmcnt<0>();
+        barrier();
+        bf16x8 fa[2][2], fb[2][4];
+        rd(IC<0>{}, IC<0>{}, fa[0], fb[0]);
+        wfrag_wait(fa[0], fb[0]);
+
+        int kt0 = 0;
+        auto stage = [&](auto PC) {
+            constexpr int P = decltype(PC)::value, Q = P ^ 1;
+            const int kt = kt0 + P;
+            issue_stage(kt + 1, Q);          // the other slot, free since the barrier
+            rd(IC<1>{}, PC, fa[1], fb[1]);
+            mma(fa[0], fb[0]);
+            wfrag_wait(fa[1], fb[1]);
+            rd(IC<2>{}, PC, fa[0], fb[0]);
+            mma(fa[1], fb[1]);
+            wfrag_wait(fa[0], fb[0]);
+            rd(IC<3>{}, PC, fa[1], fb[1]);
+            mma(fa[0], fb[0]);
+            wfrag_wait(fa[1], fb[1]);
+            mma(fa[1], fb[1]);
+            // stage kt+1 landed for this wave, after the barrier for all
+            // waves, and every wave is done reading slot P
+            wait_vmcnt<0>();
+            barrier();
+            if (kt + 1 < nk) {
+                rd(IC<0>{}, IC<Q>{}, fa[0], fb[0]);
+                wfrag_wait(fa[0], fb[0]);
+            }
+        };
+        // whole pairs of slots, then the last stage: no early exit, so the
+        // compiler sees no path between slots that skips a stage's loads
+        for (; kt0 + 2 <= nk; kt0 += 2) {
+            stage(IC<0>{});
+            stage(IC<1>{});
+        }
+        if (kt0 < nk) stage(IC<0>{});
+
+        if (KIND == kWgrad) {
+            // nothing outstanding here; saying so keeps the compiler from
+            // waiting for every earlier store before each one
+            wait_vmcnt<0>();
+            float *og = (float *)p.out + (int64_t)g * p.o_gstride;
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) {
+                    const int n = nt * WBN + wn * 128 + bj * 32 + (lane & 31);
+                    if (n >= p.Nout) continue;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = m0 + e_row(wm, bi, r);
+                        if (i < p.Mout) og[(int64_t)i * p.ldo + n] = acc[bi][bj][r];
+                    }
+                }
+        } else {
+            store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wm, wn);
+        }
+    }
+}
+
+template <int KIND, int EPI>
+hipError_t launch_wide(const Bf16Params &p, hipStream_t s)
+{
+    const int lds = wide_lds_bytes<EPI>() + table_bytes(p.G);
+    auto kern = gg_bf16_wide_kernel<KIND, EPI>;
+    static int configured_lds = 0;
+    if (configured_lds < lds) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        configured_lds = lds;
+    }
+    int occ = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, WTHREADS, lds);
+    if (e != hipSuccess) return e;
+    int64_t tiles_max;
+    if (KIND == kWgrad)
+        tiles_max = (int64_t)p.G * p.tilesM * p.tilesN;
+    else
+        tiles_max = (p.M / WBM + p.G) * (int64_t)p.tilesN;
+    const int64_t grid = persistent_grid(occ, tiles_max);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WTHREADS), lds, s, p);
+    return hipGetLastError();
+}
+
+// Which BF16 mainloop runs: PTGG_BF16_TILE=128 selects the 128 x 256
+// kernel (a tuning knob for experiments; results do not depend on it).
+bool bf16_narrow()
+{
+    static const bool narrow = [] {
+        const char *e = getenv("PTGG_BF16_TILE");
+        return e && atoi(e) == 128;
+    }();
+    return narrow;
+}
+
 }  // namespace
 
-int bf16_tile_m() { return BM; }
+int bf16_tile_m() { return bf16_narrow() ? BM : WBM; }
 int bf16_tile_n() { return BN; }
 
 hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s)
 {
+    if (!bf16_narrow()) {
+        if (kind == kWgrad) return launch_wide<kWgrad, kEpiNone>(p, s);
+        if (kind == kFwdKContig) {
+            if (epi == kEpiSwiglu) return launch_wide<kFwdKContig, kEpiSwiglu>(p, s);
+            if (epi == kEpiSwigluMxfp4) return launch_wide<kFwdKContig, kEpiSwigluMxfp4>(p, s);
+            return launch_wide<kFwdKContig, kEpiNone>(p, s);
+        }
+        if (epi == kEpiSwiglu) return launch_wide<kFwdNContig, kEpiSwiglu>(p, s);
+        if (epi == kEpiSwigluMxfp4) return launch_wide<kFwdNContig, kEpiSwigluMxfp4>(p, s);
+        return launch_wide<kFwdNContig, kEpiNone>(p, s);
+    }
     if (kind == kWgrad) return launch_depth<kWgrad, kEpiNone>(p, s);
     if (kind == kFwdKContig) {
         if (epi == kEpiSwiglu) return launch_depth<kFwdKContig, kEpiSwiglu>(p, s);
