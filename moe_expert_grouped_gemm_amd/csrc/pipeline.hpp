@@ -306,7 +306,11 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[2][4], uint
             os[(int64_t)(m0 + r) * (Nout / 64) + (j0 >> 5)] = (uint8_t)E;
         }
     }
-    __syncthreads();
+    // The next tile's loads may overwrite the LDS tile once every wave has
+    // read it; the stores stay in flight (__syncthreads() would wait for
+    // their acknowledgement, since vmcnt counts stores too).
+    wait_lgkm0();
+    barrier();
 }
 
 // Grid of a persistent launch: enough workgroups to fill every CU at the
