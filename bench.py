@@ -116,6 +116,16 @@ def summary(name, dtype, flops, nbytes, per_ms, extra=None):
 
 
 # ------------------------------------------------------------------ workloads
+# One workspace for every GEMM call: the error word and the tile queues
+# (calls on one stream run one after another, so they can share it).
+WS = [None]
+
+
+def make_workspace(dev):
+    n = ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 1, 1, 1, 1, ptm.PT_BF16)
+    WS[0] = torch.zeros(n, dtype=torch.uint8, device=dev)
+
+
 def fc1_inputs(dev):
     lens = synth.lens_topk_gaussian(8192, 256, 6, seed=1)
     G, M, K, N = 256, int(lens.sum()), 4096, 4096
@@ -172,7 +182,7 @@ def bench_fc1(dev, stream, steps, warmup):
 
     def step():
         ptm.pt_grouped_gemm_fwd(a, None, b, None, out, None, lens_d, None, G, M, N, K,
-                                ptm.PT_BF16, 0, ptm.PT_EPI_SWIGLU, stream=stream)
+                                ptm.PT_BF16, 0, ptm.PT_EPI_SWIGLU, workspace=WS[0], stream=stream)
 
     ms_step, per = time_launches(step, steps, warmup, stream)
     flops = 2.0 * M * K * N
@@ -190,7 +200,7 @@ def bench_cfg0(dev, stream, iters):
     lens_d = torch.as_tensor(lens, device=dev)
     _, per = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
         a, None, b, None, out, None, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, ptm.PT_EPI_NONE,
-        stream=stream), iters, 10, stream)
+        workspace=WS[0], stream=stream), iters, 10, stream)
     flops = 2.0 * M * K * N
     nbytes = bytes_weights(lens, K * N * 2) + M * K * 2 + M * N * 2
     return summary("tiny BF16 fwd, 4 experts, M=256, K=128, N=256", "bf16", flops, nbytes, per)
@@ -202,7 +212,7 @@ def bench_cfg2(dev, stream, iters, fc1):
     dy = synth.randn_bf16((M, N), seed=102, std=1e-2, device=dev)
     dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     _, per_d = time_launches(lambda: ptm.pt_grouped_gemm_dgrad(
-        dy, None, b, None, dx, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, stream=stream), iters, 2, stream)
+        dy, None, b, None, dx, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, workspace=WS[0], stream=stream), iters, 2, stream)
     flops = 2.0 * M * K * N
     d = summary("BF16 dgrad, 256 experts, M=49152, K=N=4096", "bf16", flops,
                 bytes_weights(lens, K * N * 2) + M * N * 2 + M * K * 2, per_d)
@@ -211,7 +221,7 @@ def bench_cfg2(dev, stream, iters, fc1):
     g.manual_seed(103)
     mg = torch.randn((G, K, N), generator=g, device=dev, dtype=torch.float32).mul_(1e-3)
     _, per_w = time_launches(lambda: ptm.pt_grouped_gemm_wgrad(
-        a, None, dy, None, mg, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, 1, stream=stream), iters, 2, stream)
+        a, None, dy, None, mg, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, 1, workspace=WS[0], stream=stream), iters, 2, stream)
     w = summary("BF16 wgrad accumulated into fp32 main_grad [256, 4096, 4096]", "bf16", flops,
                 bytes_weights(lens, K * N * 4 * 2) + M * K * 2 + M * N * 2, per_w)
     del mg, dy
@@ -237,7 +247,7 @@ def bench_cfg3(dev, stream, iters):
     lens_d = torch.as_tensor(lens, device=dev)
     _, per = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
         aq, as_, bq, bs, out, None, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, 1, ptm.PT_EPI_NONE,
-        stream=stream), iters, 3, stream)
+        workspace=WS[0], stream=stream), iters, 3, stream)
     flops = 2.0 * M * K * N
     nbytes = bytes_weights(lens, N * K + N * K // 32) + M * K + M * K // 32 + M * N * 2
     f = summary("MXFP8 fwd, 32 experts (Zipf 1.1), M=65536, K=2880, N=5760", "mxfp8", flops, nbytes, per,
@@ -268,9 +278,9 @@ def bench_cfg4(dev, stream, iters, lens):
     def mlp():
         ptm.pt_mx_quantize(x, xq, xs, M, H, ptm.PT_MXFP4_E2M1, 1, stream=stream)
         ptm.pt_grouped_gemm_fwd(xq, xs, w1q, w1s, hq, hs, lens_d, None, G, M, 2 * I, H,
-                                ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_SWIGLU_MXFP4, stream=stream)
+                                ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_SWIGLU_MXFP4, workspace=WS[0], stream=stream)
         ptm.pt_grouped_gemm_fwd(hq, hs, w2q, w2s, out, None, lens_d, None, G, M, H, I,
-                                ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_NONE, stream=stream)
+                                ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_NONE, workspace=WS[0], stream=stream)
 
     _, per = time_launches(mlp, iters, 3, stream)
     flops = 2.0 * M * H * 2 * I + 2.0 * M * I * H
@@ -303,6 +313,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     ptm.load()
+    make_workspace(dev)
     stream = torch.cuda.current_stream()
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20

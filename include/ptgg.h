@@ -110,8 +110,8 @@ typedef enum {
  *  with trans_b = 0, and MX); N % 16 == 0 for SWIGLU, N % 64 == 0 for
  *  SWIGLU_MXFP4;
  *  a_scale and b_scale 4-byte aligned (else PT_ERR_MISALIGNED).
- *  workspace  optional (may be NULL); if given and >= 4 bytes its first
- *             32-bit word receives the sticky device error bits.
+ *  workspace  optional (may be NULL): the error word and tile queues, see
+ *             pt_grouped_gemm_workspace_size.
  */
 int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale,
                         const void *b, const uint8_t *b_scale,
@@ -151,8 +151,7 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale,
  *  main_grad  trans_out = 0: [G, K, N];  trans_out = 1: [G, N, K]  (fp32)
  *  An expert with no rows leaves its main_grad slice untouched when
  *  accumulating and writes zeros when not.
- *  workspace: pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ...) bytes (may be
- *  0, in which case workspace may be NULL).
+ *  workspace  optional (may be NULL), see pt_grouped_gemm_workspace_size.
  *  Requirements: K % 8 == 0, N % 8 == 0; dtype PT_BF16.
  */
 int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
@@ -182,7 +181,22 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
 int pt_mx_quantize(const void *x, void *q, uint8_t *scales,
                    int64_t rows, int64_t cols, int dtype, int axis, void *stream);
 
-/* Bytes of workspace `op` needs for these sizes (0 when none). */
+/*
+ * Workspace of the grouped GEMMs (optional, for every op; recommended):
+ * pt_grouped_gemm_workspace_size() bytes of device memory, 4-byte aligned.
+ *  - word 0 receives the sticky device error bits (pt_read_error_flags);
+ *    a workspace of at least 4 bytes is enough for that alone;
+ *  - a workspace of the full size also holds the tile queues: every call
+ *    then first zeroes them on `stream` (a one-wave kernel) and the GEMM's
+ *    persistent workgroups take their tiles from them, in an order that
+ *    keeps the workgroups sharing an expert's rows close together in time.
+ *    Without them the tiles go in a fixed round-robin order.  Results are
+ *    bit-identical either way.
+ * The library keeps nothing in the workspace between calls; calls that may
+ * run concurrently (on different streams) need separate workspaces.  Its
+ * contents on entry do not matter.
+ */
+/* Bytes of workspace `op` needs for these sizes. */
 size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N,
                                       int64_t K, int dtype);
 

@@ -60,6 +60,24 @@ int check_groups(const int64_t *lens, int64_t G, int64_t M)
 
 uint32_t *error_word(void *ws, size_t bytes) { return (ws && bytes >= 4) ? (uint32_t *)ws : nullptr; }
 
+// The tile-queue counters, when the workspace has room for them; without
+// them the persistent kernels take tiles in a static order.
+uint32_t *queue_words(void *ws, size_t bytes)
+{
+    return (ws && bytes >= (size_t)kQueueWsBytes) ? (uint32_t *)((uint8_t *)ws + kQueueWsOffset) : nullptr;
+}
+
+// Zero the queues (if any) ahead of the launch on the same stream.
+template <class Launch>
+hipError_t queued(uint32_t *sched, hipStream_t s, Launch launch)
+{
+    if (sched) {
+        hipError_t e = launch_queue_reset(sched, s);
+        if (e != hipSuccess) return e;
+    }
+    return launch();
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? PT_OK : PT_ERR_HIP; }
 
 }  // namespace
@@ -113,8 +131,9 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
         p.ldo = (int)ldo;
         p.tilesN = (int)((Nc + (epilogue == PT_EPI_NONE ? bf16_tile_n() : bf16_tile_n() / 2) - 1) /
                          (epilogue == PT_EPI_NONE ? bf16_tile_n() : bf16_tile_n() / 2));
+        p.sched = queue_words(workspace, workspace_bytes);
         if (M == 0) return PT_OK;
-        return hip_status(launch_bf16(p, trans_b ? kFwdKContig : kFwdNContig, ep, s));
+        return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdKContig : kFwdNContig, ep, s); }));
     }
     if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) {
         if (!trans_b) return PT_ERR_UNSUPPORTED;           // scales run along K
@@ -141,8 +160,9 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
         p.ldo = (int)ldo;
         const int tn = epilogue == PT_EPI_NONE ? mx_tile_n() : mx_tile_n() / 2;
         p.tilesN = (int)((Nc + tn - 1) / tn);
+        p.sched = queue_words(workspace, workspace_bytes);
         if (M == 0) return PT_OK;
-        return hip_status(launch_mx(p, dtype == PT_MXFP8_E4M3 ? 0 : 1, ep, s));
+        return hip_status(queued(p.sched, s, [&] { return launch_mx(p, dtype == PT_MXFP8_E4M3 ? 0 : 1, ep, s); }));
     }
     return PT_ERR_UNSUPPORTED;
 }
@@ -179,8 +199,10 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
     p.b_gstride = N * K;
     p.ldo = (int)K;
     p.tilesN = (int)((K + bf16_tile_n() - 1) / bf16_tile_n());
+    p.sched = queue_words(workspace, workspace_bytes);
     if (M == 0) return PT_OK;
-    return hip_status(launch_bf16(p, trans_b ? kFwdNContig : kFwdKContig, kEpiNone, (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdNContig : kFwdKContig, kEpiNone, s); }));
 }
 
 int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy, const uint8_t *dy_scale,
@@ -220,8 +242,10 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
     p.tilesM = (p.Mout + bf16_tile_m() - 1) / bf16_tile_m();
     p.tilesN = (p.Nout + bf16_tile_n() - 1) / bf16_tile_n();
     p.accumulate = accumulate;
+    p.sched = queue_words(workspace, workspace_bytes);
     if (M == 0 && accumulate) return PT_OK;
-    return hip_status(launch_bf16(p, kWgrad, kEpiNone, (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, kWgrad, kEpiNone, s); }));
 }
 
 int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_t cols, int dtype, int axis,
@@ -242,7 +266,7 @@ int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_
 size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, int64_t K, int dtype)
 {
     (void)op; (void)G; (void)M; (void)N; (void)K; (void)dtype;
-    return 256;   // the error word, rounded up to one allocation granule
+    return kQueueWsBytes;   // the error word, then the tile-queue counters
 }
 
 int pt_read_error_flags(const void *workspace, void *stream, uint32_t *flags)

@@ -484,14 +484,19 @@ struct WOp {
 // past the bound; rows of a column-contiguous stage past the reduction
 // length lie past the operand's bound already.
 template <bool KCONTIG>
-__device__ __forceinline__ void wissue(uint8_t *lds, const WOp &o, int kt, int nk, int Kred, int wave)
+__device__ __forceinline__ void wissue(uint8_t *lds, const WOp &o, int kt, int nk, int Kred, int wave, bool once = false)
 {
     bool ok = kt < nk;
     if (KCONTIG) ok = ok && kt * WK + o.chunk / 2 < Kred;
     const uint32_t v = ok ? o.voff + (uint32_t)kt * o.kstep : kOOB;
     uint8_t *d = lds + wave * kWave * 16;
+    if (once) {
 #pragma unroll
-    for (int i = 0; i < W_LOADS; ++i) dma16(o.base, o.bytes, d + i * WTHREADS * 16, v, o.delta[i]);
+        for (int i = 0; i < W_LOADS; ++i) dma16_nt(o.base, o.bytes, d + i * WTHREADS * 16, v, o.delta[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < W_LOADS; ++i) dma16(o.base, o.bytes, d + i * WTHREADS * 16, v, o.delta[i]);
+    }
 }
 
 __device__ __forceinline__ void wfrag_wait(bf16x8 (&a)[2], bf16x8 (&b)[4]) { frag_wait(a, b); }
@@ -516,6 +521,11 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         total = build_group_table<TilesFwd, WTHREADS>(tab, p.lens, p.offs, p.G, p.M, TilesFwd{WBM, p.tilesN}, p.err,
                                                       s_scan);
     total = __builtin_amdgcn_readfirstlane(total);
+    // the scan scratch is free once the table is built: it passes tile ids
+    TileQueue tq;
+    tq.init(p.sched, total);
+    int *s_id = s_scan;
+    int par = 0;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -552,12 +562,15 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
     const int kc_row = tid >> 3, kc_chunk = (tid & 7) ^ ((tid >> 3) & 7);
     const int nc_row = tid >> 5, nc_chunk = (tid & 31) ^ (((tid >> 5) & 3) << 2);
 
-    for (int tile = xcd_logical_id(); tile < total; tile += gridDim.x) {
+    for (int tile = tq.first(s_id); tile < total;) {
         const int g = __builtin_amdgcn_readfirstlane(find_group(tab, tile));
         const int local = tile - __builtin_amdgcn_readfirstlane(tab.tile0[g]);
         const int row0 = __builtin_amdgcn_readfirstlane(tab.row0[g]);
         const int rows = __builtin_amdgcn_readfirstlane(tab.rows[g]);
         int mt, nt;
+        // the weight panel of an expert that fits one row block is read by
+        // this tile alone
+        bool b_once = false;
         if (KIND == kWgrad) {
             mt = local / p.tilesN;
             nt = local % p.tilesN;
@@ -565,6 +578,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             const int tm = (rows + WBM - 1) / WBM;
             nt = local / tm;
             mt = local % tm;
+            b_once = tm == 1;
         }
         const int m0 = mt * WBM;
         const int Kred = (KIND == kWgrad) ? rows : p.Kred;
@@ -650,7 +664,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 
         auto issue_stage = [&](int kt, int slot) {
             wissue<KIND != kWgrad>(smem + slot * WSLOT, oa, kt, nk, Kred, wave);
-            wissue<KIND == kFwdKContig>(smem + WB_REGION + slot * WSLOT, ob, kt, nk, Kred, wave);
+            wissue<KIND == kFwdKContig>(smem + WB_REGION + slot * WSLOT, ob, kt, nk, Kred, wave, b_once);
         };
         // fragments of k-step KS of slot P
         auto rd = [&](auto KSC, auto PC, bf16x8 (&af)[2], bf16x8 (&bf)[4]) {
@@ -686,9 +700,13 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 }
         };
 
-        // prologue: stage 0
+        // prologue: stage 0, and the id of the next tile (its atomic goes
+        // out first and lands under the stage's loads)
+        if (tid == 0) tq.issue();
         issue_stage(0, 0);
         wait_vmcnt<0>();
+        if (tid == 0) s_id[par ^ 1] = tq.resolve(tile);
+        wait_lgkm0();
         barrier();
         bf16x8 fa[2][2], fb[2][4];
         rd(IC<0>{}, IC<0>{}, fa[0], fb[0]);
@@ -746,6 +764,9 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         } else {
             store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wm, wn);
         }
+        barrier();
+        tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
+        par ^= 1;
     }
 }
 
@@ -773,6 +794,12 @@ hipError_t launch_wide(const Bf16Params &p, hipStream_t s)
     return hipGetLastError();
 }
 
+__global__ void queue_reset_kernel(uint32_t *sched)
+{
+    const int i = threadIdx.x;
+    if (i < kQueues) __hip_atomic_store(sched + i * kQueueStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Which BF16 mainloop runs: PTGG_BF16_TILE=128 selects the 128 x 256
 // kernel (a tuning knob for experiments; results do not depend on it).
 bool bf16_narrow()
@@ -788,6 +815,12 @@ bool bf16_narrow()
 
 int bf16_tile_m() { return bf16_narrow() ? BM : WBM; }
 int bf16_tile_n() { return BN; }
+
+hipError_t launch_queue_reset(uint32_t *sched, hipStream_t s)
+{
+    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(kWave), 0, s, sched);
+    return hipGetLastError();
+}
 
 hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s)
 {

@@ -523,6 +523,7 @@ struct WOps {
     uint32_t adelta[W_LOADS];       // row distances of loads 0..3 (bytes)
     uint32_t bdelta[W_LOADS];
     uint32_t chunk;
+    bool b_once;                    // weights read by this tile alone: non-temporal
 };
 
 // Issue the operand loads of stage kt into ring slot st (branch-free: a
@@ -538,8 +539,13 @@ __device__ __forceinline__ void wissue_stage(uint8_t *smem, const WOps &o, uint3
     uint8_t *lds = smem + st + wave * kWave * 16;
 #pragma unroll
     for (int i = 0; i < W_LOADS; ++i) dma16(o.a, o.abytes, lds + i * WTHREADS * 16, va, o.adelta[i]);
+    if (o.b_once) {
 #pragma unroll
-    for (int i = 0; i < W_LOADS; ++i) dma16(o.b, o.bbytes, lds + WA_BYTES + i * WTHREADS * 16, vb, o.bdelta[i]);
+        for (int i = 0; i < W_LOADS; ++i) dma16_nt(o.b, o.bbytes, lds + WA_BYTES + i * WTHREADS * 16, vb, o.bdelta[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < W_LOADS; ++i) dma16(o.b, o.bbytes, lds + WA_BYTES + i * WTHREADS * 16, vb, o.bdelta[i]);
+    }
 }
 
 // 16-byte LDS read at a run-time address plus immediate OFF (bi / bj rows).
@@ -574,6 +580,11 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
     int total = build_group_table<TilesFwd, WTHREADS>(tab, p.lens, p.offs, p.G, p.M, TilesFwd{WBM, p.tilesN}, p.err,
                                                       s_scan);
     total = __builtin_amdgcn_readfirstlane(total);
+    // the scan scratch is free once the table is built: it passes tile ids
+    TileQueue tq;
+    tq.init(p.sched, total);
+    int *s_id = s_scan;
+    int par = 0;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -601,7 +612,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         }
     }
 
-    for (int tile = xcd_logical_id(); tile < total; tile += gridDim.x) {
+    for (int tile = tq.first(s_id); tile < total;) {
         const int g = __builtin_amdgcn_readfirstlane(find_group(tab, tile));
         const int local = tile - __builtin_amdgcn_readfirstlane(tab.tile0[g]);
         const int row0 = __builtin_amdgcn_readfirstlane(tab.row0[g]);
@@ -615,6 +626,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         // ---- operand loads: slot i * 512 + t holds chunk c = (t & 7) ^ ((t >> 3) & 7)
         // of tile row i * 64 + t / 8
         WOps o;
+        o.b_once = tm == 1;      // an expert within one row block: no other tile reads its weights
         o.a = p.a + (int64_t)row0 * Kb;
         o.abytes = (uint32_t)rows * Kb;
         o.b = p.b + (int64_t)g * p.N * Kb;
@@ -663,12 +675,18 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                 a, b, acc[bi][bj], MF, MF, 0, wscale_of<WSC>(w, bi, s, sh), 0, wscale_of<WSC>(w, 2 + bj, s, sh));
         };
 
-        // prologue: stage 0 (the loads of each stage form one group in program order)
+        // prologue: stage 0 (the loads of each stage form one group in
+        // program order), and the id of the next tile (its atomic goes out
+        // first and lands under the stage's loads)
         uint32_t sc[2][6];
+        if (tid == 0) tq.issue();
+        asm volatile("" ::: "memory");
         wissue_stage(smem, o, 0, 0, nk, Kb, wave);
         wload_scales<WSC>(sc[0], sr, 0, nk, h);
         asm volatile("" ::: "memory");
         wait_vmcnt<0>();
+        if (tid == 0) s_id[par ^ 1] = tq.resolve(tile);
+        wait_lgkm0();
         barrier();
 
         // Fragments.  E2M1: f*[s & 1] hold chunk 2s + h for MFMA step s (A 2 x,
@@ -810,6 +828,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         }
         if (kt0 < nk) stage(IC<0>{});
         store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn);
+        tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
+        par ^= 1;
     }
 }
 

@@ -27,6 +27,7 @@ struct Bf16Params {
     int tilesN;
     int tilesM;        // wgrad only
     int accumulate;    // wgrad only
+    uint32_t *sched;   // tile-queue counters in the workspace, or null (static order)
 };
 
 enum Bf16Kind { kFwdKContig = 0, kFwdNContig = 1, kWgrad = 2 };
@@ -51,11 +52,24 @@ struct MxParams {
     int N, K;
     int ldo;                 // output row stride (elements for bf16, bytes for MXFP4)
     int tilesN;
+    uint32_t *sched;         // tile-queue counters in the workspace, or null (static order)
 };
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);
 int mx_tile_m();
 int mx_tile_n();
+
+// Tile queues of the persistent kernels: kQueues counters, kQueueStride
+// 32-bit words apart, starting kQueueWsOffset bytes into the caller's
+// workspace (whose first word holds the error bits).
+constexpr int kQueues = 8;
+constexpr int kQueueStride = 32;
+constexpr int kQueueWsOffset = 256;
+constexpr int kQueueWsBytes = kQueueWsOffset + kQueues * kQueueStride * 4;
+
+// Zero the tile-queue counters at `sched` on stream s (a one-wave kernel:
+// a memset node would not be safe to capture in a graph).
+hipError_t launch_queue_reset(uint32_t *sched, hipStream_t s);
 
 hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales,
                            int64_t rows, int64_t cols, int fmt, hipStream_t s);

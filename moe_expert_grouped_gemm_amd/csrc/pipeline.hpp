@@ -78,6 +78,14 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t bytes, uint8_t 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (lds_void *)lds, 16, voff, soff, 0, 0);
 }
 
+// The same with the non-temporal cache policy (NT, bit 1 of the cache-policy
+// field): for data no other workgroup reads, whose lines should be the first
+// to leave L2 so that data shared between workgroups stays.
+__device__ __forceinline__ void dma16_nt(const void *base, uint32_t bytes, uint8_t *lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (lds_void *)lds, 16, voff, soff, 0, 2);
+}
+
 // One operand's direct-load state for a tile: NL 16-byte loads per thread
 // per stage at voff[i] + kt * kstep (bytes) inside the buffer at `base`.
 template <int NL>
@@ -312,6 +320,89 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[2][4], uint
     wait_lgkm0();
     barrier();
 }
+
+// ------------------------------------------------------------------ tile queues
+// Dynamic tile order for the persistent 256 x 256 kernels.  The linear tile
+// ids are cut into chunks of kQueueChunk consecutive ids, and chunk c belongs
+// to queue c % Q (Q = 8 when the grid is a multiple of 8, else 1).
+// Workgroup b takes ids from queue b % Q first: workgroups are dispatched
+// round-robin over the 8 XCDs, so that is its own XCD's queue, and the tiles
+// in flight on an XCD form a sliding window of consecutive ids.  The column
+// tiles of one expert then start a few stages apart and find its activation
+// rows (and the m-tiles of a large expert its weight panel) still in the
+// XCD's L2.  A static round-robin order lets each workgroup's start times
+// drift by whole tiles, which spreads an expert's column tiles too far apart
+// for that.
+// Once its queue is empty a workgroup drains the others, so all workgroups
+// finish within about one tile of each other.  Every id is handed out exactly
+// once, whichever workgroup takes it, so results do not depend on the order.
+// The counters (one 128-byte line each) live in the caller's workspace and
+// are zeroed on the stream before every launch.  Takes are system-scope
+// atomics: they are performed past the per-XCD L2s, so increments from every
+// XCD meet in one place.
+constexpr int kQueueChunk = 32;
+
+__device__ __forceinline__ uint32_t queue_take(uint32_t *c)
+{
+    return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+struct TileQueue {
+    uint32_t *ctr;   // kQueues counters, or null: static order (ids b, b + grid, ...)
+    int total;
+    int Q;
+    int home;
+    int tried;       // thread 0: queues found empty so far
+    uint32_t got;    // thread 0: counter value of the last take
+
+    __device__ void init(uint32_t *c, int tot)
+    {
+        ctr = c;
+        total = tot;
+        Q = (gridDim.x % kQueues) == 0 ? kQueues : 1;
+        home = (int)blockIdx.x % Q;
+        tried = 0;
+        got = 0;
+    }
+    __device__ uint32_t *counter() const { return ctr + ((home + tried) % Q) * kQueueStride; }
+    __device__ int id_of(uint32_t i) const
+    {
+        const int qi = (home + tried) % Q;
+        const int64_t t = ((int64_t)(i / kQueueChunk) * Q + qi) * kQueueChunk + i % kQueueChunk;
+        return t < total ? (int)t : total;
+    }
+    // Thread 0: ids from the current queue onwards until one is in range;
+    // returns `total` once every queue is empty (at most Q failed takes).
+    __device__ int take_from(uint32_t i)
+    {
+        int t = id_of(i);
+        while (t >= total && ++tried < Q) t = id_of(queue_take(counter()));
+        return t;
+    }
+    // Thread 0: start taking an id (the atomic's latency then overlaps
+    // whatever the workgroup issues next) ...
+    __device__ void issue()
+    {
+        if (ctr && tried < Q) got = queue_take(counter());
+    }
+    // ... and finish: the id the workgroup runs after `tile`.
+    __device__ int resolve(int tile)
+    {
+        if (!ctr) return tile + (int)gridDim.x;
+        return tried < Q ? take_from(got) : total;
+    }
+    // All threads: the first tile id (from thread 0 through s_id).
+    __device__ int first(int *s_id)
+    {
+        if (!ctr) return xcd_logical_id();
+        if (threadIdx.x == 0) {
+            issue();
+            *s_id = resolve(0);
+        }
+        __syncthreads();
+        return __builtin_amdgcn_readfirstlane(*s_id);
+    }
+};
 
 // Grid of a persistent launch: enough workgroups to fill every CU at the
 // kernel's occupancy, never more than there are tiles, a multiple of the 8

@@ -7,8 +7,8 @@ import torch
 
 import moe_expert_grouped_gemm_amd as ptm
 from moe_expert_grouped_gemm_amd import synth
-from util import (BF16_TOL, bits16, bf16_values, dev_i64, floored_rel_err, group_of_rows,
-                  per_group_max)
+from util import (BF16_TOL, SCHEDS, bits16, bf16_values, dev_i64, floored_rel_err, group_of_rows,
+                  make_ws, per_group_max)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,15 +60,16 @@ def fwd(dev, a, b, lens, N, K, trans_b, epi, offs=None, ws=None):
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("trans_b", [0, 1])
 @pytest.mark.parametrize("epi", [ptm.PT_EPI_NONE, ptm.PT_EPI_SWIGLU])
-def test_fwd_random_vs_oracle(orc, dev, case, trans_b, epi):
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_fwd_random_vs_oracle(orc, dev, case, trans_b, epi, sched):
     lens = lens_of(case)
     _, _, K, N = case
     M, G = int(lens.sum()), len(lens)
-    print(f"fwd case={case[0]} trans_b={trans_b} epi={epi} M={M} G={G} K={K} N={N}", flush=True)
+    print(f"fwd case={case[0]} trans_b={trans_b} epi={epi} sched={sched} M={M} G={G} K={K} N={N}", flush=True)
     a = synth.randn_bf16((M, K), seed=100, std=K ** -0.5, device=dev)
     b = synth.randn_bf16((G, K, N), seed=101, std=K ** -0.5, device=dev)
     bb = b.transpose(1, 2).contiguous() if trans_b else b
-    got = bf16_values(fwd(dev, a, bb, lens, N, K, trans_b, epi))
+    got = bf16_values(fwd(dev, a, bb, lens, N, K, trans_b, epi, ws=make_ws(dev, sched)))
     rows = np.arange(M)
     ref = orc.grouped_fwd(orc.BF16, bits16(a), None, bits16(bb), None, lens, N, K, trans_b,
                           epi, rows)["exact"]
@@ -131,17 +132,18 @@ def test_fwd_deterministic(dev):
 # ------------------------------------------------------------------ dgrad
 @pytest.mark.parametrize("trans_b", [0, 1])
 @pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])
-def test_dgrad_random_vs_oracle(orc, dev, case, trans_b):
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_dgrad_random_vs_oracle(orc, dev, case, trans_b, sched):
     lens = lens_of(case)
     _, _, K, N = case
     M, G = int(lens.sum()), len(lens)
-    print(f"dgrad case={case[0]} trans_b={trans_b} M={M} K={K} N={N}", flush=True)
+    print(f"dgrad case={case[0]} trans_b={trans_b} sched={sched} M={M} K={K} N={N}", flush=True)
     dy = synth.randn_bf16((M, N), seed=102, std=1e-2, device=dev)
     b = synth.randn_bf16((G, K, N), seed=103, std=K ** -0.5, device=dev)
     bb = b.transpose(1, 2).contiguous() if trans_b else b
     buf, dx = guarded(M, K, torch.bfloat16, dev, NAN16)
     ptm.pt_grouped_gemm_dgrad(dy, None, bb, None, dx, dev_i64(lens, dev), None, G, M, N, K,
-                              ptm.PT_BF16, trans_b)
+                              ptm.PT_BF16, trans_b, workspace=make_ws(dev, sched))
     torch.cuda.synchronize()
     check_guards(buf, M, NAN16)
     rows = np.arange(M)
@@ -167,7 +169,7 @@ def test_dgrad_integer_bit_exact(orc, dev):
 
 
 # ------------------------------------------------------------------ wgrad
-def wgrad_run(dev, a, dy, lens, N, K, trans_out, accumulate, seed_mg=103):
+def wgrad_run(dev, a, dy, lens, N, K, trans_out, accumulate, seed_mg=103, ws=None):
     M, G = a.shape[0], len(lens)
     shape = (G, N, K) if trans_out else (G, K, N)
     g = torch.Generator(device=dev)
@@ -175,21 +177,22 @@ def wgrad_run(dev, a, dy, lens, N, K, trans_out, accumulate, seed_mg=103):
     mg = (torch.randn(shape, generator=g, device=dev) * 1e-3).float()
     before = mg.clone()
     ptm.pt_grouped_gemm_wgrad(a, None, dy, None, mg, dev_i64(lens, dev), None, G, M, N, K,
-                              ptm.PT_BF16, trans_out, accumulate)
+                              ptm.PT_BF16, trans_out, accumulate, workspace=ws)
     torch.cuda.synchronize()
     return before.cpu().numpy(), mg.cpu().numpy()
 
 
 @pytest.mark.parametrize("trans_out", [0, 1])
 @pytest.mark.parametrize("accumulate", [1, 0])
-def test_wgrad_vs_oracle(orc, dev, trans_out, accumulate):
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_wgrad_vs_oracle(orc, dev, trans_out, accumulate, sched):
     lens = np.array([0, 70, 1, 0, 300, 129, 0], np.int64)
     K, N = 200, 136
     M, G = int(lens.sum()), len(lens)
-    print(f"wgrad trans_out={trans_out} acc={accumulate}", flush=True)
+    print(f"wgrad trans_out={trans_out} acc={accumulate} sched={sched}", flush=True)
     a = synth.randn_bf16((M, K), seed=101, std=K ** -0.5, device=dev)
     dy = synth.randn_bf16((M, N), seed=102, std=1e-2, device=dev)
-    before, after = wgrad_run(dev, a, dy, lens, N, K, trans_out, accumulate)
+    before, after = wgrad_run(dev, a, dy, lens, N, K, trans_out, accumulate, ws=make_ws(dev, sched))
     gs = np.repeat(np.arange(G), K)
     ks = np.tile(np.arange(K), G)
     D = orc.wgrad_rows(bits16(a), bits16(dy), lens, N, K, gs, ks).reshape(G, K, N)
@@ -290,3 +293,40 @@ def test_host_argument_errors(dev):
     assert call(a=a.data_ptr() + 2) == 3
     assert call(G=5000) == 2
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ tile queues
+def test_queue_order_matches_static_many_tiles(dev):
+    # ~1.2k forward tiles and 1k wgrad tiles over the persistent grid: every
+    # workgroup takes several ids, every queue several chunks, and the queues
+    # drain each other at the end.  Each tile is computed identically in either
+    # order, so the results are bit-identical; a tile taken twice would
+    # double-accumulate into main_grad, one never taken would keep its guard.
+    lens = synth.lens_topk_gaussian(2400, 24, 6, seed=31)
+    K, N = 64, 4096
+    M, G = int(lens.sum()), len(lens)
+    print(f"queue fwd M={M} G={G}", flush=True)
+    a = synth.randn_bf16((M, K), seed=32, std=K ** -0.5, device=dev)
+    b = synth.randn_bf16((G, K, N), seed=33, std=K ** -0.5, device=dev)
+    ws = make_ws(dev, "queue")
+    x = fwd(dev, a, b, lens, N, K, 0, ptm.PT_EPI_SWIGLU)
+    y = fwd(dev, a, b, lens, N, K, 0, ptm.PT_EPI_SWIGLU, ws=ws)
+    z = fwd(dev, a, b, lens, N, K, 0, ptm.PT_EPI_SWIGLU, ws=ws)      # same workspace again
+    assert (x == y).all() and (x == z).all()
+    # a smaller problem through the same workspace right after
+    small = np.array([3, 0, 77], np.int64)
+    a2 = a[:80].contiguous()
+    x2 = fwd(dev, a2, b[:3].contiguous(), small, N, K, 1, ptm.PT_EPI_NONE)
+    y2 = fwd(dev, a2, b[:3].contiguous(), small, N, K, 1, ptm.PT_EPI_NONE, ws=ws)
+    assert (x2 == y2).all()
+
+    wl = np.full(64, 40, np.int64)
+    wl[[3, 17]] = 0
+    Kw, Nw = 1024, 768
+    Mw = int(wl.sum())
+    print(f"queue wgrad M={Mw} G={len(wl)}", flush=True)
+    aw = synth.randn_bf16((Mw, Kw), seed=34, std=Kw ** -0.5, device=dev)
+    dyw = synth.randn_bf16((Mw, Nw), seed=35, std=1e-2, device=dev)
+    _, p = wgrad_run(dev, aw, dyw, wl, Nw, Kw, 0, 1)
+    _, q = wgrad_run(dev, aw, dyw, wl, Nw, Kw, 0, 1, ws=ws)
+    assert (p == q).all()

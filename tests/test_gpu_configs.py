@@ -23,7 +23,7 @@ import torch
 
 import moe_expert_grouped_gemm_amd as ptm
 from moe_expert_grouped_gemm_amd import synth
-from util import (BF16_TOL, MX_TOL, bits16, bf16_values, floored_rel_err, norm_err, u8)
+from util import (BF16_TOL, MX_TOL, bits16, bf16_values, floored_rel_err, make_ws, norm_err, u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,7 +76,7 @@ def test_fc1_bf16_swiglu_sampled(orc, dev, fc1):
     out = torch.empty((M + 2, N // 2), dtype=torch.bfloat16, device=dev)
     out.view(torch.int16).fill_(0x7FC1)
     ptm.pt_grouped_gemm_fwd(a, None, b, None, out[1:M + 1], None, torch.as_tensor(lens, device=dev), None,
-                            G, M, N, K, ptm.PT_BF16, 0, ptm.PT_EPI_SWIGLU)
+                            G, M, N, K, ptm.PT_BF16, 0, ptm.PT_EPI_SWIGLU, workspace=make_ws(dev, "queue"))
     torch.cuda.synchronize()
     assert (bits16(out[0]) == 0x7FC1).all() and (bits16(out[M + 1]) == 0x7FC1).all()
     experts, rows, local = sample_plan(lens, seed=1)
@@ -97,7 +97,7 @@ def test_bwd_dgrad_sampled(orc, dev, fc1):
     dy = synth.randn_bf16((M, N), seed=102, std=1e-2, device=dev)
     dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     ptm.pt_grouped_gemm_dgrad(dy, None, b, None, dx, torch.as_tensor(lens, device=dev), None,
-                              G, M, N, K, ptm.PT_BF16, 0)
+                              G, M, N, K, ptm.PT_BF16, 0, workspace=make_ws(dev, "queue"))
     torch.cuda.synchronize()
     experts, rows, local = sample_plan(lens, seed=2)
     ref = orc.dgrad_rows(bits16(take_rows(dy, rows)), bits16(b[torch.as_tensor(experts, device=dev)]),
@@ -125,7 +125,7 @@ def test_bwd_wgrad_sampled_and_empty_experts_untouched(orc, dev, fc1):
     before_rows = mg[torch.as_tensor(gs, device=dev), torch.as_tensor(ks, device=dev)].cpu().numpy()
     before_empty = mg[torch.as_tensor(empty, device=dev)].clone()
     ptm.pt_grouped_gemm_wgrad(a, None, dy, None, mg, torch.as_tensor(lens, device=dev), None,
-                              G, M, N, K, ptm.PT_BF16, 0, 1)
+                              G, M, N, K, ptm.PT_BF16, 0, 1, workspace=make_ws(dev, "queue"))
     torch.cuda.synchronize()
     assert torch.equal(mg[torch.as_tensor(empty, device=dev)], before_empty)
     after = mg[torch.as_tensor(gs, device=dev), torch.as_tensor(ks, device=dev)].cpu().numpy()
@@ -154,7 +154,7 @@ def test_mxfp8_quantize_and_fwd(orc, dev):
     ptm.pt_mx_quantize(w, bq, bs, G * N, K, ptm.PT_MXFP8_E4M3, 1)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ptm.pt_grouped_gemm_fwd(aq, as_, bq, bs, out, None, torch.as_tensor(lens, device=dev), None,
-                            G, M, N, K, ptm.PT_MXFP8_E4M3, 1, ptm.PT_EPI_NONE)
+                            G, M, N, K, ptm.PT_MXFP8_E4M3, 1, ptm.PT_EPI_NONE, workspace=make_ws(dev, "queue"))
     torch.cuda.synchronize()
     # quantiser: whole tensors, bit-exact, against the oracle's own quantiser
     rxq, rxs = orc.mx_quantize(bits16(x), orc.E4M3)
@@ -195,10 +195,11 @@ def test_mxfp4_mlp_chain(orc, dev):
     out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     lens_d = torch.as_tensor(lens, device=dev)
     ptm.pt_mx_quantize(x, xq, xs, M, H, ptm.PT_MXFP4_E2M1, 1)
+    ws = make_ws(dev, "queue")
     ptm.pt_grouped_gemm_fwd(xq, xs, w1q, w1s, hq, hs, lens_d, None, G, M, 2 * I, H,
-                            ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_SWIGLU_MXFP4)
+                            ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_SWIGLU_MXFP4, workspace=ws)
     ptm.pt_grouped_gemm_fwd(hq, hs, w2q, w2s, out, None, lens_d, None, G, M, H, I,
-                            ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_NONE)
+                            ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_NONE, workspace=ws)
     torch.cuda.synchronize()
     experts, rows, local = sample_plan(lens, seed=5, n_experts=8)
     e_d = torch.as_tensor(experts, device=dev)

@@ -9,8 +9,8 @@ import torch
 
 import moe_expert_grouped_gemm_amd as ptm
 from moe_expert_grouped_gemm_amd import synth
-from util import (BF16_TOL, MX_TOL, bits16, bf16_values, dev_i64, floored_rel_err, group_of_rows,
-                  norm_err, per_group_max, u8)
+from util import (BF16_TOL, MX_TOL, SCHEDS, bits16, bf16_values, dev_i64, floored_rel_err, group_of_rows,
+                  make_ws, norm_err, per_group_max, u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,7 +93,7 @@ def test_quantize_host_errors(dev):
 
 
 # ------------------------------------------------------------------ MX GEMM
-def mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, epi):
+def mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, epi, ws=None):
     M, G = aq.shape[0], len(lens)
     lens_d = dev_i64(lens, dev)
     if epi == ptm.PT_EPI_SWIGLU_MXFP4:
@@ -102,7 +102,7 @@ def mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, epi):
     else:
         out = torch.empty((M, N if epi == ptm.PT_EPI_NONE else N // 2), dtype=torch.bfloat16, device=dev)
         osc = None
-    ptm.pt_grouped_gemm_fwd(aq, as_, bq, bs, out, osc, lens_d, None, G, M, N, K, fmt, 1, epi)
+    ptm.pt_grouped_gemm_fwd(aq, as_, bq, bs, out, osc, lens_d, None, G, M, N, K, fmt, 1, epi, workspace=ws)
     torch.cuda.synchronize()
     return out, osc
 
@@ -116,14 +116,15 @@ MX_CASES = [
 
 @pytest.mark.parametrize("fmt,ofmt,name", FMTS, ids=[f[2] for f in FMTS])
 @pytest.mark.parametrize("case", MX_CASES, ids=[c[0] for c in MX_CASES])
-def test_mx_fwd_random_codes_vs_oracle(orc, dev, fmt, ofmt, name, case):
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_mx_fwd_random_codes_vs_oracle(orc, dev, fmt, ofmt, name, case, sched):
     _, lens, K, N = case
     lens = np.array(lens, np.int64)
     M, G = int(lens.sum()), len(lens)
-    print(f"mx fwd {name} case={case[0]} M={M} K={K} N={N}", flush=True)
+    print(f"mx fwd {name} case={case[0]} sched={sched} M={M} K={K} N={N}", flush=True)
     aq, as_ = synth.random_mx_codes(M, K, name, seed=40, device=dev)
     bq, bs = synth.random_mx_codes(G * N, K, name, seed=41, device=dev)
-    out, _ = mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, ptm.PT_EPI_NONE)
+    out, _ = mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, ptm.PT_EPI_NONE, ws=make_ws(dev, sched))
     rows = np.arange(M)
     ref = orc.fwd_rows(ofmt, u8(aq), u8(as_), u8(bq).reshape(G, N, -1), u8(bs).reshape(G, N, -1),
                        lens, N, K, 1, rows)

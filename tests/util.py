@@ -76,3 +76,18 @@ def sample_rows(lens: np.ndarray, per_group: int, seed: int, max_groups=None) ->
 
 def dev_i64(x, device) -> torch.Tensor:
     return torch.as_tensor(np.asarray(x, np.int64), device=device)
+
+
+# The two tile orders of the persistent kernels: "static" (no workspace) and
+# "queue" (the per-XCD tile queues in a workspace).  The queue workspace is
+# filled with 0xFF so that a launch relying on leftover counter values, rather
+# than on its own reset, hands out the wrong tiles.
+SCHEDS = ["static", "queue"]
+
+
+def make_ws(device, sched):
+    if sched == "static":
+        return None
+    import moe_expert_grouped_gemm_amd as ptm
+    n = ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 1, 1, 1, 1, ptm.PT_BF16)
+    return torch.full((n,), 0xFF, dtype=torch.uint8, device=device)
