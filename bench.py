@@ -116,14 +116,18 @@ def summary(name, dtype, flops, nbytes, per_ms, extra=None):
 
 
 # ------------------------------------------------------------------ workloads
-# One workspace for every GEMM call: the error word and the tile queues
-# (calls on one stream run one after another, so they can share it).
+# One workspace for every GEMM call (calls on one stream run one after
+# another, so they can share it): the error word, the tile queues and, for the
+# MX forwards, stage-major copies of the scales; sized for the largest call.
 WS = [None]
 
 
 def make_workspace(dev):
-    n = ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 1, 1, 1, 1, ptm.PT_BF16)
-    WS[0] = torch.zeros(n, dtype=torch.uint8, device=dev)
+    sizes = [ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 1, 1, 1, 1, ptm.PT_BF16),
+             ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 32, 65536, 5760, 2880, ptm.PT_MXFP8_E4M3),
+             ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 256, 49152, 4096, 4096, ptm.PT_MXFP4_E2M1),
+             ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 256, 49152, 4096, 2048, ptm.PT_MXFP4_E2M1)]
+    WS[0] = torch.zeros(max(sizes), dtype=torch.uint8, device=dev)
 
 
 def fc1_inputs(dev):

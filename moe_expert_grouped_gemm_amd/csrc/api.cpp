@@ -67,6 +67,16 @@ uint32_t *queue_words(void *ws, size_t bytes)
     return (ws && bytes >= (size_t)kQueueWsBytes) ? (uint32_t *)((uint8_t *)ws + kQueueWsOffset) : nullptr;
 }
 
+// MX forward: the stage-major copies of the A and B scales follow the queues
+// in the workspace (256-byte aligned); 0 when the sizes do not allow them.
+int64_t round256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+int64_t mx_swz_a_bytes(int64_t M, int64_t K, int fmt) { return round256(mx_swizzle_bytes(M, K, fmt)); }
+int64_t mx_swz_b_bytes(int64_t G, int64_t N, int64_t K, int fmt) { return round256(mx_swizzle_bytes(G * N, K, fmt)); }
+bool mx_swz_possible(int64_t G, int64_t M, int64_t N, int64_t K, int fmt)
+{
+    return K <= kMxSwzMaxK && fits31(mx_swizzle_bytes(M, K, fmt)) && fits31(mx_swizzle_bytes(G * N, K, fmt));
+}
+
 // Zero the queues (if any) ahead of the launch on the same stream.
 template <class Launch>
 hipError_t queued(uint32_t *sched, hipStream_t s, Launch launch)
@@ -162,7 +172,19 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
         p.tilesN = (int)((Nc + tn - 1) / tn);
         p.sched = queue_words(workspace, workspace_bytes);
         if (M == 0) return PT_OK;
-        return hip_status(queued(p.sched, s, [&] { return launch_mx(p, dtype == PT_MXFP8_E4M3 ? 0 : 1, ep, s); }));
+        const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
+        // a workspace with room for them gets stage-major copies of the scales
+        if (p.sched && mx_swz_possible(G, M, N, K, fmt) &&
+            workspace_bytes >= (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) + mx_swz_b_bytes(G, N, K, fmt))) {
+            uint32_t *sa = (uint32_t *)((uint8_t *)workspace + kQueueWsBytes);
+            uint32_t *sb = (uint32_t *)((uint8_t *)sa + mx_swz_a_bytes(M, K, fmt));
+            hipError_t e = launch_mx_scale_swizzle(a_scale, M, K, fmt, sa, s);
+            if (e == hipSuccess) e = launch_mx_scale_swizzle(b_scale, G * N, K, fmt, sb, s);
+            if (e != hipSuccess) return PT_ERR_HIP;
+            p.sa = sa;
+            p.sb = sb;
+        }
+        return hip_status(queued(p.sched, s, [&] { return launch_mx(p, fmt, ep, s); }));
     }
     return PT_ERR_UNSUPPORTED;
 }
@@ -265,8 +287,15 @@ int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_
 
 size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, int64_t K, int dtype)
 {
-    (void)op; (void)G; (void)M; (void)N; (void)K; (void)dtype;
-    return kQueueWsBytes;   // the error word, then the tile-queue counters
+    // the error word and the tile-queue counters; for an MX forward also the
+    // stage-major copies of the A and B scales
+    if (op == PT_OP_FWD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && G > 0 && M >= 0 && N > 0 &&
+        K > 0 && K % 32 == 0) {
+        const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
+        if (mx_swz_possible(G, M, N, K, fmt))
+            return (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) + mx_swz_b_bytes(G, N, K, fmt));
+    }
+    return kQueueWsBytes;
 }
 
 int pt_read_error_flags(const void *workspace, void *stream, uint32_t *flags)

@@ -73,6 +73,7 @@ struct ScRows {
     const uint8_t *b;
     uint32_t abytes, bbytes;
     uint32_t row[6];
+    uint32_t astride, bstride;      // stage-major copies: bytes from one stage to the next
 };
 
 // E4M3: byte of the row that lane half h needs for stage kt.  The partial
@@ -464,6 +465,8 @@ enum WideScale {
     kWE4M3Word = 0,   // E4M3, K % 128 == 0: the word of bytes 4kt .. 4kt+3
     kWE4M3Span = 1,   // E4M3, other K: two words exchanged between lane halves
     kWE2M1Pair = 2,   // E2M1, K % 256 == 0: words 8kt and 8kt+4, one per lane half, exchanged
+    kWE4M3Swz = 3,    // E4M3, stage-major copy: the stage's word of the row (any K)
+    kWE2M1Swz = 4,    // E2M1, stage-major copy: the lane half's word of the row (any K)
 };
 
 // Load this lane's scale word of each of its 6 rows for stage kt.
@@ -478,7 +481,8 @@ __device__ __forceinline__ void wload_scales(uint32_t (&sc)[6], const ScRows &sr
         uint32_t a;
         if constexpr (WSC == kWE4M3Word) a = sr.row[i] + 4u * kt;
         else if constexpr (WSC == kWE4M3Span) a = ((sr.row[i] + 4u * kt) & ~3u) + 4u * h;
-        else a = sr.row[i] + 8u * kt + 4u * h;
+        else if constexpr (WSC == kWE2M1Pair) a = sr.row[i] + 8u * kt + 4u * h;
+        else a = sr.row[i] + (uint32_t)kt * (i < 2 ? sr.astride : sr.bstride);
         sc[i] = ld_u32(base, bytes, a, soff);
     }
 }
@@ -495,7 +499,7 @@ __device__ __forceinline__ void wscale_words(const uint32_t (&sc)[6], uint32_t (
     const uint32_t sel = h ? 0x07050301u : 0x06040200u;
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
-        if constexpr (WSC == kWE4M3Word) {
+        if constexpr (WSC == kWE4M3Word || WSC == kWE4M3Swz || WSC == kWE2M1Swz) {
             w[i] = sc[i];
         } else if constexpr (WSC == kWE4M3Span) {
             const auto r = __builtin_amdgcn_permlane32_swap(sc[i], sc[i], false, false);
@@ -511,7 +515,7 @@ __device__ __forceinline__ void wscale_words(const uint32_t (&sc)[6], uint32_t (
 template <int WSC>
 __device__ __forceinline__ int wscale_of(const uint32_t (&w)[6], int i, int s, uint32_t sh)
 {
-    if constexpr (WSC == kWE2M1Pair) return (int)__builtin_amdgcn_ubfe(w[i], 8u * s, 8u);
+    if constexpr (WSC == kWE2M1Pair || WSC == kWE2M1Swz) return (int)__builtin_amdgcn_ubfe(w[i], 8u * s, 8u);
     else return (int)__builtin_amdgcn_ubfe(w[i], sh + 16u * s, 8u);
 }
 
@@ -650,17 +654,37 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             o.bdelta[3] = (uint32_t)(I + 64) * Kb;
         }
         ScRows sr;
-        sr.a = p.as;
-        sr.abytes = (uint32_t)((p.M * KS + 3) & ~3ll);
-        sr.b = p.bs;
-        sr.bbytes = (uint32_t)(((int64_t)p.G * p.N * KS + 3) & ~3ll);
+        if constexpr (WSC == kWE4M3Swz || WSC == kWE2M1Swz) {
+            // word (kt * rows + r) * WPR + (E2M1: lane half) of the copies
+            constexpr uint32_t WPR = WSC == kWE4M3Swz ? 1u : 2u;
+            const uint32_t hw = WSC == kWE2M1Swz ? 4u * h : 0u;
+            sr.a = (const uint8_t *)p.sa;
+            sr.astride = (uint32_t)p.M * WPR * 4u;
+            sr.abytes = sr.astride * (uint32_t)nk;
+            sr.b = (const uint8_t *)p.sb;
+            sr.bstride = (uint32_t)p.G * (uint32_t)p.N * WPR * 4u;
+            sr.bbytes = sr.bstride * (uint32_t)nk;
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
-            sr.row[bi] = (uint32_t)((row0 + min(m0 + wm * 64 + bi * 32 + r32, rows - 1)) * KS);
+            for (int bi = 0; bi < 2; ++bi)
+                sr.row[bi] = (uint32_t)(row0 + min(m0 + wm * 64 + bi * 32 + r32, rows - 1)) * WPR * 4u + hw;
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
-            sr.row[2 + bj] =
-                (uint32_t)((g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)) * KS);
+            for (int bj = 0; bj < 4; ++bj)
+                sr.row[2 + bj] =
+                    (uint32_t)(g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)) * WPR * 4u +
+                    hw;
+        } else {
+            sr.a = p.as;
+            sr.abytes = (uint32_t)((p.M * KS + 3) & ~3ll);
+            sr.b = p.bs;
+            sr.bbytes = (uint32_t)(((int64_t)p.G * p.N * KS + 3) & ~3ll);
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+                sr.row[bi] = (uint32_t)((row0 + min(m0 + wm * 64 + bi * 32 + r32, rows - 1)) * KS);
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj)
+                sr.row[2 + bj] =
+                    (uint32_t)((g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)) * KS);
+        }
 
         floatx16 acc[2][4];
 #pragma unroll
@@ -894,6 +918,53 @@ hipError_t launch_epi(const MxParams &p, int epi, hipStream_t s)
 int mx_tile_m() { return BM; }
 int mx_tile_n() { return BN; }
 
+// Stage-major copy of a row-major E8M0 scale matrix [R][KS] for the 256 x 256
+// kernel: word w of stage kt of row r lands at ((kt * R + r) * WPR + w).
+// E4M3 (WPR 1): blocks 4kt .. 4kt+3 in byte order; E2M1 (WPR 2): word w holds
+// blocks 8kt + w + 0, 2, 4, 6, the four that lane half w of the MFMA uses.
+// Blocks past the row read as zero: a finite scale for the zero codes of a
+// partial last stage.  One stage's words of 32 consecutive rows are then 32
+// consecutive words (64 for E2M1), one or two cache lines per wave-wide scale
+// load, where the row-major layout puts every row on a line of its own.
+// One thread per row, consecutive rows in consecutive lanes, so each stage's
+// words leave as one contiguous run per workgroup; a thread walks its row in
+// chunks of four stages, realigning the covering words with v_alignbyte.
+template <int FMT>
+__global__ __launch_bounds__(256) void mx_scale_swizzle_kernel(const uint8_t *sc, uint32_t sbytes, uint32_t *out,
+                                                               int R, int KS, int NS)
+{
+    constexpr int SB = FMT == 0 ? 4 : 8;               // scale bytes per stage
+    constexpr int CH = 4;                              // stages per chunk
+    constexpr int NW = CH * SB / 4 + 1;                // covering words per chunk
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= R) return;
+    for (int c = 0; c * CH < NS; ++c) {
+        const uint32_t start = (uint32_t)r * (uint32_t)KS + (uint32_t)(c * CH * SB);
+        const uint32_t w0 = start >> 2, sh = start & 3u;
+        uint32_t wd[NW];
+#pragma unroll
+        for (int j = 0; j < NW; ++j) wd[j] = ld_u32(sc, sbytes, (w0 + j) * 4u, 0u);
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int kt = c * CH + k;
+            if (kt >= NS) break;
+            // bytes of the stage's words that lie inside the row
+            const int n0 = KS - kt * SB;
+            const uint32_t keep0 = n0 >= 4 ? 0xFFFFFFFFu : (n0 <= 0 ? 0u : (1u << (8 * n0)) - 1u);
+            const uint32_t v0 = __builtin_amdgcn_alignbyte(wd[k * SB / 4 + 1], wd[k * SB / 4], sh) & keep0;
+            if (FMT == 0) {
+                out[(int64_t)kt * R + r] = v0;
+            } else {
+                const int n1 = n0 - 4;
+                const uint32_t keep1 = n1 >= 4 ? 0xFFFFFFFFu : (n1 <= 0 ? 0u : (1u << (8 * n1)) - 1u);
+                const uint32_t v1 = __builtin_amdgcn_alignbyte(wd[k * 2 + 2], wd[k * 2 + 1], sh) & keep1;
+                *(uintx2 *)(out + ((int64_t)kt * R + r) * 2) =
+                    uintx2{__builtin_amdgcn_perm(v1, v0, 0x06040200u), __builtin_amdgcn_perm(v1, v0, 0x07050301u)};
+            }
+        }
+    }
+}
+
 // Which MX mainloop runs: PTGG_MX_TILE=128 forces the 128 x 256 kernel
 // wherever it applies (a tuning knob for experiments; results do not depend
 // on it).
@@ -906,10 +977,31 @@ bool mx_force_narrow()
     return narrow;
 }
 
+int64_t mx_swizzle_bytes(int64_t rows, int64_t K, int fmt)
+{
+    const int64_t KS = K / 32, NS = fmt == 0 ? (KS + 3) / 4 : (KS + 7) / 8;
+    return NS * rows * (fmt == 0 ? 1 : 2) * 4;
+}
+
+hipError_t launch_mx_scale_swizzle(const uint8_t *scales, int64_t rows, int64_t K, int fmt, uint32_t *out,
+                                   hipStream_t s)
+{
+    const int KS = (int)(K / 32), NS = fmt == 0 ? (KS + 3) / 4 : (KS + 7) / 8;
+    const uint32_t sbytes = (uint32_t)((rows * KS + 3) & ~3ll);
+    const dim3 grid((unsigned)((rows + 255) / 256));
+    if (fmt == 0)
+        hipLaunchKernelGGL(mx_scale_swizzle_kernel<0>, grid, dim3(256), 0, s, scales, sbytes, out, (int)rows, KS, NS);
+    else
+        hipLaunchKernelGGL(mx_scale_swizzle_kernel<1>, grid, dim3(256), 0, s, scales, sbytes, out, (int)rows, KS, NS);
+    return hipGetLastError();
+}
+
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s)
 {
     if (fmt == 1 && mx_force_narrow())
         return p.K % 128 == 0 ? launch_epi<1, kScE2M1Word>(p, epi, s) : launch_epi<1, kScE2M1Span>(p, epi, s);
+    if (p.sa && p.sb)
+        return fmt == 0 ? launch_wide_epi<0, kWE4M3Swz>(p, epi, s) : launch_wide_epi<1, kWE2M1Swz>(p, epi, s);
     if (fmt == 0) {
         if (p.K % 128 == 0) return launch_wide_epi<0, kWE4M3Word>(p, epi, s);
         return launch_wide_epi<0, kWE4M3Span>(p, epi, s);

@@ -53,9 +53,19 @@ struct MxParams {
     int ldo;                 // output row stride (elements for bf16, bytes for MXFP4)
     int tilesN;
     uint32_t *sched;         // tile-queue counters in the workspace, or null (static order)
+    const uint32_t *sa;      // stage-major copies of as / bs in the workspace, or null
+    const uint32_t *sb;
 };
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);
+
+// Stage-major copy of a row-major E8M0 scale matrix [rows, K/32] for the
+// 256 x 256 MX kernel (layout at mx_scale_swizzle): mx_swizzle_bytes() bytes
+// at `out`.  kMxSwzMaxK bounds K.
+constexpr int64_t kMxSwzMaxK = 16384;
+int64_t mx_swizzle_bytes(int64_t rows, int64_t K, int fmt);
+hipError_t launch_mx_scale_swizzle(const uint8_t *scales, int64_t rows, int64_t K, int fmt, uint32_t *out,
+                                   hipStream_t s);
 int mx_tile_m();
 int mx_tile_n();
 

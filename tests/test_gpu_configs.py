@@ -154,7 +154,8 @@ def test_mxfp8_quantize_and_fwd(orc, dev):
     ptm.pt_mx_quantize(w, bq, bs, G * N, K, ptm.PT_MXFP8_E4M3, 1)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ptm.pt_grouped_gemm_fwd(aq, as_, bq, bs, out, None, torch.as_tensor(lens, device=dev), None,
-                            G, M, N, K, ptm.PT_MXFP8_E4M3, 1, ptm.PT_EPI_NONE, workspace=make_ws(dev, "queue"))
+                            G, M, N, K, ptm.PT_MXFP8_E4M3, 1, ptm.PT_EPI_NONE,
+                            workspace=make_ws(dev, "swz", G, M, N, K, ptm.PT_MXFP8_E4M3))
     torch.cuda.synchronize()
     # quantiser: whole tensors, bit-exact, against the oracle's own quantiser
     rxq, rxs = orc.mx_quantize(bits16(x), orc.E4M3)
@@ -195,7 +196,7 @@ def test_mxfp4_mlp_chain(orc, dev):
     out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     lens_d = torch.as_tensor(lens, device=dev)
     ptm.pt_mx_quantize(x, xq, xs, M, H, ptm.PT_MXFP4_E2M1, 1)
-    ws = make_ws(dev, "queue")
+    ws = make_ws(dev, "swz", G, M, 2 * I, H, ptm.PT_MXFP4_E2M1)     # the larger of the two calls
     ptm.pt_grouped_gemm_fwd(xq, xs, w1q, w1s, hq, hs, lens_d, None, G, M, 2 * I, H,
                             ptm.PT_MXFP4_E2M1, 1, ptm.PT_EPI_SWIGLU_MXFP4, workspace=ws)
     ptm.pt_grouped_gemm_fwd(hq, hs, w2q, w2s, out, None, lens_d, None, G, M, H, I,

@@ -9,7 +9,7 @@ import torch
 
 import moe_expert_grouped_gemm_amd as ptm
 from moe_expert_grouped_gemm_amd import synth
-from util import (BF16_TOL, MX_TOL, SCHEDS, bits16, bf16_values, dev_i64, floored_rel_err, group_of_rows,
+from util import (BF16_TOL, MX_SCHEDS, MX_TOL, bits16, bf16_values, dev_i64, floored_rel_err, group_of_rows,
                   make_ws, norm_err, per_group_max, u8)
 
 pytestmark = pytest.mark.gpu
@@ -93,8 +93,10 @@ def test_quantize_host_errors(dev):
 
 
 # ------------------------------------------------------------------ MX GEMM
-def mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, epi, ws=None):
+def mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, epi, ws=None, sched=None):
     M, G = aq.shape[0], len(lens)
+    if sched is not None:
+        ws = make_ws(dev, sched, G, M, N, K, fmt)
     lens_d = dev_i64(lens, dev)
     if epi == ptm.PT_EPI_SWIGLU_MXFP4:
         out = torch.full((M, N // 4), 0xEE, dtype=torch.uint8, device=dev)
@@ -116,7 +118,7 @@ MX_CASES = [
 
 @pytest.mark.parametrize("fmt,ofmt,name", FMTS, ids=[f[2] for f in FMTS])
 @pytest.mark.parametrize("case", MX_CASES, ids=[c[0] for c in MX_CASES])
-@pytest.mark.parametrize("sched", SCHEDS)
+@pytest.mark.parametrize("sched", MX_SCHEDS)
 def test_mx_fwd_random_codes_vs_oracle(orc, dev, fmt, ofmt, name, case, sched):
     _, lens, K, N = case
     lens = np.array(lens, np.int64)
@@ -124,7 +126,7 @@ def test_mx_fwd_random_codes_vs_oracle(orc, dev, fmt, ofmt, name, case, sched):
     print(f"mx fwd {name} case={case[0]} sched={sched} M={M} K={K} N={N}", flush=True)
     aq, as_ = synth.random_mx_codes(M, K, name, seed=40, device=dev)
     bq, bs = synth.random_mx_codes(G * N, K, name, seed=41, device=dev)
-    out, _ = mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, ptm.PT_EPI_NONE, ws=make_ws(dev, sched))
+    out, _ = mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, ptm.PT_EPI_NONE, sched=sched)
     rows = np.arange(M)
     ref = orc.fwd_rows(ofmt, u8(aq), u8(as_), u8(bq).reshape(G, N, -1), u8(bs).reshape(G, N, -1),
                        lens, N, K, 1, rows)
@@ -155,36 +157,38 @@ def grid_codes(rows, cols, name, seed, dev):
 
 
 @pytest.mark.parametrize("fmt,ofmt,name", FMTS, ids=[f[2] for f in FMTS])
-def test_mx_fwd_exact_inputs_bit_exact_and_scale_doubling(orc, dev, fmt, ofmt, name):
+@pytest.mark.parametrize("sched", ["static", "swz"])
+def test_mx_fwd_exact_inputs_bit_exact_and_scale_doubling(orc, dev, fmt, ofmt, name, sched):
     lens = np.array([33, 0, 128, 1, 70], np.int64)
     K, N = 256, 256
     M, G = int(lens.sum()), len(lens)
     aq, as_ = grid_codes(M, K, name, 50, dev)
     bq, bs = grid_codes(G * N, K, name, 51, dev)
-    out, _ = mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, ptm.PT_EPI_NONE)
+    out, _ = mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, ptm.PT_EPI_NONE, sched=sched)
     ref = orc.fwd_rows(ofmt, u8(aq), u8(as_), u8(bq).reshape(G, N, -1), u8(bs).reshape(G, N, -1),
                        lens, N, K, 1, np.arange(M))
     assert (bits16(out) == orc.round_bf16(ref)).all()
     # raising every A scale byte by one doubles every output exactly
-    out2, _ = mx_fwd(dev, aq, as_ + 1, bq, bs, lens, N, K, fmt, ptm.PT_EPI_NONE)
+    out2, _ = mx_fwd(dev, aq, as_ + 1, bq, bs, lens, N, K, fmt, ptm.PT_EPI_NONE, sched=sched)
     assert (bf16_values(bits16(out2)) == 2.0 * bf16_values(bits16(out))).all()
     # raising only block 3 of B changes exactly the products of that block
     bs3 = bs.clone()
     bs3[:, 3] += 1
-    out3, _ = mx_fwd(dev, aq, as_, bq, bs3, lens, N, K, fmt, ptm.PT_EPI_NONE)
+    out3, _ = mx_fwd(dev, aq, as_, bq, bs3, lens, N, K, fmt, ptm.PT_EPI_NONE, sched=sched)
     ref3 = orc.fwd_rows(ofmt, u8(aq), u8(as_), u8(bq).reshape(G, N, -1), u8(bs3).reshape(G, N, -1),
                         lens, N, K, 1, np.arange(M))
     assert (bits16(out3) == orc.round_bf16(ref3)).all()
 
 
 @pytest.mark.parametrize("fmt,ofmt,name", FMTS, ids=[f[2] for f in FMTS])
-def test_mx_fwd_swiglu_vs_oracle(orc, dev, fmt, ofmt, name):
+@pytest.mark.parametrize("sched", ["static", "swz"])
+def test_mx_fwd_swiglu_vs_oracle(orc, dev, fmt, ofmt, name, sched):
     lens = np.array([5, 0, 140, 31, 0, 64], np.int64)
     K, N = 256, 384
     M, G = int(lens.sum()), len(lens)
     aq, as_ = synth.random_mx_codes(M, K, name, seed=60, device=dev)
     bq, bs = synth.random_mx_codes(G * N, K, name, seed=61, device=dev)
-    out, _ = mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, ptm.PT_EPI_SWIGLU)
+    out, _ = mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, ptm.PT_EPI_SWIGLU, sched=sched)
     rows = np.arange(M)
     ref = orc.grouped_fwd(ofmt, u8(aq), u8(as_), u8(bq).reshape(G, N, -1), u8(bs).reshape(G, N, -1),
                           lens, N, K, 1, orc.EPI_SWIGLU, rows)["exact"]
@@ -193,7 +197,8 @@ def test_mx_fwd_swiglu_vs_oracle(orc, dev, fmt, ofmt, name):
 
 
 @pytest.mark.parametrize("fmt,ofmt,name", FMTS + [(ptm.PT_BF16, 0, "bf16")], ids=[f[2] for f in FMTS] + ["bf16"])
-def test_swiglu_mxfp4_epilogue_vs_oracle(orc, dev, fmt, ofmt, name):
+@pytest.mark.parametrize("sched", ["static", "swz"])
+def test_swiglu_mxfp4_epilogue_vs_oracle(orc, dev, fmt, ofmt, name, sched):
     lens = np.array([0, 77, 3, 200, 0, 40], np.int64)
     K, N = 256, 512
     M, G = int(lens.sum()), len(lens)
@@ -208,7 +213,7 @@ def test_swiglu_mxfp4_epilogue_vs_oracle(orc, dev, fmt, ofmt, name):
         bq, bs = synth.random_mx_codes(G * N, K, name, seed=73, device=dev)
         ref = orc.grouped_fwd(ofmt, u8(aq), u8(as_), u8(bq).reshape(G, N, -1), u8(bs).reshape(G, N, -1),
                               lens, N, K, 1, orc.EPI_SWIGLU_MXFP4, np.arange(M))
-    out, osc = mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, ptm.PT_EPI_SWIGLU_MXFP4)
+    out, osc = mx_fwd(dev, aq, as_, bq, bs, lens, N, K, fmt, ptm.PT_EPI_SWIGLU_MXFP4, sched=sched)
     q, s = u8(out), u8(osc)
     I = N // 2
     got = orc.mx_dequantize(orc.E2M1, q, s, M, I)

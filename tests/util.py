@@ -78,16 +78,21 @@ def dev_i64(x, device) -> torch.Tensor:
     return torch.as_tensor(np.asarray(x, np.int64), device=device)
 
 
-# The two tile orders of the persistent kernels: "static" (no workspace) and
-# "queue" (the per-XCD tile queues in a workspace).  The queue workspace is
-# filled with 0xFF so that a launch relying on leftover counter values, rather
-# than on its own reset, hands out the wrong tiles.
+# Workspaces for the persistent kernels: "static" (none: fixed tile order),
+# "queue" (the per-XCD tile queues), "swz" (the full size for an MX forward of
+# the given shape: queues plus stage-major copies of the scales).  They are
+# filled with 0xFF so that a launch relying on leftover contents, rather than
+# on what it writes first, goes wrong.
 SCHEDS = ["static", "queue"]
+MX_SCHEDS = ["static", "queue", "swz"]
 
 
-def make_ws(device, sched):
+def make_ws(device, sched, G=1, M=1, N=1, K=32, dtype=None):
     if sched == "static":
         return None
     import moe_expert_grouped_gemm_amd as ptm
-    n = ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 1, 1, 1, 1, ptm.PT_BF16)
+    if sched == "queue":
+        n = ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 1, 1, 1, 1, ptm.PT_BF16)
+    else:
+        n = ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, G, M, N, K, dtype)
     return torch.full((n,), 0xFF, dtype=torch.uint8, device=device)
