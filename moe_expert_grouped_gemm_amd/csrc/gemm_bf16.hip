@@ -449,7 +449,9 @@ hipError_t launch_depth(const Bf16Params &p, hipStream_t s)
 // [A slot 0 | A slot 1 | B slot 0 | B slot 1], 32 KiB each, so slot and k-step
 // offsets fit the 16-bit immediates of the fragment reads.
 //  - reduction-contiguous: [256 rows][128 B], chunk c of row r at position
-//    c ^ (r & 7); the chunk 2j + h a lane reads is at base ^ (j << 5);
+//    c ^ ((r >> 1) & 7), so that the 16 lanes of a ds_read_b128 pass, reading
+//    one chunk of 16 consecutive rows, cover all 64 banks; the chunk 2j + h a
+//    lane reads is at base ^ (j << 5);
 //  - column-contiguous: [64 k][512 B], chunk c of k-row k at c ^ ((k & 3) << 2),
 //    read with ds_read_b64_tr_b16 (four k values of one column per lane).
 constexpr int WBM = 256, WBN = 256, WTHREADS = 512;
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 
     // ---- per-lane fragment bases (slot 0; slot 1 is + WSLOT by immediate)
     // reduction-contiguous: chunk 2j + h of the lane's first row at base ^ (j << 5)
-    const uint32_t y = (uint32_t)((h ^ (r32 & 7)) & 1) * 16u | (uint32_t)((r32 & 6) << 4);
+    const uint32_t y = (uint32_t)((h ^ (r32 >> 1)) & 1) * 16u | (uint32_t)(((r32 >> 1) & 6) << 4);
     const uint32_t aK = lds0 + (uint32_t)(wm * 64 + r32) * 128u + y;
     const uint32_t bK = lds0 + WB_REGION + (uint32_t)(wn * 128 + r32) * 128u + y;
     // column-contiguous: transposing reads of k-rows h*8 + s16/4 (+4), columns
@@ -557,9 +559,9 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         }
     }
     // ---- per-thread load slots: reduction-contiguous row i*64 + t/8, chunk
-    // (t & 7) ^ ((t >> 3) & 7); column-contiguous k-row i*16 + t/32, chunk
+    // (t & 7) ^ ((t >> 4) & 7); column-contiguous k-row i*16 + t/32, chunk
     // (t & 31) ^ (((t >> 5) & 3) << 2)
-    const int kc_row = tid >> 3, kc_chunk = (tid & 7) ^ ((tid >> 3) & 7);
+    const int kc_row = tid >> 3, kc_chunk = (tid & 7) ^ ((tid >> 4) & 7);
     const int nc_row = tid >> 5, nc_chunk = (tid & 31) ^ (((tid >> 5) & 3) << 2);
 
     for (int tile = tq.first(s_id); tile < total;) {

@@ -450,10 +450,12 @@ __global__ __launch_bounds__(kThreads, 2) void gg_mx_kernel(MxParams p)
 // kt+1 go out at the start of stage kt and land while it computes.
 //
 // LDS rows are 128 bytes, chunk c (16 bytes) of row r at position
-// c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows hit 8
-// different bank groups.  A lane reads chunks 2j + h of its rows; with the
-// row's base 128-byte aligned, the address of chunk 2j + h is
-// base ^ (j << 5) for a per-lane base that folds in h and r & 7.
+// c ^ ((r >> 1) & 7).  ds_read_b128 serves 16 lanes per pass, and the same
+// chunk of 16 consecutive rows then covers all 64 banks (with c ^ (r & 7),
+// rows r and r + 8 collided: a 2-way conflict on every read, measured as
+// 46% of the LDS's busy cycles).  A lane reads chunks 2j + h of its rows;
+// with the row's base 128-byte aligned, the address of chunk 2j + h is
+// base ^ (j << 5) for a per-lane base that folds in h and (r >> 1) & 7.
 //
 // Per stage a row holds 4 scale blocks (E4M3) or 8 (E2M1, K % 256 == 0).
 constexpr int WBM = 256, WBN = 256, WROW = 128, WTHREADS = 512;
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
     // A row / B row is at base ^ (j << 5)
     uint32_t aB[2], bB[2];
     {
-        const uint32_t y = (uint32_t)((h ^ (r32 & 7)) & 1) * 16u | (uint32_t)((r32 & 6) << 4);
+        const uint32_t y = (uint32_t)((h ^ (r32 >> 1)) & 1) * 16u | (uint32_t)(((r32 >> 1) & 6) << 4);
         const uint32_t ra = (uint32_t)(wm * 64 + r32), rb = (uint32_t)(wn * 128 + r32);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -627,7 +629,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         const int vr = min(WBM, rows - m0) - wm * 64;
         const int nvalid_bi = vr <= 0 ? 0 : (vr > 32 ? 2 : 1);
 
-        // ---- operand loads: slot i * 512 + t holds chunk c = (t & 7) ^ ((t >> 3) & 7)
+        // ---- operand loads: slot i * 512 + t holds chunk c = (t & 7) ^ ((t >> 4) & 7)
         // of tile row i * 64 + t / 8
         WOps o;
         o.b_once = tm == 1;      // an expert within one row block: no other tile reads its weights
@@ -635,7 +637,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         o.abytes = (uint32_t)rows * Kb;
         o.b = p.b + (int64_t)g * p.N * Kb;
         o.bbytes = (uint32_t)p.N * Kb;
-        o.chunk = (uint32_t)(((tid & 7) ^ ((tid >> 3) & 7)) * 16);
+        o.chunk = (uint32_t)(((tid & 7) ^ ((tid >> 4) & 7)) * 16);
         o.avoff = (uint32_t)(m0 + (tid >> 3)) * Kb + o.chunk;
 #pragma unroll
         for (int i = 0; i < W_LOADS; ++i) o.adelta[i] = (uint32_t)(i * 64) * Kb;
