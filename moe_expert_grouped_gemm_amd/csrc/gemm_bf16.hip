@@ -455,25 +455,25 @@ hipError_t launch_depth(const Bf16Params &p, hipStream_t s)
 //    column per lane).
 constexpr int WBM = 256, WBN = 256, WTHREADS = 512;
 
-// Ring shapes: WK reduction values per stage, NSLOT slots.
-//   0: 64-deep stages, 2 slots (128-byte rows: whole lines per load);
-//   1: 32-deep stages, 4 slots (three stages in flight).
+// Ring shapes: reduction values per stage and slots, for A and for B.
+//   0: both 64-deep in 2 slots (128-byte rows: whole lines per load);
+//   1: both 32-deep in 4 slots (three stages in flight);
+//   2: A 64-deep in 2 slots, B 32-deep in 4 slots: a column-contiguous B
+//      three stages ahead while A keeps whole-line rows.  The k-loop steps
+//      through B's 32-deep stages; A's stage a serves steps 2a and 2a + 1.
 template <int RING>
 struct WRing {
-    static constexpr int WK = RING == 0 ? 64 : 32;
-    static constexpr int NSLOT = RING == 0 ? 2 : 4;
-    static constexpr int ROWB = WK * 2;                  // bytes of a reduction-contiguous row per stage
-    static constexpr int KCPR = ROWB / 16;               // 16-byte chunks per such row
-    static constexpr int SLOT = 256 * ROWB;              // one operand's stage
-    static constexpr int B_REGION = NSLOT * SLOT;        // B slots start here
-    static constexpr int BYTES = 2 * NSLOT * SLOT;       // 128 KiB
-    static constexpr int LOADS = SLOT / 16 / WTHREADS;   // per operand per thread per stage
-    static constexpr int RPL = WTHREADS / KCPR;          // reduction-contiguous rows per load
-    static constexpr int KSTEPS = WK / 16;
-    static constexpr int WAIT = (NSLOT - 2) * 2 * LOADS; // loads of the stages after the next one
+    static constexpr int WKA = RING == 1 ? 32 : 64, NSA = RING == 1 ? 4 : 2;
+    static constexpr int WKB = RING == 0 ? 64 : 32, NSB = RING == 0 ? 2 : 4;
+    static constexpr int ROWBA = WKA * 2, KCPRA = ROWBA / 16, SLOTA = 256 * ROWBA;
+    static constexpr int ROWBB = WKB * 2, KCPRB = ROWBB / 16, SLOTB = 256 * ROWBB;
+    static constexpr int B_REGION = NSA * SLOTA;          // B slots start here
+    static constexpr int BYTES = B_REGION + NSB * SLOTB;  // 128 KiB
+    static constexpr int NLA = SLOTA / 16 / WTHREADS, NLB = SLOTB / 16 / WTHREADS;
+    static constexpr int RPLA = WTHREADS / KCPRA, RPLB = WTHREADS / KCPRB;
 };
 constexpr int WRING = WRing<0>::BYTES;
-static_assert(WRing<1>::BYTES == WRING, "both ring shapes use the same LDS");
+static_assert(WRing<1>::BYTES == WRING && WRing<2>::BYTES == WRING, "every ring shape uses the same LDS");
 
 // Position of chunk c of row r in a reduction-contiguous stage: the rows of
 // a 16-row group fall on distinct 16-byte bank groups for any one chunk.
@@ -481,6 +481,15 @@ template <int KCPR>
 __device__ __forceinline__ int kswz(int r, int c)
 {
     return KCPR == 8 ? c ^ ((r >> 1) & 7) : c ^ ((r >> 2) & 3);
+}
+// Per-lane part of the fragment address of chunk 2j + h of tile row r (the
+// row base is a multiple of the row length, so chunk 2j + h is at
+// (row base + kswz_base) ^ (j << 5)).
+template <int KCPR>
+__device__ __forceinline__ uint32_t kswz_base(int r32, int h)
+{
+    const int sw = KCPR == 8 ? (r32 >> 1) & 7 : (r32 >> 2) & 3;
+    return (uint32_t)((h ^ sw) & 1) * 16u | (uint32_t)((sw & (KCPR - 2)) << 4);
 }
 
 template <int EPI>
@@ -531,8 +540,10 @@ template <int KIND, int EPI, int RING>
 __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 {
     using R = WRing<RING>;
-    constexpr int WK = R::WK, NSLOT = R::NSLOT, ROWB = R::ROWB, KCPR = R::KCPR, SLOT = R::SLOT;
-    constexpr int B_REGION = R::B_REGION, NL = R::LOADS, RPL = R::RPL;
+    static_assert(RING != 2 || KIND == kFwdNContig, "the split ring is for a column-contiguous B with a reduction-contiguous A");
+    constexpr int WKA = R::WKA, WKB = R::WKB, NSB = R::NSB;
+    constexpr int SLOTA = R::SLOTA, SLOTB = R::SLOTB, B_REGION = R::B_REGION;
+    constexpr int NLA = R::NLA, NLB = R::NLB;
     constexpr int LDS_BYTES = wide_lds_bytes<EPI>();
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     GroupTable tab;
@@ -565,10 +576,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 
     // ---- per-lane fragment bases (slot 0; other slots by immediate)
     // reduction-contiguous: chunk 2j + h of the lane's first row at base ^ (j << 5)
-    const int sw = KCPR == 8 ? (r32 >> 1) & 7 : (r32 >> 2) & 3;
-    const uint32_t y = (uint32_t)((h ^ sw) & 1) * 16u | (uint32_t)((sw & (KCPR - 2)) << 4);
-    const uint32_t aK = lds0 + (uint32_t)(wm * 64 + r32) * ROWB + y;
-    const uint32_t bK = lds0 + B_REGION + (uint32_t)(wn * 128 + r32) * ROWB + y;
+    const uint32_t aK = lds0 + (uint32_t)(wm * 64 + r32) * R::ROWBA + kswz_base<R::KCPRA>(r32, h);
+    const uint32_t bK = lds0 + B_REGION + (uint32_t)(wn * 128 + r32) * R::ROWBB + kswz_base<R::KCPRB>(r32, h);
     // column-contiguous: transposing reads of k-rows h*8 + s16/4 (+4), columns
     // 16 g16 + 4 (s16 & 3) of each 32-column block
     uint32_t aN[2], bN[4];
@@ -589,7 +598,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
     // ---- per-thread load slots: reduction-contiguous row i*RPL + t/KCPR,
     // chunk kswz(row, t % KCPR); column-contiguous k-row i*16 + t/32, chunk
     // (t & 31) ^ (((t >> 5) & 3) << 2)
-    const int kc_row = tid / KCPR, kc_chunk = kswz<KCPR>(kc_row, tid % KCPR);
+    const int ka_row = tid / R::KCPRA, ka_chunk = kswz<R::KCPRA>(ka_row, tid % R::KCPRA);
+    const int kb_row = tid / R::KCPRB, kb_chunk = kswz<R::KCPRB>(kb_row, tid % R::KCPRB);
     const int nc_row = tid >> 5, nc_chunk = (tid & 31) ^ (((tid >> 5) & 3) << 2);
 
     for (int tile = tq.first(s_id); tile < total;) {
@@ -612,14 +622,16 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         }
         const int m0 = mt * WBM;
         const int Kred = (KIND == kWgrad) ? rows : p.Kred;
-        const int nk = (Kred + WK - 1) / WK;
+        const int nka = (Kred + WKA - 1) / WKA;     // A stages
+        const int nk = (Kred + WKB - 1) / WKB;      // B stages: the steps of the k-loop
         int nvalid_bi = 2;
         if (KIND != kWgrad) {
             const int vr = min(WBM, rows - m0) - wm * 64;
             nvalid_bi = vr <= 0 ? 0 : (vr > 32 ? 2 : 1);
         }
 
-        WOp<NL> oa, ob;
+        WOp<NLA> oa;
+        WOp<NLB> ob;
         if (KIND == kWgrad) {
             // [token][i] and [token][j] slices of the expert: column-contiguous
             oa.base = p.a + (int64_t)row0 * p.lda;
@@ -629,41 +641,41 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             ob.bytes = (uint32_t)rows * p.ldb * 2;
             ob.voff = (uint32_t)(nc_row * p.ldb + min(nt * WBN + nc_chunk * 8, p.Nout - 8)) * 2;
 #pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                oa.delta[i] = (uint32_t)(i * 16 * p.lda) * 2;
-                ob.delta[i] = (uint32_t)(i * 16 * p.ldb) * 2;
-            }
-            oa.kstep = (uint32_t)WK * p.lda * 2;
-            ob.kstep = (uint32_t)WK * p.ldb * 2;
+            for (int i = 0; i < NLA; ++i) oa.delta[i] = (uint32_t)(i * 16 * p.lda) * 2;
+#pragma unroll
+            for (int i = 0; i < NLB; ++i) ob.delta[i] = (uint32_t)(i * 16 * p.ldb) * 2;
+            oa.kstep = (uint32_t)WKA * p.lda * 2;
+            ob.kstep = (uint32_t)WKB * p.ldb * 2;
         } else {
             // A: the expert's rows, reduction-contiguous; rows past its end read zeros
             oa.base = p.a + (int64_t)row0 * p.lda;
             oa.bytes = (uint32_t)rows * p.lda * 2;
-            oa.voff = (uint32_t)(m0 + kc_row) * p.lda * 2 + kc_chunk * 16;
+            oa.voff = (uint32_t)(m0 + ka_row) * p.lda * 2 + ka_chunk * 16;
 #pragma unroll
-            for (int i = 0; i < NL; ++i) oa.delta[i] = (uint32_t)(i * RPL * p.lda) * 2;
-            oa.kstep = WK * 2;
-            oa.chunk = kc_chunk * 16;
+            for (int i = 0; i < NLA; ++i) oa.delta[i] = (uint32_t)(i * R::RPLA * p.lda) * 2;
+            oa.kstep = WKA * 2;
+            oa.chunk = ka_chunk * 16;
             const uint16_t *Bg = p.b + (int64_t)g * p.b_gstride;
             ob.base = Bg;
             if (KIND == kFwdKContig) {
                 // tile rows i*RPL + t/KCPR: B rows col_of(i*RPL + t/KCPR); with
                 // SwiGLU the 64-row groups are gate j, up I+j, gate j+64, up I+j+64
                 ob.bytes = (uint32_t)p.Nout * p.ldb * 2;
-                const int n0 = col_of<EPI>(nt, kc_row, p.Nout);
-                ob.voff = (uint32_t)n0 * p.ldb * 2 + kc_chunk * 16;
+                const int n0 = col_of<EPI>(nt, kb_row, p.Nout);
+                ob.voff = (uint32_t)n0 * p.ldb * 2 + kb_chunk * 16;
 #pragma unroll
-                for (int i = 0; i < NL; ++i)
-                    ob.delta[i] = (uint32_t)(col_of<EPI>(nt, i * RPL, p.Nout) - col_of<EPI>(nt, 0, p.Nout)) * p.ldb * 2;
-                ob.kstep = WK * 2;
-                ob.chunk = kc_chunk * 16;
+                for (int i = 0; i < NLB; ++i)
+                    ob.delta[i] =
+                        (uint32_t)(col_of<EPI>(nt, i * R::RPLB, p.Nout) - col_of<EPI>(nt, 0, p.Nout)) * p.ldb * 2;
+                ob.kstep = WKB * 2;
+                ob.chunk = kb_chunk * 16;
             } else {
                 ob.bytes = (uint32_t)p.Kred * p.ldb * 2;
                 const int n = clamp8<EPI>(col_of<EPI>(nt, nc_chunk * 8, p.Nout), p.Nout);
                 ob.voff = (uint32_t)(nc_row * p.ldb + n) * 2;
 #pragma unroll
-                for (int i = 0; i < NL; ++i) ob.delta[i] = (uint32_t)(i * 16 * p.ldb) * 2;
-                ob.kstep = (uint32_t)WK * p.ldb * 2;
+                for (int i = 0; i < NLB; ++i) ob.delta[i] = (uint32_t)(i * 16 * p.ldb) * 2;
+                ob.kstep = (uint32_t)WKB * p.ldb * 2;
             }
         }
 
@@ -692,30 +704,35 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                     for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
         }
 
-        auto issue_stage = [&](int kt, int slot) {
-            wissue<KIND != kWgrad, WK>(smem + slot * SLOT, oa, kt, nk, Kred, wave);
-            wissue<KIND == kFwdKContig, WK>(smem + B_REGION + slot * SLOT, ob, kt, nk, Kred, wave, b_once);
+        auto issue_a = [&](int ka, int slot) {
+            wissue<KIND != kWgrad, WKA>(smem + slot * SLOTA, oa, ka, nka, Kred, wave);
         };
-        // fragments of k-step KS of slot P
-        auto rd = [&](auto KSC, auto PC, bf16x8 (&af)[2], bf16x8 (&bf)[4]) {
-            constexpr int KS = decltype(KSC)::value, P = decltype(PC)::value;
-            constexpr int SO = P * SLOT;
-            constexpr int NO = SO + KS * 16 * 512, NJ = 4 * 512;     // column-contiguous k-step, +4 k-rows
+        auto issue_b = [&](int kb, int slot) {
+            wissue<KIND == kFwdKContig, WKB>(smem + B_REGION + slot * SLOTB, ob, kb, nk, Kred, wave, b_once);
+        };
+        // A fragments of k-step KS of A slot S; B fragments of k-step KS of B slot S
+        auto rd_a = [&](auto KSC, auto SC, bf16x8 (&af)[2]) {
+            constexpr int KS = decltype(KSC)::value, SO = decltype(SC)::value * SLOTA;
             if constexpr (KIND == kWgrad) {
+                constexpr int NO = SO + KS * 16 * 512, NJ = 4 * 512;  // k-step, +4 k-rows
                 af[0] = join(ldsr_tr<NO>(aN[0]), ldsr_tr<NO + NJ>(aN[0]));
                 af[1] = join(ldsr_tr<NO>(aN[1]), ldsr_tr<NO + NJ>(aN[1]));
             } else {
                 const uint32_t x = aK ^ (uint32_t)(KS << 5);
                 af[0] = ldsr_b128<SO>(x);
-                af[1] = ldsr_b128<SO + 32 * ROWB>(x);
+                af[1] = ldsr_b128<SO + 32 * R::ROWBA>(x);
             }
+        };
+        auto rd_b = [&](auto KSC, auto SC, bf16x8 (&bf)[4]) {
+            constexpr int KS = decltype(KSC)::value, SO = decltype(SC)::value * SLOTB;
             if constexpr (KIND == kFwdKContig) {
                 const uint32_t x = bK ^ (uint32_t)(KS << 5);
-                bf[0] = ldsr_b128<SO + 0 * 32 * ROWB>(x);
-                bf[1] = ldsr_b128<SO + 1 * 32 * ROWB>(x);
-                bf[2] = ldsr_b128<SO + 2 * 32 * ROWB>(x);
-                bf[3] = ldsr_b128<SO + 3 * 32 * ROWB>(x);
+                bf[0] = ldsr_b128<SO + 0 * 32 * R::ROWBB>(x);
+                bf[1] = ldsr_b128<SO + 1 * 32 * R::ROWBB>(x);
+                bf[2] = ldsr_b128<SO + 2 * 32 * R::ROWBB>(x);
+                bf[3] = ldsr_b128<SO + 3 * 32 * R::ROWBB>(x);
             } else {
+                constexpr int NO = SO + KS * 16 * 512, NJ = 4 * 512;
 #pragma unroll
                 for (int bj = 0; bj < 4; ++bj) bf[bj] = join(ldsr_tr<NO>(bN[bj]), ldsr_tr<NO + NJ>(bN[bj]));
             }
@@ -729,56 +746,101 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
                 }
         };
+        bf16x8 fa[2][2], fb[2][4];
+        int kt0 = 0;
 
-        // prologue: stages 0 .. NSLOT-2, and the id of the next tile (its
-        // atomic goes out first and lands under the stages' loads)
+        // prologue, and the id of the next tile (its atomic goes out first and
+        // lands under the stages' loads)
         if (tid == 0) tq.issue();
+        if constexpr (RING == 2) {
+            issue_a(0, 0);
+            issue_b(0, 0);
+            issue_b(1, 1);
+            issue_b(2, 2);
+            wait_vmcnt<2 * NLB>();           // A stage 0 and B stage 0
+        } else {
 #pragma unroll
-        for (int st = 0; st < NSLOT - 1; ++st) issue_stage(st, st);
-        wait_vmcnt<R::WAIT>();
+            for (int st = 0; st < NSB - 1; ++st) {
+                issue_a(st, st);
+                issue_b(st, st);
+            }
+            wait_vmcnt<(NSB - 2) * (NLA + NLB)>();
+        }
         if (tid == 0) s_id[par ^ 1] = tq.resolve(tile);
         wait_lgkm0();
         barrier();
-        bf16x8 fa[2][2], fb[2][4];
-        rd(IC<0>{}, IC<0>{}, fa[0], fb[0]);
+        rd_a(IC<0>{}, IC<0>{}, fa[0]);
+        rd_b(IC<0>{}, IC<0>{}, fb[0]);
         wfrag_wait(fa[0], fb[0]);
 
-        int kt0 = 0;
+        // one step of the k-loop over B's stage kt = kt0 + P in B slot P
         auto stage = [&](auto PC) {
             constexpr int P = decltype(PC)::value;
-            constexpr int PN = (P + NSLOT - 1) % NSLOT, Q = (P + 1) % NSLOT;
+            constexpr int Q = (P + 1) % NSB;
             const int kt = kt0 + P;
-            issue_stage(kt + NSLOT - 1, PN);     // the slot stage kt-1 freed at its barrier
-            if constexpr (R::KSTEPS == 4) {
-                rd(IC<1>{}, PC, fa[1], fb[1]);
+            if constexpr (RING == 2) {
+                // A stage kt/2 sits in A slot P/2, k-steps 2(P & 1) + 0, 1; on
+                // even steps A's next stage goes out first, into the other slot
+                constexpr int SA = P >> 1, JA = 2 * (P & 1);
+                if constexpr ((P & 1) == 0) issue_a(kt / 2 + 1, SA ^ 1);
+                issue_b(kt + 3, (P + 3) & 3);
+                rd_a(IC<JA + 1>{}, IC<SA>{}, fa[1]);
+                rd_b(IC<1>{}, PC, fb[1]);
                 mma(fa[0], fb[0]);
                 wfrag_wait(fa[1], fb[1]);
-                rd(IC<2>{}, PC, fa[0], fb[0]);
                 mma(fa[1], fb[1]);
-                wfrag_wait(fa[0], fb[0]);
-                rd(IC<3>{}, PC, fa[1], fb[1]);
-                mma(fa[0], fb[0]);
-                wfrag_wait(fa[1], fb[1]);
-                mma(fa[1], fb[1]);
+                // even: B's next stage landed; odd: A's next stage too
+                if constexpr ((P & 1) == 0)
+                    wait_vmcnt<2 * NLB + NLA>();
+                else
+                    wait_vmcnt<2 * NLB>();
+                barrier();
+                if (kt + 1 < nk) {
+                    constexpr int SA1 = Q >> 1, JA1 = 2 * (Q & 1);
+                    rd_a(IC<JA1>{}, IC<SA1>{}, fa[0]);
+                    rd_b(IC<0>{}, IC<Q>{}, fb[0]);
+                    wfrag_wait(fa[0], fb[0]);
+                }
             } else {
-                rd(IC<1>{}, PC, fa[1], fb[1]);
-                mma(fa[0], fb[0]);
-                wfrag_wait(fa[1], fb[1]);
-                mma(fa[1], fb[1]);
-            }
-            // stage kt+1 landed for this wave (later stages may still be in
-            // flight), after the barrier for all waves, and every wave is
-            // done reading slot P
-            wait_vmcnt<R::WAIT>();
-            barrier();
-            if (kt + 1 < nk) {
-                rd(IC<0>{}, IC<Q>{}, fa[0], fb[0]);
-                wfrag_wait(fa[0], fb[0]);
+                constexpr int PN = (P + NSB - 1) % NSB;
+                issue_a(kt + NSB - 1, PN);       // the slot stage kt-1 freed at its barrier
+                issue_b(kt + NSB - 1, PN);
+                auto rd = [&](auto KSC, bf16x8 (&af)[2], bf16x8 (&bf)[4]) {
+                    rd_a(KSC, PC, af);
+                    rd_b(KSC, PC, bf);
+                };
+                if constexpr (WKB == 64) {
+                    rd(IC<1>{}, fa[1], fb[1]);
+                    mma(fa[0], fb[0]);
+                    wfrag_wait(fa[1], fb[1]);
+                    rd(IC<2>{}, fa[0], fb[0]);
+                    mma(fa[1], fb[1]);
+                    wfrag_wait(fa[0], fb[0]);
+                    rd(IC<3>{}, fa[1], fb[1]);
+                    mma(fa[0], fb[0]);
+                    wfrag_wait(fa[1], fb[1]);
+                    mma(fa[1], fb[1]);
+                } else {
+                    rd(IC<1>{}, fa[1], fb[1]);
+                    mma(fa[0], fb[0]);
+                    wfrag_wait(fa[1], fb[1]);
+                    mma(fa[1], fb[1]);
+                }
+                // stage kt+1 landed for this wave (later stages may still be
+                // in flight), after the barrier for all waves, and every wave
+                // is done reading slot P
+                wait_vmcnt<(NSB - 2) * (NLA + NLB)>();
+                barrier();
+                if (kt + 1 < nk) {
+                    rd_a(IC<0>{}, IC<Q>{}, fa[0]);
+                    rd_b(IC<0>{}, IC<Q>{}, fb[0]);
+                    wfrag_wait(fa[0], fb[0]);
+                }
             }
         };
-        // whole rounds of slots, then the last stages: no early exit, so the
+        // whole rounds of slots, then the last steps: no early exit, so the
         // compiler sees no path between slots that skips a stage's loads
-        if constexpr (NSLOT == 2) {
+        if constexpr (NSB == 2) {
             for (; kt0 + 2 <= nk; kt0 += 2) {
                 stage(IC<0>{});
                 stage(IC<1>{});
@@ -850,15 +912,16 @@ hipError_t launch_wide(const Bf16Params &p, hipStream_t s)
     return hipGetLastError();
 }
 
-// Ring shape per kind.  Three 32-deep stages in flight pay where the weight
-// operand is column-contiguous (forward with [G,K,N] weights, and wgrad, whose
-// operands both are): measured -1.7% on the headline FC1, -4.2% on wgrad.
-// With both operands reduction-contiguous the 64-byte rows of 32-deep stages
-// fetch half lines, and dgrad measured +18%; those kinds keep 64-deep stages.
+// Ring shape per kind: B's stages three ahead where B is column-contiguous
+// (forward with [G,K,N] weights: the split ring, A keeping 64-deep stages of
+// whole-line rows; wgrad, both operands column-contiguous: 32-deep stages in
+// 4 slots).  With both operands reduction-contiguous, 32-deep stages would
+// give them 64-byte rows (half lines; dgrad measured +18%), so those kinds
+// keep 64-deep stages in 2 slots.
 template <int KIND, int EPI>
 hipError_t launch_wide_ring(const Bf16Params &p, hipStream_t s)
 {
-    return launch_wide<KIND, EPI, KIND == kFwdKContig ? 0 : 1>(p, s);
+    return launch_wide<KIND, EPI, KIND == kFwdKContig ? 0 : KIND == kFwdNContig ? 2 : 1>(p, s);
 }
 
 __global__ void queue_reset_kernel(uint32_t *sched)
