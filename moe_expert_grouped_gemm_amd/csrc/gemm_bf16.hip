@@ -535,11 +535,48 @@ __device__ __forceinline__ void wissue(uint8_t *lds, const WOp<NL> &o, int kt, i
 }
 
 __device__ __forceinline__ void wfrag_wait(bf16x8 (&a)[2], bf16x8 (&b)[4]) { frag_wait(a, b); }
+__device__ __forceinline__ void wfrag_wait(bf16x8 (&a)[4], bf16x8 (&b)[2])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]));
+}
+// Keep the MFMAs on these fragments after the preceding asm (the barrier and
+// the reads of the next stage): an empty asm the fragments pass through.
+__device__ __forceinline__ void wfrag_pin(bf16x8 (&a)[2], bf16x8 (&b)[4])
+{
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+__device__ __forceinline__ void wfrag_pin(bf16x8 (&a)[4], bf16x8 (&b)[2])
+{
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]));
+}
 
-template <int KIND, int EPI, int RING>
+// Wave grids of the 256 x 256 tile: WL 0, 4 x 2 waves of 64 x 128 (2 x 4
+// blocks of 32 x 32); WL 1, 2 x 4 waves of 128 x 64 (4 x 2 blocks).  WL 1
+// reads half as many B fragments and twice as many A fragments per MFMA,
+// which pays when B is the column-contiguous operand: its transposing reads
+// stream from LDS at about two thirds the rate of ds_read_b128.  With
+// SwiGLU, block q < NJ / 2 of a wave holds gate columns and block
+// q + NJ / 2 the up columns of the same outputs.
+template <int WL>
+struct WGrid {
+    static constexpr int MI = WL ? 4 : 2, NJ = WL ? 2 : 4;
+    static constexpr int WM_SHIFT = WL ? 2 : 1;
+};
+// Tile column (B row of the tile) of block bj of wave wn.  The SwiGLU tile
+// columns are 64-column groups gate j, up j, gate j + 64, up j + 64.
+template <int WL, int EPI>
+__device__ __forceinline__ int wgrid_bcol(int wn, int bj)
+{
+    if (WL == 0 || EPI == kEpiNone) return wn * WGrid<WL>::NJ * 32 + bj * 32;
+    return (wn >> 1) * 128 + (wn & 1) * 32 + bj * 64;
+}
+
+template <int KIND, int EPI, int RING, int WL>
 __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 {
     using R = WRing<RING>;
+    constexpr int MI = WGrid<WL>::MI, NJ = WGrid<WL>::NJ;
+    static_assert(WL == 0 || KIND != kWgrad, "wgrad keeps the 4 x 2 wave grid");
     static_assert(RING != 2 || KIND == kFwdNContig, "the split ring is for a column-contiguous B with a reduction-contiguous A");
     constexpr int WKA = R::WKA, WKB = R::WKB, NSB = R::NSB;
     constexpr int SLOTA = R::SLOTA, SLOTB = R::SLOTB, B_REGION = R::B_REGION;
@@ -570,28 +607,29 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> WGrid<WL>::WM_SHIFT, wn = wave & ((1 << WGrid<WL>::WM_SHIFT) - 1);
+    const int wrow0 = wm * MI * 32;
     const uint32_t lds0 = lds_addr(smem);
     const int r32 = lane & 31, h = lane >> 5, g16 = (lane >> 4) & 1, s16 = lane & 15;
 
     // ---- per-lane fragment bases (slot 0; other slots by immediate)
     // reduction-contiguous: chunk 2j + h of the lane's first row at base ^ (j << 5)
-    const uint32_t aK = lds0 + (uint32_t)(wm * 64 + r32) * R::ROWBA + kswz_base<R::KCPRA>(r32, h);
-    const uint32_t bK = lds0 + B_REGION + (uint32_t)(wn * 128 + r32) * R::ROWBB + kswz_base<R::KCPRB>(r32, h);
+    const uint32_t aK = lds0 + (uint32_t)(wrow0 + r32) * R::ROWBA + kswz_base<R::KCPRA>(r32, h);
+    const uint32_t bK = lds0 + B_REGION + (uint32_t)(wgrid_bcol<WL, EPI>(wn, 0) + r32) * R::ROWBB + kswz_base<R::KCPRB>(r32, h);
     // column-contiguous: transposing reads of k-rows h*8 + s16/4 (+4), columns
     // 16 g16 + 4 (s16 & 3) of each 32-column block
-    uint32_t aN[2], bN[4];
+    uint32_t aN[MI], bN[NJ];
     {
         const int krow = h * 8 + (s16 >> 2);
         const int lo = 8 * (s16 & 1);
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
-            const int col = wm * 64 + bi * 32 + 16 * g16 + 4 * (s16 & 3);
+        for (int bi = 0; bi < MI; ++bi) {
+            const int col = wrow0 + bi * 32 + 16 * g16 + 4 * (s16 & 3);
             aN[bi] = lds0 + krow * 512 + npos(krow, col >> 3) * 16 + lo;
         }
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-            const int col = wn * 128 + bj * 32 + 16 * g16 + 4 * (s16 & 3);
+        for (int bj = 0; bj < NJ; ++bj) {
+            const int col = wgrid_bcol<WL, EPI>(wn, bj) + 16 * g16 + 4 * (s16 & 3);
             bN[bj] = lds0 + B_REGION + krow * 512 + npos(krow, col >> 3) * 16 + lo;
         }
     }
@@ -624,10 +662,10 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         const int Kred = (KIND == kWgrad) ? rows : p.Kred;
         const int nka = (Kred + WKA - 1) / WKA;     // A stages
         const int nk = (Kred + WKB - 1) / WKB;      // B stages: the steps of the k-loop
-        int nvalid_bi = 2;
+        int nvalid_bi = MI;
         if (KIND != kWgrad) {
-            const int vr = min(WBM, rows - m0) - wm * 64;
-            nvalid_bi = vr <= 0 ? 0 : (vr > 32 ? 2 : 1);
+            const int vr = min(WBM, rows - m0) - wrow0;
+            nvalid_bi = vr <= 0 ? 0 : min(MI, (vr + 31) >> 5);
         }
 
         WOp<NLA> oa;
@@ -681,25 +719,25 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 
         // Accumulators start at zero, or for an accumulating wgrad at the
         // main_grad tile itself (loads overlap the operand prologue).
-        floatx16 acc[2][4];
+        floatx16 acc[MI][NJ];
         if (KIND == kWgrad && p.accumulate) {
             const float *og = (const float *)p.out + (int64_t)g * p.o_gstride;
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
+            for (int bi = 0; bi < MI; ++bi)
 #pragma unroll
-                for (int bj = 0; bj < 4; ++bj) {
-                    const int n = nt * WBN + wn * 128 + bj * 32 + (lane & 31);
+                for (int bj = 0; bj < NJ; ++bj) {
+                    const int n = nt * WBN + wgrid_bcol<WL, EPI>(wn, bj) + (lane & 31);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int i = m0 + e_row(wm, bi, r);
+                        const int i = m0 + wrow0 + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
                         acc[bi][bj][r] = (n < p.Nout && i < p.Mout) ? og[(int64_t)i * p.ldo + n] : 0.0f;
                     }
                 }
         } else {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
         }
@@ -711,7 +749,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             wissue<KIND == kFwdKContig, WKB>(smem + B_REGION + slot * SLOTB, ob, kb, nk, Kred, wave, b_once);
         };
         // A fragments of k-step KS of A slot S; B fragments of k-step KS of B slot S
-        auto rd_a = [&](auto KSC, auto SC, bf16x8 (&af)[2]) {
+        auto rd_a = [&](auto KSC, auto SC, bf16x8 (&af)[MI]) {
             constexpr int KS = decltype(KSC)::value, SO = decltype(SC)::value * SLOTA;
             if constexpr (KIND == kWgrad) {
                 constexpr int NO = SO + KS * 16 * 512, NJ = 4 * 512;  // k-step, +4 k-rows
@@ -721,9 +759,13 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 const uint32_t x = aK ^ (uint32_t)(KS << 5);
                 af[0] = ldsr_b128<SO>(x);
                 af[1] = ldsr_b128<SO + 32 * R::ROWBA>(x);
+                if constexpr (MI == 4) {
+                    af[2] = ldsr_b128<SO + 64 * R::ROWBA>(x);
+                    af[3] = ldsr_b128<SO + 96 * R::ROWBA>(x);
+                }
             }
         };
-        auto rd_b = [&](auto KSC, auto SC, bf16x8 (&bf)[4]) {
+        auto rd_b = [&](auto KSC, auto SC, bf16x8 (&bf)[NJ]) {
             constexpr int KS = decltype(KSC)::value, SO = decltype(SC)::value * SLOTB;
             if constexpr (KIND == kFwdKContig) {
                 const uint32_t x = bK ^ (uint32_t)(KS << 5);
@@ -732,21 +774,21 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 bf[2] = ldsr_b128<SO + 2 * 32 * R::ROWBB>(x);
                 bf[3] = ldsr_b128<SO + 3 * 32 * R::ROWBB>(x);
             } else {
-                constexpr int NO = SO + KS * 16 * 512, NJ = 4 * 512;
+                constexpr int NO = SO + KS * 16 * 512, K4 = 4 * 512;
 #pragma unroll
-                for (int bj = 0; bj < 4; ++bj) bf[bj] = join(ldsr_tr<NO>(bN[bj]), ldsr_tr<NO + NJ>(bN[bj]));
+                for (int bj = 0; bj < NJ; ++bj) bf[bj] = join(ldsr_tr<NO>(bN[bj]), ldsr_tr<NO + K4>(bN[bj]));
             }
         };
-        auto mma = [&](const bf16x8 (&af)[2], const bf16x8 (&bf)[4]) {
+        auto mma = [&](const bf16x8 (&af)[MI], const bf16x8 (&bf)[NJ]) {
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
+            for (int bi = 0; bi < MI; ++bi)
                 if (bi < nvalid_bi) {
 #pragma unroll
-                    for (int bj = 0; bj < 4; ++bj)
+                    for (int bj = 0; bj < NJ; ++bj)
                         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
                 }
         };
-        bf16x8 fa[2][2], fb[2][4];
+        bf16x8 fa[2][MI], fb[2][NJ];
         int kt0 = 0;
 
         // prologue, and the id of the next tile (its atomic goes out first and
@@ -773,7 +815,12 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         rd_b(IC<0>{}, IC<0>{}, fb[0]);
         wfrag_wait(fa[0], fb[0]);
 
-        // one step of the k-loop over B's stage kt = kt0 + P in B slot P
+        // One step of the k-loop over B's stage kt = kt0 + P in B slot P.  The
+        // MFMAs of the step's last k-step run after the closing barrier, on
+        // fragments already in registers, while the first fragments of the
+        // next stage are read: the barrier lines up all waves of a SIMD, and
+        // an MFMA-free wait for those reads would idle the SIMD.  Past the
+        // last stage the reads fetch unused bytes of the ring (no branch).
         auto stage = [&](auto PC) {
             constexpr int P = decltype(PC)::value;
             constexpr int Q = (P + 1) % NSB;
@@ -788,24 +835,23 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 rd_b(IC<1>{}, PC, fb[1]);
                 mma(fa[0], fb[0]);
                 wfrag_wait(fa[1], fb[1]);
-                mma(fa[1], fb[1]);
                 // even: B's next stage landed; odd: A's next stage too
                 if constexpr ((P & 1) == 0)
                     wait_vmcnt<2 * NLB + NLA>();
                 else
                     wait_vmcnt<2 * NLB>();
                 barrier();
-                if (kt + 1 < nk) {
-                    constexpr int SA1 = Q >> 1, JA1 = 2 * (Q & 1);
-                    rd_a(IC<JA1>{}, IC<SA1>{}, fa[0]);
-                    rd_b(IC<0>{}, IC<Q>{}, fb[0]);
-                    wfrag_wait(fa[0], fb[0]);
-                }
+                constexpr int SA1 = Q >> 1, JA1 = 2 * (Q & 1);
+                rd_a(IC<JA1>{}, IC<SA1>{}, fa[0]);
+                rd_b(IC<0>{}, IC<Q>{}, fb[0]);
+                wfrag_pin(fa[1], fb[1]);
+                mma(fa[1], fb[1]);
+                wfrag_wait(fa[0], fb[0]);
             } else {
                 constexpr int PN = (P + NSB - 1) % NSB;
                 issue_a(kt + NSB - 1, PN);       // the slot stage kt-1 freed at its barrier
                 issue_b(kt + NSB - 1, PN);
-                auto rd = [&](auto KSC, bf16x8 (&af)[2], bf16x8 (&bf)[4]) {
+                auto rd = [&](auto KSC, bf16x8 (&af)[MI], bf16x8 (&bf)[NJ]) {
                     rd_a(KSC, PC, af);
                     rd_b(KSC, PC, bf);
                 };
@@ -819,23 +865,21 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                     rd(IC<3>{}, fa[1], fb[1]);
                     mma(fa[0], fb[0]);
                     wfrag_wait(fa[1], fb[1]);
-                    mma(fa[1], fb[1]);
                 } else {
                     rd(IC<1>{}, fa[1], fb[1]);
                     mma(fa[0], fb[0]);
                     wfrag_wait(fa[1], fb[1]);
-                    mma(fa[1], fb[1]);
                 }
                 // stage kt+1 landed for this wave (later stages may still be
                 // in flight), after the barrier for all waves, and every wave
                 // is done reading slot P
                 wait_vmcnt<(NSB - 2) * (NLA + NLB)>();
                 barrier();
-                if (kt + 1 < nk) {
-                    rd_a(IC<0>{}, IC<Q>{}, fa[0]);
-                    rd_b(IC<0>{}, IC<Q>{}, fb[0]);
-                    wfrag_wait(fa[0], fb[0]);
-                }
+                rd_a(IC<0>{}, IC<Q>{}, fa[0]);
+                rd_b(IC<0>{}, IC<Q>{}, fb[0]);
+                wfrag_pin(fa[1], fb[1]);
+                mma(fa[1], fb[1]);
+                wfrag_wait(fa[0], fb[0]);
             }
         };
         // whole rounds of slots, then the last steps: no early exit, so the
@@ -862,25 +906,25 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             barrier();
         }
 
-        if (KIND == kWgrad) {
+        if constexpr (KIND == kWgrad) {
             // nothing outstanding here; saying so keeps the compiler from
             // waiting for every earlier store before each one
             wait_vmcnt<0>();
             float *og = (float *)p.out + (int64_t)g * p.o_gstride;
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
+            for (int bi = 0; bi < MI; ++bi)
 #pragma unroll
-                for (int bj = 0; bj < 4; ++bj) {
-                    const int n = nt * WBN + wn * 128 + bj * 32 + (lane & 31);
+                for (int bj = 0; bj < NJ; ++bj) {
+                    const int n = nt * WBN + wgrid_bcol<WL, EPI>(wn, bj) + (lane & 31);
                     if (n >= p.Nout) continue;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int i = m0 + e_row(wm, bi, r);
+                        const int i = m0 + wrow0 + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
                         if (i < p.Mout) og[(int64_t)i * p.ldo + n] = acc[bi][bj][r];
                     }
                 }
         } else {
-            store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wm, wn);
+            store_tile_lds_w<EPI, 4, MI, NJ>(acc, smem, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wrow0, wn);
         }
         barrier();
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
@@ -888,11 +932,11 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
     }
 }
 
-template <int KIND, int EPI, int RING>
+template <int KIND, int EPI, int RING, int WL>
 hipError_t launch_wide(const Bf16Params &p, hipStream_t s)
 {
     const int lds = wide_lds_bytes<EPI>() + table_bytes(p.G);
-    auto kern = gg_bf16_wide_kernel<KIND, EPI, RING>;
+    auto kern = gg_bf16_wide_kernel<KIND, EPI, RING, WL>;
     static int configured_lds = 0;
     if (configured_lds < lds) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -921,7 +965,7 @@ hipError_t launch_wide(const Bf16Params &p, hipStream_t s)
 template <int KIND, int EPI>
 hipError_t launch_wide_ring(const Bf16Params &p, hipStream_t s)
 {
-    return launch_wide<KIND, EPI, KIND == kFwdKContig ? 0 : KIND == kFwdNContig ? 2 : 1>(p, s);
+    return launch_wide<KIND, EPI, KIND == kFwdKContig ? 0 : KIND == kFwdNContig ? 2 : 1, KIND == kFwdNContig ? 1 : 0>(p, s);
 }
 
 __global__ void queue_reset_kernel(uint32_t *sched)

@@ -232,43 +232,47 @@ __device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], void *out
 // write land on different banks.  Phase 2: whole rows leave as 16-byte
 // stores, or, for MXFP4, each thread encodes one 32-value block held in its
 // own registers (amax, shared E8M0 byte, codes) and stores its 16 code bytes
-// and its scale byte.  Tile columns: kEpiNone 256 (nt * 256 + c), SwiGLU 128
-// outputs (nt * 128 + c, c = wn * 64 + bj * 32 + lane % 32).
+// and its scale byte.  A wave holds MI x NJ blocks of 32 x 32 starting at
+// tile row wrow0: tile columns kEpiNone 256 (nt * 256 + c, c = wn * NJ * 32 +
+// bj * 32 + lane % 32), SwiGLU 128 outputs (nt * 128 + c, c = wn * NJ * 16 +
+// q * 32 + lane % 32 from gate block q and up block q + NJ / 2).
 template <int EPI>
 __host__ __device__ constexpr int epi_row_bytes() { return (EPI == kEpiNone ? BN : BN / 2) * 2 + 16; }
 template <int EPI, int NWM>
 __host__ __device__ constexpr int epi_lds_bytes() { return 64 * NWM * epi_row_bytes<EPI>(); }
 
-template <int EPI, int NWM>
-__device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[2][4], uint8_t *smem, void *out,
-                                               uint8_t *out_scale, int ldo, int Nout, int64_t row0, int m0, int rows,
-                                               int nt, int wm, int wn)
+template <int EPI, int NWM, int MI, int NJ>
+__device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], uint8_t *smem, void *out,
+                                                 uint8_t *out_scale, int ldo, int Nout, int64_t row0, int m0,
+                                                 int rows, int nt, int wrow0, int wn)
 {
     constexpr int TR = 64 * NWM;                           // tile rows
     constexpr int OC = EPI == kEpiNone ? BN : BN / 2;      // output columns of the tile
     constexpr int RS = epi_row_bytes<EPI>();
     constexpr int NT = NWM * 2 * kWave;
     const int lane = threadIdx.x & 63;
+    auto row_of = [&](int bi, int r) { return wrow0 + bi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };
     if (EPI == kEpiNone) {
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
+        for (int bi = 0; bi < MI; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < 4; ++bj) {
-                const int c = wn * 128 + bj * 32 + (lane & 31);
+            for (int bj = 0; bj < NJ; ++bj) {
+                const int c = wn * NJ * 32 + bj * 32 + (lane & 31);
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    *(uint16_t *)(smem + e_row(wm, bi, r) * RS + c * 2) = (uint16_t)bf16_rne(acc[bi][bj][r]);
+                    *(uint16_t *)(smem + row_of(bi, r) * RS + c * 2) = (uint16_t)bf16_rne(acc[bi][bj][r]);
             }
     } else {
+        // blocks q < NJ / 2 hold gate columns, block q + NJ / 2 the matching up columns
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
+        for (int bi = 0; bi < MI; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj) {
-                const int c = wn * 64 + bj * 32 + (lane & 31);
+            for (int q = 0; q < NJ / 2; ++q) {
+                const int c = wn * NJ * 16 + q * 32 + (lane & 31);
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    *(uint16_t *)(smem + e_row(wm, bi, r) * RS + c * 2) =
-                        (uint16_t)bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r]));
+                    *(uint16_t *)(smem + row_of(bi, r) * RS + c * 2) =
+                        (uint16_t)bf16_rne(silu_mul(acc[bi][q][r], acc[bi][q + NJ / 2][r]));
             }
     }
     __syncthreads();
@@ -319,6 +323,16 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[2][4], uint
     // their acknowledgement, since vmcnt counts stores too).
     wait_lgkm0();
     barrier();
+}
+
+// The same for a wave grid of NWM x 2 waves, wave (wm, wn) holding rows
+// wm * 64 + bi * 32 + .. and columns wn * 128 + bj * 32 + lane % 32.
+template <int EPI, int NWM>
+__device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[2][4], uint8_t *smem, void *out,
+                                               uint8_t *out_scale, int ldo, int Nout, int64_t row0, int m0, int rows,
+                                               int nt, int wm, int wn)
+{
+    store_tile_lds_w<EPI, NWM, 2, 4>(acc, smem, out, out_scale, ldo, Nout, row0, m0, rows, nt, wm * 64, wn);
 }
 
 // ------------------------------------------------------------------ tile queues
