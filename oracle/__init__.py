@@ -70,6 +70,8 @@ def lib():
         L.orc_wgrad_rows.argtypes = [p, p, p, i64, i64, i64, i64, p, p, i64, p]
         L.orc_swiglu.restype = None
         L.orc_swiglu.argtypes = [p, i64, i64, p]
+        L.orc_swiglu_bwd.restype = None
+        L.orc_swiglu_bwd.argtypes = [p, p, i64, i64, p]
         L.orc_threads.restype = i32
         L.orc_threads.argtypes = []
         _lib = L
@@ -167,6 +169,17 @@ def swiglu(c: np.ndarray) -> np.ndarray:
     return h
 
 
+def swiglu_bwd(dh: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """Gradient of c = [gate | up] ([n, 2I]) given dh = d(silu(gate) * up) ([n, I])."""
+    dh, c = _c(dh, np.float64), _c(c, np.float64)
+    n, I = dh.shape
+    if c.shape != (n, 2 * I):
+        raise ValueError("c must be [n, 2I] for dh [n, I]")
+    dc = np.empty((n, 2 * I), np.float64)
+    lib().orc_swiglu_bwd(_ptr(dh), _ptr(c), n, I, _ptr(dc))
+    return dc
+
+
 # ------------------------------------------------------------------ GEMMs
 def _operand(dtype, x):
     return _c(x, np.uint16 if dtype == BF16 else np.uint8)
@@ -233,6 +246,22 @@ def grouped_fwd(dtype, a, a_scale, b, b_scale, group_lens, N, K, trans_b, epilog
     if epilogue == EPI_SWIGLU_MXFP4:
         out["q"], out["s"] = mx_quantize(hb, E2M1, axis=1)
     return out
+
+
+def dgrad_swiglu_rows(dy, b, c_saved, group_lens, N, K, trans_b, rows):
+    """FC2's data gradient followed by the SwiGLU backward, for the listed rows.
+
+    dH = dY_g @ B_g^T is rounded to bf16 (what the data gradient stores), then
+    the gradient of FC1's output [gate | up] (c_saved, bf16 bits [M, 2K]) is
+    formed in binary64.  Returns "dh_bf16" (uint16 [n, K]), "exact" (binary64
+    [n, 2K] before the final rounding) and "bf16" (its bf16 bits).
+    """
+    rows = _c(rows, np.int64)
+    dh = dgrad_rows(dy, b, group_lens, N, K, trans_b, rows)
+    dhb = round_bf16(dh)
+    c = bf16_to_f64(_c(c_saved, np.uint16)[rows])
+    dc = swiglu_bwd(bf16_to_f64(dhb), c)
+    return {"dh_bf16": dhb, "exact": dc, "bf16": round_bf16(dc)}
 
 
 def wgrad_accumulate(main_grad_in: np.ndarray, d_exact: np.ndarray, accumulate: bool) -> np.ndarray:

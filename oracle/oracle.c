@@ -419,6 +419,21 @@ void orc_swiglu(const double *c, int64_t nrows, int64_t N, double *h)
         }
 }
 
+/* Backward of the SwiGLU above.  h = silu(g) * u with silu(g) = g * s,
+ * s = 1 / (1 + e^-g), so dh/du = g * s and dh/dg = u * (s + g * s * (1 - s)).
+ * dh [nrows, I] and c [nrows, 2I] = [gate | up] in; dc [nrows, 2I] out, the
+ * gradient of c in the same [gate | up] layout. */
+void orc_swiglu_bwd(const double *dh, const double *c, int64_t nrows, int64_t I, double *dc)
+{
+    for (int64_t i = 0; i < nrows; ++i)
+        for (int64_t j = 0; j < I; ++j) {
+            double g = c[i * 2 * I + j], u = c[i * 2 * I + I + j], d = dh[i * I + j];
+            double s = 1.0 / (1.0 + exp(-g));
+            dc[i * 2 * I + j] = d * u * s * (1.0 + g * (1.0 - s));
+            dc[i * 2 * I + I + j] = d * g * s;
+        }
+}
+
 int orc_threads(void)
 {
 #ifdef _OPENMP

@@ -228,6 +228,61 @@ def test_swiglu_closed_forms(orc):
     assert orc.swiglu(c[:, [4, 5, 6, 7, 0, 1, 2, 3]])[0, 1] != h[0, 1]
 
 
+
+def test_swiglu_bwd_matches_central_differences_of_forward(orc):
+    # The backward is pinned to the (separately pinned) forward: d/dg and d/du
+    # of silu(g) * u by central differences in binary64.
+    rng = np.random.default_rng(21)
+    n, I = 6, 40
+    g = rng.uniform(-8.0, 8.0, size=(n, I))
+    u = rng.uniform(-4.0, 4.0, size=(n, I))
+    dh = rng.uniform(-2.0, 2.0, size=(n, I))
+    dc = orc.swiglu_bwd(dh, np.concatenate([g, u], axis=1))
+    eps = 1e-5
+    h = lambda gg, uu: orc.swiglu(np.concatenate([gg, uu], axis=1))
+    dg_fd = dh * (h(g + eps, u) - h(g - eps, u)) / (2 * eps)
+    du_fd = dh * (h(g, u + eps) - h(g, u - eps)) / (2 * eps)
+    assert np.allclose(dc[:, :I], dg_fd, rtol=1e-8, atol=1e-9)
+    assert np.allclose(dc[:, I:], du_fd, rtol=1e-8, atol=1e-9)
+
+
+def test_swiglu_bwd_closed_forms(orc):
+    # g = 0: silu'(0) = 1/2 and silu(0) = 0.  g -> +inf: silu' -> 1, silu -> g.
+    # g -> -inf: both -> 0.  Layout: [d gate | d up], gate half first.
+    c = np.array([[0.0, 40.0, -40.0, 3.0, 5.0, 7.0]])
+    dh = np.array([[2.0, 0.5, 1.0]])
+    dc = orc.swiglu_bwd(dh, c)
+    assert dc[0, 0] == 2.0 * 3.0 * 0.5 and dc[0, 3] == 0.0
+    assert dc[0, 1] == pytest.approx(0.5 * 5.0, rel=1e-15) and dc[0, 4] == pytest.approx(0.5 * 40.0, rel=1e-15)
+    assert abs(dc[0, 2]) < 1e-14 and abs(dc[0, 5]) < 1e-14
+    with pytest.raises(ValueError):
+        orc.swiglu_bwd(dh, c[:, :4])
+
+
+def test_dgrad_swiglu_rows_composition(orc):
+    # Integer operands keep dH exact; the composed op must equal the pinned
+    # backward applied to bf16(dH) from a numpy per-expert matmul, row by row,
+    # for a sampled, unordered row list.
+    lens = np.array([5, 0, 7, 4])
+    G, K, N = 4, 24, 16
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    M = int(lens.sum())
+    rng = np.random.default_rng(22)
+    dyv = rng.integers(-3, 4, size=(M, N)).astype(np.float64)
+    bv = rng.integers(-3, 4, size=(G, K, N)).astype(np.float64)
+    cv = rng.integers(-6, 7, size=(M, 2 * K)).astype(np.float64) / 4.0
+    dy, b, c = bf16_of(dyv), bf16_of(bv), bf16_of(cv)
+    rows = np.array([15, 0, 9, 4, 5, 11])
+    for trans_b in (0, 1):
+        bb = np.ascontiguousarray(b.transpose(0, 2, 1)) if trans_b else b
+        got = orc.dgrad_swiglu_rows(dy, bb, c, lens, N, K, trans_b, rows)
+        g_of = np.searchsorted(offs, rows, side="right") - 1
+        dh = np.stack([dyv[r] @ bv[g].T for r, g in zip(rows, g_of)])
+        assert np.array_equal(orc.bf16_to_f64(got["dh_bf16"]), dh)      # small integers: exact
+        ref = orc.swiglu_bwd(dh, cv[rows])
+        assert np.array_equal(got["exact"], ref)
+        assert np.array_equal(got["bf16"], orc.round_bf16(ref))
+
 # ------------------------------------------------------------------ GEMMs
 def _setup(G, lens, K, N, seed, trans_b=0, integer=False):
     M = int(sum(lens))
