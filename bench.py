@@ -295,6 +295,32 @@ def bench_cfg4(dev, stream, iters, lens):
                    "H=4096, I=2048", "mxfp4", flops, nbytes, per)
 
 
+def bench_fc2_bwd(dev, stream, iters, lens):
+    """FC2's data gradient with the SwiGLU backward fused into its epilogue, at
+    the expert-MLP shape in BF16 (256 experts, H = 4096, I = 2048), next to
+    the plain data gradient of the same shape."""
+    G, M, I, H = 256, int(lens.sum()), 2048, 4096
+    lens_d = torch.as_tensor(lens, device=dev)
+    dy = synth.randn_bf16((M, H), seed=111, std=1e-2, device=dev)
+    w2 = synth.randn_bf16((G, I, H), seed=112, std=H ** -0.5, device=dev)     # [G, K, N] with K = I, N = H
+    c = synth.randn_bf16((M, 2 * I), seed=113, std=2.0, device=dev)
+    dc = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    _, per_f = time_launches(lambda: ptm.pt_grouped_gemm_dgrad_swiglu(
+        dy, w2, c, dc, lens_d, None, G, M, H, I, 0, workspace=WS[0], stream=stream), iters, 2, stream)
+    _, per_p = time_launches(lambda: ptm.pt_grouped_gemm_dgrad(
+        dy, None, w2, None, dx, lens_d, None, G, M, H, I, ptm.PT_BF16, 0, workspace=WS[0], stream=stream),
+        iters, 2, stream)
+    flops = 2.0 * M * I * H
+    w_bytes = bytes_weights(lens, I * H * 2)
+    d = summary("BF16 FC2 dgrad + fused SwiGLU backward, 256 experts, M=49152, I=2048, H=4096", "bf16", flops,
+                w_bytes + M * H * 2 + 2 * (M * 2 * I * 2), per_f,
+                {"plain_dgrad_ms_median": round(float(np.median(per_p)), 4)})
+    del dy, w2, c, dc, dx
+    torch.cuda.empty_cache()
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -377,6 +403,10 @@ def main():
         if want is None or "cfg4" in want:
             log("per_config: MXFP4 MLP")
             per["cfg4_mxfp4_mlp"] = bench_cfg4(dev, stream, iters, b_keep_lens)
+            torch.cuda.empty_cache()
+        if want is None or "fc2bwd" in want:
+            log("per_config: FC2 dgrad + SwiGLU backward")
+            per["fc2_bf16_dgrad_swiglu_bwd"] = bench_fc2_bwd(dev, stream, iters, b_keep_lens)
         line["per_config"] = per
     print(json.dumps(line), flush=True)
 

@@ -140,6 +140,32 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Grouped data gradient of FC2 with the SwiGLU backward fused into its
+ * epilogue.  The forward computes h[r, j] = silu(g) * u from FC1's output
+ * C = [gate | up] (g = C[r, j], u = C[r, K + j]) and feeds h to FC2 (blog
+ * "Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with
+ * Primus", section "MegaMoE: fusing communication into the grouped GEMM":
+ * SwiGLU between the two grouped GEMMs; Primus-Turbo README, "What's New":
+ * the expert MLP with SwiGLU folded into the grouped GEMM).  This call
+ * takes FC2's output gradient and returns the gradient of C:
+ *     dH[r, j] = bf16( sum_n dY[r, n] * B_g[j, n] )      (as pt_grouped_gemm_dgrad)
+ *     dC[r, j]     = bf16( dH * u * s * (1 + g * (1 - s)) )
+ *     dC[r, K + j] = bf16( dH * g * s ),   s = 1 / (1 + exp(-g))
+ * (the derivative of silu(g) * u; dH is rounded to bf16 first, as the
+ * unfused dgrad would store it, and the rest runs in fp32).
+ *  dy       [M, N] bf16 (gradient of FC2's output);  b  FC2's weight as in
+ *           pt_grouped_gemm_fwd (trans_b selects [G,K,N] or [G,N,K]);
+ *  c_saved  [M, 2K] bf16, FC1's output [gate | up] saved by the forward;
+ *  dc       [M, 2K] bf16 output; rows outside every expert are not written.
+ *  All four 16-byte aligned.  Requirements: N % 8 == 0, K % 8 == 0.
+ *  workspace  optional (may be NULL), as for pt_grouped_gemm_dgrad.
+ */
+int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_saved, void *dc,
+                                 const int64_t *group_lens, const int64_t *group_offs,
+                                 int64_t G, int64_t M, int64_t N, int64_t K, int trans_b,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Grouped weight gradient, accumulated into an fp32 main_grad (PR page
  * "[Megatron-LM] feat: add grouped gemm fp4 support, ...", section "Changes":
  * the weight gradient is always accumulated into weight.main_grad and the

@@ -22,7 +22,8 @@ __all__ = [
     "PT_EPI_NONE", "PT_EPI_SWIGLU", "PT_EPI_SWIGLU_MXFP4",
     "PT_OP_FWD", "PT_OP_DGRAD", "PT_OP_WGRAD",
     "load", "lib_path", "PtggError",
-    "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_wgrad",
+    "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu",
+    "pt_grouped_gemm_wgrad",
     "pt_mx_quantize", "pt_grouped_gemm_workspace_size", "pt_read_error_flags",
     "pt_status_string", "pt_version",
 ]
@@ -32,7 +33,7 @@ PT_EPI_NONE, PT_EPI_SWIGLU, PT_EPI_SWIGLU_MXFP4 = 0, 1, 2
 PT_OP_FWD, PT_OP_DGRAD, PT_OP_WGRAD = 0, 1, 2
 
 EXPORTS = (
-    "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_wgrad",
+    "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",
     "pt_mx_quantize", "pt_grouped_gemm_workspace_size", "pt_read_error_flags",
     "pt_status_string", "pt_version",
 )
@@ -65,6 +66,8 @@ def load(require_gpu: bool = True):
     L.pt_grouped_gemm_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
     L.pt_grouped_gemm_dgrad.restype = i32
     L.pt_grouped_gemm_dgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, p, sz, p]
+    L.pt_grouped_gemm_dgrad_swiglu.restype = i32
+    L.pt_grouped_gemm_dgrad_swiglu.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i32, p, sz, p]
     L.pt_grouped_gemm_wgrad.restype = i32
     L.pt_grouped_gemm_wgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
     L.pt_mx_quantize.restype = i32
@@ -126,6 +129,14 @@ def pt_grouped_gemm_dgrad(dy, dy_scale, b, b_scale, dx, group_lens, group_offs,
         _ptr(dy), _ptr(dy_scale), _ptr(b), _ptr(b_scale), _ptr(dx),
         _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_b,
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def pt_grouped_gemm_dgrad_swiglu(dy, b, c_saved, dc, group_lens, group_offs,
+                                 G, M, N, K, trans_b, workspace=None, stream=None):
+    L = load()
+    _check("pt_grouped_gemm_dgrad_swiglu", L.pt_grouped_gemm_dgrad_swiglu(
+        _ptr(dy), _ptr(b), _ptr(c_saved), _ptr(dc), _ptr(group_lens), _ptr(group_offs),
+        G, M, N, K, trans_b, _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def pt_grouped_gemm_wgrad(a, a_scale, dy, dy_scale, main_grad, group_lens, group_offs,

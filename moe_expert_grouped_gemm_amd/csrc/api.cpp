@@ -227,6 +227,46 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
     return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdNContig : kFwdKContig, kEpiNone, s); }));
 }
 
+int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_saved, void *dc,
+                                 const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
+                                 int64_t N, int64_t K, int trans_b, void *workspace, size_t workspace_bytes,
+                                 void *stream)
+{
+    int st = check_groups(group_lens, G, M);
+    if (st) return st;
+    if (N < 1 || K < 1 || N > INT32_MAX / 4 || K > INT32_MAX / 8) return PT_ERR_INVALID_ARG;
+    if (M > 0 && (!dy || !b || !c_saved || !dc)) return PT_ERR_INVALID_ARG;
+    if (trans_b != 0 && trans_b != 1) return PT_ERR_INVALID_ARG;
+    if (N % 8 || K % 8) return PT_ERR_UNSUPPORTED;
+    if (!fits31(M * N * 2) || !fits31(N * K * 2)) return PT_ERR_UNSUPPORTED;
+    if (!aligned16(dy) || !aligned16(b) || !aligned16(c_saved) || !aligned16(dc)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    // dH[r, k] = sum_n dY[r, n] B[k, n] as in pt_grouped_gemm_dgrad; the
+    // epilogue turns each bf16 dH tile into the [gate | up] gradient.
+    Bf16Params p = {};
+    p.a = (const uint16_t *)dy;
+    p.b = (const uint16_t *)b;
+    p.out = dc;
+    p.lens = group_lens;
+    p.offs = group_offs;
+    p.err = error_word(workspace, workspace_bytes);
+    p.G = (int)G;
+    p.M = M;
+    p.Kred = (int)N;
+    p.Nout = (int)K;
+    p.lda = (int)N;
+    p.ldb = trans_b ? (int)K : (int)N;
+    p.b_gstride = N * K;
+    p.ldo = (int)(2 * K);
+    p.aux = (const uint16_t *)c_saved;
+    p.ldaux = (int)(2 * K);
+    p.tilesN = (int)((K + bf16_tile_n() - 1) / bf16_tile_n());
+    p.sched = queue_words(workspace, workspace_bytes);
+    if (M == 0) return PT_OK;
+    hipStream_t s = (hipStream_t)stream;
+    return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdNContig : kFwdKContig, kEpiDSwiglu, s); }));
+}
+
 int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy, const uint8_t *dy_scale,
                           float *main_grad, const int64_t *group_lens, const int64_t *group_offs, int64_t G,
                           int64_t M, int64_t N, int64_t K, int dtype, int trans_out, int accumulate,

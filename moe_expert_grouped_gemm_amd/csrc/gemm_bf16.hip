@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 2) void gg_bf16_kernel(Bf16Params p)
                     int r, c;
                     kslot(i * kThreads + tid, r, c);
                     int n = col_of<EPI>(nt, r, p.Nout);
-                    n = EPI == kEpiNone ? min(n, p.Nout - 1) : clamp8<EPI>(n & ~7, p.Nout) + (n & 7);
+                    n = !epi_glu(EPI) ? min(n, p.Nout - 1) : clamp8<EPI>(n & ~7, p.Nout) + (n & 7);
                     db.voff[i] = (uint32_t)(n * p.ldb + c * 8) * 2;
                 }
             } else {
@@ -567,7 +567,7 @@ struct WGrid {
 template <int WL, int EPI>
 __device__ __forceinline__ int wgrid_bcol(int wn, int bj)
 {
-    if (WL == 0 || EPI == kEpiNone) return wn * WGrid<WL>::NJ * 32 + bj * 32;
+    if (WL == 0 || !epi_glu(EPI)) return wn * WGrid<WL>::NJ * 32 + bj * 32;
     return (wn >> 1) * 128 + (wn & 1) * 32 + bj * 64;
 }
 
@@ -924,7 +924,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                     }
                 }
         } else {
-            store_tile_lds_w<EPI, 4, MI, NJ>(acc, smem, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wrow0, wn);
+            store_tile_lds_w<EPI, 4, MI, NJ>(acc, smem, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wrow0, wn,
+                                             p.aux, p.ldaux);
         }
         barrier();
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
@@ -998,6 +999,12 @@ hipError_t launch_queue_reset(uint32_t *sched, hipStream_t s)
 
 hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s)
 {
+    // the SwiGLU backward epilogue exists for the 256 x 256 kernel only
+    if (epi == kEpiDSwiglu) {
+        if (kind == kFwdKContig) return launch_wide_ring<kFwdKContig, kEpiDSwiglu>(p, s);
+        if (kind == kFwdNContig) return launch_wide_ring<kFwdNContig, kEpiDSwiglu>(p, s);
+        return hipErrorInvalidValue;
+    }
     if (!bf16_narrow()) {
         if (kind == kWgrad) return launch_wide_ring<kWgrad, kEpiNone>(p, s);
         if (kind == kFwdKContig) {

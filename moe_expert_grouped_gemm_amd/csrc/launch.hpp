@@ -28,10 +28,15 @@ struct Bf16Params {
     int tilesM;        // wgrad only
     int accumulate;    // wgrad only
     uint32_t *sched;   // tile-queue counters in the workspace, or null (static order)
+    const uint16_t *aux; // SwiGLU backward: the FC1 output [gate | up] the epilogue reads
+    int ldaux;           // its row stride (elements)
 };
 
 enum Bf16Kind { kFwdKContig = 0, kFwdNContig = 1, kWgrad = 2 };
-enum Epi { kEpiNone = 0, kEpiSwiglu = 1, kEpiSwigluMxfp4 = 2 };
+// kEpiDSwiglu: the SwiGLU backward on a data gradient dH (see store_tile_lds_w).
+enum Epi { kEpiNone = 0, kEpiSwiglu = 1, kEpiSwigluMxfp4 = 2, kEpiDSwiglu = 3 };
+// Does the epilogue pair gate and up columns of one tile?
+constexpr bool epi_glu(int epi) { return epi == kEpiSwiglu || epi == kEpiSwigluMxfp4; }
 
 hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s);
 int bf16_tile_m();

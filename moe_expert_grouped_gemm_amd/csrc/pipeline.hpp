@@ -121,7 +121,7 @@ __device__ __forceinline__ void kslot(int s, int &r, int &c) { r = s >> 2; c = k
 template <int EPI>
 __device__ __forceinline__ int col_of(int nt, int c, int Nout)
 {
-    if (EPI == kEpiNone) return nt * BN + c;
+    if (!epi_glu(EPI)) return nt * BN + c;
     const int I = Nout >> 1;
     const int w = c >> 7, cc = c & 127;
     const int j = nt * (BN / 2) + w * 64 + (cc & 63);
@@ -132,7 +132,7 @@ __device__ __forceinline__ int col_of(int nt, int c, int Nout)
 template <int EPI>
 __device__ __forceinline__ int clamp8(int n, int Nout)
 {
-    if (EPI == kEpiNone) return min(n, Nout - 8);
+    if (!epi_glu(EPI)) return min(n, Nout - 8);
     const int I = Nout >> 1;
     return n < I ? min(n, I - 8) : min(n, Nout - 8);
 }
@@ -141,7 +141,7 @@ __device__ __forceinline__ int clamp8(int n, int Nout)
 template <int EPI>
 __device__ __forceinline__ int clamp1(int n, int Nout)
 {
-    if (EPI == kEpiNone) return min(n, Nout - 1);
+    if (!epi_glu(EPI)) return min(n, Nout - 1);
     const int I = Nout >> 1;
     return n < I ? min(n, I - 1) : min(n, Nout - 1);
 }
@@ -237,22 +237,23 @@ __device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], void *out
 // bj * 32 + lane % 32), SwiGLU 128 outputs (nt * 128 + c, c = wn * NJ * 16 +
 // q * 32 + lane % 32 from gate block q and up block q + NJ / 2).
 template <int EPI>
-__host__ __device__ constexpr int epi_row_bytes() { return (EPI == kEpiNone ? BN : BN / 2) * 2 + 16; }
+__host__ __device__ constexpr int epi_row_bytes() { return (epi_glu(EPI) ? BN / 2 : BN) * 2 + 16; }
 template <int EPI, int NWM>
 __host__ __device__ constexpr int epi_lds_bytes() { return 64 * NWM * epi_row_bytes<EPI>(); }
 
 template <int EPI, int NWM, int MI, int NJ>
 __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], uint8_t *smem, void *out,
                                                  uint8_t *out_scale, int ldo, int Nout, int64_t row0, int m0,
-                                                 int rows, int nt, int wrow0, int wn)
+                                                 int rows, int nt, int wrow0, int wn,
+                                                 const uint16_t *aux = nullptr, int ldaux = 0)
 {
     constexpr int TR = 64 * NWM;                           // tile rows
-    constexpr int OC = EPI == kEpiNone ? BN : BN / 2;      // output columns of the tile
+    constexpr int OC = epi_glu(EPI) ? BN / 2 : BN;         // output columns of the tile
     constexpr int RS = epi_row_bytes<EPI>();
     constexpr int NT = NWM * 2 * kWave;
     const int lane = threadIdx.x & 63;
     auto row_of = [&](int bi, int r) { return wrow0 + bi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };
-    if (EPI == kEpiNone) {
+    if (!epi_glu(EPI)) {
 #pragma unroll
         for (int bi = 0; bi < MI; ++bi)
 #pragma unroll
@@ -276,8 +277,45 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
             }
     }
     __syncthreads();
-    const int ncols = EPI == kEpiNone ? Nout : Nout / 2;   // valid output columns (multiple of 8)
-    if (EPI != kEpiSwigluMxfp4) {
+    const int ncols = epi_glu(EPI) ? Nout / 2 : Nout;      // valid output columns (multiple of 8)
+    if (EPI == kEpiDSwiglu) {
+        // SwiGLU backward: this tile holds bf16 dH for columns k of an
+        // expert's rows; with g = aux[r, k] and u = aux[r, Nout + k] (the
+        // forward's [gate | up] output), write
+        //   out[r, k] = dH * u * s * (1 + g * (1 - s)),  out[r, Nout + k] = dH * g * s,
+        // s = sigmoid(g), in fp32, each rounded once to bf16.
+        constexpr int CPR = OC / 8;
+        uint16_t *o = (uint16_t *)out + row0 * ldo;
+        const uint16_t *x = aux + row0 * ldaux;
+        for (int i = threadIdx.x; i < TR * CPR; i += NT) {
+            const int r = i / CPR, c = i % CPR;
+            const int col = nt * OC + c * 8;
+            if (m0 + r < rows && col < ncols) {
+                const int64_t row = m0 + r;
+                const uintx4 dh = *(const uintx4 *)(smem + r * RS + c * 16);
+                const uintx4 gv = *(const uintx4 *)(x + row * ldaux + col);
+                const uintx4 uv = *(const uintx4 *)(x + row * ldaux + Nout + col);
+                uintx4 dg, du;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t pg = 0, pu = 0;
+#pragma unroll
+                    for (int hlf = 0; hlf < 2; ++hlf) {
+                        const float d = __uint_as_float((dh[e] >> (16 * hlf)) << 16);
+                        const float g = __uint_as_float((gv[e] >> (16 * hlf)) << 16);
+                        const float u = __uint_as_float((uv[e] >> (16 * hlf)) << 16);
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                        pg |= bf16_rne(d * u * (sg * (1.0f + g * (1.0f - sg)))) << (16 * hlf);
+                        pu |= bf16_rne(d * (g * sg)) << (16 * hlf);
+                    }
+                    dg[e] = pg;
+                    du[e] = pu;
+                }
+                *(uintx4 *)(o + row * ldo + col) = dg;
+                *(uintx4 *)(o + row * ldo + Nout + col) = du;
+            }
+        }
+    } else if (EPI != kEpiSwigluMxfp4) {
         constexpr int CPR = OC / 8;                        // 16-byte chunks per row
         uint16_t *o = (uint16_t *)out + row0 * ldo;
         for (int i = threadIdx.x; i < TR * CPR; i += NT) {
