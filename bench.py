@@ -126,7 +126,8 @@ def make_workspace(dev):
     sizes = [ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 1, 1, 1, 1, ptm.PT_BF16),
              ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 32, 65536, 5760, 2880, ptm.PT_MXFP8_E4M3),
              ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 256, 49152, 4096, 4096, ptm.PT_MXFP4_E2M1),
-             ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 256, 49152, 4096, 2048, ptm.PT_MXFP4_E2M1)]
+             ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 256, 49152, 4096, 2048, ptm.PT_MXFP4_E2M1),
+             ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_DGRAD, 32, 65536, 5760, 2880, ptm.PT_MXFP8_E4M3)]
     WS[0] = torch.zeros(max(sizes), dtype=torch.uint8, device=dev)
 
 
@@ -257,6 +258,44 @@ def bench_cfg3(dev, stream, iters):
     f = summary("MXFP8 fwd, 32 experts (Zipf 1.1), M=65536, K=2880, N=5760", "mxfp8", flops, nbytes, per,
                 {"group_lens_min_median_max": [int(lens.min()), int(np.median(lens)), int(lens.max())]})
     return f, q
+
+
+def bench_cfg3_dgrad(dev, stream, iters):
+    """The MXFP8 workload's data gradient: dY [65536, 5760] quantised along N,
+    then the MX grouped GEMM against the weight's transposed cache (the
+    forward weight [32, 5760, 2880] quantised along N by pt_mx_quantize_t,
+    once, outside the step, like the forward's weight quantisation)."""
+    lens = synth.lens_zipf_distinct(16384, 32, 4, 1.1, seed=3)
+    G, M, K, N = 32, int(lens.sum()), 2880, 5760
+    lens_d = torch.as_tensor(lens, device=dev)
+    w = synth.randn_bf16((G, N, K), seed=104 + 1000, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    wq = torch.empty((G, K, N), dtype=torch.uint8, device=dev)
+    wsc = torch.empty((G, K, N // 32), dtype=torch.uint8, device=dev)
+    _, per_t = time_launches(lambda: ptm.pt_mx_quantize_t(w, wq, wsc, G, N, K, ptm.PT_MXFP8_E4M3, stream=stream),
+                             max(3, iters // 4), 1, stream)
+    del w
+    dy = synth.randn_bf16((M, N), seed=106, std=1e-2, device=dev)
+    dq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    ds = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        ptm.pt_mx_quantize(dy, dq, ds, M, N, ptm.PT_MXFP8_E4M3, 1, stream=stream)
+        ptm.pt_grouped_gemm_dgrad(dq, ds, wq, wsc, dx, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, 0,
+                                  workspace=WS[0], stream=stream)
+    _, per = time_launches(step, iters, 3, stream)
+    _, per_g = time_launches(lambda: ptm.pt_grouped_gemm_dgrad(
+        dq, ds, wq, wsc, dx, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, 0, workspace=WS[0], stream=stream),
+        iters, 3, stream)
+    flops = 2.0 * M * K * N
+    nbytes = (bytes_weights(lens, N * K + N * K // 32) + M * N * 2 + 2 * (M * N + M * N // 32) + M * K * 2)
+    d = summary("MXFP8 dgrad (dY quantise + grouped GEMM on the transposed weight cache), 32 experts, "
+                "M=65536, N=5760 -> K=2880", "mxfp8", flops, nbytes, per,
+                {"gemm_only_ms_median": round(float(np.median(per_g)), 4),
+                 "weight_transposed_cache_ms": round(float(np.median(per_t)), 4)})
+    del dy, dq, ds, dx, wq, wsc
+    torch.cuda.empty_cache()
+    return d
 
 
 def bench_cfg4(dev, stream, iters, lens):
@@ -399,6 +438,10 @@ def main():
         if want is None or "cfg3" in want:
             log("per_config: MXFP8")
             per["cfg3_mxfp8_fwd"], per["cfg3_mxfp8_quantize_A"] = bench_cfg3(dev, stream, iters)
+            torch.cuda.empty_cache()
+        if want is None or "cfg3dgrad" in want:
+            log("per_config: MXFP8 dgrad")
+            per["cfg3_mxfp8_dgrad"] = bench_cfg3_dgrad(dev, stream, iters)
             torch.cuda.empty_cache()
         if want is None or "cfg4" in want:
             log("per_config: MXFP4 MLP")

@@ -127,10 +127,16 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale,
  * (the grouped GEMM's backward flow, PR page "[Megatron-LM] feat: add grouped
  * gemm fp4 support, ...", Copilot overview: the grouped linear returns to the
  * standard grouped GEMM backward).
- *  dy  [M, N] bf16;  b as in pt_grouped_gemm_fwd (trans_b selects [G,K,N] or
- *  [G,N,K]);  dx  [M, K] bf16.  dtype must be PT_BF16 (MX backward returns
- *  PT_ERR_UNSUPPORTED; the scale arguments must then be NULL).
- *  Requirements: N % 8 == 0 and K % 8 == 0.
+ *  BF16: dy [M, N] bf16;  b as in pt_grouped_gemm_fwd (trans_b selects
+ *  [G,K,N] or [G,N,K]);  the scale arguments NULL.  Requirements: N % 8 == 0
+ *  and K % 8 == 0.
+ *  MX (PT_MXFP8_E4M3, PT_MXFP4_E2M1): dy [M, N] codes with dy_scale
+ *  [M, N/32] (pt_mx_quantize of dY); b the weight's transposed cache
+ *  [G, K, N] codes with b_scale [G, K, N/32] (pt_mx_quantize_t of a [G, N, K]
+ *  weight, or pt_mx_quantize of a [G, K, N] one), so trans_b must be 0;
+ *  the products are exact and the sums fp32, as in the MX forward.
+ *  Requirements: N % 32 == 0, K % 8 == 0; scales 4-byte aligned.
+ *  dx  [M, K] bf16 in both cases.
  */
 int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale,
                           const void *b, const uint8_t *b_scale, void *dx,
@@ -206,6 +212,24 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
  */
 int pt_mx_quantize(const void *x, void *q, uint8_t *scales,
                    int64_t rows, int64_t cols, int dtype, int axis, void *stream);
+
+/*
+ * Transposing OCP-MX quantisation, the transposed weight cache of the MX
+ * data gradient (PR page "[Megatron-LM] feat: add grouped gemm fp4 support,
+ * ...", section "Changes": quantised weight buffers kept next to the
+ * weight; the data gradient reduces over the weight's other dimension).
+ * For each of `batch` bf16 matrices x_b [rows, cols] (row-major, one after
+ * another) it writes the quantisation of x_b^T by the rule of
+ * pt_mx_quantize: blocks of 32 consecutive rows of x_b, so
+ *  q       E4M3: [batch, cols, rows] bytes;  E2M1: [batch, cols, rows/2]
+ *  scales  [batch, cols, rows/32] E8M0 bytes.
+ * A forward weight [G, N, K] becomes the [G, K, N] operand, packed and
+ * scaled along N, that pt_grouped_gemm_dgrad takes for MX.
+ *  dtype   PT_MXFP8_E4M3 or PT_MXFP4_E2M1.  Requirements: rows % 32 == 0,
+ *          cols % 8 == 0, batch <= 65535; x and q 16-byte aligned.
+ */
+int pt_mx_quantize_t(const void *x, void *q, uint8_t *scales,
+                     int64_t batch, int64_t rows, int64_t cols, int dtype, void *stream);
 
 /*
  * Workspace of the grouped GEMMs (optional, for every op; recommended):

@@ -24,7 +24,7 @@ __all__ = [
     "load", "lib_path", "PtggError",
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu",
     "pt_grouped_gemm_wgrad",
-    "pt_mx_quantize", "pt_grouped_gemm_workspace_size", "pt_read_error_flags",
+    "pt_mx_quantize", "pt_mx_quantize_t", "pt_grouped_gemm_workspace_size", "pt_read_error_flags",
     "pt_status_string", "pt_version",
 ]
 
@@ -34,7 +34,7 @@ PT_OP_FWD, PT_OP_DGRAD, PT_OP_WGRAD = 0, 1, 2
 
 EXPORTS = (
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",
-    "pt_mx_quantize", "pt_grouped_gemm_workspace_size", "pt_read_error_flags",
+    "pt_mx_quantize", "pt_mx_quantize_t", "pt_grouped_gemm_workspace_size", "pt_read_error_flags",
     "pt_status_string", "pt_version",
 )
 
@@ -72,6 +72,8 @@ def load(require_gpu: bool = True):
     L.pt_grouped_gemm_wgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
     L.pt_mx_quantize.restype = i32
     L.pt_mx_quantize.argtypes = [p, p, p, i64, i64, i32, i32, p]
+    L.pt_mx_quantize_t.restype = i32
+    L.pt_mx_quantize_t.argtypes = [p, p, p, i64, i64, i64, i32, p]
     L.pt_grouped_gemm_workspace_size.restype = sz
     L.pt_grouped_gemm_workspace_size.argtypes = [i32, i64, i64, i64, i64, i32]
     L.pt_read_error_flags.restype = i32
@@ -152,6 +154,12 @@ def pt_mx_quantize(x, q, scales, rows, cols, dtype, axis=1, stream=None):
     L = load()
     _check("pt_mx_quantize", L.pt_mx_quantize(
         _ptr(x), _ptr(q), _ptr(scales), rows, cols, dtype, axis, _stream(stream)))
+
+
+def pt_mx_quantize_t(x, q, scales, batch, rows, cols, dtype, stream=None):
+    L = load()
+    _check("pt_mx_quantize_t", L.pt_mx_quantize_t(
+        _ptr(x), _ptr(q), _ptr(scales), batch, rows, cols, dtype, _stream(stream)))
 
 
 def pt_grouped_gemm_workspace_size(op, G, M, N, K, dtype) -> int:

@@ -95,6 +95,55 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PT_OK : PT_ERR_HIP; }
 
 using namespace ptgg;
 
+// An MX grouped GEMM out[r, j] = sum_q A[r, q] * B_g[j, q] over a reduction of
+// K values (A [M, K] and B [G, N, K], both packed and scaled along K), with
+// epilogue `ep` (Nc columns per expert before the epilogue's pairing, output
+// row stride ldo).  Shared by the forward and the MX data gradient.
+static int mx_gemm(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale, void *out,
+                   uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
+                   int64_t N, int64_t K, int dtype, int ep, int64_t Nc, int64_t ldo, void *workspace,
+                   size_t workspace_bytes, hipStream_t s)
+{
+    if (N % 8) return PT_ERR_UNSUPPORTED;              // outputs leave in 16-byte chunks
+    if (K % 32) return PT_ERR_UNSUPPORTED;
+    if (M > 0 && (!a_scale || !b_scale)) return PT_ERR_INVALID_ARG;
+    if (!aligned4(a_scale) || !aligned4(b_scale)) return PT_ERR_MISALIGNED;
+    const int64_t kb = dtype == PT_MXFP8_E4M3 ? K : K / 2;      // code bytes per row
+    if (!fits31(M * kb) || !fits31(N * kb) || !fits31(G * N * (K / 32) + 4)) return PT_ERR_UNSUPPORTED;
+    MxParams p = {};
+    p.a = (const uint8_t *)a;
+    p.as = a_scale;
+    p.b = (const uint8_t *)b;
+    p.bs = b_scale;
+    p.out = out;
+    p.out_scale = out_scale;
+    p.lens = group_lens;
+    p.offs = group_offs;
+    p.err = error_word(workspace, workspace_bytes);
+    p.G = (int)G;
+    p.M = M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.ldo = (int)ldo;
+    const int tn = ep == kEpiNone ? mx_tile_n() : mx_tile_n() / 2;
+    p.tilesN = (int)((Nc + tn - 1) / tn);
+    p.sched = queue_words(workspace, workspace_bytes);
+    if (M == 0) return PT_OK;
+    const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
+    // a workspace with room for them gets stage-major copies of the scales
+    if (p.sched && mx_swz_possible(G, M, N, K, fmt) &&
+        workspace_bytes >= (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) + mx_swz_b_bytes(G, N, K, fmt))) {
+        uint32_t *sa = (uint32_t *)((uint8_t *)workspace + kQueueWsBytes);
+        uint32_t *sb = (uint32_t *)((uint8_t *)sa + mx_swz_a_bytes(M, K, fmt));
+        hipError_t e = launch_mx_scale_swizzle(a_scale, M, K, fmt, sa, s);
+        if (e == hipSuccess) e = launch_mx_scale_swizzle(b_scale, G * N, K, fmt, sb, s);
+        if (e != hipSuccess) return PT_ERR_HIP;
+        p.sa = sa;
+        p.sb = sb;
+    }
+    return hip_status(queued(p.sched, s, [&] { return launch_mx(p, fmt, ep, s); }));
+}
+
 extern "C" {
 
 int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale,
@@ -147,44 +196,8 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
     }
     if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) {
         if (!trans_b) return PT_ERR_UNSUPPORTED;           // scales run along K
-        if (N % 8) return PT_ERR_UNSUPPORTED;              // outputs leave in 16-byte chunks
-        if (K % 32) return PT_ERR_UNSUPPORTED;
-        if (M > 0 && (!a_scale || !b_scale)) return PT_ERR_INVALID_ARG;
-        if (!aligned4(a_scale) || !aligned4(b_scale)) return PT_ERR_MISALIGNED;
-        const int64_t kb = dtype == PT_MXFP8_E4M3 ? K : K / 2;      // code bytes per row
-        if (!fits31(M * kb) || !fits31(N * kb) || !fits31(G * N * (K / 32) + 4)) return PT_ERR_UNSUPPORTED;
-        MxParams p = {};
-        p.a = (const uint8_t *)a;
-        p.as = a_scale;
-        p.b = (const uint8_t *)b;
-        p.bs = b_scale;
-        p.out = out;
-        p.out_scale = out_scale;
-        p.lens = group_lens;
-        p.offs = group_offs;
-        p.err = error_word(workspace, workspace_bytes);
-        p.G = (int)G;
-        p.M = M;
-        p.N = (int)N;
-        p.K = (int)K;
-        p.ldo = (int)ldo;
-        const int tn = epilogue == PT_EPI_NONE ? mx_tile_n() : mx_tile_n() / 2;
-        p.tilesN = (int)((Nc + tn - 1) / tn);
-        p.sched = queue_words(workspace, workspace_bytes);
-        if (M == 0) return PT_OK;
-        const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
-        // a workspace with room for them gets stage-major copies of the scales
-        if (p.sched && mx_swz_possible(G, M, N, K, fmt) &&
-            workspace_bytes >= (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) + mx_swz_b_bytes(G, N, K, fmt))) {
-            uint32_t *sa = (uint32_t *)((uint8_t *)workspace + kQueueWsBytes);
-            uint32_t *sb = (uint32_t *)((uint8_t *)sa + mx_swz_a_bytes(M, K, fmt));
-            hipError_t e = launch_mx_scale_swizzle(a_scale, M, K, fmt, sa, s);
-            if (e == hipSuccess) e = launch_mx_scale_swizzle(b_scale, G * N, K, fmt, sb, s);
-            if (e != hipSuccess) return PT_ERR_HIP;
-            p.sa = sa;
-            p.sb = sb;
-        }
-        return hip_status(queued(p.sched, s, [&] { return launch_mx(p, fmt, ep, s); }));
+        return mx_gemm(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype, ep, Nc,
+                       ldo, workspace, workspace_bytes, s);
     }
     return PT_ERR_UNSUPPORTED;
 }
@@ -198,6 +211,16 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
     if (N < 1 || K < 1 || N > INT32_MAX / 4 || K > INT32_MAX / 4) return PT_ERR_INVALID_ARG;
     if (M > 0 && (!dy || !b || !dx)) return PT_ERR_INVALID_ARG;
     if (trans_b != 0 && trans_b != 1) return PT_ERR_INVALID_ARG;
+    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) {
+        // dY packed and scaled along N, and the weight's transposed copy
+        // [G, K, N], packed and scaled along N (pt_mx_quantize_t): the MX
+        // grouped GEMM with K outputs per row and a reduction over N
+        if (trans_b) return PT_ERR_UNSUPPORTED;
+        if (!aligned16(dy) || !aligned16(b) || !aligned16(dx)) return PT_ERR_MISALIGNED;
+        if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+        return mx_gemm(dy, dy_scale, b, b_scale, dx, nullptr, group_lens, group_offs, G, M, K, N, dtype, kEpiNone, K,
+                       K, workspace, workspace_bytes, (hipStream_t)stream);
+    }
     if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
     if (dy_scale || b_scale) return PT_ERR_INVALID_ARG;
     if (N % 8 || K % 8) return PT_ERR_UNSUPPORTED;
@@ -325,6 +348,20 @@ int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_
                                       dtype == PT_MXFP8_E4M3 ? 0 : 1, (hipStream_t)stream));
 }
 
+int pt_mx_quantize_t(const void *x, void *q, uint8_t *scales, int64_t batch, int64_t rows, int64_t cols, int dtype,
+                     void *stream)
+{
+    if (batch < 0 || rows < 0 || cols < 0 || batch > 65535) return PT_ERR_INVALID_ARG;
+    if (dtype != PT_MXFP8_E4M3 && dtype != PT_MXFP4_E2M1) return PT_ERR_UNSUPPORTED;
+    if (rows % 32 || cols % 8) return PT_ERR_UNSUPPORTED;
+    if (batch == 0 || rows == 0 || cols == 0) return PT_OK;
+    if (!x || !q || !scales) return PT_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    return hip_status(launch_quantize_t((const uint16_t *)x, (uint8_t *)q, scales, batch, rows, cols,
+                                        dtype == PT_MXFP8_E4M3 ? 0 : 1, (hipStream_t)stream));
+}
+
 size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, int64_t K, int dtype)
 {
     // the error word and the tile-queue counters; for an MX forward also the
@@ -334,6 +371,13 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, i
         const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
         if (mx_swz_possible(G, M, N, K, fmt))
             return (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) + mx_swz_b_bytes(G, N, K, fmt));
+    }
+    // the MX data gradient: K outputs per row, a reduction over N
+    if (op == PT_OP_DGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && G > 0 && M >= 0 && N > 0 &&
+        K > 0 && N % 32 == 0) {
+        const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
+        if (mx_swz_possible(G, M, K, N, fmt))
+            return (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, N, fmt) + mx_swz_b_bytes(G, K, N, fmt));
     }
     return kQueueWsBytes;
 }

@@ -88,6 +88,10 @@ hipError_t launch_queue_reset(uint32_t *sched, hipStream_t s);
 
 hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales,
                            int64_t rows, int64_t cols, int fmt, hipStream_t s);
+// batch x [rows, cols] bf16 -> the quantisation of each matrix's transpose:
+// [cols, rows] codes (blocks of 32 along rows) and [cols, rows/32] scales.
+hipError_t launch_quantize_t(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t batch, int64_t rows,
+                             int64_t cols, int fmt, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cus();

@@ -86,6 +86,59 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const uint16_t *_
     if (t < nquads) quantise8<FMT>(*(const uintx4 *)(x + t * 8), q, scales, t);
 }
 
+// Transposing quantiser: x_b [R, C] bf16 (row-major) -> q_b = the MX
+// quantisation of x_b^T, [C, R] codes with blocks of 32 consecutive rows of
+// x_b, and scales [C, R/32].  A workgroup moves a 64 x 64 tile through LDS:
+// 16-byte row loads in, then each quad of lanes takes one column and 32
+// rows (8 per lane, read down the column), and quantise8 encodes and stores
+// them as one block of the transposed output.  R % 32 == 0, C % 8 == 0.
+constexpr int TQ = 64;                 // tile rows and columns
+constexpr int TQ_RS = TQ * 2 + 4;      // LDS row stride (bytes), padded off the bank period
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void mx_quantize_t_kernel(const uint16_t *__restrict__ x,
+                                                                 uint8_t *__restrict__ q,
+                                                                 uint8_t *__restrict__ scales, int64_t R, int64_t C)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[TQ * TQ_RS];
+    const int64_t b = blockIdx.z;
+    const int64_t r0 = (int64_t)blockIdx.y * TQ, c0 = (int64_t)blockIdx.x * TQ;
+    const uint16_t *xb = x + b * R * C;
+    // 64 rows x 8 chunks of 8 columns: two 16-byte loads per thread
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int k = threadIdx.x + j * kThreads;
+        const int row = k >> 3, c8 = (k & 7) * 8;
+        uintx4 v = uintx4{0u, 0u, 0u, 0u};
+        if (r0 + row < R && c0 + c8 < C) v = *(const uintx4 *)(xb + (r0 + row) * C + c0 + c8);
+        uint32_t *d = (uint32_t *)(tile + row * TQ_RS + c8 * 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = v[e];
+    }
+    __syncthreads();
+    const int64_t RB = R / 8;          // 8-value groups per output row
+    uint8_t *qb = q + b * C * (FMT == 0 ? R : R / 2);
+    uint8_t *sb = scales + b * C * (R / 32);
+    // quads: 64 columns x 2 blocks of 32 rows; lane qq of a quad takes rows 8qq..8qq+7
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = threadIdx.x + j * kThreads;
+        const int quad = t >> 2, qq = t & 3;
+        const int col = quad & (TQ - 1), blk = quad >> 6;
+        const int rr = blk * 32 + qq * 8;
+        uintx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = *(const uint16_t *)(tile + (rr + 2 * e) * TQ_RS + col * 2);
+            const uint32_t hi = *(const uint16_t *)(tile + (rr + 2 * e + 1) * TQ_RS + col * 2);
+            v[e] = lo | (hi << 16);
+        }
+        // whole quads are in or out together (R % 32 == 0), so the DPP
+        // exchange in quantise8 only ever pairs active lanes
+        if (c0 + col < C && r0 + blk * 32 < R) quantise8<FMT>(v, qb, sb, (c0 + col) * RB + (r0 + rr) / 8);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t rows, int64_t cols,
@@ -101,6 +154,18 @@ hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales, int64
         hipLaunchKernelGGL(mx_quantize_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, scales, nquads);
     else
         hipLaunchKernelGGL(mx_quantize_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, scales, nquads);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_t(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t batch, int64_t rows,
+                             int64_t cols, int fmt, hipStream_t s)
+{
+    if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
+    const dim3 grid((unsigned)((cols + TQ - 1) / TQ), (unsigned)((rows + TQ - 1) / TQ), (unsigned)batch);
+    if (fmt == 0)
+        hipLaunchKernelGGL(mx_quantize_t_kernel<0>, grid, dim3(kThreads), 0, s, x, q, scales, rows, cols);
+    else
+        hipLaunchKernelGGL(mx_quantize_t_kernel<1>, grid, dim3(kThreads), 0, s, x, q, scales, rows, cols);
     return hipGetLastError();
 }
 
