@@ -68,6 +68,8 @@ def lib():
         L.orc_dgrad_rows.argtypes = [p, p, p, i64, i64, i64, i64, i32, p, i64, p]
         L.orc_wgrad_rows.restype = i32
         L.orc_wgrad_rows.argtypes = [p, p, p, i64, i64, i64, i64, p, p, i64, p]
+        L.orc_fp8_quantize.restype = None
+        L.orc_fp8_quantize.argtypes = [p, i64, i64, p, p, p]
         L.orc_swiglu.restype = None
         L.orc_swiglu.argtypes = [p, i64, i64, p]
         L.orc_swiglu_bwd.restype = None
@@ -155,6 +157,19 @@ def mx_quantize(x_bits: np.ndarray, dtype: int, axis: int = 1):
     if rc:
         raise ValueError("orc_mx_quantize: bad arguments")
     return q, s
+
+
+def fp8_quantize(x_bits: np.ndarray):
+    """FP8 E4M3 with one scale per matrix: x_bits [batch, ...] bf16 bits.
+    Returns (codes uint8 of x's shape, amax float32 [batch], dequant float32 [batch])."""
+    x = _c(x_bits, np.uint16)
+    batch = x.shape[0]
+    n = x.size // max(batch, 1)
+    q = np.empty(x.shape, np.uint8)
+    amax = np.empty(batch, np.float32)
+    deq = np.empty(batch, np.float32)
+    lib().orc_fp8_quantize(_ptr(x), batch, n, _ptr(q), _ptr(amax), _ptr(deq))
+    return q, amax, deq
 
 
 def mx_dequantize(dtype: int, q: np.ndarray, s: np.ndarray, rows: int, cols: int) -> np.ndarray:
@@ -246,6 +261,22 @@ def grouped_fwd(dtype, a, a_scale, b, b_scale, group_lens, N, K, trans_b, epilog
     if epilogue == EPI_SWIGLU_MXFP4:
         out["q"], out["s"] = mx_quantize(hb, E2M1, axis=1)
     return out
+
+
+def fp8_fwd_rows(a_q, a_dequant, b_q, b_dequant, group_lens, N, K, rows):
+    """Unrounded binary64 C[rows, :] for E4M3 codes with one factor per tensor:
+    the code products summed exactly (the MX product with every block scale
+    2^0), times a_dequant * b_dequant[g].  a_q [M, K], b_q [G, N, K]."""
+    rows = _c(rows, np.int64)
+    lens = _c(group_lens, np.int64)
+    a_q, b_q = _c(a_q, np.uint8), _c(b_q, np.uint8)
+    ones_a = np.full((a_q.shape[0], K // 32), 127, np.uint8)
+    ones_b = np.full((b_q.shape[0], N, K // 32), 127, np.uint8)
+    c = fwd_rows(E4M3, a_q, ones_a, b_q, ones_b, lens, N, K, 1, rows)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    g = np.searchsorted(offs, rows, side="right") - 1
+    f = float(np.float64(a_dequant)) * np.asarray(b_dequant, np.float64)[g]
+    return c * f[:, None]
 
 
 def dgrad_swiglu_rows(dy, b, c_saved, group_lens, N, K, trans_b, rows):

@@ -36,6 +36,7 @@
  *              subnormal; max 6.
  *   E8M0:      unsigned exponent, value 2^(E-127); 0xFF is NaN.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -275,6 +276,42 @@ int orc_mx_quantize(const uint16_t *x, int64_t rows, int64_t cols, int dtype,
         }
     }
     return 0;
+}
+
+/*
+ * FP8 E4M3 with one scale per matrix (current scaling; the rule is the
+ * reading stated with the library's pt_fp8_quantize): for each of `batch`
+ * matrices of n bf16 values, amax = max |x| (exact in fp32), s = 448 / amax
+ * in fp32 (1 when amax is 0; the largest finite fp32 when the quotient
+ * overflows), each code = the E4M3 value nearest to fp32(x * s) clamped to
+ * +-448 (ties to even), and dequant = fp32(1 / s).  The fp32 steps are
+ * written as float arithmetic: every one of them is a single IEEE rounding.
+ */
+void orc_fp8_quantize(const uint16_t *x, int64_t batch, int64_t n, uint8_t *q, float *amax, float *dequant)
+{
+    double vals[128];
+    int ng = positive_grid(ORC_E4M3, vals);
+    for (int64_t b = 0; b < batch; ++b) {
+        const uint16_t *xb = x + b * n;
+        float m = 0.0f;
+        for (int64_t i = 0; i < n; ++i) {
+            float v = fabsf((float)orc_bf16_value(xb[i]));
+            if (v > m)
+                m = v;
+        }
+        float s = (m == 0.0f) ? 1.0f : 448.0f / m;
+        if (isinf(s))
+            s = FLT_MAX;
+        amax[b] = m;
+        dequant[b] = 1.0f / s;
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            float v = (float)orc_bf16_value(xb[i]);
+            float y = v * s;
+            int code = nearest_code(fabs((double)y), vals, ng);
+            q[b * n + i] = (uint8_t)(((signbit(v) ? 1 : 0) << 7) | code);
+        }
+    }
 }
 
 /* ---------------------------------------------------------------- GEMMs */

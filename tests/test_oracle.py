@@ -283,6 +283,65 @@ def test_dgrad_swiglu_rows_composition(orc):
         assert np.array_equal(got["exact"], ref)
         assert np.array_equal(got["bf16"], orc.round_bf16(ref))
 
+
+def _torch_e4m3(v32):
+    """torch's float32 -> float8_e4m3fn cast (nearest, ties to even) as codes."""
+    return torch.tensor(np.asarray(v32, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_quantize_unit_scale_matches_torch_cast(orc):
+    # amax = 448 gives s = 1: every code is the plain E4M3 cast of the value
+    v = rand_bf16((4, 256), seed=70, std=60.0)
+    vf = orc.bf16_to_f64(v)
+    vf = np.clip(vf, -448, 448)
+    vf[:, 0] = 448.0                                   # pin amax of each matrix to 448
+    x = bf16_of(vf)
+    q, amax, deq = orc.fp8_quantize(x)
+    assert (amax == 448.0).all() and (deq == 1.0).all()
+    assert (q == _torch_e4m3(orc.bf16_to_f64(x))).all()
+
+
+def test_fp8_quantize_general_scale_matches_fp32_product_then_cast(orc):
+    x = rand_bf16((3, 512), seed=71, std=0.37)
+    q, amax, deq = orc.fp8_quantize(x)
+    xf = orc.bf16_to_f64(x).astype(np.float32)
+    for b in range(3):
+        m = np.float32(np.abs(xf[b]).max())
+        assert amax[b] == m
+        s = np.float32(448.0) / m                       # one IEEE fp32 division
+        assert deq[b] == np.float32(1.0) / s
+        y = np.clip(xf[b] * s, np.float32(-448), np.float32(448))   # fp32 product
+        assert (q[b] == _torch_e4m3(y)).all(), b
+
+
+def test_fp8_quantize_power_of_two_invariance_and_zero(orc):
+    x = rand_bf16((2, 128), seed=72, std=3.0)
+    q, amax, deq = orc.fp8_quantize(x)
+    x8 = bf16_of(orc.bf16_to_f64(x) * 8.0)              # exact in bf16
+    q8, amax8, deq8 = orc.fp8_quantize(x8)
+    assert (q8 == q).all() and (amax8 == 8 * amax).all() and (deq8 == 8 * deq).all()
+    z = np.zeros((1, 64), np.uint16)
+    qz, az, dz = orc.fp8_quantize(z)
+    assert (qz == 0).all() and az[0] == 0 and dz[0] == 1.0
+
+
+def test_fp8_fwd_rows_matches_dense_on_decoded_codes(orc):
+    lens = np.array([5, 0, 9, 3])
+    G, K, N = 4, 64, 40
+    M = int(lens.sum())
+    rng = np.random.default_rng(73)
+    aq = rng.integers(0, 0x7E, size=(M, K)).astype(np.uint8) | (rng.integers(0, 2, size=(M, K)) << 7).astype(np.uint8)
+    bq = rng.integers(0, 0x7E, size=(G, N, K)).astype(np.uint8)
+    ad, bd = np.float32(0.03125), np.array([1.5, 2.0, 0.25, 3.0], np.float32)
+    rows = np.array([0, 4, 13, 16, 7])
+    got = orc.fp8_fwd_rows(aq, ad, bq, bd, lens, N, K, rows)
+    dec = lambda c: torch.tensor(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    for i, r in enumerate(rows):
+        g = np.searchsorted(offs, r, side="right") - 1
+        ref = dec(aq[r]) @ dec(bq[g]).T * (float(ad) * float(bd[g]))
+        assert np.allclose(got[i], ref, rtol=1e-14, atol=0), r
+
 # ------------------------------------------------------------------ GEMMs
 def _setup(G, lens, K, N, seed, trans_b=0, integer=False):
     M = int(sum(lens))
