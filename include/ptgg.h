@@ -68,7 +68,10 @@ typedef enum {
 typedef enum {
     PT_BF16 = 0,
     PT_MXFP8_E4M3 = 1,
-    PT_MXFP4_E2M1 = 2
+    PT_MXFP4_E2M1 = 2,
+    PT_FP8_E4M3 = 3          /* E4M3 codes with one fp32 scale per tensor (current
+                                scaling, pt_fp8_quantize): the scale arguments point
+                                to fp32 factors, one for A and one per expert for B */
 } pt_dtype;
 
 typedef enum {
@@ -110,6 +113,15 @@ typedef enum {
  *  with trans_b = 0, and MX); N % 16 == 0 for SWIGLU, N % 64 == 0 for
  *  SWIGLU_MXFP4;
  *  a_scale and b_scale 4-byte aligned (else PT_ERR_MISALIGNED).
+ *  PT_FP8_E4M3 (FP8 with current scaling: the grouped linear's FP8 path
+ *  calls the grouped FP8 GEMM, PR page "[Megatron-LM] feat: add grouped gemm
+ *  fp4 support, ...", Copilot overview, and its "Changes" treat current
+ *  scaling as an FP8 recipe): a [M, K] and b [G, N, K] E4M3 codes (trans_b = 1), a_scale one
+ *  fp32 factor and b_scale [G] fp32 factors (the `dequant` outputs of
+ *  pt_fp8_quantize), read as const float *; then
+ *      C[r, :] = (sum_k a[r, k] * b_g[:, k]) * a_scale[0] * b_scale[g]
+ *  with exact code products, an fp32 sum and one fp32 product of the two
+ *  factors, before the epilogue.  Requirements as for MXFP8.
  *  workspace  optional (may be NULL): the error word and tile queues, see
  *             pt_grouped_gemm_workspace_size.
  */
@@ -230,6 +242,25 @@ int pt_mx_quantize(const void *x, void *q, uint8_t *scales,
  */
 int pt_mx_quantize_t(const void *x, void *q, uint8_t *scales,
                      int64_t batch, int64_t rows, int64_t cols, int dtype, void *stream);
+
+/*
+ * FP8 E4M3 quantisation with one scale per matrix ("current scaling": the
+ * scale comes from the tensor being quantised; PR page "[Megatron-LM] feat:
+ * add grouped gemm fp4 support, ...", "Description" and "Changes" name
+ * current scaling as an FP8 recipe).  For each of `batch` bf16 matrices x_b of
+ * rows * cols values (one after another):
+ *   amax[b]    = max |x_b|                                   (fp32, exact)
+ *   s_b        = 448 / amax[b] in fp32 (1 if amax is 0; the largest finite
+ *                fp32 if the quotient overflows)
+ *   q_b[i]     = E4M3 code nearest to clamp(fp32(x_b[i] * s_b), -448, 448),
+ *                ties to even (OCP E4M3FN)
+ *   dequant[b] = fp32(1 / s_b), the factor pt_grouped_gemm_fwd takes
+ *  q  [batch, rows, cols] bytes;  amax, dequant  [batch] fp32.
+ *  Requirements: cols % 8 == 0, batch <= 65535; x and q 16-byte aligned.
+ *  Deterministic: the maximum does not depend on the order of its atomics.
+ */
+int pt_fp8_quantize(const void *x, void *q, float *amax, float *dequant,
+                    int64_t batch, int64_t rows, int64_t cols, void *stream);
 
 /*
  * Workspace of the grouped GEMMs (optional, for every op; recommended):

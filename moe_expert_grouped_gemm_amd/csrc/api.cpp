@@ -99,16 +99,19 @@ using namespace ptgg;
 // K values (A [M, K] and B [G, N, K], both packed and scaled along K), with
 // epilogue `ep` (Nc columns per expert before the epilogue's pairing, output
 // row stride ldo).  Shared by the forward and the MX data gradient.
+// PT_FP8_E4M3 takes the same path with one fp32 scale for A (a_scale) and
+// one per expert for B (b_scale) in place of the E8M0 block scales.
 static int mx_gemm(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale, void *out,
                    uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
                    int64_t N, int64_t K, int dtype, int ep, int64_t Nc, int64_t ldo, void *workspace,
                    size_t workspace_bytes, hipStream_t s)
 {
+    const bool tensor_scales = dtype == PT_FP8_E4M3;
     if (N % 8) return PT_ERR_UNSUPPORTED;              // outputs leave in 16-byte chunks
     if (K % 32) return PT_ERR_UNSUPPORTED;
     if (M > 0 && (!a_scale || !b_scale)) return PT_ERR_INVALID_ARG;
     if (!aligned4(a_scale) || !aligned4(b_scale)) return PT_ERR_MISALIGNED;
-    const int64_t kb = dtype == PT_MXFP8_E4M3 ? K : K / 2;      // code bytes per row
+    const int64_t kb = dtype == PT_MXFP4_E2M1 ? K / 2 : K;      // code bytes per row
     if (!fits31(M * kb) || !fits31(N * kb) || !fits31(G * N * (K / 32) + 4)) return PT_ERR_UNSUPPORTED;
     MxParams p = {};
     p.a = (const uint8_t *)a;
@@ -128,10 +131,15 @@ static int mx_gemm(const void *a, const uint8_t *a_scale, const void *b, const u
     const int tn = ep == kEpiNone ? mx_tile_n() : mx_tile_n() / 2;
     p.tilesN = (int)((Nc + tn - 1) / tn);
     p.sched = queue_words(workspace, workspace_bytes);
+    if (tensor_scales) {
+        p.sfa = (const float *)a_scale;
+        p.sfb = (const float *)b_scale;
+        p.as = p.bs = nullptr;
+    }
     if (M == 0) return PT_OK;
-    const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
+    const int fmt = dtype == PT_MXFP4_E2M1 ? 1 : 0;
     // a workspace with room for them gets stage-major copies of the scales
-    if (p.sched && mx_swz_possible(G, M, N, K, fmt) &&
+    if (!tensor_scales && p.sched && mx_swz_possible(G, M, N, K, fmt) &&
         workspace_bytes >= (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) + mx_swz_b_bytes(G, N, K, fmt))) {
         uint32_t *sa = (uint32_t *)((uint8_t *)workspace + kQueueWsBytes);
         uint32_t *sb = (uint32_t *)((uint8_t *)sa + mx_swz_a_bytes(M, K, fmt));
@@ -194,8 +202,8 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
         if (M == 0) return PT_OK;
         return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdKContig : kFwdNContig, ep, s); }));
     }
-    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) {
-        if (!trans_b) return PT_ERR_UNSUPPORTED;           // scales run along K
+    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3) {
+        if (!trans_b) return PT_ERR_UNSUPPORTED;           // K-contiguous codes
         return mx_gemm(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype, ep, Nc,
                        ldo, workspace, workspace_bytes, s);
     }
@@ -346,6 +354,20 @@ int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
     return hip_status(launch_quantize((const uint16_t *)x, (uint8_t *)q, scales, rows, cols,
                                       dtype == PT_MXFP8_E4M3 ? 0 : 1, (hipStream_t)stream));
+}
+
+int pt_fp8_quantize(const void *x, void *q, float *amax, float *dequant, int64_t batch, int64_t rows, int64_t cols,
+                    void *stream)
+{
+    if (batch < 0 || rows < 0 || cols < 0 || batch > 65535) return PT_ERR_INVALID_ARG;
+    if (cols % 8) return PT_ERR_UNSUPPORTED;
+    if (batch == 0) return PT_OK;
+    if (!amax || !dequant || ((rows > 0 && cols > 0) && (!x || !q))) return PT_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q) || !aligned4(amax) || !aligned4(dequant)) return PT_ERR_MISALIGNED;
+    if (!fits31(rows * cols / 8)) return PT_ERR_UNSUPPORTED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    return hip_status(launch_fp8_quantize((const uint16_t *)x, (uint8_t *)q, amax, dequant, batch, rows * cols,
+                                          (hipStream_t)stream));
 }
 
 int pt_mx_quantize_t(const void *x, void *q, uint8_t *scales, int64_t batch, int64_t rows, int64_t cols, int dtype,

@@ -60,6 +60,8 @@ struct MxParams {
     uint32_t *sched;         // tile-queue counters in the workspace, or null (static order)
     const uint32_t *sa;      // stage-major copies of as / bs in the workspace, or null
     const uint32_t *sb;
+    const float *sfa;        // FP8 with tensor scales: A's fp32 scale (1 value), or null (MX)
+    const float *sfb;        // and each expert's B scale [G]
 };
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);
@@ -92,6 +94,11 @@ hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales,
 // [cols, rows] codes (blocks of 32 along rows) and [cols, rows/32] scales.
 hipError_t launch_quantize_t(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t batch, int64_t rows,
                              int64_t cols, int fmt, hipStream_t s);
+// FP8 E4M3 with one scale per matrix (current scaling) for batch matrices of
+// n bf16 values each: amax[b] = max|x_b|, q = e4m3(x * 448 / amax[b]),
+// dequant[b] = amax-derived factor that multiplies the codes back.
+hipError_t launch_fp8_quantize(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t batch,
+                               int64_t n, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cus();

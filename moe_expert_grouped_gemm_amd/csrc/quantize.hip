@@ -139,6 +139,71 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_t_kernel(const uint16_t 
     }
 }
 
+// ------------------------------------------------------------------ FP8, one scale per tensor
+// Current scaling: each matrix b of a batch gets s_b = 448 / max|x_b| (fp32
+// division; 1 for an all-zero matrix, the largest finite fp32 if the quotient
+// overflows), codes e4m3(clamp(x * s_b, -448, 448)) rounded to nearest even,
+// and the dequantisation factor 1 / s_b.  Pass 1 reduces max|x| into amax[b]
+// with an integer atomic max on the fp32 bits (for non-negative values the
+// bit order is the numeric order, so the result is exact and independent of
+// the order of the atomics); pass 2 encodes.
+
+__global__ void fp8_amax_zero_kernel(uint32_t *amax, int64_t batch)
+{
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < batch) __hip_atomic_store(amax + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// grid (chunks, batch): each thread folds 8-value groups, each wave combines
+// its lanes with xor shuffles and issues one atomic.
+__global__ __launch_bounds__(kThreads) void fp8_amax_kernel(const uint16_t *__restrict__ x, uint32_t *amax,
+                                                            int64_t n8)
+{
+    const int64_t b = blockIdx.y;
+    const uint16_t *xb = x + b * n8 * 8;
+    uint32_t m = 0;
+    for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < n8; t += (int64_t)gridDim.x * kThreads) {
+        const uintx4 v = *(const uintx4 *)(xb + t * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+    // bf16 magnitude bits -> fp32 bits of the same value
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_max(amax + b, m << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float fp8_tensor_scale(float amax)
+{
+    if (amax == 0.0f) return 1.0f;
+    const float s = 448.0f / amax;
+    return s > 3.402823466e+38f ? 3.402823466e+38f : s;
+}
+
+__global__ __launch_bounds__(kThreads) void fp8_encode_kernel(const uint16_t *__restrict__ x, uint8_t *__restrict__ q,
+                                                              const uint32_t *amax, float *dequant, int64_t n8)
+{
+    const int64_t b = blockIdx.y;
+    const float s = fp8_tensor_scale(__uint_as_float(amax[b]));
+    if (blockIdx.x == 0 && threadIdx.x == 0) dequant[b] = 1.0f / s;
+    const uint16_t *xb = x + b * n8 * 8;
+    uint8_t *qb = q + b * n8 * 8;
+    for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < n8; t += (int64_t)gridDim.x * kThreads) {
+        const uintx4 v = *(const uintx4 *)(xb + t * 8);
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(v[i] & 0xFFFFu) * s, -448.0f), 448.0f);
+            f[2 * i + 1] = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(v[i] >> 16) * s, -448.0f), 448.0f);
+        }
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
+        *(uintx2 *)(qb + t * 8) = uintx2{(uint32_t)w0, (uint32_t)w1};
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t rows, int64_t cols,
@@ -166,6 +231,23 @@ hipError_t launch_quantize_t(const uint16_t *x, uint8_t *q, uint8_t *scales, int
         hipLaunchKernelGGL(mx_quantize_t_kernel<0>, grid, dim3(kThreads), 0, s, x, q, scales, rows, cols);
     else
         hipLaunchKernelGGL(mx_quantize_t_kernel<1>, grid, dim3(kThreads), 0, s, x, q, scales, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t batch,
+                               int64_t n, hipStream_t s)
+{
+    if (batch == 0) return hipSuccess;
+    uint32_t *am = (uint32_t *)amax;
+    hipLaunchKernelGGL(fp8_amax_zero_kernel, dim3((unsigned)((batch + 63) / 64)), dim3(64), 0, s, am, batch);
+    const int64_t n8 = n / 8;
+    int64_t chunks = (n8 + kThreads - 1) / kThreads;
+    const int64_t cap = (int64_t)device_cus() * 8;
+    if (chunks > cap) chunks = cap;
+    if (chunks < 1) chunks = 1;
+    const dim3 grid((unsigned)chunks, (unsigned)batch);
+    hipLaunchKernelGGL(fp8_amax_kernel, grid, dim3(kThreads), 0, s, x, am, n8);
+    hipLaunchKernelGGL(fp8_encode_kernel, grid, dim3(kThreads), 0, s, x, q, am, dequant, n8);
     return hipGetLastError();
 }
 
