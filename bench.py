@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 import moe_expert_grouped_gemm_amd as ptm  # noqa: E402
 from moe_expert_grouped_gemm_amd import synth  # noqa: E402
 
-PEAK_TFLOPS = {"bf16": 2516.6, "mxfp8": 5033.2, "mxfp4": 10066.3}   # dense MFMA
+PEAK_TFLOPS = {"bf16": 2516.6, "mxfp8": 5033.2, "fp8": 5033.2, "mxfp4": 10066.3}   # dense MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "grouped-GEMM TFLOP/s (useful FLOPs) + % of dtype MFMA peak, BF16/MXFP8/MXFP4"
 
@@ -298,6 +298,43 @@ def bench_cfg3_dgrad(dev, stream, iters):
     return d
 
 
+def bench_cfg3_fp8(dev, stream, iters):
+    """The MXFP8 workload's shapes in FP8 with one scale per tensor (current
+    scaling): the activations are quantised inside the step (two passes:
+    amax, then codes), the weights once outside it."""
+    lens = synth.lens_zipf_distinct(16384, 32, 4, 1.1, seed=3)
+    G, M, K, N = 32, int(lens.sum()), 2880, 5760
+    lens_d = torch.as_tensor(lens, device=dev)
+    w = synth.randn_bf16((G, N, K), seed=104 + 1000, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    bq = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+    bamax = torch.empty((G,), dtype=torch.float32, device=dev)
+    bd = torch.empty((G,), dtype=torch.float32, device=dev)
+    ptm.pt_fp8_quantize(w, bq, bamax, bd, G, N, K, stream=stream)
+    del w
+    x = synth.randn_bf16((M, K), seed=104, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    aq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    aamax = torch.empty((1,), dtype=torch.float32, device=dev)
+    ad = torch.empty((1,), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        ptm.pt_fp8_quantize(x, aq, aamax, ad, 1, M, K, stream=stream)
+        ptm.pt_grouped_gemm_fwd(aq, ad, bq, bd, out, None, lens_d, None, G, M, N, K, ptm.PT_FP8_E4M3, 1,
+                                ptm.PT_EPI_NONE, workspace=WS[0], stream=stream)
+    _, per = time_launches(step, iters, 3, stream)
+    _, per_g = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
+        aq, ad, bq, bd, out, None, lens_d, None, G, M, N, K, ptm.PT_FP8_E4M3, 1, ptm.PT_EPI_NONE,
+        workspace=WS[0], stream=stream), iters, 3, stream)
+    flops = 2.0 * M * K * N
+    nbytes = bytes_weights(lens, N * K) + M * K * 2 * 2 + M * K + M * K + M * N * 2
+    d = summary("FP8 E4M3 with one scale per tensor (activation quantise + grouped GEMM), 32 experts, "
+                "M=65536, K=2880, N=5760", "fp8", flops, nbytes, per,
+                {"gemm_only_ms_median": round(float(np.median(per_g)), 4)})
+    del x, aq, out, bq
+    torch.cuda.empty_cache()
+    return d
+
+
 def bench_cfg4(dev, stream, iters, lens):
     G, M, H, I = 256, int(lens.sum()), 4096, 2048
     x = synth.randn_bf16((M, H), seed=105, device=dev)
@@ -438,6 +475,10 @@ def main():
         if want is None or "cfg3" in want:
             log("per_config: MXFP8")
             per["cfg3_mxfp8_fwd"], per["cfg3_mxfp8_quantize_A"] = bench_cfg3(dev, stream, iters)
+            torch.cuda.empty_cache()
+        if want is None or "cfg3fp8" in want:
+            log("per_config: FP8 with tensor scales")
+            per["cfg3_fp8_tensor_fwd"] = bench_cfg3_fp8(dev, stream, iters)
             torch.cuda.empty_cache()
         if want is None or "cfg3dgrad" in want:
             log("per_config: MXFP8 dgrad")
