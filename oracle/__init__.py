@@ -161,7 +161,8 @@ def mx_quantize(x_bits: np.ndarray, dtype: int, axis: int = 1):
 
 def fp8_quantize(x_bits: np.ndarray):
     """FP8 E4M3 with one scale per matrix: x_bits [batch, ...] bf16 bits.
-    Returns (codes uint8 of x's shape, amax float32 [batch], dequant float32 [batch])."""
+    Returns (codes uint8 of x's shape, amax float32 [batch], dequant float32 [batch]).
+    A 2-D [rows, cols] input gives one scale per row (the rowwise recipe)."""
     x = _c(x_bits, np.uint16)
     batch = x.shape[0]
     n = x.size // max(batch, 1)
@@ -277,6 +278,23 @@ def fp8_fwd_rows(a_q, a_dequant, b_q, b_dequant, group_lens, N, K, rows):
     g = np.searchsorted(offs, rows, side="right") - 1
     f = float(np.float64(a_dequant)) * np.asarray(b_dequant, np.float64)[g]
     return c * f[:, None]
+
+
+def fp8_fwd_rows_rowwise(a_q, a_dequant, b_q, b_dequant, group_lens, N, K, rows):
+    """As fp8_fwd_rows with one factor per row of A (a_dequant [M]) and per
+    row of each expert's B (b_dequant [G, N]): C[r, n] = (sum of code
+    products) * a_dequant[r] * b_dequant[g, n]."""
+    rows = _c(rows, np.int64)
+    lens = _c(group_lens, np.int64)
+    a_q, b_q = _c(a_q, np.uint8), _c(b_q, np.uint8)
+    ones_a = np.full((a_q.shape[0], K // 32), 127, np.uint8)
+    ones_b = np.full((b_q.shape[0], N, K // 32), 127, np.uint8)
+    c = fwd_rows(E4M3, a_q, ones_a, b_q, ones_b, lens, N, K, 1, rows)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    g = np.searchsorted(offs, rows, side="right") - 1
+    fa = np.asarray(a_dequant, np.float64)[rows]
+    fb = np.asarray(b_dequant, np.float64).reshape(-1, N)[g]
+    return c * fa[:, None] * fb
 
 
 def dgrad_swiglu_rows(dy, b, c_saved, group_lens, N, K, trans_b, rows):

@@ -342,6 +342,37 @@ def test_fp8_fwd_rows_matches_dense_on_decoded_codes(orc):
         ref = dec(aq[r]) @ dec(bq[g]).T * (float(ad) * float(bd[g]))
         assert np.allclose(got[i], ref, rtol=1e-14, atol=0), r
 
+
+def test_fp8_rowwise_scales_each_row_on_its_own(orc):
+    # rows of very different magnitude: each row's codes are torch's cast of
+    # fp32(x * 448 / amax_row), independent of the other rows
+    x = np.concatenate([rand_bf16((1, 96), seed=74, std=s) for s in (1e-3, 1.0, 300.0)])
+    q, amax, deq = orc.fp8_quantize(x)
+    xf = orc.bf16_to_f64(x).astype(np.float32)
+    for r in range(3):
+        s = np.float32(448.0) / np.float32(np.abs(xf[r]).max())
+        assert deq[r] == np.float32(1.0) / s
+        assert (q[r] == _torch_e4m3(np.clip(xf[r] * s, -448, 448))).all(), r
+
+
+def test_fp8_fwd_rows_rowwise_matches_dense(orc):
+    lens = np.array([4, 6, 0, 2])
+    G, K, N = 4, 32, 24
+    M = int(lens.sum())
+    rng = np.random.default_rng(75)
+    aq = rng.integers(0, 0x7E, size=(M, K)).astype(np.uint8)
+    bq = (rng.integers(0, 0x7E, size=(G, N, K)) | (rng.integers(0, 2, size=(G, N, K)) << 7)).astype(np.uint8)
+    ad = rng.uniform(0.5, 2.0, size=M).astype(np.float32)
+    bd = rng.uniform(0.01, 0.1, size=(G, N)).astype(np.float32)
+    rows = np.array([1, 9, 11, 4])
+    got = orc.fp8_fwd_rows_rowwise(aq, ad, bq, bd, lens, N, K, rows)
+    dec = lambda c: torch.tensor(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    for i, r in enumerate(rows):
+        g = np.searchsorted(offs, r, side="right") - 1
+        ref = (dec(aq[r]) @ dec(bq[g]).T) * float(ad[r]) * bd[g].astype(np.float64)
+        assert np.allclose(got[i], ref, rtol=1e-14, atol=0), r
+
 # ------------------------------------------------------------------ GEMMs
 def _setup(G, lens, K, N, seed, trans_b=0, integer=False):
     M = int(sum(lens))
