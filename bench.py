@@ -330,9 +330,25 @@ def bench_cfg3_fp8(dev, stream, iters):
     d = summary("FP8 E4M3 with one scale per tensor (activation quantise + grouped GEMM), 32 experts, "
                 "M=65536, K=2880, N=5760", "fp8", flops, nbytes, per,
                 {"gemm_only_ms_median": round(float(np.median(per_g)), 4)})
+    # rowwise: one scale per activation row and per weight row (output column)
+    bamax_r = torch.empty((G * N,), dtype=torch.float32, device=dev)
+    bd_r = torch.empty((G * N,), dtype=torch.float32, device=dev)
+    w = synth.randn_bf16((G * N, K), seed=104 + 1000, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    ptm.pt_fp8_quantize_rows(w, bq, bamax_r, bd_r, G * N, K, stream=stream)
+    del w
+    aamax_r = torch.empty((M,), dtype=torch.float32, device=dev)
+    ad_r = torch.empty((M,), dtype=torch.float32, device=dev)
+
+    def step_rows():
+        ptm.pt_fp8_quantize_rows(x, aq, aamax_r, ad_r, M, K, stream=stream)
+        ptm.pt_grouped_gemm_fwd(aq, ad_r, bq, bd_r, out, None, lens_d, None, G, M, N, K, ptm.PT_FP8_E4M3_ROWWISE, 1,
+                                ptm.PT_EPI_NONE, workspace=WS[0], stream=stream)
+    _, per_r = time_launches(step_rows, iters, 3, stream)
+    r = summary("FP8 E4M3 rowwise (one scale per row of A and of B; activation quantise + grouped GEMM), "
+                "32 experts, M=65536, K=2880, N=5760", "fp8", flops, nbytes - M * K * 2, per_r)
     del x, aq, out, bq
     torch.cuda.empty_cache()
-    return d
+    return d, r
 
 
 def bench_cfg4(dev, stream, iters, lens):
@@ -478,7 +494,7 @@ def main():
             torch.cuda.empty_cache()
         if want is None or "cfg3fp8" in want:
             log("per_config: FP8 with tensor scales")
-            per["cfg3_fp8_tensor_fwd"] = bench_cfg3_fp8(dev, stream, iters)
+            per["cfg3_fp8_tensor_fwd"], per["cfg3_fp8_rowwise_fwd"] = bench_cfg3_fp8(dev, stream, iters)
             torch.cuda.empty_cache()
         if want is None or "cfg3dgrad" in want:
             log("per_config: MXFP8 dgrad")

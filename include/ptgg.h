@@ -69,9 +69,11 @@ typedef enum {
     PT_BF16 = 0,
     PT_MXFP8_E4M3 = 1,
     PT_MXFP4_E2M1 = 2,
-    PT_FP8_E4M3 = 3          /* E4M3 codes with one fp32 scale per tensor (current
+    PT_FP8_E4M3 = 3,         /* E4M3 codes with one fp32 scale per tensor (current
                                 scaling, pt_fp8_quantize): the scale arguments point
                                 to fp32 factors, one for A and one per expert for B */
+    PT_FP8_E4M3_ROWWISE = 4  /* E4M3 codes with one fp32 scale per row of A [M] and per
+                                row of B [G, N] (pt_fp8_quantize_rows) */
 } pt_dtype;
 
 typedef enum {
@@ -122,6 +124,10 @@ typedef enum {
  *      C[r, :] = (sum_k a[r, k] * b_g[:, k]) * a_scale[0] * b_scale[g]
  *  with exact code products, an fp32 sum and one fp32 product of the two
  *  factors, before the epilogue.  Requirements as for MXFP8.
+ *  PT_FP8_E4M3_ROWWISE: the same with a_scale [M] fp32 (one factor per row
+ *  of A) and b_scale [G, N] fp32 (one per row of each expert's B, i.e. per
+ *  output column): C[r, n] = (sum_k a[r, k] * b_g[n, k]) * (a_scale[r] *
+ *  b_scale[g, n]), the two factors multiplied in fp32 first.
  *  workspace  optional (may be NULL): the error word and tile queues, see
  *             pt_grouped_gemm_workspace_size.
  */
@@ -261,6 +267,17 @@ int pt_mx_quantize_t(const void *x, void *q, uint8_t *scales,
  */
 int pt_fp8_quantize(const void *x, void *q, float *amax, float *dequant,
                     int64_t batch, int64_t rows, int64_t cols, void *stream);
+
+/*
+ * The same rule with one scale per row: for each row r of x [rows, cols]
+ * (bf16), amax[r] = max |x[r, :]|, s_r = 448 / amax[r], codes as in
+ * pt_fp8_quantize, dequant[r] = fp32(1 / s_r).  For B of a rowwise FP8
+ * GEMM pass the weights [G, N, K] as rows = G * N, cols = K.
+ *  q  [rows, cols] bytes;  amax, dequant  [rows] fp32.
+ *  Requirements: cols % 8 == 0; x and q 16-byte aligned.
+ */
+int pt_fp8_quantize_rows(const void *x, void *q, float *amax, float *dequant,
+                         int64_t rows, int64_t cols, void *stream);
 
 /*
  * Workspace of the grouped GEMMs (optional, for every op; recommended):

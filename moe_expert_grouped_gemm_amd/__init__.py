@@ -18,24 +18,24 @@ import torch
 from . import build as _build
 
 __all__ = [
-    "PT_BF16", "PT_MXFP8_E4M3", "PT_MXFP4_E2M1", "PT_FP8_E4M3",
+    "PT_BF16", "PT_MXFP8_E4M3", "PT_MXFP4_E2M1", "PT_FP8_E4M3", "PT_FP8_E4M3_ROWWISE",
     "PT_EPI_NONE", "PT_EPI_SWIGLU", "PT_EPI_SWIGLU_MXFP4",
     "PT_OP_FWD", "PT_OP_DGRAD", "PT_OP_WGRAD",
     "load", "lib_path", "PtggError",
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu",
     "pt_grouped_gemm_wgrad",
-    "pt_mx_quantize", "pt_mx_quantize_t", "pt_fp8_quantize", "pt_grouped_gemm_workspace_size",
-    "pt_read_error_flags", "pt_status_string", "pt_version",
+    "pt_mx_quantize", "pt_mx_quantize_t", "pt_fp8_quantize", "pt_fp8_quantize_rows",
+    "pt_grouped_gemm_workspace_size", "pt_read_error_flags", "pt_status_string", "pt_version",
 ]
 
-PT_BF16, PT_MXFP8_E4M3, PT_MXFP4_E2M1, PT_FP8_E4M3 = 0, 1, 2, 3
+PT_BF16, PT_MXFP8_E4M3, PT_MXFP4_E2M1, PT_FP8_E4M3, PT_FP8_E4M3_ROWWISE = 0, 1, 2, 3, 4
 PT_EPI_NONE, PT_EPI_SWIGLU, PT_EPI_SWIGLU_MXFP4 = 0, 1, 2
 PT_OP_FWD, PT_OP_DGRAD, PT_OP_WGRAD = 0, 1, 2
 
 EXPORTS = (
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",
-    "pt_mx_quantize", "pt_mx_quantize_t", "pt_fp8_quantize", "pt_grouped_gemm_workspace_size",
-    "pt_read_error_flags", "pt_status_string", "pt_version",
+    "pt_mx_quantize", "pt_mx_quantize_t", "pt_fp8_quantize", "pt_fp8_quantize_rows",
+    "pt_grouped_gemm_workspace_size", "pt_read_error_flags", "pt_status_string", "pt_version",
 )
 
 _lib = None
@@ -76,6 +76,8 @@ def load(require_gpu: bool = True):
     L.pt_mx_quantize_t.argtypes = [p, p, p, i64, i64, i64, i32, p]
     L.pt_fp8_quantize.restype = i32
     L.pt_fp8_quantize.argtypes = [p, p, p, p, i64, i64, i64, p]
+    L.pt_fp8_quantize_rows.restype = i32
+    L.pt_fp8_quantize_rows.argtypes = [p, p, p, p, i64, i64, p]
     L.pt_grouped_gemm_workspace_size.restype = sz
     L.pt_grouped_gemm_workspace_size.argtypes = [i32, i64, i64, i64, i64, i32]
     L.pt_read_error_flags.restype = i32
@@ -168,6 +170,12 @@ def pt_fp8_quantize(x, q, amax, dequant, batch, rows, cols, stream=None):
     L = load()
     _check("pt_fp8_quantize", L.pt_fp8_quantize(
         _ptr(x), _ptr(q), _ptr(amax), _ptr(dequant), batch, rows, cols, _stream(stream)))
+
+
+def pt_fp8_quantize_rows(x, q, amax, dequant, rows, cols, stream=None):
+    L = load()
+    _check("pt_fp8_quantize_rows", L.pt_fp8_quantize_rows(
+        _ptr(x), _ptr(q), _ptr(amax), _ptr(dequant), rows, cols, _stream(stream)))
 
 
 def pt_grouped_gemm_workspace_size(op, G, M, N, K, dtype) -> int:

@@ -106,7 +106,7 @@ static int mx_gemm(const void *a, const uint8_t *a_scale, const void *b, const u
                    int64_t N, int64_t K, int dtype, int ep, int64_t Nc, int64_t ldo, void *workspace,
                    size_t workspace_bytes, hipStream_t s)
 {
-    const bool tensor_scales = dtype == PT_FP8_E4M3;
+    const bool tensor_scales = dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE;
     if (N % 8) return PT_ERR_UNSUPPORTED;              // outputs leave in 16-byte chunks
     if (K % 32) return PT_ERR_UNSUPPORTED;
     if (M > 0 && (!a_scale || !b_scale)) return PT_ERR_INVALID_ARG;
@@ -134,6 +134,7 @@ static int mx_gemm(const void *a, const uint8_t *a_scale, const void *b, const u
     if (tensor_scales) {
         p.sfa = (const float *)a_scale;
         p.sfb = (const float *)b_scale;
+        p.sf_rows = dtype == PT_FP8_E4M3_ROWWISE;
         p.as = p.bs = nullptr;
     }
     if (M == 0) return PT_OK;
@@ -202,7 +203,7 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
         if (M == 0) return PT_OK;
         return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdKContig : kFwdNContig, ep, s); }));
     }
-    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3) {
+    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE) {
         if (!trans_b) return PT_ERR_UNSUPPORTED;           // K-contiguous codes
         return mx_gemm(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype, ep, Nc,
                        ldo, workspace, workspace_bytes, s);
@@ -368,6 +369,20 @@ int pt_fp8_quantize(const void *x, void *q, float *amax, float *dequant, int64_t
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
     return hip_status(launch_fp8_quantize((const uint16_t *)x, (uint8_t *)q, amax, dequant, batch, rows * cols,
                                           (hipStream_t)stream));
+}
+
+int pt_fp8_quantize_rows(const void *x, void *q, float *amax, float *dequant, int64_t rows, int64_t cols,
+                         void *stream)
+{
+    if (rows < 0 || cols < 0) return PT_ERR_INVALID_ARG;
+    if (cols % 8) return PT_ERR_UNSUPPORTED;
+    if (rows == 0) return PT_OK;
+    if (!amax || !dequant || (cols > 0 && (!x || !q))) return PT_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q) || !aligned4(amax) || !aligned4(dequant)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    if (cols == 0) return PT_OK;
+    return hip_status(launch_fp8_quantize_rows((const uint16_t *)x, (uint8_t *)q, amax, dequant, rows, cols,
+                                               (hipStream_t)stream));
 }
 
 int pt_mx_quantize_t(const void *x, void *q, uint8_t *scales, int64_t batch, int64_t rows, int64_t cols, int dtype,

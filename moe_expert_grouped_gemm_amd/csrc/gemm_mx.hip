@@ -470,13 +470,14 @@ enum WideScale {
     kWE4M3Swz = 3,    // E4M3, stage-major copy: the stage's word of the row (any K)
     kWE2M1Swz = 4,    // E2M1, stage-major copy: the lane half's word of the row (any K)
     kWConst = 5,      // E4M3 with one fp32 scale per operand tensor: block scales all 1 (byte 127)
+    kWConstRow = 6,   // the same with one fp32 scale per row of A and per row of B (output column)
 };
 
 // Load this lane's scale word of each of its 6 rows for stage kt.
 template <int WSC>
 __device__ __forceinline__ void wload_scales(uint32_t (&sc)[6], const ScRows &sr, int kt, int nk, int h)
 {
-    if constexpr (WSC == kWConst) {
+    if constexpr (WSC == kWConst || WSC == kWConstRow) {
 #pragma unroll
         for (int i = 0; i < 6; ++i) sc[i] = 0x7F7F7F7Fu;
         return;
@@ -507,7 +508,8 @@ __device__ __forceinline__ void wscale_words(const uint32_t (&sc)[6], uint32_t (
     const uint32_t sel = h ? 0x07050301u : 0x06040200u;
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
-        if constexpr (WSC == kWE4M3Word || WSC == kWE4M3Swz || WSC == kWE2M1Swz || WSC == kWConst) {
+        if constexpr (WSC == kWE4M3Word || WSC == kWE4M3Swz || WSC == kWE2M1Swz || WSC == kWConst ||
+                      WSC == kWConstRow) {
             w[i] = sc[i];
         } else if constexpr (WSC == kWE4M3Span) {
             const auto r = __builtin_amdgcn_permlane32_swap(sc[i], sc[i], false, false);
@@ -523,7 +525,7 @@ __device__ __forceinline__ void wscale_words(const uint32_t (&sc)[6], uint32_t (
 template <int WSC>
 __device__ __forceinline__ int wscale_of(const uint32_t (&w)[6], int i, int s, uint32_t sh)
 {
-    if constexpr (WSC == kWConst) return 127;
+    if constexpr (WSC == kWConst || WSC == kWConstRow) return 127;
     if constexpr (WSC == kWE2M1Pair || WSC == kWE2M1Swz) return (int)__builtin_amdgcn_ubfe(w[i], 8u * s, 8u);
     else return (int)__builtin_amdgcn_ubfe(w[i], sh + 16u * s, 8u);
 }
@@ -869,6 +871,21 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[i][j][r] *= f;
+        } else if constexpr (WSC == kWConstRow) {
+            // one factor per output row (A's row scale) and per column (the
+            // expert's B row scale), multiplied together in fp32 first
+            float fb[4];
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj)
+                fb[bj] = p.sfb[(int64_t)g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)];
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float fa = p.sfa[row0 + min(m0 + e_row(wm, bi, r), rows - 1)];
+#pragma unroll
+                    for (int bj = 0; bj < 4; ++bj) acc[bi][bj][r] *= fa * fb[bj];
+                }
         }
         store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn);
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
@@ -1017,7 +1034,7 @@ hipError_t launch_mx_scale_swizzle(const uint8_t *scales, int64_t rows, int64_t 
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s)
 {
-    if (p.sfa) return launch_wide_epi<0, kWConst>(p, epi, s);
+    if (p.sfa) return p.sf_rows ? launch_wide_epi<0, kWConstRow>(p, epi, s) : launch_wide_epi<0, kWConst>(p, epi, s);
     if (fmt == 1 && mx_force_narrow())
         return p.K % 128 == 0 ? launch_epi<1, kScE2M1Word>(p, epi, s) : launch_epi<1, kScE2M1Span>(p, epi, s);
     if (p.sa && p.sb)

@@ -62,6 +62,7 @@ struct MxParams {
     const uint32_t *sb;
     const float *sfa;        // FP8 with tensor scales: A's fp32 scale (1 value), or null (MX)
     const float *sfb;        // and each expert's B scale [G]
+    int sf_rows;             // sfa / sfb hold one scale per row of A [M] and per row of B [G, N]
 };
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);
@@ -99,6 +100,9 @@ hipError_t launch_quantize_t(const uint16_t *x, uint8_t *q, uint8_t *scales, int
 // dequant[b] = amax-derived factor that multiplies the codes back.
 hipError_t launch_fp8_quantize(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t batch,
                                int64_t n, hipStream_t s);
+// The same with one scale per row of x [rows, cols].
+hipError_t launch_fp8_quantize_rows(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t rows,
+                                    int64_t cols, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cus();

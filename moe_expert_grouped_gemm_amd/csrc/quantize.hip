@@ -204,6 +204,46 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(const uint16_t *__
     }
 }
 
+// One scale per row: a wave per row, one pass for the amax (a wave
+// reduction, no atomics) and one for the codes (the row is then in L2).
+__global__ __launch_bounds__(kThreads) void fp8_rows_kernel(const uint16_t *__restrict__ x, uint8_t *__restrict__ q,
+                                                            float *amax, float *dequant, int64_t rows, int64_t cols)
+{
+    const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const uint16_t *xr = x + r * cols;
+    uint32_t m = 0;
+    for (int64_t c = lane * 8; c < cols; c += 512) {
+        const uintx4 v = *(const uintx4 *)(xr + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+    const float mf = __uint_as_float(m << 16);
+    const float s = fp8_tensor_scale(mf);
+    if (lane == 0) {
+        amax[r] = mf;
+        dequant[r] = 1.0f / s;
+    }
+    uint8_t *qr = q + r * cols;
+    for (int64_t c = lane * 8; c < cols; c += 512) {
+        const uintx4 v = *(const uintx4 *)(xr + c);
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(v[i] & 0xFFFFu) * s, -448.0f), 448.0f);
+            f[2 * i + 1] = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(v[i] >> 16) * s, -448.0f), 448.0f);
+        }
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
+        *(uintx2 *)(qr + c) = uintx2{(uint32_t)w0, (uint32_t)w1};
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t rows, int64_t cols,
@@ -248,6 +288,15 @@ hipError_t launch_fp8_quantize(const uint16_t *x, uint8_t *q, float *amax, float
     const dim3 grid((unsigned)chunks, (unsigned)batch);
     hipLaunchKernelGGL(fp8_amax_kernel, grid, dim3(kThreads), 0, s, x, am, n8);
     hipLaunchKernelGGL(fp8_encode_kernel, grid, dim3(kThreads), 0, s, x, q, am, dequant, n8);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_rows(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t rows,
+                                    int64_t cols, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const int64_t grid = (rows + kThreads / 64 - 1) / (kThreads / 64);
+    hipLaunchKernelGGL(fp8_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, amax, dequant, rows, cols);
     return hipGetLastError();
 }
 

@@ -168,3 +168,50 @@ def test_fp8_fwd_mxfp8_shape_sampled(orc, dev):
         sl = slice(start, start + r.size)
         assert floored_rel_err(got[sl], ref[sl]) <= BF16_TOL, g
         start += r.size
+
+
+# ------------------------------------------------------------------ rowwise
+def fp8_quantize_rows(dev, x2d):
+    rows, cols = x2d.shape
+    q = torch.full((rows, cols), 0xEE, dtype=torch.uint8, device=dev)
+    amax = torch.full((rows,), -1.0, dtype=torch.float32, device=dev)
+    deq = torch.full((rows,), -1.0, dtype=torch.float32, device=dev)
+    ptm.pt_fp8_quantize_rows(x2d, q, amax, deq, rows, cols)
+    torch.cuda.synchronize()
+    return q, amax, deq
+
+
+@pytest.mark.parametrize("rows,cols", [(1000, 2880), (7, 8), (3, 600)], ids=["rows1000", "tiny", "odd512"])
+def test_fp8_quantize_rows_bit_exact(orc, dev, rows, cols):
+    x = synth.randn_bf16((rows, cols), seed=90, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    x[0] = 0                                                   # an all-zero row
+    if rows > 2:
+        x[2] *= 1e-36                                           # a row whose scale overflows fp32
+    q, amax, deq = fp8_quantize_rows(dev, x)
+    rq, ra, rd = orc.fp8_quantize(bits16(x))
+    assert (amax.cpu().numpy() == ra).all()
+    assert (deq.cpu().numpy() == rd).all()
+    assert (u8(q) == rq).all()
+
+
+@pytest.mark.parametrize("epi", [ptm.PT_EPI_NONE, ptm.PT_EPI_SWIGLU])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fp8_rowwise_fwd_vs_oracle(orc, dev, case, epi):
+    _, lens, K, N = case
+    lens = np.array(lens, np.int64)
+    M, G = int(lens.sum()), len(lens)
+    a = synth.randn_bf16((M, K), seed=91, device=dev)
+    w = synth.randn_bf16((G * N, K), seed=92, std=K ** -0.5, device=dev)
+    aq, _, ad = fp8_quantize_rows(dev, a)
+    bq, _, bd = fp8_quantize_rows(dev, w)
+    M_out = N if epi == ptm.PT_EPI_NONE else N // 2
+    out = torch.empty((M, M_out), dtype=torch.bfloat16, device=dev)
+    ptm.pt_grouped_gemm_fwd(aq, ad, bq, bd, out, None, dev_i64(lens, dev), None, G, M, N, K,
+                            ptm.PT_FP8_E4M3_ROWWISE, 1, epi)
+    torch.cuda.synchronize()
+    rows = np.arange(M)
+    c = orc.fp8_fwd_rows_rowwise(u8(aq), ad.cpu().numpy(), u8(bq).reshape(G, N, K), bd.cpu().numpy().reshape(G, N),
+                                 lens, N, K, rows)
+    ref = c if epi == ptm.PT_EPI_NONE else orc.swiglu(c)
+    grp = group_of_rows(lens, rows)
+    assert per_group_max(floored_rel_err, bf16_values(bits16(out)), ref, grp) <= BF16_TOL
