@@ -68,6 +68,8 @@ def lib():
         L.orc_dgrad_rows.argtypes = [p, p, p, i64, i64, i64, i64, i32, p, i64, p]
         L.orc_wgrad_rows.restype = i32
         L.orc_wgrad_rows.argtypes = [p, p, p, i64, i64, i64, i64, p, p, i64, p]
+        L.orc_mx_quantize_tokens.restype = i64
+        L.orc_mx_quantize_tokens.argtypes = [p, p, i64, i64, i64, p, p]
         L.orc_fp8_quantize.restype = None
         L.orc_fp8_quantize.argtypes = [p, i64, i64, p, p, p]
         L.orc_swiglu.restype = None
@@ -157,6 +159,35 @@ def mx_quantize(x_bits: np.ndarray, dtype: int, axis: int = 1):
     if rc:
         raise ValueError("orc_mx_quantize: bad arguments")
     return q, s
+
+
+def mx_quantize_tokens(x_bits: np.ndarray, group_lens: np.ndarray):
+    """MXFP8 (E4M3) quantisation along tokens within each expert: x_bits
+    [M, cols] bf16 bits.  Returns (codes [M, cols], scales [M // 32 + G, cols],
+    number of scale rows used); unused scale rows are zero."""
+    x = _c(x_bits, np.uint16)
+    lens = _c(group_lens, np.int64)
+    M, cols = x.shape
+    q = np.zeros((M, cols), np.uint8)
+    s = np.zeros((M // 32 + lens.size, cols), np.uint8)
+    nb = lib().orc_mx_quantize_tokens(_ptr(x), _ptr(lens), lens.size, M, cols, _ptr(q), _ptr(s))
+    return q, s, int(nb)
+
+
+def mx_dequantize_tokens(q: np.ndarray, s: np.ndarray, group_lens: np.ndarray) -> np.ndarray:
+    """Exact binary64 values of mx_quantize_tokens' output."""
+    lens = np.asarray(group_lens, np.int64)
+    table = np.array([e4m3_value(c) for c in range(256)], np.float64)
+    vals = table[_c(q, np.uint8)]
+    out = np.empty(q.shape, np.float64)
+    off = b = 0
+    for g in range(lens.size):
+        for j in range((int(lens[g]) + 31) // 32):
+            r0, r1 = off + 32 * j, min(off + 32 * j + 32, off + int(lens[g]))
+            out[r0:r1] = vals[r0:r1] * np.ldexp(1.0, s[b].astype(np.int64) - 127)[None, :]
+            b += 1
+        off += int(lens[g])
+    return out
 
 
 def fp8_quantize(x_bits: np.ndarray):

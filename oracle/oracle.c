@@ -314,6 +314,47 @@ void orc_fp8_quantize(const uint16_t *x, int64_t batch, int64_t n, uint8_t *q, f
     }
 }
 
+/*
+ * MX quantisation along tokens for the weight gradient, one expert at a
+ * time: expert g's rows [off_g, off_g + len_g) of x [M, cols] form blocks of
+ * 32 consecutive rows, the last one partial when len_g % 32 != 0 (its
+ * missing rows are simply absent: the block scale comes from the rows that
+ * exist), so no block straddles two experts.  Codes keep x's layout
+ * (q [M, cols], E4M3 only); block j of expert g takes scale row
+ * bstart_g + j, bstart_g = sum over earlier experts of ceil(len / 32).
+ * Returns the number of scale rows used.
+ */
+int64_t orc_mx_quantize_tokens(const uint16_t *x, const int64_t *lens, int64_t G, int64_t M, int64_t cols,
+                               uint8_t *q, uint8_t *scales)
+{
+    double vals[128];
+    int n = positive_grid(ORC_E4M3, vals);
+    int64_t off = 0, bstart = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        int64_t len = lens[g], nb = (len + 31) / 32;
+        for (int64_t j = 0; j < nb; ++j) {
+            int64_t r0 = off + 32 * j, nr = len - 32 * j < 32 ? len - 32 * j : 32;
+#pragma omp parallel for schedule(static)
+            for (int64_t c = 0; c < cols; ++c) {
+                double v[32];
+                for (int64_t i = 0; i < nr; ++i)
+                    v[i] = orc_bf16_value(x[(r0 + i) * cols + c]);
+                int E = block_scale(ORC_E4M3, v, (int)nr);
+                scales[(bstart + j) * cols + c] = (uint8_t)E;
+                for (int64_t i = 0; i < nr; ++i) {
+                    double xi = ldexp(v[i], 127 - E);
+                    int code = nearest_code(fabs(xi), vals, n);
+                    q[(r0 + i) * cols + c] = (uint8_t)(((signbit(v[i]) ? 1 : 0) << 7) | code);
+                }
+            }
+        }
+        off += len;
+        bstart += nb;
+    }
+    (void)M;
+    return bstart;
+}
+
 /* ---------------------------------------------------------------- GEMMs */
 
 /* Expert of global row r: offs[g] <= r < offs[g] + lens[g]; -1 if none. */

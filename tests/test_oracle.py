@@ -373,6 +373,47 @@ def test_fp8_fwd_rows_rowwise_matches_dense(orc):
         ref = (dec(aq[r]) @ dec(bq[g]).T) * float(ad[r]) * bd[g].astype(np.float64)
         assert np.allclose(got[i], ref, rtol=1e-14, atol=0), r
 
+
+def test_mx_quantize_tokens_full_blocks_equal_axis0(orc):
+    # experts whose lengths are multiples of 32 reduce to the plain column-block
+    # quantiser (axis 0) on each expert's rows
+    lens = np.array([64, 0, 32, 96])
+    x = rand_bf16((int(lens.sum()), 48), seed=76, std=2.0)
+    q, s, nb = orc.mx_quantize_tokens(x, lens)
+    assert nb == 6
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    b = 0
+    for g in range(lens.size):
+        if lens[g] == 0:
+            continue
+        rq, rs = orc.mx_quantize(x[offs[g]:offs[g + 1]], E4M3, axis=0)
+        assert (q[offs[g]:offs[g + 1]] == rq).all(), g
+        assert (s[b:b + lens[g] // 32] == rs).all(), g
+        b += lens[g] // 32
+
+
+def test_mx_quantize_tokens_partial_block_equals_zero_padding(orc):
+    # a partial last block behaves as if padded with zero rows (zeros change
+    # neither the amax nor the other codes), and it never mixes two experts
+    lens = np.array([45, 7, 33])
+    M = int(lens.sum())
+    x = rand_bf16((M, 32), seed=77, std=1.0)
+    q, s, nb = orc.mx_quantize_tokens(x, lens)
+    assert nb == 2 + 1 + 2
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    b = 0
+    for g in range(lens.size):
+        n = int(lens[g])
+        pad = np.zeros((((n + 31) // 32) * 32, 32), np.uint16)
+        pad[:n] = x[offs[g]:offs[g + 1]]
+        rq, rs = orc.mx_quantize(pad, E4M3, axis=0)
+        assert (q[offs[g]:offs[g + 1]] == rq[:n]).all(), g
+        assert (s[b:b + (n + 31) // 32] == rs).all(), g
+        b += (n + 31) // 32
+    # the dequantised values are the codes times their block's scale
+    v = orc.mx_dequantize_tokens(q, s, lens)
+    assert np.abs(v - orc.bf16_to_f64(x)).max() <= np.abs(orc.bf16_to_f64(x)).max() * 2 ** -3
+
 # ------------------------------------------------------------------ GEMMs
 def _setup(G, lens, K, N, seed, trans_b=0, integer=False):
     M = int(sum(lens))
