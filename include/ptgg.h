@@ -201,8 +201,16 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_sa
  *  main_grad  trans_out = 0: [G, K, N];  trans_out = 1: [G, N, K]  (fp32)
  *  An expert with no rows leaves its main_grad slice untouched when
  *  accumulating and writes zeros when not.
- *  workspace  optional (may be NULL), see pt_grouped_gemm_workspace_size.
- *  Requirements: K % 8 == 0, N % 8 == 0; dtype PT_BF16.
+ *  workspace  optional (may be NULL) for BF16, see
+ *             pt_grouped_gemm_workspace_size.
+ *  PT_MXFP8_E4M3: a and dy are E4M3 codes [M, K] / [M, N] blocked along
+ *  tokens within each expert, with scales [M/32 + G, K] / [M/32 + G, N]
+ *  (pt_mx_quantize_tokens); D_g sums the products of their exact values
+ *  (each code times its block's scale; values below bf16's smallest
+ *  subnormal round to nearest even).  The workspace is required and holds
+ *  bf16 copies of both operands: pt_grouped_gemm_workspace_size(PT_OP_WGRAD,
+ *  ..., PT_MXFP8_E4M3) bytes, else PT_ERR_WORKSPACE.
+ *  Requirements: K % 8 == 0, N % 8 == 0; dtype PT_BF16 or PT_MXFP8_E4M3.
  */
 int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
                           const void *dy, const uint8_t *dy_scale,
@@ -248,6 +256,27 @@ int pt_mx_quantize(const void *x, void *q, uint8_t *scales,
  */
 int pt_mx_quantize_t(const void *x, void *q, uint8_t *scales,
                      int64_t batch, int64_t rows, int64_t cols, int dtype, void *stream);
+
+/*
+ * MXFP8 quantisation along tokens for the weight gradient (the MX grouped
+ * GEMM's backward flow, PR page "[Megatron-LM] feat: add grouped gemm fp4
+ * support, ...", Copilot overview; the Primus-Turbo README's "pad-aware
+ * paths" keep quantisation blocks inside one expert): within each expert g,
+ * rows [off_g, off_g + len_g) of x [M, cols] (bf16) form blocks of 32
+ * consecutive rows, the last one partial when len_g % 32 != 0, so no block
+ * straddles two experts.  Each block of each column is quantised by the
+ * rule of pt_mx_quantize (E4M3) over the rows it has.
+ *  q       [M, cols] E4M3 codes (x's layout);
+ *  scales  [M/32 + G, cols] E8M0: block j of expert g is row
+ *          sum over earlier experts of ceil(len/32), plus j; rows past the
+ *          last block are left as they are.
+ *  group_offs may be NULL (derived by exclusive scan on the device).
+ *  dtype   PT_MXFP8_E4M3.  Requirements: cols % 8 == 0; x, q and scales
+ *          16-byte aligned.  workspace optional (the error word).
+ */
+int pt_mx_quantize_tokens(const void *x, const int64_t *group_lens, const int64_t *group_offs, void *q,
+                          uint8_t *scales, int64_t G, int64_t M, int64_t cols, int dtype,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * FP8 E4M3 quantisation with one scale per matrix ("current scaling": the

@@ -24,7 +24,7 @@ __all__ = [
     "load", "lib_path", "PtggError",
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu",
     "pt_grouped_gemm_wgrad",
-    "pt_mx_quantize", "pt_mx_quantize_t", "pt_fp8_quantize", "pt_fp8_quantize_rows",
+    "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_grouped_gemm_workspace_size", "pt_read_error_flags", "pt_status_string", "pt_version",
 ]
 
@@ -34,7 +34,7 @@ PT_OP_FWD, PT_OP_DGRAD, PT_OP_WGRAD = 0, 1, 2
 
 EXPORTS = (
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",
-    "pt_mx_quantize", "pt_mx_quantize_t", "pt_fp8_quantize", "pt_fp8_quantize_rows",
+    "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_grouped_gemm_workspace_size", "pt_read_error_flags", "pt_status_string", "pt_version",
 )
 
@@ -76,6 +76,8 @@ def load(require_gpu: bool = True):
     L.pt_mx_quantize_t.argtypes = [p, p, p, i64, i64, i64, i32, p]
     L.pt_fp8_quantize.restype = i32
     L.pt_fp8_quantize.argtypes = [p, p, p, p, i64, i64, i64, p]
+    L.pt_mx_quantize_tokens.restype = i32
+    L.pt_mx_quantize_tokens.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p, sz, p]
     L.pt_fp8_quantize_rows.restype = i32
     L.pt_fp8_quantize_rows.argtypes = [p, p, p, p, i64, i64, p]
     L.pt_grouped_gemm_workspace_size.restype = sz
@@ -170,6 +172,13 @@ def pt_fp8_quantize(x, q, amax, dequant, batch, rows, cols, stream=None):
     L = load()
     _check("pt_fp8_quantize", L.pt_fp8_quantize(
         _ptr(x), _ptr(q), _ptr(amax), _ptr(dequant), batch, rows, cols, _stream(stream)))
+
+
+def pt_mx_quantize_tokens(x, group_lens, group_offs, q, scales, G, M, cols, dtype, workspace=None, stream=None):
+    L = load()
+    _check("pt_mx_quantize_tokens", L.pt_mx_quantize_tokens(
+        _ptr(x), _ptr(group_lens), _ptr(group_offs), _ptr(q), _ptr(scales), G, M, cols, dtype,
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def pt_fp8_quantize_rows(x, q, amax, dequant, rows, cols, stream=None):

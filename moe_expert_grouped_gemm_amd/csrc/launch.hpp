@@ -100,6 +100,13 @@ hipError_t launch_quantize_t(const uint16_t *x, uint8_t *q, uint8_t *scales, int
 // dequant[b] = amax-derived factor that multiplies the codes back.
 hipError_t launch_fp8_quantize(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t batch,
                                int64_t n, hipStream_t s);
+// MXFP8 along tokens within each expert (blocks of 32 rows, the last
+// partial), codes [M, C] and scales [M / 32 + G, C]; and the exact bf16
+// values of such codes (the MX weight gradient runs on them).
+hipError_t launch_mx_quantize_tokens(const uint16_t *x, const int64_t *lens, const int64_t *offs, int G, int64_t M,
+                                     int64_t C, uint8_t *q, uint8_t *scales, uint32_t *err, hipStream_t s);
+hipError_t launch_mx_dequant_tokens(const uint8_t *q, const uint8_t *scales, const int64_t *lens,
+                                    const int64_t *offs, int G, int64_t M, int64_t C, uint16_t *out, hipStream_t s);
 // The same with one scale per row of x [rows, cols].
 hipError_t launch_fp8_quantize_rows(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t rows,
                                     int64_t cols, hipStream_t s);

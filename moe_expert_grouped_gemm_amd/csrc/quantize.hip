@@ -244,6 +244,93 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(const uint16_t *__re
     }
 }
 
+// ------------------------------------------------------------------ MX along tokens
+// The weight gradient reduces over tokens, so its MX operands are blocked
+// along them: within each expert, blocks of 32 consecutive rows (the last one
+// partial), never two experts in one block.  Block j of expert g is scale
+// row tile0[g] + j of the group table built with 32-row "tiles".
+
+__device__ __forceinline__ int tokens_table(GroupTable &tab, int *sm, const int64_t *lens, const int64_t *offs,
+                                            int G, int64_t M, uint32_t *err)
+{
+    tab.G = G;
+    tab.row0 = sm;
+    tab.rows = sm + G;
+    tab.tile0 = sm + 2 * G;
+    return build_group_table<TilesFwd, kThreads>(tab, lens, offs, G, M, TilesFwd{32, 1}, err, tab.tile0 + G + 1);
+}
+
+// grid (scale rows, column tiles of 256): one thread per column of a block
+__global__ __launch_bounds__(kThreads) void mx_tokens_quant_kernel(const uint16_t *__restrict__ x,
+                                                                   const int64_t *lens, const int64_t *offs, int G,
+                                                                   int64_t M, int64_t C, uint8_t *__restrict__ q,
+                                                                   uint8_t *__restrict__ scales, uint32_t *err)
+{
+    extern __shared__ __attribute__((aligned(16))) int sm_tok[];
+    GroupTable tab;
+    const int total = tokens_table(tab, sm_tok, lens, offs, G, M, err);
+    const int b = blockIdx.x;
+    const int64_t c = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+    if (b >= total || c >= C) return;
+    const int g = find_group(tab, b);
+    const int j = b - tab.tile0[g];
+    const int64_t r0 = tab.row0[g] + 32 * j;
+    const int nr = min(32, tab.rows[g] - 32 * j);
+    uint32_t h[32];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        h[i] = i < nr ? x[(r0 + i) * C + c] : 0u;
+        amax = max(amax, h[i] & 0x7FFFu);
+    }
+    const uint32_t E = mx_scale_byte<8>(amax);
+    const int e = 127 - (int)E;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        if (i < nr) {
+            const float f = __builtin_fminf(__builtin_fmaxf(__builtin_ldexpf(bf16_to_f32(h[i]), e), -448.0f), 448.0f);
+            q[(r0 + i) * C + c] = (uint8_t)__builtin_amdgcn_cvt_pk_fp8_f32(f, 0.0f, 0, false);
+        }
+    scales[(int64_t)b * C + c] = (uint8_t)E;
+}
+
+// MX codes blocked along tokens -> their exact values as bf16 (values below
+// bf16's smallest subnormal round to nearest even): one wave per row.
+__global__ __launch_bounds__(kThreads) void mx_tokens_dequant_kernel(const uint8_t *__restrict__ q,
+                                                                     const uint8_t *__restrict__ scales,
+                                                                     const int64_t *lens, const int64_t *offs, int G,
+                                                                     int64_t M, int64_t C, uint16_t *__restrict__ out)
+{
+    extern __shared__ __attribute__((aligned(16))) int sm_tok[];
+    GroupTable tab;
+    tokens_table(tab, sm_tok, lens, offs, G, M, nullptr);
+    const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (r >= M) return;
+    const int lane = threadIdx.x & 63;
+    int lo = 0, hi = G;                            // the last expert with row0 <= r
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tab.row0[mid] <= r) lo = mid; else hi = mid;
+    }
+    const bool in = G > 0 && r >= tab.row0[lo] && r < (int64_t)tab.row0[lo] + tab.rows[lo];
+    const int64_t b = in ? tab.tile0[lo] + (r - tab.row0[lo]) / 32 : 0;
+    for (int64_t c = lane * 8; c < C; c += 512) {
+        uintx4 o = uintx4{0u, 0u, 0u, 0u};
+        if (in) {
+            const uintx2 cw = *(const uintx2 *)(q + r * C + c);
+            const uintx2 sw = *(const uintx2 *)(scales + b * C + c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t code = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+                const int E = (int)((sw[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+                const float v = __builtin_ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)code, 0), E - 127);
+                o[e >> 1] |= bf16_rne(v) << (16 * (e & 1));
+            }
+        }
+        *(uintx4 *)(out + r * C + c) = o;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t rows, int64_t cols,
@@ -297,6 +384,27 @@ hipError_t launch_fp8_quantize_rows(const uint16_t *x, uint8_t *q, float *amax, 
     if (rows == 0 || cols == 0) return hipSuccess;
     const int64_t grid = (rows + kThreads / 64 - 1) / (kThreads / 64);
     hipLaunchKernelGGL(fp8_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, amax, dequant, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize_tokens(const uint16_t *x, const int64_t *lens, const int64_t *offs, int G, int64_t M,
+                                     int64_t C, uint8_t *q, uint8_t *scales, uint32_t *err, hipStream_t s)
+{
+    const int64_t nb = M / 32 + G;                 // scale rows an upper bound allows
+    if (nb == 0 || C == 0) return hipSuccess;
+    const dim3 grid((unsigned)nb, (unsigned)((C + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL(mx_tokens_quant_kernel, grid, dim3(kThreads), table_bytes(G), s, x, lens, offs, G, M, C, q,
+                       scales, err);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_dequant_tokens(const uint8_t *q, const uint8_t *scales, const int64_t *lens,
+                                    const int64_t *offs, int G, int64_t M, int64_t C, uint16_t *out, hipStream_t s)
+{
+    if (M == 0 || C == 0) return hipSuccess;
+    const dim3 grid((unsigned)((M + kThreads / 64 - 1) / (kThreads / 64)));
+    hipLaunchKernelGGL(mx_tokens_dequant_kernel, grid, dim3(kThreads), table_bytes(G), s, q, scales, lens, offs, G, M,
+                       C, out);
     return hipGetLastError();
 }
 

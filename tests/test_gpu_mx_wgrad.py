@@ -1,0 +1,139 @@
+"""GPU parity of the MXFP8 weight gradient: pt_mx_quantize_tokens bit-exact
+against the oracle (blocks of 32 tokens inside each expert, the last one
+partial), and pt_grouped_gemm_wgrad on those codes against the oracle's sum
+of exact products, accumulating into and overwriting main_grad, in both
+output layouts, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_grouped_gemm_amd as ptm
+from moe_expert_grouped_gemm_amd import synth
+from util import BF16_TOL, bits16, dev_i64, floored_rel_err, u8
+
+pytestmark = pytest.mark.gpu
+
+
+def quantize_tokens(dev, x, lens):
+    M, C = x.shape
+    G = len(lens)
+    q = torch.full((M, C), 0xEE, dtype=torch.uint8, device=dev)
+    s = torch.zeros((M // 32 + G, C), dtype=torch.uint8, device=dev)
+    ptm.pt_mx_quantize_tokens(x, dev_i64(lens, dev), None, q, s, G, M, C, ptm.PT_MXFP8_E4M3)
+    torch.cuda.synchronize()
+    return q, s
+
+
+@pytest.mark.parametrize("lens,C", [([0, 70, 1, 0, 300, 129, 0], 136), ([32, 64, 33], 48), ([5], 8)],
+                         ids=["ragged", "aligned_and_one_over", "tiny"])
+def test_quantize_tokens_bit_exact(orc, dev, lens, C):
+    lens = np.array(lens, np.int64)
+    M = int(lens.sum())
+    x = synth.randn_bf16((M, C), seed=100, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    q, s = quantize_tokens(dev, x, lens)
+    rq, rs, nb = orc.mx_quantize_tokens(bits16(x), lens)
+    assert (u8(q) == rq).all()
+    assert (u8(s)[:nb] == rs[:nb]).all()
+
+
+def wgrad_mx(dev, aq, as_, dq, ds, lens, N, K, trans_out, accumulate, seed_mg=103):
+    M, G = aq.shape[0], len(lens)
+    shape = (G, N, K) if trans_out else (G, K, N)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed_mg)
+    mg = (torch.randn(shape, generator=g, device=dev) * 1e-3).float()
+    before = mg.clone()
+    ws = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, ptm.PT_MXFP8_E4M3),),
+                     dtype=torch.uint8, device=dev)
+    ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, dev_i64(lens, dev), None, G, M, N, K, ptm.PT_MXFP8_E4M3,
+                              trans_out, accumulate, workspace=ws)
+    torch.cuda.synchronize()
+    return before.cpu().numpy(), mg.cpu().numpy()
+
+
+@pytest.mark.parametrize("trans_out", [0, 1])
+@pytest.mark.parametrize("accumulate", [1, 0])
+def test_mx_wgrad_vs_oracle(orc, dev, trans_out, accumulate):
+    lens = np.array([0, 70, 1, 0, 300, 129, 0], np.int64)
+    K, N = 200, 136
+    M, G = int(lens.sum()), len(lens)
+    print(f"mx wgrad trans_out={trans_out} acc={accumulate}", flush=True)
+    a = synth.randn_bf16((M, K), seed=101, std=K ** -0.5, device=dev)
+    dy = synth.randn_bf16((M, N), seed=102, std=1e-2, device=dev)
+    aq, as_ = quantize_tokens(dev, a, lens)
+    dq, ds = quantize_tokens(dev, dy, lens)
+    raq, ras, _ = orc.mx_quantize_tokens(bits16(a), lens)
+    rdq, rds, nb = orc.mx_quantize_tokens(bits16(dy), lens)
+    assert (u8(aq) == raq).all() and (u8(dq) == rdq).all()
+    before, after = wgrad_mx(dev, aq, as_, dq, ds, lens, N, K, trans_out, accumulate)
+    av = orc.mx_dequantize_tokens(raq, ras, lens)
+    dv = orc.mx_dequantize_tokens(rdq, rds, lens)
+    offs = synth.offsets(lens)
+    for g in range(G):
+        if lens[g] == 0:
+            if accumulate:
+                assert (after[g] == before[g]).all(), "empty expert touched"
+            else:
+                assert (after[g] == 0).all()
+            continue
+        D = av[offs[g]:offs[g + 1]].T @ dv[offs[g]:offs[g + 1]]          # [K, N], binary64
+        if trans_out:
+            D = D.T
+        inc = after[g].astype(np.float64) - (before[g] if accumulate else 0.0)
+        assert floored_rel_err(inc, D) <= BF16_TOL, g
+
+
+def test_mx_wgrad_needs_its_workspace(dev):
+    lens = dev_i64(np.array([40], np.int64), dev)
+    q = torch.zeros((40, 64), dtype=torch.uint8, device=dev)
+    s = torch.zeros((3, 64), dtype=torch.uint8, device=dev)
+    mg = torch.zeros((1, 64, 64), dtype=torch.float32, device=dev)
+    L = ptm.load()
+    st = torch.cuda.current_stream().cuda_stream
+    small = torch.zeros((4096,), dtype=torch.uint8, device=dev)
+    args = (q.data_ptr(), s.data_ptr(), q.data_ptr(), s.data_ptr(), mg.data_ptr(), lens.data_ptr(), None,
+            1, 40, 64, 64, ptm.PT_MXFP8_E4M3, 0, 1)
+    assert L.pt_grouped_gemm_wgrad(*args, None, 0, st) == 4
+    assert L.pt_grouped_gemm_wgrad(*args, small.data_ptr(), 4096, st) == 4
+    assert L.pt_grouped_gemm_wgrad(q.data_ptr(), s.data_ptr(), q.data_ptr(), s.data_ptr(), mg.data_ptr(),
+                                   lens.data_ptr(), None, 1, 40, 64, 64, ptm.PT_MXFP4_E2M1, 0, 1, None, 0, st) == 2
+
+
+def test_mx_wgrad_full_shape_sampled(orc, dev):
+    # The weight gradient at the headline's shape: 256 experts, 49152 tokens,
+    # K = N = 4096, accumulated into a seeded fp32 main_grad; sampled
+    # (expert, k) rows of the increment against the oracle.
+    lens = synth.lens_topk_gaussian(8192, 256, 6, seed=1)
+    G, M, K, N = 256, int(lens.sum()), 4096, 4096
+    offs = synth.offsets(lens)
+    a = synth.randn_bf16((M, K), seed=101, std=K ** -0.5, device=dev)
+    dy = synth.randn_bf16((M, N), seed=102, std=1e-2, device=dev)
+    aq, as_ = quantize_tokens(dev, a, lens)
+    dq, ds = quantize_tokens(dev, dy, lens)
+    del a, dy
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(103)
+    mg = torch.randn((G, K, N), generator=gen, device=dev, dtype=torch.float32).mul_(1e-3)
+    rng = np.random.default_rng(11)
+    nz = np.nonzero(lens)[0]
+    gs = np.concatenate([rng.choice(nz, size=8, replace=False), [nz[np.argmax(lens[nz])]]])
+    ks = rng.integers(0, K, size=gs.size)
+    gi, ki = torch.as_tensor(gs, device=dev), torch.as_tensor(ks, device=dev)
+    before = mg[gi, ki].cpu().numpy()
+    ws = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, ptm.PT_MXFP8_E4M3),),
+                     dtype=torch.uint8, device=dev)
+    ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, dev_i64(lens, dev), None, G, M, N, K, ptm.PT_MXFP8_E4M3, 0, 1,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    after = mg[gi, ki].cpu().numpy()
+    del mg, ws
+    aqn, asn, dqn, dsn = u8(aq), u8(as_), u8(dq), u8(ds)
+    table = np.array([orc.e4m3_value(c) for c in range(256)], np.float64)
+    for i, (g, k) in enumerate(zip(gs, ks)):
+        r0, r1 = offs[g], offs[g + 1]
+        b0 = int(sum((int(l) + 31) // 32 for l in lens[:g]))
+        blk = b0 + (np.arange(r1 - r0) // 32)
+        av = table[aqn[r0:r1, k]] * np.ldexp(1.0, asn[blk, k].astype(np.int64) - 127)
+        dv = table[dqn[r0:r1]] * np.ldexp(1.0, dsn[blk].astype(np.int64) - 127)
+        D = av @ dv                                                     # [N], binary64
+        assert floored_rel_err(after[i].astype(np.float64) - before[i], D) <= BF16_TOL, (g, k)
