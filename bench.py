@@ -413,6 +413,52 @@ def bench_fc2_bwd(dev, stream, iters, lens):
     return d
 
 
+def bench_cfg3_wgrad(dev, stream, iters):
+    """The MXFP8 workload's weight gradient: A [65536, 2880] and dY
+    [65536, 5760] quantised along tokens in blocks of 32 inside each expert,
+    then the weight gradient accumulated into fp32 main_grad [32, 2880, 5760]
+    (exact dequantisation into the workspace, then the BF16 kernel)."""
+    lens = synth.lens_zipf_distinct(16384, 32, 4, 1.1, seed=3)
+    G, M, K, N = 32, int(lens.sum()), 2880, 5760
+    lens_d = torch.as_tensor(lens, device=dev)
+    a = synth.randn_bf16((M, K), seed=104, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    dy = synth.randn_bf16((M, N), seed=106, std=1e-2, device=dev)
+    aq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((M // 32 + G, K), dtype=torch.uint8, device=dev)
+    dq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    ds = torch.empty((M // 32 + G, N), dtype=torch.uint8, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(103)
+    mg = torch.randn((G, K, N), generator=g, device=dev, dtype=torch.float32).mul_(1e-3)
+    ws = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, ptm.PT_MXFP8_E4M3),),
+                     dtype=torch.uint8, device=dev)
+
+    def quant():
+        ptm.pt_mx_quantize_tokens(a, lens_d, None, aq, as_, G, M, K, ptm.PT_MXFP8_E4M3, workspace=ws, stream=stream)
+        ptm.pt_mx_quantize_tokens(dy, lens_d, None, dq, ds, G, M, N, ptm.PT_MXFP8_E4M3, workspace=ws, stream=stream)
+
+    def gemm():
+        ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, 0, 1,
+                                  workspace=ws, stream=stream)
+
+    def step():
+        quant()
+        gemm()
+    _, per = time_launches(step, iters, 3, stream)
+    _, per_q = time_launches(quant, iters, 3, stream)
+    _, per_g = time_launches(gemm, iters, 3, stream)
+    flops = 2.0 * M * K * N
+    codes = M * K + M * N + (M // 32 + G) * (K + N)
+    nbytes = M * K * 2 + M * N * 2 + 2 * codes + bytes_weights(lens, K * N * 4 * 2)
+    w = summary("MXFP8 wgrad (A and dY quantised along tokens + weight gradient into fp32 main_grad), "
+                "32 experts, M=65536, K=2880, N=5760", "mxfp8", flops, nbytes, per,
+                {"quantize_tokens_ms_median": round(float(np.median(per_q)), 4),
+                 "wgrad_only_ms_median": round(float(np.median(per_g)), 4)})
+    del a, dy, aq, as_, dq, ds, mg, ws
+    torch.cuda.empty_cache()
+    return w
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -499,6 +545,10 @@ def main():
         if want is None or "cfg3dgrad" in want:
             log("per_config: MXFP8 dgrad")
             per["cfg3_mxfp8_dgrad"] = bench_cfg3_dgrad(dev, stream, iters)
+            torch.cuda.empty_cache()
+        if want is None or "cfg3wgrad" in want:
+            log("per_config: MXFP8 wgrad")
+            per["cfg3_mxfp8_wgrad"] = bench_cfg3_wgrad(dev, stream, iters)
             torch.cuda.empty_cache()
         if want is None or "cfg4" in want:
             log("per_config: MXFP4 MLP")

@@ -414,6 +414,26 @@ def test_mx_quantize_tokens_partial_block_equals_zero_padding(orc):
     v = orc.mx_dequantize_tokens(q, s, lens)
     assert np.abs(v - orc.bf16_to_f64(x)).max() <= np.abs(orc.bf16_to_f64(x)).max() * 2 ** -3
 
+def test_mx_dequantize_tokens_matches_torch_decode(orc):
+    # every finite E4M3 code, decoded by torch's float8_e4m3fn and scaled by
+    # its own block's E8M0 byte (decoded by torch's float8_e8m0fnu): a wrong
+    # block index (expert start, short last block) moves some row's scale
+    lens = np.array([0, 40, 1, 31, 0, 70])
+    M, C = int(lens.sum()), 24
+    rng = np.random.default_rng(78)
+    q = rng.integers(0, 256, size=(M, C)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x3C
+    nb = int(sum((n + 31) // 32 for n in lens))
+    s = np.zeros((M // 32 + lens.size, C), np.uint8)
+    s[:nb] = rng.integers(110, 145, size=(nb, C))
+    got = orc.mx_dequantize_tokens(q, s, lens)
+    vals = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy()
+    blk = np.concatenate([b0 + np.arange(n) // 32 for b0, n in
+                          zip(np.concatenate([[0], np.cumsum((lens + 31) // 32)[:-1]]), lens)])
+    scl = torch.from_numpy(np.ascontiguousarray(s[blk])).view(torch.float8_e8m0fnu).double().numpy()
+    assert (got == vals * scl).all()
+
+
 # ------------------------------------------------------------------ GEMMs
 def _setup(G, lens, K, N, seed, trans_b=0, integer=False):
     M = int(sum(lens))
