@@ -161,6 +161,24 @@ def mx_quantize(x_bits: np.ndarray, dtype: int, axis: int = 1):
     return q, s
 
 
+def stack_experts(weights, transpose: bool) -> np.ndarray:
+    """The stacked expert weight ([Primus DeepSeek-V4-Flash blog],
+    "Performance optimizations", kernel-fusion table, grouped expert weight
+    stack): out[g] = W_g, or W_g^T with transpose.  Pure data movement, so
+    the definition is numpy's stack of the (transposed) matrices."""
+    return np.stack([np.ascontiguousarray(w.T) if transpose else np.asarray(w) for w in weights])
+
+
+def mx_quantize_experts(weights, dtype: int):
+    """Both MX weight caches per expert: (q, s) = mx_quantize(W_g) along the
+    columns, stacked; (qt, st) = mx_quantize(W_g^T) along its columns (the
+    rows of W_g), stacked."""
+    fw = [mx_quantize(w, dtype, axis=1) for w in weights]
+    tr = [mx_quantize(np.ascontiguousarray(np.asarray(w).T), dtype, axis=1) for w in weights]
+    return (np.stack([f[0] for f in fw]), np.stack([f[1] for f in fw]),
+            np.stack([t[0] for t in tr]), np.stack([t[1] for t in tr]))
+
+
 def mx_quantize_tokens(x_bits: np.ndarray, group_lens: np.ndarray):
     """MXFP8 (E4M3) quantisation along tokens within each expert: x_bits
     [M, cols] bf16 bits.  Returns (codes [M, cols], scales [M // 32 + G, cols],

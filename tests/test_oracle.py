@@ -434,6 +434,34 @@ def test_mx_dequantize_tokens_matches_torch_decode(orc):
     assert (got == vals * scl).all()
 
 
+def test_stack_experts_by_index(orc):
+    # element by element on tiny experts: out[g, i, j] = W_g[i, j], or W_g[j, i]
+    ws = [rand_bf16((3, 5), seed=80 + g) for g in range(4)]
+    for transpose in (False, True):
+        out = orc.stack_experts(ws, transpose)
+        assert out.shape == ((4, 5, 3) if transpose else (4, 3, 5))
+        for g in range(4):
+            for i in range(3):
+                for j in range(5):
+                    assert (out[g, j, i] if transpose else out[g, i, j]) == ws[g][i, j]
+
+
+def test_mx_quantize_experts_caches(orc):
+    # the forward cache is the row quantiser on each expert; the transposed
+    # cache equals the column-block (axis 0) quantiser's codes and scales,
+    # transposed -- an independent route through the C oracle
+    ws = [rand_bf16((64, 96), seed=90 + g, std=3.0) for g in range(3)]
+    for fmt in (E4M3, E2M1):
+        q, s, qt, st = orc.mx_quantize_experts(ws, fmt)
+        for g, w in enumerate(ws):
+            rq, rs = orc.mx_quantize(w, fmt, axis=1)
+            assert (q[g] == rq).all() and (s[g] == rs).all()
+            aq, as_ = orc.mx_quantize(w, fmt, axis=0)
+            # (for E2M1 axis 0 packs rows 2i, 2i+1 of a column into one byte,
+            # the same pair the transpose packs along its row)
+            assert (st[g] == as_.T).all() and (qt[g] == aq.T).all()
+
+
 # ------------------------------------------------------------------ GEMMs
 def _setup(G, lens, K, N, seed, trans_b=0, integer=False):
     M = int(sum(lens))
