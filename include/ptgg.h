@@ -309,6 +309,46 @@ int pt_fp8_quantize_rows(const void *x, void *q, float *amax, float *dequant,
                          int64_t rows, int64_t cols, void *stream);
 
 /*
+ * Expert weight stack in one pass (the Primus DeepSeek-V4-Flash blog,
+ * "Performance optimizations", kernel-fusion table: the grouped expert weight
+ * stack replaces a stack, a transpose and a contiguous copy -- two full
+ * passes over the per-expert weights -- with one kernel).
+ *  experts  device array of G device addresses; expert g's weight W_g is a
+ *           bf16 [rows, cols] row-major matrix, 16-byte aligned.  A NULL or
+ *           misaligned address reads as a zero matrix and sets error bit 3
+ *           in the workspace's error word (pt_read_error_flags).
+ *  out      transpose = 0: [G, rows, cols], out[g] = W_g;
+ *           transpose = 1: [G, cols, rows], out[g] = W_g^T.
+ *           With W_g = an expert's [out, in] linear weight, transpose = 1
+ *           gives the [G, K, N] operand of pt_grouped_gemm_fwd (trans_b 0)
+ *           and transpose = 0 the [G, N, K] one (trans_b 1).
+ *  Requirements: rows % 8 == 0, cols % 8 == 0, G <= 65535; out 16-byte
+ *  aligned, experts 8-byte aligned.  workspace optional (the error word).
+ */
+int pt_stack_experts(const void *const *experts, void *out, int64_t G, int64_t rows, int64_t cols, int transpose,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The MX weight caches straight from per-expert weights, one read of each
+ * (the same kernel-fusion table's single-pass weight stack, fused with the
+ * quantised weight buffers that the PR page "[Megatron-LM] feat: add grouped
+ * gemm fp4 support, ...", section "Changes", keeps next to the weight):
+ *  q, scales      the forward cache, pt_mx_quantize of each W_g along its
+ *                 columns: E4M3 [G, rows, cols] / E2M1 [G, rows, cols/2]
+ *                 codes, [G, rows, cols/32] scales (cols % 32 == 0);
+ *  q_t, scales_t  the data gradient's transposed cache, pt_mx_quantize_t
+ *                 of each W_g: E4M3 [G, cols, rows] / E2M1 [G, cols, rows/2]
+ *                 codes, [G, cols, rows/32] scales (rows % 32 == 0).
+ * Either pair may be NULL (not both).  experts as for pt_stack_experts (a
+ * bad address quantises a zero matrix and sets error bit 3).
+ *  dtype   PT_MXFP8_E4M3 or PT_MXFP4_E2M1.  Requirements: rows % 8 == 0,
+ *          cols % 8 == 0, G <= 65535; q and q_t 16-byte aligned.
+ */
+int pt_mx_quantize_experts(const void *const *experts, void *q, uint8_t *scales, void *q_t, uint8_t *scales_t,
+                           int64_t G, int64_t rows, int64_t cols, int dtype, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
  * Workspace of the grouped GEMMs (optional, for every op; recommended):
  * pt_grouped_gemm_workspace_size() bytes of device memory, 4-byte aligned.
  *  - word 0 receives the sticky device error bits (pt_read_error_flags);
@@ -330,7 +370,9 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N,
 /*
  * Sticky device error bits recorded in the first word of a workspace by the
  * grouped GEMM kernels (bit 0: a negative group length; bit 1: an expert
- * range outside [0, M] was clamped; bit 2: the lengths do not sum to M).
+ * range outside [0, M] was clamped; bit 2: the lengths do not sum to M) and
+ * by the expert-weight kernels (bit 3: an expert address was NULL or not
+ * 16-byte aligned).
  * The caller zeroes the word before the calls it wants to check.  This call
  * synchronises `stream` and copies the word to *flags (host pointer).
  */

@@ -25,6 +25,7 @@ __all__ = [
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu",
     "pt_grouped_gemm_wgrad",
     "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
+    "pt_stack_experts", "pt_mx_quantize_experts", "expert_addresses",
     "pt_grouped_gemm_workspace_size", "pt_read_error_flags", "pt_status_string", "pt_version",
 ]
 
@@ -35,6 +36,7 @@ PT_OP_FWD, PT_OP_DGRAD, PT_OP_WGRAD = 0, 1, 2
 EXPORTS = (
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",
     "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
+    "pt_stack_experts", "pt_mx_quantize_experts",
     "pt_grouped_gemm_workspace_size", "pt_read_error_flags", "pt_status_string", "pt_version",
 )
 
@@ -81,6 +83,10 @@ def load(require_gpu: bool = True):
     L.pt_fp8_quantize_rows.restype = i32
     L.pt_fp8_quantize_rows.argtypes = [p, p, p, p, i64, i64, p]
     L.pt_grouped_gemm_workspace_size.restype = sz
+    L.pt_stack_experts.restype = i32
+    L.pt_stack_experts.argtypes = [p, p, i64, i64, i64, i32, p, sz, p]
+    L.pt_mx_quantize_experts.restype = i32
+    L.pt_mx_quantize_experts.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p, sz, p]
     L.pt_grouped_gemm_workspace_size.argtypes = [i32, i64, i64, i64, i64, i32]
     L.pt_read_error_flags.restype = i32
     L.pt_read_error_flags.argtypes = [p, p, ctypes.POINTER(ctypes.c_uint32)]
@@ -185,6 +191,29 @@ def pt_fp8_quantize_rows(x, q, amax, dequant, rows, cols, stream=None):
     L = load()
     _check("pt_fp8_quantize_rows", L.pt_fp8_quantize_rows(
         _ptr(x), _ptr(q), _ptr(amax), _ptr(dequant), rows, cols, _stream(stream)))
+
+
+def expert_addresses(weights, device=None) -> torch.Tensor:
+    """The device array of expert weight addresses that pt_stack_experts and
+    pt_mx_quantize_experts take, from a list of device tensors (the tensors
+    must outlive the calls that use it)."""
+    for w in weights:
+        _ptr(w)
+    dev = device if device is not None else (weights[0].device if len(weights) else "cuda")
+    return torch.tensor([w.data_ptr() for w in weights], dtype=torch.int64, device=dev)
+
+
+def pt_stack_experts(experts, out, G, rows, cols, transpose, workspace=None, stream=None):
+    L = load()
+    _check("pt_stack_experts", L.pt_stack_experts(
+        _ptr(experts), _ptr(out), G, rows, cols, transpose, _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def pt_mx_quantize_experts(experts, q, scales, q_t, scales_t, G, rows, cols, dtype, workspace=None, stream=None):
+    L = load()
+    _check("pt_mx_quantize_experts", L.pt_mx_quantize_experts(
+        _ptr(experts), _ptr(q), _ptr(scales), _ptr(q_t), _ptr(scales_t), G, rows, cols, dtype,
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def pt_grouped_gemm_workspace_size(op, G, M, N, K, dtype) -> int:

@@ -437,6 +437,37 @@ int pt_mx_quantize_t(const void *x, void *q, uint8_t *scales, int64_t batch, int
                                         dtype == PT_MXFP8_E4M3 ? 0 : 1, (hipStream_t)stream));
 }
 
+int pt_stack_experts(const void *const *experts, void *out, int64_t G, int64_t rows, int64_t cols, int transpose,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (G < 0 || rows < 0 || cols < 0 || (transpose != 0 && transpose != 1)) return PT_ERR_INVALID_ARG;
+    if (G > 65535 || rows % 8 || cols % 8) return PT_ERR_UNSUPPORTED;
+    if (G == 0 || rows == 0 || cols == 0) return PT_OK;
+    if (!experts || !out) return PT_ERR_INVALID_ARG;
+    if (!aligned16(out) || ((uintptr_t)experts & 7)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    return hip_status(launch_stack_experts(experts, (uint16_t *)out, (int)G, rows, cols, transpose,
+                                           error_word(workspace, workspace_bytes), (hipStream_t)stream));
+}
+
+int pt_mx_quantize_experts(const void *const *experts, void *q, uint8_t *scales, void *q_t, uint8_t *scales_t,
+                           int64_t G, int64_t rows, int64_t cols, int dtype, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    if (G < 0 || rows < 0 || cols < 0) return PT_ERR_INVALID_ARG;
+    if ((q == nullptr) != (scales == nullptr) || (q_t == nullptr) != (scales_t == nullptr)) return PT_ERR_INVALID_ARG;
+    if (!q && !q_t) return PT_ERR_INVALID_ARG;
+    if (dtype != PT_MXFP8_E4M3 && dtype != PT_MXFP4_E2M1) return PT_ERR_UNSUPPORTED;
+    if (G > 65535 || rows % 8 || cols % 8 || (q && cols % 32) || (q_t && rows % 32)) return PT_ERR_UNSUPPORTED;
+    if (G == 0 || rows == 0 || cols == 0) return PT_OK;
+    if (!experts) return PT_ERR_INVALID_ARG;
+    if ((q && !aligned16(q)) || (q_t && !aligned16(q_t)) || ((uintptr_t)experts & 7)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    return hip_status(launch_mx_quantize_experts(experts, (uint8_t *)q, scales, (uint8_t *)q_t, scales_t, (int)G,
+                                                 rows, cols, dtype == PT_MXFP8_E4M3 ? 0 : 1,
+                                                 error_word(workspace, workspace_bytes), (hipStream_t)stream));
+}
+
 size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, int64_t K, int dtype)
 {
     // the error word and the tile-queue counters; for an MX forward also the

@@ -21,6 +21,7 @@ constexpr int kWave = 64;
 constexpr uint32_t kErrNegativeLen = 1u;
 constexpr uint32_t kErrClamped = 2u;
 constexpr uint32_t kErrSumMismatch = 4u;
+constexpr uint32_t kErrBadPointer = 8u;     // an expert weight address NULL or not 16-byte aligned
 
 // ------------------------------------------------------------------ numerics
 __device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }

@@ -331,6 +331,139 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_dequant_kernel(const uint8
     }
 }
 
+// ------------------------------------------------------------------ expert weight stack
+// Per-expert weights are G separate bf16 matrices W_g [R, C] (row-major),
+// given as a device array of their addresses.  One read of each builds the
+// stacked operand of the grouped GEMMs -- [G, R, C], or the per-expert
+// transpose [G, C, R] -- or directly its MX caches, where a stack followed
+// by a transposing copy would move every byte twice.  Each workgroup owns a
+// 64 x 64 tile of one expert (grid: column tiles, row tiles, experts).  A
+// NULL or misaligned address reads as a zero matrix and sets an error bit.
+
+__device__ __forceinline__ const uint16_t *expert_ptr(const void *const *ptrs, uint32_t *err)
+{
+    const uint16_t *p = (const uint16_t *)ptrs[blockIdx.z];
+    const bool ok = p != nullptr && ((uintptr_t)p & 15) == 0;
+    if (!ok && err && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) atomicOr(err, kErrBadPointer);
+    return ok ? p : nullptr;
+}
+
+// This thread's two 16-byte row chunks of the tile (zeros outside W_g): 64
+// rows x 8 chunks of 8 columns, eight lanes per row.
+__device__ __forceinline__ void load_rows(const uint16_t *xb, int64_t R, int64_t C, int64_t r0, int64_t c0,
+                                          uintx4 (&v)[2])
+{
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int k = threadIdx.x + j * kThreads;
+        const int row = k >> 3, c8 = (k & 7) * 8;
+        v[j] = uintx4{0u, 0u, 0u, 0u};
+        if (xb && r0 + row < R && c0 + c8 < C) v[j] = *(const uintx4 *)(xb + (r0 + row) * C + c0 + c8);
+    }
+}
+
+__device__ __forceinline__ void rows_to_lds(const uintx4 (&v)[2], uint8_t *tile)
+{
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int k = threadIdx.x + j * kThreads;
+        uint32_t *d = (uint32_t *)(tile + (k >> 3) * TQ_RS + (k & 7) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = v[j][e];
+    }
+}
+
+template <int TRANS>
+__global__ __launch_bounds__(kThreads) void stack_experts_kernel(const void *const *ptrs, uint16_t *__restrict__ out,
+                                                                 int64_t R, int64_t C, uint32_t *err)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[TRANS ? TQ * TQ_RS : 16];
+    const int64_t g = blockIdx.z;
+    const int64_t r0 = (int64_t)blockIdx.y * TQ, c0 = (int64_t)blockIdx.x * TQ;
+    uintx4 v[2];
+    load_rows(expert_ptr(ptrs, err), R, C, r0, c0, v);
+    if (!TRANS) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int k = threadIdx.x + j * kThreads;
+            const int row = k >> 3, c8 = (k & 7) * 8;
+            if (r0 + row < R && c0 + c8 < C) *(uintx4 *)(out + (g * R + r0 + row) * C + c0 + c8) = v[j];
+        }
+        return;
+    }
+    rows_to_lds(v, tile);
+    __syncthreads();
+    // the tile's 64 columns become 64 output rows of 8 chunks of 8 values,
+    // each chunk read down a column of the LDS tile
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int k = threadIdx.x + j * kThreads;
+        const int oc = k >> 3, r8 = (k & 7) * 8;
+        if (c0 + oc < C && r0 + r8 < R) {
+            uintx4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = *(const uint16_t *)(tile + (r8 + 2 * e) * TQ_RS + oc * 2);
+                const uint32_t hi = *(const uint16_t *)(tile + (r8 + 2 * e + 1) * TQ_RS + oc * 2);
+                o[e] = lo | (hi << 16);
+            }
+            *(uintx4 *)(out + (g * C + c0 + oc) * R + r0 + r8) = o;
+        }
+    }
+}
+
+// Both MX caches of the expert weights from one read: q/scales quantise W_g
+// along C (each lane quad holds 32 consecutive columns of one row in
+// registers: C % 32 == 0), qt/scales_t quantise W_g^T along R through the
+// LDS tile as mx_quantize_t_kernel does (R % 32 == 0).  Either pair may be
+// absent; the choice is uniform over the grid.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void mx_quantize_experts_kernel(const void *const *ptrs,
+                                                                       uint8_t *__restrict__ q,
+                                                                       uint8_t *__restrict__ scales,
+                                                                       uint8_t *__restrict__ qt,
+                                                                       uint8_t *__restrict__ scales_t, int64_t R,
+                                                                       int64_t C, uint32_t *err)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[TQ * TQ_RS];
+    const int64_t g = blockIdx.z;
+    const int64_t r0 = (int64_t)blockIdx.y * TQ, c0 = (int64_t)blockIdx.x * TQ;
+    uintx4 v[2];
+    load_rows(expert_ptr(ptrs, err), R, C, r0, c0, v);
+    if (qt) rows_to_lds(v, tile);
+    if (q) {
+        uint8_t *qb = q + g * R * (FMT == 0 ? C : C / 2);
+        uint8_t *sb = scales + g * R * (C / 32);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int k = threadIdx.x + j * kThreads;
+            const int row = k >> 3, c8 = (k & 7) * 8;
+            // a quad's 32 columns are in or out together (C % 32 == 0)
+            if (r0 + row < R && c0 + c8 < C) quantise8<FMT>(v[j], qb, sb, ((r0 + row) * C + c0 + c8) / 8);
+        }
+    }
+    if (!qt) return;
+    __syncthreads();
+    const int64_t RB = R / 8;
+    uint8_t *qb = qt + g * C * (FMT == 0 ? R : R / 2);
+    uint8_t *sb = scales_t + g * C * (R / 32);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = threadIdx.x + j * kThreads;
+        const int quad = t >> 2, qq = t & 3;
+        const int col = quad & (TQ - 1), blk = quad >> 6;
+        const int rr = blk * 32 + qq * 8;
+        uintx4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = *(const uint16_t *)(tile + (rr + 2 * e) * TQ_RS + col * 2);
+            const uint32_t hi = *(const uint16_t *)(tile + (rr + 2 * e + 1) * TQ_RS + col * 2);
+            w[e] = lo | (hi << 16);
+        }
+        if (c0 + col < C && r0 + blk * 32 < R) quantise8<FMT>(w, qb, sb, (c0 + col) * RB + (r0 + rr) / 8);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t rows, int64_t cols,
@@ -405,6 +538,34 @@ hipError_t launch_mx_dequant_tokens(const uint8_t *q, const uint8_t *scales, con
     const dim3 grid((unsigned)((M + kThreads / 64 - 1) / (kThreads / 64)));
     hipLaunchKernelGGL(mx_tokens_dequant_kernel, grid, dim3(kThreads), table_bytes(G), s, q, scales, lens, offs, G, M,
                        C, out);
+    return hipGetLastError();
+}
+
+
+hipError_t launch_stack_experts(const void *const *ptrs, uint16_t *out, int G, int64_t R, int64_t C, int trans,
+                                uint32_t *err, hipStream_t s)
+{
+    if (G == 0 || R == 0 || C == 0) return hipSuccess;
+    const dim3 grid((unsigned)((C + TQ - 1) / TQ), (unsigned)((R + TQ - 1) / TQ), (unsigned)G);
+    if (trans)
+        hipLaunchKernelGGL(stack_experts_kernel<1>, grid, dim3(kThreads), 0, s, ptrs, out, R, C, err);
+    else
+        hipLaunchKernelGGL(stack_experts_kernel<0>, grid, dim3(kThreads), 0, s, ptrs, out, R, C, err);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize_experts(const void *const *ptrs, uint8_t *q, uint8_t *scales, uint8_t *qt,
+                                      uint8_t *scales_t, int G, int64_t R, int64_t C, int fmt, uint32_t *err,
+                                      hipStream_t s)
+{
+    if (G == 0 || R == 0 || C == 0) return hipSuccess;
+    const dim3 grid((unsigned)((C + TQ - 1) / TQ), (unsigned)((R + TQ - 1) / TQ), (unsigned)G);
+    if (fmt == 0)
+        hipLaunchKernelGGL(mx_quantize_experts_kernel<0>, grid, dim3(kThreads), 0, s, ptrs, q, scales, qt, scales_t,
+                           R, C, err);
+    else
+        hipLaunchKernelGGL(mx_quantize_experts_kernel<1>, grid, dim3(kThreads), 0, s, ptrs, q, scales, qt, scales_t,
+                           R, C, err);
     return hipGetLastError();
 }
 
