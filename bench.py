@@ -459,6 +459,36 @@ def bench_cfg3_wgrad(dev, stream, iters):
     return w
 
 
+def bench_stack(dev, stream, iters):
+    """The expert weight stack at the expert-MLP shape: 256 separately
+    allocated FC1 weights [2I, H] = [4096, 4096] -> the [G, H, 2I] operand in
+    one pass, and both MXFP8 weight caches from one read; the eager
+    stack-then-transpose copy is timed beside it for context."""
+    G, R, C = 256, 4096, 4096
+    ws = [synth.randn_bf16((R, C), seed=300 + g, std=R ** -0.5, device=dev) for g in range(G)]
+    addr = ptm.expert_addresses(ws)
+    out = torch.empty((G, C, R), dtype=torch.bfloat16, device=dev)
+    _, per = time_launches(lambda: ptm.pt_stack_experts(addr, out, G, R, C, 1, stream=stream), iters, 2, stream)
+    _, per_eager = time_launches(lambda: torch.stack(ws).transpose(1, 2).contiguous(), max(3, iters // 4), 1, stream)
+    nbytes = 2 * G * R * C * 2
+    st = summary("expert weight stack + transpose, 256 x [4096, 4096] bf16 -> [256, 4096, 4096]", "bf16", 0,
+                 nbytes, per, {"eager_stack_transpose_contiguous_ms_median": round(float(np.median(per_eager)), 4)})
+    del out
+    torch.cuda.empty_cache()
+    q = torch.empty((G, R, C), dtype=torch.uint8, device=dev)
+    s = torch.empty((G, R, C // 32), dtype=torch.uint8, device=dev)
+    qt = torch.empty((G, C, R), dtype=torch.uint8, device=dev)
+    sct = torch.empty((G, C, R // 32), dtype=torch.uint8, device=dev)
+    _, per_q = time_launches(lambda: ptm.pt_mx_quantize_experts(addr, q, s, qt, sct, G, R, C, ptm.PT_MXFP8_E4M3,
+                                                                stream=stream), iters, 2, stream)
+    nbytes_q = G * R * C * 2 + 2 * (G * R * C + G * R * C // 32)
+    mq = summary("both MXFP8 weight caches (along K, and transposed along N) from 256 separate [4096, 4096] "
+                 "bf16 weights, one read", "mxfp8", 0, nbytes_q, per_q)
+    del ws, addr, q, s, qt, sct
+    torch.cuda.empty_cache()
+    return st, mq
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -550,6 +580,9 @@ def main():
             log("per_config: MXFP8 wgrad")
             per["cfg3_mxfp8_wgrad"] = bench_cfg3_wgrad(dev, stream, iters)
             torch.cuda.empty_cache()
+        if want is None or "stack" in want:
+            log("per_config: expert weight stack")
+            per["stack_experts_transpose"], per["stack_experts_mxfp8_caches"] = bench_stack(dev, stream, iters)
         if want is None or "cfg4" in want:
             log("per_config: MXFP4 MLP")
             per["cfg4_mxfp4_mlp"] = bench_cfg4(dev, stream, iters, b_keep_lens)
