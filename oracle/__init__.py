@@ -69,7 +69,7 @@ def lib():
         L.orc_wgrad_rows.restype = i32
         L.orc_wgrad_rows.argtypes = [p, p, p, i64, i64, i64, i64, p, p, i64, p]
         L.orc_mx_quantize_tokens.restype = i64
-        L.orc_mx_quantize_tokens.argtypes = [p, p, i64, i64, i64, p, p]
+        L.orc_mx_quantize_tokens.argtypes = [p, p, i64, i64, i64, ctypes.c_int, p, p]
         L.orc_fp8_quantize.restype = None
         L.orc_fp8_quantize.argtypes = [p, i64, i64, p, p, p]
         L.orc_swiglu.restype = None
@@ -179,25 +179,40 @@ def mx_quantize_experts(weights, dtype: int):
             np.stack([t[0] for t in tr]), np.stack([t[1] for t in tr]))
 
 
-def mx_quantize_tokens(x_bits: np.ndarray, group_lens: np.ndarray):
-    """MXFP8 (E4M3) quantisation along tokens within each expert: x_bits
-    [M, cols] bf16 bits.  Returns (codes [M, cols], scales [M // 32 + G, cols],
-    number of scale rows used); unused scale rows are zero."""
+def mx_quantize_tokens(x_bits: np.ndarray, group_lens: np.ndarray, dtype: int = E4M3):
+    """MX quantisation along tokens within each expert: x_bits [M, cols] bf16
+    bits.  Returns (codes: E4M3 [M, cols] / E2M1 [M, cols/2] with the even
+    column in the low nibble, scales [M // 32 + G, cols], number of scale
+    rows used); unused scale rows are zero."""
     x = _c(x_bits, np.uint16)
     lens = _c(group_lens, np.int64)
     M, cols = x.shape
-    q = np.zeros((M, cols), np.uint8)
+    q = np.zeros((M, cols if dtype == E4M3 else cols // 2), np.uint8)
     s = np.zeros((M // 32 + lens.size, cols), np.uint8)
-    nb = lib().orc_mx_quantize_tokens(_ptr(x), _ptr(lens), lens.size, M, cols, _ptr(q), _ptr(s))
+    nb = lib().orc_mx_quantize_tokens(_ptr(x), _ptr(lens), lens.size, M, cols, dtype, _ptr(q), _ptr(s))
+    if nb < 0:
+        raise ValueError("orc_mx_quantize_tokens: bad arguments")
     return q, s, int(nb)
 
 
-def mx_dequantize_tokens(q: np.ndarray, s: np.ndarray, group_lens: np.ndarray) -> np.ndarray:
+def _element_values(q: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact values of E4M3 codes, or of E2M1 nibble pairs unpacked along the
+    row (low nibble first)."""
+    if dtype == E4M3:
+        table = np.array([e4m3_value(c) for c in range(256)], np.float64)
+        return table[q]
+    table = np.array([e2m1_value(c) for c in range(16)], np.float64)
+    out = np.empty((q.shape[0], 2 * q.shape[1]), np.float64)
+    out[:, 0::2] = table[q & 0xF]
+    out[:, 1::2] = table[q >> 4]
+    return out
+
+
+def mx_dequantize_tokens(q: np.ndarray, s: np.ndarray, group_lens: np.ndarray, dtype: int = E4M3) -> np.ndarray:
     """Exact binary64 values of mx_quantize_tokens' output."""
     lens = np.asarray(group_lens, np.int64)
-    table = np.array([e4m3_value(c) for c in range(256)], np.float64)
-    vals = table[_c(q, np.uint8)]
-    out = np.empty(q.shape, np.float64)
+    vals = _element_values(_c(q, np.uint8), dtype)
+    out = np.empty(vals.shape, np.float64)
     off = b = 0
     for g in range(lens.size):
         for j in range((int(lens[g]) + 31) // 32):

@@ -319,32 +319,58 @@ void orc_fp8_quantize(const uint16_t *x, int64_t batch, int64_t n, uint8_t *q, f
  * time: expert g's rows [off_g, off_g + len_g) of x [M, cols] form blocks of
  * 32 consecutive rows, the last one partial when len_g % 32 != 0 (its
  * missing rows are simply absent: the block scale comes from the rows that
- * exist), so no block straddles two experts.  Codes keep x's layout
- * (q [M, cols], E4M3 only); block j of expert g takes scale row
- * bstart_g + j, bstart_g = sum over earlier experts of ceil(len / 32).
- * Returns the number of scale rows used.
+ * exist), so no block straddles two experts.  Codes keep x's row layout:
+ * E4M3 q [M, cols]; E2M1 q [M, cols/2] with column 2c in the low nibble of
+ * byte c and column 2c+1 in the high one.  Block j of expert g takes scale
+ * row bstart_g + j, bstart_g = sum over earlier experts of ceil(len / 32).
+ * Returns the number of scale rows used, or -1 for a bad dtype or an odd
+ * E2M1 column count.
  */
-int64_t orc_mx_quantize_tokens(const uint16_t *x, const int64_t *lens, int64_t G, int64_t M, int64_t cols,
-                               uint8_t *q, uint8_t *scales)
+static void tokens_block(const uint16_t *x, int64_t cols, int64_t r0, int64_t nr, int64_t c, int dtype,
+                         const double *vals, int n, int *codes, uint8_t *scale)
 {
+    double v[32];
+    for (int64_t i = 0; i < nr; ++i)
+        v[i] = orc_bf16_value(x[(r0 + i) * cols + c]);
+    int E = block_scale(dtype, v, (int)nr);
+    *scale = (uint8_t)E;
+    const int sbit = dtype == ORC_E4M3 ? 7 : 3;
+    for (int64_t i = 0; i < nr; ++i) {
+        double xi = ldexp(v[i], 127 - E);
+        codes[i] = ((signbit(v[i]) ? 1 : 0) << sbit) | nearest_code(fabs(xi), vals, n);
+    }
+}
+
+int64_t orc_mx_quantize_tokens(const uint16_t *x, const int64_t *lens, int64_t G, int64_t M, int64_t cols,
+                               int dtype, uint8_t *q, uint8_t *scales)
+{
+    if ((dtype != ORC_E4M3 && dtype != ORC_E2M1) || (dtype == ORC_E2M1 && cols % 2))
+        return -1;
     double vals[128];
-    int n = positive_grid(ORC_E4M3, vals);
+    int n = positive_grid(dtype, vals);
     int64_t off = 0, bstart = 0;
     for (int64_t g = 0; g < G; ++g) {
         int64_t len = lens[g], nb = (len + 31) / 32;
         for (int64_t j = 0; j < nb; ++j) {
             int64_t r0 = off + 32 * j, nr = len - 32 * j < 32 ? len - 32 * j : 32;
+            uint8_t *srow = scales + (bstart + j) * cols;
+            if (dtype == ORC_E4M3) {
 #pragma omp parallel for schedule(static)
-            for (int64_t c = 0; c < cols; ++c) {
-                double v[32];
-                for (int64_t i = 0; i < nr; ++i)
-                    v[i] = orc_bf16_value(x[(r0 + i) * cols + c]);
-                int E = block_scale(ORC_E4M3, v, (int)nr);
-                scales[(bstart + j) * cols + c] = (uint8_t)E;
-                for (int64_t i = 0; i < nr; ++i) {
-                    double xi = ldexp(v[i], 127 - E);
-                    int code = nearest_code(fabs(xi), vals, n);
-                    q[(r0 + i) * cols + c] = (uint8_t)(((signbit(v[i]) ? 1 : 0) << 7) | code);
+                for (int64_t c = 0; c < cols; ++c) {
+                    int codes[32];
+                    tokens_block(x, cols, r0, nr, c, dtype, vals, n, codes, srow + c);
+                    for (int64_t i = 0; i < nr; ++i)
+                        q[(r0 + i) * cols + c] = (uint8_t)codes[i];
+                }
+            } else {
+                /* a byte holds two columns, so one thread takes both */
+#pragma omp parallel for schedule(static)
+                for (int64_t cp = 0; cp < cols / 2; ++cp) {
+                    int lo[32], hi[32];
+                    tokens_block(x, cols, r0, nr, 2 * cp, dtype, vals, n, lo, srow + 2 * cp);
+                    tokens_block(x, cols, r0, nr, 2 * cp + 1, dtype, vals, n, hi, srow + 2 * cp + 1);
+                    for (int64_t i = 0; i < nr; ++i)
+                        q[(r0 + i) * (cols / 2) + cp] = (uint8_t)(lo[i] | (hi[i] << 4));
                 }
             }
         }

@@ -374,45 +374,75 @@ def test_fp8_fwd_rows_rowwise_matches_dense(orc):
         assert np.allclose(got[i], ref, rtol=1e-14, atol=0), r
 
 
-def test_mx_quantize_tokens_full_blocks_equal_axis0(orc):
+def _codes_axis0(q, fmt):
+    # per-element codes of the axis-0 quantiser (E2M1 packs rows 2i, 2i+1)
+    if fmt == E4M3:
+        return q
+    out = np.empty((2 * q.shape[0], q.shape[1]), np.uint8)
+    out[0::2], out[1::2] = q & 0xF, q >> 4
+    return out
+
+
+def _codes_tokens(q, fmt):
+    # per-element codes along tokens (E2M1 packs columns 2c, 2c+1)
+    if fmt == E4M3:
+        return q
+    out = np.empty((q.shape[0], 2 * q.shape[1]), np.uint8)
+    out[:, 0::2], out[:, 1::2] = q & 0xF, q >> 4
+    return out
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E2M1], ids=["e4m3", "e2m1"])
+def test_mx_quantize_tokens_full_blocks_equal_axis0(orc, fmt):
     # experts whose lengths are multiples of 32 reduce to the plain column-block
     # quantiser (axis 0) on each expert's rows
     lens = np.array([64, 0, 32, 96])
     x = rand_bf16((int(lens.sum()), 48), seed=76, std=2.0)
-    q, s, nb = orc.mx_quantize_tokens(x, lens)
+    q, s, nb = orc.mx_quantize_tokens(x, lens, fmt)
     assert nb == 6
+    codes = _codes_tokens(q, fmt)
     offs = np.concatenate([[0], np.cumsum(lens)])
     b = 0
     for g in range(lens.size):
         if lens[g] == 0:
             continue
-        rq, rs = orc.mx_quantize(x[offs[g]:offs[g + 1]], E4M3, axis=0)
-        assert (q[offs[g]:offs[g + 1]] == rq).all(), g
+        rq, rs = orc.mx_quantize(x[offs[g]:offs[g + 1]], fmt, axis=0)
+        assert (codes[offs[g]:offs[g + 1]] == _codes_axis0(rq, fmt)).all(), g
         assert (s[b:b + lens[g] // 32] == rs).all(), g
         b += lens[g] // 32
 
 
-def test_mx_quantize_tokens_partial_block_equals_zero_padding(orc):
+@pytest.mark.parametrize("fmt", [E4M3, E2M1], ids=["e4m3", "e2m1"])
+def test_mx_quantize_tokens_partial_block_equals_zero_padding(orc, fmt):
     # a partial last block behaves as if padded with zero rows (zeros change
     # neither the amax nor the other codes), and it never mixes two experts
     lens = np.array([45, 7, 33])
     M = int(lens.sum())
     x = rand_bf16((M, 32), seed=77, std=1.0)
-    q, s, nb = orc.mx_quantize_tokens(x, lens)
+    q, s, nb = orc.mx_quantize_tokens(x, lens, fmt)
     assert nb == 2 + 1 + 2
+    codes = _codes_tokens(q, fmt)
     offs = np.concatenate([[0], np.cumsum(lens)])
     b = 0
     for g in range(lens.size):
         n = int(lens[g])
         pad = np.zeros((((n + 31) // 32) * 32, 32), np.uint16)
         pad[:n] = x[offs[g]:offs[g + 1]]
-        rq, rs = orc.mx_quantize(pad, E4M3, axis=0)
-        assert (q[offs[g]:offs[g + 1]] == rq[:n]).all(), g
+        rq, rs = orc.mx_quantize(pad, fmt, axis=0)
+        assert (codes[offs[g]:offs[g + 1]] == _codes_axis0(rq, fmt)[:n]).all(), g
         assert (s[b:b + (n + 31) // 32] == rs).all(), g
         b += (n + 31) // 32
     # the dequantised values are the codes times their block's scale
-    v = orc.mx_dequantize_tokens(q, s, lens)
-    assert np.abs(v - orc.bf16_to_f64(x)).max() <= np.abs(orc.bf16_to_f64(x)).max() * 2 ** -3
+    v = orc.mx_dequantize_tokens(q, s, lens, fmt)
+    tol = 2 ** -3 if fmt == E4M3 else 2 ** -1
+    assert np.abs(v - orc.bf16_to_f64(x)).max() <= np.abs(orc.bf16_to_f64(x)).max() * tol
+
+
+def _token_block_scales(s, lens):
+    blk = np.concatenate([b0 + np.arange(n) // 32 for b0, n in
+                          zip(np.concatenate([[0], np.cumsum((lens + 31) // 32)[:-1]]), lens)])
+    return torch.from_numpy(np.ascontiguousarray(s[blk])).view(torch.float8_e8m0fnu).double().numpy()
+
 
 def test_mx_dequantize_tokens_matches_torch_decode(orc):
     # every finite E4M3 code, decoded by torch's float8_e4m3fn and scaled by
@@ -428,10 +458,28 @@ def test_mx_dequantize_tokens_matches_torch_decode(orc):
     s[:nb] = rng.integers(110, 145, size=(nb, C))
     got = orc.mx_dequantize_tokens(q, s, lens)
     vals = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy()
-    blk = np.concatenate([b0 + np.arange(n) // 32 for b0, n in
-                          zip(np.concatenate([[0], np.cumsum((lens + 31) // 32)[:-1]]), lens)])
-    scl = torch.from_numpy(np.ascontiguousarray(s[blk])).view(torch.float8_e8m0fnu).double().numpy()
-    assert (got == vals * scl).all()
+    assert (got == vals * _token_block_scales(s, lens)).all()
+
+
+def test_mx_dequantize_tokens_e2m1_matches_golden_table(orc):
+    # E2M1 nibbles decoded from the OCP table in tests/golden (low nibble =
+    # even column), times torch's decoding of the row's block scale
+    table = dict(_read_table("e2m1_values.txt"))
+    assert len(table) == 16
+    lens = np.array([33, 0, 64, 5])
+    M, C = int(lens.sum()), 16
+    rng = np.random.default_rng(79)
+    q = rng.integers(0, 256, size=(M, C // 2)).astype(np.uint8)
+    nb = int(sum((n + 31) // 32 for n in lens))
+    s = np.zeros((M // 32 + lens.size, C), np.uint8)
+    s[:nb] = rng.integers(110, 145, size=(nb, C))
+    got = orc.mx_dequantize_tokens(q, s, lens, E2M1)
+    vals = np.empty((M, C))
+    for r in range(M):
+        for c in range(C):
+            nib = (q[r, c // 2] >> (4 * (c & 1))) & 0xF
+            vals[r, c] = table[int(nib)]
+    assert (got == vals * _token_block_scales(s, lens)).all()
 
 
 def test_stack_experts_by_index(orc):
