@@ -203,14 +203,16 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_sa
  *  accumulating and writes zeros when not.
  *  workspace  optional (may be NULL) for BF16, see
  *             pt_grouped_gemm_workspace_size.
- *  PT_MXFP8_E4M3: a and dy are E4M3 codes [M, K] / [M, N] blocked along
- *  tokens within each expert, with scales [M/32 + G, K] / [M/32 + G, N]
- *  (pt_mx_quantize_tokens); D_g sums the products of their exact values
- *  (each code times its block's scale; values below bf16's smallest
- *  subnormal round to nearest even).  The workspace is required and holds
- *  bf16 copies of both operands: pt_grouped_gemm_workspace_size(PT_OP_WGRAD,
- *  ..., PT_MXFP8_E4M3) bytes, else PT_ERR_WORKSPACE.
- *  Requirements: K % 8 == 0, N % 8 == 0; dtype PT_BF16 or PT_MXFP8_E4M3.
+ *  PT_MXFP8_E4M3 / PT_MXFP4_E2M1: a and dy are codes blocked along tokens
+ *  within each expert (pt_mx_quantize_tokens): E4M3 [M, K] / [M, N], or
+ *  E2M1 [M, K/2] / [M, N/2], with scales [M/32 + G, K] / [M/32 + G, N];
+ *  D_g sums the products of their exact values (each code times its
+ *  block's scale; values below bf16's smallest subnormal round to nearest
+ *  even).  The workspace is required and holds bf16 copies of both
+ *  operands: pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ..., dtype) bytes,
+ *  else PT_ERR_WORKSPACE.
+ *  Requirements: K % 8 == 0, N % 8 == 0; dtype PT_BF16, PT_MXFP8_E4M3 or
+ *  PT_MXFP4_E2M1.
  */
 int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
                           const void *dy, const uint8_t *dy_scale,
@@ -258,20 +260,21 @@ int pt_mx_quantize_t(const void *x, void *q, uint8_t *scales,
                      int64_t batch, int64_t rows, int64_t cols, int dtype, void *stream);
 
 /*
- * MXFP8 quantisation along tokens for the weight gradient (the MX grouped
+ * MX quantisation along tokens for the weight gradient (the MX grouped
  * GEMM's backward flow, PR page "[Megatron-LM] feat: add grouped gemm fp4
  * support, ...", Copilot overview; the Primus-Turbo README's "pad-aware
  * paths" keep quantisation blocks inside one expert): within each expert g,
  * rows [off_g, off_g + len_g) of x [M, cols] (bf16) form blocks of 32
  * consecutive rows, the last one partial when len_g % 32 != 0, so no block
  * straddles two experts.  Each block of each column is quantised by the
- * rule of pt_mx_quantize (E4M3) over the rows it has.
- *  q       [M, cols] E4M3 codes (x's layout);
+ * rule of pt_mx_quantize over the rows it has.
+ *  q       E4M3: [M, cols] codes (x's layout); E2M1: [M, cols/2], column
+ *          2c in the low nibble of byte c, column 2c + 1 in the high one;
  *  scales  [M/32 + G, cols] E8M0: block j of expert g is row
  *          sum over earlier experts of ceil(len/32), plus j; rows past the
  *          last block are left as they are.
  *  group_offs may be NULL (derived by exclusive scan on the device).
- *  dtype   PT_MXFP8_E4M3.  Requirements: cols % 8 == 0; x, q and scales
+ *  dtype   PT_MXFP8_E4M3 or PT_MXFP4_E2M1.  Requirements: cols % 8 == 0; x, q and scales
  *          16-byte aligned.  workspace optional (the error word).
  */
 int pt_mx_quantize_tokens(const void *x, const int64_t *group_lens, const int64_t *group_offs, void *q,

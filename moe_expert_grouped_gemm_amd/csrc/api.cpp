@@ -313,10 +313,11 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
     if (N % 8 || K % 8) return PT_ERR_UNSUPPORTED;
     if (!fits31(M * K * 2) || !fits31(M * N * 2)) return PT_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    if (dtype == PT_MXFP8_E4M3) {
+    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) {
         // codes blocked along tokens (pt_mx_quantize_tokens): their exact
         // values are written as bf16 into the workspace, then the BF16 weight
         // gradient runs on them (exact products, fp32 sums, as MX does)
+        const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
         if (M > 0 && (!a_scale || !dy_scale)) return PT_ERR_INVALID_ARG;
         if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad) || !aligned16(a_scale) || !aligned16(dy_scale))
             return PT_ERR_MISALIGNED;
@@ -325,9 +326,11 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
         if (!workspace || workspace_bytes < need) return PT_ERR_WORKSPACE;
         uint16_t *wa = (uint16_t *)((uint8_t *)workspace + kQueueWsBytes);
         uint16_t *wd = (uint16_t *)((uint8_t *)wa + round256(M * K * 2));
-        hipError_t e = launch_mx_dequant_tokens((const uint8_t *)a, a_scale, group_lens, group_offs, (int)G, M, K, wa, s);
+        hipError_t e =
+            launch_mx_dequant_tokens((const uint8_t *)a, a_scale, group_lens, group_offs, (int)G, M, K, fmt, wa, s);
         if (e == hipSuccess)
-            e = launch_mx_dequant_tokens((const uint8_t *)dy, dy_scale, group_lens, group_offs, (int)G, M, N, wd, s);
+            e = launch_mx_dequant_tokens((const uint8_t *)dy, dy_scale, group_lens, group_offs, (int)G, M, N, fmt, wd,
+                                         s);
         if (e != hipSuccess) return PT_ERR_HIP;
         return pt_grouped_gemm_wgrad(wa, nullptr, wd, nullptr, main_grad, group_lens, group_offs, G, M, N, K, PT_BF16,
                                      trans_out, accumulate, workspace, workspace_bytes, stream);
@@ -397,7 +400,7 @@ int pt_mx_quantize_tokens(const void *x, const int64_t *group_lens, const int64_
     int st = check_groups(group_lens, G, M);
     if (st) return st;
     if (cols < 0) return PT_ERR_INVALID_ARG;
-    if (dtype != PT_MXFP8_E4M3) return PT_ERR_UNSUPPORTED;
+    if (dtype != PT_MXFP8_E4M3 && dtype != PT_MXFP4_E2M1) return PT_ERR_UNSUPPORTED;
     if (cols % 8 || M / 32 + G > INT32_MAX) return PT_ERR_UNSUPPORTED;
     if (M == 0 || cols == 0) return PT_OK;
     if (!x || !q || !scales) return PT_ERR_INVALID_ARG;
@@ -405,8 +408,8 @@ int pt_mx_quantize_tokens(const void *x, const int64_t *group_lens, const int64_
     if (!fits31(M * cols)) return PT_ERR_UNSUPPORTED;
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
     return hip_status(launch_mx_quantize_tokens((const uint16_t *)x, group_lens, group_offs, (int)G, M, cols,
-                                                (uint8_t *)q, scales, error_word(workspace, workspace_bytes),
-                                                (hipStream_t)stream));
+                                                dtype == PT_MXFP8_E4M3 ? 0 : 1, (uint8_t *)q, scales,
+                                                error_word(workspace, workspace_bytes), (hipStream_t)stream));
 }
 
 int pt_fp8_quantize_rows(const void *x, void *q, float *amax, float *dequant, int64_t rows, int64_t cols,
@@ -479,7 +482,7 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, i
             return (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) + mx_swz_b_bytes(G, N, K, fmt));
     }
     // the MXFP8 weight gradient: bf16 copies of both operands
-    if (op == PT_OP_WGRAD && dtype == PT_MXFP8_E4M3 && M >= 0 && N > 0 && K > 0)
+    if (op == PT_OP_WGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && M >= 0 && N > 0 && K > 0)
         return (size_t)(kQueueWsBytes + round256(M * K * 2) + round256(M * N * 2));
     // the MX data gradient: K outputs per row, a reduction over N
     if (op == PT_OP_DGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && G > 0 && M >= 0 && N > 0 &&

@@ -103,13 +103,15 @@ hipError_t launch_fp8_quantize(const uint16_t *x, uint8_t *q, float *amax, float
 // The same with one scale per row of x [rows, cols].
 hipError_t launch_fp8_quantize_rows(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t rows,
                                     int64_t cols, hipStream_t s);
-// MXFP8 along tokens within each expert (blocks of 32 rows, the last
-// partial), codes [M, C] and scales [M / 32 + G, C]; and the exact bf16
-// values of such codes (the MX weight gradient runs on them).
+// MX along tokens within each expert (blocks of 32 rows, the last
+// partial), codes E4M3 [M, C] / E2M1 [M, C/2] (fmt 0 / 1) and scales
+// [M / 32 + G, C]; and the exact bf16 values of such codes (the MX weight
+// gradient runs on them).
 hipError_t launch_mx_quantize_tokens(const uint16_t *x, const int64_t *lens, const int64_t *offs, int G, int64_t M,
-                                     int64_t C, uint8_t *q, uint8_t *scales, uint32_t *err, hipStream_t s);
+                                     int64_t C, int fmt, uint8_t *q, uint8_t *scales, uint32_t *err, hipStream_t s);
 hipError_t launch_mx_dequant_tokens(const uint8_t *q, const uint8_t *scales, const int64_t *lens,
-                                    const int64_t *offs, int G, int64_t M, int64_t C, uint16_t *out, hipStream_t s);
+                                    const int64_t *offs, int G, int64_t M, int64_t C, int fmt, uint16_t *out,
+                                    hipStream_t s);
 // Expert weight stack: G separate bf16 matrices (a device array of their
 // addresses) -> [G, R, C], or [G, C, R] with trans; and their MX caches
 // along C ([G, R, C(/2)] + [G, R, C/32]) and/or along R of the transpose

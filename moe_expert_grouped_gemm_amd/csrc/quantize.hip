@@ -261,6 +261,8 @@ __device__ __forceinline__ int tokens_table(GroupTable &tab, int *sm, const int6
 }
 
 // grid (scale rows, column tiles of 256): one thread per column of a block
+// (E4M3), or per pair of columns, which share a code byte (E2M1)
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void mx_tokens_quant_kernel(const uint16_t *__restrict__ x,
                                                                    const int64_t *lens, const int64_t *offs, int G,
                                                                    int64_t M, int64_t C, uint8_t *__restrict__ q,
@@ -271,31 +273,67 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_kernel(const uint16_
     const int total = tokens_table(tab, sm_tok, lens, offs, G, M, err);
     const int b = blockIdx.x;
     const int64_t c = (int64_t)blockIdx.y * kThreads + threadIdx.x;
-    if (b >= total || c >= C) return;
+    if (b >= total || c >= (FMT == 0 ? C : C / 2)) return;
     const int g = find_group(tab, b);
     const int j = b - tab.tile0[g];
     const int64_t r0 = tab.row0[g] + 32 * j;
     const int nr = min(32, tab.rows[g] - 32 * j);
     uint32_t h[32];
-    uint32_t amax = 0;
+    if (FMT == 0) {
+        uint32_t amax = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        h[i] = i < nr ? x[(r0 + i) * C + c] : 0u;
-        amax = max(amax, h[i] & 0x7FFFu);
-    }
-    const uint32_t E = mx_scale_byte<8>(amax);
-    const int e = 127 - (int)E;
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-        if (i < nr) {
-            const float f = __builtin_fminf(__builtin_fmaxf(__builtin_ldexpf(bf16_to_f32(h[i]), e), -448.0f), 448.0f);
-            q[(r0 + i) * C + c] = (uint8_t)__builtin_amdgcn_cvt_pk_fp8_f32(f, 0.0f, 0, false);
+        for (int i = 0; i < 32; ++i) {
+            h[i] = i < nr ? x[(r0 + i) * C + c] : 0u;
+            amax = max(amax, h[i] & 0x7FFFu);
         }
-    scales[(int64_t)b * C + c] = (uint8_t)E;
+        const uint32_t E = mx_scale_byte<8>(amax);
+        const int e = 127 - (int)E;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            if (i < nr) {
+                const float f =
+                    __builtin_fminf(__builtin_fmaxf(__builtin_ldexpf(bf16_to_f32(h[i]), e), -448.0f), 448.0f);
+                q[(r0 + i) * C + c] = (uint8_t)__builtin_amdgcn_cvt_pk_fp8_f32(f, 0.0f, 0, false);
+            }
+        scales[(int64_t)b * C + c] = (uint8_t)E;
+    } else {
+        // columns 2c (low half of each word, low nibble) and 2c + 1
+        uint32_t a0 = 0, a1 = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            h[i] = i < nr ? *(const uint32_t *)(x + (r0 + i) * C + 2 * c) : 0u;
+            a0 = max(a0, h[i] & 0x7FFFu);
+            a1 = max(a1, (h[i] >> 16) & 0x7FFFu);
+        }
+        const uint32_t E0 = mx_scale_byte<2>(a0), E1 = mx_scale_byte<2>(a1);
+        const int e0 = 127 - (int)E0, e1 = 127 - (int)E1;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            if (i < nr) {
+                const float f0 =
+                    __builtin_fminf(__builtin_fmaxf(__builtin_ldexpf(bf16_to_f32(h[i] & 0xFFFFu), e0), -6.0f), 6.0f);
+                const float f1 =
+                    __builtin_fminf(__builtin_fmaxf(__builtin_ldexpf(bf16_to_f32(h[i] >> 16), e1), -6.0f), 6.0f);
+                const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f0, f1, 1.0f, 0);
+                q[(r0 + i) * (C / 2) + c] = (uint8_t)(w & 0xFFu);
+            }
+        *(uint16_t *)(scales + (int64_t)b * C + 2 * c) = (uint16_t)(E0 | (E1 << 8));
+    }
+}
+
+// Exact value of an E2M1 code (OCP MX: bias 1, one mantissa bit; exponent
+// field 0 holds the subnormals 0 and 0.5).
+__device__ __forceinline__ float e2m1_to_f32(uint32_t n)
+{
+    const uint32_t mag = n & 7u;
+    const float v =
+        mag < 2u ? 0.5f * (float)mag : __builtin_ldexpf(1.0f + 0.5f * (float)(mag & 1u), (int)(mag >> 1) - 1);
+    return (n & 8u) ? -v : v;
 }
 
 // MX codes blocked along tokens -> their exact values as bf16 (values below
 // bf16's smallest subnormal round to nearest even): one wave per row.
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void mx_tokens_dequant_kernel(const uint8_t *__restrict__ q,
                                                                      const uint8_t *__restrict__ scales,
                                                                      const int64_t *lens, const int64_t *offs, int G,
@@ -317,14 +355,22 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_dequant_kernel(const uint8
     for (int64_t c = lane * 8; c < C; c += 512) {
         uintx4 o = uintx4{0u, 0u, 0u, 0u};
         if (in) {
-            const uintx2 cw = *(const uintx2 *)(q + r * C + c);
             const uintx2 sw = *(const uintx2 *)(scales + b * C + c);
+            float f[8];
+            if (FMT == 0) {
+                const uintx2 cw = *(const uintx2 *)(q + r * C + c);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    f[e] = __builtin_amdgcn_cvt_f32_fp8((int)((cw[e >> 2] >> (8 * (e & 3))) & 0xFFu), 0);
+            } else {
+                const uint32_t cw = *(const uint32_t *)(q + r * (C / 2) + c / 2);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = e2m1_to_f32((cw >> (4 * e)) & 0xFu);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t code = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
                 const int E = (int)((sw[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-                const float v = __builtin_ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)code, 0), E - 127);
-                o[e >> 1] |= bf16_rne(v) << (16 * (e & 1));
+                o[e >> 1] |= bf16_rne(__builtin_ldexpf(f[e], E - 127)) << (16 * (e & 1));
             }
         }
         *(uintx4 *)(out + r * C + c) = o;
@@ -521,23 +567,33 @@ hipError_t launch_fp8_quantize_rows(const uint16_t *x, uint8_t *q, float *amax, 
 }
 
 hipError_t launch_mx_quantize_tokens(const uint16_t *x, const int64_t *lens, const int64_t *offs, int G, int64_t M,
-                                     int64_t C, uint8_t *q, uint8_t *scales, uint32_t *err, hipStream_t s)
+                                     int64_t C, int fmt, uint8_t *q, uint8_t *scales, uint32_t *err, hipStream_t s)
 {
     const int64_t nb = M / 32 + G;                 // scale rows an upper bound allows
-    if (nb == 0 || C == 0) return hipSuccess;
-    const dim3 grid((unsigned)nb, (unsigned)((C + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL(mx_tokens_quant_kernel, grid, dim3(kThreads), table_bytes(G), s, x, lens, offs, G, M, C, q,
-                       scales, err);
+    const int64_t nc = fmt == 0 ? C : C / 2;       // threads per scale row
+    if (nb == 0 || nc == 0) return hipSuccess;
+    const dim3 grid((unsigned)nb, (unsigned)((nc + kThreads - 1) / kThreads));
+    if (fmt == 0)
+        hipLaunchKernelGGL(mx_tokens_quant_kernel<0>, grid, dim3(kThreads), table_bytes(G), s, x, lens, offs, G, M, C,
+                           q, scales, err);
+    else
+        hipLaunchKernelGGL(mx_tokens_quant_kernel<1>, grid, dim3(kThreads), table_bytes(G), s, x, lens, offs, G, M, C,
+                           q, scales, err);
     return hipGetLastError();
 }
 
 hipError_t launch_mx_dequant_tokens(const uint8_t *q, const uint8_t *scales, const int64_t *lens,
-                                    const int64_t *offs, int G, int64_t M, int64_t C, uint16_t *out, hipStream_t s)
+                                    const int64_t *offs, int G, int64_t M, int64_t C, int fmt, uint16_t *out,
+                                    hipStream_t s)
 {
     if (M == 0 || C == 0) return hipSuccess;
     const dim3 grid((unsigned)((M + kThreads / 64 - 1) / (kThreads / 64)));
-    hipLaunchKernelGGL(mx_tokens_dequant_kernel, grid, dim3(kThreads), table_bytes(G), s, q, scales, lens, offs, G, M,
-                       C, out);
+    if (fmt == 0)
+        hipLaunchKernelGGL(mx_tokens_dequant_kernel<0>, grid, dim3(kThreads), table_bytes(G), s, q, scales, lens, offs,
+                           G, M, C, out);
+    else
+        hipLaunchKernelGGL(mx_tokens_dequant_kernel<1>, grid, dim3(kThreads), table_bytes(G), s, q, scales, lens, offs,
+                           G, M, C, out);
     return hipGetLastError();
 }
 

@@ -1,8 +1,8 @@
-"""GPU parity of the MXFP8 weight gradient: pt_mx_quantize_tokens bit-exact
-against the oracle (blocks of 32 tokens inside each expert, the last one
-partial), and pt_grouped_gemm_wgrad on those codes against the oracle's sum
-of exact products, accumulating into and overwriting main_grad, in both
-output layouts, through the C ABI."""
+"""GPU parity of the MX weight gradient (MXFP8 and MXFP4):
+pt_mx_quantize_tokens bit-exact against the oracle (blocks of 32 tokens
+inside each expert, the last one partial), and pt_grouped_gemm_wgrad on those
+codes against the oracle's sum of exact products, accumulating into and
+overwriting main_grad, in both output layouts, through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -14,60 +14,67 @@ from util import BF16_TOL, bits16, dev_i64, floored_rel_err, u8
 pytestmark = pytest.mark.gpu
 
 
-def quantize_tokens(dev, x, lens):
+FMTS = [ptm.PT_MXFP8_E4M3, ptm.PT_MXFP4_E2M1]
+FMT_IDS = ["e4m3", "e2m1"]
+
+
+def quantize_tokens(dev, x, lens, fmt=ptm.PT_MXFP8_E4M3):
     M, C = x.shape
     G = len(lens)
-    q = torch.full((M, C), 0xEE, dtype=torch.uint8, device=dev)
+    q = torch.full((M, C if fmt == ptm.PT_MXFP8_E4M3 else C // 2), 0xEE, dtype=torch.uint8, device=dev)
     s = torch.zeros((M // 32 + G, C), dtype=torch.uint8, device=dev)
-    ptm.pt_mx_quantize_tokens(x, dev_i64(lens, dev), None, q, s, G, M, C, ptm.PT_MXFP8_E4M3)
+    ptm.pt_mx_quantize_tokens(x, dev_i64(lens, dev), None, q, s, G, M, C, fmt)
     torch.cuda.synchronize()
     return q, s
 
 
+# the oracle numbers its encodings as the library does (1 = E4M3, 2 = E2M1)
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("lens,C", [([0, 70, 1, 0, 300, 129, 0], 136), ([32, 64, 33], 48), ([5], 8)],
                          ids=["ragged", "aligned_and_one_over", "tiny"])
-def test_quantize_tokens_bit_exact(orc, dev, lens, C):
+def test_quantize_tokens_bit_exact(orc, dev, lens, C, fmt):
     lens = np.array(lens, np.int64)
     M = int(lens.sum())
     x = synth.randn_bf16((M, C), seed=100, device=dev, outlier_frac=0.01, outlier_mult=50.0)
-    q, s = quantize_tokens(dev, x, lens)
-    rq, rs, nb = orc.mx_quantize_tokens(bits16(x), lens)
+    q, s = quantize_tokens(dev, x, lens, fmt)
+    rq, rs, nb = orc.mx_quantize_tokens(bits16(x), lens, fmt)
     assert (u8(q) == rq).all()
     assert (u8(s)[:nb] == rs[:nb]).all()
 
 
-def wgrad_mx(dev, aq, as_, dq, ds, lens, N, K, trans_out, accumulate, seed_mg=103):
+def wgrad_mx(dev, aq, as_, dq, ds, lens, N, K, trans_out, accumulate, fmt=ptm.PT_MXFP8_E4M3, seed_mg=103):
     M, G = aq.shape[0], len(lens)
     shape = (G, N, K) if trans_out else (G, K, N)
     g = torch.Generator(device=dev)
     g.manual_seed(seed_mg)
     mg = (torch.randn(shape, generator=g, device=dev) * 1e-3).float()
     before = mg.clone()
-    ws = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, ptm.PT_MXFP8_E4M3),),
+    ws = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, fmt),),
                      dtype=torch.uint8, device=dev)
-    ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, dev_i64(lens, dev), None, G, M, N, K, ptm.PT_MXFP8_E4M3,
+    ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, dev_i64(lens, dev), None, G, M, N, K, fmt,
                               trans_out, accumulate, workspace=ws)
     torch.cuda.synchronize()
     return before.cpu().numpy(), mg.cpu().numpy()
 
 
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
 @pytest.mark.parametrize("trans_out", [0, 1])
 @pytest.mark.parametrize("accumulate", [1, 0])
-def test_mx_wgrad_vs_oracle(orc, dev, trans_out, accumulate):
+def test_mx_wgrad_vs_oracle(orc, dev, trans_out, accumulate, fmt):
     lens = np.array([0, 70, 1, 0, 300, 129, 0], np.int64)
     K, N = 200, 136
     M, G = int(lens.sum()), len(lens)
-    print(f"mx wgrad trans_out={trans_out} acc={accumulate}", flush=True)
+    print(f"mx wgrad fmt={fmt} trans_out={trans_out} acc={accumulate}", flush=True)
     a = synth.randn_bf16((M, K), seed=101, std=K ** -0.5, device=dev)
     dy = synth.randn_bf16((M, N), seed=102, std=1e-2, device=dev)
-    aq, as_ = quantize_tokens(dev, a, lens)
-    dq, ds = quantize_tokens(dev, dy, lens)
-    raq, ras, _ = orc.mx_quantize_tokens(bits16(a), lens)
-    rdq, rds, nb = orc.mx_quantize_tokens(bits16(dy), lens)
+    aq, as_ = quantize_tokens(dev, a, lens, fmt)
+    dq, ds = quantize_tokens(dev, dy, lens, fmt)
+    raq, ras, _ = orc.mx_quantize_tokens(bits16(a), lens, fmt)
+    rdq, rds, nb = orc.mx_quantize_tokens(bits16(dy), lens, fmt)
     assert (u8(aq) == raq).all() and (u8(dq) == rdq).all()
-    before, after = wgrad_mx(dev, aq, as_, dq, ds, lens, N, K, trans_out, accumulate)
-    av = orc.mx_dequantize_tokens(raq, ras, lens)
-    dv = orc.mx_dequantize_tokens(rdq, rds, lens)
+    before, after = wgrad_mx(dev, aq, as_, dq, ds, lens, N, K, trans_out, accumulate, fmt)
+    av = orc.mx_dequantize_tokens(raq, ras, lens, fmt)
+    dv = orc.mx_dequantize_tokens(rdq, rds, lens, fmt)
     offs = synth.offsets(lens)
     for g in range(G):
         if lens[g] == 0:
@@ -96,10 +103,24 @@ def test_mx_wgrad_needs_its_workspace(dev):
     assert L.pt_grouped_gemm_wgrad(*args, None, 0, st) == 4
     assert L.pt_grouped_gemm_wgrad(*args, small.data_ptr(), 4096, st) == 4
     assert L.pt_grouped_gemm_wgrad(q.data_ptr(), s.data_ptr(), q.data_ptr(), s.data_ptr(), mg.data_ptr(),
-                                   lens.data_ptr(), None, 1, 40, 64, 64, ptm.PT_MXFP4_E2M1, 0, 1, None, 0, st) == 2
+                                   lens.data_ptr(), None, 1, 40, 64, 64, ptm.PT_MXFP4_E2M1, 0, 1, None, 0, st) == 4
+    # FP8 with tensor scales has no weight gradient here
+    assert L.pt_grouped_gemm_wgrad(q.data_ptr(), s.data_ptr(), q.data_ptr(), s.data_ptr(), mg.data_ptr(),
+                                   lens.data_ptr(), None, 1, 40, 64, 64, ptm.PT_FP8_E4M3, 0, 1, None, 0, st) == 2
 
 
-def test_mx_wgrad_full_shape_sampled(orc, dev):
+def element_values(orc, codes, fmt):
+    # exact values of a [rows, cols] (E4M3) or [rows, cols/2] (E2M1) code array
+    if fmt == ptm.PT_MXFP8_E4M3:
+        return np.array([orc.e4m3_value(c) for c in range(256)], np.float64)[codes]
+    table = np.array([orc.e2m1_value(c) for c in range(16)], np.float64)
+    out = np.empty(codes.shape[:-1] + (2 * codes.shape[-1],), np.float64)
+    out[..., 0::2], out[..., 1::2] = table[codes & 0xF], table[codes >> 4]
+    return out
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_mx_wgrad_full_shape_sampled(orc, dev, fmt):
     # The weight gradient at the headline's shape: 256 experts, 49152 tokens,
     # K = N = 4096, accumulated into a seeded fp32 main_grad; sampled
     # (expert, k) rows of the increment against the oracle.
@@ -108,8 +129,8 @@ def test_mx_wgrad_full_shape_sampled(orc, dev):
     offs = synth.offsets(lens)
     a = synth.randn_bf16((M, K), seed=101, std=K ** -0.5, device=dev)
     dy = synth.randn_bf16((M, N), seed=102, std=1e-2, device=dev)
-    aq, as_ = quantize_tokens(dev, a, lens)
-    dq, ds = quantize_tokens(dev, dy, lens)
+    aq, as_ = quantize_tokens(dev, a, lens, fmt)
+    dq, ds = quantize_tokens(dev, dy, lens, fmt)
     del a, dy
     gen = torch.Generator(device=dev)
     gen.manual_seed(103)
@@ -120,20 +141,19 @@ def test_mx_wgrad_full_shape_sampled(orc, dev):
     ks = rng.integers(0, K, size=gs.size)
     gi, ki = torch.as_tensor(gs, device=dev), torch.as_tensor(ks, device=dev)
     before = mg[gi, ki].cpu().numpy()
-    ws = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, ptm.PT_MXFP8_E4M3),),
+    ws = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, fmt),),
                      dtype=torch.uint8, device=dev)
-    ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, dev_i64(lens, dev), None, G, M, N, K, ptm.PT_MXFP8_E4M3, 0, 1,
+    ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, dev_i64(lens, dev), None, G, M, N, K, fmt, 0, 1,
                               workspace=ws)
     torch.cuda.synchronize()
     after = mg[gi, ki].cpu().numpy()
     del mg, ws
     aqn, asn, dqn, dsn = u8(aq), u8(as_), u8(dq), u8(ds)
-    table = np.array([orc.e4m3_value(c) for c in range(256)], np.float64)
     for i, (g, k) in enumerate(zip(gs, ks)):
         r0, r1 = offs[g], offs[g + 1]
         b0 = int(sum((int(l) + 31) // 32 for l in lens[:g]))
         blk = b0 + (np.arange(r1 - r0) // 32)
-        av = table[aqn[r0:r1, k]] * np.ldexp(1.0, asn[blk, k].astype(np.int64) - 127)
-        dv = table[dqn[r0:r1]] * np.ldexp(1.0, dsn[blk].astype(np.int64) - 127)
+        av = element_values(orc, aqn[r0:r1], fmt)[:, k] * np.ldexp(1.0, asn[blk, k].astype(np.int64) - 127)
+        dv = element_values(orc, dqn[r0:r1], fmt) * np.ldexp(1.0, dsn[blk].astype(np.int64) - 127)
         D = av @ dv                                                     # [N], binary64
         assert floored_rel_err(after[i].astype(np.float64) - before[i], D) <= BF16_TOL, (g, k)
