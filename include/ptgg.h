@@ -153,8 +153,16 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale,
  *  [G, K, N] codes with b_scale [G, K, N/32] (pt_mx_quantize_t of a [G, N, K]
  *  weight, or pt_mx_quantize of a [G, K, N] one), so trans_b must be 0;
  *  the products are exact and the sums fp32, as in the MX forward.
+ *  FP8 (PT_FP8_E4M3): dy [M, N] codes with its one fp32 factor
+ *  (pt_fp8_quantize of dY, batch 1) as dy_scale; b the transposed weight
+ *  [G, K, N] as E4M3 codes with one fp32 factor per expert (pt_fp8_quantize,
+ *  batch G, of the transposed weight, whose amax is the forward weight's) as
+ *  b_scale.  PT_FP8_E4M3_ROWWISE: factors per row of dY [M] and per row of
+ *  the transposed weight [G, K] (pt_fp8_quantize_rows), i.e. per output row
+ *  and per output column.  dX = factors times the exact code products
+ *  summed in fp32, as in the FP8 forward.
  *  Requirements: N % 32 == 0, K % 8 == 0; scales 4-byte aligned.
- *  dx  [M, K] bf16 in both cases.
+ *  dx  [M, K] bf16 in every case.
  */
 int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale,
                           const void *b, const uint8_t *b_scale, void *dx,

@@ -220,10 +220,12 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
     if (N < 1 || K < 1 || N > INT32_MAX / 4 || K > INT32_MAX / 4) return PT_ERR_INVALID_ARG;
     if (M > 0 && (!dy || !b || !dx)) return PT_ERR_INVALID_ARG;
     if (trans_b != 0 && trans_b != 1) return PT_ERR_INVALID_ARG;
-    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) {
+    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE) {
         // dY packed and scaled along N, and the weight's transposed copy
         // [G, K, N], packed and scaled along N (pt_mx_quantize_t): the MX
-        // grouped GEMM with K outputs per row and a reduction over N
+        // grouped GEMM with K outputs per row and a reduction over N.  FP8:
+        // one factor for dY and one per expert's transposed weight, or one
+        // per row of each (per output row and per output column)
         if (trans_b) return PT_ERR_UNSUPPORTED;
         if (!aligned16(dy) || !aligned16(b) || !aligned16(dx)) return PT_ERR_MISALIGNED;
         if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
