@@ -351,6 +351,56 @@ def bench_cfg3_fp8(dev, stream, iters):
     return d, r
 
 
+def bench_cfg3_fp8_dgrad(dev, stream, iters):
+    """The MXFP8 workload's data gradient in FP8 with tensor factors and with
+    row factors: dY [65536, 5760] quantised inside the step, the transposed
+    weight cache [32, 2880, 5760] (pt_stack_experts, then the FP8 quantiser)
+    built once outside it."""
+    lens = synth.lens_zipf_distinct(16384, 32, 4, 1.1, seed=3)
+    G, M, K, N = 32, int(lens.sum()), 2880, 5760
+    lens_d = torch.as_tensor(lens, device=dev)
+    w = synth.randn_bf16((G, N, K), seed=104 + 1000, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    addr = torch.tensor([w.data_ptr() + g * N * K * 2 for g in range(G)], dtype=torch.int64, device=dev)
+    wt = torch.empty((G, K, N), dtype=torch.bfloat16, device=dev)
+    ptm.pt_stack_experts(addr, wt, G, N, K, 1, stream=stream)
+    del w
+    wq = torch.empty((G, K, N), dtype=torch.uint8, device=dev)
+    wamax, wd = torch.empty((G,), dtype=torch.float32, device=dev), torch.empty((G,), dtype=torch.float32, device=dev)
+    ptm.pt_fp8_quantize(wt, wq, wamax, wd, G, K, N, stream=stream)
+    wq_r = torch.empty((G, K, N), dtype=torch.uint8, device=dev)
+    wamax_r = torch.empty((G * K,), dtype=torch.float32, device=dev)
+    wd_r = torch.empty((G * K,), dtype=torch.float32, device=dev)
+    ptm.pt_fp8_quantize_rows(wt, wq_r, wamax_r, wd_r, G * K, N, stream=stream)
+    del wt
+    dy = synth.randn_bf16((M, N), seed=106, std=1e-2, device=dev)
+    dq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    damax, dd = torch.empty((1,), dtype=torch.float32, device=dev), torch.empty((1,), dtype=torch.float32, device=dev)
+    damax_r, dd_r = (torch.empty((M,), dtype=torch.float32, device=dev),
+                     torch.empty((M,), dtype=torch.float32, device=dev))
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        ptm.pt_fp8_quantize(dy, dq, damax, dd, 1, M, N, stream=stream)
+        ptm.pt_grouped_gemm_dgrad(dq, dd, wq, wd, dx, lens_d, None, G, M, N, K, ptm.PT_FP8_E4M3, 0,
+                                  workspace=WS[0], stream=stream)
+
+    def step_rows():
+        ptm.pt_fp8_quantize_rows(dy, dq, damax_r, dd_r, M, N, stream=stream)
+        ptm.pt_grouped_gemm_dgrad(dq, dd_r, wq_r, wd_r, dx, lens_d, None, G, M, N, K, ptm.PT_FP8_E4M3_ROWWISE, 0,
+                                  workspace=WS[0], stream=stream)
+    _, per = time_launches(step, iters, 3, stream)
+    _, per_r = time_launches(step_rows, iters, 3, stream)
+    flops = 2.0 * M * K * N
+    nbytes = bytes_weights(lens, N * K) + M * N * 2 * 2 + M * N * 2 + M * K * 2
+    d = summary("FP8 dgrad with tensor factors (two-pass dY quantise + grouped GEMM on the transposed FP8 weight "
+                "cache), 32 experts, M=65536, N=5760 -> K=2880", "fp8", flops, nbytes, per)
+    r = summary("FP8 dgrad with row factors (one-pass dY quantise + grouped GEMM), 32 experts, M=65536, "
+                "N=5760 -> K=2880", "fp8", flops, nbytes - M * N * 2, per_r)
+    del dy, dq, dx, wq, wq_r
+    torch.cuda.empty_cache()
+    return d, r
+
+
 def bench_cfg4(dev, stream, iters, lens):
     G, M, H, I = 256, int(lens.sum()), 4096, 2048
     x = synth.randn_bf16((M, H), seed=105, device=dev)
@@ -572,6 +622,9 @@ def main():
             log("per_config: FP8 with tensor scales")
             per["cfg3_fp8_tensor_fwd"], per["cfg3_fp8_rowwise_fwd"] = bench_cfg3_fp8(dev, stream, iters)
             torch.cuda.empty_cache()
+        if want is None or "cfg3fp8dgrad" in want:
+            log("per_config: FP8 dgrad")
+            per["cfg3_fp8_tensor_dgrad"], per["cfg3_fp8_rowwise_dgrad"] = bench_cfg3_fp8_dgrad(dev, stream, iters)
         if want is None or "cfg3dgrad" in want:
             log("per_config: MXFP8 dgrad")
             per["cfg3_mxfp8_dgrad"] = bench_cfg3_dgrad(dev, stream, iters)
