@@ -307,6 +307,17 @@ def wgrad_rows(a, dy, group_lens, N, K, gs, ks):
     return out
 
 
+def fp8_wgrad_rows(a_q, a_dequant, dy_q, dy_dequant, group_lens, N, K, gs, ks):
+    """Unrounded D_g[k, :] for E4M3 codes with one factor per tensor: the
+    exact code products summed over expert g's rows (wgrad_rows on the codes'
+    values, which every bf16 holds exactly), times a_dequant * dy_dequant."""
+    table = np.array([e4m3_value(c) for c in range(256)], np.float64)
+    a_bits = round_bf16(table[_c(a_q, np.uint8)])
+    dy_bits = round_bf16(table[_c(dy_q, np.uint8)])
+    d = wgrad_rows(a_bits, dy_bits, group_lens, N, K, gs, ks)
+    return d * (float(np.float64(a_dequant)) * float(np.float64(dy_dequant)))
+
+
 # ------------------------------------------------------------------ composed ops
 def grouped_fwd(dtype, a, a_scale, b, b_scale, group_lens, N, K, trans_b, epilogue, rows):
     """Forward with its epilogue, for the listed rows.

@@ -343,6 +343,28 @@ def test_fp8_fwd_rows_matches_dense_on_decoded_codes(orc):
         assert np.allclose(got[i], ref, rtol=1e-14, atol=0), r
 
 
+def test_fp8_wgrad_rows_matches_dense_on_torch_decoded_codes(orc):
+    # per expert: factors times (decoded A_g)^T (decoded dY_g), the codes
+    # decoded by torch's float8_e4m3fn, the product by numpy
+    lens = np.array([5, 0, 40, 17])
+    M, K, N = int(lens.sum()), 24, 16
+    rng = np.random.default_rng(70)
+    aq = rng.integers(0, 256, size=(M, K)).astype(np.uint8)
+    dq = rng.integers(0, 256, size=(M, N)).astype(np.uint8)
+    aq[(aq & 0x7F) == 0x7F] = 0x38
+    dq[(dq & 0x7F) == 0x7F] = 0xB8
+    da, dd = np.float32(0.0123), np.float32(3.5e-4)
+    G = lens.size
+    gs, ks = np.repeat(np.arange(G), K), np.tile(np.arange(K), G)
+    got = orc.fp8_wgrad_rows(aq, da, dq, dd, lens, N, K, gs, ks).reshape(G, K, N)
+    av = torch.from_numpy(aq).view(torch.float8_e4m3fn).double().numpy()
+    dv = torch.from_numpy(dq).view(torch.float8_e4m3fn).double().numpy()
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    for g in range(G):
+        want = (av[offs[g]:offs[g + 1]].T @ dv[offs[g]:offs[g + 1]]) * (float(da) * float(dd))
+        assert np.allclose(got[g], want, rtol=1e-13, atol=0), g
+
+
 def test_fp8_rowwise_scales_each_row_on_its_own(orc):
     # rows of very different magnitude: each row's codes are torch's cast of
     # fp32(x * 448 / amax_row), independent of the other rows
