@@ -504,9 +504,27 @@ def bench_cfg3_wgrad(dev, stream, iters):
                 "32 experts, M=65536, K=2880, N=5760", "mxfp8", flops, nbytes, per,
                 {"quantize_tokens_ms_median": round(float(np.median(per_q)), 4),
                  "wgrad_only_ms_median": round(float(np.median(per_g)), 4)})
-    del a, dy, aq, as_, dq, ds, mg, ws
+    del as_, ds, ws
     torch.cuda.empty_cache()
-    return w
+    # FP8 with one factor per tensor: two-pass quantise of A and dY, then the
+    # weight gradient (decode, BF16 sums into the workspace, fused main_grad update)
+    fa, ma = torch.empty((1,), dtype=torch.float32, device=dev), torch.empty((1,), dtype=torch.float32, device=dev)
+    fd, md = torch.empty((1,), dtype=torch.float32, device=dev), torch.empty((1,), dtype=torch.float32, device=dev)
+    ws8 = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, ptm.PT_FP8_E4M3),),
+                      dtype=torch.uint8, device=dev)
+
+    def step8():
+        ptm.pt_fp8_quantize(a, aq, ma, fa, 1, M, K, stream=stream)
+        ptm.pt_fp8_quantize(dy, dq, md, fd, 1, M, N, stream=stream)
+        ptm.pt_grouped_gemm_wgrad(aq, fa, dq, fd, mg, lens_d, None, G, M, N, K, ptm.PT_FP8_E4M3, 0, 1,
+                                  workspace=ws8, stream=stream)
+    _, per8 = time_launches(step8, iters, 3, stream)
+    nbytes8 = M * K * 2 * 2 + M * N * 2 * 2 + 2 * (M * K + M * N) + bytes_weights(lens, K * N * 4 * 2)
+    w8 = summary("FP8 wgrad with tensor factors (two-pass quantise of A and dY + weight gradient into fp32 "
+                 "main_grad), 32 experts, M=65536, K=2880, N=5760", "fp8", flops, nbytes8, per8)
+    del a, dy, aq, dq, mg, ws8
+    torch.cuda.empty_cache()
+    return w, w8
 
 
 def bench_stack(dev, stream, iters):
@@ -631,7 +649,7 @@ def main():
             torch.cuda.empty_cache()
         if want is None or "cfg3wgrad" in want:
             log("per_config: MXFP8 wgrad")
-            per["cfg3_mxfp8_wgrad"] = bench_cfg3_wgrad(dev, stream, iters)
+            per["cfg3_mxfp8_wgrad"], per["cfg3_fp8_tensor_wgrad"] = bench_cfg3_wgrad(dev, stream, iters)
             torch.cuda.empty_cache()
         if want is None or "stack" in want:
             log("per_config: expert weight stack")

@@ -219,8 +219,16 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_sa
  *  even).  The workspace is required and holds bf16 copies of both
  *  operands: pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ..., dtype) bytes,
  *  else PT_ERR_WORKSPACE.
- *  Requirements: K % 8 == 0, N % 8 == 0; dtype PT_BF16, PT_MXFP8_E4M3 or
- *  PT_MXFP4_E2M1.
+ *  PT_FP8_E4M3: a [M, K] and dy [M, N] E4M3 codes with one fp32 factor
+ *  each (a_scale, dy_scale: pt_fp8_quantize, batch 1);
+ *      main_grad[g] = (accumulate ? main_grad[g] : 0) + fp32(d_a * d_dy) * S_g
+ *  with S_g the fp32 sum of the exact code products, one fused multiply-add
+ *  per element.  The workspace is required: bf16 copies of both operands
+ *  and the fp32 sums [G, K, N], pt_grouped_gemm_workspace_size(PT_OP_WGRAD,
+ *  ..., PT_FP8_E4M3) bytes.  (Row factors vary along the reduction, so
+ *  PT_FP8_E4M3_ROWWISE has no weight gradient: PT_ERR_UNSUPPORTED.)
+ *  Requirements: K % 8 == 0, N % 8 == 0; dtype PT_BF16, PT_MXFP8_E4M3,
+ *  PT_MXFP4_E2M1 or PT_FP8_E4M3.
  */
 int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
                           const void *dy, const uint8_t *dy_scale,

@@ -337,6 +337,32 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
         return pt_grouped_gemm_wgrad(wa, nullptr, wd, nullptr, main_grad, group_lens, group_offs, G, M, N, K, PT_BF16,
                                      trans_out, accumulate, workspace, workspace_bytes, stream);
     }
+    if (dtype == PT_FP8_E4M3) {
+        // one factor per tensor: the codes' values (exact in bf16) go to the
+        // BF16 weight gradient, whose fp32 sums land in the workspace; then
+        // main_grad (+)= d_a * d_dy * sum, one fused multiply-add each
+        if (M == 0) return pt_grouped_gemm_wgrad(nullptr, nullptr, nullptr, nullptr, main_grad, group_lens, group_offs,
+                                                 G, M, N, K, PT_BF16, trans_out, accumulate, workspace,
+                                                 workspace_bytes, stream);
+        if (!a_scale || !dy_scale) return PT_ERR_INVALID_ARG;
+        if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad) || !aligned4(a_scale) || !aligned4(dy_scale))
+            return PT_ERR_MISALIGNED;
+        if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+        const size_t need =
+            (size_t)(kQueueWsBytes + round256(M * K * 2) + round256(M * N * 2) + round256(G * K * N * 4));
+        if (!workspace || workspace_bytes < need) return PT_ERR_WORKSPACE;
+        uint16_t *wa = (uint16_t *)((uint8_t *)workspace + kQueueWsBytes);
+        uint16_t *wd = (uint16_t *)((uint8_t *)wa + round256(M * K * 2));
+        float *sum = (float *)((uint8_t *)wd + round256(M * N * 2));
+        hipError_t e = launch_fp8_decode((const uint8_t *)a, wa, M * K, s);
+        if (e == hipSuccess) e = launch_fp8_decode((const uint8_t *)dy, wd, M * N, s);
+        if (e != hipSuccess) return PT_ERR_HIP;
+        st = pt_grouped_gemm_wgrad(wa, nullptr, wd, nullptr, sum, group_lens, group_offs, G, M, N, K, PT_BF16,
+                                   trans_out, 0, workspace, workspace_bytes, stream);
+        if (st) return st;
+        return hip_status(launch_fp8_wgrad_axpy(main_grad, sum, group_lens, (const float *)a_scale,
+                                                (const float *)dy_scale, (int)G, K * N, accumulate, s));
+    }
     if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
     if (a_scale || dy_scale) return PT_ERR_INVALID_ARG;
     if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad)) return PT_ERR_MISALIGNED;
@@ -486,6 +512,9 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, i
     // the MXFP8 weight gradient: bf16 copies of both operands
     if (op == PT_OP_WGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && M >= 0 && N > 0 && K > 0)
         return (size_t)(kQueueWsBytes + round256(M * K * 2) + round256(M * N * 2));
+    // FP8 with tensor factors: bf16 copies of both operands and fp32 sums
+    if (op == PT_OP_WGRAD && dtype == PT_FP8_E4M3 && G > 0 && M >= 0 && N > 0 && K > 0)
+        return (size_t)(kQueueWsBytes + round256(M * K * 2) + round256(M * N * 2) + round256(G * K * N * 4));
     // the MX data gradient: K outputs per row, a reduction over N
     if (op == PT_OP_DGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && G > 0 && M >= 0 && N > 0 &&
         K > 0 && N % 32 == 0) {

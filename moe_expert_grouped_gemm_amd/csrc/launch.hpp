@@ -103,6 +103,13 @@ hipError_t launch_fp8_quantize(const uint16_t *x, uint8_t *q, float *amax, float
 // The same with one scale per row of x [rows, cols].
 hipError_t launch_fp8_quantize_rows(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t rows,
                                     int64_t cols, hipStream_t s);
+// FP8 weight gradient with tensor factors: E4M3 codes -> their bf16 values
+// (n % 8 == 0), and main_grad[g] (+)= fa[0] * fd[0] * sum[g] over G slices
+// of P fp32 values (P % 4 == 0; experts with lens <= 0 skipped when
+// accumulating).
+hipError_t launch_fp8_decode(const uint8_t *q, uint16_t *out, int64_t n, hipStream_t s);
+hipError_t launch_fp8_wgrad_axpy(float *main_grad, const float *sum, const int64_t *lens, const float *fa,
+                                 const float *fd, int G, int64_t P, int accumulate, hipStream_t s);
 // MX along tokens within each expert (blocks of 32 rows, the last
 // partial), codes E4M3 [M, C] / E2M1 [M, C/2] (fmt 0 / 1) and scales
 // [M / 32 + G, C]; and the exact bf16 values of such codes (the MX weight
