@@ -206,9 +206,21 @@ def bench_cfg0(dev, stream, iters):
     _, per = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
         a, None, b, None, out, None, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, ptm.PT_EPI_NONE,
         workspace=WS[0], stream=stream), iters, 10, stream)
+    # with tuning on: the first call times the configurations, the rest use the choice
+    ptm.pt_clear_gemm_tuning()
+    ptm.pt_set_gemm_config(ptm.PT_CONFIG_TUNE)
+    try:
+        _, per_t = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
+            a, None, b, None, out, None, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, ptm.PT_EPI_NONE,
+            workspace=WS[0], stream=stream), iters, 10, stream)
+        chosen = ptm.pt_gemm_config_of(ptm.PT_OP_FWD, ptm.PT_BF16, ptm.PT_EPI_NONE, 0, G, M, N, K)
+    finally:
+        ptm.pt_set_gemm_config(ptm.PT_CONFIG_RULES)
+        ptm.pt_clear_gemm_tuning()
     flops = 2.0 * M * K * N
     nbytes = bytes_weights(lens, K * N * 2) + M * K * 2 + M * N * 2
-    return summary("tiny BF16 fwd, 4 experts, M=256, K=128, N=256", "bf16", flops, nbytes, per)
+    return summary("tiny BF16 fwd, 4 experts, M=256, K=128, N=256", "bf16", flops, nbytes, per,
+                   {"tuned_config": chosen, "tuned_ms_median": round(float(np.median(per_t)), 4)})
 
 
 def bench_cfg2(dev, stream, iters, fc1):

@@ -87,7 +87,8 @@ typedef enum {
 typedef enum {
     PT_OP_FWD = 0,
     PT_OP_DGRAD = 1,
-    PT_OP_WGRAD = 2
+    PT_OP_WGRAD = 2,
+    PT_OP_DGRAD_SWIGLU = 3   /* pt_grouped_gemm_dgrad_swiglu (for pt_gemm_config_of) */
 } pt_op;
 
 /* Largest expert count one call accepts. */
@@ -385,6 +386,41 @@ int pt_mx_quantize_experts(const void *const *experts, void *q, uint8_t *scales,
 /* Bytes of workspace `op` needs for these sizes. */
 size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N,
                                       int64_t K, int dtype);
+
+/*
+ * Kernel configurations and tuning (the Primus-Turbo README, "What's New":
+ * grouped GEMM autotune).  A configuration of one grouped GEMM call is a
+ * number 0..3: bit 0 takes tiles in the static order even when the
+ * workspace holds tile queues, bit 1 runs the 128 x 256 kernel instead of
+ * the 256 x 256 one (BF16 and MX only; FP8 with tensor or row factors and the
+ * SwiGLU backward have no 128 x 256 kernel, and a bit that does not apply is
+ * dropped).  Every configuration computes the same sums in the same order:
+ * results are bit-identical, only speed differs.
+ * pt_set_gemm_config sets the process-wide mode and returns the previous one
+ * (-3 for an unknown mode):
+ *   PT_CONFIG_RULES  configuration 0 (the default);
+ *   PT_CONFIG_TUNE   the first call of each problem class -- (device, op,
+ *                    dtype, epilogue, layout, G, N, K, and M rounded up to a
+ *                    power of two) -- times every configuration that applies
+ *                    on the call's own buffers (one warm-up and three timed
+ *                    launches each, then a stream synchronisation) and
+ *                    keeps the fastest; later calls of the class use it.
+ *                    The call's outputs come from the chosen configuration.
+ *                    A call that must not run twice (a weight gradient that
+ *                    accumulates) or a stream under graph capture is not
+ *                    timed: it uses its class's choice if there is one,
+ *                    else configuration 0;
+ *   0..3             that configuration for every call.
+ * pt_gemm_config_of returns the tuned configuration of a problem class (the
+ * arguments of the entry point; op PT_OP_DGRAD_SWIGLU for the SwiGLU
+ * backward), or -1 if it has none.  pt_clear_gemm_tuning forgets every
+ * tuned class.  The table holds 512 classes; later ones use configuration 0.
+ */
+#define PT_CONFIG_RULES (-1)
+#define PT_CONFIG_TUNE (-2)
+int pt_set_gemm_config(int config);
+int pt_gemm_config_of(int op, int dtype, int epilogue, int trans, int64_t G, int64_t M, int64_t N, int64_t K);
+void pt_clear_gemm_tuning(void);
 
 /*
  * Sticky device error bits recorded in the first word of a workspace by the

@@ -26,17 +26,21 @@ __all__ = [
     "pt_grouped_gemm_wgrad",
     "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts", "expert_addresses",
+    "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning", "PT_CONFIG_RULES", "PT_CONFIG_TUNE",
+    "PT_OP_DGRAD_SWIGLU",
     "pt_grouped_gemm_workspace_size", "pt_read_error_flags", "pt_status_string", "pt_version",
 ]
 
 PT_BF16, PT_MXFP8_E4M3, PT_MXFP4_E2M1, PT_FP8_E4M3, PT_FP8_E4M3_ROWWISE = 0, 1, 2, 3, 4
 PT_EPI_NONE, PT_EPI_SWIGLU, PT_EPI_SWIGLU_MXFP4 = 0, 1, 2
-PT_OP_FWD, PT_OP_DGRAD, PT_OP_WGRAD = 0, 1, 2
+PT_OP_FWD, PT_OP_DGRAD, PT_OP_WGRAD, PT_OP_DGRAD_SWIGLU = 0, 1, 2, 3
+PT_CONFIG_RULES, PT_CONFIG_TUNE = -1, -2
 
 EXPORTS = (
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",
     "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts",
+    "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning",
     "pt_grouped_gemm_workspace_size", "pt_read_error_flags", "pt_status_string", "pt_version",
 )
 
@@ -87,6 +91,12 @@ def load(require_gpu: bool = True):
     L.pt_stack_experts.argtypes = [p, p, i64, i64, i64, i32, p, sz, p]
     L.pt_mx_quantize_experts.restype = i32
     L.pt_mx_quantize_experts.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p, sz, p]
+    L.pt_set_gemm_config.restype = i32
+    L.pt_set_gemm_config.argtypes = [i32]
+    L.pt_gemm_config_of.restype = i32
+    L.pt_gemm_config_of.argtypes = [i32, i32, i32, i32, i64, i64, i64, i64]
+    L.pt_clear_gemm_tuning.restype = None
+    L.pt_clear_gemm_tuning.argtypes = []
     L.pt_grouped_gemm_workspace_size.argtypes = [i32, i64, i64, i64, i64, i32]
     L.pt_read_error_flags.restype = i32
     L.pt_read_error_flags.argtypes = [p, p, ctypes.POINTER(ctypes.c_uint32)]
@@ -214,6 +224,21 @@ def pt_mx_quantize_experts(experts, q, scales, q_t, scales_t, G, rows, cols, dty
     _check("pt_mx_quantize_experts", L.pt_mx_quantize_experts(
         _ptr(experts), _ptr(q), _ptr(scales), _ptr(q_t), _ptr(scales_t), G, rows, cols, dtype,
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def pt_set_gemm_config(config) -> int:
+    prev = load(require_gpu=False).pt_set_gemm_config(config)
+    if prev == -3:
+        raise ValueError(f"unknown GEMM configuration mode {config}")
+    return int(prev)
+
+
+def pt_gemm_config_of(op, dtype, epilogue, trans, G, M, N, K) -> int:
+    return int(load(require_gpu=False).pt_gemm_config_of(op, dtype, epilogue, trans, G, M, N, K))
+
+
+def pt_clear_gemm_tuning() -> None:
+    load(require_gpu=False).pt_clear_gemm_tuning()
 
 
 def pt_grouped_gemm_workspace_size(op, G, M, N, K, dtype) -> int:

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "../../include/ptgg.h"
@@ -90,6 +91,127 @@ hipError_t queued(uint32_t *sched, hipStream_t s, Launch launch)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PT_OK : PT_ERR_HIP; }
 
+// ---------------------------------------------------------------- kernel configurations and tuning
+// A configuration of one grouped GEMM call: bit 0 takes tiles in the static
+// order even when the workspace holds queues, bit 1 runs the 128 x 256
+// kernel.  Every configuration computes the same sums in the same order, so
+// results are bit-identical; only speed differs.  The mode is process-wide:
+// fixed rules (configuration 0), a forced configuration, or tuning, where
+// the first call of each problem class times every configuration that
+// applies on the call's own buffers and keeps the fastest.
+constexpr int kCfgStatic = 1, kCfgNarrow = 2, kNumCfg = 4;
+constexpr int kTuneSlots = 512;
+std::atomic<int> g_mode{PT_CONFIG_RULES};
+
+struct TuneKey {
+    int dev, op, dtype, epi, trans;
+    int64_t G, Mb, N, K;
+    bool operator==(const TuneKey &o) const
+    {
+        return dev == o.dev && op == o.op && dtype == o.dtype && epi == o.epi && trans == o.trans && G == o.G &&
+               Mb == o.Mb && N == o.N && K == o.K;
+    }
+};
+struct TuneEntry {
+    TuneKey key;
+    int cfg;
+};
+std::mutex g_tune_mu;
+TuneEntry g_tune[kTuneSlots];
+int g_ntune = 0;
+
+// Problem class: the row count enters rounded up to a power of two.
+TuneKey tune_key(int op, int dtype, int epi, int trans, int64_t G, int64_t M, int64_t N, int64_t K)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    int64_t mb = 1;
+    while (mb < M) mb <<= 1;
+    return TuneKey{dev, op, dtype, epi, trans, G, mb, N, K};
+}
+
+int tune_lookup(const TuneKey &k)
+{
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    for (int i = 0; i < g_ntune; ++i)
+        if (g_tune[i].key == k) return g_tune[i].cfg;
+    return -1;
+}
+
+void tune_store(const TuneKey &k, int cfg)
+{
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    for (int i = 0; i < g_ntune; ++i)
+        if (g_tune[i].key == k) {
+            g_tune[i].cfg = cfg;
+            return;
+        }
+    if (g_ntune < kTuneSlots) g_tune[g_ntune++] = TuneEntry{k, cfg};
+}
+
+// The applicable configuration nearest to c (dropping what does not apply).
+int clamp_cfg(int c, unsigned allowed)
+{
+    if ((allowed >> c) & 1u) return c;
+    if ((allowed >> (c & ~kCfgNarrow)) & 1u) return c & ~kCfgNarrow;
+    if ((allowed >> (c & ~kCfgStatic)) & 1u) return c & ~kCfgStatic;
+    return 0;
+}
+
+// Configurations that apply: the static order only differs when the
+// workspace holds queues, the narrow kernel only where one exists.
+unsigned cfg_mask(bool queues, bool narrow_ok)
+{
+    unsigned m = 0;
+    for (int c = 0; c < kNumCfg; ++c)
+        if ((queues || !(c & kCfgStatic)) && (narrow_ok || !(c & kCfgNarrow))) m |= 1u << c;
+    return m;
+}
+
+// Launch through run(cfg) under the current mode.  A call that must not run
+// twice (an accumulating weight gradient) is never timed: it takes a tuned
+// choice if its class has one, else the rules.
+template <class Run>
+int configured(const TuneKey &key, unsigned allowed, bool repeatable, hipStream_t s, Run run)
+{
+    const int mode = g_mode.load(std::memory_order_relaxed);
+    if (mode >= 0) return hip_status(run(clamp_cfg(mode, allowed)));
+    if (mode == PT_CONFIG_RULES) return hip_status(run(0));
+    const int known = tune_lookup(key);
+    if (known >= 0) return hip_status(run(clamp_cfg(known, allowed)));
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (!repeatable || hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+        return hip_status(run(0));
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return PT_ERR_HIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return PT_ERR_HIP;
+    }
+    int best = -1;
+    float best_ms = 0.0f;
+    hipError_t e = hipSuccess;
+    for (int c = 0; c < kNumCfg && e == hipSuccess; ++c) {
+        if (!((allowed >> c) & 1u)) continue;
+        e = run(c);                                       // warm-up (and first-use set-up)
+        if (e == hipSuccess) e = hipEventRecord(e0, s);
+        for (int i = 0; i < 3 && e == hipSuccess; ++i) e = run(c);
+        if (e == hipSuccess) e = hipEventRecord(e1, s);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+        if (e == hipSuccess && (best < 0 || ms < best_ms)) {
+            best = c;
+            best_ms = ms;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (e != hipSuccess || best < 0) return PT_ERR_HIP;
+    tune_store(key, best);
+    return hip_status(run(best));                         // the output comes from the choice
+}
+
 }  // namespace
 }  // namespace ptgg
 
@@ -101,7 +223,7 @@ using namespace ptgg;
 // row stride ldo).  Shared by the forward and the MX data gradient.
 // PT_FP8_E4M3 takes the same path with one fp32 scale for A (a_scale) and
 // one per expert for B (b_scale) in place of the E8M0 block scales.
-static int mx_gemm(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale, void *out,
+static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale, void *out,
                    uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
                    int64_t N, int64_t K, int dtype, int ep, int64_t Nc, int64_t ldo, void *workspace,
                    size_t workspace_bytes, hipStream_t s)
@@ -140,17 +262,27 @@ static int mx_gemm(const void *a, const uint8_t *a_scale, const void *b, const u
     if (M == 0) return PT_OK;
     const int fmt = dtype == PT_MXFP4_E2M1 ? 1 : 0;
     // a workspace with room for them gets stage-major copies of the scales
-    if (!tensor_scales && p.sched && mx_swz_possible(G, M, N, K, fmt) &&
-        workspace_bytes >= (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) + mx_swz_b_bytes(G, N, K, fmt))) {
-        uint32_t *sa = (uint32_t *)((uint8_t *)workspace + kQueueWsBytes);
-        uint32_t *sb = (uint32_t *)((uint8_t *)sa + mx_swz_a_bytes(M, K, fmt));
-        hipError_t e = launch_mx_scale_swizzle(a_scale, M, K, fmt, sa, s);
-        if (e == hipSuccess) e = launch_mx_scale_swizzle(b_scale, G * N, K, fmt, sb, s);
-        if (e != hipSuccess) return PT_ERR_HIP;
-        p.sa = sa;
-        p.sb = sb;
-    }
-    return hip_status(queued(p.sched, s, [&] { return launch_mx(p, fmt, ep, s); }));
+    // (read by the 256 x 256 kernel; the 128 x 256 one reads them row-major)
+    const bool swz = !tensor_scales && p.sched && mx_swz_possible(G, M, N, K, fmt) &&
+                     workspace_bytes >= (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) +
+                                                 mx_swz_b_bytes(G, N, K, fmt));
+    uint32_t *queues = p.sched;
+    const TuneKey key = tune_key(op, dtype, ep, 0, G, M, N, K);
+    return configured(key, cfg_mask(queues != nullptr, !tensor_scales), true, s, [&](int cfg) {
+        p.narrow = (cfg & kCfgNarrow) != 0;
+        p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+        p.sa = p.sb = nullptr;
+        if (swz && !p.narrow) {
+            uint32_t *sa = (uint32_t *)((uint8_t *)workspace + kQueueWsBytes);
+            uint32_t *sb = (uint32_t *)((uint8_t *)sa + mx_swz_a_bytes(M, K, fmt));
+            hipError_t e = launch_mx_scale_swizzle(a_scale, M, K, fmt, sa, s);
+            if (e == hipSuccess) e = launch_mx_scale_swizzle(b_scale, G * N, K, fmt, sb, s);
+            if (e != hipSuccess) return e;
+            p.sa = sa;
+            p.sb = sb;
+        }
+        return queued(p.sched, s, [&] { return launch_mx(p, fmt, ep, s); });
+    });
 }
 
 extern "C" {
@@ -201,12 +333,18 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
                          (epilogue == PT_EPI_NONE ? bf16_tile_n() : bf16_tile_n() / 2));
         p.sched = queue_words(workspace, workspace_bytes);
         if (M == 0) return PT_OK;
-        return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdKContig : kFwdNContig, ep, s); }));
+        uint32_t *queues = p.sched;
+        const TuneKey key = tune_key(PT_OP_FWD, dtype, ep, trans_b, G, M, N, K);
+        return configured(key, cfg_mask(queues != nullptr, true), true, s, [&](int cfg) {
+            p.narrow = (cfg & kCfgNarrow) != 0;
+            p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+            return queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdKContig : kFwdNContig, ep, s); });
+        });
     }
     if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE) {
         if (!trans_b) return PT_ERR_UNSUPPORTED;           // K-contiguous codes
-        return mx_gemm(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype, ep, Nc,
-                       ldo, workspace, workspace_bytes, s);
+        return mx_gemm(PT_OP_FWD, a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype,
+                       ep, Nc, ldo, workspace, workspace_bytes, s);
     }
     return PT_ERR_UNSUPPORTED;
 }
@@ -229,8 +367,8 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
         if (trans_b) return PT_ERR_UNSUPPORTED;
         if (!aligned16(dy) || !aligned16(b) || !aligned16(dx)) return PT_ERR_MISALIGNED;
         if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
-        return mx_gemm(dy, dy_scale, b, b_scale, dx, nullptr, group_lens, group_offs, G, M, K, N, dtype, kEpiNone, K,
-                       K, workspace, workspace_bytes, (hipStream_t)stream);
+        return mx_gemm(PT_OP_DGRAD, dy, dy_scale, b, b_scale, dx, nullptr, group_lens, group_offs, G, M, K, N, dtype,
+                       kEpiNone, K, K, workspace, workspace_bytes, (hipStream_t)stream);
     }
     if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
     if (dy_scale || b_scale) return PT_ERR_INVALID_ARG;
@@ -258,7 +396,13 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
     p.sched = queue_words(workspace, workspace_bytes);
     if (M == 0) return PT_OK;
     hipStream_t s = (hipStream_t)stream;
-    return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdNContig : kFwdKContig, kEpiNone, s); }));
+    uint32_t *queues = p.sched;
+    const TuneKey key = tune_key(PT_OP_DGRAD, dtype, kEpiNone, trans_b, G, M, N, K);
+    return configured(key, cfg_mask(queues != nullptr, true), true, s, [&](int cfg) {
+        p.narrow = (cfg & kCfgNarrow) != 0;
+        p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+        return queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdNContig : kFwdKContig, kEpiNone, s); });
+    });
 }
 
 int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_saved, void *dc,
@@ -298,7 +442,12 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_sa
     p.sched = queue_words(workspace, workspace_bytes);
     if (M == 0) return PT_OK;
     hipStream_t s = (hipStream_t)stream;
-    return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdNContig : kFwdKContig, kEpiDSwiglu, s); }));
+    uint32_t *queues = p.sched;
+    const TuneKey key = tune_key(PT_OP_DGRAD_SWIGLU, PT_BF16, kEpiDSwiglu, trans_b, G, M, N, K);
+    return configured(key, cfg_mask(queues != nullptr, false), true, s, [&](int cfg) {
+        p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+        return queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdNContig : kFwdKContig, kEpiDSwiglu, s); });
+    });
 }
 
 int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy, const uint8_t *dy_scale,
@@ -384,12 +533,17 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
     p.err = error_word(workspace, workspace_bytes);
     p.G = (int)G;
     p.M = M;
-    p.tilesM = (p.Mout + bf16_tile_m() - 1) / bf16_tile_m();
     p.tilesN = (p.Nout + bf16_tile_n() - 1) / bf16_tile_n();
     p.accumulate = accumulate;
-    p.sched = queue_words(workspace, workspace_bytes);
     if (M == 0 && accumulate) return PT_OK;
-    return hip_status(queued(p.sched, s, [&] { return launch_bf16(p, kWgrad, kEpiNone, s); }));
+    uint32_t *queues = queue_words(workspace, workspace_bytes);
+    const TuneKey key = tune_key(PT_OP_WGRAD, dtype, kEpiNone, trans_out, G, M, N, K);
+    return configured(key, cfg_mask(queues != nullptr, true), !accumulate, s, [&](int cfg) {
+        p.narrow = (cfg & kCfgNarrow) != 0;
+        p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+        p.tilesM = (p.Mout + bf16_tile_m(p.narrow) - 1) / bf16_tile_m(p.narrow);
+        return queued(p.sched, s, [&] { return launch_bf16(p, kWgrad, kEpiNone, s); });
+    });
 }
 
 int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_t cols, int dtype, int axis,
@@ -523,6 +677,39 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, i
             return (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, N, fmt) + mx_swz_b_bytes(G, K, N, fmt));
     }
     return kQueueWsBytes;
+}
+
+int pt_set_gemm_config(int config)
+{
+    if (config != PT_CONFIG_RULES && config != PT_CONFIG_TUNE && (config < 0 || config >= kNumCfg)) return -3;
+    return g_mode.exchange(config);
+}
+
+int pt_gemm_config_of(int op, int dtype, int epilogue, int trans, int64_t G, int64_t M, int64_t N, int64_t K)
+{
+    // the classes as the entry points record them
+    switch (op) {
+    case PT_OP_FWD: {
+        const int ep =
+            epilogue == PT_EPI_SWIGLU ? kEpiSwiglu : epilogue == PT_EPI_SWIGLU_MXFP4 ? kEpiSwigluMxfp4 : kEpiNone;
+        return tune_lookup(tune_key(op, dtype, ep, dtype == PT_BF16 ? trans : 0, G, M, N, K));
+    }
+    case PT_OP_DGRAD:      // the MX / FP8 data gradient runs as a GEMM with K outputs over N
+        if (dtype == PT_BF16) return tune_lookup(tune_key(op, dtype, kEpiNone, trans, G, M, N, K));
+        return tune_lookup(tune_key(op, dtype, kEpiNone, 0, G, M, K, N));
+    case PT_OP_WGRAD:      // every dtype's weight gradient runs the BF16 kernel
+        return tune_lookup(tune_key(op, PT_BF16, kEpiNone, trans, G, M, N, K));
+    case PT_OP_DGRAD_SWIGLU:
+        return tune_lookup(tune_key(op, PT_BF16, kEpiDSwiglu, trans, G, M, N, K));
+    default:
+        return -1;
+    }
+}
+
+void pt_clear_gemm_tuning(void)
+{
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    g_ntune = 0;
 }
 
 int pt_read_error_flags(const void *workspace, void *stream, uint32_t *flags)

@@ -975,20 +975,9 @@ __global__ void queue_reset_kernel(uint32_t *sched)
     if (i < kQueues) __hip_atomic_store(sched + i * kQueueStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Which BF16 mainloop runs: PTGG_BF16_TILE=128 selects the 128 x 256
-// kernel (a tuning knob for experiments; results do not depend on it).
-bool bf16_narrow()
-{
-    static const bool narrow = [] {
-        const char *e = getenv("PTGG_BF16_TILE");
-        return e && atoi(e) == 128;
-    }();
-    return narrow;
-}
-
 }  // namespace
 
-int bf16_tile_m() { return bf16_narrow() ? BM : WBM; }
+int bf16_tile_m(int narrow) { return narrow ? BM : WBM; }
 int bf16_tile_n() { return BN; }
 
 hipError_t launch_queue_reset(uint32_t *sched, hipStream_t s)
@@ -1005,7 +994,8 @@ hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s)
         if (kind == kFwdNContig) return launch_wide_ring<kFwdNContig, kEpiDSwiglu>(p, s);
         return hipErrorInvalidValue;
     }
-    if (!bf16_narrow()) {
+    // the 256 x 256 kernel, or the 128 x 256 one (bit-identical results)
+    if (!p.narrow) {
         if (kind == kWgrad) return launch_wide_ring<kWgrad, kEpiNone>(p, s);
         if (kind == kFwdKContig) {
             if (epi == kEpiSwiglu) return launch_wide_ring<kFwdKContig, kEpiSwiglu>(p, s);

@@ -1001,18 +1001,6 @@ __global__ __launch_bounds__(256) void mx_scale_swizzle_kernel(const uint8_t *sc
     }
 }
 
-// Which MX mainloop runs: PTGG_MX_TILE=128 forces the 128 x 256 kernel
-// wherever it applies (a tuning knob for experiments; results do not depend
-// on it).
-bool mx_force_narrow()
-{
-    static const bool narrow = [] {
-        const char *e = getenv("PTGG_MX_TILE");
-        return e && atoi(e) == 128;
-    }();
-    return narrow;
-}
-
 int64_t mx_swizzle_bytes(int64_t rows, int64_t K, int fmt)
 {
     const int64_t KS = K / 32, NS = fmt == 0 ? (KS + 3) / 4 : (KS + 7) / 8;
@@ -1035,8 +1023,11 @@ hipError_t launch_mx_scale_swizzle(const uint8_t *scales, int64_t rows, int64_t 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s)
 {
     if (p.sfa) return p.sf_rows ? launch_wide_epi<0, kWConstRow>(p, epi, s) : launch_wide_epi<0, kWConst>(p, epi, s);
-    if (fmt == 1 && mx_force_narrow())
+    // the 128 x 256 kernel on row-major scales when asked (bit-identical results)
+    if (p.narrow) {
+        if (fmt == 0) return launch_epi<0, kScE4M3>(p, epi, s);
         return p.K % 128 == 0 ? launch_epi<1, kScE2M1Word>(p, epi, s) : launch_epi<1, kScE2M1Span>(p, epi, s);
+    }
     if (p.sa && p.sb)
         return fmt == 0 ? launch_wide_epi<0, kWE4M3Swz>(p, epi, s) : launch_wide_epi<1, kWE2M1Swz>(p, epi, s);
     if (fmt == 0) {

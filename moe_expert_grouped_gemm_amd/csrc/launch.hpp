@@ -30,6 +30,7 @@ struct Bf16Params {
     uint32_t *sched;   // tile-queue counters in the workspace, or null (static order)
     const uint16_t *aux; // SwiGLU backward: the FC1 output [gate | up] the epilogue reads
     int ldaux;           // its row stride (elements)
+    int narrow;          // 1: the 128 x 256 kernel (not for kEpiDSwiglu), 0: the 256 x 256 one
 };
 
 enum Bf16Kind { kFwdKContig = 0, kFwdNContig = 1, kWgrad = 2 };
@@ -39,7 +40,7 @@ enum Epi { kEpiNone = 0, kEpiSwiglu = 1, kEpiSwigluMxfp4 = 2, kEpiDSwiglu = 3 };
 constexpr bool epi_glu(int epi) { return epi == kEpiSwiglu || epi == kEpiSwigluMxfp4; }
 
 hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s);
-int bf16_tile_m();
+int bf16_tile_m(int narrow);
 int bf16_tile_n();
 
 struct MxParams {
@@ -63,6 +64,7 @@ struct MxParams {
     const float *sfa;        // FP8 with tensor scales: A's fp32 scale (1 value), or null (MX)
     const float *sfb;        // and each expert's B scale [G]
     int sf_rows;             // sfa / sfb hold one scale per row of A [M] and per row of B [G, N]
+    int narrow;              // 1: the 128 x 256 kernel on row-major scales (MX only), 0: rules
 };
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);

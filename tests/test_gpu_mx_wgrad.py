@@ -104,9 +104,10 @@ def test_mx_wgrad_needs_its_workspace(dev):
     assert L.pt_grouped_gemm_wgrad(*args, small.data_ptr(), 4096, st) == 4
     assert L.pt_grouped_gemm_wgrad(q.data_ptr(), s.data_ptr(), q.data_ptr(), s.data_ptr(), mg.data_ptr(),
                                    lens.data_ptr(), None, 1, 40, 64, 64, ptm.PT_MXFP4_E2M1, 0, 1, None, 0, st) == 4
-    # FP8 with tensor scales has no weight gradient here
+    # FP8 with row factors has no weight gradient
     assert L.pt_grouped_gemm_wgrad(q.data_ptr(), s.data_ptr(), q.data_ptr(), s.data_ptr(), mg.data_ptr(),
-                                   lens.data_ptr(), None, 1, 40, 64, 64, ptm.PT_FP8_E4M3, 0, 1, None, 0, st) == 2
+                                   lens.data_ptr(), None, 1, 40, 64, 64, ptm.PT_FP8_E4M3_ROWWISE, 0, 1, None, 0,
+                                   st) == 2
 
 
 def element_values(orc, codes, fmt):
