@@ -73,9 +73,9 @@ def lib():
         L.orc_fp8_quantize.restype = None
         L.orc_fp8_quantize.argtypes = [p, i64, i64, p, p, p]
         L.orc_swiglu.restype = None
-        L.orc_swiglu.argtypes = [p, i64, i64, p]
+        L.orc_swiglu.argtypes = [p, i64, i64, ctypes.c_double, p]
         L.orc_swiglu_bwd.restype = None
-        L.orc_swiglu_bwd.argtypes = [p, p, i64, i64, p]
+        L.orc_swiglu_bwd.argtypes = [p, p, i64, i64, ctypes.c_double, p]
         L.orc_threads.restype = i32
         L.orc_threads.argtypes = []
         _lib = L
@@ -241,22 +241,26 @@ def mx_dequantize(dtype: int, q: np.ndarray, s: np.ndarray, rows: int, cols: int
     return decode(dtype, q, s, rows, cols)
 
 
-def swiglu(c: np.ndarray) -> np.ndarray:
+def swiglu(c: np.ndarray, limit: float = 0.0) -> np.ndarray:
+    """silu(gate) * up over c = [gate | up] ([n, 2I]); with a limit L > 0 the
+    clamped SwiGLU (the DeepSeek-V4 blog's swiglu_limit knob): gate clamped to
+    at most L, up to [-L, L]."""
     c = _c(c, np.float64)
     n, N = c.shape
     h = np.empty((n, N // 2), np.float64)
-    lib().orc_swiglu(_ptr(c), n, N, _ptr(h))
+    lib().orc_swiglu(_ptr(c), n, N, float(limit), _ptr(h))
     return h
 
 
-def swiglu_bwd(dh: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """Gradient of c = [gate | up] ([n, 2I]) given dh = d(silu(gate) * up) ([n, I])."""
+def swiglu_bwd(dh: np.ndarray, c: np.ndarray, limit: float = 0.0) -> np.ndarray:
+    """Gradient of c = [gate | up] ([n, 2I]) given dh = d(silu(gate) * up) ([n, I]);
+    with a limit, of the clamped SwiGLU (no gradient into a clamped input)."""
     dh, c = _c(dh, np.float64), _c(c, np.float64)
     n, I = dh.shape
     if c.shape != (n, 2 * I):
         raise ValueError("c must be [n, 2I] for dh [n, I]")
     dc = np.empty((n, 2 * I), np.float64)
-    lib().orc_swiglu_bwd(_ptr(dh), _ptr(c), n, I, _ptr(dc))
+    lib().orc_swiglu_bwd(_ptr(dh), _ptr(c), n, I, float(limit), _ptr(dc))
     return dc
 
 
@@ -319,7 +323,7 @@ def fp8_wgrad_rows(a_q, a_dequant, dy_q, dy_dequant, group_lens, N, K, gs, ks):
 
 
 # ------------------------------------------------------------------ composed ops
-def grouped_fwd(dtype, a, a_scale, b, b_scale, group_lens, N, K, trans_b, epilogue, rows):
+def grouped_fwd(dtype, a, a_scale, b, b_scale, group_lens, N, K, trans_b, epilogue, rows, limit=0.0):
     """Forward with its epilogue, for the listed rows.
 
     Returns a dict:
@@ -331,7 +335,7 @@ def grouped_fwd(dtype, a, a_scale, b, b_scale, group_lens, N, K, trans_b, epilog
     c = fwd_rows(dtype, a, a_scale, b, b_scale, group_lens, N, K, trans_b, rows)
     if epilogue == EPI_NONE:
         return {"exact": c, "bf16": round_bf16(c)}
-    h = swiglu(c)
+    h = swiglu(c, limit)
     hb = round_bf16(h)
     out = {"exact": h, "bf16": hb}
     if epilogue == EPI_SWIGLU_MXFP4:
@@ -372,7 +376,7 @@ def fp8_fwd_rows_rowwise(a_q, a_dequant, b_q, b_dequant, group_lens, N, K, rows)
     return c * fa[:, None] * fb
 
 
-def dgrad_swiglu_rows(dy, b, c_saved, group_lens, N, K, trans_b, rows):
+def dgrad_swiglu_rows(dy, b, c_saved, group_lens, N, K, trans_b, rows, limit=0.0):
     """FC2's data gradient followed by the SwiGLU backward, for the listed rows.
 
     dH = dY_g @ B_g^T is rounded to bf16 (what the data gradient stores), then
@@ -384,7 +388,7 @@ def dgrad_swiglu_rows(dy, b, c_saved, group_lens, N, K, trans_b, rows):
     dh = dgrad_rows(dy, b, group_lens, N, K, trans_b, rows)
     dhb = round_bf16(dh)
     c = bf16_to_f64(_c(c_saved, np.uint16)[rows])
-    dc = swiglu_bwd(bf16_to_f64(dhb), c)
+    dc = swiglu_bwd(bf16_to_f64(dhb), c, limit)
     return {"dh_bf16": dhb, "exact": dc, "bf16": round_bf16(dc)}
 
 

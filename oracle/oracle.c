@@ -512,29 +512,50 @@ int orc_wgrad_rows(const uint16_t *a, const uint16_t *dy,
     return bad;
 }
 
-/* SwiGLU over [gate | up] halves: h[i, j] = silu(c[i, j]) * c[i, I + j]. */
-void orc_swiglu(const double *c, int64_t nrows, int64_t N, double *h)
+/*
+ * SwiGLU over [gate | up] halves: h[i, j] = silu(g) * u with g = c[i, j],
+ * u = c[i, I + j].  With a limit L > 0 (finite) the SwiGLU is clamped first:
+ * g = min(g, L) and u = min(max(u, -L), L); limit <= 0 or infinite leaves it
+ * plain.
+ */
+static int clamp_on(double limit) { return limit > 0.0 && isfinite(limit); }
+
+void orc_swiglu(const double *c, int64_t nrows, int64_t N, double limit, double *h)
 {
     int64_t I = N / 2;
+    const int on = clamp_on(limit);
     for (int64_t i = 0; i < nrows; ++i)
         for (int64_t j = 0; j < I; ++j) {
             double gate = c[i * N + j], up = c[i * N + I + j];
+            if (on) {
+                gate = gate < limit ? gate : limit;
+                up = up < -limit ? -limit : (up > limit ? limit : up);
+            }
             h[i * I + j] = gate / (1.0 + exp(-gate)) * up;
         }
 }
 
 /* Backward of the SwiGLU above.  h = silu(g) * u with silu(g) = g * s,
- * s = 1 / (1 + e^-g), so dh/du = g * s and dh/dg = u * (s + g * s * (1 - s)).
- * dh [nrows, I] and c [nrows, 2I] = [gate | up] in; dc [nrows, 2I] out, the
- * gradient of c in the same [gate | up] layout. */
-void orc_swiglu_bwd(const double *dh, const double *c, int64_t nrows, int64_t I, double *dc)
+ * s = 1 / (1 + e^-g), so dh/du = g * s and dh/dg = u * (s + g * s * (1 - s)),
+ * taken at the clamped g and u.  A clamped input gets no gradient: the gate
+ * where g > L, the up value where |u| > L (at the limit itself the gradient
+ * passes).  dh [nrows, I] and c [nrows, 2I] = [gate | up] in; dc [nrows, 2I]
+ * out, the gradient of c in the same [gate | up] layout. */
+void orc_swiglu_bwd(const double *dh, const double *c, int64_t nrows, int64_t I, double limit, double *dc)
 {
+    const int on = clamp_on(limit);
     for (int64_t i = 0; i < nrows; ++i)
         for (int64_t j = 0; j < I; ++j) {
             double g = c[i * 2 * I + j], u = c[i * 2 * I + I + j], d = dh[i * I + j];
+            int pass_g = 1, pass_u = 1;
+            if (on) {
+                if (g > limit) { g = limit; pass_g = 0; }
+                if (u > limit) { u = limit; pass_u = 0; }
+                if (u < -limit) { u = -limit; pass_u = 0; }
+            }
             double s = 1.0 / (1.0 + exp(-g));
-            dc[i * 2 * I + j] = d * u * s * (1.0 + g * (1.0 - s));
-            dc[i * 2 * I + I + j] = d * g * s;
+            dc[i * 2 * I + j] = pass_g ? d * u * s * (1.0 + g * (1.0 - s)) : 0.0;
+            dc[i * 2 * I + I + j] = pass_u ? d * g * s : 0.0;
         }
 }
 

@@ -259,6 +259,44 @@ def test_swiglu_bwd_closed_forms(orc):
         orc.swiglu_bwd(dh, c[:, :4])
 
 
+def test_swiglu_clamp_closed_forms(orc):
+    # L = 10: a gate above L becomes L, an up value outside [-L, L] becomes
+    # +-L; a gate far below -L is left alone (the gate clamp is one-sided)
+    c = np.array([[20.0, 1.0, 0.5, -30.0, 3.0, -20.0, 30.0, 2.0]])
+    h = orc.swiglu(c, 10.0)
+    silu = lambda x: x / (1 + math.exp(-x))
+    assert h[0, 0] == pytest.approx(silu(10.0) * 3.0, rel=1e-15)
+    assert h[0, 1] == pytest.approx(silu(1.0) * -10.0, rel=1e-15)
+    assert h[0, 2] == pytest.approx(silu(0.5) * 10.0, rel=1e-15)
+    assert h[0, 3] == pytest.approx(silu(-30.0) * 2.0, rel=1e-15)
+    # a limit at or above every input changes nothing; 0 and inf mean "off"
+    rng = np.random.default_rng(22)
+    c2 = rng.uniform(-5.0, 5.0, size=(4, 16))
+    for lim in (5.0, 0.0, math.inf):
+        assert np.array_equal(orc.swiglu(c2, lim), orc.swiglu(c2))
+
+
+def test_swiglu_clamp_bwd_matches_central_differences(orc):
+    # away from the kinks the clamped backward is the derivative of the
+    # clamped forward: zero into a clamped input, the plain one elsewhere
+    rng = np.random.default_rng(23)
+    n, I, lim = 6, 40, 2.5
+    g = rng.uniform(-6.0, 6.0, size=(n, I))
+    u = rng.uniform(-6.0, 6.0, size=(n, I))
+    g[np.abs(g - lim) < 1e-3] += 0.01
+    u[np.abs(np.abs(u) - lim) < 1e-3] += 0.01
+    dh = rng.uniform(-2.0, 2.0, size=(n, I))
+    dc = orc.swiglu_bwd(dh, np.concatenate([g, u], axis=1), lim)
+    eps = 1e-6
+    h = lambda gg, uu: orc.swiglu(np.concatenate([gg, uu], axis=1), lim)
+    dg_fd = dh * (h(g + eps, u) - h(g - eps, u)) / (2 * eps)
+    du_fd = dh * (h(g, u + eps) - h(g, u - eps)) / (2 * eps)
+    assert np.allclose(dc[:, :I], dg_fd, rtol=1e-7, atol=1e-8)
+    assert np.allclose(dc[:, I:], du_fd, rtol=1e-7, atol=1e-8)
+    assert (dc[:, :I][g > lim] == 0).all() and (dc[:, I:][np.abs(u) > lim] == 0).all()
+    assert (dc[:, :I][g < lim] != 0).any()
+
+
 def test_dgrad_swiglu_rows_composition(orc):
     # Integer operands keep dH exact; the composed op must equal the pinned
     # backward applied to bf16(dH) from a numpy per-expert matmul, row by row,
