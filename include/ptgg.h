@@ -129,6 +129,13 @@ typedef enum {
  *  of A) and b_scale [G, N] fp32 (one per row of each expert's B, i.e. per
  *  output column): C[r, n] = (sum_k a[r, k] * b_g[n, k]) * (a_scale[r] *
  *  b_scale[g, n]), the two factors multiplied in fp32 first.
+ *  swiglu_limit  the clamped SwiGLU of the SWIGLU epilogues (the DeepSeek-V4
+ *             blog lists a swiglu_limit knob, 10.0 for V4-Flash, "clamped
+ *             SwiGLU" for FP8 and FP4 stability, without a formula; the
+ *             reading taken): with L = swiglu_limit > 0 and finite, the
+ *             epilogue computes silu(min(g, L)) * min(max(u, -L), L).  0 or
+ *             infinity: the plain SwiGLU; NaN: PT_ERR_INVALID_ARG.  Ignored
+ *             by PT_EPI_NONE.
  *  workspace  optional (may be NULL): the error word and tile queues, see
  *             pt_grouped_gemm_workspace_size.
  */
@@ -137,7 +144,7 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale,
                         void *out, uint8_t *out_scale,
                         const int64_t *group_lens, const int64_t *group_offs,
                         int64_t G, int64_t M, int64_t N, int64_t K,
-                        int dtype, int trans_b, int epilogue,
+                        int dtype, int trans_b, int epilogue, float swiglu_limit,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -191,12 +198,16 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale,
  *  c_saved  [M, 2K] bf16, FC1's output [gate | up] saved by the forward;
  *  dc       [M, 2K] bf16 output; rows outside every expert are not written.
  *  All four 16-byte aligned.  Requirements: N % 8 == 0, K % 8 == 0.
+ *  swiglu_limit  the forward's clamp (see pt_grouped_gemm_fwd; 0 or
+ *           infinity for none): g and u are clamped as in the forward, and a
+ *           clamped input gets no gradient (dC[r, j] = 0 where g > L,
+ *           dC[r, K + j] = 0 where |u| > L).
  *  workspace  optional (may be NULL), as for pt_grouped_gemm_dgrad.
  */
 int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_saved, void *dc,
                                  const int64_t *group_lens, const int64_t *group_offs,
                                  int64_t G, int64_t M, int64_t N, int64_t K, int trans_b,
-                                 void *workspace, size_t workspace_bytes, void *stream);
+                                 float swiglu_limit, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Grouped weight gradient, accumulated into an fp32 main_grad (PR page

@@ -67,13 +67,13 @@ def load(require_gpu: bool = True):
     if not os.path.exists(_build.LIB):
         _build.build()
     L = ctypes.CDLL(_build.LIB)
-    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    p, i64, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     L.pt_grouped_gemm_fwd.restype = i32
-    L.pt_grouped_gemm_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
+    L.pt_grouped_gemm_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, f32, p, sz, p]
     L.pt_grouped_gemm_dgrad.restype = i32
     L.pt_grouped_gemm_dgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, p, sz, p]
     L.pt_grouped_gemm_dgrad_swiglu.restype = i32
-    L.pt_grouped_gemm_dgrad_swiglu.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i32, p, sz, p]
+    L.pt_grouped_gemm_dgrad_swiglu.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i32, f32, p, sz, p]
     L.pt_grouped_gemm_wgrad.restype = i32
     L.pt_grouped_gemm_wgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
     L.pt_mx_quantize.restype = i32
@@ -138,11 +138,11 @@ def _check(fn, status):
 
 
 def pt_grouped_gemm_fwd(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs,
-                        G, M, N, K, dtype, trans_b, epilogue, workspace=None, stream=None):
+                        G, M, N, K, dtype, trans_b, epilogue, workspace=None, stream=None, swiglu_limit=0.0):
     L = load()
     _check("pt_grouped_gemm_fwd", L.pt_grouped_gemm_fwd(
         _ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), _ptr(out), _ptr(out_scale),
-        _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_b, epilogue,
+        _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_b, epilogue, swiglu_limit,
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
@@ -156,11 +156,11 @@ def pt_grouped_gemm_dgrad(dy, dy_scale, b, b_scale, dx, group_lens, group_offs,
 
 
 def pt_grouped_gemm_dgrad_swiglu(dy, b, c_saved, dc, group_lens, group_offs,
-                                 G, M, N, K, trans_b, workspace=None, stream=None):
+                                 G, M, N, K, trans_b, workspace=None, stream=None, swiglu_limit=0.0):
     L = load()
     _check("pt_grouped_gemm_dgrad_swiglu", L.pt_grouped_gemm_dgrad_swiglu(
         _ptr(dy), _ptr(b), _ptr(c_saved), _ptr(dc), _ptr(group_lens), _ptr(group_offs),
-        G, M, N, K, trans_b, _ptr(workspace), _nbytes(workspace), _stream(stream)))
+        G, M, N, K, trans_b, swiglu_limit, _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def pt_grouped_gemm_wgrad(a, a_scale, dy, dy_scale, main_grad, group_lens, group_offs,

@@ -91,6 +91,12 @@ hipError_t queued(uint32_t *sched, hipStream_t s, Launch launch)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PT_OK : PT_ERR_HIP; }
 
+// The SwiGLU clamp the kernels apply: +inf (none) for a limit <= 0 or infinite.
+float swiglu_clamp(float limit)
+{
+    return (limit > 0.0f && limit < __builtin_huge_valf()) ? limit : __builtin_huge_valf();
+}
+
 // ---------------------------------------------------------------- kernel configurations and tuning
 // A configuration of one grouped GEMM call: bit 0 takes tiles in the static
 // order even when the workspace holds queues, bit 1 runs the 128 x 256
@@ -225,8 +231,8 @@ using namespace ptgg;
 // one per expert for B (b_scale) in place of the E8M0 block scales.
 static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale, void *out,
                    uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
-                   int64_t N, int64_t K, int dtype, int ep, int64_t Nc, int64_t ldo, void *workspace,
-                   size_t workspace_bytes, hipStream_t s)
+                   int64_t N, int64_t K, int dtype, int ep, int64_t Nc, int64_t ldo, float swiglu_limit,
+                   void *workspace, size_t workspace_bytes, hipStream_t s)
 {
     const bool tensor_scales = dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE;
     if (N % 8) return PT_ERR_UNSUPPORTED;              // outputs leave in 16-byte chunks
@@ -236,6 +242,7 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
     const int64_t kb = dtype == PT_MXFP4_E2M1 ? K / 2 : K;      // code bytes per row
     if (!fits31(M * kb) || !fits31(N * kb) || !fits31(G * N * (K / 32) + 4)) return PT_ERR_UNSUPPORTED;
     MxParams p = {};
+    p.swiglu_limit = swiglu_clamp(swiglu_limit);
     p.a = (const uint8_t *)a;
     p.as = a_scale;
     p.b = (const uint8_t *)b;
@@ -290,8 +297,9 @@ extern "C" {
 int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale,
                         void *out, uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs,
                         int64_t G, int64_t M, int64_t N, int64_t K, int dtype, int trans_b, int epilogue,
-                        void *workspace, size_t workspace_bytes, void *stream)
+                        float swiglu_limit, void *workspace, size_t workspace_bytes, void *stream)
 {
+    if (swiglu_limit != swiglu_limit) return PT_ERR_INVALID_ARG;   // NaN
     int st = check_groups(group_lens, G, M);
     if (st) return st;
     if (N < 1 || K < 1 || N > INT32_MAX / 4 || K > INT32_MAX / 4) return PT_ERR_INVALID_ARG;
@@ -314,10 +322,12 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
         if (!trans_b && N % 8) return PT_ERR_UNSUPPORTED;
         if (!fits31(M * K * 2) || !fits31(N * K * 2)) return PT_ERR_UNSUPPORTED;
         Bf16Params p = {};
+        p.swiglu_limit = __builtin_huge_valf();
         p.a = (const uint16_t *)a;
         p.b = (const uint16_t *)b;
         p.out = out;
         p.out_scale = out_scale;
+        p.swiglu_limit = swiglu_clamp(swiglu_limit);
         p.lens = group_lens;
         p.offs = group_offs;
         p.err = error_word(workspace, workspace_bytes);
@@ -344,7 +354,7 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
     if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE) {
         if (!trans_b) return PT_ERR_UNSUPPORTED;           // K-contiguous codes
         return mx_gemm(PT_OP_FWD, a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype,
-                       ep, Nc, ldo, workspace, workspace_bytes, s);
+                       ep, Nc, ldo, swiglu_limit, workspace, workspace_bytes, s);
     }
     return PT_ERR_UNSUPPORTED;
 }
@@ -368,7 +378,7 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
         if (!aligned16(dy) || !aligned16(b) || !aligned16(dx)) return PT_ERR_MISALIGNED;
         if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
         return mx_gemm(PT_OP_DGRAD, dy, dy_scale, b, b_scale, dx, nullptr, group_lens, group_offs, G, M, K, N, dtype,
-                       kEpiNone, K, K, workspace, workspace_bytes, (hipStream_t)stream);
+                       kEpiNone, K, K, 0.0f, workspace, workspace_bytes, (hipStream_t)stream);
     }
     if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
     if (dy_scale || b_scale) return PT_ERR_INVALID_ARG;
@@ -378,6 +388,7 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
     // dX[r, k] = sum_n dY[r, n] B[k, n]: reduction over n, output columns k.
     Bf16Params p = {};
+    p.swiglu_limit = __builtin_huge_valf();
     p.a = (const uint16_t *)dy;
     p.b = (const uint16_t *)b;
     p.out = dx;
@@ -407,9 +418,10 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
 
 int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_saved, void *dc,
                                  const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
-                                 int64_t N, int64_t K, int trans_b, void *workspace, size_t workspace_bytes,
-                                 void *stream)
+                                 int64_t N, int64_t K, int trans_b, float swiglu_limit, void *workspace,
+                                 size_t workspace_bytes, void *stream)
 {
+    if (swiglu_limit != swiglu_limit) return PT_ERR_INVALID_ARG;   // NaN
     int st = check_groups(group_lens, G, M);
     if (st) return st;
     if (N < 1 || K < 1 || N > INT32_MAX / 4 || K > INT32_MAX / 8) return PT_ERR_INVALID_ARG;
@@ -422,6 +434,7 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_sa
     // dH[r, k] = sum_n dY[r, n] B[k, n] as in pt_grouped_gemm_dgrad; the
     // epilogue turns each bf16 dH tile into the [gate | up] gradient.
     Bf16Params p = {};
+    p.swiglu_limit = __builtin_huge_valf();
     p.a = (const uint16_t *)dy;
     p.b = (const uint16_t *)b;
     p.out = dc;
@@ -437,6 +450,7 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_sa
     p.b_gstride = N * K;
     p.ldo = (int)(2 * K);
     p.aux = (const uint16_t *)c_saved;
+    p.swiglu_limit = swiglu_clamp(swiglu_limit);
     p.ldaux = (int)(2 * K);
     p.tilesN = (int)((K + bf16_tile_n() - 1) / bf16_tile_n());
     p.sched = queue_words(workspace, workspace_bytes);
@@ -517,6 +531,7 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
     if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad)) return PT_ERR_MISALIGNED;
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
     Bf16Params p = {};
+    p.swiglu_limit = __builtin_huge_valf();
     // trans_out = 0: D[k, n] = sum_r A[r, k] dY[r, n];  1: D^T[n, k] with the
     // operands swapped
     p.a = (const uint16_t *)(trans_out ? dy : a);

@@ -39,8 +39,12 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return bits_f32(h << 
 // silu(gate) * up = gate / (1 + e^-gate) * up, with the hardware reciprocal
 // (1 ulp) instead of an IEEE division; 1/inf = 0 gives the limit for very
 // negative gates.
-__device__ __forceinline__ float silu_mul(float gate, float up)
+// With a finite lim the clamped form: gate at most lim, up within
+// [-lim, lim]; lim = +inf leaves both as they are.
+__device__ __forceinline__ float silu_mul(float gate, float up, float lim)
 {
+    gate = __builtin_fminf(gate, lim);
+    up = __builtin_fminf(__builtin_fmaxf(up, -lim), lim);
     return gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
 }
 

@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void gg_bf16_kernel(Bf16Params p)
                     }
                 }
         } else {
-            store_out<EPI>(acc, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wm, wn);
+            store_out<EPI>(acc, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wm, wn, p.swiglu_limit);
         }
     }
 }
@@ -925,7 +925,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 }
         } else {
             store_tile_lds_w<EPI, 4, MI, NJ>(acc, smem, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wrow0, wn,
-                                             p.aux, p.ldaux);
+                                             p.swiglu_limit, p.aux, p.ldaux);
         }
         barrier();
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);

@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 2) void gg_mx_kernel(MxParams p)
         // drain the dummy stages still in flight before the slots are reused
         wait_vmcnt<0>();
         barrier();
-        store_out<EPI>(acc, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn);
+        store_out<EPI>(acc, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn, p.swiglu_limit);
     }
 }
 
@@ -887,7 +887,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                     for (int bj = 0; bj < 4; ++bj) acc[bi][bj][r] *= fa * fb[bj];
                 }
         }
-        store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn);
+        store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn, p.swiglu_limit);
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
         par ^= 1;
     }

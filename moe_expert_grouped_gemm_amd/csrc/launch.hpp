@@ -31,6 +31,7 @@ struct Bf16Params {
     const uint16_t *aux; // SwiGLU backward: the FC1 output [gate | up] the epilogue reads
     int ldaux;           // its row stride (elements)
     int narrow;          // 1: the 128 x 256 kernel (not for kEpiDSwiglu), 0: the 256 x 256 one
+    float swiglu_limit;  // SwiGLU clamp (forward and backward epilogues); +inf for none
 };
 
 enum Bf16Kind { kFwdKContig = 0, kFwdNContig = 1, kWgrad = 2 };
@@ -65,6 +66,7 @@ struct MxParams {
     const float *sfb;        // and each expert's B scale [G]
     int sf_rows;             // sfa / sfb hold one scale per row of A [M] and per row of B [G, N]
     int narrow;              // 1: the 128 x 256 kernel on row-major scales (MX only), 0: rules
+    float swiglu_limit;      // SwiGLU clamp; +inf for none
 };
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);

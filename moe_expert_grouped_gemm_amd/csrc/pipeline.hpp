@@ -159,9 +159,10 @@ __device__ __forceinline__ int e_row(int wm, int bi, int reg)
 //   kEpiSwigluMxfp4: codes out[M, ldo bytes] (two per byte, low nibble the
 //                    even output), scales out_scale[M, Nout/64]; requires
 //                    (Nout/2) % 32 == 0
+// lim: the SwiGLU clamp (+inf for none).
 template <int EPI>
 __device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], void *out, uint8_t *out_scale, int ldo,
-                                          int Nout, int64_t row0, int m0, int rows, int nt, int wm, int wn)
+                                          int Nout, int64_t row0, int m0, int rows, int nt, int wm, int wn, float lim)
 {
     const int lane = threadIdx.x & 63;
     if (EPI == kEpiNone) {
@@ -191,7 +192,8 @@ __device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], void *out
                 for (int r = 0; r < 16; ++r) {
                     const int m = m0 + e_row(wm, bi, r);
                     if (m < rows)
-                        o[(int64_t)m * ldo + j] = (uint16_t)bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r]));
+                        o[(int64_t)m * ldo + j] =
+                            (uint16_t)bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r], lim));
                 }
         }
     } else {
@@ -209,7 +211,7 @@ __device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], void *out
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = m0 + e_row(wm, bi, r);
-                    const uint32_t hb = bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r]));
+                    const uint32_t hb = bf16_rne(silu_mul(acc[bi][bj][r], acc[bi][bj + 2][r], lim));
                     uint32_t amax = hb & 0x7FFFu;
 #pragma unroll
                     for (int d = 1; d < 32; d <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, d, 64));
@@ -244,7 +246,7 @@ __host__ __device__ constexpr int epi_lds_bytes() { return 64 * NWM * epi_row_by
 template <int EPI, int NWM, int MI, int NJ>
 __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], uint8_t *smem, void *out,
                                                  uint8_t *out_scale, int ldo, int Nout, int64_t row0, int m0,
-                                                 int rows, int nt, int wrow0, int wn,
+                                                 int rows, int nt, int wrow0, int wn, float lim,
                                                  const uint16_t *aux = nullptr, int ldaux = 0)
 {
     constexpr int TR = 64 * NWM;                           // tile rows
@@ -273,7 +275,7 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     *(uint16_t *)(smem + row_of(bi, r) * RS + c * 2) =
-                        (uint16_t)bf16_rne(silu_mul(acc[bi][q][r], acc[bi][q + NJ / 2][r]));
+                        (uint16_t)bf16_rne(silu_mul(acc[bi][q][r], acc[bi][q + NJ / 2][r], lim));
             }
     }
     __syncthreads();
@@ -283,7 +285,9 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
         // expert's rows; with g = aux[r, k] and u = aux[r, Nout + k] (the
         // forward's [gate | up] output), write
         //   out[r, k] = dH * u * s * (1 + g * (1 - s)),  out[r, Nout + k] = dH * g * s,
-        // s = sigmoid(g), in fp32, each rounded once to bf16.
+        // s = sigmoid(g), in fp32, each rounded once to bf16.  Clamped
+        // (finite lim): g and u clamped as in the forward, and no gradient
+        // into a clamped input (g > lim, |u| > lim).
         constexpr int CPR = OC / 8;
         uint16_t *o = (uint16_t *)out + row0 * ldo;
         const uint16_t *x = aux + row0 * ldaux;
@@ -302,11 +306,15 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
 #pragma unroll
                     for (int hlf = 0; hlf < 2; ++hlf) {
                         const float d = __uint_as_float((dh[e] >> (16 * hlf)) << 16);
-                        const float g = __uint_as_float((gv[e] >> (16 * hlf)) << 16);
-                        const float u = __uint_as_float((uv[e] >> (16 * hlf)) << 16);
+                        const float g0 = __uint_as_float((gv[e] >> (16 * hlf)) << 16);
+                        const float u0 = __uint_as_float((uv[e] >> (16 * hlf)) << 16);
+                        const float g = __builtin_fminf(g0, lim);
+                        const float u = __builtin_fminf(__builtin_fmaxf(u0, -lim), lim);
                         const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                        pg |= bf16_rne(d * u * (sg * (1.0f + g * (1.0f - sg)))) << (16 * hlf);
-                        pu |= bf16_rne(d * (g * sg)) << (16 * hlf);
+                        const float vg = g0 <= lim ? d * u * (sg * (1.0f + g * (1.0f - sg))) : 0.0f;
+                        const float vu = __builtin_fabsf(u0) <= lim ? d * (g * sg) : 0.0f;
+                        pg |= bf16_rne(vg) << (16 * hlf);
+                        pu |= bf16_rne(vu) << (16 * hlf);
                     }
                     dg[e] = pg;
                     du[e] = pu;
@@ -368,9 +376,9 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
 template <int EPI, int NWM>
 __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[2][4], uint8_t *smem, void *out,
                                                uint8_t *out_scale, int ldo, int Nout, int64_t row0, int m0, int rows,
-                                               int nt, int wm, int wn)
+                                               int nt, int wm, int wn, float lim)
 {
-    store_tile_lds_w<EPI, NWM, 2, 4>(acc, smem, out, out_scale, ldo, Nout, row0, m0, rows, nt, wm * 64, wn);
+    store_tile_lds_w<EPI, NWM, 2, 4>(acc, smem, out, out_scale, ldo, Nout, row0, m0, rows, nt, wm * 64, wn, lim);
 }
 
 // ------------------------------------------------------------------ tile queues

@@ -280,7 +280,7 @@ def test_host_argument_errors(dev):
         return L.pt_grouped_gemm_fwd(args["a"], args["a_scale"], args["b"], args["b_scale"],
                                      args["out"], args["out_scale"], args["lens"], args["offs"],
                                      args["G"], args["M"], args["N"], args["K"], args["dtype"],
-                                     args["trans_b"], args["epi"], None, 0, s)
+                                     args["trans_b"], args["epi"], 0.0, None, 0, s)
 
     assert call() == 0
     assert call(a=None) == 1

@@ -133,7 +133,7 @@ def test_fp8_refusals(dev):
     out = torch.zeros((8, 64), dtype=torch.bfloat16, device=dev)
     g = lambda tb, K, sa=f.data_ptr(): L.pt_grouped_gemm_fwd(a.data_ptr(), sa, b.data_ptr(), f.data_ptr(),
                                                             out.data_ptr(), None, lens.data_ptr(), None, 1, 8, 64,
-                                                            K, ptm.PT_FP8_E4M3, tb, 0, None, 0, st)
+                                                            K, ptm.PT_FP8_E4M3, tb, 0, 0.0, None, 0, st)
     assert g(0, 64) == 2            # codes must be K-contiguous ([G, N, K])
     assert g(1, 48) == 2            # K % 32
     assert g(1, 64, None) == 1      # factors required

@@ -108,11 +108,11 @@ def test_dgrad_swiglu_empty_batch_and_errors(dev):
     st = torch.cuda.current_stream().cuda_stream
     # a missing saved FC1 output, an odd K, and a bad layout flag are refused
     assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), w.data_ptr(), None, cc.data_ptr(), lens1.data_ptr(),
-                                          None, 1, 8, 64, 64, 0, None, 0, st) == 1
+                                          None, 1, 8, 64, 64, 0, 0.0, None, 0, st) == 1
     assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), w.data_ptr(), cc.data_ptr(), cc.data_ptr(),
-                                          lens1.data_ptr(), None, 1, 8, 64, 60, 0, None, 0, st) == 2
+                                          lens1.data_ptr(), None, 1, 8, 64, 60, 0, 0.0, None, 0, st) == 2
     assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), w.data_ptr(), cc.data_ptr(), cc.data_ptr(),
-                                          lens1.data_ptr(), None, 1, 8, 64, 64, 2, None, 0, st) == 1
+                                          lens1.data_ptr(), None, 1, 8, 64, 64, 2, 0.0, None, 0, st) == 1
 
 
 def test_dgrad_swiglu_mlp_shape_sampled(orc, dev):
