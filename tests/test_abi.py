@@ -69,3 +69,67 @@ def test_package_refuses_to_run_without_gpu():
         pytest.skip("GPU present")
     with pytest.raises(RuntimeError):
         pt.load()
+
+
+def test_new_enums_match_header():
+    import moe_expert_grouped_gemm_amd as pt
+    text = open(HEADER).read()
+    for name in ("PT_FP8_E4M3", "PT_FP8_E4M3_ROWWISE", "PT_OP_DGRAD_SWIGLU"):
+        m = re.search(r"\b%s\s*=\s*(\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(pt, name), name
+    for name in ("PT_CONFIG_RULES", "PT_CONFIG_TUNE"):
+        m = re.search(r"#define\s+%s\s+\((-?\d+)\)" % name, text)
+        assert m and int(m.group(1)) == getattr(pt, name), name
+
+
+def test_workspace_sizes_host_only():
+    # closed forms of the scratch each op needs (host arithmetic, no GPU)
+    import moe_expert_grouped_gemm_amd as pt
+    r256 = lambda x: (x + 255) // 256 * 256
+    G, M, N, K = 32, 65536, 5760, 2880
+    base = pt.pt_grouped_gemm_workspace_size(pt.PT_OP_FWD, 1, 1, 1, 1, pt.PT_BF16)
+    assert base == 1280
+    assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, pt.PT_BF16) == base
+    for dt in (pt.PT_MXFP8_E4M3, pt.PT_MXFP4_E2M1):
+        assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, dt) == base + r256(M * K * 2) + r256(M * N * 2)
+    assert (pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, pt.PT_FP8_E4M3) ==
+            base + r256(M * K * 2) + r256(M * N * 2) + r256(G * K * N * 4))
+    # the MX forward adds stage-major scale copies: more than the queues alone
+    assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_FWD, G, M, N, K, pt.PT_MXFP8_E4M3) > base
+
+
+def test_argument_checks_host_only():
+    # refusals decided before any device call (no GPU needed)
+    import ctypes
+    import math
+    import moe_expert_grouped_gemm_amd as pt
+    L = pt.load(require_gpu=False)
+    lens = (ctypes.c_int64 * 4)(1, 2, 3, 4)
+    lp = ctypes.cast(lens, ctypes.c_void_p).value
+    assert L.pt_grouped_gemm_fwd(None, None, None, None, None, None, lp, None, 0, 10, 64, 64, 0, 0, 0, 0.0,
+                                 None, 0, None) == 1                                  # G = 0
+    assert L.pt_grouped_gemm_fwd(None, None, None, None, None, None, lp, None, 4, 10, 64, 64, 0, 0, 1, math.nan,
+                                 None, 0, None) == 1                                  # NaN limit
+    assert L.pt_grouped_gemm_dgrad_swiglu(None, None, None, None, lp, None, 4, 10, 64, 64, 0, math.nan,
+                                          None, 0, None) == 1
+    assert L.pt_stack_experts(None, None, 2, 64, 64, 2, None, 0, None) == 1          # layout flag
+    assert L.pt_stack_experts(None, None, 2, 60, 64, 0, None, 0, None) == 2          # rows % 8
+    assert L.pt_stack_experts(None, None, 0, 64, 64, 0, None, 0, None) == 0          # nothing to do
+    assert L.pt_mx_quantize_experts(None, None, None, None, None, 2, 64, 64, 1, None, 0, None) == 1
+    assert L.pt_mx_quantize_tokens(None, lp, None, None, None, 4, 10, 64, 0, None, 0, None) == 2   # BF16
+
+
+def test_config_mode_host_only():
+    import moe_expert_grouped_gemm_amd as pt
+    pt.pt_clear_gemm_tuning()
+    try:
+        assert pt.pt_set_gemm_config(2) == pt.PT_CONFIG_RULES
+        assert pt.pt_set_gemm_config(pt.PT_CONFIG_TUNE) == 2
+        with pytest.raises(ValueError):
+            pt.pt_set_gemm_config(4)
+        assert pt.pt_set_gemm_config(pt.PT_CONFIG_RULES) == pt.PT_CONFIG_TUNE
+        for op in (pt.PT_OP_FWD, pt.PT_OP_DGRAD, pt.PT_OP_WGRAD, pt.PT_OP_DGRAD_SWIGLU):
+            assert pt.pt_gemm_config_of(op, pt.PT_BF16, 0, 0, 8, 1000, 256, 256) == -1
+        assert pt.pt_gemm_config_of(9, pt.PT_BF16, 0, 0, 8, 1000, 256, 256) == -1
+    finally:
+        pt.pt_set_gemm_config(pt.PT_CONFIG_RULES)
