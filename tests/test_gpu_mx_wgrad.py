@@ -158,3 +158,60 @@ def test_mx_wgrad_full_shape_sampled(orc, dev, fmt):
         dv = element_values(orc, dqn[r0:r1], fmt) * np.ldexp(1.0, dsn[blk].astype(np.int64) - 127)
         D = av @ dv                                                     # [N], binary64
         assert floored_rel_err(after[i].astype(np.float64) - before[i], D) <= BF16_TOL, (g, k)
+
+
+@pytest.mark.parametrize("fmt", FMTS + [ptm.PT_FP8_E4M3], ids=FMT_IDS + ["fp8"])
+def test_wgrad_with_offsets_and_gaps(orc, dev, fmt):
+    # experts at explicit offsets with unowned rows between them: the token
+    # quantiser leaves those rows alone, and the weight gradients read only
+    # each expert's own rows
+    lens = np.array([40, 0, 70, 33], np.int64)
+    offs = np.array([5, 60, 60, 140, 173], np.int64)      # rows 0-4, 45-59, 130-139 unowned
+    M, G, K, N = 180, len(lens), 64, 48
+    a = synth.randn_bf16((M, K), seed=150, std=K ** -0.5, device=dev)
+    dy = synth.randn_bf16((M, N), seed=151, std=1e-2, device=dev)
+    owned = np.concatenate([np.arange(offs[g], offs[g] + lens[g]) for g in range(G)])
+    lens_d, offs_d = dev_i64(lens, dev), dev_i64(offs, dev)
+    if fmt == ptm.PT_FP8_E4M3:
+        aq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        dq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        f = [torch.empty((1,), dtype=torch.float32, device=dev) for _ in range(4)]
+        ptm.pt_fp8_quantize(a, aq, f[0], f[1], 1, M, K)
+        ptm.pt_fp8_quantize(dy, dq, f[2], f[3], 1, M, N)
+        as_, ds = f[1], f[3]
+    else:
+        cols = lambda c: c if fmt == ptm.PT_MXFP8_E4M3 else c // 2
+        aq = torch.full((M, cols(K)), 0xEE, dtype=torch.uint8, device=dev)
+        dq = torch.full((M, cols(N)), 0xEE, dtype=torch.uint8, device=dev)
+        as_ = torch.zeros((M // 32 + G, K), dtype=torch.uint8, device=dev)
+        ds = torch.zeros((M // 32 + G, N), dtype=torch.uint8, device=dev)
+        ptm.pt_mx_quantize_tokens(a, lens_d, offs_d, aq, as_, G, M, K, fmt)
+        ptm.pt_mx_quantize_tokens(dy, lens_d, offs_d, dq, ds, G, M, N, fmt)
+        torch.cuda.synchronize()
+        unowned = np.setdiff1d(np.arange(M), owned)
+        assert (u8(aq)[unowned] == 0xEE).all() and (u8(dq)[unowned] == 0xEE).all()
+        # the owned rows equal the quantisation of the compacted batch
+        raq, ras, _ = orc.mx_quantize_tokens(bits16(a)[owned], lens, fmt)
+        assert (u8(aq)[owned] == raq).all()
+    mg = torch.full((G, K, N), 0.25, dtype=torch.float32, device=dev)
+    ws = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, fmt),), dtype=torch.uint8,
+                     device=dev)
+    ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, lens_d, offs_d, G, M, N, K, fmt, 0, 1, workspace=ws)
+    torch.cuda.synchronize()
+    got = mg.cpu().numpy().astype(np.float64) - 0.25
+    gs, ks = np.repeat(np.arange(G), K), np.tile(np.arange(K), G)
+    if fmt == ptm.PT_FP8_E4M3:
+        D = orc.fp8_wgrad_rows(u8(aq)[owned], as_.cpu().numpy()[0], u8(dq)[owned], ds.cpu().numpy()[0], lens, N, K,
+                               gs, ks).reshape(G, K, N)
+    else:
+        raq, ras, _ = orc.mx_quantize_tokens(bits16(a)[owned], lens, fmt)
+        rdq, rds, _ = orc.mx_quantize_tokens(bits16(dy)[owned], lens, fmt)
+        av = orc.mx_dequantize_tokens(raq, ras, lens, fmt)
+        dv = orc.mx_dequantize_tokens(rdq, rds, lens, fmt)
+        co = np.concatenate([[0], np.cumsum(lens)])
+        D = np.stack([av[co[g]:co[g + 1]].T @ dv[co[g]:co[g + 1]] for g in range(G)])
+    for g in range(G):
+        if lens[g] == 0:
+            assert (got[g] == 0).all()
+        else:
+            assert floored_rel_err(got[g], D[g]) <= BF16_TOL, g
