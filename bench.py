@@ -637,6 +637,15 @@ def main():
         if want is None or "cfg0" in want:
             log("per_config: tiny")
             per["cfg0_tiny_bf16_fwd"] = bench_cfg0(dev, stream, 50)
+        if want is None or "clamp" in want:
+            log("per_config: headline with the clamped SwiGLU")
+            _, per_c = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
+                fc1["a"], None, fc1["b"], None, fc1["out"], None, fc1["lens_d"], None, fc1["G"], fc1["M"], fc1["N"],
+                fc1["K"], ptm.PT_BF16, 0, ptm.PT_EPI_SWIGLU, workspace=WS[0], stream=stream, swiglu_limit=10.0),
+                iters, 3, stream)
+            per["fc1_bf16_swiglu_clamped"] = summary(
+                "BF16 FC1 + SwiGLU clamped at swiglu_limit 10, 256 experts, M=49152, K=N=4096", "bf16",
+                fc1["flops"], fc1["nbytes"], per_c)
         if want is None or "cfg2" in want:
             log("per_config: dgrad / wgrad")
             per["cfg2_bf16_dgrad"], per["cfg2_bf16_wgrad"] = bench_cfg2(dev, stream, iters, fc1)
