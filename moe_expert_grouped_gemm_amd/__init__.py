@@ -23,7 +23,7 @@ __all__ = [
     "PT_OP_FWD", "PT_OP_DGRAD", "PT_OP_WGRAD",
     "load", "lib_path", "PtggError",
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu",
-    "pt_grouped_gemm_wgrad",
+    "pt_grouped_gemm_wgrad", "pt_grouped_gemm_fwd_swiglu_save",
     "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts", "expert_addresses",
     "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning", "PT_CONFIG_RULES", "PT_CONFIG_TUNE",
@@ -38,6 +38,7 @@ PT_CONFIG_RULES, PT_CONFIG_TUNE = -1, -2
 
 EXPORTS = (
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",
+    "pt_grouped_gemm_fwd_swiglu_save",
     "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts",
     "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning",
@@ -87,6 +88,8 @@ def load(require_gpu: bool = True):
     L.pt_fp8_quantize_rows.restype = i32
     L.pt_fp8_quantize_rows.argtypes = [p, p, p, p, i64, i64, p]
     L.pt_grouped_gemm_workspace_size.restype = sz
+    L.pt_grouped_gemm_fwd_swiglu_save.restype = i32
+    L.pt_grouped_gemm_fwd_swiglu_save.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i32, f32, p, sz, p]
     L.pt_stack_experts.restype = i32
     L.pt_stack_experts.argtypes = [p, p, i64, i64, i64, i32, p, sz, p]
     L.pt_mx_quantize_experts.restype = i32
@@ -153,6 +156,14 @@ def pt_grouped_gemm_dgrad(dy, dy_scale, b, b_scale, dx, group_lens, group_offs,
         _ptr(dy), _ptr(dy_scale), _ptr(b), _ptr(b_scale), _ptr(dx),
         _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_b,
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def pt_grouped_gemm_fwd_swiglu_save(a, b, h, c, group_lens, group_offs, G, M, N, K, trans_b,
+                                    workspace=None, stream=None, swiglu_limit=0.0):
+    L = load()
+    _check("pt_grouped_gemm_fwd_swiglu_save", L.pt_grouped_gemm_fwd_swiglu_save(
+        _ptr(a), _ptr(b), _ptr(h), _ptr(c), _ptr(group_lens), _ptr(group_offs), G, M, N, K, trans_b,
+        swiglu_limit, _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def pt_grouped_gemm_dgrad_swiglu(dy, b, c_saved, dc, group_lens, group_offs,

@@ -416,6 +416,50 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
     });
 }
 
+int pt_grouped_gemm_fwd_swiglu_save(const void *a, const void *b, void *h, void *c, const int64_t *group_lens,
+                                    const int64_t *group_offs, int64_t G, int64_t M, int64_t N, int64_t K, int trans_b,
+                                    float swiglu_limit, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (swiglu_limit != swiglu_limit) return PT_ERR_INVALID_ARG;   // NaN
+    int st = check_groups(group_lens, G, M);
+    if (st) return st;
+    if (N < 1 || K < 1 || N > INT32_MAX / 4 || K > INT32_MAX / 4) return PT_ERR_INVALID_ARG;
+    if (M > 0 && (!a || !b || !h || !c)) return PT_ERR_INVALID_ARG;
+    if (trans_b != 0 && trans_b != 1) return PT_ERR_INVALID_ARG;
+    if (N % 16 || K % 8) return PT_ERR_UNSUPPORTED;
+    if (!fits31(M * K * 2) || !fits31(N * K * 2) || !fits31(M * N * 2)) return PT_ERR_UNSUPPORTED;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(h) || !aligned16(c)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    Bf16Params p = {};
+    p.swiglu_limit = swiglu_clamp(swiglu_limit);
+    p.a = (const uint16_t *)a;
+    p.b = (const uint16_t *)b;
+    p.out = h;
+    p.save = (uint16_t *)c;
+    p.ldsave = (int)N;
+    p.lens = group_lens;
+    p.offs = group_offs;
+    p.err = error_word(workspace, workspace_bytes);
+    p.G = (int)G;
+    p.M = M;
+    p.Kred = (int)K;
+    p.Nout = (int)N;
+    p.lda = (int)K;
+    p.ldb = trans_b ? (int)K : (int)N;
+    p.b_gstride = N * K;
+    p.ldo = (int)(N / 2);
+    p.tilesN = (int)((N / 2 + bf16_tile_n() / 2 - 1) / (bf16_tile_n() / 2));
+    p.sched = queue_words(workspace, workspace_bytes);
+    if (M == 0) return PT_OK;
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t *queues = p.sched;
+    const TuneKey key = tune_key(PT_OP_FWD, PT_BF16, kEpiSwigluSave, trans_b, G, M, N, K);
+    return configured(key, cfg_mask(queues != nullptr, false), true, s, [&](int cfg) {
+        p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+        return queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdKContig : kFwdNContig, kEpiSwigluSave, s); });
+    });
+}
+
 int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_saved, void *dc,
                                  const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
                                  int64_t N, int64_t K, int trans_b, float swiglu_limit, void *workspace,

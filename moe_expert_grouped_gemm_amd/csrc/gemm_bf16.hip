@@ -925,7 +925,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 }
         } else {
             store_tile_lds_w<EPI, 4, MI, NJ>(acc, smem, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wrow0, wn,
-                                             p.swiglu_limit, p.aux, p.ldaux);
+                                             p.swiglu_limit, p.aux, p.ldaux, p.save, p.ldsave);
         }
         barrier();
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
@@ -988,10 +988,16 @@ hipError_t launch_queue_reset(uint32_t *sched, hipStream_t s)
 
 hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s)
 {
-    // the SwiGLU backward epilogue exists for the 256 x 256 kernel only
+    // the SwiGLU backward epilogue and the SwiGLU that keeps its input exist
+    // for the 256 x 256 kernel only
     if (epi == kEpiDSwiglu) {
         if (kind == kFwdKContig) return launch_wide_ring<kFwdKContig, kEpiDSwiglu>(p, s);
         if (kind == kFwdNContig) return launch_wide_ring<kFwdNContig, kEpiDSwiglu>(p, s);
+        return hipErrorInvalidValue;
+    }
+    if (epi == kEpiSwigluSave) {
+        if (kind == kFwdKContig) return launch_wide_ring<kFwdKContig, kEpiSwigluSave>(p, s);
+        if (kind == kFwdNContig) return launch_wide_ring<kFwdNContig, kEpiSwigluSave>(p, s);
         return hipErrorInvalidValue;
     }
     // the 256 x 256 kernel, or the 128 x 256 one (bit-identical results)

@@ -30,15 +30,18 @@ struct Bf16Params {
     uint32_t *sched;   // tile-queue counters in the workspace, or null (static order)
     const uint16_t *aux; // SwiGLU backward: the FC1 output [gate | up] the epilogue reads
     int ldaux;           // its row stride (elements)
-    int narrow;          // 1: the 128 x 256 kernel (not for kEpiDSwiglu), 0: the 256 x 256 one
+    int narrow;          // 1: the 128 x 256 kernel (not for kEpiDSwiglu / kEpiSwigluSave), 0: the 256 x 256 one
     float swiglu_limit;  // SwiGLU clamp (forward and backward epilogues); +inf for none
+    uint16_t *save;      // kEpiSwigluSave: the GEMM output [M, Nout] bf16 (gate | up) kept for the backward
+    int ldsave;          // its row stride (elements)
 };
 
 enum Bf16Kind { kFwdKContig = 0, kFwdNContig = 1, kWgrad = 2 };
 // kEpiDSwiglu: the SwiGLU backward on a data gradient dH (see store_tile_lds_w).
-enum Epi { kEpiNone = 0, kEpiSwiglu = 1, kEpiSwigluMxfp4 = 2, kEpiDSwiglu = 3 };
+// kEpiSwigluSave: the SwiGLU output, and the bf16 GEMM output itself to Bf16Params::save.
+enum Epi { kEpiNone = 0, kEpiSwiglu = 1, kEpiSwigluMxfp4 = 2, kEpiDSwiglu = 3, kEpiSwigluSave = 4 };
 // Does the epilogue pair gate and up columns of one tile?
-constexpr bool epi_glu(int epi) { return epi == kEpiSwiglu || epi == kEpiSwigluMxfp4; }
+constexpr bool epi_glu(int epi) { return epi == kEpiSwiglu || epi == kEpiSwigluMxfp4 || epi == kEpiSwigluSave; }
 
 hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s);
 int bf16_tile_m(int narrow);

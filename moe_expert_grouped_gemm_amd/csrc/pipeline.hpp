@@ -247,7 +247,8 @@ template <int EPI, int NWM, int MI, int NJ>
 __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], uint8_t *smem, void *out,
                                                  uint8_t *out_scale, int ldo, int Nout, int64_t row0, int m0,
                                                  int rows, int nt, int wrow0, int wn, float lim,
-                                                 const uint16_t *aux = nullptr, int ldaux = 0)
+                                                 const uint16_t *aux = nullptr, int ldaux = 0,
+                                                 uint16_t *save = nullptr, int ldsave = 0)
 {
     constexpr int TR = 64 * NWM;                           // tile rows
     constexpr int OC = epi_glu(EPI) ? BN / 2 : BN;         // output columns of the tile
@@ -362,6 +363,35 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
             }
             *(uintx4 *)(o + (int64_t)(m0 + r) * ldo + (j0 >> 1)) = uintx4{packed[0], packed[1], packed[2], packed[3]};
             os[(int64_t)(m0 + r) * (Nout / 64) + (j0 >> 5)] = (uint8_t)E;
+        }
+    }
+    if (EPI == kEpiSwigluSave) {
+        // the GEMM output itself, for the backward: the gate half, then the
+        // up half, each through the same LDS tile as bf16 (column j of the
+        // tile is gate column nt * OC + j, up column Nout / 2 + nt * OC + j)
+        constexpr int CPR = OC / 8;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            wait_lgkm0();
+            barrier();
+#pragma unroll
+            for (int bi = 0; bi < MI; ++bi)
+#pragma unroll
+                for (int q = 0; q < NJ / 2; ++q) {
+                    const int c = wn * NJ * 16 + q * 32 + (lane & 31);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        *(uint16_t *)(smem + row_of(bi, r) * RS + c * 2) =
+                            (uint16_t)bf16_rne(acc[bi][q + half * (NJ / 2)][r]);
+                }
+            __syncthreads();
+            uint16_t *o = save + row0 * ldsave + half * (Nout / 2);
+            for (int i = threadIdx.x; i < TR * CPR; i += NT) {
+                const int r = i / CPR, c = i % CPR;
+                const int col = nt * OC + c * 8;
+                if (m0 + r < rows && col < ncols)
+                    *(uintx4 *)(o + (int64_t)(m0 + r) * ldsave + col) = *(const uintx4 *)(smem + r * RS + c * 16);
+            }
         }
     }
     // The next tile's loads may overwrite the LDS tile once every wave has
