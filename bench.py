@@ -645,8 +645,8 @@ def main():
                 iters, 3, stream)
             c_keep = torch.empty((fc1["M"], fc1["N"]), dtype=torch.bfloat16, device=dev)
             _, per_s = time_launches(lambda: ptm.pt_grouped_gemm_fwd_swiglu_save(
-                fc1["a"], fc1["b"], fc1["out"], c_keep, fc1["lens_d"], None, fc1["G"], fc1["M"], fc1["N"], fc1["K"], 0,
-                workspace=WS[0], stream=stream, swiglu_limit=10.0), iters, 3, stream)
+                fc1["a"], None, fc1["b"], None, fc1["out"], c_keep, fc1["lens_d"], None, fc1["G"], fc1["M"], fc1["N"],
+                fc1["K"], ptm.PT_BF16, 0, workspace=WS[0], stream=stream, swiglu_limit=10.0), iters, 3, stream)
             per["fc1_bf16_swiglu_save"] = summary(
                 "BF16 FC1 + clamped SwiGLU that also stores FC1's output [49152, 4096] for the backward", "bf16",
                 fc1["flops"], fc1["nbytes"] + fc1["M"] * fc1["N"] * 2, per_s)

@@ -183,18 +183,23 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale,
  * FC1 with the fused SwiGLU epilogue that also keeps FC1's output for the
  * backward (the training form of the Primus-Turbo README's fused grouped MLP,
  * "What's New": SwiGLU folded into the grouped GEMM; the SwiGLU backward,
- * pt_grouped_gemm_dgrad_swiglu, reads that output).  BF16 only:
- *     c[r, :] = bf16(A[r, :] B_g)                  [M, N]  (= PT_EPI_NONE's output)
+ * pt_grouped_gemm_dgrad_swiglu, reads that output):
+ *     c[r, :] = bf16(C[r, :])                        [M, N]  (= PT_EPI_NONE's output)
  *     h[r, j] = bf16(silu(C[r, j]) * C[r, N/2 + j])  [M, N/2] (= PT_EPI_SWIGLU's output,
  *               with the same swiglu_limit clamp)
- * both from one pass over the operands; each is bit-identical to the call
- * with that single epilogue.  a, b, trans_b, lengths and workspace as for
- * pt_grouped_gemm_fwd.  Requirements: N % 16 == 0, K % 8 == 0; a, b, h and c
- * 16-byte aligned.  Runs on the 256 x 256 kernel in every configuration.
+ * both from one pass over the operands, C = A B_g as pt_grouped_gemm_fwd
+ * computes it for the dtype (BF16, MXFP8, MXFP4, FP8 with tensor or row
+ * factors; the scale arguments, dtype, trans_b, lengths and workspace as
+ * there); each output is bit-identical to the call with that single
+ * epilogue.  Requirements: N % 16 == 0, K % 8 == 0 and those of the dtype;
+ * a, b, h and c 16-byte aligned.  Runs on the 256 x 256 kernels in every
+ * configuration, so MXFP4 with K % 256 != 0 needs the workspace that holds
+ * the scale copies (else PT_ERR_UNSUPPORTED).
  */
-int pt_grouped_gemm_fwd_swiglu_save(const void *a, const void *b, void *h, void *c,
+int pt_grouped_gemm_fwd_swiglu_save(const void *a, const uint8_t *a_scale,
+                                    const void *b, const uint8_t *b_scale, void *h, void *c,
                                     const int64_t *group_lens, const int64_t *group_offs,
-                                    int64_t G, int64_t M, int64_t N, int64_t K, int trans_b,
+                                    int64_t G, int64_t M, int64_t N, int64_t K, int dtype, int trans_b,
                                     float swiglu_limit, void *workspace, size_t workspace_bytes, void *stream);
 
 /*

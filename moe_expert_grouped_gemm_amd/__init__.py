@@ -89,7 +89,7 @@ def load(require_gpu: bool = True):
     L.pt_fp8_quantize_rows.argtypes = [p, p, p, p, i64, i64, p]
     L.pt_grouped_gemm_workspace_size.restype = sz
     L.pt_grouped_gemm_fwd_swiglu_save.restype = i32
-    L.pt_grouped_gemm_fwd_swiglu_save.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i32, f32, p, sz, p]
+    L.pt_grouped_gemm_fwd_swiglu_save.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, f32, p, sz, p]
     L.pt_stack_experts.restype = i32
     L.pt_stack_experts.argtypes = [p, p, i64, i64, i64, i32, p, sz, p]
     L.pt_mx_quantize_experts.restype = i32
@@ -158,12 +158,12 @@ def pt_grouped_gemm_dgrad(dy, dy_scale, b, b_scale, dx, group_lens, group_offs,
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
-def pt_grouped_gemm_fwd_swiglu_save(a, b, h, c, group_lens, group_offs, G, M, N, K, trans_b,
+def pt_grouped_gemm_fwd_swiglu_save(a, a_scale, b, b_scale, h, c, group_lens, group_offs, G, M, N, K, dtype, trans_b,
                                     workspace=None, stream=None, swiglu_limit=0.0):
     L = load()
     _check("pt_grouped_gemm_fwd_swiglu_save", L.pt_grouped_gemm_fwd_swiglu_save(
-        _ptr(a), _ptr(b), _ptr(h), _ptr(c), _ptr(group_lens), _ptr(group_offs), G, M, N, K, trans_b,
-        swiglu_limit, _ptr(workspace), _nbytes(workspace), _stream(stream)))
+        _ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), _ptr(h), _ptr(c), _ptr(group_lens), _ptr(group_offs),
+        G, M, N, K, dtype, trans_b, swiglu_limit, _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def pt_grouped_gemm_dgrad_swiglu(dy, b, c_saved, dc, group_lens, group_offs,

@@ -232,7 +232,7 @@ using namespace ptgg;
 static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale, void *out,
                    uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
                    int64_t N, int64_t K, int dtype, int ep, int64_t Nc, int64_t ldo, float swiglu_limit,
-                   void *workspace, size_t workspace_bytes, hipStream_t s)
+                   void *workspace, size_t workspace_bytes, hipStream_t s, uint16_t *save = nullptr)
 {
     const bool tensor_scales = dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE;
     if (N % 8) return PT_ERR_UNSUPPORTED;              // outputs leave in 16-byte chunks
@@ -243,6 +243,8 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
     if (!fits31(M * kb) || !fits31(N * kb) || !fits31(G * N * (K / 32) + 4)) return PT_ERR_UNSUPPORTED;
     MxParams p = {};
     p.swiglu_limit = swiglu_clamp(swiglu_limit);
+    p.save = save;
+    p.ldsave = (int)N;
     p.a = (const uint8_t *)a;
     p.as = a_scale;
     p.b = (const uint8_t *)b;
@@ -273,9 +275,12 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
     const bool swz = !tensor_scales && p.sched && mx_swz_possible(G, M, N, K, fmt) &&
                      workspace_bytes >= (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) +
                                                  mx_swz_b_bytes(G, N, K, fmt));
+    // the SwiGLU that keeps its input exists for the 256 x 256 kernel only,
+    // which E2M1 with K % 256 != 0 reaches through the scale copies alone
+    if (ep == kEpiSwigluSave && fmt == 1 && K % 256 && !swz) return PT_ERR_UNSUPPORTED;
     uint32_t *queues = p.sched;
     const TuneKey key = tune_key(op, dtype, ep, 0, G, M, N, K);
-    return configured(key, cfg_mask(queues != nullptr, !tensor_scales), true, s, [&](int cfg) {
+    return configured(key, cfg_mask(queues != nullptr, !tensor_scales && ep != kEpiSwigluSave), true, s, [&](int cfg) {
         p.narrow = (cfg & kCfgNarrow) != 0;
         p.sched = (cfg & kCfgStatic) ? nullptr : queues;
         p.sa = p.sb = nullptr;
@@ -416,9 +421,10 @@ int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b
     });
 }
 
-int pt_grouped_gemm_fwd_swiglu_save(const void *a, const void *b, void *h, void *c, const int64_t *group_lens,
-                                    const int64_t *group_offs, int64_t G, int64_t M, int64_t N, int64_t K, int trans_b,
-                                    float swiglu_limit, void *workspace, size_t workspace_bytes, void *stream)
+int pt_grouped_gemm_fwd_swiglu_save(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale,
+                                    void *h, void *c, const int64_t *group_lens, const int64_t *group_offs, int64_t G,
+                                    int64_t M, int64_t N, int64_t K, int dtype, int trans_b, float swiglu_limit,
+                                    void *workspace, size_t workspace_bytes, void *stream)
 {
     if (swiglu_limit != swiglu_limit) return PT_ERR_INVALID_ARG;   // NaN
     int st = check_groups(group_lens, G, M);
@@ -427,9 +433,18 @@ int pt_grouped_gemm_fwd_swiglu_save(const void *a, const void *b, void *h, void 
     if (M > 0 && (!a || !b || !h || !c)) return PT_ERR_INVALID_ARG;
     if (trans_b != 0 && trans_b != 1) return PT_ERR_INVALID_ARG;
     if (N % 16 || K % 8) return PT_ERR_UNSUPPORTED;
-    if (!fits31(M * K * 2) || !fits31(N * K * 2) || !fits31(M * N * 2)) return PT_ERR_UNSUPPORTED;
+    if (!fits31(M * N * 2)) return PT_ERR_UNSUPPORTED;
     if (!aligned16(a) || !aligned16(b) || !aligned16(h) || !aligned16(c)) return PT_ERR_MISALIGNED;
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE) {
+        if (!trans_b) return PT_ERR_UNSUPPORTED;           // K-contiguous codes
+        return mx_gemm(PT_OP_FWD, a, a_scale, b, b_scale, h, nullptr, group_lens, group_offs, G, M, N, K, dtype,
+                       kEpiSwigluSave, N / 2, N / 2, swiglu_limit, workspace, workspace_bytes, (hipStream_t)stream,
+                       (uint16_t *)c);
+    }
+    if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
+    if (a_scale || b_scale) return PT_ERR_INVALID_ARG;
+    if (!fits31(M * K * 2) || !fits31(N * K * 2)) return PT_ERR_UNSUPPORTED;
     Bf16Params p = {};
     p.swiglu_limit = swiglu_clamp(swiglu_limit);
     p.a = (const uint16_t *)a;

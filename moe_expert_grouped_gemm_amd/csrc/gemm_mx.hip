@@ -887,7 +887,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                     for (int bj = 0; bj < 4; ++bj) acc[bi][bj][r] *= fa * fb[bj];
                 }
         }
-        store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn, p.swiglu_limit);
+        store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn, p.swiglu_limit, p.save,
+                               p.ldsave);
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
         par ^= 1;
     }
@@ -918,6 +919,7 @@ hipError_t launch_wide_epi(const MxParams &p, int epi, hipStream_t s)
 {
     if (epi == kEpiSwiglu) return launch_wide<FMT, kEpiSwiglu, WSC>(p, s);
     if (epi == kEpiSwigluMxfp4) return launch_wide<FMT, kEpiSwigluMxfp4, WSC>(p, s);
+    if (epi == kEpiSwigluSave) return launch_wide<FMT, kEpiSwigluSave, WSC>(p, s);
     return launch_wide<FMT, kEpiNone, WSC>(p, s);
 }
 
@@ -944,6 +946,7 @@ hipError_t launch_one(const MxParams &p, hipStream_t s)
 template <int FMT, int SCM>
 hipError_t launch_epi(const MxParams &p, int epi, hipStream_t s)
 {
+    if (epi == kEpiSwigluSave) return hipErrorInvalidValue;      // the 256 x 256 kernel only
     if (epi == kEpiSwiglu) return launch_one<FMT, kEpiSwiglu, SCM>(p, s);
     if (epi == kEpiSwigluMxfp4) return launch_one<FMT, kEpiSwigluMxfp4, SCM>(p, s);
     return launch_one<FMT, kEpiNone, SCM>(p, s);

@@ -70,6 +70,8 @@ struct MxParams {
     int sf_rows;             // sfa / sfb hold one scale per row of A [M] and per row of B [G, N]
     int narrow;              // 1: the 128 x 256 kernel on row-major scales (MX only), 0: rules
     float swiglu_limit;      // SwiGLU clamp; +inf for none
+    uint16_t *save;          // kEpiSwigluSave: the GEMM output [M, N] bf16 (gate | up)
+    int ldsave;              // its row stride (elements)
 };
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);

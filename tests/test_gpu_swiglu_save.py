@@ -37,8 +37,8 @@ def test_save_equals_single_epilogues(dev, trans_b, sched, limit):
     ws = make_ws(dev, sched)
     hb, h = guarded(dev, M, N // 2)
     cb, c = guarded(dev, M, N)
-    ptm.pt_grouped_gemm_fwd_swiglu_save(a, b, h, c, lens_d, None, G, M, N, K, trans_b, workspace=ws,
-                                        swiglu_limit=limit)
+    ptm.pt_grouped_gemm_fwd_swiglu_save(a, None, b, None, h, c, lens_d, None, G, M, N, K, ptm.PT_BF16, trans_b,
+                                        workspace=ws, swiglu_limit=limit)
     c_ref = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     h_ref = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
     ptm.pt_grouped_gemm_fwd(a, None, b, None, c_ref, None, lens_d, None, G, M, N, K, ptm.PT_BF16, trans_b,
@@ -61,14 +61,17 @@ def test_save_refusals_and_empty_batch(dev):
     b = torch.zeros((1, 64, 64), dtype=torch.bfloat16, device=dev)
     h = torch.zeros((8, 32), dtype=torch.bfloat16, device=dev)
     c = torch.zeros((8, 64), dtype=torch.bfloat16, device=dev)
-    args = lambda N=64, tb=0, cc=c.data_ptr(): (a.data_ptr(), b.data_ptr(), h.data_ptr(), cc, lens.data_ptr(), None,
-                                                 1, 8, N, 64, tb, 0.0, None, 0, st)
+    args = lambda N=64, tb=0, cc=c.data_ptr(), dt=ptm.PT_BF16: (a.data_ptr(), None, b.data_ptr(), None, h.data_ptr(),
+                                                                cc, lens.data_ptr(), None, 1, 8, N, 64, dt, tb, 0.0,
+                                                                None, 0, st)
     assert L.pt_grouped_gemm_fwd_swiglu_save(*args(cc=None)) == 1            # no place for FC1's output
     assert L.pt_grouped_gemm_fwd_swiglu_save(*args(N=56)) == 2               # N % 16
     assert L.pt_grouped_gemm_fwd_swiglu_save(*args(tb=2)) == 1
     assert L.pt_grouped_gemm_fwd_swiglu_save(*args(cc=c.data_ptr() + 2)) == 3
+    assert L.pt_grouped_gemm_fwd_swiglu_save(*args(dt=ptm.PT_MXFP8_E4M3, tb=0)) == 2      # MX codes need [G, N, K]
+    assert L.pt_grouped_gemm_fwd_swiglu_save(*args(dt=9)) == 2
     zl = dev_i64(np.zeros(3, np.int64), dev)
-    ptm.pt_grouped_gemm_fwd_swiglu_save(a[:0], b, h[:0], c[:0], zl, None, 3, 0, 64, 64, 0)
+    ptm.pt_grouped_gemm_fwd_swiglu_save(a[:0], None, b, None, h[:0], c[:0], zl, None, 3, 0, 64, 64, ptm.PT_BF16, 0)
     torch.cuda.synchronize()
 
 
@@ -81,7 +84,7 @@ def test_save_mlp_shape_sampled(orc, dev):
     b = synth.randn_bf16((G, K, N), seed=1101, std=K ** -0.5, device=dev)
     h = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    ptm.pt_grouped_gemm_fwd_swiglu_save(a, b, h, c, dev_i64(lens, dev), None, G, M, N, K, 0,
+    ptm.pt_grouped_gemm_fwd_swiglu_save(a, None, b, None, h, c, dev_i64(lens, dev), None, G, M, N, K, ptm.PT_BF16, 0,
                                         workspace=make_ws(dev, "queue"))
     torch.cuda.synchronize()
     offs = synth.offsets(lens)
@@ -97,3 +100,40 @@ def test_save_mlp_shape_sampled(orc, dev):
     idx = torch.as_tensor(rows, device=dev)
     assert floored_rel_err(bf16_values(bits16(c[idx])), ref["exact"]) <= BF16_TOL
     assert floored_rel_err(bf16_values(bits16(h[idx])), refh["exact"]) <= BF16_TOL
+
+
+
+@pytest.mark.parametrize("dtype,name", [(ptm.PT_MXFP8_E4M3, "e4m3"), (ptm.PT_MXFP4_E2M1, "e2m1"),
+                                        (ptm.PT_FP8_E4M3, "fp8"), (ptm.PT_FP8_E4M3_ROWWISE, "fp8rows")],
+                         ids=["mxfp8", "mxfp4", "fp8", "fp8_rowwise"])
+@pytest.mark.parametrize("sched", ["static", "swz"])
+def test_save_low_precision_equals_single_epilogues(dev, dtype, name, sched):
+    lens = np.array([0, 1, 130, 0, 257, 64, 33], np.int64)
+    M, G, K, N = int(lens.sum()), len(lens), 512, 256
+    print(f"swiglu save dtype={name} sched={sched}", flush=True)
+    if dtype in (ptm.PT_MXFP8_E4M3, ptm.PT_MXFP4_E2M1):
+        aq, as_ = synth.random_mx_codes(M, K, name, seed=162, device=dev, scale_lo=122, scale_hi=125)
+        bq, bs = synth.random_mx_codes(G * N, K, name, seed=163, device=dev, scale_lo=116, scale_hi=119)
+    else:
+        g = torch.Generator(device=dev)
+        g.manual_seed(164)
+        aq = torch.randint(0, 126, (M, K), generator=g, device=dev, dtype=torch.int32).to(torch.uint8)
+        bq = torch.randint(0, 126, (G * N, K), generator=g, device=dev, dtype=torch.int32).to(torch.uint8)
+        rows_a, rows_b = (M, G * N) if dtype == ptm.PT_FP8_E4M3_ROWWISE else (1, G)
+        as_ = torch.rand((rows_a,), generator=g, device=dev).mul_(1e-2).add_(1e-3)
+        bs = torch.rand((rows_b,), generator=g, device=dev).mul_(1e-2).add_(1e-3)
+    ws = make_ws(dev, sched, G, M, N, K, dtype if dtype in (ptm.PT_MXFP8_E4M3, ptm.PT_MXFP4_E2M1) else ptm.PT_BF16)
+    lens_d = dev_i64(lens, dev)
+    h = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ptm.pt_grouped_gemm_fwd_swiglu_save(aq, as_, bq, bs, h, c, lens_d, None, G, M, N, K, dtype, 1, workspace=ws,
+                                        swiglu_limit=4.0)
+    c_ref = torch.empty_like(c)
+    h_ref = torch.empty_like(h)
+    ptm.pt_grouped_gemm_fwd(aq, as_, bq, bs, c_ref, None, lens_d, None, G, M, N, K, dtype, 1, ptm.PT_EPI_NONE,
+                            workspace=ws)
+    ptm.pt_grouped_gemm_fwd(aq, as_, bq, bs, h_ref, None, lens_d, None, G, M, N, K, dtype, 1, ptm.PT_EPI_SWIGLU,
+                            workspace=ws, swiglu_limit=4.0)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16))
+    assert torch.equal(h.view(torch.int16), h_ref.view(torch.int16))
