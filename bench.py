@@ -8,6 +8,10 @@ hidden K = 4096, N = 4096 ([gate | up] for intermediate 2048), weights
 useful FLOPs (2 * sum(group_lens) * K * N per step).  A step is one call of
 pt_grouped_gemm_fwd with inputs resident in HBM.
 
+Every `per_config` launch is timed after a 512 MiB write that flushes the
+MALL (outside the launch's event pair); the headline is timed back to back
+and reported flushed as well (`kernel_ms_median_cache_flushed`).
+
 `per_config` adds the other workloads (measured the same way, not part of
 `value`): the tiny 4-expert case, BF16 dgrad and wgrad into an fp32
 main_grad at the same shape, MXFP8 forward and its quantise kernel at a
@@ -67,19 +71,31 @@ def measured_traffic(kernel_key: str):
     return ent.get("bytes_per_launch")
 
 
-def time_launches(fn, steps, warmup, stream):
+FLUSH_BYTES = 512 << 20       # twice the 256 MB MALL (the last-level cache in front of HBM)
+FLUSH = [None]
+
+
+def time_launches(fn, steps, warmup, stream, flush=True):
     """Warm up, then time exactly `steps` calls: wall clock between two
     device synchronisations, and each launch between HIP events on the
-    stream the kernels run on."""
+    stream the kernels run on.  With `flush`, a 512 MiB buffer is written on
+    that stream before every timed call, outside its event pair, so each
+    call starts with caches holding none of its operands (the wall clock
+    then includes the flushes)."""
     for _ in range(warmup):
         fn()
+    if flush and FLUSH[0] is None:
+        FLUSH[0] = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=stream.device)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for s, e in evs:
-        s.record(stream)
-        fn()
-        e.record(stream)
+    with torch.cuda.stream(stream):
+        for i, (s, e) in enumerate(evs):
+            if flush:
+                FLUSH[0].fill_(i & 0xFF)
+            s.record(stream)
+            fn()
+            e.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     per = np.array([s.elapsed_time(e) for s, e in evs])
@@ -189,11 +205,14 @@ def bench_fc1(dev, stream, steps, warmup):
         ptm.pt_grouped_gemm_fwd(a, None, b, None, out, None, lens_d, None, G, M, N, K,
                                 ptm.PT_BF16, 0, ptm.PT_EPI_SWIGLU, workspace=WS[0], stream=stream)
 
-    ms_step, per = time_launches(step, steps, warmup, stream)
+    # back to back, as a training step issues them (the 8.5 GB of weights
+    # dwarf every cache, so warm and cold launches time alike: see per_flush)
+    ms_step, per = time_launches(step, steps, warmup, stream, flush=False)
+    _, per_flush = time_launches(step, max(5, min(steps, 20)), 1, stream, flush=True)
     flops = 2.0 * M * K * N
     nbytes = bytes_weights(lens, K * N * 2) + M * K * 2 + M * (N // 2) * 2
     return dict(lens=lens, G=G, M=M, K=K, N=N, a=a, b=b, out=out, lens_d=lens_d,
-                ms_step=ms_step, per=per, flops=flops, nbytes=nbytes)
+                ms_step=ms_step, per=per, per_flush=per_flush, flops=flops, nbytes=nbytes)
 
 
 def bench_cfg0(dev, stream, iters):
@@ -206,6 +225,9 @@ def bench_cfg0(dev, stream, iters):
     _, per = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
         a, None, b, None, out, None, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, ptm.PT_EPI_NONE,
         workspace=WS[0], stream=stream), iters, 10, stream)
+    _, per_warm = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
+        a, None, b, None, out, None, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, ptm.PT_EPI_NONE,
+        workspace=WS[0], stream=stream), iters, 10, stream, flush=False)
     # with tuning on: the first call times the configurations, the rest use the choice
     ptm.pt_clear_gemm_tuning()
     ptm.pt_set_gemm_config(ptm.PT_CONFIG_TUNE)
@@ -220,7 +242,8 @@ def bench_cfg0(dev, stream, iters):
     flops = 2.0 * M * K * N
     nbytes = bytes_weights(lens, K * N * 2) + M * K * 2 + M * N * 2
     return summary("tiny BF16 fwd, 4 experts, M=256, K=128, N=256", "bf16", flops, nbytes, per,
-                   {"tuned_config": chosen, "tuned_ms_median": round(float(np.median(per_t)), 4)})
+                   {"tuned_config": chosen, "tuned_ms_median": round(float(np.median(per_t)), 4),
+                    "warm_ms_median": round(float(np.median(per_warm)), 4)})
 
 
 def bench_cfg2(dev, stream, iters, fc1):
@@ -597,7 +620,7 @@ def main():
         n = args.copy_probe_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        _, per = time_launches(lambda: dst.copy_(src), args.steps, args.warmup, stream)
+        _, per = time_launches(lambda: dst.copy_(src), args.steps, args.warmup, stream, flush=False)
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
                           "ms_mean": float(np.mean(per)), "gbs": 2 * n / (np.mean(per) * 1e-3) / 1e9}))
         return
@@ -623,6 +646,7 @@ def main():
                    "empty_experts": int((lens == 0).sum())},
         "pct_mfma_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
         "kernel_ms_mean": round(kern_ms, 4),
+        "kernel_ms_median_cache_flushed": round(float(np.median(fc1["per_flush"])), 4),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

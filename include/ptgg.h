@@ -22,6 +22,9 @@
  *  - Row ranges: expert g owns rows [offs[g], offs[g] + group_lens[g]) of the
  *    row-indexed operands, where offs = group_offs (int64[G+1]) when given,
  *    else the exclusive prefix sum of group_lens computed on the device.
+ *    With group_offs the ranges must come in expert order without
+ *    overlapping (offs[g] + lens[g] <= offs[g + 1], offs[G] <= M); rows
+ *    between them belong to no expert.
  *    group_lens are int64, >= 0, and come from the router on the device; the
  *    host never reads them.  Experts with zero rows are allowed anywhere.
  *    Device code clamps every range into [0, M], so malformed lengths never
@@ -275,7 +278,7 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
 
 /*
  * OCP-MX quantisation of a bf16 matrix x [rows, cols], one block per 32
- * consecutive elements along the columns (axis = 1; the only axis served):
+ * consecutive elements along one axis:
  *   E = clamp(floor(log2(max|v|)) - emax + 127, 0, 254)   (E = 0 for an
  *       all-zero block; emax = 8 for E4M3, 2 for E2M1)
  *   code_i = nearest element-format value to v_i / 2^(E-127), ties to even,
@@ -283,10 +286,21 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
  * (MX weight buffers of the PR page "[Megatron-LM] feat: add grouped gemm fp4
  * support, ...", section "Changes"; the Primus-Turbo README lists MXFP8 and
  * MXFP4 grouped GEMMs under "What's New".)
- *  q       E4M3: [rows, cols] bytes;  E2M1: [rows, cols/2] bytes (even column
- *          in the low nibble)
- *  scales  [rows, cols/32] E8M0 bytes
- *  dtype   PT_MXFP8_E4M3 or PT_MXFP4_E2M1.  Requirements: cols % 32 == 0.
+ *  axis = 1: blocks of 32 consecutive columns of a row (the forward's
+ *          reduction-contiguous operands).
+ *    q       E4M3: [rows, cols] bytes;  E2M1: [rows, cols/2] bytes (even
+ *            column in the low nibble)
+ *    scales  [rows, cols/32] E8M0 bytes
+ *    Requirements: cols % 32 == 0.
+ *  axis = 0: blocks of 32 consecutive rows of a column.
+ *    q       E4M3: [rows, cols] bytes (x's layout);  E2M1: [rows/2, cols]
+ *            bytes, rows 2i and 2i + 1 of a column sharing byte (i, c), the
+ *            even row in the low nibble (pairs along the blocking axis, as
+ *            in the axis-1 layout of the transpose)
+ *    scales  [rows/32, cols] E8M0 bytes, 4-byte aligned
+ *    Requirements: rows % 32 == 0, cols % 8 == 0.
+ *  dtype   PT_MXFP8_E4M3 or PT_MXFP4_E2M1; another axis is PT_ERR_INVALID_ARG.
+ *  x and q 16-byte aligned.
  *  NaN/Inf inputs are outside the contract (no fault; results unspecified).
  */
 int pt_mx_quantize(const void *x, void *q, uint8_t *scales,
@@ -459,9 +473,14 @@ void pt_clear_gemm_tuning(void);
 /*
  * Sticky device error bits recorded in the first word of a workspace by the
  * grouped GEMM kernels (bit 0: a negative group length; bit 1: an expert
- * range outside [0, M] was clamped; bit 2: the lengths do not sum to M) and
- * by the expert-weight kernels (bit 3: an expert address was NULL or not
- * 16-byte aligned).
+ * range outside [0, M] was clamped; bit 2: without group_offs, the lengths
+ * do not sum to M; with group_offs, two experts' ranges overlap or come out
+ * of expert order, offs[g] + lens[g] > offs[g + 1], or offs[G] lies outside
+ * [0, M]) and by the expert-weight kernels (bit 3: an expert address was
+ * NULL or not 16-byte aligned).  Rows between experts' ranges that no
+ * expert owns (explicit offsets with gaps) are valid input and set no bit:
+ * the forward and data gradient leave them unwritten, the weight gradient
+ * and the token quantiser do not read them.
  * The caller zeroes the word before the calls it wants to check.  This call
  * synchronises `stream` and copies the word to *flags (host pointer).
  */

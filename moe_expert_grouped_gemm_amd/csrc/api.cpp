@@ -15,15 +15,16 @@ namespace ptgg {
 
 int device_cus()
 {
-    static int cus[64] = {0};
+    // per device; concurrent first calls store the same value
+    static std::atomic<int> cus[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return n;
 }
 
 namespace {
@@ -232,7 +233,8 @@ using namespace ptgg;
 static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale, void *out,
                    uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
                    int64_t N, int64_t K, int dtype, int ep, int64_t Nc, int64_t ldo, float swiglu_limit,
-                   void *workspace, size_t workspace_bytes, hipStream_t s, uint16_t *save = nullptr)
+                   void *workspace, size_t workspace_bytes, hipStream_t s, uint16_t *save = nullptr,
+                   bool timing = true)
 {
     const bool tensor_scales = dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE;
     if (N % 8) return PT_ERR_UNSUPPORTED;              // outputs leave in 16-byte chunks
@@ -280,7 +282,7 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
     if (ep == kEpiSwigluSave && fmt == 1 && K % 256 && !swz) return PT_ERR_UNSUPPORTED;
     uint32_t *queues = p.sched;
     const TuneKey key = tune_key(op, dtype, ep, 0, G, M, N, K);
-    return configured(key, cfg_mask(queues != nullptr, !tensor_scales && ep != kEpiSwigluSave), true, s, [&](int cfg) {
+    return configured(key, cfg_mask(queues != nullptr, !tensor_scales && ep != kEpiSwigluSave), timing, s, [&](int cfg) {
         p.narrow = (cfg & kCfgNarrow) != 0;
         p.sched = (cfg & kCfgStatic) ? nullptr : queues;
         p.sa = p.sb = nullptr;
@@ -297,12 +299,13 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
     });
 }
 
-extern "C" {
-
-int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale,
-                        void *out, uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs,
-                        int64_t G, int64_t M, int64_t N, int64_t K, int dtype, int trans_b, int epilogue,
-                        float swiglu_limit, void *workspace, size_t workspace_bytes, void *stream)
+// The grouped forward behind pt_grouped_gemm_fwd; `timing` false never
+// times configurations (tuning mode then takes a tuned choice or
+// configuration 0).
+static int grouped_fwd(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale, void *out,
+                       uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
+                       int64_t N, int64_t K, int dtype, int trans_b, int epilogue, float swiglu_limit,
+                       void *workspace, size_t workspace_bytes, void *stream, bool timing)
 {
     if (swiglu_limit != swiglu_limit) return PT_ERR_INVALID_ARG;   // NaN
     int st = check_groups(group_lens, G, M);
@@ -350,7 +353,7 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
         if (M == 0) return PT_OK;
         uint32_t *queues = p.sched;
         const TuneKey key = tune_key(PT_OP_FWD, dtype, ep, trans_b, G, M, N, K);
-        return configured(key, cfg_mask(queues != nullptr, true), true, s, [&](int cfg) {
+        return configured(key, cfg_mask(queues != nullptr, true), timing, s, [&](int cfg) {
             p.narrow = (cfg & kCfgNarrow) != 0;
             p.sched = (cfg & kCfgStatic) ? nullptr : queues;
             return queued(p.sched, s, [&] { return launch_bf16(p, trans_b ? kFwdKContig : kFwdNContig, ep, s); });
@@ -359,9 +362,20 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
     if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE) {
         if (!trans_b) return PT_ERR_UNSUPPORTED;           // K-contiguous codes
         return mx_gemm(PT_OP_FWD, a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype,
-                       ep, Nc, ldo, swiglu_limit, workspace, workspace_bytes, s);
+                       ep, Nc, ldo, swiglu_limit, workspace, workspace_bytes, s, nullptr, timing);
     }
     return PT_ERR_UNSUPPORTED;
+}
+
+extern "C" {
+
+int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale,
+                        void *out, uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs,
+                        int64_t G, int64_t M, int64_t N, int64_t K, int dtype, int trans_b, int epilogue,
+                        float swiglu_limit, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return grouped_fwd(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype, trans_b,
+                       epilogue, swiglu_limit, workspace, workspace_bytes, stream, true);
 }
 
 int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b, const uint8_t *b_scale, void *dx,
@@ -624,15 +638,21 @@ int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_
                    void *stream)
 {
     if (rows < 0 || cols < 0) return PT_ERR_INVALID_ARG;
-    if (axis != 1) return PT_ERR_UNSUPPORTED;
+    if (axis != 0 && axis != 1) return PT_ERR_INVALID_ARG;
     if (dtype != PT_MXFP8_E4M3 && dtype != PT_MXFP4_E2M1) return PT_ERR_UNSUPPORTED;
-    if (cols % 32) return PT_ERR_UNSUPPORTED;
+    if (axis == 1 && cols % 32) return PT_ERR_UNSUPPORTED;
+    if (axis == 0 && (rows % 32 || cols % 8)) return PT_ERR_UNSUPPORTED;
     if (rows == 0 || cols == 0) return PT_OK;
     if (!x || !q || !scales) return PT_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(q)) return PT_ERR_MISALIGNED;
+    if (axis == 0 && !aligned4(scales)) return PT_ERR_MISALIGNED;
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
-    return hip_status(launch_quantize((const uint16_t *)x, (uint8_t *)q, scales, rows, cols,
-                                      dtype == PT_MXFP8_E4M3 ? 0 : 1, (hipStream_t)stream));
+    const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
+    if (axis == 0)
+        return hip_status(launch_quantize_cols((const uint16_t *)x, (uint8_t *)q, scales, rows, cols, fmt,
+                                               (hipStream_t)stream));
+    return hip_status(launch_quantize((const uint16_t *)x, (uint8_t *)q, scales, rows, cols, fmt,
+                                      (hipStream_t)stream));
 }
 
 int pt_fp8_quantize(const void *x, void *q, float *amax, float *dequant, int64_t batch, int64_t rows, int64_t cols,

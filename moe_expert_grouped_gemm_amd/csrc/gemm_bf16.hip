@@ -407,14 +407,11 @@ hipError_t launch_one(const Bf16Params &p, hipStream_t s)
 {
     const int lds = NSTAGE * STAGE_BYTES + table_bytes(p.G);
     auto kern = gg_bf16_kernel<KIND, EPI, NSTAGE>;
-    static int configured_lds = 0;
-    if (configured_lds < lds) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        configured_lds = lds;
-    }
+    static LdsLimit lds_limit;
+    hipError_t e = lds_limit.ensure((const void *)kern, lds);
+    if (e != hipSuccess) return e;
     int occ = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, lds);
     if (e != hipSuccess) return e;
     if (occ < 1) occ = 1;
     int64_t tiles_max;
@@ -938,14 +935,11 @@ hipError_t launch_wide(const Bf16Params &p, hipStream_t s)
 {
     const int lds = wide_lds_bytes<EPI>() + table_bytes(p.G);
     auto kern = gg_bf16_wide_kernel<KIND, EPI, RING, WL>;
-    static int configured_lds = 0;
-    if (configured_lds < lds) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        configured_lds = lds;
-    }
+    static LdsLimit lds_limit;
+    hipError_t e = lds_limit.ensure((const void *)kern, lds);
+    if (e != hipSuccess) return e;
     int occ = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, WTHREADS, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, WTHREADS, lds);
     if (e != hipSuccess) return e;
     int64_t tiles_max;
     if (KIND == kWgrad)

@@ -899,14 +899,11 @@ hipError_t launch_wide(const MxParams &p, hipStream_t s)
 {
     const int lds = wide_lds_bytes<EPI>() + table_bytes(p.G);
     auto kern = gg_mx_wide_kernel<FMT, EPI, WSC>;
-    static int configured_lds = 0;
-    if (configured_lds < lds) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        configured_lds = lds;
-    }
+    static LdsLimit lds_limit;
+    hipError_t e = lds_limit.ensure((const void *)kern, lds);
+    if (e != hipSuccess) return e;
     int occ = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, WTHREADS, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, WTHREADS, lds);
     if (e != hipSuccess) return e;
     const int64_t tiles_max = (p.M / WBM + p.G) * (int64_t)p.tilesN;
     const int64_t grid = persistent_grid(occ, tiles_max);
@@ -928,14 +925,11 @@ hipError_t launch_one(const MxParams &p, hipStream_t s)
 {
     const int lds = NSTAGE * STAGE_BYTES + table_bytes(p.G);
     auto kern = gg_mx_kernel<FMT, EPI, SCM>;
-    static int configured_lds = 0;
-    if (configured_lds < lds) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        configured_lds = lds;
-    }
+    static LdsLimit lds_limit;
+    hipError_t e = lds_limit.ensure((const void *)kern, lds);
+    if (e != hipSuccess) return e;
     int occ = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, lds);
     if (e != hipSuccess) return e;
     const int64_t tiles_max = (p.M / BM + p.G) * (int64_t)p.tilesN;
     const int64_t grid = persistent_grid(occ, tiles_max);

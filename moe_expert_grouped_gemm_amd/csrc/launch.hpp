@@ -100,6 +100,11 @@ hipError_t launch_queue_reset(uint32_t *sched, hipStream_t s);
 
 hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales,
                            int64_t rows, int64_t cols, int fmt, hipStream_t s);
+// Blocks of 32 along the rows (axis 0): x [rows, cols] bf16 -> E4M3
+// [rows, cols] / E2M1 [rows/2, cols] codes (row pairs share a byte, even row
+// low) and [rows/32, cols] scales; rows % 32 == 0, cols % 4 == 0.
+hipError_t launch_quantize_cols(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t rows, int64_t cols, int fmt,
+                                hipStream_t s);
 // batch x [rows, cols] bf16 -> the quantisation of each matrix's transpose:
 // [cols, rows] codes (blocks of 32 along rows) and [cols, rows/32] scales.
 hipError_t launch_quantize_t(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t batch, int64_t rows,

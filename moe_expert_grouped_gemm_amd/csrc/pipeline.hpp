@@ -9,6 +9,9 @@
 // and column l%32 of its block).  Every stage of the ring carries 64 bytes of
 // each operand row along the reduction (32 BF16, 64 E4M3 or 128 E2M1 values).
 #pragma once
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -493,6 +496,30 @@ struct TileQueue {
         }
         __syncthreads();
         return __builtin_amdgcn_readfirstlane(*s_id);
+    }
+};
+
+// The dynamic-LDS limit granted to one kernel (hipFuncSetAttribute), kept
+// per device and raised only under a lock, so concurrent callers never
+// lower a limit another thread's launch relies on; the fast path is one
+// atomic load.
+constexpr int kMaxDevices = 64;
+struct LdsLimit {
+    std::atomic<int> granted[kMaxDevices] = {};
+    std::mutex mu;
+    hipError_t ensure(const void *kern, int lds)
+    {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kMaxDevices)
+            return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (granted[dev].load(std::memory_order_acquire) >= lds) return hipSuccess;
+        std::lock_guard<std::mutex> lock(mu);
+        if (granted[dev].load(std::memory_order_relaxed) >= lds) return hipSuccess;
+        e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e == hipSuccess) granted[dev].store(lds, std::memory_order_release);
+        return e;
     }
 };
 

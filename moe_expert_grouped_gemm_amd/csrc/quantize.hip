@@ -86,6 +86,70 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const uint16_t *_
     if (t < nquads) quantise8<FMT>(*(const uintx4 *)(x + t * 8), q, scales, t);
 }
 
+// Quantisation along the columns (axis 0): blocks of 32 consecutive rows of
+// one column.  x [R, C] bf16 -> E4M3 [R, C] codes (x's layout) or E2M1
+// [R/2, C] (rows 2i and 2i + 1 of a column share a byte, the even row in
+// the low nibble), scales [R/32, C].  One thread per 4 columns of a 32-row
+// block, so a wave reads 512 consecutive bytes of each of the block's rows
+// and stores whole words; the four columns' values stay in registers between
+// the amax and the encode, which takes the row quantiser's steps (ldexp by
+// 2^(127 - E), clamp to the grid maximum, hardware nearest-even convert).
+// R % 32 == 0, C % 4 == 0; grid (column groups, row blocks), the row blocks
+// strided by gridDim.y.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void mx_quantize_cols_kernel(const uint16_t *__restrict__ x,
+                                                                    uint8_t *__restrict__ q,
+                                                                    uint8_t *__restrict__ scales, int64_t R,
+                                                                    int64_t C)
+{
+    constexpr int EMAX = FMT == 0 ? 8 : 2;
+    constexpr float LIM = FMT == 0 ? 448.0f : 6.0f;
+    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;     // group of 4 columns
+    if (c >= C / 4) return;
+    for (int64_t blk = blockIdx.y; blk < R / 32; blk += gridDim.y) {
+        const int64_t r0 = blk * 32;
+        uintx2 h[32];
+        uint32_t am[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            h[i] = *(const uintx2 *)(x + (r0 + i) * C + 4 * c);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) am[k] = max(am[k], (h[i][k >> 1] >> (16 * (k & 1))) & 0x7FFFu);
+        }
+        int e[4];
+        uint32_t Ew = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t E = mx_scale_byte<EMAX>(am[k]);
+            e[k] = 127 - (int)E;
+            Ew |= E << (8 * k);
+        }
+        auto val = [&](int i, int k) {
+            const float f = __builtin_ldexpf(bf16_to_f32((h[i][k >> 1] >> (16 * (k & 1))) & 0xFFFFu), e[k]);
+            return __builtin_fminf(__builtin_fmaxf(f, -LIM), LIM);
+        };
+        if (FMT == 0) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(val(i, 0), val(i, 1), 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(val(i, 2), val(i, 3), w, true);
+                *(uint32_t *)(q + (r0 + i) * C + 4 * c) = (uint32_t)w;
+            }
+        } else {
+            // byte k of a word: column 4c + k, rows 2i (low nibble) and 2i + 1
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, val(2 * i, 0), val(2 * i + 1, 0), 1.0f, 0);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(2 * i, 1), val(2 * i + 1, 1), 1.0f, 1);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(2 * i, 2), val(2 * i + 1, 2), 1.0f, 2);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(2 * i, 3), val(2 * i + 1, 3), 1.0f, 3);
+                *(uint32_t *)(q + (r0 / 2 + i) * C + 4 * c) = w;
+            }
+        }
+        *(uint32_t *)(scales + blk * C + 4 * c) = Ew;
+    }
+}
+
 // Transposing quantiser: x_b [R, C] bf16 (row-major) -> q_b = the MX
 // quantisation of x_b^T, [C, R] codes with blocks of 32 consecutive rows of
 // x_b, and scales [C, R/32].  A workgroup moves a 64 x 64 tile through LDS:
@@ -588,6 +652,19 @@ hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales, int64
         hipLaunchKernelGGL(mx_quantize_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, scales, nquads);
     else
         hipLaunchKernelGGL(mx_quantize_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, scales, nquads);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_cols(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t rows, int64_t cols,
+                                int fmt, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const int64_t nb = rows / 32;
+    const dim3 grid((unsigned)((cols / 4 + kThreads - 1) / kThreads), (unsigned)(nb < 65535 ? nb : 65535));
+    if (fmt == 0)
+        hipLaunchKernelGGL(mx_quantize_cols_kernel<0>, grid, dim3(kThreads), 0, s, x, q, scales, rows, cols);
+    else
+        hipLaunchKernelGGL(mx_quantize_cols_kernel<1>, grid, dim3(kThreads), 0, s, x, q, scales, rows, cols);
     return hipGetLastError();
 }
 

@@ -263,6 +263,34 @@ def test_device_error_word_and_clamping(dev):
     assert ptm.pt_read_error_flags(ws) == 0
 
 
+def test_explicit_offsets_gaps_legal_overlaps_flagged(orc, dev):
+    # explicit offsets with rows no expert owns: those rows stay unwritten and
+    # no error bit is set; overlapping or out-of-order ranges, or offs[G] past
+    # M, set bit 2
+    K, N, M = 64, 128, 200
+    a = synth.randn_bf16((M, K), seed=25, std=K ** -0.5, device=dev)
+    b = synth.randn_bf16((3, K, N), seed=26, std=K ** -0.5, device=dev)
+    lens = np.array([50, 0, 90], np.int64)
+    offs = np.array([10, 70, 70, 190], np.int64)        # rows 0-9, 60-69 and 160-199 unowned
+    ws = torch.zeros(64, dtype=torch.int32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    out.view(torch.int16).fill_(NAN16)
+    ptm.pt_grouped_gemm_fwd(a, None, b, None, out, None, dev_i64(lens, dev), dev_i64(offs, dev), 3, M, N, K,
+                            ptm.PT_BF16, 0, ptm.PT_EPI_NONE, workspace=ws)
+    assert ptm.pt_read_error_flags(ws) == 0
+    got = bits16(out)
+    owned = np.concatenate([np.arange(offs[g], offs[g] + lens[g]) for g in range(3)])
+    unowned = np.setdiff1d(np.arange(M), owned)
+    assert (got[unowned] == NAN16).all()
+    ref = orc.fwd_rows(orc.BF16, bits16(a)[owned], None, bits16(b), None, lens, N, K, 0, np.arange(owned.size))
+    assert floored_rel_err(bf16_values(got[owned]), ref) <= BF16_TOL
+    for bad_offs in ([10, 50, 70, 190], [70, 10, 10, 100], [10, 70, 70, 201]):
+        ws.zero_()
+        ptm.pt_grouped_gemm_fwd(a, None, b, None, out, None, dev_i64(lens, dev), dev_i64(bad_offs, dev), 3, M, N,
+                                K, ptm.PT_BF16, 0, ptm.PT_EPI_NONE, workspace=ws)
+        assert ptm.pt_read_error_flags(ws) & 4, bad_offs
+
+
 def test_host_argument_errors(dev):
     K, N, M = 64, 128, 64
     a = synth.randn_bf16((M, K), seed=23, device=dev)

@@ -172,6 +172,8 @@ def test_wgrad_with_offsets_and_gaps(orc, dev, fmt):
     dy = synth.randn_bf16((M, N), seed=151, std=1e-2, device=dev)
     owned = np.concatenate([np.arange(offs[g], offs[g] + lens[g]) for g in range(G)])
     lens_d, offs_d = dev_i64(lens, dev), dev_i64(offs, dev)
+    ws = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, fmt),), dtype=torch.uint8,
+                     device=dev)
     if fmt == ptm.PT_FP8_E4M3:
         aq = torch.empty((M, K), dtype=torch.uint8, device=dev)
         dq = torch.empty((M, N), dtype=torch.uint8, device=dev)
@@ -185,8 +187,8 @@ def test_wgrad_with_offsets_and_gaps(orc, dev, fmt):
         dq = torch.full((M, cols(N)), 0xEE, dtype=torch.uint8, device=dev)
         as_ = torch.zeros((M // 32 + G, K), dtype=torch.uint8, device=dev)
         ds = torch.zeros((M // 32 + G, N), dtype=torch.uint8, device=dev)
-        ptm.pt_mx_quantize_tokens(a, lens_d, offs_d, aq, as_, G, M, K, fmt)
-        ptm.pt_mx_quantize_tokens(dy, lens_d, offs_d, dq, ds, G, M, N, fmt)
+        ptm.pt_mx_quantize_tokens(a, lens_d, offs_d, aq, as_, G, M, K, fmt, workspace=ws)
+        ptm.pt_mx_quantize_tokens(dy, lens_d, offs_d, dq, ds, G, M, N, fmt, workspace=ws)
         torch.cuda.synchronize()
         unowned = np.setdiff1d(np.arange(M), owned)
         assert (u8(aq)[unowned] == 0xEE).all() and (u8(dq)[unowned] == 0xEE).all()
@@ -194,10 +196,9 @@ def test_wgrad_with_offsets_and_gaps(orc, dev, fmt):
         raq, ras, _ = orc.mx_quantize_tokens(bits16(a)[owned], lens, fmt)
         assert (u8(aq)[owned] == raq).all()
     mg = torch.full((G, K, N), 0.25, dtype=torch.float32, device=dev)
-    ws = torch.zeros((ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, fmt),), dtype=torch.uint8,
-                     device=dev)
     ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, lens_d, offs_d, G, M, N, K, fmt, 0, 1, workspace=ws)
-    torch.cuda.synchronize()
+    # rows between the experts' ranges are valid input: no error bit
+    assert ptm.pt_read_error_flags(ws) == 0
     got = mg.cpu().numpy().astype(np.float64) - 0.25
     gs, ks = np.repeat(np.arange(G), K), np.tile(np.arange(K), G)
     if fmt == ptm.PT_FP8_E4M3:
