@@ -151,6 +151,31 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pt_grouped_gemm_fwd without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and
+ * requirements as pt_grouped_gemm_fwd, bit for bit; the scratch that the
+ * workspace would carry -- the error word and the eight tile-queue counters,
+ * 1280 bytes whatever the problem size -- lives in a static device array of
+ * the library (4 KiB, one copy per GPU, held until the process ends), so no
+ * size can exceed it.  The call allocates nothing and never times kernel
+ * configurations (under PT_CONFIG_TUNE it takes a tuned choice of its
+ * class, else configuration 0).  The MX forwards run on row-major scales
+ * (no stage-major scale copies, which need a workspace).  The counters are
+ * zeroed on `stream` at every call; the device error bits are not reported.
+ * Every call on one GPU shares that array: calls that may overlap on one GPU
+ * (different streams, or different host threads) race and must be
+ * serialised by the caller.
+ */
+int pt_grouped_gemm_fwd_noalloc(const void *a, const uint8_t *a_scale,
+                                const void *b, const uint8_t *b_scale,
+                                void *out, uint8_t *out_scale,
+                                const int64_t *group_lens, const int64_t *group_offs,
+                                int64_t G, int64_t M, int64_t N, int64_t K,
+                                int dtype, int trans_b, int epilogue, float swiglu_limit,
+                                void *stream);
+
+/*
  * Grouped data gradient: for every expert g and each of its rows r,
  *     dX[r, k] = sum_n dY[r, n] * B_g[k, n]
  * (the grouped GEMM's backward flow, PR page "[Megatron-LM] feat: add grouped

@@ -23,7 +23,7 @@ __all__ = [
     "PT_OP_FWD", "PT_OP_DGRAD", "PT_OP_WGRAD",
     "load", "lib_path", "PtggError",
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu",
-    "pt_grouped_gemm_wgrad", "pt_grouped_gemm_fwd_swiglu_save",
+    "pt_grouped_gemm_wgrad", "pt_grouped_gemm_fwd_swiglu_save", "pt_grouped_gemm_fwd_noalloc",
     "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts", "expert_addresses",
     "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning", "PT_CONFIG_RULES", "PT_CONFIG_TUNE",
@@ -38,7 +38,7 @@ PT_CONFIG_RULES, PT_CONFIG_TUNE = -1, -2
 
 EXPORTS = (
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",
-    "pt_grouped_gemm_fwd_swiglu_save",
+    "pt_grouped_gemm_fwd_swiglu_save", "pt_grouped_gemm_fwd_noalloc",
     "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts",
     "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning",
@@ -71,6 +71,8 @@ def load(require_gpu: bool = True):
     p, i64, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     L.pt_grouped_gemm_fwd.restype = i32
     L.pt_grouped_gemm_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, f32, p, sz, p]
+    L.pt_grouped_gemm_fwd_noalloc.restype = i32
+    L.pt_grouped_gemm_fwd_noalloc.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, f32, p]
     L.pt_grouped_gemm_dgrad.restype = i32
     L.pt_grouped_gemm_dgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, p, sz, p]
     L.pt_grouped_gemm_dgrad_swiglu.restype = i32
@@ -147,6 +149,15 @@ def pt_grouped_gemm_fwd(a, a_scale, b, b_scale, out, out_scale, group_lens, grou
         _ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), _ptr(out), _ptr(out_scale),
         _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_b, epilogue, swiglu_limit,
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def pt_grouped_gemm_fwd_noalloc(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs,
+                                G, M, N, K, dtype, trans_b, epilogue, stream=None, swiglu_limit=0.0):
+    L = load()
+    _check("pt_grouped_gemm_fwd_noalloc", L.pt_grouped_gemm_fwd_noalloc(
+        _ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), _ptr(out), _ptr(out_scale),
+        _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_b, epilogue, swiglu_limit,
+        _stream(stream)))
 
 
 def pt_grouped_gemm_dgrad(dy, dy_scale, b, b_scale, dx, group_lens, group_offs,

@@ -299,9 +299,9 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
     });
 }
 
-// The grouped forward behind pt_grouped_gemm_fwd; `timing` false never
-// times configurations (tuning mode then takes a tuned choice or
-// configuration 0).
+// The grouped forward behind pt_grouped_gemm_fwd and
+// pt_grouped_gemm_fwd_noalloc; `timing` false never times configurations
+// (tuning mode then takes a tuned choice or configuration 0).
 static int grouped_fwd(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale, void *out,
                        uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
                        int64_t N, int64_t K, int dtype, int trans_b, int epilogue, float swiglu_limit,
@@ -367,6 +367,39 @@ static int grouped_fwd(const void *a, const uint8_t *a_scale, const void *b, con
     return PT_ERR_UNSUPPORTED;
 }
 
+// ---------------------------------------------------------------- library-held scratch
+// pt_grouped_gemm_fwd_noalloc keeps the forward's scratch -- the error word
+// and the eight tile-queue counters, kQueueWsBytes bytes whatever the
+// problem size -- in this array instead of a caller's workspace.  Every GPU
+// the library runs on holds its own copy until the process ends.  The
+// array's name is only a host-side stand-in: host code uses the device
+// address hipGetSymbolAddress returns, fetched once per device with that
+// device current.  The counters are zeroed on the stream at every call; the
+// error bits accumulate there and are not reported.
+constexpr size_t kScratchBytes = 4096;
+static_assert((size_t)kQueueWsBytes <= kScratchBytes, "the forward's scratch must fit the static array");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[64] = {};
+
+// Device address of this device's copy of `scratch` (looked up on the first
+// call on each device).
+static int scratch_address(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PT_ERR_HIP;
+    if (dev < 0 || dev >= 64) return PT_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PT_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PT_OK;
+}
+
 extern "C" {
 
 int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale,
@@ -376,6 +409,20 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
 {
     return grouped_fwd(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype, trans_b,
                        epilogue, swiglu_limit, workspace, workspace_bytes, stream, true);
+}
+
+int pt_grouped_gemm_fwd_noalloc(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale,
+                                void *out, uint8_t *out_scale, const int64_t *group_lens,
+                                const int64_t *group_offs, int64_t G, int64_t M, int64_t N, int64_t K, int dtype,
+                                int trans_b, int epilogue, float swiglu_limit, void *stream)
+{
+    // the scratch need does not grow with the problem: kQueueWsBytes always
+    // fits kScratchBytes (static_assert above), so no size is refused for it
+    void *ws = nullptr;
+    const int st = scratch_address(&ws);
+    if (st) return st;
+    return grouped_fwd(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype, trans_b,
+                       epilogue, swiglu_limit, ws, (size_t)kQueueWsBytes, stream, false);
 }
 
 int pt_grouped_gemm_dgrad(const void *dy, const uint8_t *dy_scale, const void *b, const uint8_t *b_scale, void *dx,
