@@ -538,6 +538,30 @@ __device__ __forceinline__ void wfrag_wait(bf16x8 (&a)[4], bf16x8 (&b)[2])
 }
 // Keep the MFMAs on these fragments after the preceding asm (the barrier and
 // the reads of the next stage): an empty asm the fragments pass through.
+__device__ __forceinline__ void wfrag_wait(bf16x8 (&a)[2], bf16x8 (&b)[2])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]));
+}
+__device__ __forceinline__ void wfrag_wait(bf16x8 (&a)[1], bf16x8 (&b)[2])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(b[0]), "+v"(b[1]));
+}
+__device__ __forceinline__ void wfrag_wait(bf16x8 (&a)[1], bf16x8 (&b)[4])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+__device__ __forceinline__ void wfrag_pin(bf16x8 (&a)[1], bf16x8 (&b)[4])
+{
+    asm volatile("" : "+v"(a[0]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
+}
+__device__ __forceinline__ void wfrag_pin(bf16x8 (&a)[2], bf16x8 (&b)[2])
+{
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]));
+}
+__device__ __forceinline__ void wfrag_pin(bf16x8 (&a)[1], bf16x8 (&b)[2])
+{
+    asm volatile("" : "+v"(a[0]), "+v"(b[0]), "+v"(b[1]));
+}
 __device__ __forceinline__ void wfrag_pin(bf16x8 (&a)[2], bf16x8 (&b)[4])
 {
     asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]));
@@ -605,30 +629,22 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> WGrid<WL>::WM_SHIFT, wn = wave & ((1 << WGrid<WL>::WM_SHIFT) - 1);
-    const int wrow0 = wm * MI * 32;
     const uint32_t lds0 = lds_addr(smem);
     const int r32 = lane & 31, h = lane >> 5, g16 = (lane >> 4) & 1, s16 = lane & 15;
 
-    // ---- per-lane fragment bases (slot 0; other slots by immediate)
+    // ---- per-lane B fragment bases (slot 0; other slots by immediate); the
+    // A bases depend on the tile's height and are set per tile below.
     // reduction-contiguous: chunk 2j + h of the lane's first row at base ^ (j << 5)
-    const uint32_t aK = lds0 + (uint32_t)(wrow0 + r32) * R::ROWBA + kswz_base<R::KCPRA>(r32, h);
     const uint32_t bK = lds0 + B_REGION + (uint32_t)(wgrid_bcol<WL, EPI>(wn, 0) + r32) * R::ROWBB + kswz_base<R::KCPRB>(r32, h);
     // column-contiguous: transposing reads of k-rows h*8 + s16/4 (+4), columns
     // 16 g16 + 4 (s16 & 3) of each 32-column block
-    uint32_t aN[MI], bN[NJ];
-    {
-        const int krow = h * 8 + (s16 >> 2);
-        const int lo = 8 * (s16 & 1);
+    const int krow = h * 8 + (s16 >> 2);
+    const int klo = 8 * (s16 & 1);
+    uint32_t bN[NJ];
 #pragma unroll
-        for (int bi = 0; bi < MI; ++bi) {
-            const int col = wrow0 + bi * 32 + 16 * g16 + 4 * (s16 & 3);
-            aN[bi] = lds0 + krow * 512 + npos(krow, col >> 3) * 16 + lo;
-        }
-#pragma unroll
-        for (int bj = 0; bj < NJ; ++bj) {
-            const int col = wgrid_bcol<WL, EPI>(wn, bj) + 16 * g16 + 4 * (s16 & 3);
-            bN[bj] = lds0 + B_REGION + krow * 512 + npos(krow, col >> 3) * 16 + lo;
-        }
+    for (int bj = 0; bj < NJ; ++bj) {
+        const int col = wgrid_bcol<WL, EPI>(wn, bj) + 16 * g16 + 4 * (s16 & 3);
+        bN[bj] = lds0 + B_REGION + krow * 512 + npos(krow, col >> 3) * 16 + klo;
     }
     // ---- per-thread load slots: reduction-contiguous row i*RPL + t/KCPR,
     // chunk kswz(row, t % KCPR); column-contiguous k-row i*16 + t/32, chunk
@@ -659,13 +675,35 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         const int Kred = (KIND == kWgrad) ? rows : p.Kred;
         const int nka = (Kred + WKA - 1) / WKA;     // A stages
         const int nk = (Kred + WKB - 1) / WKB;      // B stages: the steps of the k-loop
-        int nvalid_bi = MI;
+
+        // One tile of TMI 32-row blocks per wave (tile height TMI * 32 per
+        // row of waves).  In the forward and data gradient a row block
+        // holding at most 128 (or, on the 2 x 4 grid, 64) valid rows runs as
+        // a tile of that height: A loads, A fragment reads and MFMAs then
+        // scale with the valid rows while every wave keeps working.  The tile
+        // ids, the B panel and the order of every accumulation are the same
+        // for each height, so results do not depend on it.
+        auto run_tile = [&](auto MIC) {
+        constexpr int TMI = decltype(MIC)::value;
+        constexpr int TBM = TMI * 32 * (WL ? 2 : 4);          // rows of this tile height
+        constexpr int TNLA = KIND == kWgrad ? NLA : TBM / R::RPLA;
+        static_assert(TMI <= MI && TNLA >= 1 && TNLA <= NLA, "tile height");
+        const int wrow0 = wm * TMI * 32;
+        // reduction-contiguous A: chunk 2j + h of the lane's first row at base ^ (j << 5)
+        const uint32_t aK = lds0 + (uint32_t)(wrow0 + r32) * R::ROWBA + kswz_base<R::KCPRA>(r32, h);
+        uint32_t aN[TMI];
+#pragma unroll
+        for (int bi = 0; bi < TMI; ++bi) {
+            const int col = wrow0 + bi * 32 + 16 * g16 + 4 * (s16 & 3);
+            aN[bi] = lds0 + krow * 512 + npos(krow, col >> 3) * 16 + klo;
+        }
+        int nvalid_bi = TMI;
         if (KIND != kWgrad) {
-            const int vr = min(WBM, rows - m0) - wrow0;
-            nvalid_bi = vr <= 0 ? 0 : min(MI, (vr + 31) >> 5);
+            const int vr = min(TBM, rows - m0) - wrow0;
+            nvalid_bi = vr <= 0 ? 0 : min(TMI, (vr + 31) >> 5);
         }
 
-        WOp<NLA> oa;
+        WOp<TNLA> oa;
         WOp<NLB> ob;
         if (KIND == kWgrad) {
             // [token][i] and [token][j] slices of the expert: column-contiguous
@@ -676,7 +714,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             ob.bytes = (uint32_t)rows * p.ldb * 2;
             ob.voff = (uint32_t)(nc_row * p.ldb + min(nt * WBN + nc_chunk * 8, p.Nout - 8)) * 2;
 #pragma unroll
-            for (int i = 0; i < NLA; ++i) oa.delta[i] = (uint32_t)(i * 16 * p.lda) * 2;
+            for (int i = 0; i < TNLA; ++i) oa.delta[i] = (uint32_t)(i * 16 * p.lda) * 2;
 #pragma unroll
             for (int i = 0; i < NLB; ++i) ob.delta[i] = (uint32_t)(i * 16 * p.ldb) * 2;
             oa.kstep = (uint32_t)WKA * p.lda * 2;
@@ -687,7 +725,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             oa.bytes = (uint32_t)rows * p.lda * 2;
             oa.voff = (uint32_t)(m0 + ka_row) * p.lda * 2 + ka_chunk * 16;
 #pragma unroll
-            for (int i = 0; i < NLA; ++i) oa.delta[i] = (uint32_t)(i * R::RPLA * p.lda) * 2;
+            for (int i = 0; i < TNLA; ++i) oa.delta[i] = (uint32_t)(i * R::RPLA * p.lda) * 2;
             oa.kstep = WKA * 2;
             oa.chunk = ka_chunk * 16;
             const uint16_t *Bg = p.b + (int64_t)g * p.b_gstride;
@@ -716,11 +754,11 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 
         // Accumulators start at zero, or for an accumulating wgrad at the
         // main_grad tile itself (loads overlap the operand prologue).
-        floatx16 acc[MI][NJ];
+        floatx16 acc[TMI][NJ];
         if (KIND == kWgrad && p.accumulate) {
             const float *og = (const float *)p.out + (int64_t)g * p.o_gstride;
 #pragma unroll
-            for (int bi = 0; bi < MI; ++bi)
+            for (int bi = 0; bi < TMI; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < NJ; ++bj) {
                     const int n = nt * WBN + wgrid_bcol<WL, EPI>(wn, bj) + (lane & 31);
@@ -732,7 +770,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 }
         } else {
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+            for (int i = 0; i < TMI; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -746,7 +784,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             wissue<KIND == kFwdKContig, WKB>(smem + B_REGION + slot * SLOTB, ob, kb, nk, Kred, wave, b_once);
         };
         // A fragments of k-step KS of A slot S; B fragments of k-step KS of B slot S
-        auto rd_a = [&](auto KSC, auto SC, bf16x8 (&af)[MI]) {
+        auto rd_a = [&](auto KSC, auto SC, bf16x8 (&af)[TMI]) {
             constexpr int KS = decltype(KSC)::value, SO = decltype(SC)::value * SLOTA;
             if constexpr (KIND == kWgrad) {
                 constexpr int NO = SO + KS * 16 * 512, NJ = 4 * 512;  // k-step, +4 k-rows
@@ -755,8 +793,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             } else {
                 const uint32_t x = aK ^ (uint32_t)(KS << 5);
                 af[0] = ldsr_b128<SO>(x);
-                af[1] = ldsr_b128<SO + 32 * R::ROWBA>(x);
-                if constexpr (MI == 4) {
+                if constexpr (TMI >= 2) af[1] = ldsr_b128<SO + 32 * R::ROWBA>(x);
+                if constexpr (TMI == 4) {
                     af[2] = ldsr_b128<SO + 64 * R::ROWBA>(x);
                     af[3] = ldsr_b128<SO + 96 * R::ROWBA>(x);
                 }
@@ -776,16 +814,16 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 for (int bj = 0; bj < NJ; ++bj) bf[bj] = join(ldsr_tr<NO>(bN[bj]), ldsr_tr<NO + K4>(bN[bj]));
             }
         };
-        auto mma = [&](const bf16x8 (&af)[MI], const bf16x8 (&bf)[NJ]) {
+        auto mma = [&](const bf16x8 (&af)[TMI], const bf16x8 (&bf)[NJ]) {
 #pragma unroll
-            for (int bi = 0; bi < MI; ++bi)
+            for (int bi = 0; bi < TMI; ++bi)
                 if (bi < nvalid_bi) {
 #pragma unroll
                     for (int bj = 0; bj < NJ; ++bj)
                         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
                 }
         };
-        bf16x8 fa[2][MI], fb[2][NJ];
+        bf16x8 fa[2][TMI], fb[2][NJ];
         int kt0 = 0;
 
         // prologue, and the id of the next tile (its atomic goes out first and
@@ -803,7 +841,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 issue_a(st, st);
                 issue_b(st, st);
             }
-            wait_vmcnt<(NSB - 2) * (NLA + NLB)>();
+            wait_vmcnt<(NSB - 2) * (TNLA + NLB)>();
         }
         if (tid == 0) s_id[par ^ 1] = tq.resolve(tile);
         wait_lgkm0();
@@ -834,7 +872,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 wfrag_wait(fa[1], fb[1]);
                 // even: B's next stage landed; odd: A's next stage too
                 if constexpr ((P & 1) == 0)
-                    wait_vmcnt<2 * NLB + NLA>();
+                    wait_vmcnt<2 * NLB + TNLA>();
                 else
                     wait_vmcnt<2 * NLB>();
                 barrier();
@@ -848,7 +886,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 constexpr int PN = (P + NSB - 1) % NSB;
                 issue_a(kt + NSB - 1, PN);       // the slot stage kt-1 freed at its barrier
                 issue_b(kt + NSB - 1, PN);
-                auto rd = [&](auto KSC, bf16x8 (&af)[MI], bf16x8 (&bf)[NJ]) {
+                auto rd = [&](auto KSC, bf16x8 (&af)[TMI], bf16x8 (&bf)[NJ]) {
                     rd_a(KSC, PC, af);
                     rd_b(KSC, PC, bf);
                 };
@@ -870,7 +908,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 // stage kt+1 landed for this wave (later stages may still be
                 // in flight), after the barrier for all waves, and every wave
                 // is done reading slot P
-                wait_vmcnt<(NSB - 2) * (NLA + NLB)>();
+                wait_vmcnt<(NSB - 2) * (TNLA + NLB)>();
                 barrier();
                 rd_a(IC<0>{}, IC<Q>{}, fa[0]);
                 rd_b(IC<0>{}, IC<Q>{}, fb[0]);
@@ -909,7 +947,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             wait_vmcnt<0>();
             float *og = (float *)p.out + (int64_t)g * p.o_gstride;
 #pragma unroll
-            for (int bi = 0; bi < MI; ++bi)
+            for (int bi = 0; bi < TMI; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < NJ; ++bj) {
                     const int n = nt * WBN + wgrid_bcol<WL, EPI>(wn, bj) + (lane & 31);
@@ -921,8 +959,20 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                     }
                 }
         } else {
-            store_tile_lds_w<EPI, 4, MI, NJ>(acc, smem, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt, wrow0, wn,
-                                             p.swiglu_limit, p.aux, p.ldaux, p.save, p.ldsave);
+            store_tile_lds_w<EPI, 4, TMI, NJ, TBM>(acc, smem, p.out, p.out_scale, p.ldo, p.Nout, row0, m0, rows, nt,
+                                                  wrow0, wn, p.swiglu_limit, p.aux, p.ldaux, p.save, p.ldsave);
+        }
+        };  // run_tile
+        if constexpr (KIND == kFwdNContig && WL == 1) {
+            const int hb = rows - m0;        // valid rows of the row block
+            if (hb <= 64) run_tile(IC<1>{});
+            else if (hb <= 128) run_tile(IC<2>{});
+            else run_tile(IC<MI>{});
+        } else if constexpr (KIND == kFwdKContig && WL == 0) {
+            if (rows - m0 <= 128) run_tile(IC<1>{});
+            else run_tile(IC<MI>{});
+        } else {
+            run_tile(IC<MI>{});
         }
         barrier();
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);

@@ -230,7 +230,7 @@ __device__ __forceinline__ void store_out(const floatx16 (&acc)[2][4], void *out
     }
 }
 
-// Epilogue through LDS, for a tile of 64 * NWM rows computed by NWM x 2
+// Epilogue through LDS, for a tile of TROWS (at most 64 * NWM) rows computed by NWM x 2
 // waves (the ring is idle by then).  Phase 1: every wave writes its results
 // as bf16 (after SwiGLU when asked) into a row-major LDS tile whose rows are
 // padded by 16 bytes, so the two lane halves (rows 4 apart) of a 2-byte
@@ -246,14 +246,15 @@ __host__ __device__ constexpr int epi_row_bytes() { return (epi_glu(EPI) ? BN / 
 template <int EPI, int NWM>
 __host__ __device__ constexpr int epi_lds_bytes() { return 64 * NWM * epi_row_bytes<EPI>(); }
 
-template <int EPI, int NWM, int MI, int NJ>
+template <int EPI, int NWM, int MI, int NJ, int TROWS = 64 * NWM>
 __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], uint8_t *smem, void *out,
                                                  uint8_t *out_scale, int ldo, int Nout, int64_t row0, int m0,
                                                  int rows, int nt, int wrow0, int wn, float lim,
                                                  const uint16_t *aux = nullptr, int ldaux = 0,
                                                  uint16_t *save = nullptr, int ldsave = 0)
 {
-    constexpr int TR = 64 * NWM;                           // tile rows
+    constexpr int TR = TROWS;                              // tile rows (at most 64 * NWM)
+    static_assert(TROWS <= 64 * NWM, "tile rows");
     constexpr int OC = epi_glu(EPI) ? BN / 2 : BN;         // output columns of the tile
     constexpr int RS = epi_row_bytes<EPI>();
     constexpr int NT = NWM * 2 * kWave;
