@@ -562,6 +562,35 @@ def bench_cfg3_wgrad(dev, stream, iters):
     return w, w8
 
 
+def bench_wgrad_split(dev, stream, iters):
+    """BF16 weight gradient with few output tiles per expert (K = N = 512,
+    four 256 x 256 tiles each) over the GPT-OSS-20B-like skewed routing (32
+    experts, 65536 rows, one of 12541 tokens): with the split reduction's
+    workspace, experts are cut into 512-token chunks; without it each
+    expert's four tiles reduce all its tokens serially."""
+    lens = synth.lens_zipf_distinct(16384, 32, 4, 1.1, seed=3)
+    G, M, K, N = 32, int(lens.sum()), 512, 512
+    a = synth.randn_bf16((M, K), seed=220, std=K ** -0.5, device=dev)
+    dy = synth.randn_bf16((M, N), seed=221, std=1e-2, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(222)
+    mg = torch.randn((G, K, N), generator=g, device=dev, dtype=torch.float32).mul_(1e-3)
+    lens_d = torch.as_tensor(lens, device=dev)
+    ws = torch.zeros(ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, ptm.PT_BF16),
+                     dtype=torch.uint8, device=dev)
+    _, per_s = time_launches(lambda: ptm.pt_grouped_gemm_wgrad(
+        a, None, dy, None, mg, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, 1, workspace=ws, stream=stream),
+        iters, 2, stream)
+    _, per_n = time_launches(lambda: ptm.pt_grouped_gemm_wgrad(
+        a, None, dy, None, mg, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, 1, workspace=WS[0][:1280],
+        stream=stream), iters, 2, stream)
+    flops = 2.0 * M * K * N
+    return summary("BF16 wgrad into fp32 main_grad [32, 512, 512], skewed routing (max 12541 tokens), split "
+                   "reduction into 512-token chunks", "bf16", flops,
+                   bytes_weights(lens, K * N * 4 * 2) + M * K * 2 + M * N * 2, per_s,
+                   {"unsplit_ms_median": round(float(np.median(per_n)), 4), "workspace_bytes": ws.numel()})
+
+
 def bench_stack(dev, stream, iters):
     """The expert weight stack at the expert-MLP shape: 256 separately
     allocated FC1 weights [2I, H] = [4096, 4096] -> the [G, H, 2I] operand in
@@ -703,6 +732,10 @@ def main():
         if want is None or "cfg3wgrad" in want:
             log("per_config: MXFP8 wgrad")
             per["cfg3_mxfp8_wgrad"], per["cfg3_fp8_tensor_wgrad"] = bench_cfg3_wgrad(dev, stream, iters)
+            torch.cuda.empty_cache()
+        if want is None or "wgradsplit" in want:
+            log("per_config: split weight gradient")
+            per["wgrad_split_skewed_k512"] = bench_wgrad_split(dev, stream, iters)
             torch.cuda.empty_cache()
         if want is None or "stack" in want:
             log("per_config: expert weight stack")

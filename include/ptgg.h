@@ -273,7 +273,22 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_sa
  *  An expert with no rows leaves its main_grad slice untouched when
  *  accumulating and writes zeros when not.
  *  workspace  optional (may be NULL) for BF16, see
- *             pt_grouped_gemm_workspace_size.
+ *             pt_grouped_gemm_workspace_size.  With the full size
+ *             (pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ...), any dtype)
+ *             the reduction over an expert's tokens is split: with
+ *             T = ceil(K/256) * ceil(N/256) output tiles per expert and the
+ *             chunk length L = max(512, ceil(M * T / 1024)), an expert with
+ *             more than L rows is cut into chunks of L consecutive rows
+ *             (the last one shorter); chunk 0 is added into main_grad as an
+ *             uncut expert is, each later chunk's fp32 partial sum goes to a
+ *             workspace slot, and a second pass adds the partials to
+ *             main_grad in chunk order:
+ *                 main_grad[g] = fp32(... fp32(fp32(main_grad[g] + S_0) + S_1) ... + S_last)
+ *             (S_0 itself accumulated onto main_grad[g] in fp32).  The order
+ *             is fixed, so results are deterministic, and within fp32
+ *             rounding of the uncut sum.  The split engages only where few
+ *             output tiles per expert would leave a long expert as a serial
+ *             tail.  A smaller workspace runs every expert uncut.
  *  PT_MXFP8_E4M3 / PT_MXFP4_E2M1: a and dy are codes blocked along tokens
  *  within each expert (pt_mx_quantize_tokens): E4M3 [M, K] / [M, N], or
  *  E2M1 [M, K/2] / [M, N/2], with scales [M/32 + G, K] / [M/32 + G, N];
@@ -443,7 +458,11 @@ int pt_mx_quantize_experts(const void *const *experts, void *q, uint8_t *scales,
 
 /*
  * Workspace of the grouped GEMMs (optional, for every op; recommended):
- * pt_grouped_gemm_workspace_size() bytes of device memory, 4-byte aligned.
+ * pt_grouped_gemm_workspace_size() bytes of device memory, 256-byte aligned
+ * (4-byte alignment is enough for the error word and tile queues alone).
+ *  - the weight gradient's full size adds the split reduction's partial
+ *    slots: floor(M / L) fp32 [K, N] matrices (L as at
+ *    pt_grouped_gemm_wgrad), after the MX / FP8 operand copies;
  *  - word 0 receives the sticky device error bits (pt_read_error_flags);
  *    a workspace of at least 4 bytes is enough for that alone;
  *  - a workspace of the full size also holds the tile queues: every call

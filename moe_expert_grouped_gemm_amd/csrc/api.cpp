@@ -79,6 +79,25 @@ bool mx_swz_possible(int64_t G, int64_t M, int64_t N, int64_t K, int fmt)
     return K <= kMxSwzMaxK && fits31(mx_swizzle_bytes(M, K, fmt)) && fits31(mx_swizzle_bytes(G * N, K, fmt));
 }
 
+// Split weight gradient: token chunk length and partial slots for a problem
+// with M rows and ntl output tiles per expert (256 x 256).  About 4 work units
+// per compute unit of the 256 on an MI355X: L = max(512, ceil(M ntl / 1024)),
+// so the split only engages where few output tiles per expert leave long
+// experts as a serial tail; at most M / L experts are cut, and the chunks
+// past each expert's first need at most M / L partial slots.
+constexpr int64_t kSplitMinLen = 512;
+int64_t wgrad_split_len(int64_t M, int64_t Mout, int64_t Nout)
+{
+    const int64_t ntl = ((Mout + 255) / 256) * ((Nout + 255) / 256);
+    const int64_t L = (M * ntl + 1023) / 1024;
+    return L > kSplitMinLen ? L : kSplitMinLen;
+}
+int64_t wgrad_split_slots(int64_t M, int64_t Mout, int64_t Nout) { return M / wgrad_split_len(M, Mout, Nout); }
+int64_t wgrad_split_bytes(int64_t M, int64_t K, int64_t N)
+{
+    return round256(wgrad_split_slots(M, K, N) * K * N * 4);
+}
+
 // Zero the queues (if any) ahead of the launch on the same stream.
 template <class Launch>
 hipError_t queued(uint32_t *sched, hipStream_t s, Launch launch)
@@ -584,6 +603,59 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_sa
     });
 }
 
+// The BF16 weight gradient (also the second half of the MX and FP8 ones);
+// its split reduction's partial slots start split_off bytes into the
+// workspace.
+static int bf16_wgrad(const void *a, const void *dy, float *main_grad, const int64_t *group_lens,
+                      const int64_t *group_offs, int64_t G, int64_t M, int64_t N, int64_t K, int trans_out,
+                      int accumulate, void *workspace, size_t workspace_bytes, size_t split_off, hipStream_t s)
+{
+    if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    Bf16Params p = {};
+    p.swiglu_limit = __builtin_huge_valf();
+    // trans_out = 0: D[k, n] = sum_r A[r, k] dY[r, n];  1: D^T[n, k] with the
+    // operands swapped
+    p.a = (const uint16_t *)(trans_out ? dy : a);
+    p.b = (const uint16_t *)(trans_out ? a : dy);
+    p.lda = (int)(trans_out ? N : K);
+    p.ldb = (int)(trans_out ? K : N);
+    p.Mout = (int)(trans_out ? N : K);
+    p.Nout = (int)(trans_out ? K : N);
+    p.out = main_grad;
+    p.ldo = p.Nout;
+    p.o_gstride = N * K;
+    p.lens = group_lens;
+    p.offs = group_offs;
+    p.err = error_word(workspace, workspace_bytes);
+    p.G = (int)G;
+    p.M = M;
+    p.tilesN = (p.Nout + bf16_tile_n() - 1) / bf16_tile_n();
+    p.accumulate = accumulate;
+    if (M == 0 && accumulate) return PT_OK;
+    uint32_t *queues = queue_words(workspace, workspace_bytes);
+    // the split reduction, when the workspace holds its partial slots
+    const int64_t split_len = wgrad_split_len(M, p.Mout, p.Nout);
+    const int64_t nslots = wgrad_split_slots(M, p.Mout, p.Nout);
+    const bool split = queues && aligned16(workspace) && nslots > 0 &&
+                       workspace_bytes >= split_off + (size_t)wgrad_split_bytes(M, K, N);
+    if (split) {
+        p.split_len = (int)split_len;
+        p.nslots = (int)nslots;
+        p.partials = (float *)((uint8_t *)workspace + split_off);
+    }
+    const TuneKey key = tune_key(PT_OP_WGRAD, PT_BF16, kEpiNone, trans_out, G, M, N, K);
+    return configured(key, cfg_mask(queues != nullptr, !split), !accumulate, s, [&](int cfg) {
+        p.narrow = (cfg & kCfgNarrow) != 0;
+        p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+        p.tilesM = (p.Mout + bf16_tile_m(p.narrow) - 1) / bf16_tile_m(p.narrow);
+        hipError_t e = queued(p.sched, s, [&] { return launch_bf16(p, kWgrad, kEpiNone, s); });
+        if (e == hipSuccess && split) e = launch_wgrad_split_reduce(p, s);
+        return e;
+    });
+}
+
+
 int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy, const uint8_t *dy_scale,
                           float *main_grad, const int64_t *group_lens, const int64_t *group_offs, int64_t G,
                           int64_t M, int64_t N, int64_t K, int dtype, int trans_out, int accumulate,
@@ -617,16 +689,15 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
             e = launch_mx_dequant_tokens((const uint8_t *)dy, dy_scale, group_lens, group_offs, (int)G, M, N, fmt, wd,
                                          s);
         if (e != hipSuccess) return PT_ERR_HIP;
-        return pt_grouped_gemm_wgrad(wa, nullptr, wd, nullptr, main_grad, group_lens, group_offs, G, M, N, K, PT_BF16,
-                                     trans_out, accumulate, workspace, workspace_bytes, stream);
+        return bf16_wgrad(wa, wd, main_grad, group_lens, group_offs, G, M, N, K, trans_out, accumulate, workspace,
+                          workspace_bytes, need, s);
     }
     if (dtype == PT_FP8_E4M3) {
         // one factor per tensor: the codes' values (exact in bf16) go to the
         // BF16 weight gradient, whose fp32 sums land in the workspace; then
         // main_grad (+)= d_a * d_dy * sum, one fused multiply-add each
-        if (M == 0) return pt_grouped_gemm_wgrad(nullptr, nullptr, nullptr, nullptr, main_grad, group_lens, group_offs,
-                                                 G, M, N, K, PT_BF16, trans_out, accumulate, workspace,
-                                                 workspace_bytes, stream);
+        if (M == 0) return bf16_wgrad(nullptr, nullptr, main_grad, group_lens, group_offs, G, M, N, K, trans_out,
+                                      accumulate, workspace, workspace_bytes, kQueueWsBytes, s);
         if (!a_scale || !dy_scale) return PT_ERR_INVALID_ARG;
         if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad) || !aligned4(a_scale) || !aligned4(dy_scale))
             return PT_ERR_MISALIGNED;
@@ -640,45 +711,16 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
         hipError_t e = launch_fp8_decode((const uint8_t *)a, wa, M * K, s);
         if (e == hipSuccess) e = launch_fp8_decode((const uint8_t *)dy, wd, M * N, s);
         if (e != hipSuccess) return PT_ERR_HIP;
-        st = pt_grouped_gemm_wgrad(wa, nullptr, wd, nullptr, sum, group_lens, group_offs, G, M, N, K, PT_BF16,
-                                   trans_out, 0, workspace, workspace_bytes, stream);
+        st = bf16_wgrad(wa, wd, sum, group_lens, group_offs, G, M, N, K, trans_out, 0, workspace, workspace_bytes,
+                        need, s);
         if (st) return st;
         return hip_status(launch_fp8_wgrad_axpy(main_grad, sum, group_lens, (const float *)a_scale,
                                                 (const float *)dy_scale, (int)G, K * N, accumulate, s));
     }
     if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
     if (a_scale || dy_scale) return PT_ERR_INVALID_ARG;
-    if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad)) return PT_ERR_MISALIGNED;
-    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
-    Bf16Params p = {};
-    p.swiglu_limit = __builtin_huge_valf();
-    // trans_out = 0: D[k, n] = sum_r A[r, k] dY[r, n];  1: D^T[n, k] with the
-    // operands swapped
-    p.a = (const uint16_t *)(trans_out ? dy : a);
-    p.b = (const uint16_t *)(trans_out ? a : dy);
-    p.lda = (int)(trans_out ? N : K);
-    p.ldb = (int)(trans_out ? K : N);
-    p.Mout = (int)(trans_out ? N : K);
-    p.Nout = (int)(trans_out ? K : N);
-    p.out = main_grad;
-    p.ldo = p.Nout;
-    p.o_gstride = N * K;
-    p.lens = group_lens;
-    p.offs = group_offs;
-    p.err = error_word(workspace, workspace_bytes);
-    p.G = (int)G;
-    p.M = M;
-    p.tilesN = (p.Nout + bf16_tile_n() - 1) / bf16_tile_n();
-    p.accumulate = accumulate;
-    if (M == 0 && accumulate) return PT_OK;
-    uint32_t *queues = queue_words(workspace, workspace_bytes);
-    const TuneKey key = tune_key(PT_OP_WGRAD, dtype, kEpiNone, trans_out, G, M, N, K);
-    return configured(key, cfg_mask(queues != nullptr, true), !accumulate, s, [&](int cfg) {
-        p.narrow = (cfg & kCfgNarrow) != 0;
-        p.sched = (cfg & kCfgStatic) ? nullptr : queues;
-        p.tilesM = (p.Mout + bf16_tile_m(p.narrow) - 1) / bf16_tile_m(p.narrow);
-        return queued(p.sched, s, [&] { return launch_bf16(p, kWgrad, kEpiNone, s); });
-    });
+    return bf16_wgrad(a, dy, main_grad, group_lens, group_offs, G, M, N, K, trans_out, accumulate, workspace,
+                      workspace_bytes, kQueueWsBytes, s);
 }
 
 int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_t cols, int dtype, int axis,
@@ -804,12 +846,17 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, i
         if (mx_swz_possible(G, M, N, K, fmt))
             return (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) + mx_swz_b_bytes(G, N, K, fmt));
     }
-    // the MXFP8 weight gradient: bf16 copies of both operands
-    if (op == PT_OP_WGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && M >= 0 && N > 0 && K > 0)
-        return (size_t)(kQueueWsBytes + round256(M * K * 2) + round256(M * N * 2));
-    // FP8 with tensor factors: bf16 copies of both operands and fp32 sums
-    if (op == PT_OP_WGRAD && dtype == PT_FP8_E4M3 && G > 0 && M >= 0 && N > 0 && K > 0)
-        return (size_t)(kQueueWsBytes + round256(M * K * 2) + round256(M * N * 2) + round256(G * K * N * 4));
+    // the weight gradients: the split reduction's partial slots last; before
+    // them bf16 copies of both operands (MX), and the fp32 sums (FP8 with
+    // tensor factors)
+    if (op == PT_OP_WGRAD && M > 0 && N > 0 && K > 0 && G > 0) {
+        int64_t bytes = kQueueWsBytes;
+        if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3)
+            bytes += round256(M * K * 2) + round256(M * N * 2);
+        if (dtype == PT_FP8_E4M3) bytes += round256(G * K * N * 4);
+        return (size_t)(bytes + wgrad_split_bytes(M, K, N));
+    }
+    if (op == PT_OP_WGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && M == 0) return kQueueWsBytes;
     // the MX data gradient: K outputs per row, a reduction over N
     if (op == PT_OP_DGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && G > 0 && M >= 0 && N > 0 &&
         K > 0 && N % 32 == 0) {

@@ -434,6 +434,42 @@ hipError_t launch_depth(const Bf16Params &p, hipStream_t s)
     }
 }
 
+// ------------------------------------------------------------------ split weight gradient
+// The weight gradient reduces over an expert's tokens.  With a chunk length
+// L > 0, an expert is cut into chunks of L consecutive tokens (the last one
+// shorter), and every chunk covers the whole output: tiles (expert, chunk,
+// K tile, N tile).  Chunk 0 reads-modifies-writes main_grad as an uncut
+// expert does; chunk c >= 1 writes its fp32 partial sum to workspace slot
+// slot0[g] + c - 1, and launch_wgrad_split_reduce then adds the partials to
+// main_grad in chunk order.  The order of every sum is fixed, so the result
+// is deterministic.  Experts with no tokens: no tiles when accumulating, one
+// zero-writing chunk when not.
+struct TilesWgradSplit {
+    int ntiles, accumulate, L;
+    __device__ int chunks(int rows) const { return rows > 0 ? (L > 0 ? (rows + L - 1) / L : 1) : (accumulate ? 0 : 1); }
+    __device__ int operator()(int rows) const { return chunks(rows) * ntiles; }
+};
+
+// slot0[g] = sum over earlier experts of (chunks - 1): the first partial
+// slot of expert g (needs the table's clamped rows).  NT threads.
+template <int NT>
+__device__ __forceinline__ void wgrad_slot_table(const GroupTable &tab, const TilesWgradSplit &tw, int *slot0,
+                                                 int *s_scan)
+{
+    const int per = (tab.G + NT - 1) / NT, g0 = (int)threadIdx.x * per;
+    int v = 0;
+    for (int i = 0; i < per; ++i)
+        if (g0 + i < tab.G) v += max(tw.chunks(tab.rows[g0 + i]) - 1, 0);
+    int tot;
+    int pre = block_exclusive_scan<NT>(v, s_scan, &tot);
+    for (int i = 0; i < per; ++i)
+        if (g0 + i < tab.G) {
+            slot0[g0 + i] = pre;
+            pre += max(tw.chunks(tab.rows[g0 + i]) - 1, 0);
+        }
+    __syncthreads();
+}
+
 // ====================================================================== wide
 // The main BF16 kernel: one workgroup of 8 waves per CU (two waves per SIMD)
 // computes 256 x 256 tiles; wave (wm, wn), wm = 0..3, owns 64 x 128 outputs
@@ -612,12 +648,15 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
     tab.tile0 = tb + 2 * p.G;
     int *s_scan = tab.tile0 + p.G + 1;
     int total;
-    if (KIND == kWgrad)
-        total = build_group_table<TilesWgrad, WTHREADS>(tab, p.lens, p.offs, p.G, p.M,
-                                                        TilesWgrad{p.tilesM * p.tilesN, p.accumulate}, p.err, s_scan);
-    else
+    const TilesWgradSplit tw{p.tilesM * p.tilesN, p.accumulate, p.split_len};
+    int *slot0 = (int *)(smem + LDS_BYTES + table_bytes(p.G));       // wgrad only
+    if (KIND == kWgrad) {
+        total = build_group_table<TilesWgradSplit, WTHREADS>(tab, p.lens, p.offs, p.G, p.M, tw, p.err, s_scan);
+        if (p.split_len > 0) wgrad_slot_table<WTHREADS>(tab, tw, slot0, s_scan);
+    } else {
         total = build_group_table<TilesFwd, WTHREADS>(tab, p.lens, p.offs, p.G, p.M, TilesFwd{WBM, p.tilesN}, p.err,
                                                       s_scan);
+    }
     total = __builtin_amdgcn_readfirstlane(total);
     // the scan scratch is free once the table is built: it passes tile ids
     TileQueue tq;
@@ -662,9 +701,18 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         // the weight panel of an expert that fits one row block is read by
         // this tile alone
         bool b_once = false;
+        // wgrad: the tile's token chunk (rows crow0 .. crow0 + crows of the expert)
+        int chunk = 0, crow0 = 0, crows = rows;
         if (KIND == kWgrad) {
-            mt = local / p.tilesN;
-            nt = local % p.tilesN;
+            const int ntl = p.tilesM * p.tilesN;
+            chunk = local / ntl;
+            const int rest = local - chunk * ntl;
+            mt = rest / p.tilesN;
+            nt = rest % p.tilesN;
+            if (p.split_len > 0) {
+                crow0 = chunk * p.split_len;
+                crows = min(rows - crow0, p.split_len);
+            }
         } else {
             const int tm = (rows + WBM - 1) / WBM;
             nt = local / tm;
@@ -672,7 +720,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             b_once = tm == 1;
         }
         const int m0 = mt * WBM;
-        const int Kred = (KIND == kWgrad) ? rows : p.Kred;
+        const int Kred = (KIND == kWgrad) ? crows : p.Kred;
         const int nka = (Kred + WKA - 1) / WKA;     // A stages
         const int nk = (Kred + WKB - 1) / WKB;      // B stages: the steps of the k-loop
 
@@ -706,12 +754,12 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         WOp<TNLA> oa;
         WOp<NLB> ob;
         if (KIND == kWgrad) {
-            // [token][i] and [token][j] slices of the expert: column-contiguous
-            oa.base = p.a + (int64_t)row0 * p.lda;
-            oa.bytes = (uint32_t)rows * p.lda * 2;
+            // [token][i] and [token][j] slices of the tile's token chunk: column-contiguous
+            oa.base = p.a + (int64_t)(row0 + crow0) * p.lda;
+            oa.bytes = (uint32_t)crows * p.lda * 2;
             oa.voff = (uint32_t)(nc_row * p.lda + min(m0 + nc_chunk * 8, p.Mout - 8)) * 2;
-            ob.base = p.b + (int64_t)row0 * p.ldb;
-            ob.bytes = (uint32_t)rows * p.ldb * 2;
+            ob.base = p.b + (int64_t)(row0 + crow0) * p.ldb;
+            ob.bytes = (uint32_t)crows * p.ldb * 2;
             ob.voff = (uint32_t)(nc_row * p.ldb + min(nt * WBN + nc_chunk * 8, p.Nout - 8)) * 2;
 #pragma unroll
             for (int i = 0; i < TNLA; ++i) oa.delta[i] = (uint32_t)(i * 16 * p.lda) * 2;
@@ -755,7 +803,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         // Accumulators start at zero, or for an accumulating wgrad at the
         // main_grad tile itself (loads overlap the operand prologue).
         floatx16 acc[TMI][NJ];
-        if (KIND == kWgrad && p.accumulate) {
+        if (KIND == kWgrad && p.accumulate && chunk == 0) {
             const float *og = (const float *)p.out + (int64_t)g * p.o_gstride;
 #pragma unroll
             for (int bi = 0; bi < TMI; ++bi)
@@ -945,13 +993,21 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             // nothing outstanding here; saying so keeps the compiler from
             // waiting for every earlier store before each one
             wait_vmcnt<0>();
+            // chunk 0: main_grad; chunk c >= 1: its partial slot (none past
+            // the workspace's slots, which only malformed lengths reach)
             float *og = (float *)p.out + (int64_t)g * p.o_gstride;
+            bool keep = true;
+            if (chunk > 0) {
+                const int slot = slot0[g] + chunk - 1;
+                keep = slot < p.nslots;
+                og = p.partials + (int64_t)slot * p.o_gstride;
+            }
 #pragma unroll
             for (int bi = 0; bi < TMI; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < NJ; ++bj) {
                     const int n = nt * WBN + wgrid_bcol<WL, EPI>(wn, bj) + (lane & 31);
-                    if (n >= p.Nout) continue;
+                    if (n >= p.Nout || !keep) continue;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int i = m0 + wrow0 + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
@@ -983,7 +1039,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 template <int KIND, int EPI, int RING, int WL>
 hipError_t launch_wide(const Bf16Params &p, hipStream_t s)
 {
-    const int lds = wide_lds_bytes<EPI>() + table_bytes(p.G);
+    const int lds = wide_lds_bytes<EPI>() + table_bytes(p.G) + (KIND == kWgrad ? 4 * p.G : 0);
     auto kern = gg_bf16_wide_kernel<KIND, EPI, RING, WL>;
     static LdsLimit lds_limit;
     hipError_t e = lds_limit.ensure((const void *)kern, lds);
@@ -993,7 +1049,7 @@ hipError_t launch_wide(const Bf16Params &p, hipStream_t s)
     if (e != hipSuccess) return e;
     int64_t tiles_max;
     if (KIND == kWgrad)
-        tiles_max = (int64_t)p.G * p.tilesM * p.tilesN;
+        tiles_max = ((int64_t)p.G + (p.split_len > 0 ? p.M / p.split_len : 0)) * p.tilesM * p.tilesN;
     else
         tiles_max = (p.M / WBM + p.G) * (int64_t)p.tilesN;
     const int64_t grid = persistent_grid(occ, tiles_max);
@@ -1013,6 +1069,54 @@ hipError_t launch_wide_ring(const Bf16Params &p, hipStream_t s)
     return launch_wide<KIND, EPI, KIND == kFwdKContig ? 0 : KIND == kFwdNContig ? 2 : 1, KIND == kFwdNContig ? 1 : 0>(p, s);
 }
 
+// Second pass of the split weight gradient.  Every workgroup rebuilds the
+// chunk table from the lengths, lists the experts cut into more than one
+// chunk, then walks (expert, 1024-float block) pairs: main_grad += partial of
+// chunk 1, then chunk 2, ..., each add one fp32 rounding, in chunk order.
+__global__ __launch_bounds__(256) void wgrad_split_reduce_kernel(Bf16Params p)
+{
+    extern __shared__ __attribute__((aligned(16))) int sm_red[];
+    GroupTable tab;
+    tab.G = p.G;
+    tab.row0 = sm_red;
+    tab.rows = sm_red + p.G;
+    tab.tile0 = sm_red + 2 * p.G;
+    int *s_scan = tab.tile0 + p.G + 1;
+    int *slot0 = sm_red + 3 * p.G + 1 + 8;
+    int *list = slot0 + p.G;                // split experts, in order
+    const TilesWgradSplit tw{1, p.accumulate, p.split_len};
+    build_group_table<TilesWgradSplit, 256>(tab, p.lens, p.offs, p.G, p.M, tw, nullptr, s_scan);
+    wgrad_slot_table<256>(tab, tw, slot0, s_scan);
+    // compact list of the experts with more than one chunk
+    const int per = (p.G + 255) / 256, g0 = (int)threadIdx.x * per;
+    int v = 0;
+    for (int i = 0; i < per; ++i)
+        if (g0 + i < p.G && tw.chunks(tab.rows[g0 + i]) > 1) ++v;
+    int nsplit;
+    int pos = block_exclusive_scan<256>(v, s_scan, &nsplit);
+    for (int i = 0; i < per; ++i)
+        if (g0 + i < p.G && tw.chunks(tab.rows[g0 + i]) > 1) list[pos++] = g0 + i;
+    __syncthreads();
+    const int64_t P = (int64_t)p.Mout * p.Nout;        // floats per expert (a multiple of 4)
+    const int64_t nblk = (P / 4 + 255) / 256;
+    for (int64_t w = blockIdx.x; w < (int64_t)nsplit * nblk; w += gridDim.x) {
+        const int g = list[w / nblk];
+        const int64_t q = (w % nblk) * 256 + threadIdx.x;   // float4 index inside the expert
+        if (q >= P / 4) continue;
+        const int nch = tw.chunks(tab.rows[g]);
+        floatx4 *mg = (floatx4 *)((float *)p.out + (int64_t)g * p.o_gstride) + q;
+        floatx4 acc = *mg;
+        for (int c = 1; c < nch; ++c) {
+            const int slot = slot0[g] + c - 1;
+            if (slot >= p.nslots) break;
+            const floatx4 v4 = *((const floatx4 *)(p.partials + (int64_t)slot * p.o_gstride) + q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += v4[e];
+        }
+        *mg = acc;
+    }
+}
+
 __global__ void queue_reset_kernel(uint32_t *sched)
 {
     const int i = threadIdx.x;
@@ -1023,6 +1127,18 @@ __global__ void queue_reset_kernel(uint32_t *sched)
 
 int bf16_tile_m(int narrow) { return narrow ? BM : WBM; }
 int bf16_tile_n() { return BN; }
+
+hipError_t launch_wgrad_split_reduce(const Bf16Params &p, hipStream_t s)
+{
+    const int lds = 4 * (5 * p.G + 1 + 8);
+    const int64_t P4 = (int64_t)p.Mout * p.Nout / 4;
+    int64_t grid = (int64_t)device_cus() * 4;
+    const int64_t most = ((P4 + 255) / 256) * (p.M / p.split_len);   // split experts <= M / split_len
+    if (grid > most) grid = most;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(wgrad_split_reduce_kernel, dim3((unsigned)grid), dim3(256), lds, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_queue_reset(uint32_t *sched, hipStream_t s)
 {

@@ -34,6 +34,9 @@ struct Bf16Params {
     float swiglu_limit;  // SwiGLU clamp (forward and backward epilogues); +inf for none
     uint16_t *save;      // kEpiSwigluSave: the GEMM output [M, Nout] bf16 (gate | up) kept for the backward
     int ldsave;          // its row stride (elements)
+    int split_len;       // wgrad: token chunk length of the split reduction, or 0 (one chunk per expert)
+    float *partials;     // wgrad with split_len: nslots fp32 [Mout, Nout] partial sums in the workspace
+    int nslots;
 };
 
 enum Bf16Kind { kFwdKContig = 0, kFwdNContig = 1, kWgrad = 2 };
@@ -44,6 +47,9 @@ enum Epi { kEpiNone = 0, kEpiSwiglu = 1, kEpiSwigluMxfp4 = 2, kEpiDSwiglu = 3, k
 constexpr bool epi_glu(int epi) { return epi == kEpiSwiglu || epi == kEpiSwigluMxfp4 || epi == kEpiSwigluSave; }
 
 hipError_t launch_bf16(const Bf16Params &p, int kind, int epi, hipStream_t s);
+// Split weight gradient, second pass: for every expert cut into more than one
+// token chunk, main_grad[g] += the partial sums of chunks 1, 2, ... in order.
+hipError_t launch_wgrad_split_reduce(const Bf16Params &p, hipStream_t s);
 int bf16_tile_m(int narrow);
 int bf16_tile_n();
 

@@ -89,11 +89,25 @@ def test_workspace_sizes_host_only():
     G, M, N, K = 32, 65536, 5760, 2880
     base = pt.pt_grouped_gemm_workspace_size(pt.PT_OP_FWD, 1, 1, 1, 1, pt.PT_BF16)
     assert base == 1280
-    assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, pt.PT_BF16) == base
+
+    # the weight gradient's split reduction: floor(M / L) fp32 [K, N] slots,
+    # L = max(512, ceil(M * tiles / 1024)), tiles = ceil(K/256) * ceil(N/256)
+    def split(M, N, K):
+        tiles = -(-K // 256) * -(-N // 256)
+        L = max(512, -(-M * tiles // 1024))
+        return r256((M // L) * K * N * 4)
+    assert split(M, N, K) == r256(3 * K * N * 4)            # L = 17664 here: three slots
+    assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, pt.PT_BF16) == base + split(M, N, K)
     for dt in (pt.PT_MXFP8_E4M3, pt.PT_MXFP4_E2M1):
-        assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, dt) == base + r256(M * K * 2) + r256(M * N * 2)
+        assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, dt) == \
+            base + r256(M * K * 2) + r256(M * N * 2) + split(M, N, K)
     assert (pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, pt.PT_FP8_E4M3) ==
-            base + r256(M * K * 2) + r256(M * N * 2) + r256(G * K * N * 4))
+            base + r256(M * K * 2) + r256(M * N * 2) + r256(G * K * N * 4) + split(M, N, K))
+    # one output tile per expert and 14030 rows: 512-token chunks, 27 slots
+    assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, 7, 14030, 256, 256, pt.PT_BF16) == \
+        base + 27 * 256 * 256 * 4
+    # fewer rows than one chunk: nothing to split
+    assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, 4, 500, 256, 256, pt.PT_BF16) == base
     # the MX forward adds stage-major scale copies: more than the queues alone
     assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_FWD, G, M, N, K, pt.PT_MXFP8_E4M3) > base
 
