@@ -143,7 +143,9 @@ def make_workspace(dev):
              ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 32, 65536, 5760, 2880, ptm.PT_MXFP8_E4M3),
              ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 256, 49152, 4096, 4096, ptm.PT_MXFP4_E2M1),
              ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_FWD, 256, 49152, 4096, 2048, ptm.PT_MXFP4_E2M1),
-             ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_DGRAD, 32, 65536, 5760, 2880, ptm.PT_MXFP8_E4M3)]
+             ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_DGRAD, 32, 65536, 5760, 2880, ptm.PT_MXFP8_E4M3),
+             ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_DGRAD_SWIGLU, 256, 49152, 4096, 2048, ptm.PT_MXFP8_E4M3),
+             ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_DGRAD_SWIGLU, 256, 49152, 4096, 2048, ptm.PT_MXFP4_E2M1)]
     WS[0] = torch.zeros(max(sizes), dtype=torch.uint8, device=dev)
 
 
@@ -498,6 +500,43 @@ def bench_fc2_bwd(dev, stream, iters, lens):
     return d
 
 
+def bench_fc2_bwd_mx(dev, stream, iters, lens, dtype):
+    """The same FC2 backward with MX operands at the MXFP4 expert-MLP shape:
+    dY quantised along H inside the step (pt_mx_quantize), the transposed
+    weight cache [G, I, H] quantised along H outside it, dH on the scaled
+    matrix cores and the SwiGLU backward in the epilogue."""
+    G, M, I, H = 256, int(lens.sum()), 2048, 4096
+    fmt = "MXFP4" if dtype == ptm.PT_MXFP4_E2M1 else "MXFP8"
+    cb = H // 2 if dtype == ptm.PT_MXFP4_E2M1 else H
+    lens_d = torch.as_tensor(lens, device=dev)
+    dy = synth.randn_bf16((M, H), seed=111, std=1e-2, device=dev)
+    w2t = synth.randn_bf16((G * I, H), seed=112, std=H ** -0.5, device=dev)
+    wq = torch.empty((G * I, cb), dtype=torch.uint8, device=dev)
+    ws_ = torch.empty((G * I, H // 32), dtype=torch.uint8, device=dev)
+    ptm.pt_mx_quantize(w2t, wq, ws_, G * I, H, dtype, 1, stream=stream)
+    del w2t
+    dq = torch.empty((M, cb), dtype=torch.uint8, device=dev)
+    ds = torch.empty((M, H // 32), dtype=torch.uint8, device=dev)
+    c = synth.randn_bf16((M, 2 * I), seed=113, std=2.0, device=dev)
+    dc = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        ptm.pt_mx_quantize(dy, dq, ds, M, H, dtype, 1, stream=stream)
+        ptm.pt_grouped_gemm_dgrad_swiglu(dq, wq, c, dc, lens_d, None, G, M, H, I, 0, workspace=WS[0],
+                                         stream=stream, swiglu_limit=10.0, dtype=dtype, dy_scale=ds, b_scale=ws_)
+
+    _, per = time_launches(step, iters, 2, stream)
+    flops = 2.0 * M * I * H
+    el = 0.5 if dtype == ptm.PT_MXFP4_E2M1 else 1.0
+    w_bytes = bytes_weights(lens, int(I * H * (el + 1 / 32)))
+    nbytes = w_bytes + M * H * 2 + int(M * H * (el + 1 / 32)) * 2 + 2 * (M * 2 * I * 2)
+    d = summary(f"{fmt} FC2 dgrad + fused clamped SwiGLU backward (dY quantise included), 256 experts, "
+                f"M=49152, I=2048, H=4096", "mxfp4" if dtype == ptm.PT_MXFP4_E2M1 else "mxfp8", flops, nbytes, per)
+    del dy, wq, ws_, dq, ds, c, dc
+    torch.cuda.empty_cache()
+    return d
+
+
 def bench_cfg3_wgrad(dev, stream, iters):
     """The MXFP8 workload's weight gradient: A [65536, 2880] and dY
     [65536, 5760] quantised along tokens in blocks of 32 inside each expert,
@@ -747,6 +786,8 @@ def main():
         if want is None or "fc2bwd" in want:
             log("per_config: FC2 dgrad + SwiGLU backward")
             per["fc2_bf16_dgrad_swiglu_bwd"] = bench_fc2_bwd(dev, stream, iters, b_keep_lens)
+            per["fc2_mxfp8_dgrad_swiglu_bwd"] = bench_fc2_bwd_mx(dev, stream, iters, b_keep_lens, ptm.PT_MXFP8_E4M3)
+            per["fc2_mxfp4_dgrad_swiglu_bwd"] = bench_fc2_bwd_mx(dev, stream, iters, b_keep_lens, ptm.PT_MXFP4_E2M1)
         line["per_config"] = per
     print(json.dumps(line), flush=True)
 

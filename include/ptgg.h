@@ -244,8 +244,19 @@ int pt_grouped_gemm_fwd_swiglu_save(const void *a, const uint8_t *a_scale,
  *     dC[r, K + j] = bf16( dH * g * s ),   s = 1 / (1 + exp(-g))
  * (the derivative of silu(g) * u; dH is rounded to bf16 first, as the
  * unfused dgrad would store it, and the rest runs in fp32).
- *  dy       [M, N] bf16 (gradient of FC2's output);  b  FC2's weight as in
- *           pt_grouped_gemm_fwd (trans_b selects [G,K,N] or [G,N,K]);
+ *  dtype    PT_BF16: dy [M, N] bf16 (gradient of FC2's output), b FC2's
+ *           weight as in pt_grouped_gemm_fwd (trans_b selects [G,K,N] or
+ *           [G,N,K]), the scale arguments NULL.
+ *           PT_MXFP8_E4M3, PT_MXFP4_E2M1, PT_FP8_E4M3, PT_FP8_E4M3_ROWWISE:
+ *           dy, dy_scale, b, b_scale as pt_grouped_gemm_dgrad takes them
+ *           for the dtype (dY quantised along N, the weight's transposed
+ *           cache [G, K, N], trans_b = 0), so dH is that call's output; the
+ *           low-precision training step of the expert MLP (Primus-Turbo
+ *           README, "What's New": FP8 / MXFP8 grouped MLP with SwiGLU folded
+ *           into the grouped GEMM; the DeepSeek-V4 blog's knob table lists
+ *           swiglu_limit for FP8 and FP4 stability).  MXFP4 with N % 256 !=
+ *           0 needs the workspace of pt_grouped_gemm_workspace_size
+ *           (PT_OP_DGRAD_SWIGLU, ...), else PT_ERR_UNSUPPORTED.
  *  c_saved  [M, 2K] bf16, FC1's output [gate | up] saved by the forward;
  *  dc       [M, 2K] bf16 output; rows outside every expert are not written.
  *  All four 16-byte aligned.  Requirements: N % 8 == 0, K % 8 == 0.
@@ -255,9 +266,10 @@ int pt_grouped_gemm_fwd_swiglu_save(const void *a, const uint8_t *a_scale,
  *           dC[r, K + j] = 0 where |u| > L).
  *  workspace  optional (may be NULL), as for pt_grouped_gemm_dgrad.
  */
-int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_saved, void *dc,
+int pt_grouped_gemm_dgrad_swiglu(const void *dy, const uint8_t *dy_scale, const void *b, const uint8_t *b_scale,
+                                 const void *c_saved, void *dc,
                                  const int64_t *group_lens, const int64_t *group_offs,
-                                 int64_t G, int64_t M, int64_t N, int64_t K, int trans_b,
+                                 int64_t G, int64_t M, int64_t N, int64_t K, int dtype, int trans_b,
                                  float swiglu_limit, void *workspace, size_t workspace_bytes, void *stream);
 
 /*

@@ -76,7 +76,7 @@ def load(require_gpu: bool = True):
     L.pt_grouped_gemm_dgrad.restype = i32
     L.pt_grouped_gemm_dgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, p, sz, p]
     L.pt_grouped_gemm_dgrad_swiglu.restype = i32
-    L.pt_grouped_gemm_dgrad_swiglu.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i32, f32, p, sz, p]
+    L.pt_grouped_gemm_dgrad_swiglu.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, f32, p, sz, p]
     L.pt_grouped_gemm_wgrad.restype = i32
     L.pt_grouped_gemm_wgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
     L.pt_mx_quantize.restype = i32
@@ -178,11 +178,13 @@ def pt_grouped_gemm_fwd_swiglu_save(a, a_scale, b, b_scale, h, c, group_lens, gr
 
 
 def pt_grouped_gemm_dgrad_swiglu(dy, b, c_saved, dc, group_lens, group_offs,
-                                 G, M, N, K, trans_b, workspace=None, stream=None, swiglu_limit=0.0):
+                                 G, M, N, K, trans_b, workspace=None, stream=None, swiglu_limit=0.0,
+                                 dtype=PT_BF16, dy_scale=None, b_scale=None):
     L = load()
     _check("pt_grouped_gemm_dgrad_swiglu", L.pt_grouped_gemm_dgrad_swiglu(
-        _ptr(dy), _ptr(b), _ptr(c_saved), _ptr(dc), _ptr(group_lens), _ptr(group_offs),
-        G, M, N, K, trans_b, swiglu_limit, _ptr(workspace), _nbytes(workspace), _stream(stream)))
+        _ptr(dy), _ptr(dy_scale), _ptr(b), _ptr(b_scale), _ptr(c_saved), _ptr(dc), _ptr(group_lens),
+        _ptr(group_offs), G, M, N, K, dtype, trans_b, swiglu_limit, _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))
 
 
 def pt_grouped_gemm_wgrad(a, a_scale, dy, dy_scale, main_grad, group_lens, group_offs,

@@ -253,7 +253,7 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
                    uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
                    int64_t N, int64_t K, int dtype, int ep, int64_t Nc, int64_t ldo, float swiglu_limit,
                    void *workspace, size_t workspace_bytes, hipStream_t s, uint16_t *save = nullptr,
-                   bool timing = true)
+                   bool timing = true, const uint16_t *aux = nullptr)
 {
     const bool tensor_scales = dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE;
     if (N % 8) return PT_ERR_UNSUPPORTED;              // outputs leave in 16-byte chunks
@@ -266,6 +266,8 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
     p.swiglu_limit = swiglu_clamp(swiglu_limit);
     p.save = save;
     p.ldsave = (int)N;
+    p.aux = aux;
+    p.ldaux = (int)(2 * N);
     p.a = (const uint8_t *)a;
     p.as = a_scale;
     p.b = (const uint8_t *)b;
@@ -280,7 +282,7 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
     p.N = (int)N;
     p.K = (int)K;
     p.ldo = (int)ldo;
-    const int tn = ep == kEpiNone ? mx_tile_n() : mx_tile_n() / 2;
+    const int tn = epi_glu(ep) ? mx_tile_n() / 2 : mx_tile_n();
     p.tilesN = (int)((Nc + tn - 1) / tn);
     p.sched = queue_words(workspace, workspace_bytes);
     if (tensor_scales) {
@@ -298,10 +300,11 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
                                                  mx_swz_b_bytes(G, N, K, fmt));
     // the SwiGLU that keeps its input exists for the 256 x 256 kernel only,
     // which E2M1 with K % 256 != 0 reaches through the scale copies alone
-    if (ep == kEpiSwigluSave && fmt == 1 && K % 256 && !swz) return PT_ERR_UNSUPPORTED;
+    const bool wide_only = ep == kEpiSwigluSave || ep == kEpiDSwiglu;
+    if (wide_only && fmt == 1 && K % 256 && !swz) return PT_ERR_UNSUPPORTED;
     uint32_t *queues = p.sched;
     const TuneKey key = tune_key(op, dtype, ep, 0, G, M, N, K);
-    return configured(key, cfg_mask(queues != nullptr, !tensor_scales && ep != kEpiSwigluSave), timing, s, [&](int cfg) {
+    return configured(key, cfg_mask(queues != nullptr, !tensor_scales && !wide_only), timing, s, [&](int cfg) {
         p.narrow = (cfg & kCfgNarrow) != 0;
         p.sched = (cfg & kCfgStatic) ? nullptr : queues;
         p.sa = p.sb = nullptr;
@@ -555,10 +558,11 @@ int pt_grouped_gemm_fwd_swiglu_save(const void *a, const uint8_t *a_scale, const
     });
 }
 
-int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_saved, void *dc,
-                                 const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
-                                 int64_t N, int64_t K, int trans_b, float swiglu_limit, void *workspace,
-                                 size_t workspace_bytes, void *stream)
+int pt_grouped_gemm_dgrad_swiglu(const void *dy, const uint8_t *dy_scale, const void *b, const uint8_t *b_scale,
+                                 const void *c_saved, void *dc, const int64_t *group_lens,
+                                 const int64_t *group_offs, int64_t G, int64_t M, int64_t N, int64_t K, int dtype,
+                                 int trans_b, float swiglu_limit, void *workspace, size_t workspace_bytes,
+                                 void *stream)
 {
     if (swiglu_limit != swiglu_limit) return PT_ERR_INVALID_ARG;   // NaN
     int st = check_groups(group_lens, G, M);
@@ -570,6 +574,17 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const void *b, const void *c_sa
     if (!fits31(M * N * 2) || !fits31(N * K * 2)) return PT_ERR_UNSUPPORTED;
     if (!aligned16(dy) || !aligned16(b) || !aligned16(c_saved) || !aligned16(dc)) return PT_ERR_MISALIGNED;
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE) {
+        // dH as pt_grouped_gemm_dgrad computes it for the dtype (dY packed
+        // and scaled along N, the weight's transposed cache [G, K, N]), then
+        // the same SwiGLU-backward epilogue
+        if (trans_b) return PT_ERR_UNSUPPORTED;
+        return mx_gemm(PT_OP_DGRAD_SWIGLU, dy, dy_scale, b, b_scale, dc, nullptr, group_lens, group_offs, G, M, K, N,
+                       dtype, kEpiDSwiglu, K, 2 * K, swiglu_limit, workspace, workspace_bytes, (hipStream_t)stream,
+                       nullptr, true, (const uint16_t *)c_saved);
+    }
+    if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
+    if (dy_scale || b_scale) return PT_ERR_INVALID_ARG;
     // dH[r, k] = sum_n dY[r, n] B[k, n] as in pt_grouped_gemm_dgrad; the
     // epilogue turns each bf16 dH tile into the [gate | up] gradient.
     Bf16Params p = {};
@@ -858,7 +873,8 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, i
     }
     if (op == PT_OP_WGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && M == 0) return kQueueWsBytes;
     // the MX data gradient: K outputs per row, a reduction over N
-    if (op == PT_OP_DGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && G > 0 && M >= 0 && N > 0 &&
+    if ((op == PT_OP_DGRAD || op == PT_OP_DGRAD_SWIGLU) && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) &&
+        G > 0 && M >= 0 && N > 0 &&
         K > 0 && N % 32 == 0) {
         const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
         if (mx_swz_possible(G, M, K, N, fmt))
@@ -888,7 +904,8 @@ int pt_gemm_config_of(int op, int dtype, int epilogue, int trans, int64_t G, int
     case PT_OP_WGRAD:      // every dtype's weight gradient runs the BF16 kernel
         return tune_lookup(tune_key(op, PT_BF16, kEpiNone, trans, G, M, N, K));
     case PT_OP_DGRAD_SWIGLU:
-        return tune_lookup(tune_key(op, PT_BF16, kEpiDSwiglu, trans, G, M, N, K));
+        if (dtype == PT_BF16) return tune_lookup(tune_key(op, PT_BF16, kEpiDSwiglu, trans, G, M, N, K));
+        return tune_lookup(tune_key(op, dtype, kEpiDSwiglu, 0, G, M, K, N));
     default:
         return -1;
     }

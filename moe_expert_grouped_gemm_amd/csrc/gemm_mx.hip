@@ -650,7 +650,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         o.avoff = (uint32_t)(m0 + (tid >> 3)) * Kb + o.chunk;
 #pragma unroll
         for (int i = 0; i < W_LOADS; ++i) o.adelta[i] = (uint32_t)(i * 64) * Kb;
-        if (EPI == kEpiNone) {
+        if (!epi_glu(EPI)) {
             o.bvoff = (uint32_t)(nt * WBN + (tid >> 3)) * Kb + o.chunk;
 #pragma unroll
             for (int i = 0; i < W_LOADS; ++i) o.bdelta[i] = (uint32_t)(i * 64) * Kb;
@@ -887,8 +887,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                     for (int bj = 0; bj < 4; ++bj) acc[bi][bj][r] *= fa * fb[bj];
                 }
         }
-        store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn, p.swiglu_limit, p.save,
-                               p.ldsave);
+        store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn, p.swiglu_limit,
+                               p.save, p.ldsave, p.aux, p.ldaux);
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
         par ^= 1;
     }
@@ -917,6 +917,7 @@ hipError_t launch_wide_epi(const MxParams &p, int epi, hipStream_t s)
     if (epi == kEpiSwiglu) return launch_wide<FMT, kEpiSwiglu, WSC>(p, s);
     if (epi == kEpiSwigluMxfp4) return launch_wide<FMT, kEpiSwigluMxfp4, WSC>(p, s);
     if (epi == kEpiSwigluSave) return launch_wide<FMT, kEpiSwigluSave, WSC>(p, s);
+    if (epi == kEpiDSwiglu) return launch_wide<FMT, kEpiDSwiglu, WSC>(p, s);
     return launch_wide<FMT, kEpiNone, WSC>(p, s);
 }
 
@@ -940,7 +941,7 @@ hipError_t launch_one(const MxParams &p, hipStream_t s)
 template <int FMT, int SCM>
 hipError_t launch_epi(const MxParams &p, int epi, hipStream_t s)
 {
-    if (epi == kEpiSwigluSave) return hipErrorInvalidValue;      // the 256 x 256 kernel only
+    if (epi == kEpiSwigluSave || epi == kEpiDSwiglu) return hipErrorInvalidValue;   // the 256 x 256 kernel only
     if (epi == kEpiSwiglu) return launch_one<FMT, kEpiSwiglu, SCM>(p, s);
     if (epi == kEpiSwigluMxfp4) return launch_one<FMT, kEpiSwigluMxfp4, SCM>(p, s);
     return launch_one<FMT, kEpiNone, SCM>(p, s);

@@ -78,6 +78,8 @@ struct MxParams {
     float swiglu_limit;      // SwiGLU clamp; +inf for none
     uint16_t *save;          // kEpiSwigluSave: the GEMM output [M, N] bf16 (gate | up)
     int ldsave;              // its row stride (elements)
+    const uint16_t *aux;     // kEpiDSwiglu: FC1's saved output [gate | up] [M, 2N] bf16
+    int ldaux;               // its row stride (elements)
 };
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);

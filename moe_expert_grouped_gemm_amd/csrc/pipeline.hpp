@@ -411,10 +411,10 @@ template <int EPI, int NWM>
 __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[2][4], uint8_t *smem, void *out,
                                                uint8_t *out_scale, int ldo, int Nout, int64_t row0, int m0, int rows,
                                                int nt, int wm, int wn, float lim, uint16_t *save = nullptr,
-                                               int ldsave = 0)
+                                               int ldsave = 0, const uint16_t *aux = nullptr, int ldaux = 0)
 {
     store_tile_lds_w<EPI, NWM, 2, 4>(acc, smem, out, out_scale, ldo, Nout, row0, m0, rows, nt, wm * 64, wn, lim,
-                                     nullptr, 0, save, ldsave);
+                                     aux, ldaux, save, ldsave);
 }
 
 // ------------------------------------------------------------------ tile queues

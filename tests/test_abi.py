@@ -124,8 +124,8 @@ def test_argument_checks_host_only():
                                  None, 0, None) == 1                                  # G = 0
     assert L.pt_grouped_gemm_fwd(None, None, None, None, None, None, lp, None, 4, 10, 64, 64, 0, 0, 1, math.nan,
                                  None, 0, None) == 1                                  # NaN limit
-    assert L.pt_grouped_gemm_dgrad_swiglu(None, None, None, None, lp, None, 4, 10, 64, 64, 0, math.nan,
-                                          None, 0, None) == 1
+    assert L.pt_grouped_gemm_dgrad_swiglu(None, None, None, None, None, None, lp, None, 4, 10, 64, 64, 0, 0,
+                                          math.nan, None, 0, None) == 1
     assert L.pt_stack_experts(None, None, 2, 64, 64, 2, None, 0, None) == 1          # layout flag
     assert L.pt_stack_experts(None, None, 2, 60, 64, 0, None, 0, None) == 2          # rows % 8
     assert L.pt_stack_experts(None, None, 0, 64, 64, 0, None, 0, None) == 0          # nothing to do

@@ -107,12 +107,19 @@ def test_dgrad_swiglu_empty_batch_and_errors(dev):
     cc = torch.zeros((8, 128), dtype=torch.bfloat16, device=dev)
     st = torch.cuda.current_stream().cuda_stream
     # a missing saved FC1 output, an odd K, and a bad layout flag are refused
-    assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), w.data_ptr(), None, cc.data_ptr(), lens1.data_ptr(),
-                                          None, 1, 8, 64, 64, 0, 0.0, None, 0, st) == 1
-    assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), w.data_ptr(), cc.data_ptr(), cc.data_ptr(),
-                                          lens1.data_ptr(), None, 1, 8, 64, 60, 0, 0.0, None, 0, st) == 2
-    assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), w.data_ptr(), cc.data_ptr(), cc.data_ptr(),
-                                          lens1.data_ptr(), None, 1, 8, 64, 64, 2, 0.0, None, 0, st) == 1
+    assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), None, w.data_ptr(), None, None, cc.data_ptr(),
+                                          lens1.data_ptr(), None, 1, 8, 64, 64, ptm.PT_BF16, 0, 0.0, None, 0, st) == 1
+    assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), None, w.data_ptr(), None, cc.data_ptr(), cc.data_ptr(),
+                                          lens1.data_ptr(), None, 1, 8, 64, 60, ptm.PT_BF16, 0, 0.0, None, 0, st) == 2
+    assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), None, w.data_ptr(), None, cc.data_ptr(), cc.data_ptr(),
+                                          lens1.data_ptr(), None, 1, 8, 64, 64, ptm.PT_BF16, 2, 0.0, None, 0, st) == 1
+    # BF16 takes no scales; the low-precision dtypes need the [G, K, N] cache (trans_b = 0)
+    assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), t.data_ptr(), w.data_ptr(), None, cc.data_ptr(),
+                                          cc.data_ptr(), lens1.data_ptr(), None, 1, 8, 64, 64, ptm.PT_BF16, 0, 0.0,
+                                          None, 0, st) == 1
+    assert L.pt_grouped_gemm_dgrad_swiglu(t.data_ptr(), t.data_ptr(), w.data_ptr(), t.data_ptr(), cc.data_ptr(),
+                                          cc.data_ptr(), lens1.data_ptr(), None, 1, 8, 64, 64, ptm.PT_MXFP8_E4M3, 1,
+                                          0.0, None, 0, st) == 2
 
 
 def test_dgrad_swiglu_mlp_shape_sampled(orc, dev):
