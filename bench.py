@@ -75,6 +75,27 @@ FLUSH_BYTES = 512 << 20       # twice the 256 MB MALL (the last-level cache in f
 FLUSH = [None]
 
 
+# per_config rows -> the profiled kernels whose HBM bytes per launch (from the
+# counter summaries in profiles/) make up that row's `traffic`
+TRAFFIC_KEYS = {
+    "cfg2_bf16_dgrad": ["cfg2_bf16_dgrad"],
+    "cfg2_bf16_wgrad": ["cfg2_bf16_wgrad"],
+    "cfg3_mxfp8_fwd": ["cfg3_mxfp8_fwd"],
+    "cfg3_mxfp8_quantize_A": ["cfg3_mx_quantize_e4m3_A"],
+    "cfg4_mxfp4_mlp": ["cfg4_mx_quantize_e2m1_X", "cfg4_mxfp4_fc1_swiglu_mxfp4", "cfg4_mxfp4_fc2"],
+    "fc2_bf16_dgrad_swiglu_bwd": ["fc2_bf16_dgrad_swiglu_bwd"],
+    "fc2_mxfp8_dgrad_swiglu_bwd": ["fc2_mxfp8_dgrad_swiglu_bwd"],
+    "fc2_mxfp4_dgrad_swiglu_bwd": ["fc2_mxfp4_dgrad_swiglu_bwd"],
+}
+
+
+def attach_traffic(per):
+    for row, keys in TRAFFIC_KEYS.items():
+        if row in per:
+            vals = [measured_traffic(k) for k in keys]
+            per[row]["roofline"]["traffic"] = None if any(v is None for v in vals) else int(sum(vals))
+
+
 def time_launches(fn, steps, warmup, stream, flush=True):
     """Warm up, then time exactly `steps` calls: wall clock between two
     device synchronisations, and each launch between HIP events on the
@@ -788,6 +809,7 @@ def main():
             per["fc2_bf16_dgrad_swiglu_bwd"] = bench_fc2_bwd(dev, stream, iters, b_keep_lens)
             per["fc2_mxfp8_dgrad_swiglu_bwd"] = bench_fc2_bwd_mx(dev, stream, iters, b_keep_lens, ptm.PT_MXFP8_E4M3)
             per["fc2_mxfp4_dgrad_swiglu_bwd"] = bench_fc2_bwd_mx(dev, stream, iters, b_keep_lens, ptm.PT_MXFP4_E2M1)
+        attach_traffic(per)
         line["per_config"] = per
     print(json.dumps(line), flush=True)
 
