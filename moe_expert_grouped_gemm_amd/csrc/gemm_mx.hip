@@ -541,11 +541,14 @@ struct WOps {
     bool b_once;                    // weights read by this tile alone: non-temporal
 };
 
-// Issue the operand loads of stage kt into ring slot st (branch-free: a
-// thread whose chunk lies past the row length in a partial last stage, and
-// every thread of a stage past the end, gets an offset past the bound).
+// Issue the operand loads of stage kt into the ring slot at LDS byte st: NA
+// A loads per thread (the tile's rows), then the B loads at st + boff
+// (branch-free: a thread whose chunk lies past the row length in a partial
+// last stage, and every thread of a stage past the end, gets an offset past
+// the bound).
+template <int NA>
 __device__ __forceinline__ void wissue_stage(uint8_t *smem, const WOps &o, uint32_t st, int kt, int nk, int Kb,
-                                             int wave)
+                                             int wave, uint32_t boff)
 {
     const int k0 = kt * WROW;
     const int room = kt < nk ? Kb - k0 : 0;
@@ -553,13 +556,13 @@ __device__ __forceinline__ void wissue_stage(uint8_t *smem, const WOps &o, uint3
     const uint32_t va = ok ? o.avoff + k0 : kOOB, vb = ok ? o.bvoff + k0 : kOOB;
     uint8_t *lds = smem + st + wave * kWave * 16;
 #pragma unroll
-    for (int i = 0; i < W_LOADS; ++i) dma16(o.a, o.abytes, lds + i * WTHREADS * 16, va, o.adelta[i]);
+    for (int i = 0; i < NA; ++i) dma16(o.a, o.abytes, lds + i * WTHREADS * 16, va, o.adelta[i]);
     if (o.b_once) {
 #pragma unroll
-        for (int i = 0; i < W_LOADS; ++i) dma16_nt(o.b, o.bbytes, lds + WA_BYTES + i * WTHREADS * 16, vb, o.bdelta[i]);
+        for (int i = 0; i < W_LOADS; ++i) dma16_nt(o.b, o.bbytes, lds + boff + i * WTHREADS * 16, vb, o.bdelta[i]);
     } else {
 #pragma unroll
-        for (int i = 0; i < W_LOADS; ++i) dma16(o.b, o.bbytes, lds + WA_BYTES + i * WTHREADS * 16, vb, o.bdelta[i]);
+        for (int i = 0; i < W_LOADS; ++i) dma16(o.b, o.bbytes, lds + boff + i * WTHREADS * 16, vb, o.bdelta[i]);
     }
 }
 
@@ -570,12 +573,19 @@ __device__ __forceinline__ uintx4 wld(uint32_t addr)
     return ldsr_u128<OFF>(addr);
 }
 
+// The ring per tile height: a 256-row tile keeps two 64 KiB slots (one
+// stage in flight while one computes); a tile of at most 128 rows has 16 KiB
+// A slots, so three 48 KiB slots fit and two stages are in flight -- such a
+// tile has half the MFMAs per stage, and its loads would otherwise wait.
+constexpr int MX_RING = 3 * (128 * WROW + WBN * WROW);
+static_assert(MX_RING >= 2 * WSTAGE, "ring sizes");
+
 // LDS of the ring or of the epilogue tile, whichever is larger; the group
 // table follows it.
 template <int EPI>
 constexpr int wide_lds_bytes()
 {
-    return 2 * WSTAGE > epi_lds_bytes<EPI, 4>() ? 2 * WSTAGE : epi_lds_bytes<EPI, 4>();
+    return MX_RING > epi_lds_bytes<EPI, 4>() ? MX_RING : epi_lds_bytes<EPI, 4>();
 }
 
 template <int FMT, int EPI, int WSC>
@@ -614,16 +624,16 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
     const int nk = (Kb + WROW - 1) / WROW, nfull = Kb / WROW;
     const int nb_last = (Kb - nfull * WROW) / 32;           // E4M3 blocks of the partial stage
 
-    // per-lane fragment bases (slot 0 / 1): chunk 2j + h of the lane's first
-    // A row / B row is at base ^ (j << 5)
-    uint32_t aB[2], bB[2];
+    // per-lane fragment bases of a 256-row tile in slot 0 / 1: chunk 2j + h
+    // of the lane's first A row / B row is at base ^ (j << 5)
+    uint32_t aT[2], bT[2];
     {
         const uint32_t y = (uint32_t)((h ^ (r32 >> 1)) & 1) * 16u | (uint32_t)(((r32 >> 1) & 6) << 4);
         const uint32_t ra = (uint32_t)(wm * 64 + r32), rb = (uint32_t)(wn * 128 + r32);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            aB[s] = lds0 + s * WSTAGE + ra * WROW + y;
-            bB[s] = lds0 + s * WSTAGE + WA_BYTES + rb * WROW + y;
+            aT[s] = lds0 + s * WSTAGE + ra * WROW + y;
+            bT[s] = lds0 + s * WSTAGE + WA_BYTES + rb * WROW + y;
         }
     }
 
@@ -635,8 +645,41 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         const int tm = (rows + WBM - 1) / WBM;
         const int nt = local / tm, mt = local % tm;
         const int m0 = mt * WBM;
-        const int vr = min(WBM, rows - m0) - wm * 64;
-        const int nvalid_bi = vr <= 0 ? 0 : (vr > 32 ? 2 : 1);
+
+        // One tile of TMI 32-row blocks per wave: a row block holding at most
+        // 128 valid rows runs as a 128-row tile (every wave 32 rows) on the
+        // three-slot ring, others as a 256-row tile on two slots.  The tile
+        // ids, B panel and the order of every accumulation are the same for
+        // both heights, so results do not depend on it.
+        auto run_tile = [&](auto MIC) {
+        constexpr int TMI = decltype(MIC)::value;
+        constexpr int TBM = TMI * 128;                      // tile rows
+        constexpr int NS = TMI == 2 ? 2 : 3;                // ring slots
+        constexpr int ASLOT = TBM * WROW, SLOT = ASLOT + WBN * WROW;
+        constexpr int TNA = ASLOT / 16 / WTHREADS;          // A loads per thread per stage
+        constexpr bool CONST_SC = WSC == kWConst || WSC == kWConstRow;
+        constexpr int NLS = TNA + W_LOADS + (CONST_SC ? 0 : 6);   // vector-memory ops per stage
+        static_assert(NS * SLOT <= MX_RING, "ring fits");
+        // a 128-row tile's per-wave offsets take a zero the compiler cannot
+        // see through, so they are computed per tile rather than hoisted out
+        // of the tile loop and kept live through the 256-row path
+        uint32_t z = 0;
+        if constexpr (TMI == 1) asm volatile("" : "+s"(z));
+        const int wrow0 = wm * TMI * 32 + (int)z;
+        const int vr = min(TBM, rows - m0) - wrow0;
+        const int nvalid_bi = vr <= 0 ? 0 : min(TMI, (vr + 31) >> 5);
+        // LDS address of chunk pair c (c = j << 5) in ring slot sl.  A 128-row
+        // tile derives it from the 256-row tile's slot-0 bases (slot and row
+        // offsets are multiples of 256 bytes, so they add after the XOR).
+        const uint32_t a1 = aT[0] + z, b1 = bT[0] + z;
+        auto aX = [&](int sl, uint32_t c) {
+            if constexpr (TMI == 2) return aT[sl] ^ c;
+            else return (a1 ^ c) + ((uint32_t)(sl * SLOT) - (uint32_t)(wm * 32 * WROW));
+        };
+        auto bX = [&](int sl, uint32_t c) {
+            if constexpr (TMI == 2) return bT[sl] ^ c;
+            else return (b1 ^ c) + (uint32_t)(sl * SLOT - (WA_BYTES - ASLOT));
+        };
 
         // ---- operand loads: slot i * 512 + t holds chunk c = (t & 7) ^ ((t >> 4) & 7)
         // of tile row i * 64 + t / 8
@@ -649,7 +692,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         o.chunk = (uint32_t)(((tid & 7) ^ ((tid >> 4) & 7)) * 16);
         o.avoff = (uint32_t)(m0 + (tid >> 3)) * Kb + o.chunk;
 #pragma unroll
-        for (int i = 0; i < W_LOADS; ++i) o.adelta[i] = (uint32_t)(i * 64) * Kb;
+        for (int i = 0; i < TNA; ++i) o.adelta[i] = (uint32_t)(i * 64) * Kb;
         if (!epi_glu(EPI)) {
             o.bvoff = (uint32_t)(nt * WBN + (tid >> 3)) * Kb + o.chunk;
 #pragma unroll
@@ -677,7 +720,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             sr.bbytes = sr.bstride * (uint32_t)nk;
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
-                sr.row[bi] = (uint32_t)(row0 + min(m0 + wm * 64 + bi * 32 + r32, rows - 1)) * WPR * 4u + hw;
+                sr.row[bi] = (uint32_t)(row0 + min(m0 + wrow0 + bi * 32 + r32, rows - 1)) * WPR * 4u + hw;
 #pragma unroll
             for (int bj = 0; bj < 4; ++bj)
                 sr.row[2 + bj] =
@@ -690,16 +733,16 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             sr.bbytes = (uint32_t)(((int64_t)p.G * p.N * KS + 3) & ~3ll);
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
-                sr.row[bi] = (uint32_t)((row0 + min(m0 + wm * 64 + bi * 32 + r32, rows - 1)) * KS);
+                sr.row[bi] = (uint32_t)((row0 + min(m0 + wrow0 + bi * 32 + r32, rows - 1)) * KS);
 #pragma unroll
             for (int bj = 0; bj < 4; ++bj)
                 sr.row[2 + bj] =
                     (uint32_t)((g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)) * KS);
         }
 
-        floatx16 acc[2][4];
+        floatx16 acc[TMI][4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TMI; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -713,13 +756,16 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         // prologue: stage 0 (the loads of each stage form one group in
         // program order), and the id of the next tile (its atomic goes out
         // first and lands under the stage's loads)
-        uint32_t sc[2][6];
+        uint32_t sc[NS][6];
         if (tid == 0) tq.issue();
         asm volatile("" ::: "memory");
-        wissue_stage(smem, o, 0, 0, nk, Kb, wave);
-        wload_scales<WSC>(sc[0], sr, 0, nk, h);
-        asm volatile("" ::: "memory");
-        wait_vmcnt<0>();
+#pragma unroll
+        for (int st = 0; st < NS - 1; ++st) {
+            wissue_stage<TNA>(smem, o, st * SLOT, st, nk, Kb, wave, ASLOT);
+            wload_scales<WSC>(sc[st], sr, st, nk, h);
+            asm volatile("" ::: "memory");
+        }
+        wait_vmcnt<(NS - 2) * NLS>();              // stage 0 landed
         if (tid == 0) s_id[par ^ 1] = tq.resolve(tile);
         wait_lgkm0();
         barrier();
@@ -731,22 +777,22 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         uintx4 ea[2][2], eb[2][2][2];       // E4M3 A [chunk][block], B [half][chunk][block]
         auto rdA = [&](uintx4 (&x)[2], uint32_t addr) {
             x[0] = wld<0>(addr);
-            x[1] = wld<RB>(addr);
+            if constexpr (TMI == 2) x[1] = wld<RB>(addr);
         };
         if constexpr (FMT == 1) {
-            rdA(fa[0], aB[0]);
-            fb[0][0] = wld<0 * RB>(bB[0]);
-            fb[0][1] = wld<1 * RB>(bB[0]);
-            fb[0][2] = wld<2 * RB>(bB[0]);
-            fb[0][3] = wld<3 * RB>(bB[0]);
+            rdA(fa[0], aX(0, 0));
+            fb[0][0] = wld<0 * RB>(bX(0, 0));
+            fb[0][1] = wld<1 * RB>(bX(0, 0));
+            fb[0][2] = wld<2 * RB>(bX(0, 0));
+            fb[0][3] = wld<3 * RB>(bX(0, 0));
             asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fb[0][0]), "+v"(fb[0][1]),
                          "+v"(fb[0][2]), "+v"(fb[0][3]));
         } else {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                rdA(ea[c], aB[0] ^ (uint32_t)(c << 5));
-                eb[0][c][0] = wld<0>(bB[0] ^ (uint32_t)(c << 5));
-                eb[0][c][1] = wld<RB>(bB[0] ^ (uint32_t)(c << 5));
+                rdA(ea[c], aX(0, (uint32_t)(c << 5)));
+                eb[0][c][0] = wld<0>(bX(0, (uint32_t)(c << 5)));
+                eb[0][c][1] = wld<RB>(bX(0, (uint32_t)(c << 5)));
             }
             asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ea[0][0]), "+v"(ea[0][1]), "+v"(ea[1][0]), "+v"(ea[1][1]),
                          "+v"(eb[0][0][0]), "+v"(eb[0][0][1]), "+v"(eb[0][1][0]), "+v"(eb[0][1][1]));
@@ -755,20 +801,20 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         int kt0 = 0;
         auto stage = [&](auto PC) {
             constexpr int P = decltype(PC)::value;          // ring slot of stage kt
-            constexpr int Q = P ^ 1;
+            constexpr int Q = (P + 1) % NS, PN = (P + NS - 1) % NS;
             const int kt = kt0 + P;
             uint32_t w[6];
             wscale_words<WSC>(sc[P], w, sr, kt, nfull, nb_last, h);
-            // the next stage's loads go to the other slot, free since the barrier
-            wissue_stage(smem, o, Q * WSTAGE, kt + 1, nk, Kb, wave);
-            wload_scales<WSC>(sc[Q], sr, kt + 1, nk, h);
+            // stage kt + NS - 1 goes to the slot stage kt - 1 freed at its barrier
+            wissue_stage<TNA>(smem, o, PN * SLOT, kt + NS - 1, nk, Kb, wave, ASLOT);
+            wload_scales<WSC>(sc[PN], sr, kt + NS - 1, nk, h);
             asm volatile("" ::: "memory");
             if constexpr (FMT == 1) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const int cur = s & 1, nxt = cur ^ 1;
                     if (s < 3) {
-                        const uint32_t xa = aB[P] ^ (uint32_t)((s + 1) << 5), xb = bB[P] ^ (uint32_t)((s + 1) << 5);
+                        const uint32_t xa = aX(P, (uint32_t)((s + 1) << 5)), xb = bX(P, (uint32_t)((s + 1) << 5));
                         rdA(fa[nxt], xa);
                         fb[nxt][0] = wld<0 * RB>(xb);
                         fb[nxt][1] = wld<1 * RB>(xb);
@@ -776,7 +822,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                         fb[nxt][3] = wld<3 * RB>(xb);
                     }
 #pragma unroll
-                    for (int bi = 0; bi < 2; ++bi)
+                    for (int bi = 0; bi < TMI; ++bi)
                         if (bi < nvalid_bi) {
 #pragma unroll
                             for (int bj = 0; bj < 4; ++bj) mfma(bi, bj, pad8(fa[cur][bi]), pad8(fb[cur][bj]), w, s);
@@ -796,20 +842,20 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                     if (q == 0 || q == 2) {
 #pragma unroll
                         for (int c = 0; c < 2; ++c) {
-                            const uint32_t xb = bB[P] ^ (uint32_t)((2 * s + c) << 5);
+                            const uint32_t xb = bX(P, (uint32_t)((2 * s + c) << 5));
                             eb[1][c][0] = wld<2 * RB>(xb);
                             eb[1][c][1] = wld<3 * RB>(xb);
                         }
                     } else if (q == 1) {
 #pragma unroll
                         for (int c = 0; c < 2; ++c) {
-                            const uint32_t xb = bB[P] ^ (uint32_t)((2 + c) << 5);
+                            const uint32_t xb = bX(P, (uint32_t)((2 + c) << 5));
                             eb[0][c][0] = wld<0>(xb);
                             eb[0][c][1] = wld<RB>(xb);
                         }
                     }
 #pragma unroll
-                    for (int bi = 0; bi < 2; ++bi)
+                    for (int bi = 0; bi < TMI; ++bi)
                         if (bi < nvalid_bi) {
 #pragma unroll
                             for (int k = 0; k < 2; ++k)
@@ -818,7 +864,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                         }
                     if (q == 1) {
 #pragma unroll
-                        for (int c = 0; c < 2; ++c) rdA(ea[c], aB[P] ^ (uint32_t)((2 + c) << 5));
+                        for (int c = 0; c < 2; ++c) rdA(ea[c], aX(P, (uint32_t)((2 + c) << 5)));
                     }
                     if (q == 0 || q == 2)
                         asm volatile("s_waitcnt lgkmcnt(0)"
@@ -829,25 +875,26 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                                        "+v"(eb[0][0][0]), "+v"(eb[0][0][1]), "+v"(eb[0][1][0]), "+v"(eb[0][1][1]));
                 }
             }
-            // stage kt+1 landed for this wave; after the barrier for all waves,
-            // and every wave is done reading slot P
-            wait_vmcnt<0>();
+            // stage kt+1 landed for this wave (NS - 2 later stages may still be
+            // in flight); after the barrier for all waves, and every wave is
+            // done reading slot P
+            wait_vmcnt<(NS - 2) * NLS>();
             barrier();
             if (kt + 1 < nk) {
                 if constexpr (FMT == 1) {
-                    rdA(fa[0], aB[Q]);
-                    fb[0][0] = wld<0 * RB>(bB[Q]);
-                    fb[0][1] = wld<1 * RB>(bB[Q]);
-                    fb[0][2] = wld<2 * RB>(bB[Q]);
-                    fb[0][3] = wld<3 * RB>(bB[Q]);
+                    rdA(fa[0], aX(Q, 0));
+                    fb[0][0] = wld<0 * RB>(bX(Q, 0));
+                    fb[0][1] = wld<1 * RB>(bX(Q, 0));
+                    fb[0][2] = wld<2 * RB>(bX(Q, 0));
+                    fb[0][3] = wld<3 * RB>(bX(Q, 0));
                     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fb[0][0]),
                                  "+v"(fb[0][1]), "+v"(fb[0][2]), "+v"(fb[0][3]));
                 } else {
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
-                        rdA(ea[c], aB[Q] ^ (uint32_t)(c << 5));
-                        eb[0][c][0] = wld<0>(bB[Q] ^ (uint32_t)(c << 5));
-                        eb[0][c][1] = wld<RB>(bB[Q] ^ (uint32_t)(c << 5));
+                        rdA(ea[c], aX(Q, (uint32_t)(c << 5)));
+                        eb[0][c][0] = wld<0>(bX(Q, (uint32_t)(c << 5)));
+                        eb[0][c][1] = wld<RB>(bX(Q, (uint32_t)(c << 5)));
                     }
                     asm volatile("s_waitcnt lgkmcnt(0)"
                                  : "+v"(ea[0][0]), "+v"(ea[0][1]), "+v"(ea[1][0]), "+v"(ea[1][1]),
@@ -855,18 +902,34 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                 }
             }
         };
-        // whole pairs of slots, then the last stage; no early exit (see the
-        // 128 x 256 kernel)
-        for (; kt0 + 2 <= nk; kt0 += 2) {
-            stage(IC<0>{});
-            stage(IC<1>{});
+        // whole rounds of the slots, then the last stages; no early exit (see
+        // the 128 x 256 kernel)
+        if constexpr (NS == 2) {
+            for (; kt0 + 2 <= nk; kt0 += 2) {
+                stage(IC<0>{});
+                stage(IC<1>{});
+            }
+            if (kt0 < nk) stage(IC<0>{});
+        } else {
+            for (; kt0 + 3 <= nk; kt0 += 3) {
+                stage(IC<0>{});
+                stage(IC<1>{});
+                stage(IC<2>{});
+            }
+            if (kt0 < nk) {
+                stage(IC<0>{});
+                if (kt0 + 1 < nk) stage(IC<1>{});
+            }
+            // the loads of a stage past the end (zeros) may still be landing in
+            // the ring, which the epilogue and the next tile reuse
+            wait_vmcnt<0>();
+            barrier();
         }
-        if (kt0 < nk) stage(IC<0>{});
         if constexpr (WSC == kWConst) {
             // one fp32 factor per tile: the product of the two tensors' scales
             const float f = p.sfa[0] * p.sfb[g];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < TMI; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -879,16 +942,19 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             for (int bj = 0; bj < 4; ++bj)
                 fb[bj] = p.sfb[(int64_t)g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)];
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
+            for (int bi = 0; bi < TMI; ++bi)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float fa = p.sfa[row0 + min(m0 + e_row(wm, bi, r), rows - 1)];
+                    const float fa = p.sfa[row0 + min(m0 + wrow0 + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3), rows - 1)];
 #pragma unroll
                     for (int bj = 0; bj < 4; ++bj) acc[bi][bj][r] *= fa * fb[bj];
                 }
         }
-        store_tile_lds<EPI, 4>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wm, wn, p.swiglu_limit,
-                               p.save, p.ldsave, p.aux, p.ldaux);
+        store_tile_lds_w<EPI, 4, TMI, 4, TBM>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wrow0, wn,
+                                              p.swiglu_limit, p.aux, p.ldaux, p.save, p.ldsave);
+        };  // run_tile
+        if (rows - m0 <= 128) run_tile(IC<1>{});
+        else run_tile(IC<2>{});
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
         par ^= 1;
     }
