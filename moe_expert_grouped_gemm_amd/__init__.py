@@ -27,7 +27,7 @@ __all__ = [
     "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts", "expert_addresses",
     "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning", "PT_CONFIG_RULES", "PT_CONFIG_TUNE",
-    "PT_OP_DGRAD_SWIGLU",
+    "PT_OP_DGRAD_SWIGLU", "PT_MAX_GROUPS",
     "pt_grouped_gemm_workspace_size", "pt_read_error_flags", "pt_status_string", "pt_version",
 ]
 
@@ -35,6 +35,7 @@ PT_BF16, PT_MXFP8_E4M3, PT_MXFP4_E2M1, PT_FP8_E4M3, PT_FP8_E4M3_ROWWISE = 0, 1, 
 PT_EPI_NONE, PT_EPI_SWIGLU, PT_EPI_SWIGLU_MXFP4 = 0, 1, 2
 PT_OP_FWD, PT_OP_DGRAD, PT_OP_WGRAD, PT_OP_DGRAD_SWIGLU = 0, 1, 2, 3
 PT_CONFIG_RULES, PT_CONFIG_TUNE = -1, -2
+PT_MAX_GROUPS = 1024
 
 EXPORTS = (
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",

@@ -80,6 +80,8 @@ def test_new_enums_match_header():
     for name in ("PT_CONFIG_RULES", "PT_CONFIG_TUNE"):
         m = re.search(r"#define\s+%s\s+\((-?\d+)\)" % name, text)
         assert m and int(m.group(1)) == getattr(pt, name), name
+    m = re.search(r"#define\s+PT_MAX_GROUPS\s+(\d+)", text)
+    assert m and int(m.group(1)) == pt.PT_MAX_GROUPS
 
 
 def test_workspace_sizes_host_only():

@@ -107,10 +107,14 @@ def test_save_mlp_shape_sampled(orc, dev):
                                         (ptm.PT_FP8_E4M3, "fp8"), (ptm.PT_FP8_E4M3_ROWWISE, "fp8rows")],
                          ids=["mxfp8", "mxfp4", "fp8", "fp8_rowwise"])
 @pytest.mark.parametrize("sched", ["static", "swz"])
-def test_save_low_precision_equals_single_epilogues(dev, dtype, name, sched):
+@pytest.mark.parametrize("K", [512, 320])
+def test_save_low_precision_equals_single_epilogues(dev, dtype, name, sched, K):
+    # K = 320 leaves a partial 256-deep MXFP4 step, which the save epilogue
+    # serves only through the swizzled-scale kernel; every kernel
+    # configuration is forced in turn (the save falls back to the
+    # configurations it has)
     lens = np.array([0, 1, 130, 0, 257, 64, 33], np.int64)
-    M, G, K, N = int(lens.sum()), len(lens), 512, 256
-    print(f"swiglu save dtype={name} sched={sched}", flush=True)
+    M, G, N = int(lens.sum()), len(lens), 256
     if dtype in (ptm.PT_MXFP8_E4M3, ptm.PT_MXFP4_E2M1):
         aq, as_ = synth.random_mx_codes(M, K, name, seed=162, device=dev, scale_lo=122, scale_hi=125)
         bq, bs = synth.random_mx_codes(G * N, K, name, seed=163, device=dev, scale_lo=116, scale_hi=119)
@@ -124,16 +128,28 @@ def test_save_low_precision_equals_single_epilogues(dev, dtype, name, sched):
         bs = torch.rand((rows_b,), generator=g, device=dev).mul_(1e-2).add_(1e-3)
     ws = make_ws(dev, sched, G, M, N, K, dtype if dtype in (ptm.PT_MXFP8_E4M3, ptm.PT_MXFP4_E2M1) else ptm.PT_BF16)
     lens_d = dev_i64(lens, dev)
-    h = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
-    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    ptm.pt_grouped_gemm_fwd_swiglu_save(aq, as_, bq, bs, h, c, lens_d, None, G, M, N, K, dtype, 1, workspace=ws,
-                                        swiglu_limit=4.0)
-    c_ref = torch.empty_like(c)
-    h_ref = torch.empty_like(h)
-    ptm.pt_grouped_gemm_fwd(aq, as_, bq, bs, c_ref, None, lens_d, None, G, M, N, K, dtype, 1, ptm.PT_EPI_NONE,
-                            workspace=ws)
-    ptm.pt_grouped_gemm_fwd(aq, as_, bq, bs, h_ref, None, lens_d, None, G, M, N, K, dtype, 1, ptm.PT_EPI_SWIGLU,
-                            workspace=ws, swiglu_limit=4.0)
-    torch.cuda.synchronize()
-    assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16))
-    assert torch.equal(h.view(torch.int16), h_ref.view(torch.int16))
+    try:
+        for cfg in (ptm.PT_CONFIG_RULES, 0, 1, 2, 3):
+            ptm.pt_set_gemm_config(cfg)
+            print(f"swiglu save dtype={name} sched={sched} K={K} cfg={cfg}", flush=True)
+            h = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
+            c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            if dtype == ptm.PT_MXFP4_E2M1 and K % 256 and ws is None:
+                with pytest.raises(ptm.PtggError) as e:
+                    ptm.pt_grouped_gemm_fwd_swiglu_save(aq, as_, bq, bs, h, c, lens_d, None, G, M, N, K, dtype, 1,
+                                                        workspace=ws, swiglu_limit=4.0)
+                assert e.value.status == 2          # PT_ERR_UNSUPPORTED
+                continue
+            ptm.pt_grouped_gemm_fwd_swiglu_save(aq, as_, bq, bs, h, c, lens_d, None, G, M, N, K, dtype, 1,
+                                                workspace=ws, swiglu_limit=4.0)
+            c_ref = torch.empty_like(c)
+            h_ref = torch.empty_like(h)
+            ptm.pt_grouped_gemm_fwd(aq, as_, bq, bs, c_ref, None, lens_d, None, G, M, N, K, dtype, 1,
+                                    ptm.PT_EPI_NONE, workspace=ws)
+            ptm.pt_grouped_gemm_fwd(aq, as_, bq, bs, h_ref, None, lens_d, None, G, M, N, K, dtype, 1,
+                                    ptm.PT_EPI_SWIGLU, workspace=ws, swiglu_limit=4.0)
+            torch.cuda.synchronize()
+            assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16))
+            assert torch.equal(h.view(torch.int16), h_ref.view(torch.int16))
+    finally:
+        ptm.pt_set_gemm_config(ptm.PT_CONFIG_RULES)
