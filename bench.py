@@ -562,7 +562,7 @@ def bench_cfg3_wgrad(dev, stream, iters):
     """The MXFP8 workload's weight gradient: A [65536, 2880] and dY
     [65536, 5760] quantised along tokens in blocks of 32 inside each expert,
     then the weight gradient accumulated into fp32 main_grad [32, 2880, 5760]
-    (exact dequantisation into the workspace, then the BF16 kernel)."""
+    (both transposed to channel rows in the workspace, then the MX kernel)."""
     lens = synth.lens_zipf_distinct(16384, 32, 4, 1.1, seed=3)
     G, M, K, N = 32, int(lens.sum()), 2880, 5760
     lens_d = torch.as_tensor(lens, device=dev)

@@ -304,11 +304,15 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const uint8_t *dy_scale, const 
  *  PT_MXFP8_E4M3 / PT_MXFP4_E2M1: a and dy are codes blocked along tokens
  *  within each expert (pt_mx_quantize_tokens): E4M3 [M, K] / [M, N], or
  *  E2M1 [M, K/2] / [M, N/2], with scales [M/32 + G, K] / [M/32 + G, N];
- *  D_g sums the products of their exact values (each code times its
- *  block's scale; values below bf16's smallest subnormal round to nearest
- *  even).  The workspace is required and holds bf16 copies of both
- *  operands: pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ..., dtype) bytes,
- *  else PT_ERR_WORKSPACE.
+ *  D_g sums the products of their values (each code times its block's
+ *  scale) in fp32 on the scaled matrix instructions, the block scales of
+ *  both operands applied per 32 tokens.  The workspace is required:
+ *  pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ..., dtype) bytes, else
+ *  PT_ERR_WORKSPACE.  It receives both operands transposed to channel
+ *  rows (each expert's tokens padded with zero codes to whole blocks of
+ *  32), their scales, the experts' starts and the split reduction's
+ *  slots; the split's chunk length is L rounded up to a multiple of 256
+ *  tokens.
  *  PT_FP8_E4M3: a [M, K] and dy [M, N] E4M3 codes with one fp32 factor
  *  each (a_scale, dy_scale: pt_fp8_quantize, batch 1);
  *      main_grad[g] = (accumulate ? main_grad[g] : 0) + fp32(d_a * d_dy) * S_g
@@ -474,7 +478,8 @@ int pt_mx_quantize_experts(const void *const *experts, void *q, uint8_t *scales,
  * (4-byte alignment is enough for the error word and tile queues alone).
  *  - the weight gradient's full size adds the split reduction's partial
  *    slots: floor(M / L) fp32 [K, N] matrices (L as at
- *    pt_grouped_gemm_wgrad), after the MX / FP8 operand copies;
+ *    pt_grouped_gemm_wgrad), after the MX transposed operands or the FP8
+ *    operand copies;
  *  - word 0 receives the sticky device error bits (pt_read_error_flags);
  *    a workspace of at least 4 bytes is enough for that alone;
  *  - a workspace of the full size also holds the tile queues: every call

@@ -618,7 +618,28 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const uint8_t *dy_scale, const 
     });
 }
 
-// The BF16 weight gradient (also the second half of the MX and FP8 ones);
+// The MX weight gradient's workspace: the error word and queues, the
+// experts' plan (block and stage starts), both gradients' transposed codes
+// and their stage-major scale words.
+struct MxWgradWs {
+    int64_t pitch, stages, plan, qa, qd, sa, sd, total;
+};
+MxWgradWs mx_wgrad_ws(int64_t G, int64_t M, int64_t N, int64_t K, int fmt)
+{
+    MxWgradWs w;
+    w.pitch = mx_wgrad_pitch(M, (int)G, fmt);
+    w.stages = mx_wgrad_stages(M, (int)G, fmt);
+    const int64_t wpr = fmt == 0 ? 1 : 2;
+    w.plan = kQueueWsBytes;
+    w.qa = w.plan + round256(8 * G);
+    w.qd = w.qa + round256(K * w.pitch);
+    w.sa = w.qd + round256(N * w.pitch);
+    w.sd = w.sa + round256(w.stages * K * wpr * 4);
+    w.total = w.sd + round256(w.stages * N * wpr * 4);
+    return w;
+}
+
+// The BF16 weight gradient (also the second half of the FP8 one);
 // its split reduction's partial slots start split_off bytes into the
 // workspace.
 static int bf16_wgrad(const void *a, const void *dy, float *main_grad, const int64_t *group_lens,
@@ -686,26 +707,85 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
     if (!fits31(M * K * 2) || !fits31(M * N * 2)) return PT_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) {
-        // codes blocked along tokens (pt_mx_quantize_tokens): their exact
-        // values are written as bf16 into the workspace, then the BF16 weight
-        // gradient runs on them (exact products, fp32 sums, as MX does)
+        // codes blocked along tokens (pt_mx_quantize_tokens): both are
+        // transposed into the workspace (channel rows, each expert's tokens
+        // padded to whole blocks; stage-major scales), and the 256 x 256 MX
+        // kernel reduces over each expert's tokens with the block scales
+        // applied in the matrix cores
         const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
         if (M > 0 && (!a_scale || !dy_scale)) return PT_ERR_INVALID_ARG;
         if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad) || !aligned16(a_scale) || !aligned16(dy_scale))
             return PT_ERR_MISALIGNED;
+        if (M == 0 && accumulate) return PT_OK;
         if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
-        const size_t need = (size_t)(kQueueWsBytes + round256(M * K * 2) + round256(M * N * 2));
-        if (!workspace || workspace_bytes < need) return PT_ERR_WORKSPACE;
-        uint16_t *wa = (uint16_t *)((uint8_t *)workspace + kQueueWsBytes);
-        uint16_t *wd = (uint16_t *)((uint8_t *)wa + round256(M * K * 2));
-        hipError_t e =
-            launch_mx_dequant_tokens((const uint8_t *)a, a_scale, group_lens, group_offs, (int)G, M, K, fmt, wa, s);
+        const MxWgradWs w = mx_wgrad_ws(G, M, N, K, fmt);
+        if (!fits31(K * w.pitch) || !fits31(N * w.pitch) || !fits31(w.stages * (K + N) * 8))
+            return PT_ERR_UNSUPPORTED;
+        if (!workspace || !aligned16(workspace) || workspace_bytes < (size_t)w.total) return PT_ERR_WORKSPACE;
+        uint8_t *base = (uint8_t *)workspace;
+        int *plan = (int *)(base + w.plan);
+        uint8_t *qa = base + w.qa, *qd = base + w.qd;
+        uint32_t *sa = (uint32_t *)(base + w.sa), *sd = (uint32_t *)(base + w.sd);
+        hipError_t e = launch_mx_tokens_transpose((const uint8_t *)a, a_scale, group_lens, group_offs, (int)G, M, K,
+                                                  fmt, qa, w.pitch, sa, plan, s);
         if (e == hipSuccess)
-            e = launch_mx_dequant_tokens((const uint8_t *)dy, dy_scale, group_lens, group_offs, (int)G, M, N, fmt, wd,
-                                         s);
+            e = launch_mx_tokens_transpose((const uint8_t *)dy, dy_scale, group_lens, group_offs, (int)G, M, N, fmt,
+                                           qd, w.pitch, sd, plan, s);
         if (e != hipSuccess) return PT_ERR_HIP;
-        return bf16_wgrad(wa, wd, main_grad, group_lens, group_offs, G, M, N, K, trans_out, accumulate, workspace,
-                          workspace_bytes, need, s);
+        // trans_out = 0: rows are A's channels (K), columns dY's (N); 1: swapped
+        MxParams p = {};
+        p.a = trans_out ? qd : qa;
+        p.sa = trans_out ? sd : sa;
+        p.b = trans_out ? qa : qd;
+        p.sb = trans_out ? sa : sd;
+        p.wrows = (int)(trans_out ? N : K);
+        p.wcols = (int)(trans_out ? K : N);
+        p.pitch = w.pitch;
+        p.plan = plan;
+        p.out = main_grad;
+        p.ldo = p.wcols;
+        p.o_gstride = N * K;
+        p.tilesM = (p.wrows + mx_wide_tile() - 1) / mx_wide_tile();
+        p.tilesN = (p.wcols + mx_wide_tile() - 1) / mx_wide_tile();
+        p.accumulate = accumulate;
+        p.lens = group_lens;
+        p.offs = group_offs;
+        p.err = error_word(workspace, workspace_bytes);
+        p.G = (int)G;
+        p.M = M;
+        p.K = 32;
+        p.N = p.wcols;
+        p.swiglu_limit = __builtin_huge_valf();
+        uint32_t *queues = queue_words(workspace, workspace_bytes);
+        // the split reduction, when the workspace holds its partial slots: the
+        // chunk length of the BF16 rule rounded up to whole 256-token stages
+        const int64_t split_len = (wgrad_split_len(M, p.wrows, p.wcols) + 255) / 256 * 256;
+        const int64_t nslots = M / split_len;
+        Bf16Params rp = {};
+        if (queues && nslots > 0 && workspace_bytes >= (size_t)(w.total + wgrad_split_bytes(M, K, N))) {
+            p.split_len = (int)split_len;
+            p.nslots = (int)nslots;
+            p.partials = (float *)(base + w.total);
+            rp.lens = group_lens;
+            rp.offs = group_offs;
+            rp.G = (int)G;
+            rp.M = M;
+            rp.split_len = p.split_len;
+            rp.nslots = p.nslots;
+            rp.partials = p.partials;
+            rp.out = main_grad;
+            rp.o_gstride = N * K;
+            rp.Mout = p.wrows;
+            rp.Nout = p.wcols;
+            rp.accumulate = accumulate;
+        }
+        const TuneKey key = tune_key(PT_OP_WGRAD, dtype, kEpiWgrad, trans_out, G, M, N, K);
+        return configured(key, cfg_mask(queues != nullptr, false), false, s, [&](int cfg) {
+            p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+            hipError_t e2 = queued(p.sched, s, [&] { return launch_mx_wgrad(p, fmt, s); });
+            if (e2 == hipSuccess && p.split_len > 0) e2 = launch_wgrad_split_reduce(rp, s);
+            return e2;
+        });
     }
     if (dtype == PT_FP8_E4M3) {
         // one factor per tensor: the codes' values (exact in bf16) go to the
@@ -864,14 +944,14 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, i
     // the weight gradients: the split reduction's partial slots last; before
     // them bf16 copies of both operands (MX), and the fp32 sums (FP8 with
     // tensor factors)
+    if (op == PT_OP_WGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && M >= 0 && N > 0 && K > 0 &&
+        G > 0)
+        return (size_t)(mx_wgrad_ws(G, M, N, K, dtype == PT_MXFP8_E4M3 ? 0 : 1).total + wgrad_split_bytes(M, K, N));
     if (op == PT_OP_WGRAD && M > 0 && N > 0 && K > 0 && G > 0) {
         int64_t bytes = kQueueWsBytes;
-        if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3)
-            bytes += round256(M * K * 2) + round256(M * N * 2);
-        if (dtype == PT_FP8_E4M3) bytes += round256(G * K * N * 4);
+        if (dtype == PT_FP8_E4M3) bytes += round256(M * K * 2) + round256(M * N * 2) + round256(G * K * N * 4);
         return (size_t)(bytes + wgrad_split_bytes(M, K, N));
     }
-    if (op == PT_OP_WGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && M == 0) return kQueueWsBytes;
     // the MX data gradient: K outputs per row, a reduction over N
     if ((op == PT_OP_DGRAD || op == PT_OP_DGRAD_SWIGLU) && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) &&
         G > 0 && M >= 0 && N > 0 &&
@@ -901,7 +981,9 @@ int pt_gemm_config_of(int op, int dtype, int epilogue, int trans, int64_t G, int
     case PT_OP_DGRAD:      // the MX / FP8 data gradient runs as a GEMM with K outputs over N
         if (dtype == PT_BF16) return tune_lookup(tune_key(op, dtype, kEpiNone, trans, G, M, N, K));
         return tune_lookup(tune_key(op, dtype, kEpiNone, 0, G, M, K, N));
-    case PT_OP_WGRAD:      // every dtype's weight gradient runs the BF16 kernel
+    case PT_OP_WGRAD:      // the MX weight gradient has its own class; the others run the BF16 kernel
+        if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1)
+            return tune_lookup(tune_key(op, dtype, kEpiWgrad, trans, G, M, N, K));
         return tune_lookup(tune_key(op, PT_BF16, kEpiNone, trans, G, M, N, K));
     case PT_OP_DGRAD_SWIGLU:
         if (dtype == PT_BF16) return tune_lookup(tune_key(op, PT_BF16, kEpiDSwiglu, trans, G, M, N, K));

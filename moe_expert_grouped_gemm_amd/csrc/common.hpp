@@ -239,6 +239,42 @@ __device__ __forceinline__ int build_group_table(GroupTable &t, const int64_t *l
     return t.tile0[G];
 }
 
+// Split weight gradient (the BF16 and MX kernels).  The weight gradient
+// reduces over an expert's tokens.  With a chunk length
+// L > 0, an expert is cut into chunks of L consecutive tokens (the last one
+// shorter), and every chunk covers the whole output: tiles (expert, chunk,
+// K tile, N tile).  Chunk 0 reads-modifies-writes main_grad as an uncut
+// expert does; chunk c >= 1 writes its fp32 partial sum to workspace slot
+// slot0[g] + c - 1, and launch_wgrad_split_reduce then adds the partials to
+// main_grad in chunk order.  The order of every sum is fixed, so the result
+// is deterministic.  Experts with no tokens: no tiles when accumulating, one
+// zero-writing chunk when not.
+struct TilesWgradSplit {
+    int ntiles, accumulate, L;
+    __device__ int chunks(int rows) const { return rows > 0 ? (L > 0 ? (rows + L - 1) / L : 1) : (accumulate ? 0 : 1); }
+    __device__ int operator()(int rows) const { return chunks(rows) * ntiles; }
+};
+
+// slot0[g] = sum over earlier experts of (chunks - 1): the first partial
+// slot of expert g (needs the table's clamped rows).  NT threads.
+template <int NT>
+__device__ __forceinline__ void wgrad_slot_table(const GroupTable &tab, const TilesWgradSplit &tw, int *slot0,
+                                                 int *s_scan)
+{
+    const int per = (tab.G + NT - 1) / NT, g0 = (int)threadIdx.x * per;
+    int v = 0;
+    for (int i = 0; i < per; ++i)
+        if (g0 + i < tab.G) v += max(tw.chunks(tab.rows[g0 + i]) - 1, 0);
+    int tot;
+    int pre = block_exclusive_scan<NT>(v, s_scan, &tot);
+    for (int i = 0; i < per; ++i)
+        if (g0 + i < tab.G) {
+            slot0[g0 + i] = pre;
+            pre += max(tw.chunks(tab.rows[g0 + i]) - 1, 0);
+        }
+    __syncthreads();
+}
+
 // Expert owning linear tile id `tile` (the last g with tile0[g] <= tile).
 __device__ __forceinline__ int find_group(const GroupTable &t, int tile)
 {

@@ -434,42 +434,6 @@ hipError_t launch_depth(const Bf16Params &p, hipStream_t s)
     }
 }
 
-// ------------------------------------------------------------------ split weight gradient
-// The weight gradient reduces over an expert's tokens.  With a chunk length
-// L > 0, an expert is cut into chunks of L consecutive tokens (the last one
-// shorter), and every chunk covers the whole output: tiles (expert, chunk,
-// K tile, N tile).  Chunk 0 reads-modifies-writes main_grad as an uncut
-// expert does; chunk c >= 1 writes its fp32 partial sum to workspace slot
-// slot0[g] + c - 1, and launch_wgrad_split_reduce then adds the partials to
-// main_grad in chunk order.  The order of every sum is fixed, so the result
-// is deterministic.  Experts with no tokens: no tiles when accumulating, one
-// zero-writing chunk when not.
-struct TilesWgradSplit {
-    int ntiles, accumulate, L;
-    __device__ int chunks(int rows) const { return rows > 0 ? (L > 0 ? (rows + L - 1) / L : 1) : (accumulate ? 0 : 1); }
-    __device__ int operator()(int rows) const { return chunks(rows) * ntiles; }
-};
-
-// slot0[g] = sum over earlier experts of (chunks - 1): the first partial
-// slot of expert g (needs the table's clamped rows).  NT threads.
-template <int NT>
-__device__ __forceinline__ void wgrad_slot_table(const GroupTable &tab, const TilesWgradSplit &tw, int *slot0,
-                                                 int *s_scan)
-{
-    const int per = (tab.G + NT - 1) / NT, g0 = (int)threadIdx.x * per;
-    int v = 0;
-    for (int i = 0; i < per; ++i)
-        if (g0 + i < tab.G) v += max(tw.chunks(tab.rows[g0 + i]) - 1, 0);
-    int tot;
-    int pre = block_exclusive_scan<NT>(v, s_scan, &tot);
-    for (int i = 0; i < per; ++i)
-        if (g0 + i < tab.G) {
-            slot0[g0 + i] = pre;
-            pre += max(tw.chunks(tab.rows[g0 + i]) - 1, 0);
-        }
-    __syncthreads();
-}
-
 // ====================================================================== wide
 // The main BF16 kernel: one workgroup of 8 waves per CU (two waves per SIMD)
 // computes 256 x 256 tiles; wave (wm, wn), wm = 0..3, owns 64 x 128 outputs

@@ -585,6 +585,8 @@ static_assert(MX_RING >= 2 * WSTAGE, "ring sizes");
 template <int EPI>
 constexpr int wide_lds_bytes()
 {
+    // the weight gradient: 256-row tiles only, stored from the registers
+    if constexpr (EPI == kEpiWgrad) return 2 * WSTAGE;
     return MX_RING > epi_lds_bytes<EPI, 4>() ? MX_RING : epi_lds_bytes<EPI, 4>();
 }
 
@@ -602,7 +604,17 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
     tab.rows = tb + p.G;
     tab.tile0 = tb + 2 * p.G;
     int *s_scan = tab.tile0 + p.G + 1;
-    int total = build_group_table<TilesFwd, WTHREADS>(tab, p.lens, p.offs, p.G, p.M, TilesFwd{WBM, p.tilesN}, p.err,
+    // kEpiWgrad: the weight gradient, whose rows are the first gradient's
+    // channels and whose reduction runs over each expert's (padded) tokens
+    constexpr bool WG = EPI == kEpiWgrad;
+    int total;
+    const TilesWgradSplit tw{p.tilesM * p.tilesN, p.accumulate, p.split_len};
+    int *slot0 = (int *)(smem + GEMM_LDS_BYTES + table_bytes(p.G));   // weight gradient, split
+    if constexpr (WG) {
+        total = build_group_table<TilesWgradSplit, WTHREADS>(tab, p.lens, p.offs, p.G, p.M, tw, p.err, s_scan);
+        if (p.split_len > 0) wgrad_slot_table<WTHREADS>(tab, tw, slot0, s_scan);
+    } else
+        total = build_group_table<TilesFwd, WTHREADS>(tab, p.lens, p.offs, p.G, p.M, TilesFwd{WBM, p.tilesN}, p.err,
                                                       s_scan);
     total = __builtin_amdgcn_readfirstlane(total);
     // the scan scratch is free once the table is built: it passes tile ids
@@ -619,10 +631,12 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
     const int r32 = lane & 31, h = lane >> 5;
     const uint32_t sh = 8u * h;
 
-    const int Kb = FMT == 0 ? p.K : p.K / 2;
+    // reduction bytes per row and their stages (the weight gradient sets
+    // them per expert)
+    int Kb = FMT == 0 ? p.K : p.K / 2;
     const int KS = p.K / 32;
-    const int nk = (Kb + WROW - 1) / WROW, nfull = Kb / WROW;
-    const int nb_last = (Kb - nfull * WROW) / 32;           // E4M3 blocks of the partial stage
+    int nk = (Kb + WROW - 1) / WROW, nfull = Kb / WROW;
+    int nb_last = (Kb - nfull * WROW) / 32;                 // E4M3 blocks of the partial stage
 
     // per-lane fragment bases of a 256-row tile in slot 0 / 1: chunk 2j + h
     // of the lane's first A row / B row is at base ^ (j << 5)
@@ -640,10 +654,35 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
     for (int tile = tq.first(s_id); tile < total;) {
         const int g = __builtin_amdgcn_readfirstlane(find_group(tab, tile));
         const int local = tile - __builtin_amdgcn_readfirstlane(tab.tile0[g]);
-        const int row0 = __builtin_amdgcn_readfirstlane(tab.row0[g]);
-        const int rows = __builtin_amdgcn_readfirstlane(tab.rows[g]);
-        const int tm = (rows + WBM - 1) / WBM;
-        const int nt = local / tm, mt = local % tm;
+        int row0 = __builtin_amdgcn_readfirstlane(tab.row0[g]);
+        int rows = __builtin_amdgcn_readfirstlane(tab.rows[g]);
+        int tm = (rows + WBM - 1) / WBM;
+        int nt = local / tm, mt = local % tm;
+        // weight gradient: the tile's token chunk of the expert (all of its
+        // tokens, padded to whole blocks, without a split) starts at byte pb
+        // of every channel row, its scale words at global stage s0
+        uint32_t pb = 0;
+        int s0 = 0, chunk = 0;
+        if constexpr (WG) {
+            constexpr int TPB = FMT == 0 ? 1 : 2;       // tokens per code byte
+            const int ntl = p.tilesM * p.tilesN;
+            chunk = local / ntl;
+            const int rest = local - chunk * ntl;
+            mt = rest / p.tilesN;
+            nt = rest % p.tilesN;
+            const int padded = 32 * ((rows + 31) / 32);
+            const int c0 = chunk * p.split_len;
+            const int clen = p.split_len > 0 ? min(p.split_len, padded - c0) : padded;
+            pb = (uint32_t)(32 * __builtin_amdgcn_readfirstlane(p.plan[2 * g]) + c0) / TPB;
+            s0 = __builtin_amdgcn_readfirstlane(p.plan[2 * g + 1]) + c0 / (WROW * TPB);
+            Kb = clen / TPB;
+            nk = (Kb + WROW - 1) / WROW;
+            nfull = Kb / WROW;
+            nb_last = (Kb - nfull * WROW) / 32;
+            row0 = 0;
+            rows = p.wrows;
+            tm = p.tilesM;
+        }
         const int m0 = mt * WBM;
 
         // One tile of TMI 32-row blocks per wave: a row block holding at most
@@ -684,19 +723,22 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         // ---- operand loads: slot i * 512 + t holds chunk c = (t & 7) ^ ((t >> 4) & 7)
         // of tile row i * 64 + t / 8
         WOps o;
-        o.b_once = tm == 1;      // an expert within one row block: no other tile reads its weights
-        o.a = p.a + (int64_t)row0 * Kb;
-        o.abytes = (uint32_t)rows * Kb;
-        o.b = p.b + (int64_t)g * p.N * Kb;
-        o.bbytes = (uint32_t)p.N * Kb;
+        // row pitch of the operands: the reduction length, or the channel
+        // rows' pitch of the weight gradient
+        const uint32_t ap = WG ? (uint32_t)p.pitch : (uint32_t)Kb;
+        o.b_once = !WG && tm == 1;   // an expert within one row block: no other tile reads its weights
+        o.a = WG ? p.a + pb : p.a + (int64_t)row0 * Kb;
+        o.abytes = WG ? (uint32_t)rows * ap - pb : (uint32_t)rows * Kb;
+        o.b = WG ? p.b + pb : p.b + (int64_t)g * p.N * Kb;
+        o.bbytes = WG ? (uint32_t)p.wcols * ap - pb : (uint32_t)p.N * Kb;
         o.chunk = (uint32_t)(((tid & 7) ^ ((tid >> 4) & 7)) * 16);
-        o.avoff = (uint32_t)(m0 + (tid >> 3)) * Kb + o.chunk;
+        o.avoff = (uint32_t)(m0 + (tid >> 3)) * ap + o.chunk;
 #pragma unroll
-        for (int i = 0; i < TNA; ++i) o.adelta[i] = (uint32_t)(i * 64) * Kb;
+        for (int i = 0; i < TNA; ++i) o.adelta[i] = (uint32_t)(i * 64) * ap;
         if (!epi_glu(EPI)) {
-            o.bvoff = (uint32_t)(nt * WBN + (tid >> 3)) * Kb + o.chunk;
+            o.bvoff = (uint32_t)(nt * WBN + (tid >> 3)) * ap + o.chunk;
 #pragma unroll
-            for (int i = 0; i < W_LOADS; ++i) o.bdelta[i] = (uint32_t)(i * 64) * Kb;
+            for (int i = 0; i < W_LOADS; ++i) o.bdelta[i] = (uint32_t)(i * 64) * ap;
         } else {
             // tile rows 0-63 / 64-127 / 128-191 / 192-255: gate j, up I + j,
             // gate j + 64, up I + j + 64, with j = nt * 128 + row % 64
@@ -713,10 +755,15 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             constexpr uint32_t WPR = WSC == kWE4M3Swz ? 1u : 2u;
             const uint32_t hw = WSC == kWE2M1Swz ? 4u * h : 0u;
             sr.a = (const uint8_t *)p.sa;
-            sr.astride = (uint32_t)p.M * WPR * 4u;
-            sr.abytes = sr.astride * (uint32_t)nk;
+            sr.astride = (uint32_t)(WG ? p.wrows : p.M) * WPR * 4u;
             sr.b = (const uint8_t *)p.sb;
-            sr.bstride = (uint32_t)p.G * (uint32_t)p.N * WPR * 4u;
+            sr.bstride = WG ? (uint32_t)p.wcols * WPR * 4u : (uint32_t)p.G * (uint32_t)p.N * WPR * 4u;
+            if constexpr (WG) {
+                // the expert's stages start at global stage s0
+                sr.a += (int64_t)s0 * sr.astride;
+                sr.b += (int64_t)s0 * sr.bstride;
+            }
+            sr.abytes = sr.astride * (uint32_t)nk;
             sr.bbytes = sr.bstride * (uint32_t)nk;
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
@@ -724,8 +771,10 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
 #pragma unroll
             for (int bj = 0; bj < 4; ++bj)
                 sr.row[2 + bj] =
-                    (uint32_t)(g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)) * WPR * 4u +
-                    hw;
+                    WG ? (uint32_t)min(nt * WBN + wn * 128 + bj * 32 + r32, p.wcols - 1) * WPR * 4u + hw
+                       : (uint32_t)(g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)) *
+                                 WPR * 4u +
+                             hw;
         } else {
             sr.a = p.as;
             sr.abytes = (uint32_t)((p.M * KS + 3) & ~3ll);
@@ -740,13 +789,30 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                     (uint32_t)((g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)) * KS);
         }
 
+        // accumulators start at zero, or for an accumulating weight gradient
+        // at the main_grad tile itself (its loads land with stage 0's)
         floatx16 acc[TMI][4];
+        if (WG && p.accumulate && chunk == 0) {
+            const float *og = (const float *)p.out + (int64_t)g * p.o_gstride;
 #pragma unroll
-        for (int i = 0; i < TMI; ++i)
+            for (int bi = 0; bi < TMI; ++bi)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int bj = 0; bj < 4; ++bj) {
+                    const int n = nt * WBN + wn * 128 + bj * 32 + r32;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = m0 + wrow0 + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                        acc[bi][bj][r] = (n < p.wcols && i < rows) ? og[(int64_t)i * p.ldo + n] : 0.0f;
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TMI; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        }
 
         auto mfma = [&](int bi, int bj, intx8 a, intx8 b, const uint32_t (&w)[6], int s) {
             acc[bi][bj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -950,11 +1016,43 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                     for (int bj = 0; bj < 4; ++bj) acc[bi][bj][r] *= fa * fb[bj];
                 }
         }
-        store_tile_lds_w<EPI, 4, TMI, 4, TBM>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wrow0, wn,
-                                              p.swiglu_limit, p.aux, p.ldaux, p.save, p.ldsave);
+        if constexpr (WG) {
+            // fp32 tile straight from the accumulators (32 lanes write 128
+            // contiguous bytes of a row); nothing is outstanding, and saying
+            // so keeps the compiler from waiting before each store.  Chunk 0
+            // goes to main_grad, chunk c >= 1 to its partial slot (none past
+            // the workspace's slots, which only malformed lengths reach).
+            wait_vmcnt<0>();
+            float *og = (float *)p.out + (int64_t)g * p.o_gstride;
+            bool keep = true;
+            if (chunk > 0) {
+                const int slot = slot0[g] + chunk - 1;
+                keep = slot < p.nslots;
+                og = p.partials + (int64_t)slot * p.o_gstride;
+            }
+#pragma unroll
+            for (int bi = 0; bi < TMI; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) {
+                    const int n = nt * WBN + wn * 128 + bj * 32 + r32;
+                    if (n >= p.wcols || !keep) continue;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = m0 + wrow0 + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                        if (i < rows) og[(int64_t)i * p.ldo + n] = acc[bi][bj][r];
+                    }
+                }
+        } else {
+            store_tile_lds_w<EPI, 4, TMI, 4, TBM>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wrow0,
+                                                  wn, p.swiglu_limit, p.aux, p.ldaux, p.save, p.ldsave);
+        }
         };  // run_tile
-        if (rows - m0 <= 128) run_tile(IC<1>{});
-        else run_tile(IC<2>{});
+        if constexpr (WG) {
+            run_tile(IC<2>{});
+        } else {
+            if (rows - m0 <= 128) run_tile(IC<1>{});
+            else run_tile(IC<2>{});
+        }
         tile = __builtin_amdgcn_readfirstlane(s_id[par ^ 1]);
         par ^= 1;
     }
@@ -972,6 +1070,24 @@ hipError_t launch_wide(const MxParams &p, hipStream_t s)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, WTHREADS, lds);
     if (e != hipSuccess) return e;
     const int64_t tiles_max = (p.M / WBM + p.G) * (int64_t)p.tilesN;
+    const int64_t grid = persistent_grid(occ, tiles_max);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WTHREADS), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int FMT, int WSC>
+hipError_t launch_wide_wgrad(const MxParams &p, hipStream_t s)
+{
+    const int lds = wide_lds_bytes<kEpiWgrad>() + table_bytes(p.G) + 4 * p.G;
+    auto kern = gg_mx_wide_kernel<FMT, kEpiWgrad, WSC>;
+    static LdsLimit lds_limit;
+    hipError_t e = lds_limit.ensure((const void *)kern, lds);
+    if (e != hipSuccess) return e;
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, WTHREADS, lds);
+    if (e != hipSuccess) return e;
+    const int64_t chunks_max = p.G + (p.split_len > 0 ? p.M / p.split_len + 1 : 0);
+    const int64_t tiles_max = chunks_max * p.tilesM * p.tilesN;
     const int64_t grid = persistent_grid(occ, tiles_max);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WTHREADS), lds, s, p);
     return hipGetLastError();
@@ -1016,6 +1132,7 @@ hipError_t launch_epi(const MxParams &p, int epi, hipStream_t s)
 }  // namespace
 
 int mx_tile_m() { return BM; }
+int mx_wide_tile() { return WBM; }
 int mx_tile_n() { return BN; }
 
 // Stage-major copy of a row-major E8M0 scale matrix [R][KS] for the 256 x 256
@@ -1082,6 +1199,11 @@ hipError_t launch_mx_scale_swizzle(const uint8_t *scales, int64_t rows, int64_t 
     else
         hipLaunchKernelGGL(mx_scale_swizzle_kernel<1>, grid, dim3(256), 0, s, scales, sbytes, out, (int)rows, KS, NS);
     return hipGetLastError();
+}
+
+hipError_t launch_mx_wgrad(const MxParams &p, int fmt, hipStream_t s)
+{
+    return fmt == 0 ? launch_wide_wgrad<0, kWE4M3Swz>(p, s) : launch_wide_wgrad<1, kWE2M1Swz>(p, s);
 }
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s)

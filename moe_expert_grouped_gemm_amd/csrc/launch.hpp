@@ -42,7 +42,8 @@ struct Bf16Params {
 enum Bf16Kind { kFwdKContig = 0, kFwdNContig = 1, kWgrad = 2 };
 // kEpiDSwiglu: the SwiGLU backward on a data gradient dH (see store_tile_lds_w).
 // kEpiSwigluSave: the SwiGLU output, and the bf16 GEMM output itself to Bf16Params::save.
-enum Epi { kEpiNone = 0, kEpiSwiglu = 1, kEpiSwigluMxfp4 = 2, kEpiDSwiglu = 3, kEpiSwigluSave = 4 };
+// kEpiWgrad (MX kernel): the weight gradient, fp32 tiles accumulated into main_grad.
+enum Epi { kEpiNone = 0, kEpiSwiglu = 1, kEpiSwigluMxfp4 = 2, kEpiDSwiglu = 3, kEpiSwigluSave = 4, kEpiWgrad = 5 };
 // Does the epilogue pair gate and up columns of one tile?
 constexpr bool epi_glu(int epi) { return epi == kEpiSwiglu || epi == kEpiSwigluMxfp4 || epi == kEpiSwigluSave; }
 
@@ -80,9 +81,24 @@ struct MxParams {
     int ldsave;              // its row stride (elements)
     const uint16_t *aux;     // kEpiDSwiglu: FC1's saved output [gate | up] [M, 2N] bf16
     int ldaux;               // its row stride (elements)
+    // kEpiWgrad: a / b are the two gradients' codes transposed to channel
+    // rows [wrows / wcols, pitch bytes] (launch_mx_tokens_transpose), sa / sb
+    // their stage-major scale words, plan the experts' block and stage
+    // starts; out is main_grad, fp32 [G][wrows][ldo] at o_gstride elements
+    const int *plan;
+    int64_t pitch;
+    int wrows, wcols;
+    int64_t o_gstride;
+    int tilesM;
+    int accumulate;
+    int split_len;           // split reduction: chunk length in padded tokens (a multiple of 256), or 0
+    float *partials;         // nslots fp32 [wrows, wcols] partial sums in the workspace
+    int nslots;
 };
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);
+// The MX weight gradient (p as for kEpiWgrad) on the 256 x 256 kernel.
+hipError_t launch_mx_wgrad(const MxParams &p, int fmt, hipStream_t s);
 
 // Stage-major copy of a row-major E8M0 scale matrix [rows, K/32] for the
 // 256 x 256 MX kernel (layout at mx_scale_swizzle): mx_swizzle_bytes() bytes
@@ -92,6 +108,7 @@ int64_t mx_swizzle_bytes(int64_t rows, int64_t K, int fmt);
 hipError_t launch_mx_scale_swizzle(const uint8_t *scales, int64_t rows, int64_t K, int fmt, uint32_t *out,
                                    hipStream_t s);
 int mx_tile_m();
+int mx_wide_tile();      // rows and columns of the 256 x 256 MX kernel's tile
 int mx_tile_n();
 
 // Tile queues of the persistent kernels: kQueues counters, kQueueStride
@@ -134,13 +151,21 @@ hipError_t launch_fp8_wgrad_axpy(float *main_grad, const float *sum, const int64
                                  const float *fd, int G, int64_t P, int accumulate, hipStream_t s);
 // MX along tokens within each expert (blocks of 32 rows, the last
 // partial), codes E4M3 [M, C] / E2M1 [M, C/2] (fmt 0 / 1) and scales
-// [M / 32 + G, C]; and the exact bf16 values of such codes (the MX weight
-// gradient runs on them).
+// [M / 32 + G, C].
 hipError_t launch_mx_quantize_tokens(const uint16_t *x, const int64_t *lens, const int64_t *offs, int G, int64_t M,
                                      int64_t C, int fmt, uint8_t *q, uint8_t *scales, uint32_t *err, hipStream_t s);
-hipError_t launch_mx_dequant_tokens(const uint8_t *q, const uint8_t *scales, const int64_t *lens,
-                                    const int64_t *offs, int G, int64_t M, int64_t C, int fmt, uint16_t *out,
-                                    hipStream_t s);
+// The MX weight gradient's operands: token-blocked codes [M, C(/2)] and
+// scales [M/32 + G, C] -> channel rows qt [C, pitch] (each expert's tokens
+// padded to whole blocks, expert g from byte 32 (E4M3) / 16 (E2M1) *
+// bstart_g) and stage-major scale words st (global stage S_g + kt of expert
+// g: word ((S_g + kt) * C + c) * WPR + w); plan[2g] = bstart_g, plan[2g+1] =
+// S_g.  mx_wgrad_pitch / mx_wgrad_stages bound the row bytes and the stages
+// for any lengths summing to at most M.
+int64_t mx_wgrad_pitch(int64_t M, int G, int fmt);
+int64_t mx_wgrad_stages(int64_t M, int G, int fmt);
+hipError_t launch_mx_tokens_transpose(const uint8_t *q, const uint8_t *scales, const int64_t *lens,
+                                      const int64_t *offs, int G, int64_t M, int64_t C, int fmt, uint8_t *qt,
+                                      int64_t pitch, uint32_t *st, int *plan, hipStream_t s);
 // Expert weight stack: G separate bf16 matrices (a device array of their
 // addresses) -> [G, R, C], or [G, C, R] with trans; and their MX caches
 // along C ([G, R, C(/2)] + [G, R, C/32]) and/or along R of the transpose

@@ -458,49 +458,172 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t n)
     return (n & 8u) ? -v : v;
 }
 
-// MX codes blocked along tokens -> their exact values as bf16 (values below
-// bf16's smallest subnormal round to nearest even): one wave per row.
+// ------------------------------------------------------------------ MX weight-gradient operands
+// The MX weight gradient contracts over each expert's tokens, so the 256 x
+// 256 MX kernel takes the token-blocked codes transposed: channel rows
+// [C, pitch bytes] in which expert g's tokens, padded with zero codes to
+// whole blocks of 32, start at byte 32 * bstart_g (E4M3) or 16 * bstart_g
+// (E2M1), bstart_g being the blocks of earlier experts (the scale-row
+// numbering of the token quantiser).  The scales go to the kernel's
+// stage-major layout with stages numbered across experts (stage kt of expert
+// g is global stage S_g + kt, S_g = stages of earlier experts, a stage being
+// 128 code bytes of a row): word ((S_g + kt) * C + c) * WPR + w, E4M3 blocks
+// 4kt .. 4kt + 3 in byte order (WPR 1), E2M1 word w blocks 8kt + w + 0, 2,
+// 4, 6 (WPR 2); blocks past an expert's last one read zero.  plan[2g] =
+// bstart_g and plan[2g + 1] = S_g (written by workgroup 0) tell the GEMM
+// where each expert starts.  A work item is one stage of one expert for 128
+// channels: its tokens are staged in LDS and read back as blocks of 4 tokens
+// x 4 channels turned with byte permutes (E4M3) or 16 tokens x 8 channels of
+// nibbles (E2M1) into an LDS copy of the output rows, which then leave as
+// 128-byte runs.
+constexpr int kTrCh = 128;                              // channels per work item
+
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void mx_tokens_dequant_kernel(const uint8_t *__restrict__ q,
-                                                                     const uint8_t *__restrict__ scales,
-                                                                     const int64_t *lens, const int64_t *offs, int G,
-                                                                     int64_t M, int64_t C, uint16_t *__restrict__ out)
+__global__ __launch_bounds__(kThreads) void mx_tokens_transpose_kernel(
+    const uint8_t *__restrict__ q, const uint8_t *__restrict__ scales, const int64_t *lens, const int64_t *offs,
+    int G, int64_t M, int C, uint8_t *__restrict__ qt, int64_t pitch, uint32_t *__restrict__ st, int *plan)
 {
+    constexpr int TS = FMT == 0 ? 128 : 256;            // tokens per stage
+    constexpr int RB = FMT == 0 ? kTrCh : kTrCh / 2;    // input bytes of a token's 128 channels
+    constexpr int LROW = FMT == 0 ? RB + 8 : RB + 4;    // LDS row pitch (bytes): 34 / 17 words
+    constexpr int OROW = 132;                           // output rows: 33 words
     extern __shared__ __attribute__((aligned(16))) int sm_tok[];
     GroupTable tab;
-    tokens_table(tab, sm_tok, lens, offs, G, M, nullptr);
-    const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (r >= M) return;
-    const int lane = threadIdx.x & 63;
-    int lo = 0, hi = G;                            // the last expert with row0 <= r
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (tab.row0[mid] <= r) lo = mid; else hi = mid;
-    }
-    const bool in = G > 0 && r >= tab.row0[lo] && r < (int64_t)tab.row0[lo] + tab.rows[lo];
-    const int64_t b = in ? tab.tile0[lo] + (r - tab.row0[lo]) / 32 : 0;
-    for (int64_t c = lane * 8; c < C; c += 512) {
-        uintx4 o = uintx4{0u, 0u, 0u, 0u};
-        if (in) {
-            const uintx2 sw = *(const uintx2 *)(scales + b * C + c);
-            float f[8];
-            if (FMT == 0) {
-                const uintx2 cw = *(const uintx2 *)(q + r * C + c);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    f[e] = __builtin_amdgcn_cvt_f32_fp8((int)((cw[e >> 2] >> (8 * (e & 3))) & 0xFFu), 0);
-            } else {
-                const uint32_t cw = *(const uint32_t *)(q + r * (C / 2) + c / 2);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] = e2m1_to_f32((cw >> (4 * e)) & 0xFu);
+    tokens_table(tab, sm_tok, lens, offs, G, M, nullptr);      // tile0: each expert's first block
+    int *sst = tab.tile0 + G + 1 + 8;                           // each expert's first stage, [G + 1]
+    int *scr = sst + G + 1;
+    uint8_t *tile = (uint8_t *)(scr + 8);
+    uint8_t *otile = tile + TS * LROW;                          // [128 channels][OROW] output bytes
+    {
+        const int per = (G + kThreads - 1) / kThreads, g0 = threadIdx.x * per;
+        int sum = 0;
+        for (int i = 0; i < per; ++i)
+            if (g0 + i < G) sum += (tab.rows[g0 + i] + TS - 1) / TS;
+        int all;
+        int pre = block_exclusive_scan<kThreads>(sum, scr, &all);
+        for (int i = 0; i < per; ++i)
+            if (g0 + i < G) {
+                sst[g0 + i] = pre;
+                pre += (tab.rows[g0 + i] + TS - 1) / TS;
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int E = (int)((sw[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-                o[e >> 1] |= bf16_rne(__builtin_ldexpf(f[e], E - 127)) << (16 * (e & 1));
+        if (threadIdx.x == 0) sst[G] = all;
+        __syncthreads();
+    }
+    if (blockIdx.x == 0)
+        for (int g = threadIdx.x; g < G; g += kThreads) {
+            plan[2 * g] = tab.tile0[g];
+            plan[2 * g + 1] = sst[g];
+        }
+    const int nch = (C + kTrCh - 1) / kTrCh;
+    const int64_t items = (int64_t)sst[G] * nch;
+    const int tid = threadIdx.x;
+    for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
+        const int sg = (int)(w / nch), c0 = (int)(w % nch) * kTrCh;
+        int lo = 0, hi = G;                              // the last expert with sst <= sg
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sst[mid] <= sg) lo = mid; else hi = mid;
+        }
+        const int g = lo, kt = sg - sst[g];
+        const int rows = tab.rows[g], nb = (rows + 31) / 32, tok0 = kt * TS;
+        const int nvalid = min(TS, rows - tok0);        // real tokens of the stage
+        const int nbytes = (FMT == 0 ? 32 : 16) * min(TS / 32, nb - kt * (TS / 32));   // output bytes per row
+        const int64_t r0 = (int64_t)tab.row0[g] + tok0;
+        const int64_t ob = (int64_t)(FMT == 0 ? 32 : 16) * tab.tile0[g] + (int64_t)kt * 128;
+        // stage the tokens' channel bytes (E4M3 rows hold C bytes, 8-byte
+        // loads; E2M1 rows C/2, a multiple of 4)
+        const int64_t rowb = FMT == 0 ? C : C / 2;
+        const int cb0 = FMT == 0 ? c0 : c0 / 2;
+        constexpr int LW = FMT == 0 ? 8 : 4;
+        for (int e = tid; e < TS * (RB / LW); e += kThreads) {
+            const int t = e / (RB / LW), k = (e % (RB / LW)) * LW;
+            const bool in = t < nvalid && cb0 + k < rowb;
+            const uint8_t *src = q + (r0 + t) * rowb + cb0 + k;
+            if constexpr (FMT == 0) {
+                const uintx2 v = in ? *(const uintx2 *)src : uintx2{0u, 0u};
+                *(uintx2 *)(tile + t * LROW + k) = v;
+            } else {
+                *(uint32_t *)(tile + t * LROW + k) = in ? *(const uint32_t *)src : 0u;
             }
         }
-        *(uintx4 *)(out + r * C + c) = o;
+        __syncthreads();
+        if constexpr (FMT == 0) {
+            // thread: channels 4cq .. 4cq + 3, tokens 16j .. 16j + 15; 4 x 4
+            // byte blocks turned with v_perm; lanes on consecutive channel
+            // quads (row pitch 34 words: the two token chunks of a wave land
+            // on disjoint banks)
+            const int cq = tid & 31, j = tid >> 5;
+            if (16 * j < nbytes) {
+                uint32_t o[4][4];                    // [channel][token quad]
+#pragma unroll
+                for (int tq4 = 0; tq4 < 4; ++tq4) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) w[u] = *(const uint32_t *)(tile + (16 * j + 4 * tq4 + u) * LROW + 4 * cq);
+                    const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+                    const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+                    const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+                    const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+                    o[0][tq4] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+                    o[1][tq4] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+                    o[2][tq4] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+                    o[3][tq4] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+                }
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) *(uint32_t *)(otile + (4 * cq + d) * OROW + 16 * j + 4 * e) = o[d][e];
+            }
+        } else {
+            // thread: channels 8co .. 8co + 7 (one input word per token),
+            // tokens 16j .. 16j + 15 -> 8 bytes per channel (row pitch 17
+            // words: the wave's four token chunks land on disjoint banks)
+            const int co = tid & 15, j = tid >> 4;
+            if (8 * j < nbytes) {
+                uint32_t w[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) w[u] = *(const uint32_t *)(tile + (16 * j + u) * LROW + 4 * co);
+#pragma unroll
+                for (int d = 0; d < 8; ++d) {
+                    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        lo |= ((w[u] >> (4 * d)) & 0xFu) << (4 * u);
+                        hi |= ((w[8 + u] >> (4 * d)) & 0xFu) << (4 * u);
+                    }
+                    *(uint32_t *)(otile + (8 * co + d) * OROW + 8 * j) = lo;
+                    *(uint32_t *)(otile + (8 * co + d) * OROW + 8 * j + 4) = hi;
+                }
+            }
+        }
+        __syncthreads();
+        // the channel rows leave as 128-byte runs (8 lanes per row)
+        for (int e = tid; e < kTrCh * 8; e += kThreads) {
+            const int row = e >> 3, ch = e & 7;
+            if (16 * ch < nbytes && c0 + row < C) {
+                const uint8_t *src = otile + row * OROW + 16 * ch;
+                *(uintx4 *)(qt + (int64_t)(c0 + row) * pitch + ob + 16 * ch) =
+                    uintx4{*(const uint32_t *)src, *(const uint32_t *)(src + 4), *(const uint32_t *)(src + 8),
+                           *(const uint32_t *)(src + 12)};
+            }
+        }
+        // the stage's scale words, one channel per thread
+        const int c = tid;
+        if (c < kTrCh && c0 + c < C) {
+            const int64_t b0 = (int64_t)tab.tile0[g] + (int64_t)kt * (TS / 32);
+            uint32_t v[2] = {0u, 0u};
+#pragma unroll
+            for (int j = 0; j < TS / 32; ++j)
+                if (kt * (TS / 32) + j < nb) v[j >> 2] |= (uint32_t)scales[(b0 + j) * C + c0 + c] << (8 * (j & 3));
+            const int64_t wi = ((int64_t)(sst[g] + kt) * C + c0 + c);
+            if (FMT == 0) {
+                st[wi] = v[0];
+            } else {
+                *(uintx2 *)(st + 2 * wi) =
+                    uintx2{__builtin_amdgcn_perm(v[1], v[0], 0x06040200u), __builtin_amdgcn_perm(v[1], v[0], 0x07050301u)};
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -722,21 +845,37 @@ hipError_t launch_mx_quantize_tokens(const uint16_t *x, const int64_t *lens, con
     return hipGetLastError();
 }
 
-hipError_t launch_mx_dequant_tokens(const uint8_t *q, const uint8_t *scales, const int64_t *lens,
-                                    const int64_t *offs, int G, int64_t M, int64_t C, int fmt, uint16_t *out,
-                                    hipStream_t s)
+int64_t mx_wgrad_pitch(int64_t M, int G, int fmt)
 {
-    if (M == 0 || C == 0) return hipSuccess;
-    const dim3 grid((unsigned)((M + kThreads / 64 - 1) / (kThreads / 64)));
-    if (fmt == 0)
-        hipLaunchKernelGGL(mx_tokens_dequant_kernel<0>, grid, dim3(kThreads), table_bytes(G), s, q, scales, lens, offs,
-                           G, M, C, out);
-    else
-        hipLaunchKernelGGL(mx_tokens_dequant_kernel<1>, grid, dim3(kThreads), table_bytes(G), s, q, scales, lens, offs,
-                           G, M, C, out);
-    return hipGetLastError();
+    const int64_t tokens = 32 * (M / 32 + G);             // every expert padded to whole blocks
+    const int64_t bytes = fmt == 0 ? tokens : tokens / 2;
+    return (bytes + 127) / 128 * 128;
 }
 
+int64_t mx_wgrad_stages(int64_t M, int G, int fmt)
+{
+    return mx_wgrad_pitch(M, G, fmt) / 128 + G;           // a partial last stage per expert at most
+}
+
+hipError_t launch_mx_tokens_transpose(const uint8_t *q, const uint8_t *scales, const int64_t *lens,
+                                      const int64_t *offs, int G, int64_t M, int64_t C, int fmt, uint8_t *qt,
+                                      int64_t pitch, uint32_t *st, int *plan, hipStream_t s)
+{
+    if (G == 0 || C == 0) return hipSuccess;
+    const int rb = fmt == 0 ? kTrCh : kTrCh / 2, ts = fmt == 0 ? 128 : 256;
+    const size_t lds = table_bytes(G) + 4 * (G + 1) + 32 + (size_t)ts * (fmt == 0 ? rb + 8 : rb + 4) + kTrCh * 132;
+    const int64_t items = mx_wgrad_stages(M, G, fmt) * ((C + kTrCh - 1) / kTrCh);
+    int64_t grid = (int64_t)device_cus() * 4;
+    if (grid > items) grid = items;
+    if (grid < 1) grid = 1;
+    if (fmt == 0)
+        hipLaunchKernelGGL(mx_tokens_transpose_kernel<0>, dim3((unsigned)grid), dim3(kThreads), lds, s, q, scales,
+                           lens, offs, G, M, (int)C, qt, pitch, st, plan);
+    else
+        hipLaunchKernelGGL(mx_tokens_transpose_kernel<1>, dim3((unsigned)grid), dim3(kThreads), lds, s, q, scales,
+                           lens, offs, G, M, (int)C, qt, pitch, st, plan);
+    return hipGetLastError();
+}
 
 hipError_t launch_stack_experts(const void *const *ptrs, uint16_t *out, int G, int64_t R, int64_t C, int trans,
                                 uint32_t *err, hipStream_t s)

@@ -100,9 +100,18 @@ def test_workspace_sizes_host_only():
         return r256((M // L) * K * N * 4)
     assert split(M, N, K) == r256(3 * K * N * 4)            # L = 17664 here: three slots
     assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, pt.PT_BF16) == base + split(M, N, K)
-    for dt in (pt.PT_MXFP8_E4M3, pt.PT_MXFP4_E2M1):
-        assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, dt) == \
-            base + r256(M * K * 2) + r256(M * N * 2) + split(M, N, K)
+    # MX: the experts' plan (block and stage starts), both gradients' codes
+    # transposed to channel rows of `pitch` bytes (every expert padded to
+    # whole 32-token blocks), their stage-major scale words (a stage is 128
+    # code bytes of a row; each expert adds at most one partial stage), then
+    # the split reduction's slots
+    for dt, tok_bytes, wpr in ((pt.PT_MXFP8_E4M3, 1.0, 1), (pt.PT_MXFP4_E2M1, 0.5, 2)):
+        for g_, m_, n_, k_ in ((G, M, N, K), (3, 40, 64, 136), (5, 0, 64, 64)):
+            pitch = -(-int(32 * (m_ // 32 + g_) * tok_bytes) // 128) * 128
+            stages = pitch // 128 + g_
+            want = (base + r256(8 * g_) + r256(k_ * pitch) + r256(n_ * pitch) + r256(stages * k_ * wpr * 4) +
+                    r256(stages * n_ * wpr * 4) + split(m_, n_, k_))
+            assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, g_, m_, n_, k_, dt) == want, (dt, g_, m_)
     assert (pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, pt.PT_FP8_E4M3) ==
             base + r256(M * K * 2) + r256(M * N * 2) + r256(G * K * N * 4) + split(M, N, K))
     # one output tile per expert and 14030 rows: 512-token chunks, 27 slots

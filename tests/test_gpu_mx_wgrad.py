@@ -90,6 +90,43 @@ def test_mx_wgrad_vs_oracle(orc, dev, trans_out, accumulate, fmt):
         assert floored_rel_err(inc, D) <= BF16_TOL, g
 
 
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("trans_out", [0, 1])
+def test_mx_wgrad_multi_tile_both_orders(orc, dev, trans_out, fmt):
+    # several output tiles with ragged edges (K = 520, N = 264), an expert
+    # over five 128-byte stages and experts ending inside a stage, block and
+    # tile; the queued and the static tile order give the same bits
+    lens = np.array([700, 0, 33, 260, 1, 64], np.int64)
+    K, N = 520, 264
+    M, G = int(lens.sum()), len(lens)
+    a = synth.randn_bf16((M, K), seed=111, std=K ** -0.5, device=dev)
+    dy = synth.randn_bf16((M, N), seed=112, std=1e-2, device=dev)
+    aq, as_ = quantize_tokens(dev, a, lens, fmt)
+    dq, ds = quantize_tokens(dev, dy, lens, fmt)
+    raq, ras, _ = orc.mx_quantize_tokens(bits16(a), lens, fmt)
+    rdq, rds, _ = orc.mx_quantize_tokens(bits16(dy), lens, fmt)
+    av = orc.mx_dequantize_tokens(raq, ras, lens, fmt)
+    dv = orc.mx_dequantize_tokens(rdq, rds, lens, fmt)
+    offs = synth.offsets(lens)
+    runs = []
+    try:
+        for cfg in (ptm.PT_CONFIG_RULES, 1):
+            ptm.pt_set_gemm_config(cfg)
+            print(f"mx wgrad multi-tile fmt={fmt} trans_out={trans_out} cfg={cfg}", flush=True)
+            runs.append(wgrad_mx(dev, aq, as_, dq, ds, lens, N, K, trans_out, 1, fmt))
+    finally:
+        ptm.pt_set_gemm_config(ptm.PT_CONFIG_RULES)
+    before, after = runs[0]
+    assert (runs[1][0] == before).all() and (runs[1][1] == after).all(), "tile orders disagree"
+    for g in range(G):
+        if lens[g] == 0:
+            assert (after[g] == before[g]).all()
+            continue
+        D = av[offs[g]:offs[g + 1]].T @ dv[offs[g]:offs[g + 1]]
+        inc = after[g].astype(np.float64) - before[g]
+        assert floored_rel_err(inc, D.T if trans_out else D) <= BF16_TOL, g
+
+
 def test_mx_wgrad_needs_its_workspace(dev):
     lens = dev_i64(np.array([40], np.int64), dev)
     q = torch.zeros((40, 64), dtype=torch.uint8, device=dev)

@@ -8,8 +8,9 @@ with one output tile per expert (K = N = 256, chunk length 512 tokens) a
 chunks.  Checked: the increment against the oracle's A_g^T dY_g (BF16
 tolerance), zero-token experts untouched when accumulating and zeroed when
 not, bit-identical reruns, both output layouts, the static and queued tile
-orders, MXFP8 operands through the same path, and that malformed
-(overlapping) ranges never write past the partial slots."""
+orders, the MXFP8 / MXFP4 weight gradient's own split (whole 256-token
+stages per chunk), and that malformed (overlapping) ranges never write past
+the partial slots."""
 import numpy as np
 import pytest
 import torch
@@ -113,27 +114,43 @@ def test_split_close_to_unsplit(dev, data):
     assert floored_rel_err(split, whole) <= 1e-4
 
 
-def test_split_mxfp8_wgrad_vs_oracle(orc, dev, data):
+@pytest.mark.parametrize("fmt", [ptm.PT_MXFP8_E4M3, ptm.PT_MXFP4_E2M1], ids=["e4m3", "e2m1"])
+def test_split_mx_wgrad_vs_oracle_and_deterministic(orc, dev, data, fmt):
+    # the MX weight gradient cuts the long expert the same way (chunks of
+    # 512 tokens, whole 256-token stages): against the oracle on the same
+    # codes, bit-identical on a rerun and within fp32 rounding of the uncut
+    # sum (a workspace one byte short of the full size has no slots)
     a, dy, _ = data
     M, G = a.shape[0], len(LENS)
     lens_d = dev_i64(LENS, dev)
-    aq = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    dq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    cols = (lambda c: c) if fmt == ptm.PT_MXFP8_E4M3 else (lambda c: c // 2)
+    aq = torch.empty((M, cols(K)), dtype=torch.uint8, device=dev)
+    dq = torch.empty((M, cols(N)), dtype=torch.uint8, device=dev)
     as_ = torch.zeros((M // 32 + G, K), dtype=torch.uint8, device=dev)
     ds = torch.zeros((M // 32 + G, N), dtype=torch.uint8, device=dev)
-    ptm.pt_mx_quantize_tokens(a, lens_d, None, aq, as_, G, M, K, ptm.PT_MXFP8_E4M3)
-    ptm.pt_mx_quantize_tokens(dy, lens_d, None, dq, ds, G, M, N, ptm.PT_MXFP8_E4M3)
-    ws, n = ws_full(dev, G, M, ptm.PT_MXFP8_E4M3, tail=4096)
+    ptm.pt_mx_quantize_tokens(a, lens_d, None, aq, as_, G, M, K, fmt)
+    ptm.pt_mx_quantize_tokens(dy, lens_d, None, dq, ds, G, M, N, fmt)
+    ws, n = ws_full(dev, G, M, fmt, tail=4096)
+    print(f"split mx wgrad fmt={fmt}", flush=True)
     before, after = run(dev, aq, dy=dq, lens=LENS, trans_out=0, accumulate=1, ws=ws, nbytes=n,
-                        dtype=ptm.PT_MXFP8_E4M3, a_s=as_, d_s=ds)
+                        dtype=fmt, a_s=as_, d_s=ds)
     assert (u8(ws[n:]) == 0xA5).all()
-    raq, ras, _ = orc.mx_quantize_tokens(bits16(a), LENS, orc.E4M3)
-    rdq, rds, _ = orc.mx_quantize_tokens(bits16(dy), LENS, orc.E4M3)
-    av = orc.mx_dequantize_tokens(raq, ras, LENS, orc.E4M3)
-    dv = orc.mx_dequantize_tokens(rdq, rds, LENS, orc.E4M3)
+    ofmt = orc.E4M3 if fmt == ptm.PT_MXFP8_E4M3 else orc.E2M1
+    raq, ras, _ = orc.mx_quantize_tokens(bits16(a), LENS, ofmt)
+    rdq, rds, _ = orc.mx_quantize_tokens(bits16(dy), LENS, ofmt)
+    assert (u8(aq) == raq).all() and (u8(dq) == rdq).all()
+    av = orc.mx_dequantize_tokens(raq, ras, LENS, ofmt)
+    dv = orc.mx_dequantize_tokens(rdq, rds, LENS, ofmt)
     co = np.concatenate([[0], np.cumsum(LENS)])
     D = np.stack([av[co[g]:co[g + 1]].T @ dv[co[g]:co[g + 1]] for g in range(G)])
     check(before, after, D, LENS, 0, 1)
+    _, again = run(dev, aq, dy=dq, lens=LENS, trans_out=0, accumulate=1, ws=ws, nbytes=n, dtype=fmt, a_s=as_,
+                   d_s=ds)
+    assert (again == after).all(), "split reduction not deterministic"
+    _, whole = run(dev, aq, dy=dq, lens=LENS, trans_out=0, accumulate=1, ws=ws, nbytes=n - 1, dtype=fmt, a_s=as_,
+                   d_s=ds)
+    assert not (whole == after).all(), "the short workspace should run uncut"
+    assert floored_rel_err(after, whole) <= 1e-4
 
 
 def test_split_overlapping_ranges_stay_in_bounds(dev, data):
