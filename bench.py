@@ -82,6 +82,9 @@ TRAFFIC_KEYS = {
     "cfg2_bf16_wgrad": ["cfg2_bf16_wgrad"],
     "cfg3_mxfp8_fwd": ["cfg3_mxfp8_fwd"],
     "cfg3_mxfp8_quantize_A": ["cfg3_mx_quantize_e4m3_A"],
+    # A and dY each quantised along tokens and transposed (per-launch means), then the weight gradient
+    "cfg3_mxfp8_wgrad": ["cfg3_mx_tokens_quant", "cfg3_mx_tokens_quant", "cfg3_mx_wgrad_transpose",
+                         "cfg3_mx_wgrad_transpose", "cfg3_mxfp8_wgrad"],
     "cfg4_mxfp4_mlp": ["cfg4_mx_quantize_e2m1_X", "cfg4_mxfp4_fc1_swiglu_mxfp4", "cfg4_mxfp4_fc2"],
     "fc2_bf16_dgrad_swiglu_bwd": ["fc2_bf16_dgrad_swiglu_bwd"],
     "fc2_mxfp8_dgrad_swiglu_bwd": ["fc2_mxfp8_dgrad_swiglu_bwd"],
