@@ -472,10 +472,10 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t n)
 // 4, 6 (WPR 2); blocks past an expert's last one read zero.  plan[2g] =
 // bstart_g and plan[2g + 1] = S_g (written by workgroup 0) tell the GEMM
 // where each expert starts.  A work item is one stage of one expert for 128
-// channels: its tokens are staged in LDS and read back as blocks of 4 tokens
-// x 4 channels turned with byte permutes (E4M3) or 16 tokens x 8 channels of
-// nibbles (E2M1) into an LDS copy of the output rows, which then leave as
-// 128-byte runs.
+// channels: its tokens are staged in LDS (swizzled 16-byte chunks) and read
+// back as blocks of 4 tokens x 4 channels turned with byte permutes (E4M3)
+// or 16 tokens x 8 channels of nibbles (E2M1), the lanes of a channel group
+// writing whole 128-byte runs of its rows.
 constexpr int kTrCh = 128;                              // channels per work item
 
 template <int FMT>
@@ -485,15 +485,13 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_transpose_kernel(
 {
     constexpr int TS = FMT == 0 ? 128 : 256;            // tokens per stage
     constexpr int RB = FMT == 0 ? kTrCh : kTrCh / 2;    // input bytes of a token's 128 channels
-    constexpr int LROW = FMT == 0 ? RB + 8 : RB + 4;    // LDS row pitch (bytes): 34 / 17 words
-    constexpr int OROW = 132;                           // output rows: 33 words
+    constexpr int LROW = 256;                           // LDS row pitch (bytes): 16 chunks of 16
     extern __shared__ __attribute__((aligned(16))) int sm_tok[];
     GroupTable tab;
     tokens_table(tab, sm_tok, lens, offs, G, M, nullptr);      // tile0: each expert's first block
     int *sst = tab.tile0 + G + 1 + 8;                           // each expert's first stage, [G + 1]
     int *scr = sst + G + 1;
     uint8_t *tile = (uint8_t *)(scr + 8);
-    uint8_t *otile = tile + TS * LROW;                          // [128 channels][OROW] output bytes
     {
         const int per = (G + kThreads - 1) / kThreads, g0 = threadIdx.x * per;
         int sum = 0;
@@ -530,36 +528,49 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_transpose_kernel(
         const int nbytes = (FMT == 0 ? 32 : 16) * min(TS / 32, nb - kt * (TS / 32));   // output bytes per row
         const int64_t r0 = (int64_t)tab.row0[g] + tok0;
         const int64_t ob = (int64_t)(FMT == 0 ? 32 : 16) * tab.tile0[g] + (int64_t)kt * 128;
-        // stage the tokens' channel bytes (E4M3 rows hold C bytes, 8-byte
-        // loads; E2M1 rows C/2, a multiple of 4)
+        // Stage the tokens' channel bytes: 16-byte chunk k of token row t at
+        // chunk position k ^ sw(t) of a 256-byte LDS row, sw(t) = 2j ^ 8 (t & 1)
+        // (E4M3) or j ^ 4 (t & 3) (E2M1) with j = t / 16, so that both the
+        // row-wise writes and the column reads below hit 64 distinct banks.
+        // Loads of 16 bytes where a row's bytes allow it, else 8 or 4.
         const int64_t rowb = FMT == 0 ? C : C / 2;
         const int cb0 = FMT == 0 ? c0 : c0 / 2;
-        constexpr int LW = FMT == 0 ? 8 : 4;
-        for (int e = tid; e < TS * (RB / LW); e += kThreads) {
-            const int t = e / (RB / LW), k = (e % (RB / LW)) * LW;
-            const bool in = t < nvalid && cb0 + k < rowb;
-            const uint8_t *src = q + (r0 + t) * rowb + cb0 + k;
-            if constexpr (FMT == 0) {
-                const uintx2 v = in ? *(const uintx2 *)src : uintx2{0u, 0u};
-                *(uintx2 *)(tile + t * LROW + k) = v;
+        auto swz = [](int t) { return FMT == 0 ? (2 * (t >> 4)) ^ (8 * (t & 1)) : (t >> 4) ^ (4 * (t & 3)); };
+        constexpr int NCH = RB / 16;                         // 16-byte chunks of a token's bytes
+        const int lw = rowb % 16 == 0 ? 16 : (rowb % 8 == 0 ? 8 : 4);
+        for (int e = tid; e < TS * NCH; e += kThreads) {
+            const int t = e / NCH, k = e % NCH;
+            uint8_t *dst = tile + t * LROW + 16 * (k ^ swz(t));
+            const int64_t off = (r0 + t) * rowb + cb0 + 16 * k;
+            const bool in = t < nvalid;
+            const int room = (int)(rowb - (cb0 + 16 * k));      // bytes of this chunk inside the row
+            if (lw == 16) {
+                *(uintx4 *)dst = in && room > 0 ? *(const uintx4 *)(q + off) : uintx4{0u, 0u, 0u, 0u};
             } else {
-                *(uint32_t *)(tile + t * LROW + k) = in ? *(const uint32_t *)src : 0u;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const bool ok = in && 4 * w < room;
+                    ((uint32_t *)dst)[w] = ok ? *(const uint32_t *)(q + off + 4 * w) : 0u;
+                }
             }
         }
         __syncthreads();
+        // 32-bit word w of token row t
+        auto word = [&](int t, int w) {
+            return *(const uint32_t *)(tile + t * LROW + 16 * ((w >> 2) ^ swz(t)) + 4 * (w & 3));
+        };
         if constexpr (FMT == 0) {
-            // thread: channels 4cq .. 4cq + 3, tokens 16j .. 16j + 15; 4 x 4
-            // byte blocks turned with v_perm; lanes on consecutive channel
-            // quads (row pitch 34 words: the two token chunks of a wave land
-            // on disjoint banks)
-            const int cq = tid & 31, j = tid >> 5;
+            // thread: channels 4cq .. 4cq + 3, tokens 16j .. 16j + 15, turned
+            // as 4 x 4 byte blocks with v_perm; the eight lanes of a channel
+            // quad write 128 contiguous bytes of each of its four rows
+            const int j = tid & 7, cq = tid >> 3;
             if (16 * j < nbytes) {
                 uint32_t o[4][4];                    // [channel][token quad]
 #pragma unroll
                 for (int tq4 = 0; tq4 < 4; ++tq4) {
                     uint32_t w[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) w[u] = *(const uint32_t *)(tile + (16 * j + 4 * tq4 + u) * LROW + 4 * cq);
+                    for (int u = 0; u < 4; ++u) w[u] = word(16 * j + 4 * tq4 + u, cq);
                     const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
                     const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
                     const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
@@ -571,18 +582,19 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_transpose_kernel(
                 }
 #pragma unroll
                 for (int d = 0; d < 4; ++d)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) *(uint32_t *)(otile + (4 * cq + d) * OROW + 16 * j + 4 * e) = o[d][e];
+                    if (c0 + 4 * cq + d < C)
+                        *(uintx4 *)(qt + (int64_t)(c0 + 4 * cq + d) * pitch + ob + 16 * j) =
+                            uintx4{o[d][0], o[d][1], o[d][2], o[d][3]};
             }
         } else {
-            // thread: channels 8co .. 8co + 7 (one input word per token),
-            // tokens 16j .. 16j + 15 -> 8 bytes per channel (row pitch 17
-            // words: the wave's four token chunks land on disjoint banks)
-            const int co = tid & 15, j = tid >> 4;
+            // thread: channels 8co .. 8co + 7 (one word per token), tokens
+            // 16j .. 16j + 15 -> 8 bytes per channel; the sixteen lanes of a
+            // channel octet write 128 contiguous bytes of each of its rows
+            const int j = tid & 15, co = tid >> 4;
             if (8 * j < nbytes) {
                 uint32_t w[16];
 #pragma unroll
-                for (int u = 0; u < 16; ++u) w[u] = *(const uint32_t *)(tile + (16 * j + u) * LROW + 4 * co);
+                for (int u = 0; u < 16; ++u) w[u] = word(16 * j + u, co);
 #pragma unroll
                 for (int d = 0; d < 8; ++d) {
                     uint32_t lo = 0u, hi = 0u;
@@ -591,20 +603,9 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_transpose_kernel(
                         lo |= ((w[u] >> (4 * d)) & 0xFu) << (4 * u);
                         hi |= ((w[8 + u] >> (4 * d)) & 0xFu) << (4 * u);
                     }
-                    *(uint32_t *)(otile + (8 * co + d) * OROW + 8 * j) = lo;
-                    *(uint32_t *)(otile + (8 * co + d) * OROW + 8 * j + 4) = hi;
+                    if (c0 + 8 * co + d < C)
+                        *(uintx2 *)(qt + (int64_t)(c0 + 8 * co + d) * pitch + ob + 8 * j) = uintx2{lo, hi};
                 }
-            }
-        }
-        __syncthreads();
-        // the channel rows leave as 128-byte runs (8 lanes per row)
-        for (int e = tid; e < kTrCh * 8; e += kThreads) {
-            const int row = e >> 3, ch = e & 7;
-            if (16 * ch < nbytes && c0 + row < C) {
-                const uint8_t *src = otile + row * OROW + 16 * ch;
-                *(uintx4 *)(qt + (int64_t)(c0 + row) * pitch + ob + 16 * ch) =
-                    uintx4{*(const uint32_t *)src, *(const uint32_t *)(src + 4), *(const uint32_t *)(src + 8),
-                           *(const uint32_t *)(src + 12)};
             }
         }
         // the stage's scale words, one channel per thread
@@ -862,8 +863,8 @@ hipError_t launch_mx_tokens_transpose(const uint8_t *q, const uint8_t *scales, c
                                       int64_t pitch, uint32_t *st, int *plan, hipStream_t s)
 {
     if (G == 0 || C == 0) return hipSuccess;
-    const int rb = fmt == 0 ? kTrCh : kTrCh / 2, ts = fmt == 0 ? 128 : 256;
-    const size_t lds = table_bytes(G) + 4 * (G + 1) + 32 + (size_t)ts * (fmt == 0 ? rb + 8 : rb + 4) + kTrCh * 132;
+    const int ts = fmt == 0 ? 128 : 256;
+    const size_t lds = table_bytes(G) + 4 * (G + 1) + 32 + (size_t)ts * 256;
     const int64_t items = mx_wgrad_stages(M, G, fmt) * ((C + kTrCh - 1) / kTrCh);
     int64_t grid = (int64_t)device_cus() * 4;
     if (grid > items) grid = items;
