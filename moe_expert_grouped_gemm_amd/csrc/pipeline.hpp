@@ -354,15 +354,26 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) amax = max(amax, max(v[q][e] & 0x7FFFu, (v[q][e] >> 16) & 0x7FFFu));
             const uint32_t E = mx_scale_byte<2>(amax);
+            // each value times 2^(127 - E) (exact: a power of two), clamped to
+            // the grid maximum 6, then the hardware's nearest-even E2M1
+            // conversion, as the row quantiser encodes (the 128 x 256 kernels'
+            // integer encoder gives the same codes; the tests compare both)
+            const int sc = 127 - (int)E;
             uint32_t packed[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                uint32_t w = 0;
+                float f[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    w |= mx_encode<1>(v[q][e] & 0xFFFFu, E) << (8 * e);
-                    w |= mx_encode<1>(v[q][e] >> 16, E) << (8 * e + 4);
+                    f[2 * e] = __builtin_ldexpf(bf16_to_f32(v[q][e] & 0xFFFFu), sc);
+                    f[2 * e + 1] = __builtin_ldexpf(bf16_to_f32(v[q][e] >> 16), sc);
                 }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = __builtin_fminf(__builtin_fmaxf(f[e], -6.0f), 6.0f);
+                uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], 1.0f, 0);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], 1.0f, 1);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], 1.0f, 2);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], 1.0f, 3);
                 packed[q] = w;
             }
             *(uintx4 *)(o + (int64_t)(m0 + r) * ldo + (j0 >> 1)) = uintx4{packed[0], packed[1], packed[2], packed[3]};

@@ -1,6 +1,8 @@
-"""CPU check of the integer MX encoder that the grouped GEMM's SwiGLU ->
-MXFP4 epilogue uses (mx_scale_byte / mx_encode in the library's
-common.hpp), compiled for the host and compared byte for byte with the
+"""CPU check of the library's integer MX rules in common.hpp, compiled for
+the host: the E8M0 scale rule that every SwiGLU -> MXFP4 epilogue uses
+(mx_scale_byte) and the integer encoder of the 128 x 256 kernels' epilogue
+(mx_encode; the 256 x 256 kernels encode with the hardware conversion the
+row quantiser uses, pinned on the GPU).  Compared byte for byte with the
 oracle's quantiser over every finite bf16 pattern combined with every scale
 byte a 32-value block holding it can reach.
 
