@@ -3,7 +3,8 @@
 next to each kernel's operand ring, so every kernel family is run: the BF16
 forward (both weight layouts, plain and SwiGLU epilogues, every kernel
 configuration and both tile orders), the dgrad, the weight gradient (with
-and without the split-reduction workspace) and the MXFP8 / MXFP4 forward.
+and without the split-reduction workspace), and the MXFP8 / MXFP4 forward
+and weight gradient.
 The routing mixes empty experts, single rows, experts under one tile and a
 few over two tiles."""
 import numpy as np
@@ -152,3 +153,44 @@ def test_mx_fwd_max_groups(orc, dev, rules, fmt, name, epi):
             if first is None:
                 first = got
             assert (got == first).all(), "configurations or tile orders disagree"
+
+
+@pytest.mark.parametrize("fmt,name", FMTS, ids=[f[1] for f in FMTS])
+def test_mx_wgrad_max_groups(orc, dev, fmt, name):
+    # the MX weight gradient's transposer and kernel at 1024 experts (most of
+    # them far shorter than one 32-token block, one over five stages)
+    K, N = 64, 96
+    ofmt = orc.E4M3 if fmt == ptm.PT_MXFP8_E4M3 else orc.E2M1
+    a = synth.randn_bf16((M, K), seed=309, std=K ** -0.5, device=dev)
+    dy = synth.randn_bf16((M, N), seed=310, std=1e-2, device=dev)
+    lens_d = dev_i64(LENS, dev)
+    cols = (lambda c: c) if fmt == ptm.PT_MXFP8_E4M3 else (lambda c: c // 2)
+    aq = torch.empty((M, cols(K)), dtype=torch.uint8, device=dev)
+    dq = torch.empty((M, cols(N)), dtype=torch.uint8, device=dev)
+    as_ = torch.zeros((M // 32 + G, K), dtype=torch.uint8, device=dev)
+    ds = torch.zeros((M // 32 + G, N), dtype=torch.uint8, device=dev)
+    ptm.pt_mx_quantize_tokens(a, lens_d, None, aq, as_, G, M, K, fmt)
+    ptm.pt_mx_quantize_tokens(dy, lens_d, None, dq, ds, G, M, N, fmt)
+    g = torch.Generator(device=dev)
+    g.manual_seed(311)
+    mg = (torch.randn((G, K, N), generator=g, device=dev) * 1e-3).float()
+    before = mg.cpu().numpy()
+    n = ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, fmt)
+    ws = torch.zeros((n,), dtype=torch.uint8, device=dev)
+    print(f"G=1024 {name} wgrad M={M}", flush=True)
+    ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, lens_d, None, G, M, N, K, fmt, 0, 1, workspace=ws)
+    torch.cuda.synchronize()
+    after = mg.cpu().numpy()
+    assert ptm.pt_read_error_flags(ws) == 0
+    raq, ras, _ = orc.mx_quantize_tokens(bits16(a), LENS, ofmt)
+    rdq, rds, _ = orc.mx_quantize_tokens(bits16(dy), LENS, ofmt)
+    assert (u8(aq) == raq).all() and (u8(dq) == rdq).all()
+    av = orc.mx_dequantize_tokens(raq, ras, LENS, ofmt)
+    dv = orc.mx_dequantize_tokens(rdq, rds, LENS, ofmt)
+    offs = np.concatenate([[0], np.cumsum(LENS)])
+    for e in range(G):
+        if LENS[e] == 0:
+            assert (after[e] == before[e]).all(), f"empty expert {e} touched"
+            continue
+        D = av[offs[e]:offs[e + 1]].T @ dv[offs[e]:offs[e + 1]]
+        assert floored_rel_err(after[e].astype(np.float64) - before[e], D) <= BF16_TOL, e
