@@ -578,6 +578,9 @@ __device__ __forceinline__ uintx4 wld(uint32_t addr)
 // A slots, so three 48 KiB slots fit and two stages are in flight -- such a
 // tile has half the MFMAs per stage, and its loads would otherwise wait.
 constexpr int MX_RING = 3 * (128 * WROW + WBN * WROW);
+// LDS row pitch of the weight gradient's fp32 epilogue rows: 256 values and
+// 32 bytes, so rows 4 apart (the two lane halves of a store) are 32 banks apart
+constexpr int WG_RP = WBN * 4 + 32;
 static_assert(MX_RING >= 2 * WSTAGE, "ring sizes");
 
 // LDS of the ring or of the epilogue tile, whichever is larger; the group
@@ -585,8 +588,9 @@ static_assert(MX_RING >= 2 * WSTAGE, "ring sizes");
 template <int EPI>
 constexpr int wide_lds_bytes()
 {
-    // the weight gradient: 256-row tiles only, stored from the registers
-    if constexpr (EPI == kEpiWgrad) return 2 * WSTAGE;
+    // the weight gradient: 256-row tiles only; its epilogue stages half a
+    // tile of fp32 rows (WG_RP bytes apart)
+    if constexpr (EPI == kEpiWgrad) return 2 * WSTAGE > 128 * WG_RP ? 2 * WSTAGE : 128 * WG_RP;
     return MX_RING > epi_lds_bytes<EPI, 4>() ? MX_RING : epi_lds_bytes<EPI, 4>();
 }
 
@@ -789,23 +793,10 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                     (uint32_t)((g * p.N + clamp1<EPI>(col_of<EPI>(nt, wn * 128 + bj * 32 + r32, p.N), p.N)) * KS);
         }
 
-        // accumulators start at zero, or for an accumulating weight gradient
-        // at the main_grad tile itself (its loads land with stage 0's)
+        // accumulators start at zero (the weight gradient adds main_grad in
+        // its epilogue)
         floatx16 acc[TMI][4];
-        if (WG && p.accumulate && chunk == 0) {
-            const float *og = (const float *)p.out + (int64_t)g * p.o_gstride;
-#pragma unroll
-            for (int bi = 0; bi < TMI; ++bi)
-#pragma unroll
-                for (int bj = 0; bj < 4; ++bj) {
-                    const int n = nt * WBN + wn * 128 + bj * 32 + r32;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int i = m0 + wrow0 + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                        acc[bi][bj][r] = (n < p.wcols && i < rows) ? og[(int64_t)i * p.ldo + n] : 0.0f;
-                    }
-                }
-        } else {
+        {
 #pragma unroll
             for (int i = 0; i < TMI; ++i)
 #pragma unroll
@@ -1017,12 +1008,13 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                 }
         }
         if constexpr (WG) {
-            // fp32 tile straight from the accumulators (32 lanes write 128
-            // contiguous bytes of a row); nothing is outstanding, and saying
-            // so keeps the compiler from waiting before each store.  Chunk 0
-            // goes to main_grad, chunk c >= 1 to its partial slot (none past
-            // the workspace's slots, which only malformed lengths reach).
-            wait_vmcnt<0>();
+            // The fp32 tile goes through LDS half a tile (128 rows) at a time,
+            // so that main_grad is read, added to and written in whole 16-byte
+            // pieces (a lane's accumulators hold one column of 16 rows).  Chunk
+            // 0 adds the sum into main_grad (or overwrites it when not
+            // accumulating), chunk c >= 1 writes its partial slot (none past the
+            // workspace's slots, which only malformed lengths reach).  The ring
+            // is free: the k-loop ended with a barrier and nothing in flight.
             float *og = (float *)p.out + (int64_t)g * p.o_gstride;
             bool keep = true;
             if (chunk > 0) {
@@ -1030,18 +1022,46 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                 keep = slot < p.nslots;
                 og = p.partials + (int64_t)slot * p.o_gstride;
             }
+            const bool rmw = p.accumulate && chunk == 0;
 #pragma unroll
-            for (int bi = 0; bi < TMI; ++bi)
+            for (int half = 0; half < 2; ++half) {
+                if ((wm >> 1) == half) {
 #pragma unroll
-                for (int bj = 0; bj < 4; ++bj) {
-                    const int n = nt * WBN + wn * 128 + bj * 32 + r32;
-                    if (n >= p.wcols || !keep) continue;
+                    for (int bi = 0; bi < TMI; ++bi)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int i = m0 + wrow0 + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                        if (i < rows) og[(int64_t)i * p.ldo + n] = acc[bi][bj][r];
+                        for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int row = wrow0 - 128 * half + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                                *(float *)(smem + row * WG_RP + (wn * 128 + bj * 32 + r32) * 4) = acc[bi][bj][r];
+                            }
+                }
+                wait_lgkm0();
+                barrier();
+                // 128 rows of 64 pieces, 16 per thread, in two rounds whose
+                // main_grad pieces are loaded first, all at once
+                constexpr int NPC = 128 * (WBN / 4) / WTHREADS / 2;
+#pragma unroll
+                for (int rd = 0; rd < 2; ++rd) {
+                    floatx4 mgv[NPC];
+#pragma unroll
+                    for (int k = 0; k < NPC; ++k) {
+                        const int ci = (rd * NPC + k) * WTHREADS + tid, rr = ci >> 6, c4 = ci & 63;
+                        const int i = m0 + 128 * half + rr, n = nt * WBN + 4 * c4;
+                        mgv[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                        if (rmw && i < rows && n < p.wcols) mgv[k] = *(const floatx4 *)(og + (int64_t)i * p.ldo + n);
+                    }
+#pragma unroll
+                    for (int k = 0; k < NPC; ++k) {
+                        const int ci = (rd * NPC + k) * WTHREADS + tid, rr = ci >> 6, c4 = ci & 63;
+                        const int i = m0 + 128 * half + rr, n = nt * WBN + 4 * c4;
+                        const floatx4 v = *(const floatx4 *)(smem + rr * WG_RP + c4 * 16);
+                        if (keep && i < rows && n < p.wcols) *(floatx4 *)(og + (int64_t)i * p.ldo + n) = mgv[k] + v;
                     }
                 }
+                wait_lgkm0();
+                barrier();
+            }
         } else {
             store_tile_lds_w<EPI, 4, TMI, 4, TBM>(acc, smem, p.out, p.out_scale, p.ldo, p.N, row0, m0, rows, nt, wrow0,
                                                   wn, p.swiglu_limit, p.aux, p.ldaux, p.save, p.ldsave);
