@@ -573,6 +573,14 @@ __device__ __forceinline__ uintx4 wld(uint32_t addr)
     return ldsr_u128<OFF>(addr);
 }
 
+// 4-byte LDS read (inline asm, for the same reason as the fragment reads)
+__device__ __forceinline__ uint32_t wld32(uint32_t addr)
+{
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
 // The ring per tile height: a 256-row tile keeps two 64 KiB slots (one
 // stage in flight while one computes); a tile of at most 128 rows has 16 KiB
 // A slots, so three 48 KiB slots fit and two stages are in flight -- such a
@@ -581,6 +589,12 @@ constexpr int MX_RING = 3 * (128 * WROW + WBN * WROW);
 // LDS row pitch of the weight gradient's fp32 epilogue rows: 256 values and
 // 32 bytes, so rows 4 apart (the two lane halves of a store) are 32 banks apart
 constexpr int WG_RP = WBN * 4 + 32;
+// 256-row tiles with stage-major scale copies: each ring slot's scale words
+// (A's 256 rows, then B's, 4 bytes per row for E4M3 and 8 for E2M1) come in
+// by direct loads with the stage, into this area after the two slots
+constexpr int WSC_LDS = 2 * WSTAGE;
+constexpr int WSC_SLOT = 2 * 256 * 8;                   // 4 KiB
+static_assert(WSC_LDS + 2 * WSC_SLOT <= MX_RING, "scale slots fit beside the ring");
 static_assert(MX_RING >= 2 * WSTAGE, "ring sizes");
 
 // LDS of the ring or of the epilogue tile, whichever is larger; the group
@@ -590,7 +604,7 @@ constexpr int wide_lds_bytes()
 {
     // the weight gradient: 256-row tiles only; its epilogue stages half a
     // tile of fp32 rows (WG_RP bytes apart)
-    if constexpr (EPI == kEpiWgrad) return 2 * WSTAGE > 128 * WG_RP ? 2 * WSTAGE : 128 * WG_RP;
+    if constexpr (EPI == kEpiWgrad) return WSC_LDS + 2 * WSC_SLOT > 128 * WG_RP ? WSC_LDS + 2 * WSC_SLOT : 128 * WG_RP;
     return MX_RING > epi_lds_bytes<EPI, 4>() ? MX_RING : epi_lds_bytes<EPI, 4>();
 }
 
@@ -813,19 +827,74 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         // prologue: stage 0 (the loads of each stage form one group in
         // program order), and the id of the next tile (its atomic goes out
         // first and lands under the stage's loads)
+        // scale words through LDS (256-row tiles, stage-major copies): waves
+        // 0 .. NSW / 2 - 1 load A's 256 rows of stage kt, the next NSW / 2
+        // B's, 16 bytes per lane in row order (B's SwiGLU order: runs of 64
+        // rows gate j, up I + j, gate j + 64, up I + j + 64); every lane then
+        // reads its 6 rows' words after the stage's barrier
+        constexpr bool LSC = TMI == 2 && (WSC == kWE4M3Swz || WSC == kWE2M1Swz);
+        constexpr int SWPR = WSC == kWE2M1Swz ? 2 : 1;      // words per row
+        constexpr int NSW = 2 * SWPR;                        // loading waves
+        uint32_t scvoff = 0, scstride = 0, scbytes = 0;
+        const uint8_t *scbase = sr.a;
+        uint32_t wsc[6] = {0, 0, 0, 0, 0, 0};
+        if constexpr (LSC) {
+            const int isb = wave >= SWPR;                      // B's scale words
+            const int pc = (wave - isb * SWPR) * 64 + lane;    // 16-byte piece of the operand's 256 rows
+            const int tr = pc * 4 / SWPR;                      // its first tile row
+            uint32_t row;
+            if (!isb) {
+                row = (uint32_t)(row0 + m0 + tr);
+            } else if (!epi_glu(EPI)) {
+                row = (uint32_t)((WG ? 0 : g * p.N) + nt * WBN + tr);
+            } else {
+                const int q = tr >> 6;
+                row = (uint32_t)(g * p.N + (q & 1) * (p.N >> 1) + nt * (WBN / 2) + (q >> 1) * 64 + (tr & 63));
+            }
+            scvoff = row * SWPR * 4u;
+            scbase = isb ? sr.b : sr.a;
+            scstride = isb ? sr.bstride : sr.astride;
+            scbytes = isb ? sr.bbytes : sr.abytes;
+        }
+        // stage kt's words into scale slot sl (past the end: nothing read)
+        auto issue_sc = [&](int kt, int sl) {
+            if (wave < NSW)
+                dma16(scbase, scbytes,
+                      smem + WSC_LDS + sl * WSC_SLOT + (wave >= SWPR ? 256 * SWPR * 4 : 0) + (wave % SWPR) * 1024,
+                      kt < nk ? scvoff + (uint32_t)kt * scstride : kOOB, 0u);
+        };
+        // this lane's 6 words of scale slot sl: A rows wrow0 + 32 bi + r32, B
+        // rows wn * 128 + 32 bj + r32 (E2M1: the lane half's word)
+        auto read_sc = [&](int sl) {
+            const uint32_t b0 = lds0 + WSC_LDS + sl * WSC_SLOT + (WSC == kWE2M1Swz ? 4u * h : 0u);
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi) wsc[bi] = wld32(b0 + (uint32_t)(wrow0 + bi * 32 + r32) * SWPR * 4);
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj)
+                wsc[2 + bj] = wld32(b0 + 256 * SWPR * 4 + (uint32_t)(wn * 128 + bj * 32 + r32) * SWPR * 4);
+        };
+        auto wait_sc = [&]() {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(wsc[0]), "+v"(wsc[1]), "+v"(wsc[2]), "+v"(wsc[3]), "+v"(wsc[4]), "+v"(wsc[5]));
+        };
         uint32_t sc[NS][6];
         if (tid == 0) tq.issue();
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int st = 0; st < NS - 1; ++st) {
             wissue_stage<TNA>(smem, o, st * SLOT, st, nk, Kb, wave, ASLOT);
-            wload_scales<WSC>(sc[st], sr, st, nk, h);
+            if constexpr (LSC) issue_sc(st, st);
+            else wload_scales<WSC>(sc[st], sr, st, nk, h);
             asm volatile("" ::: "memory");
         }
         wait_vmcnt<(NS - 2) * NLS>();              // stage 0 landed
         if (tid == 0) s_id[par ^ 1] = tq.resolve(tile);
         wait_lgkm0();
         barrier();
+        if constexpr (LSC) {
+            read_sc(0);
+            wait_sc();
+        }
 
         // Fragments.  E2M1: f*[s & 1] hold chunk 2s + h for MFMA step s (A 2 x,
         // B 4 x 16 bytes).  E4M3: step s uses chunks 4s + h and 4s + 2 + h;
@@ -861,10 +930,16 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             constexpr int Q = (P + 1) % NS, PN = (P + NS - 1) % NS;
             const int kt = kt0 + P;
             uint32_t w[6];
-            wscale_words<WSC>(sc[P], w, sr, kt, nfull, nb_last, h);
+            if constexpr (LSC) {
+#pragma unroll
+                for (int i = 0; i < 6; ++i) w[i] = wsc[i];
+            } else {
+                wscale_words<WSC>(sc[P], w, sr, kt, nfull, nb_last, h);
+            }
             // stage kt + NS - 1 goes to the slot stage kt - 1 freed at its barrier
             wissue_stage<TNA>(smem, o, PN * SLOT, kt + NS - 1, nk, Kb, wave, ASLOT);
-            wload_scales<WSC>(sc[PN], sr, kt + NS - 1, nk, h);
+            if constexpr (LSC) issue_sc(kt + NS - 1, PN);
+            else wload_scales<WSC>(sc[PN], sr, kt + NS - 1, nk, h);
             asm volatile("" ::: "memory");
             if constexpr (FMT == 1) {
 #pragma unroll
@@ -938,6 +1013,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             wait_vmcnt<(NS - 2) * NLS>();
             barrier();
             if (kt + 1 < nk) {
+                if constexpr (LSC) read_sc(Q);
                 if constexpr (FMT == 1) {
                     rdA(fa[0], aX(Q, 0));
                     fb[0][0] = wld<0 * RB>(bX(Q, 0));
@@ -957,6 +1033,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                                  : "+v"(ea[0][0]), "+v"(ea[0][1]), "+v"(ea[1][0]), "+v"(ea[1][1]),
                                    "+v"(eb[0][0][0]), "+v"(eb[0][0][1]), "+v"(eb[0][1][0]), "+v"(eb[0][1][1]));
                 }
+                if constexpr (LSC) wait_sc();
             }
         };
         // whole rounds of the slots, then the last stages; no early exit (see
