@@ -473,8 +473,13 @@ enum WideScale {
     kWConstRow = 6,   // the same with one fp32 scale per row of A and per row of B (output column)
 };
 
-// Load this lane's scale word of each of its 6 rows for stage kt.
-template <int WSC>
+// Load this lane's scale word of each of its rows for stage kt: NA A rows
+// (a 128-row tile uses one) and the 4 B rows.  Only rows the MFMAs read are
+// loaded: the k-loop waits on exact counts of its vector-memory operations,
+// and a load whose result is never used would be dropped by the compiler,
+// leaving one operation fewer in flight than counted (the wait for a stage
+// would then let that stage's last direct load still be landing).
+template <int WSC, int NA = 2>
 __device__ __forceinline__ void wload_scales(uint32_t (&sc)[6], const ScRows &sr, int kt, int nk, int h)
 {
     if constexpr (WSC == kWConst || WSC == kWConstRow) {
@@ -483,8 +488,10 @@ __device__ __forceinline__ void wload_scales(uint32_t (&sc)[6], const ScRows &sr
         return;
     }
     const uint32_t soff = kt >= nk ? kOOB : 0u;
+    if constexpr (NA < 2) sc[1] = 0u;
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
+        if (i == 1 && NA < 2) continue;
         const uint8_t *base = i < 2 ? sr.a : sr.b;
         const uint32_t bytes = i < 2 ? sr.abytes : sr.bbytes;
         uint32_t a;
@@ -715,7 +722,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         constexpr int ASLOT = TBM * WROW, SLOT = ASLOT + WBN * WROW;
         constexpr int TNA = ASLOT / 16 / WTHREADS;          // A loads per thread per stage
         constexpr bool CONST_SC = WSC == kWConst || WSC == kWConstRow;
-        constexpr int NLS = TNA + W_LOADS + (CONST_SC ? 0 : 6);   // vector-memory ops per stage
+        constexpr int NLS = TNA + W_LOADS + (CONST_SC ? 0 : TMI + 4);   // vector-memory ops per stage
         static_assert(NS * SLOT <= MX_RING, "ring fits");
         // a 128-row tile's per-wave offsets take a zero the compiler cannot
         // see through, so they are computed per tile rather than hoisted out
@@ -883,8 +890,10 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
 #pragma unroll
         for (int st = 0; st < NS - 1; ++st) {
             wissue_stage<TNA>(smem, o, st * SLOT, st, nk, Kb, wave, ASLOT);
+            // the scale words' loads (if any) last in the stage's group
+            asm volatile("" ::: "memory");
             if constexpr (LSC) issue_sc(st, st);
-            else wload_scales<WSC>(sc[st], sr, st, nk, h);
+            else wload_scales<WSC, TMI>(sc[st], sr, st, nk, h);
             asm volatile("" ::: "memory");
         }
         wait_vmcnt<(NS - 2) * NLS>();              // stage 0 landed
@@ -938,8 +947,10 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             }
             // stage kt + NS - 1 goes to the slot stage kt - 1 freed at its barrier
             wissue_stage<TNA>(smem, o, PN * SLOT, kt + NS - 1, nk, Kb, wave, ASLOT);
+            // the scale words' loads (if any) last in the stage's group
+            asm volatile("" ::: "memory");
             if constexpr (LSC) issue_sc(kt + NS - 1, PN);
-            else wload_scales<WSC>(sc[PN], sr, kt + NS - 1, nk, h);
+            else wload_scales<WSC, TMI>(sc[PN], sr, kt + NS - 1, nk, h);
             asm volatile("" ::: "memory");
             if constexpr (FMT == 1) {
 #pragma unroll
