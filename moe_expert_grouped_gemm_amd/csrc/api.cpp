@@ -788,29 +788,60 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
         });
     }
     if (dtype == PT_FP8_E4M3) {
-        // one factor per tensor: the codes' values (exact in bf16) go to the
-        // BF16 weight gradient, whose fp32 sums land in the workspace; then
-        // main_grad (+)= d_a * d_dy * sum, one fused multiply-add each
+        // one factor per tensor: both gradients' codes are transposed into
+        // the workspace as for MXFP8 (channel rows, each expert's tokens
+        // padded to whole 32-token blocks, no block scales), the MX kernel
+        // sums exact code products in fp32 (unit block scales), and its
+        // epilogue adds fp32(d_a * d_dy) * sum into main_grad by one fused
+        // multiply-add per element.  Experts are not split along tokens here:
+        // the factor scales each expert's whole sum before main_grad is added.
         if (M == 0) return bf16_wgrad(nullptr, nullptr, main_grad, group_lens, group_offs, G, M, N, K, trans_out,
                                       accumulate, workspace, workspace_bytes, kQueueWsBytes, s);
         if (!a_scale || !dy_scale) return PT_ERR_INVALID_ARG;
         if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad) || !aligned4(a_scale) || !aligned4(dy_scale))
             return PT_ERR_MISALIGNED;
         if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
-        const size_t need =
-            (size_t)(kQueueWsBytes + round256(M * K * 2) + round256(M * N * 2) + round256(G * K * N * 4));
-        if (!workspace || workspace_bytes < need) return PT_ERR_WORKSPACE;
-        uint16_t *wa = (uint16_t *)((uint8_t *)workspace + kQueueWsBytes);
-        uint16_t *wd = (uint16_t *)((uint8_t *)wa + round256(M * K * 2));
-        float *sum = (float *)((uint8_t *)wd + round256(M * N * 2));
-        hipError_t e = launch_fp8_decode((const uint8_t *)a, wa, M * K, s);
-        if (e == hipSuccess) e = launch_fp8_decode((const uint8_t *)dy, wd, M * N, s);
+        const MxWgradWs w = mx_wgrad_ws(G, M, N, K, 0);
+        if (!fits31(K * w.pitch) || !fits31(N * w.pitch)) return PT_ERR_UNSUPPORTED;
+        if (!workspace || !aligned16(workspace) || workspace_bytes < (size_t)w.sa) return PT_ERR_WORKSPACE;
+        uint8_t *base = (uint8_t *)workspace;
+        int *plan = (int *)(base + w.plan);
+        uint8_t *qa = base + w.qa, *qd = base + w.qd;
+        hipError_t e = launch_mx_tokens_transpose((const uint8_t *)a, nullptr, group_lens, group_offs, (int)G, M, K,
+                                                  0, qa, w.pitch, nullptr, plan, s);
+        if (e == hipSuccess)
+            e = launch_mx_tokens_transpose((const uint8_t *)dy, nullptr, group_lens, group_offs, (int)G, M, N, 0, qd,
+                                           w.pitch, nullptr, plan, s);
         if (e != hipSuccess) return PT_ERR_HIP;
-        st = bf16_wgrad(wa, wd, sum, group_lens, group_offs, G, M, N, K, trans_out, 0, workspace, workspace_bytes,
-                        need, s);
-        if (st) return st;
-        return hip_status(launch_fp8_wgrad_axpy(main_grad, sum, group_lens, (const float *)a_scale,
-                                                (const float *)dy_scale, (int)G, K * N, accumulate, s));
+        MxParams p = {};
+        p.a = trans_out ? qd : qa;
+        p.b = trans_out ? qa : qd;
+        p.sfa = (const float *)a_scale;
+        p.sfb = (const float *)dy_scale;
+        p.wrows = (int)(trans_out ? N : K);
+        p.wcols = (int)(trans_out ? K : N);
+        p.pitch = w.pitch;
+        p.plan = plan;
+        p.out = main_grad;
+        p.ldo = p.wcols;
+        p.o_gstride = N * K;
+        p.tilesM = (p.wrows + mx_wide_tile() - 1) / mx_wide_tile();
+        p.tilesN = (p.wcols + mx_wide_tile() - 1) / mx_wide_tile();
+        p.accumulate = accumulate;
+        p.lens = group_lens;
+        p.offs = group_offs;
+        p.err = error_word(workspace, workspace_bytes);
+        p.G = (int)G;
+        p.M = M;
+        p.K = 32;
+        p.N = p.wcols;
+        p.swiglu_limit = __builtin_huge_valf();
+        uint32_t *queues = queue_words(workspace, workspace_bytes);
+        const TuneKey key = tune_key(PT_OP_WGRAD, dtype, kEpiWgrad, trans_out, G, M, N, K);
+        return configured(key, cfg_mask(queues != nullptr, false), false, s, [&](int cfg) {
+            p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+            return queued(p.sched, s, [&] { return launch_mx_wgrad(p, 2, s); });
+        });
     }
     if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
     if (a_scale || dy_scale) return PT_ERR_INVALID_ARG;
@@ -942,16 +973,16 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, i
             return (size_t)(kQueueWsBytes + mx_swz_a_bytes(M, K, fmt) + mx_swz_b_bytes(G, N, K, fmt));
     }
     // the weight gradients: the split reduction's partial slots last; before
-    // them bf16 copies of both operands (MX), and the fp32 sums (FP8 with
-    // tensor factors)
+    // them the experts' plan and both gradients' transposed codes and
+    // stage-major scale words (MX)
     if (op == PT_OP_WGRAD && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) && M >= 0 && N > 0 && K > 0 &&
         G > 0)
         return (size_t)(mx_wgrad_ws(G, M, N, K, dtype == PT_MXFP8_E4M3 ? 0 : 1).total + wgrad_split_bytes(M, K, N));
-    if (op == PT_OP_WGRAD && M > 0 && N > 0 && K > 0 && G > 0) {
-        int64_t bytes = kQueueWsBytes;
-        if (dtype == PT_FP8_E4M3) bytes += round256(M * K * 2) + round256(M * N * 2) + round256(G * K * N * 4);
-        return (size_t)(bytes + wgrad_split_bytes(M, K, N));
-    }
+    // FP8 with tensor factors: the plan and both gradients' transposed codes
+    if (op == PT_OP_WGRAD && dtype == PT_FP8_E4M3 && M > 0 && N > 0 && K > 0 && G > 0)
+        return (size_t)mx_wgrad_ws(G, M, N, K, 0).sa;
+    if (op == PT_OP_WGRAD && M > 0 && N > 0 && K > 0 && G > 0)
+        return (size_t)(kQueueWsBytes + wgrad_split_bytes(M, K, N));
     // the MX data gradient: K outputs per row, a reduction over N
     if ((op == PT_OP_DGRAD || op == PT_OP_DGRAD_SWIGLU) && (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1) &&
         G > 0 && M >= 0 && N > 0 &&

@@ -1070,7 +1070,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             wait_vmcnt<0>();
             barrier();
         }
-        if constexpr (WSC == kWConst) {
+        if constexpr (WSC == kWConst && !WG) {
             // one fp32 factor per tile: the product of the two tensors' scales
             const float f = p.sfa[0] * p.sfb[g];
 #pragma unroll
@@ -1111,6 +1111,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                 og = p.partials + (int64_t)slot * p.o_gstride;
             }
             const bool rmw = p.accumulate && chunk == 0;
+            float fwg = 1.0f;
+            if constexpr (WSC == kWConst) fwg = p.sfa[0] * p.sfb[0];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 if ((wm >> 1) == half) {
@@ -1144,7 +1146,16 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                         const int ci = (rd * NPC + k) * WTHREADS + tid, rr = ci >> 6, c4 = ci & 63;
                         const int i = m0 + 128 * half + rr, n = nt * WBN + 4 * c4;
                         const floatx4 v = *(const floatx4 *)(smem + rr * WG_RP + c4 * 16);
-                        if (keep && i < rows && n < p.wcols) *(floatx4 *)(og + (int64_t)i * p.ldo + n) = mgv[k] + v;
+                        floatx4 r;
+                        if constexpr (WSC == kWConst) {
+                            // FP8 codes with one factor per tensor: the sum times
+                            // fp32(d_a * d_dy), added by one fused multiply-add
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(fwg, v[e], mgv[k][e]);
+                        } else {
+                            r = mgv[k] + v;
+                        }
+                        if (keep && i < rows && n < p.wcols) *(floatx4 *)(og + (int64_t)i * p.ldo + n) = r;
                     }
                 }
                 wait_lgkm0();
@@ -1311,6 +1322,7 @@ hipError_t launch_mx_scale_swizzle(const uint8_t *scales, int64_t rows, int64_t 
 
 hipError_t launch_mx_wgrad(const MxParams &p, int fmt, hipStream_t s)
 {
+    if (fmt == 2) return launch_wide_wgrad<0, kWConst>(p, s);     // E4M3 codes with one factor per tensor
     return fmt == 0 ? launch_wide_wgrad<0, kWE4M3Swz>(p, s) : launch_wide_wgrad<1, kWE2M1Swz>(p, s);
 }
 

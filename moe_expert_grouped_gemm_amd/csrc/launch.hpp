@@ -83,8 +83,10 @@ struct MxParams {
     int ldaux;               // its row stride (elements)
     // kEpiWgrad: a / b are the two gradients' codes transposed to channel
     // rows [wrows / wcols, pitch bytes] (launch_mx_tokens_transpose), sa / sb
-    // their stage-major scale words, plan the experts' block and stage
-    // starts; out is main_grad, fp32 [G][wrows][ldo] at o_gstride elements
+    // their stage-major scale words (FP8 with tensor factors: none; sfa[0]
+    // and sfb[0] are the two gradients' factors), plan the experts' block and
+    // stage starts; out is main_grad, fp32 [G][wrows][ldo] at o_gstride
+    // elements
     const int *plan;
     int64_t pitch;
     int wrows, wcols;
@@ -97,7 +99,8 @@ struct MxParams {
 };
 
 hipError_t launch_mx(const MxParams &p, int fmt, int epi, hipStream_t s);
-// The MX weight gradient (p as for kEpiWgrad) on the 256 x 256 kernel.
+// The MX weight gradient (p as for kEpiWgrad) on the 256 x 256 kernel: fmt
+// 0 MXFP8, 1 MXFP4, 2 E4M3 codes with one factor per tensor.
 hipError_t launch_mx_wgrad(const MxParams &p, int fmt, hipStream_t s);
 
 // Stage-major copy of a row-major E8M0 scale matrix [rows, K/32] for the
@@ -142,13 +145,6 @@ hipError_t launch_fp8_quantize(const uint16_t *x, uint8_t *q, float *amax, float
 // The same with one scale per row of x [rows, cols].
 hipError_t launch_fp8_quantize_rows(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t rows,
                                     int64_t cols, hipStream_t s);
-// FP8 weight gradient with tensor factors: E4M3 codes -> their bf16 values
-// (n % 8 == 0), and main_grad[g] (+)= fa[0] * fd[0] * sum[g] over G slices
-// of P fp32 values (P % 4 == 0; experts with lens <= 0 skipped when
-// accumulating).
-hipError_t launch_fp8_decode(const uint8_t *q, uint16_t *out, int64_t n, hipStream_t s);
-hipError_t launch_fp8_wgrad_axpy(float *main_grad, const float *sum, const int64_t *lens, const float *fa,
-                                 const float *fd, int G, int64_t P, int accumulate, hipStream_t s);
 // MX along tokens within each expert (blocks of 32 rows, the last
 // partial), codes E4M3 [M, C] / E2M1 [M, C/2] (fmt 0 / 1) and scales
 // [M / 32 + G, C].
@@ -161,6 +157,7 @@ hipError_t launch_mx_quantize_tokens(const uint16_t *x, const int64_t *lens, con
 // g: word ((S_g + kt) * C + c) * WPR + w); plan[2g] = bstart_g, plan[2g+1] =
 // S_g.  mx_wgrad_pitch / mx_wgrad_stages bound the row bytes and the stages
 // for any lengths summing to at most M.
+// scales == nullptr (codes without block scales): no scale words.
 int64_t mx_wgrad_pitch(int64_t M, int G, int fmt);
 int64_t mx_wgrad_stages(int64_t M, int G, int fmt);
 hipError_t launch_mx_tokens_transpose(const uint8_t *q, const uint8_t *scales, const int64_t *lens,

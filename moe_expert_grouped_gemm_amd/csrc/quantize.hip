@@ -308,52 +308,6 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(const uint16_t *__re
     }
 }
 
-// FP8 weight gradient with one factor per tensor: the codes' exact values
-// as bf16 (every finite E4M3 value is one), for the BF16 weight-gradient
-// kernel; then main_grad (+)= d_a * d_dy * sum, one fused multiply-add per
-// element, skipping the experts with no rows when accumulating.
-__global__ __launch_bounds__(kThreads) void fp8_decode_kernel(const uint8_t *__restrict__ q,
-                                                              uint16_t *__restrict__ out, int64_t n8)
-{
-    for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < n8; t += (int64_t)gridDim.x * kThreads) {
-        const uintx2 c = *(const uintx2 *)(q + t * 8);
-        uintx4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t w = c[e >> 1] >> (16 * (e & 1));
-            o[e] = bf16_rne(__builtin_amdgcn_cvt_f32_fp8((int)(w & 0xFFu), 0)) |
-                   (bf16_rne(__builtin_amdgcn_cvt_f32_fp8((int)((w >> 8) & 0xFFu), 0)) << 16);
-        }
-        *(uintx4 *)(out + t * 8) = o;
-    }
-}
-
-// grid (chunks, G): expert g's slice of P fp32 values, four per thread
-__global__ __launch_bounds__(kThreads) void fp8_wgrad_axpy_kernel(float *__restrict__ main_grad,
-                                                                  const float *__restrict__ sum,
-                                                                  const int64_t *lens, const float *fa,
-                                                                  const float *fd, int64_t P, int accumulate)
-{
-    const int64_t g = blockIdx.y;
-    if (accumulate && lens[g] <= 0) return;
-    const float alpha = fa[0] * fd[0];
-    float *m = main_grad + g * P;
-    const float *d = sum + g * P;
-    for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < P / 4; t += (int64_t)gridDim.x * kThreads) {
-        const floatx4 v = *(const floatx4 *)(d + t * 4);
-        floatx4 o;
-        if (accumulate) {
-            const floatx4 b = *(const floatx4 *)(m + t * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(alpha, v[e], b[e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = alpha * v[e];
-        }
-        *(floatx4 *)(m + t * 4) = o;
-    }
-}
-
 // ------------------------------------------------------------------ MX along tokens
 // The weight gradient reduces over tokens, so its MX operands are blocked
 // along them: within each expert, blocks of 32 consecutive rows (the last one
@@ -608,9 +562,10 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_transpose_kernel(
                 }
             }
         }
-        // the stage's scale words, one channel per thread
+        // the stage's scale words, one channel per thread (none for codes
+        // without block scales: FP8 with one factor per tensor)
         const int c = tid;
-        if (c < kTrCh && c0 + c < C) {
+        if (scales && c < kTrCh && c0 + c < C) {
             const int64_t b0 = (int64_t)tab.tile0[g] + (int64_t)kt * (TS / 32);
             uint32_t v[2] = {0u, 0u};
 #pragma unroll
@@ -905,29 +860,5 @@ hipError_t launch_mx_quantize_experts(const void *const *ptrs, uint8_t *q, uint8
     return hipGetLastError();
 }
 
-
-hipError_t launch_fp8_decode(const uint8_t *q, uint16_t *out, int64_t n, hipStream_t s)
-{
-    const int64_t n8 = n / 8;
-    if (n8 == 0) return hipSuccess;
-    int64_t grid = (n8 + kThreads - 1) / kThreads;
-    const int64_t cap = (int64_t)device_cus() * 16;
-    if (grid > cap) grid = cap;
-    hipLaunchKernelGGL(fp8_decode_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, q, out, n8);
-    return hipGetLastError();
-}
-
-hipError_t launch_fp8_wgrad_axpy(float *main_grad, const float *sum, const int64_t *lens, const float *fa,
-                                 const float *fd, int G, int64_t P, int accumulate, hipStream_t s)
-{
-    if (G == 0 || P == 0) return hipSuccess;
-    int64_t chunks = (P / 4 + kThreads - 1) / kThreads;
-    int64_t cap = (int64_t)device_cus() * 16 / G;
-    if (cap < 1) cap = 1;
-    if (chunks > cap) chunks = cap;
-    hipLaunchKernelGGL(fp8_wgrad_axpy_kernel, dim3((unsigned)chunks, (unsigned)G), dim3(kThreads), 0, s, main_grad,
-                       sum, lens, fa, fd, P, accumulate);
-    return hipGetLastError();
-}
 
 }  // namespace ptgg

@@ -112,8 +112,11 @@ def test_workspace_sizes_host_only():
             want = (base + r256(8 * g_) + r256(k_ * pitch) + r256(n_ * pitch) + r256(stages * k_ * wpr * 4) +
                     r256(stages * n_ * wpr * 4) + split(m_, n_, k_))
             assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, g_, m_, n_, k_, dt) == want, (dt, g_, m_)
+    # FP8 with one factor per tensor: the plan and both gradients' transposed
+    # codes as for MXFP8 (no scale words, no split)
+    pitch8 = -(-32 * (M // 32 + G) // 128) * 128
     assert (pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, pt.PT_FP8_E4M3) ==
-            base + r256(M * K * 2) + r256(M * N * 2) + r256(G * K * N * 4) + split(M, N, K))
+            base + r256(8 * G) + r256(K * pitch8) + r256(N * pitch8))
     # one output tile per expert and 14030 rows: 512-token chunks, 27 slots
     assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, 7, 14030, 256, 256, pt.PT_BF16) == \
         base + 27 * 256 * 256 * 4
