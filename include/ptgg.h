@@ -316,10 +316,12 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const uint8_t *dy_scale, const 
  *  PT_FP8_E4M3: a [M, K] and dy [M, N] E4M3 codes with one fp32 factor
  *  each (a_scale, dy_scale: pt_fp8_quantize, batch 1);
  *      main_grad[g] = (accumulate ? main_grad[g] : 0) + fp32(d_a * d_dy) * S_g
- *  with S_g the fp32 sum of the exact code products, one fused multiply-add
- *  per element.  The workspace is required: bf16 copies of both operands
- *  and the fp32 sums [G, K, N], pt_grouped_gemm_workspace_size(PT_OP_WGRAD,
- *  ..., PT_FP8_E4M3) bytes.  (Row factors vary along the reduction, so
+ *  with S_g the fp32 sum of the exact code products (the whole expert's:
+ *  no split along tokens), one fused multiply-add per element.  The
+ *  workspace is required: both operands' codes transposed to channel rows
+ *  as for MXFP8 (no scales) and the experts' starts,
+ *  pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ..., PT_FP8_E4M3) bytes,
+ *  else PT_ERR_WORKSPACE.  (Row factors vary along the reduction, so
  *  PT_FP8_E4M3_ROWWISE has no weight gradient: PT_ERR_UNSUPPORTED.)
  *  Requirements: K % 8 == 0, N % 8 == 0; dtype PT_BF16, PT_MXFP8_E4M3,
  *  PT_MXFP4_E2M1 or PT_FP8_E4M3.
@@ -476,10 +478,10 @@ int pt_mx_quantize_experts(const void *const *experts, void *q, uint8_t *scales,
  * Workspace of the grouped GEMMs (optional, for every op; recommended):
  * pt_grouped_gemm_workspace_size() bytes of device memory, 256-byte aligned
  * (4-byte alignment is enough for the error word and tile queues alone).
- *  - the weight gradient's full size adds the split reduction's partial
- *    slots: floor(M / L) fp32 [K, N] matrices (L as at
- *    pt_grouped_gemm_wgrad), after the MX transposed operands or the FP8
- *    operand copies;
+ *  - the BF16 and MX weight gradients' full size adds the split
+ *    reduction's partial slots: floor(M / L) fp32 [K, N] matrices (L as at
+ *    pt_grouped_gemm_wgrad), after the MX transposed operands; the FP8
+ *    weight gradient's holds its transposed codes;
  *  - word 0 receives the sticky device error bits (pt_read_error_flags);
  *    a workspace of at least 4 bytes is enough for that alone;
  *  - a workspace of the full size also holds the tile queues: every call
