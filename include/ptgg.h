@@ -160,7 +160,7 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale,
  * the library (4 KiB, one copy per GPU, held until the process ends), so no
  * size can exceed it.  The call allocates nothing and never times kernel
  * configurations (under PT_CONFIG_TUNE it takes a tuned choice of its
- * class, else configuration 0).  The MX forwards run on row-major scales
+ * class, else the rules' choice).  The MX forwards run on row-major scales
  * (no stage-major scale copies, which need a workspace).  The counters are
  * zeroed on `stream` at every call; the device error bits are not reported.
  * Every call on one GPU shares that array: calls that may overlap on one GPU
@@ -509,7 +509,11 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N,
  * results are bit-identical, only speed differs.
  * pt_set_gemm_config sets the process-wide mode and returns the previous one
  * (-3 for an unknown mode):
- *   PT_CONFIG_RULES  configuration 0 (the default);
+ *   PT_CONFIG_RULES  configuration 0 (the default), or configuration 1 (the
+ *                    static order, one launch fewer) for a problem whose
+ *                    every 256 x 256 tile can start at once: at most one
+ *                    tile per compute unit, counted with M rounded up to a
+ *                    power of two;
  *   PT_CONFIG_TUNE   the first call of each problem class -- (device, op,
  *                    dtype, epilogue, layout, G, N, K, and M rounded up to a
  *                    power of two) -- times every configuration that applies
@@ -520,12 +524,13 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N,
  *                    A call that must not run twice (a weight gradient that
  *                    accumulates) or a stream under graph capture is not
  *                    timed: it uses its class's choice if there is one,
- *                    else configuration 0;
+ *                    else the rules' configuration;
  *   0..3             that configuration for every call.
  * pt_gemm_config_of returns the tuned configuration of a problem class (the
  * arguments of the entry point; op PT_OP_DGRAD_SWIGLU for the SwiGLU
  * backward), or -1 if it has none.  pt_clear_gemm_tuning forgets every
- * tuned class.  The table holds 512 classes; later ones use configuration 0.
+ * tuned class.  The table holds 512 classes; once it is full, a class not
+ * in it is not timed and takes the rules' configuration.
  */
 #define PT_CONFIG_RULES (-1)
 #define PT_CONFIG_TUNE (-2)

@@ -175,6 +175,12 @@ void tune_store(const TuneKey &k, int cfg)
     if (g_ntune < kTuneSlots) g_tune[g_ntune++] = TuneEntry{k, cfg};
 }
 
+bool tune_full()
+{
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return g_ntune >= kTuneSlots;
+}
+
 // The applicable configuration nearest to c (dropping what does not apply).
 int clamp_cfg(int c, unsigned allowed)
 {
@@ -194,6 +200,18 @@ unsigned cfg_mask(bool queues, bool narrow_ok)
     return m;
 }
 
+// The rules' configuration: the queued 256 x 256 kernel, except that a
+// problem whose every tile can start at once (at most one 256 x 256 tile per
+// CU, bounded with M rounded up to a power of two) takes the static order,
+// which saves the queue-reset launch and changes nothing else.
+int rules_cfg(const TuneKey &key, unsigned allowed)
+{
+    const int64_t w = key.op == PT_OP_WGRAD ? ((key.K + 255) / 256) * ((key.N + 255) / 256)
+                                            : (std::max(key.N, key.K) + 255) / 256;
+    const int64_t tiles = key.op == PT_OP_WGRAD ? key.G * w : (key.Mb / 256 + key.G) * w;
+    return (tiles <= device_cus() && ((allowed >> kCfgStatic) & 1u)) ? kCfgStatic : 0;
+}
+
 // Launch through run(cfg) under the current mode.  A call that must not run
 // twice (an accumulating weight gradient) is never timed: it takes a tuned
 // choice if its class has one, else the rules.
@@ -202,12 +220,13 @@ int configured(const TuneKey &key, unsigned allowed, bool repeatable, hipStream_
 {
     const int mode = g_mode.load(std::memory_order_relaxed);
     if (mode >= 0) return hip_status(run(clamp_cfg(mode, allowed)));
-    if (mode == PT_CONFIG_RULES) return hip_status(run(0));
+    if (mode == PT_CONFIG_RULES) return hip_status(run(rules_cfg(key, allowed)));
     const int known = tune_lookup(key);
     if (known >= 0) return hip_status(run(clamp_cfg(known, allowed)));
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (!repeatable || hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
-        return hip_status(run(0));
+    if (!repeatable || tune_full() || hipStreamIsCapturing(s, &cap) != hipSuccess ||
+        cap != hipStreamCaptureStatusNone)
+        return hip_status(run(rules_cfg(key, allowed)));
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess) return PT_ERR_HIP;
     if (hipEventCreate(&e1) != hipSuccess) {
