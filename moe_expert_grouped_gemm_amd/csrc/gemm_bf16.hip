@@ -296,7 +296,8 @@ __global__ __launch_bounds__(kThreads, 2) void gg_bf16_kernel(Bf16Params p)
 
         // Accumulators start at zero, or for an accumulating wgrad at the
         // main_grad tile itself: its loads go out before the operand
-        // prologue and overlap it, and the tile ends with plain stores.
+        // prologue and overlap it, and the tile ends with plain stores (both
+        // non-temporal: main_grad is touched once).
         floatx16 acc[2][4];
         if (KIND == kWgrad && p.accumulate) {
             const float *og = (const float *)p.out + (int64_t)g * p.o_gstride;
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void gg_bf16_kernel(Bf16Params p)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int i = m0 + e_row(wm, bi, r);
-                        acc[bi][bj][r] = (n < p.Nout && i < p.Mout) ? og[(int64_t)i * p.ldo + n] : 0.0f;
+                        acc[bi][bj][r] = (n < p.Nout && i < p.Mout) ? __builtin_nontemporal_load(og + (int64_t)i * p.ldo + n) : 0.0f;
                     }
                 }
         } else {
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 2) void gg_bf16_kernel(Bf16Params p)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int i = m0 + e_row(wm, bi, r);
-                        if (i < p.Mout) og[(int64_t)i * p.ldo + n] = acc[bi][bj][r];
+                        if (i < p.Mout) __builtin_nontemporal_store(acc[bi][bj][r], og + (int64_t)i * p.ldo + n);
                     }
                 }
         } else {
@@ -766,6 +767,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 
         // Accumulators start at zero, or for an accumulating wgrad at the
         // main_grad tile itself (loads overlap the operand prologue).
+        // main_grad is read and written once, with the non-temporal policy,
+        // so its stream leaves L2 first and the operand panels stay.
         floatx16 acc[TMI][NJ];
         if (KIND == kWgrad && p.accumulate && chunk == 0) {
             const float *og = (const float *)p.out + (int64_t)g * p.o_gstride;
@@ -777,7 +780,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int i = m0 + wrow0 + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                        acc[bi][bj][r] = (n < p.Nout && i < p.Mout) ? og[(int64_t)i * p.ldo + n] : 0.0f;
+                        acc[bi][bj][r] = (n < p.Nout && i < p.Mout) ? __builtin_nontemporal_load(og + (int64_t)i * p.ldo + n) : 0.0f;
                     }
                 }
         } else {
@@ -975,7 +978,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int i = m0 + wrow0 + bi * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                        if (i < p.Mout) og[(int64_t)i * p.ldo + n] = acc[bi][bj][r];
+                        if (i < p.Mout) __builtin_nontemporal_store(acc[bi][bj][r], og + (int64_t)i * p.ldo + n);
                     }
                 }
         } else {
@@ -1069,15 +1072,15 @@ __global__ __launch_bounds__(256) void wgrad_split_reduce_kernel(Bf16Params p)
         if (q >= P / 4) continue;
         const int nch = tw.chunks(tab.rows[g]);
         floatx4 *mg = (floatx4 *)((float *)p.out + (int64_t)g * p.o_gstride) + q;
-        floatx4 acc = *mg;
+        floatx4 acc = __builtin_nontemporal_load(mg);
         for (int c = 1; c < nch; ++c) {
             const int slot = slot0[g] + c - 1;
             if (slot >= p.nslots) break;
-            const floatx4 v4 = *((const floatx4 *)(p.partials + (int64_t)slot * p.o_gstride) + q);
+            const floatx4 v4 = __builtin_nontemporal_load((const floatx4 *)(p.partials + (int64_t)slot * p.o_gstride) + q);
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] += v4[e];
         }
-        *mg = acc;
+        __builtin_nontemporal_store(acc, mg);
     }
 }
 

@@ -1098,7 +1098,9 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         if constexpr (WG) {
             // The fp32 tile goes through LDS half a tile (128 rows) at a time,
             // so that main_grad is read, added to and written in whole 16-byte
-            // pieces (a lane's accumulators hold one column of 16 rows).  Chunk
+            // pieces (a lane's accumulators hold one column of 16 rows), with
+            // the non-temporal policy: that stream then leaves L2 before the
+            // operand panels that other tiles still read.  Chunk
             // 0 adds the sum into main_grad (or overwrites it when not
             // accumulating), chunk c >= 1 writes its partial slot (none past the
             // workspace's slots, which only malformed lengths reach).  The ring
@@ -1139,7 +1141,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                         const int ci = (rd * NPC + k) * WTHREADS + tid, rr = ci >> 6, c4 = ci & 63;
                         const int i = m0 + 128 * half + rr, n = nt * WBN + 4 * c4;
                         mgv[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-                        if (rmw && i < rows && n < p.wcols) mgv[k] = *(const floatx4 *)(og + (int64_t)i * p.ldo + n);
+                        if (rmw && i < rows && n < p.wcols) mgv[k] = __builtin_nontemporal_load((const floatx4 *)(og + (int64_t)i * p.ldo + n));
                     }
 #pragma unroll
                     for (int k = 0; k < NPC; ++k) {
@@ -1155,7 +1157,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
                         } else {
                             r = mgv[k] + v;
                         }
-                        if (keep && i < rows && n < p.wcols) *(floatx4 *)(og + (int64_t)i * p.ldo + n) = r;
+                        if (keep && i < rows && n < p.wcols) __builtin_nontemporal_store(r, (floatx4 *)(og + (int64_t)i * p.ldo + n));
                     }
                 }
                 wait_lgkm0();

@@ -302,8 +302,8 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
             if (m0 + r < rows && col < ncols) {
                 const int64_t row = m0 + r;
                 const uintx4 dh = *(const uintx4 *)(smem + r * RS + c * 16);
-                const uintx4 gv = *(const uintx4 *)(x + row * ldaux + col);
-                const uintx4 uv = *(const uintx4 *)(x + row * ldaux + Nout + col);
+                const uintx4 gv = __builtin_nontemporal_load((const uintx4 *)(x + row * ldaux + col));
+                const uintx4 uv = __builtin_nontemporal_load((const uintx4 *)(x + row * ldaux + Nout + col));
                 uintx4 dg, du;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -324,8 +324,8 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
                     dg[e] = pg;
                     du[e] = pu;
                 }
-                *(uintx4 *)(o + row * ldo + col) = dg;
-                *(uintx4 *)(o + row * ldo + Nout + col) = du;
+                __builtin_nontemporal_store(dg, (uintx4 *)(o + row * ldo + col));
+                __builtin_nontemporal_store(du, (uintx4 *)(o + row * ldo + Nout + col));
             }
         }
     } else if (EPI != kEpiSwigluMxfp4) {
@@ -335,7 +335,7 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
             const int r = i / CPR, c = i % CPR;
             const int col = nt * OC + c * 8;
             if (m0 + r < rows && col < ncols)
-                *(uintx4 *)(o + (int64_t)(m0 + r) * ldo + col) = *(const uintx4 *)(smem + r * RS + c * 16);
+                __builtin_nontemporal_store(*(const uintx4 *)(smem + r * RS + c * 16), (uintx4 *)(o + (int64_t)(m0 + r) * ldo + col));
         }
     } else {
         constexpr int BPR = OC / 32;                       // MXFP4 blocks per row
@@ -376,7 +376,7 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
                 w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], 1.0f, 3);
                 packed[q] = w;
             }
-            *(uintx4 *)(o + (int64_t)(m0 + r) * ldo + (j0 >> 1)) = uintx4{packed[0], packed[1], packed[2], packed[3]};
+            __builtin_nontemporal_store(uintx4{packed[0], packed[1], packed[2], packed[3]}, (uintx4 *)(o + (int64_t)(m0 + r) * ldo + (j0 >> 1)));
             os[(int64_t)(m0 + r) * (Nout / 64) + (j0 >> 5)] = (uint8_t)E;
         }
     }
@@ -405,7 +405,7 @@ __device__ __forceinline__ void store_tile_lds_w(const floatx16 (&acc)[MI][NJ], 
                 const int r = i / CPR, c = i % CPR;
                 const int col = nt * OC + c * 8;
                 if (m0 + r < rows && col < ncols)
-                    *(uintx4 *)(o + (int64_t)(m0 + r) * ldsave + col) = *(const uintx4 *)(smem + r * RS + c * 16);
+                    __builtin_nontemporal_store(*(const uintx4 *)(smem + r * RS + c * 16), (uintx4 *)(o + (int64_t)(m0 + r) * ldsave + col));
             }
         }
     }

@@ -29,8 +29,11 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t x)
     return x;
 }
 
-// Quantise 8 consecutive values (one lane's share of a block).
-template <int FMT>
+// Quantise 8 consecutive values (one lane's share of a block).  Codes that
+// consecutive lanes write to whole lines (NT) are stored with the
+// non-temporal policy; the transposing kernels' codes fill half lines, which
+// the default policy merges in L2 before they reach memory.
+template <int FMT, bool NT = true>
 __device__ __forceinline__ void quantise8(const uintx4 v, uint8_t *__restrict__ q, uint8_t *__restrict__ scales,
                                           int64_t t)
 {
@@ -55,13 +58,19 @@ __device__ __forceinline__ void quantise8(const uintx4 v, uint8_t *__restrict__ 
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
         int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
         w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
-        *(uintx2 *)(q + t * 8) = uintx2{(uint32_t)w0, (uint32_t)w1};
+        if constexpr (NT)
+            __builtin_nontemporal_store(uintx2{(uint32_t)w0, (uint32_t)w1}, (uintx2 *)(q + t * 8));
+        else
+            *(uintx2 *)(q + t * 8) = uintx2{(uint32_t)w0, (uint32_t)w1};
     } else {
         uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], 1.0f, 0);
         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], 1.0f, 1);
         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], 1.0f, 2);
         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], 1.0f, 3);
-        *(uint32_t *)(q + t * 4) = w;
+        if constexpr (NT)
+            __builtin_nontemporal_store(w, (uint32_t *)(q + t * 4));
+        else
+            *(uint32_t *)(q + t * 4) = w;
     }
     if ((t & 3) == 0) scales[t >> 2] = (uint8_t)E;
 }
@@ -78,12 +87,12 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const uint16_t *_
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     for (; t + stride < nquads; t += 2 * stride) {
-        const uintx4 v0 = *(const uintx4 *)(x + t * 8);
-        const uintx4 v1 = *(const uintx4 *)(x + (t + stride) * 8);
+        const uintx4 v0 = __builtin_nontemporal_load((const uintx4 *)(x + t * 8));
+        const uintx4 v1 = __builtin_nontemporal_load((const uintx4 *)(x + (t + stride) * 8));
         quantise8<FMT>(v0, q, scales, t);
         quantise8<FMT>(v1, q, scales, t + stride);
     }
-    if (t < nquads) quantise8<FMT>(*(const uintx4 *)(x + t * 8), q, scales, t);
+    if (t < nquads) quantise8<FMT>(__builtin_nontemporal_load((const uintx4 *)(x + t * 8)), q, scales, t);
 }
 
 // Quantisation along the columns (axis 0): blocks of 32 consecutive rows of
@@ -112,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_cols_kernel(const uint16
         uint32_t am[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            h[i] = *(const uintx2 *)(x + (r0 + i) * C + 4 * c);
+            h[i] = __builtin_nontemporal_load((const uintx2 *)(x + (r0 + i) * C + 4 * c));
 #pragma unroll
             for (int k = 0; k < 4; ++k) am[k] = max(am[k], (h[i][k >> 1] >> (16 * (k & 1))) & 0x7FFFu);
         }
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_cols_kernel(const uint16
             for (int i = 0; i < 32; ++i) {
                 int w = __builtin_amdgcn_cvt_pk_fp8_f32(val(i, 0), val(i, 1), 0, false);
                 w = __builtin_amdgcn_cvt_pk_fp8_f32(val(i, 2), val(i, 3), w, true);
-                *(uint32_t *)(q + (r0 + i) * C + 4 * c) = (uint32_t)w;
+                __builtin_nontemporal_store((uint32_t)w, (uint32_t *)(q + (r0 + i) * C + 4 * c));
             }
         } else {
             // byte k of a word: column 4c + k, rows 2i (low nibble) and 2i + 1
@@ -143,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_cols_kernel(const uint16
                 w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(2 * i, 1), val(2 * i + 1, 1), 1.0f, 1);
                 w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(2 * i, 2), val(2 * i + 1, 2), 1.0f, 2);
                 w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, val(2 * i, 3), val(2 * i + 1, 3), 1.0f, 3);
-                *(uint32_t *)(q + (r0 / 2 + i) * C + 4 * c) = w;
+                __builtin_nontemporal_store(w, (uint32_t *)(q + (r0 / 2 + i) * C + 4 * c));
             }
         }
         *(uint32_t *)(scales + blk * C + 4 * c) = Ew;
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_t_kernel(const uint16_t 
         const int k = threadIdx.x + j * kThreads;
         const int row = k >> 3, c8 = (k & 7) * 8;
         uintx4 v = uintx4{0u, 0u, 0u, 0u};
-        if (r0 + row < R && c0 + c8 < C) v = *(const uintx4 *)(xb + (r0 + row) * C + c0 + c8);
+        if (r0 + row < R && c0 + c8 < C) v = __builtin_nontemporal_load((const uintx4 *)(xb + (r0 + row) * C + c0 + c8));
         uint32_t *d = (uint32_t *)(tile + row * TQ_RS + c8 * 2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) d[e] = v[e];
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_t_kernel(const uint16_t 
         }
         // whole quads are in or out together (R % 32 == 0), so the DPP
         // exchange in quantise8 only ever pairs active lanes
-        if (c0 + col < C && r0 + blk * 32 < R) quantise8<FMT>(v, qb, sb, (c0 + col) * RB + (r0 + rr) / 8);
+        if (c0 + col < C && r0 + blk * 32 < R) quantise8<FMT, false>(v, qb, sb, (c0 + col) * RB + (r0 + rr) / 8);
     }
 }
 
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(const uint16_t *__
     const uint16_t *xb = x + b * n8 * 8;
     uint8_t *qb = q + b * n8 * 8;
     for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < n8; t += (int64_t)gridDim.x * kThreads) {
-        const uintx4 v = *(const uintx4 *)(xb + t * 8);
+        const uintx4 v = __builtin_nontemporal_load((const uintx4 *)(xb + t * 8));
         float f[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(const uint16_t *__
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
         int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
         w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
-        *(uintx2 *)(qb + t * 8) = uintx2{(uint32_t)w0, (uint32_t)w1};
+        __builtin_nontemporal_store(uintx2{(uint32_t)w0, (uint32_t)w1}, (uintx2 *)(qb + t * 8));
     }
 }
 
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(const uint16_t *__re
     }
     uint8_t *qr = q + r * cols;
     for (int64_t c = lane * 8; c < cols; c += 512) {
-        const uintx4 v = *(const uintx4 *)(xr + c);
+        const uintx4 v = __builtin_nontemporal_load((const uintx4 *)(xr + c));
         float f[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(const uint16_t *__re
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
         int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
         w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
-        *(uintx2 *)(qr + c) = uintx2{(uint32_t)w0, (uint32_t)w1};
+        __builtin_nontemporal_store(uintx2{(uint32_t)w0, (uint32_t)w1}, (uintx2 *)(qr + c));
     }
 }
 
@@ -349,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_kernel(const uint16_
         uint32_t am[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            h[i] = i < nr ? *(const uintx2 *)(x + (r0 + i) * C + 4 * c) : uintx2{0u, 0u};
+            h[i] = i < nr ? __builtin_nontemporal_load((const uintx2 *)(x + (r0 + i) * C + 4 * c)) : uintx2{0u, 0u};
 #pragma unroll
             for (int k = 0; k < 4; ++k) am[k] = max(am[k], (h[i][k >> 1] >> (16 * (k & 1))) & 0x7FFFu);
         }
@@ -373,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_kernel(const uint16_
                         448.0f);
                 int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
                 w = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w, true);
-                *(uint32_t *)(q + (r0 + i) * C + 4 * c) = (uint32_t)w;
+                __builtin_nontemporal_store((uint32_t)w, (uint32_t *)(q + (r0 + i) * C + 4 * c));
             }
         *(uint32_t *)(scales + (int64_t)b * C + 4 * c) = Ew;
     } else {
@@ -382,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_kernel(const uint16_
         uint32_t a0 = 0, a1 = 0;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            h[i] = i < nr ? *(const uint32_t *)(x + (r0 + i) * C + 2 * c) : 0u;
+            h[i] = i < nr ? __builtin_nontemporal_load((const uint32_t *)(x + (r0 + i) * C + 2 * c)) : 0u;
             a0 = max(a0, h[i] & 0x7FFFu);
             a1 = max(a1, (h[i] >> 16) & 0x7FFFu);
         }
@@ -610,7 +619,7 @@ __device__ __forceinline__ void load_rows(const uint16_t *xb, int64_t R, int64_t
         const int k = threadIdx.x + j * kThreads;
         const int row = k >> 3, c8 = (k & 7) * 8;
         v[j] = uintx4{0u, 0u, 0u, 0u};
-        if (xb && r0 + row < R && c0 + c8 < C) v[j] = *(const uintx4 *)(xb + (r0 + row) * C + c0 + c8);
+        if (xb && r0 + row < R && c0 + c8 < C) v[j] = __builtin_nontemporal_load((const uintx4 *)(xb + (r0 + row) * C + c0 + c8));
     }
 }
 
@@ -639,7 +648,7 @@ __global__ __launch_bounds__(kThreads) void stack_experts_kernel(const void *con
         for (int j = 0; j < 2; ++j) {
             const int k = threadIdx.x + j * kThreads;
             const int row = k >> 3, c8 = (k & 7) * 8;
-            if (r0 + row < R && c0 + c8 < C) *(uintx4 *)(out + (g * R + r0 + row) * C + c0 + c8) = v[j];
+            if (r0 + row < R && c0 + c8 < C) __builtin_nontemporal_store(v[j], (uintx4 *)(out + (g * R + r0 + row) * C + c0 + c8));
         }
         return;
     }
@@ -659,7 +668,7 @@ __global__ __launch_bounds__(kThreads) void stack_experts_kernel(const void *con
                 const uint32_t hi = *(const uint16_t *)(tile + (r8 + 2 * e + 1) * TQ_RS + oc * 2);
                 o[e] = lo | (hi << 16);
             }
-            *(uintx4 *)(out + (g * C + c0 + oc) * R + r0 + r8) = o;
+            __builtin_nontemporal_store(o, (uintx4 *)(out + (g * C + c0 + oc) * R + r0 + r8));
         }
     }
 }
@@ -712,7 +721,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_experts_kernel(const voi
             const uint32_t hi = *(const uint16_t *)(tile + (rr + 2 * e + 1) * TQ_RS + col * 2);
             w[e] = lo | (hi << 16);
         }
-        if (c0 + col < C && r0 + blk * 32 < R) quantise8<FMT>(w, qb, sb, (c0 + col) * RB + (r0 + rr) / 8);
+        if (c0 + col < C && r0 + blk * 32 < R) quantise8<FMT, false>(w, qb, sb, (c0 + col) * RB + (r0 + rr) / 8);
     }
 }
 
