@@ -286,6 +286,25 @@ __device__ __forceinline__ int find_group(const GroupTable &t, int tile)
     return lo;
 }
 
+// Row tile mt and column tile nt of an expert's local tile id (tm row tiles,
+// tn column tiles).  Ids walk the row tiles first inside bands of up to 8 row
+// tiles, then the column tiles, then the next band: a window of consecutive
+// ids (what one XCD runs at a time) then reads a few weight panels and a few
+// activation row blocks, each shared by several tiles in the XCD's L2, where
+// walking all row tiles of a long expert first would stream its whole
+// activation block through L2 once per column tile.  An expert of at most 8
+// row tiles keeps the plain row-first order.
+__device__ __forceinline__ void grouped_tile_order(int local, int tm, int tn, int &mt, int &nt)
+{
+    constexpr int GM = 8;
+    const int band = local / (GM * tn);
+    const int m0 = band * GM;
+    const int h = min(GM, tm - m0);
+    const int rem = local - band * GM * tn;
+    nt = rem / h;
+    mt = m0 + rem % h;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so that
 // consecutive logical ids share an XCD (and its L2): tiles that read the same
 // weight panel then run on the same XCD at the same time.

@@ -680,8 +680,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             }
         } else {
             const int tm = (rows + WBM - 1) / WBM;
-            nt = local / tm;
-            mt = local % tm;
+            grouped_tile_order(local, tm, p.tilesN, mt, nt);
             b_once = tm == 1;
         }
         const int m0 = mt * WBM;

@@ -682,7 +682,8 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         int row0 = __builtin_amdgcn_readfirstlane(tab.row0[g]);
         int rows = __builtin_amdgcn_readfirstlane(tab.rows[g]);
         int tm = (rows + WBM - 1) / WBM;
-        int nt = local / tm, mt = local % tm;
+        int nt, mt;
+        grouped_tile_order(local, tm, p.tilesN, mt, nt);
         // weight gradient: the tile's token chunk of the expert (all of its
         // tokens, padded to whole blocks, without a split) starts at byte pb
         // of every channel row, its scale words at global stage s0
