@@ -490,10 +490,21 @@ __device__ __forceinline__ uint32_t kswz_base(int r32, int h)
     return (uint32_t)((h ^ sw) & 1) * 16u | (uint32_t)((sw & (KCPR - 2)) << 4);
 }
 
-template <int EPI>
+// Both operands reduction-contiguous (4 x 2 wave grid, 64-deep stages): a
+// 256-row tile keeps two 64 KiB slots, one stage in flight while one
+// computes; a tile of at most 128 rows has 16 KiB A slots, so three 48 KiB
+// slots fit and two stages are in flight (such a tile has half the MFMAs per
+// stage, and its loads would otherwise wait).
+template <int KIND, int RING, int WL>
+constexpr bool kc_three_slots() { return KIND == kFwdKContig && RING == 0 && WL == 0; }
+constexpr int KC3_SLOTA = 128 * WRing<0>::ROWBA;              // 16 KiB
+constexpr int KC3_RING = 3 * (KC3_SLOTA + WRing<0>::SLOTB);     // 144 KiB
+
+template <int KIND, int EPI, int RING, int WL>
 constexpr int wide_lds_bytes()
 {
-    return WRING > epi_lds_bytes<EPI, 4>() ? WRING : epi_lds_bytes<EPI, 4>();
+    constexpr int ring = kc_three_slots<KIND, RING, WL>() ? KC3_RING : WRING;
+    return ring > epi_lds_bytes<EPI, 4>() ? ring : epi_lds_bytes<EPI, 4>();
 }
 
 // One operand's loads of a tile: NL per thread per stage, all at one
@@ -603,7 +614,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
     constexpr int WKA = R::WKA, WKB = R::WKB, NSB = R::NSB;
     constexpr int SLOTA = R::SLOTA, SLOTB = R::SLOTB, B_REGION = R::B_REGION;
     constexpr int NLA = R::NLA, NLB = R::NLB;
-    constexpr int LDS_BYTES = wide_lds_bytes<EPI>();
+    constexpr int LDS_BYTES = wide_lds_bytes<KIND, EPI, RING, WL>();
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     GroupTable tab;
     tab.G = p.G;
@@ -700,6 +711,20 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         constexpr int TBM = TMI * 32 * (WL ? 2 : 4);          // rows of this tile height
         constexpr int TNLA = KIND == kWgrad ? NLA : TBM / R::RPLA;
         static_assert(TMI <= MI && TNLA >= 1 && TNLA <= NLA, "tile height");
+        // the ring of this tile height: three slots for a 128-row tile of
+        // the reduction-contiguous kind, else the kind's own
+        constexpr bool R3 = kc_three_slots<KIND, RING, WL>() && TMI == 1;
+        constexpr int NS = R3 ? 3 : NSB;
+        constexpr int SA = R3 ? KC3_SLOTA : SLOTA;           // A slot bytes
+        constexpr int BR = R3 ? 3 * KC3_SLOTA : B_REGION;     // B slots start here
+        static_assert(!R3 || (TNLA == 2 && BR + NS * SLOTB == KC3_RING && KC3_RING <= LDS_BYTES), "three-slot ring");
+        // B fragment bases of the three-slot ring: slots 0 and 1 from one
+        // base, slot 2 from a second 64 KiB on (a read's offset field holds
+        // 16 bits); both derived per tile through a zero the compiler cannot
+        // see through, so they are not kept live through the other paths
+        uint32_t z3 = 0;
+        if constexpr (R3) asm volatile("" : "+v"(z3));
+        const uint32_t bK3 = bK - (uint32_t)(B_REGION - BR) + z3, bK3b = bK3 + 2u * SLOTB;
         const int wrow0 = wm * TMI * 32;
         // reduction-contiguous A: chunk 2j + h of the lane's first row at base ^ (j << 5)
         const uint32_t aK = lds0 + (uint32_t)(wrow0 + r32) * R::ROWBA + kswz_base<R::KCPRA>(r32, h);
@@ -792,14 +817,14 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         }
 
         auto issue_a = [&](int ka, int slot) {
-            wissue<KIND != kWgrad, WKA>(smem + slot * SLOTA, oa, ka, nka, Kred, wave);
+            wissue<KIND != kWgrad, WKA>(smem + slot * SA, oa, ka, nka, Kred, wave);
         };
         auto issue_b = [&](int kb, int slot) {
-            wissue<KIND == kFwdKContig, WKB>(smem + B_REGION + slot * SLOTB, ob, kb, nk, Kred, wave, b_once);
+            wissue<KIND == kFwdKContig, WKB>(smem + BR + slot * SLOTB, ob, kb, nk, Kred, wave, b_once);
         };
         // A fragments of k-step KS of A slot S; B fragments of k-step KS of B slot S
         auto rd_a = [&](auto KSC, auto SC, bf16x8 (&af)[TMI]) {
-            constexpr int KS = decltype(KSC)::value, SO = decltype(SC)::value * SLOTA;
+            constexpr int KS = decltype(KSC)::value, SO = decltype(SC)::value * SA;
             if constexpr (KIND == kWgrad) {
                 constexpr int NO = SO + KS * 16 * 512, NJ = 4 * 512;  // k-step, +4 k-rows
                 af[0] = join(ldsr_tr<NO>(aN[0]), ldsr_tr<NO + NJ>(aN[0]));
@@ -817,11 +842,13 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         auto rd_b = [&](auto KSC, auto SC, bf16x8 (&bf)[NJ]) {
             constexpr int KS = decltype(KSC)::value, SO = decltype(SC)::value * SLOTB;
             if constexpr (KIND == kFwdKContig) {
-                const uint32_t x = bK ^ (uint32_t)(KS << 5);
-                bf[0] = ldsr_b128<SO + 0 * 32 * R::ROWBB>(x);
-                bf[1] = ldsr_b128<SO + 1 * 32 * R::ROWBB>(x);
-                bf[2] = ldsr_b128<SO + 2 * 32 * R::ROWBB>(x);
-                bf[3] = ldsr_b128<SO + 3 * 32 * R::ROWBB>(x);
+                constexpr int SL = decltype(SC)::value;
+                constexpr int SOB = R3 ? (SL == 2 ? 0 : SL * SLOTB) : SO;
+                const uint32_t x = (R3 ? (SL == 2 ? bK3b : bK3) : bK) ^ (uint32_t)(KS << 5);
+                bf[0] = ldsr_b128<SOB + 0 * 32 * R::ROWBB>(x);
+                bf[1] = ldsr_b128<SOB + 1 * 32 * R::ROWBB>(x);
+                bf[2] = ldsr_b128<SOB + 2 * 32 * R::ROWBB>(x);
+                bf[3] = ldsr_b128<SOB + 3 * 32 * R::ROWBB>(x);
             } else {
                 constexpr int NO = SO + KS * 16 * 512, K4 = 4 * 512;
 #pragma unroll
@@ -851,11 +878,11 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
             wait_vmcnt<2 * NLB>();           // A stage 0 and B stage 0
         } else {
 #pragma unroll
-            for (int st = 0; st < NSB - 1; ++st) {
+            for (int st = 0; st < NS - 1; ++st) {
                 issue_a(st, st);
                 issue_b(st, st);
             }
-            wait_vmcnt<(NSB - 2) * (TNLA + NLB)>();
+            wait_vmcnt<(NS - 2) * (TNLA + NLB)>();
         }
         if (tid == 0) s_id[par ^ 1] = tq.resolve(tile);
         wait_lgkm0();
@@ -872,7 +899,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         // last stage the reads fetch unused bytes of the ring (no branch).
         auto stage = [&](auto PC) {
             constexpr int P = decltype(PC)::value;
-            constexpr int Q = (P + 1) % NSB;
+            constexpr int Q = (P + 1) % NS;
             const int kt = kt0 + P;
             if constexpr (RING == 2) {
                 // A stage kt/2 sits in A slot P/2, k-steps 2(P & 1) + 0, 1; on
@@ -897,9 +924,9 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 mma(fa[1], fb[1]);
                 wfrag_wait(fa[0], fb[0]);
             } else {
-                constexpr int PN = (P + NSB - 1) % NSB;
-                issue_a(kt + NSB - 1, PN);       // the slot stage kt-1 freed at its barrier
-                issue_b(kt + NSB - 1, PN);
+                constexpr int PN = (P + NS - 1) % NS;
+                issue_a(kt + NS - 1, PN);        // the slot stage kt-1 freed at its barrier
+                issue_b(kt + NS - 1, PN);
                 auto rd = [&](auto KSC, bf16x8 (&af)[TMI], bf16x8 (&bf)[NJ]) {
                     rd_a(KSC, PC, af);
                     rd_b(KSC, PC, bf);
@@ -922,7 +949,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
                 // stage kt+1 landed for this wave (later stages may still be
                 // in flight), after the barrier for all waves, and every wave
                 // is done reading slot P
-                wait_vmcnt<(NSB - 2) * (TNLA + NLB)>();
+                wait_vmcnt<(NS - 2) * (TNLA + NLB)>();
                 barrier();
                 rd_a(IC<0>{}, IC<Q>{}, fa[0]);
                 rd_b(IC<0>{}, IC<Q>{}, fb[0]);
@@ -933,12 +960,24 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
         };
         // whole rounds of slots, then the last steps: no early exit, so the
         // compiler sees no path between slots that skips a stage's loads
-        if constexpr (NSB == 2) {
+        if constexpr (NS == 2) {
             for (; kt0 + 2 <= nk; kt0 += 2) {
                 stage(IC<0>{});
                 stage(IC<1>{});
             }
             if (kt0 < nk) stage(IC<0>{});
+        } else if constexpr (NS == 3) {
+            for (; kt0 + 3 <= nk; kt0 += 3) {
+                stage(IC<0>{});
+                stage(IC<1>{});
+                stage(IC<2>{});
+            }
+            if (kt0 < nk) stage(IC<0>{});
+            if (kt0 + 1 < nk) stage(IC<1>{});
+            // the loads of the stage past the end (zeros) may still be
+            // landing in the ring, which the epilogue and the next tile reuse
+            wait_vmcnt<0>();
+            barrier();
         } else {
             for (; kt0 + 4 <= nk; kt0 += 4) {
                 stage(IC<0>{});
@@ -1005,7 +1044,7 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
 template <int KIND, int EPI, int RING, int WL>
 hipError_t launch_wide(const Bf16Params &p, hipStream_t s)
 {
-    const int lds = wide_lds_bytes<EPI>() + table_bytes(p.G) + (KIND == kWgrad ? 4 * p.G : 0);
+    const int lds = wide_lds_bytes<KIND, EPI, RING, WL>() + table_bytes(p.G) + (KIND == kWgrad ? 4 * p.G : 0);
     auto kern = gg_bf16_wide_kernel<KIND, EPI, RING, WL>;
     static LdsLimit lds_limit;
     hipError_t e = lds_limit.ensure((const void *)kern, lds);

@@ -694,8 +694,11 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             const int ntl = p.tilesM * p.tilesN;
             chunk = local / ntl;
             const int rest = local - chunk * ntl;
-            mt = rest / p.tilesN;
-            nt = rest % p.tilesN;
+            // channel tiles in bands as in the forward: a window of tiles
+            // shares a few A and dY channel panels (measured on the MXFP8
+            // shape: -2.3%; the BF16 weight gradient, whose experts are a few
+            // hundred tokens, keeps its column-first order: +1.7% in bands)
+            grouped_tile_order(rest, p.tilesM, p.tilesN, mt, nt);
             const int padded = 32 * ((rows + 31) / 32);
             const int c0 = chunk * p.split_len;
             const int clen = p.split_len > 0 ? min(p.split_len, padded - c0) : padded;
