@@ -636,7 +636,13 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_bf16_wide_kernel(Bf16Params p)
     total = __builtin_amdgcn_readfirstlane(total);
     // the scan scratch is free once the table is built: it passes tile ids
     TileQueue tq;
-    tq.init(p.sched, total);
+    // the weight gradient hands out an expert's output tiles (of one token
+    // chunk) as one queue chunk: they all run on one XCD, which then reads
+    // that expert's activations and output gradient from HBM once, where
+    // chunks of 32 tiles spread them over every XCD's L2 (measured -3 to -4%;
+    // the MX weight gradient, whose experts hold thousands of tokens, lost
+    // 3% that way and keeps chunks of 32)
+    tq.init(p.sched, total, KIND == kWgrad ? max(kQueueChunk, p.tilesM * p.tilesN) : kQueueChunk);
     int *s_id = s_scan;
     int par = 0;
 

@@ -430,8 +430,9 @@ __device__ __forceinline__ void store_tile_lds(const floatx16 (&acc)[2][4], uint
 
 // ------------------------------------------------------------------ tile queues
 // Dynamic tile order for the persistent 256 x 256 kernels.  The linear tile
-// ids are cut into chunks of kQueueChunk consecutive ids, and chunk c belongs
-// to queue c % Q (Q = 8 when the grid is a multiple of 8, else 1).
+// ids are cut into chunks of kQueueChunk consecutive ids (or more, as the
+// kernel asks), and chunk c belongs to queue c % Q (Q = 8 when the grid is a
+// multiple of 8, else 1).
 // Workgroup b takes ids from queue b % Q first: workgroups are dispatched
 // round-robin over the 8 XCDs, so that is its own XCD's queue, and the tiles
 // in flight on an XCD form a sliding window of consecutive ids.  The column
@@ -461,11 +462,13 @@ struct TileQueue {
     int home;
     int tried;       // thread 0: queues found empty so far
     uint32_t got;    // thread 0: counter value of the last take
+    int chunk;       // consecutive ids per queue chunk
 
-    __device__ void init(uint32_t *c, int tot)
+    __device__ void init(uint32_t *c, int tot, int ch = kQueueChunk)
     {
         ctr = c;
         total = tot;
+        chunk = ch;
         Q = (gridDim.x % kQueues) == 0 ? kQueues : 1;
         home = (int)blockIdx.x % Q;
         tried = 0;
@@ -475,7 +478,7 @@ struct TileQueue {
     __device__ int id_of(uint32_t i) const
     {
         const int qi = (home + tried) % Q;
-        const int64_t t = ((int64_t)(i / kQueueChunk) * Q + qi) * kQueueChunk + i % kQueueChunk;
+        const int64_t t = ((int64_t)(i / (uint32_t)chunk) * Q + qi) * chunk + i % (uint32_t)chunk;
         return t < total ? (int)t : total;
     }
     // Thread 0: ids from the current queue onwards until one is in range;
