@@ -272,6 +272,30 @@ def bench_cfg0(dev, stream, iters):
                     "warm_ms_median": round(float(np.median(per_warm)), 4)})
 
 
+def bench_ep_share(dev, stream, iters):
+    """One GPU's share under 8-way expert parallelism at the training shape
+    of the headline (4096 tokens per GPU, top-6 over 256 experts): its 32
+    local experts receive 8 * 4096 * 6 / 8 = 24576 rows, 768 per expert on
+    average, so the kernel is MFMA-bound here where the headline streams
+    weights.  The rows are spread over the 32 experts by the headline's
+    imbalanced routing recipe (4096 tokens, top-6 over 32 experts, no
+    masked experts)."""
+    lens = synth.lens_topk_gaussian(4096, 32, 6, seed=7, n_masked=0)
+    G, M, K, N = 32, int(lens.sum()), 4096, 4096
+    a = synth.randn_bf16((M, K), seed=107, std=K ** -0.5, device=dev)
+    b = synth.randn_bf16((G, K, N), seed=108, std=K ** -0.5, device=dev)
+    out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
+    lens_d = torch.as_tensor(lens, device=dev)
+    _, per = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
+        a, None, b, None, out, None, lens_d, None, G, M, N, K, ptm.PT_BF16, 0, ptm.PT_EPI_SWIGLU,
+        workspace=WS[0], stream=stream), iters, 3, stream)
+    flops = 2.0 * M * K * N
+    nbytes = bytes_weights(lens, K * N * 2) + M * K * 2 + M * (N // 2) * 2
+    return summary(f"one GPU's share of 8-way expert parallelism: BF16 FC1 + SwiGLU, 32 experts, M={M}, "
+                   "K=N=4096, [G,K,N] weights", "bf16", flops, nbytes, per,
+                   {"group_lens_min_median_max": [int(lens.min()), int(np.median(lens)), int(lens.max())]})
+
+
 def bench_cfg2(dev, stream, iters, fc1):
     lens, G, M, K, N, a, b = fc1["lens"], fc1["G"], fc1["M"], fc1["K"], fc1["N"], fc1["a"], fc1["b"]
     lens_d = fc1["lens_d"]
@@ -777,6 +801,10 @@ def main():
         for k in ("a", "b", "out"):
             fc1.pop(k)
         torch.cuda.empty_cache()
+        if want is None or "ep" in want:
+            log("per_config: one GPU's share of expert parallelism")
+            per["ep8_share_bf16_fc1_swiglu"] = bench_ep_share(dev, stream, iters)
+            torch.cuda.empty_cache()
         if want is None or "cfg3" in want:
             log("per_config: MXFP8")
             per["cfg3_mxfp8_fwd"], per["cfg3_mxfp8_quantize_A"] = bench_cfg3(dev, stream, iters)
