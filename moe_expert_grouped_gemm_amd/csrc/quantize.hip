@@ -161,55 +161,83 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_cols_kernel(const uint16
 
 // Transposing quantiser: x_b [R, C] bf16 (row-major) -> q_b = the MX
 // quantisation of x_b^T, [C, R] codes with blocks of 32 consecutive rows of
-// x_b, and scales [C, R/32].  A workgroup moves a 64 x 64 tile through LDS:
-// 16-byte row loads in, then each quad of lanes takes one column and 32
-// rows (8 per lane, read down the column), and quantise8 encodes and stores
-// them as one block of the transposed output.  R % 32 == 0, C % 8 == 0.
-constexpr int TQ = 64;                 // tile rows and columns
+// x_b, and scales [C, R/32].  A workgroup moves a 128 x 128 tile through LDS
+// (16-byte row loads), then 16 lanes take one column's 128 rows (8 per
+// lane, read down the column, four 32-row blocks of four lanes each), and
+// quantise8 encodes them: the column's codes are one 128-byte run of the
+// transposed output (E4M3), written by one store of those 16 lanes.  With
+// 64 x 64 tiles two workgroups wrote the halves of each run.
+// R % 32 == 0, C % 8 == 0.
+constexpr int TQ = 64;                 // the weight stack's tile rows and columns
 constexpr int TQ_RS = TQ * 2 + 4;      // LDS row stride (bytes), padded off the bank period
+constexpr int TB = 128;                // the transposing quantisers' tile rows and columns
+constexpr int TB_RS = TB * 2 + 4;
+
+// This thread's eight 16-byte row chunks of a 128 x 128 tile (zeros outside
+// x_b): chunk k = threadIdx.x + j * kThreads is row k / 16, columns
+// 8 (k % 16) .. + 7, so a lane quad holds 32 consecutive columns of a row.
+__device__ __forceinline__ void load_rows_tb(const uint16_t *xb, int64_t R, int64_t C, int64_t r0, int64_t c0,
+                                             uintx4 (&v)[8])
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int k = threadIdx.x + j * kThreads;
+        const int row = k >> 4, c8 = (k & 15) * 8;
+        v[j] = uintx4{0u, 0u, 0u, 0u};
+        if (xb && r0 + row < R && c0 + c8 < C)
+            v[j] = __builtin_nontemporal_load((const uintx4 *)(xb + (r0 + row) * C + c0 + c8));
+    }
+}
+
+__device__ __forceinline__ void rows_to_lds_tb(const uintx4 (&v)[8], uint8_t *tile)
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int k = threadIdx.x + j * kThreads;
+        uint32_t *d = (uint32_t *)(tile + (k >> 4) * TB_RS + (k & 15) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = v[j][e];
+    }
+}
+
+// The transposed codes of a 128 x 128 LDS tile at rows r0, columns c0 of
+// x_b: pass p, lane t of the workgroup takes column 16 p + t / 16 and rows
+// 8 (t % 16) .. + 7.  Whole lane quads (one 32-row block) are in or out
+// together (R % 32 == 0), so the DPP exchange in quantise8 only ever pairs
+// active lanes.
+template <int FMT>
+__device__ __forceinline__ void quantise_t_tile(const uint8_t *tile, uint8_t *qb, uint8_t *sb, int64_t R, int64_t C,
+                                                int64_t r0, int64_t c0)
+{
+    const int64_t RB = R / 8;          // 8-value groups per output row
+#pragma unroll 2
+    for (int p = 0; p < TB * 16 / kThreads; ++p) {
+        const int t = threadIdx.x + p * kThreads;
+        const int col = t >> 4, rr = (t & 15) * 8;
+        uintx4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = *(const uint16_t *)(tile + (rr + 2 * e) * TB_RS + col * 2);
+            const uint32_t hi = *(const uint16_t *)(tile + (rr + 2 * e + 1) * TB_RS + col * 2);
+            w[e] = lo | (hi << 16);
+        }
+        if (c0 + col < C && r0 + (rr & ~31) < R) quantise8<FMT, false>(w, qb, sb, (c0 + col) * RB + (r0 + rr) / 8);
+    }
+}
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void mx_quantize_t_kernel(const uint16_t *__restrict__ x,
                                                                  uint8_t *__restrict__ q,
                                                                  uint8_t *__restrict__ scales, int64_t R, int64_t C)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[TQ * TQ_RS];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[TB * TB_RS];
     const int64_t b = blockIdx.z;
-    const int64_t r0 = (int64_t)blockIdx.y * TQ, c0 = (int64_t)blockIdx.x * TQ;
-    const uint16_t *xb = x + b * R * C;
-    // 64 rows x 8 chunks of 8 columns: two 16-byte loads per thread
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int k = threadIdx.x + j * kThreads;
-        const int row = k >> 3, c8 = (k & 7) * 8;
-        uintx4 v = uintx4{0u, 0u, 0u, 0u};
-        if (r0 + row < R && c0 + c8 < C) v = __builtin_nontemporal_load((const uintx4 *)(xb + (r0 + row) * C + c0 + c8));
-        uint32_t *d = (uint32_t *)(tile + row * TQ_RS + c8 * 2);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = v[e];
-    }
+    const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
+    uintx4 v[8];
+    load_rows_tb(x + b * R * C, R, C, r0, c0, v);
+    rows_to_lds_tb(v, tile);
     __syncthreads();
-    const int64_t RB = R / 8;          // 8-value groups per output row
-    uint8_t *qb = q + b * C * (FMT == 0 ? R : R / 2);
-    uint8_t *sb = scales + b * C * (R / 32);
-    // quads: 64 columns x 2 blocks of 32 rows; lane qq of a quad takes rows 8qq..8qq+7
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int t = threadIdx.x + j * kThreads;
-        const int quad = t >> 2, qq = t & 3;
-        const int col = quad & (TQ - 1), blk = quad >> 6;
-        const int rr = blk * 32 + qq * 8;
-        uintx4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = *(const uint16_t *)(tile + (rr + 2 * e) * TQ_RS + col * 2);
-            const uint32_t hi = *(const uint16_t *)(tile + (rr + 2 * e + 1) * TQ_RS + col * 2);
-            v[e] = lo | (hi << 16);
-        }
-        // whole quads are in or out together (R % 32 == 0), so the DPP
-        // exchange in quantise8 only ever pairs active lanes
-        if (c0 + col < C && r0 + blk * 32 < R) quantise8<FMT, false>(v, qb, sb, (c0 + col) * RB + (r0 + rr) / 8);
-    }
+    quantise_t_tile<FMT>(tile, q + b * C * (FMT == 0 ? R : R / 2), scales + b * C * (R / 32), R, C, r0, c0);
 }
 
 // ------------------------------------------------------------------ FP8, one scale per tensor
@@ -673,11 +701,12 @@ __global__ __launch_bounds__(kThreads) void stack_experts_kernel(const void *con
     }
 }
 
-// Both MX caches of the expert weights from one read: q/scales quantise W_g
-// along C (each lane quad holds 32 consecutive columns of one row in
-// registers: C % 32 == 0), qt/scales_t quantise W_g^T along R through the
-// LDS tile as mx_quantize_t_kernel does (R % 32 == 0).  Either pair may be
-// absent; the choice is uniform over the grid.
+// Both MX caches of the expert weights from one read of 128 x 128 tiles:
+// q/scales quantise W_g along C (each lane quad holds 32 consecutive columns
+// of one row in registers, C % 32 == 0; 16 lanes write a row's 128 code
+// bytes), qt/scales_t quantise W_g^T along R through the LDS tile as
+// mx_quantize_t_kernel does (R % 32 == 0).  Either pair may be absent; the
+// choice is uniform over the grid.
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void mx_quantize_experts_kernel(const void *const *ptrs,
                                                                        uint8_t *__restrict__ q,
@@ -686,43 +715,26 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_experts_kernel(const voi
                                                                        uint8_t *__restrict__ scales_t, int64_t R,
                                                                        int64_t C, uint32_t *err)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[TQ * TQ_RS];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[TB * TB_RS];
     const int64_t g = blockIdx.z;
-    const int64_t r0 = (int64_t)blockIdx.y * TQ, c0 = (int64_t)blockIdx.x * TQ;
-    uintx4 v[2];
-    load_rows(expert_ptr(ptrs, err), R, C, r0, c0, v);
-    if (qt) rows_to_lds(v, tile);
+    const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
+    uintx4 v[8];
+    load_rows_tb(expert_ptr(ptrs, err), R, C, r0, c0, v);
+    if (qt) rows_to_lds_tb(v, tile);
     if (q) {
         uint8_t *qb = q + g * R * (FMT == 0 ? C : C / 2);
         uint8_t *sb = scales + g * R * (C / 32);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 8; ++j) {
             const int k = threadIdx.x + j * kThreads;
-            const int row = k >> 3, c8 = (k & 7) * 8;
+            const int row = k >> 4, c8 = (k & 15) * 8;
             // a quad's 32 columns are in or out together (C % 32 == 0)
             if (r0 + row < R && c0 + c8 < C) quantise8<FMT>(v[j], qb, sb, ((r0 + row) * C + c0 + c8) / 8);
         }
     }
     if (!qt) return;
     __syncthreads();
-    const int64_t RB = R / 8;
-    uint8_t *qb = qt + g * C * (FMT == 0 ? R : R / 2);
-    uint8_t *sb = scales_t + g * C * (R / 32);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int t = threadIdx.x + j * kThreads;
-        const int quad = t >> 2, qq = t & 3;
-        const int col = quad & (TQ - 1), blk = quad >> 6;
-        const int rr = blk * 32 + qq * 8;
-        uintx4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = *(const uint16_t *)(tile + (rr + 2 * e) * TQ_RS + col * 2);
-            const uint32_t hi = *(const uint16_t *)(tile + (rr + 2 * e + 1) * TQ_RS + col * 2);
-            w[e] = lo | (hi << 16);
-        }
-        if (c0 + col < C && r0 + blk * 32 < R) quantise8<FMT, false>(w, qb, sb, (c0 + col) * RB + (r0 + rr) / 8);
-    }
+    quantise_t_tile<FMT>(tile, qt + g * C * (FMT == 0 ? R : R / 2), scales_t + g * C * (R / 32), R, C, r0, c0);
 }
 
 }  // namespace
@@ -760,7 +772,7 @@ hipError_t launch_quantize_t(const uint16_t *x, uint8_t *q, uint8_t *scales, int
                              int64_t cols, int fmt, hipStream_t s)
 {
     if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
-    const dim3 grid((unsigned)((cols + TQ - 1) / TQ), (unsigned)((rows + TQ - 1) / TQ), (unsigned)batch);
+    const dim3 grid((unsigned)((cols + TB - 1) / TB), (unsigned)((rows + TB - 1) / TB), (unsigned)batch);
     if (fmt == 0)
         hipLaunchKernelGGL(mx_quantize_t_kernel<0>, grid, dim3(kThreads), 0, s, x, q, scales, rows, cols);
     else
@@ -859,7 +871,7 @@ hipError_t launch_mx_quantize_experts(const void *const *ptrs, uint8_t *q, uint8
                                       hipStream_t s)
 {
     if (G == 0 || R == 0 || C == 0) return hipSuccess;
-    const dim3 grid((unsigned)((C + TQ - 1) / TQ), (unsigned)((R + TQ - 1) / TQ), (unsigned)G);
+    const dim3 grid((unsigned)((C + TB - 1) / TB), (unsigned)((R + TB - 1) / TB), (unsigned)G);
     if (fmt == 0)
         hipLaunchKernelGGL(mx_quantize_experts_kernel<0>, grid, dim3(kThreads), 0, s, ptrs, q, scales, qt, scales_t,
                            R, C, err);
