@@ -168,10 +168,8 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_cols_kernel(const uint16
 // transposed output (E4M3), written by one store of those 16 lanes.  With
 // 64 x 64 tiles two workgroups wrote the halves of each run.
 // R % 32 == 0, C % 8 == 0.
-constexpr int TQ = 64;                 // the weight stack's tile rows and columns
-constexpr int TQ_RS = TQ * 2 + 4;      // LDS row stride (bytes), padded off the bank period
-constexpr int TB = 128;                // the transposing quantisers' tile rows and columns
-constexpr int TB_RS = TB * 2 + 4;
+constexpr int TB = 128;                // tile rows and columns
+constexpr int TB_RS = TB * 2 + 4;      // LDS row stride (bytes), padded off the bank period
 
 // This thread's eight 16-byte row chunks of a 128 x 128 tile (zeros outside
 // x_b): chunk k = threadIdx.x + j * kThreads is row k / 16, columns
@@ -626,7 +624,8 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_transpose_kernel(
 // stacked operand of the grouped GEMMs -- [G, R, C], or the per-expert
 // transpose [G, C, R] -- or directly its MX caches, where a stack followed
 // by a transposing copy would move every byte twice.  Each workgroup owns a
-// 64 x 64 tile of one expert (grid: column tiles, row tiles, experts).  A
+// 128 x 128 tile of one expert (grid: column tiles, row tiles, experts),
+// eight 16-byte loads per thread (`load_rows_tb`).  A
 // NULL or misaligned address reads as a zero matrix and sets an error bit.
 
 __device__ __forceinline__ const uint16_t *expert_ptr(const void *const *ptrs, uint32_t *err)
@@ -637,63 +636,40 @@ __device__ __forceinline__ const uint16_t *expert_ptr(const void *const *ptrs, u
     return ok ? p : nullptr;
 }
 
-// This thread's two 16-byte row chunks of the tile (zeros outside W_g): 64
-// rows x 8 chunks of 8 columns, eight lanes per row.
-__device__ __forceinline__ void load_rows(const uint16_t *xb, int64_t R, int64_t C, int64_t r0, int64_t c0,
-                                          uintx4 (&v)[2])
-{
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int k = threadIdx.x + j * kThreads;
-        const int row = k >> 3, c8 = (k & 7) * 8;
-        v[j] = uintx4{0u, 0u, 0u, 0u};
-        if (xb && r0 + row < R && c0 + c8 < C) v[j] = __builtin_nontemporal_load((const uintx4 *)(xb + (r0 + row) * C + c0 + c8));
-    }
-}
-
-__device__ __forceinline__ void rows_to_lds(const uintx4 (&v)[2], uint8_t *tile)
-{
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int k = threadIdx.x + j * kThreads;
-        uint32_t *d = (uint32_t *)(tile + (k >> 3) * TQ_RS + (k & 7) * 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = v[j][e];
-    }
-}
-
 template <int TRANS>
 __global__ __launch_bounds__(kThreads) void stack_experts_kernel(const void *const *ptrs, uint16_t *__restrict__ out,
                                                                  int64_t R, int64_t C, uint32_t *err)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[TRANS ? TQ * TQ_RS : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[TRANS ? TB * TB_RS : 16];
     const int64_t g = blockIdx.z;
-    const int64_t r0 = (int64_t)blockIdx.y * TQ, c0 = (int64_t)blockIdx.x * TQ;
-    uintx4 v[2];
-    load_rows(expert_ptr(ptrs, err), R, C, r0, c0, v);
+    const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
+    uintx4 v[8];
+    load_rows_tb(expert_ptr(ptrs, err), R, C, r0, c0, v);
     if (!TRANS) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 8; ++j) {
             const int k = threadIdx.x + j * kThreads;
-            const int row = k >> 3, c8 = (k & 7) * 8;
-            if (r0 + row < R && c0 + c8 < C) __builtin_nontemporal_store(v[j], (uintx4 *)(out + (g * R + r0 + row) * C + c0 + c8));
+            const int row = k >> 4, c8 = (k & 15) * 8;
+            if (r0 + row < R && c0 + c8 < C)
+                __builtin_nontemporal_store(v[j], (uintx4 *)(out + (g * R + r0 + row) * C + c0 + c8));
         }
         return;
     }
-    rows_to_lds(v, tile);
+    rows_to_lds_tb(v, tile);
     __syncthreads();
-    // the tile's 64 columns become 64 output rows of 8 chunks of 8 values,
-    // each chunk read down a column of the LDS tile
+    // the tile's 128 columns become 128 output rows of 16 chunks of 8
+    // values, each chunk read down a column of the LDS tile; the 16 lanes of
+    // an output row write its 256 contiguous bytes
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 8; ++j) {
         const int k = threadIdx.x + j * kThreads;
-        const int oc = k >> 3, r8 = (k & 7) * 8;
+        const int oc = k >> 4, r8 = (k & 15) * 8;
         if (c0 + oc < C && r0 + r8 < R) {
             uintx4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = *(const uint16_t *)(tile + (r8 + 2 * e) * TQ_RS + oc * 2);
-                const uint32_t hi = *(const uint16_t *)(tile + (r8 + 2 * e + 1) * TQ_RS + oc * 2);
+                const uint32_t lo = *(const uint16_t *)(tile + (r8 + 2 * e) * TB_RS + oc * 2);
+                const uint32_t hi = *(const uint16_t *)(tile + (r8 + 2 * e + 1) * TB_RS + oc * 2);
                 o[e] = lo | (hi << 16);
             }
             __builtin_nontemporal_store(o, (uintx4 *)(out + (g * C + c0 + oc) * R + r0 + r8));
@@ -858,7 +834,7 @@ hipError_t launch_stack_experts(const void *const *ptrs, uint16_t *out, int G, i
                                 uint32_t *err, hipStream_t s)
 {
     if (G == 0 || R == 0 || C == 0) return hipSuccess;
-    const dim3 grid((unsigned)((C + TQ - 1) / TQ), (unsigned)((R + TQ - 1) / TQ), (unsigned)G);
+    const dim3 grid((unsigned)((C + TB - 1) / TB), (unsigned)((R + TB - 1) / TB), (unsigned)G);
     if (trans)
         hipLaunchKernelGGL(stack_experts_kernel<1>, grid, dim3(kThreads), 0, s, ptrs, out, R, C, err);
     else
