@@ -18,7 +18,7 @@ NAN16 = 0x7FC1       # bf16 NaN pattern the kernels never write
 
 CASES = [
     # (name, lens, K, N)
-    ("tiny_cfg0", None, 128, 256),
+    ("tiny_4_experts", None, 128, 256),
     ("ragged", [0, 1, 130, 0, 257, 64, 33], 200, 208),
     ("one_expert", [300], 64, 144),
     ("many_small", [3, 0, 0, 5, 1, 2, 0, 7, 129, 4, 0, 1], 96, 80),
