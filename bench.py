@@ -630,13 +630,19 @@ def bench_cfg3_wgrad(dev, stream, iters):
     _, per = time_launches(step, iters, 3, stream)
     _, per_q = time_launches(quant, iters, 3, stream)
     _, per_g = time_launches(gemm, iters, 3, stream)
+    # the same from the bf16 gradients in one call: quantisation along tokens
+    # fused into the transpose to the weight gradient's operand layout
+    _, per_f = time_launches(lambda: ptm.pt_grouped_gemm_wgrad_quantize(
+        a, dy, mg, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, 0, 1, workspace=ws, stream=stream),
+        iters, 3, stream)
     flops = 2.0 * M * K * N
     codes = M * K + M * N + (M // 32 + G) * (K + N)
     nbytes = M * K * 2 + M * N * 2 + 2 * codes + bytes_weights(lens, K * N * 4 * 2)
     w = summary("MXFP8 wgrad (A and dY quantised along tokens + weight gradient into fp32 main_grad), "
                 "32 experts, M=65536, K=2880, N=5760", "mxfp8", flops, nbytes, per,
                 {"quantize_tokens_ms_median": round(float(np.median(per_q)), 4),
-                 "wgrad_only_ms_median": round(float(np.median(per_g)), 4)})
+                 "wgrad_only_ms_median": round(float(np.median(per_g)), 4),
+                 "fused_quantize_wgrad_ms_median": round(float(np.median(per_f)), 4)})
     del as_, ds, ws
     torch.cuda.empty_cache()
     # FP8 with one factor per tensor: two-pass quantise of A and dY, then the

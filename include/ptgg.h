@@ -335,6 +335,31 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The MX weight gradient from the bf16 gradients themselves (Primus-Turbo
+ * README, "What's New": MXFP8 grouped MLP backward; PR page "[Megatron-LM]
+ * feat: add grouped gemm fp4 support, ...", "Changes": the gradient added
+ * into weight.main_grad).  a [M, K] and dy [M, N] are bf16, rows grouped by
+ * expert as for pt_grouped_gemm_wgrad; dtype PT_MXFP8_E4M3 or
+ * PT_MXFP4_E2M1.  Both are quantised along tokens within each expert
+ * (blocks of 32 rows, the rule of pt_mx_quantize_tokens) straight into the
+ * workspace's transposed operand layout, then the MX weight gradient runs:
+ * main_grad comes out bit-identical to pt_mx_quantize_tokens on a and on dy
+ * followed by pt_grouped_gemm_wgrad with that dtype and workspace, but the
+ * [M, K] and [M, N] codes are neither written nor read back.  Same
+ * arguments, layouts (trans_out), accumulate rule, split reduction and
+ * errors as pt_grouped_gemm_wgrad; the workspace is required,
+ * pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ..., dtype) bytes, else
+ * PT_ERR_WORKSPACE.  a, dy and main_grad 16-byte aligned (else
+ * PT_ERR_MISALIGNED).  Requirements: K % 8 == 0, N % 8 == 0; another dtype
+ * returns PT_ERR_UNSUPPORTED.
+ */
+int pt_grouped_gemm_wgrad_quantize(const void *a, const void *dy, float *main_grad,
+                                   const int64_t *group_lens, const int64_t *group_offs,
+                                   int64_t G, int64_t M, int64_t N, int64_t K,
+                                   int dtype, int trans_out, int accumulate,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * OCP-MX quantisation of a bf16 matrix x [rows, cols], one block per 32
  * consecutive elements along one axis:
  *   E = clamp(floor(log2(max|v|)) - emax + 127, 0, 254)   (E = 0 for an

@@ -23,8 +23,8 @@ __all__ = [
     "PT_OP_FWD", "PT_OP_DGRAD", "PT_OP_WGRAD",
     "load", "lib_path", "PtggError",
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu",
-    "pt_grouped_gemm_wgrad", "pt_grouped_gemm_fwd_swiglu_save", "pt_grouped_gemm_fwd_noalloc",
-    "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
+    "pt_grouped_gemm_wgrad", "pt_grouped_gemm_wgrad_quantize", "pt_grouped_gemm_fwd_swiglu_save",
+    "pt_grouped_gemm_fwd_noalloc", "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts", "expert_addresses",
     "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning", "PT_CONFIG_RULES", "PT_CONFIG_TUNE",
     "PT_OP_DGRAD_SWIGLU", "PT_MAX_GROUPS",
@@ -39,7 +39,7 @@ PT_MAX_GROUPS = 1024
 
 EXPORTS = (
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",
-    "pt_grouped_gemm_fwd_swiglu_save", "pt_grouped_gemm_fwd_noalloc",
+    "pt_grouped_gemm_wgrad_quantize", "pt_grouped_gemm_fwd_swiglu_save", "pt_grouped_gemm_fwd_noalloc",
     "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts",
     "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning",
@@ -80,6 +80,8 @@ def load(require_gpu: bool = True):
     L.pt_grouped_gemm_dgrad_swiglu.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, f32, p, sz, p]
     L.pt_grouped_gemm_wgrad.restype = i32
     L.pt_grouped_gemm_wgrad.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
+    L.pt_grouped_gemm_wgrad_quantize.restype = i32
+    L.pt_grouped_gemm_wgrad_quantize.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
     L.pt_mx_quantize.restype = i32
     L.pt_mx_quantize.argtypes = [p, p, p, i64, i64, i32, i32, p]
     L.pt_mx_quantize_t.restype = i32
@@ -195,6 +197,14 @@ def pt_grouped_gemm_wgrad(a, a_scale, dy, dy_scale, main_grad, group_lens, group
         _ptr(a), _ptr(a_scale), _ptr(dy), _ptr(dy_scale), _ptr(main_grad),
         _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_out, accumulate,
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def pt_grouped_gemm_wgrad_quantize(a, dy, main_grad, group_lens, group_offs, G, M, N, K, dtype, trans_out,
+                                   accumulate, workspace=None, stream=None):
+    L = load()
+    _check("pt_grouped_gemm_wgrad_quantize", L.pt_grouped_gemm_wgrad_quantize(
+        _ptr(a), _ptr(dy), _ptr(main_grad), _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, trans_out,
+        accumulate, _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def pt_mx_quantize(x, q, scales, rows, cols, dtype, axis=1, stream=None):

@@ -712,6 +712,74 @@ static int bf16_wgrad(const void *a, const void *dy, float *main_grad, const int
 }
 
 
+// The MX weight gradient on operands already in the workspace (channel rows
+// and stage-major scale words of both gradients, and the experts' plan):
+// the 256 x 256 MX kernel reduces over each expert's tokens with the block
+// scales applied in the matrix cores, optionally split along tokens.
+static int mx_wgrad_gemm(const MxWgradWs &w, uint8_t *base, int dtype, float *main_grad, const int64_t *group_lens,
+                         const int64_t *group_offs, int64_t G, int64_t M, int64_t N, int64_t K, int trans_out,
+                         int accumulate, void *workspace, size_t workspace_bytes, hipStream_t s)
+{
+    const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
+    int *plan = (int *)(base + w.plan);
+    uint8_t *qa = base + w.qa, *qd = base + w.qd;
+    uint32_t *sa = (uint32_t *)(base + w.sa), *sd = (uint32_t *)(base + w.sd);
+    // trans_out = 0: rows are A's channels (K), columns dY's (N); 1: swapped
+    MxParams p = {};
+    p.a = trans_out ? qd : qa;
+    p.sa = trans_out ? sd : sa;
+    p.b = trans_out ? qa : qd;
+    p.sb = trans_out ? sa : sd;
+    p.wrows = (int)(trans_out ? N : K);
+    p.wcols = (int)(trans_out ? K : N);
+    p.pitch = w.pitch;
+    p.plan = plan;
+    p.out = main_grad;
+    p.ldo = p.wcols;
+    p.o_gstride = N * K;
+    p.tilesM = (p.wrows + mx_wide_tile() - 1) / mx_wide_tile();
+    p.tilesN = (p.wcols + mx_wide_tile() - 1) / mx_wide_tile();
+    p.accumulate = accumulate;
+    p.lens = group_lens;
+    p.offs = group_offs;
+    p.err = error_word(workspace, workspace_bytes);
+    p.G = (int)G;
+    p.M = M;
+    p.K = 32;
+    p.N = p.wcols;
+    p.swiglu_limit = __builtin_huge_valf();
+    uint32_t *queues = queue_words(workspace, workspace_bytes);
+    // the split reduction, when the workspace holds its partial slots: the
+    // chunk length of the BF16 rule rounded up to whole 256-token stages
+    const int64_t split_len = (wgrad_split_len(M, p.wrows, p.wcols) + 255) / 256 * 256;
+    const int64_t nslots = M / split_len;
+    Bf16Params rp = {};
+    if (queues && nslots > 0 && workspace_bytes >= (size_t)(w.total + wgrad_split_bytes(M, K, N))) {
+        p.split_len = (int)split_len;
+        p.nslots = (int)nslots;
+        p.partials = (float *)(base + w.total);
+        rp.lens = group_lens;
+        rp.offs = group_offs;
+        rp.G = (int)G;
+        rp.M = M;
+        rp.split_len = p.split_len;
+        rp.nslots = p.nslots;
+        rp.partials = p.partials;
+        rp.out = main_grad;
+        rp.o_gstride = N * K;
+        rp.Mout = p.wrows;
+        rp.Nout = p.wcols;
+        rp.accumulate = accumulate;
+    }
+    const TuneKey key = tune_key(PT_OP_WGRAD, dtype, kEpiWgrad, trans_out, G, M, N, K);
+    return configured(key, cfg_mask(queues != nullptr, false), false, s, [&](int cfg) {
+        p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+        hipError_t e2 = queued(p.sched, s, [&] { return launch_mx_wgrad(p, fmt, s); });
+        if (e2 == hipSuccess && p.split_len > 0) e2 = launch_wgrad_split_reduce(rp, s);
+        return e2;
+    });
+}
+
 int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy, const uint8_t *dy_scale,
                           float *main_grad, const int64_t *group_lens, const int64_t *group_offs, int64_t G,
                           int64_t M, int64_t N, int64_t K, int dtype, int trans_out, int accumulate,
@@ -752,60 +820,8 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
             e = launch_mx_tokens_transpose((const uint8_t *)dy, dy_scale, group_lens, group_offs, (int)G, M, N, fmt,
                                            qd, w.pitch, sd, plan, s);
         if (e != hipSuccess) return PT_ERR_HIP;
-        // trans_out = 0: rows are A's channels (K), columns dY's (N); 1: swapped
-        MxParams p = {};
-        p.a = trans_out ? qd : qa;
-        p.sa = trans_out ? sd : sa;
-        p.b = trans_out ? qa : qd;
-        p.sb = trans_out ? sa : sd;
-        p.wrows = (int)(trans_out ? N : K);
-        p.wcols = (int)(trans_out ? K : N);
-        p.pitch = w.pitch;
-        p.plan = plan;
-        p.out = main_grad;
-        p.ldo = p.wcols;
-        p.o_gstride = N * K;
-        p.tilesM = (p.wrows + mx_wide_tile() - 1) / mx_wide_tile();
-        p.tilesN = (p.wcols + mx_wide_tile() - 1) / mx_wide_tile();
-        p.accumulate = accumulate;
-        p.lens = group_lens;
-        p.offs = group_offs;
-        p.err = error_word(workspace, workspace_bytes);
-        p.G = (int)G;
-        p.M = M;
-        p.K = 32;
-        p.N = p.wcols;
-        p.swiglu_limit = __builtin_huge_valf();
-        uint32_t *queues = queue_words(workspace, workspace_bytes);
-        // the split reduction, when the workspace holds its partial slots: the
-        // chunk length of the BF16 rule rounded up to whole 256-token stages
-        const int64_t split_len = (wgrad_split_len(M, p.wrows, p.wcols) + 255) / 256 * 256;
-        const int64_t nslots = M / split_len;
-        Bf16Params rp = {};
-        if (queues && nslots > 0 && workspace_bytes >= (size_t)(w.total + wgrad_split_bytes(M, K, N))) {
-            p.split_len = (int)split_len;
-            p.nslots = (int)nslots;
-            p.partials = (float *)(base + w.total);
-            rp.lens = group_lens;
-            rp.offs = group_offs;
-            rp.G = (int)G;
-            rp.M = M;
-            rp.split_len = p.split_len;
-            rp.nslots = p.nslots;
-            rp.partials = p.partials;
-            rp.out = main_grad;
-            rp.o_gstride = N * K;
-            rp.Mout = p.wrows;
-            rp.Nout = p.wcols;
-            rp.accumulate = accumulate;
-        }
-        const TuneKey key = tune_key(PT_OP_WGRAD, dtype, kEpiWgrad, trans_out, G, M, N, K);
-        return configured(key, cfg_mask(queues != nullptr, false), false, s, [&](int cfg) {
-            p.sched = (cfg & kCfgStatic) ? nullptr : queues;
-            hipError_t e2 = queued(p.sched, s, [&] { return launch_mx_wgrad(p, fmt, s); });
-            if (e2 == hipSuccess && p.split_len > 0) e2 = launch_wgrad_split_reduce(rp, s);
-            return e2;
-        });
+        return mx_wgrad_gemm(w, base, dtype, main_grad, group_lens, group_offs, G, M, N, K, trans_out, accumulate,
+                             workspace, workspace_bytes, s);
     }
     if (dtype == PT_FP8_E4M3) {
         // one factor per tensor: both gradients' codes are transposed into
@@ -867,6 +883,42 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
     if (a_scale || dy_scale) return PT_ERR_INVALID_ARG;
     return bf16_wgrad(a, dy, main_grad, group_lens, group_offs, G, M, N, K, trans_out, accumulate, workspace,
                       workspace_bytes, kQueueWsBytes, s);
+}
+
+int pt_grouped_gemm_wgrad_quantize(const void *a, const void *dy, float *main_grad, const int64_t *group_lens,
+                                   const int64_t *group_offs, int64_t G, int64_t M, int64_t N, int64_t K, int dtype,
+                                   int trans_out, int accumulate, void *workspace, size_t workspace_bytes,
+                                   void *stream)
+{
+    int st = check_groups(group_lens, G, M);
+    if (st) return st;
+    if (N < 8 || K < 8 || N > INT32_MAX / 4 || K > INT32_MAX / 4) return PT_ERR_INVALID_ARG;
+    if (!main_grad || (M > 0 && (!a || !dy))) return PT_ERR_INVALID_ARG;
+    if (trans_out != 0 && trans_out != 1) return PT_ERR_INVALID_ARG;
+    if (accumulate != 0 && accumulate != 1) return PT_ERR_INVALID_ARG;
+    if (dtype != PT_MXFP8_E4M3 && dtype != PT_MXFP4_E2M1) return PT_ERR_UNSUPPORTED;
+    if (N % 8 || K % 8) return PT_ERR_UNSUPPORTED;
+    if (!fits31(M * K * 2) || !fits31(M * N * 2)) return PT_ERR_UNSUPPORTED;
+    if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad)) return PT_ERR_MISALIGNED;
+    if (M == 0 && accumulate) return PT_OK;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
+    const MxWgradWs w = mx_wgrad_ws(G, M, N, K, fmt);
+    if (!fits31(K * w.pitch) || !fits31(N * w.pitch) || !fits31(w.stages * (K + N) * 8)) return PT_ERR_UNSUPPORTED;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < (size_t)w.total) return PT_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *base = (uint8_t *)workspace;
+    int *plan = (int *)(base + w.plan);
+    // both gradients quantised along tokens straight into the operand layout
+    // of the MX weight gradient (the GEMM validates the lengths itself)
+    hipError_t e = launch_mx_tokens_quant_t((const uint16_t *)a, group_lens, group_offs, (int)G, M, K, fmt,
+                                            base + w.qa, w.pitch, (uint32_t *)(base + w.sa), plan, nullptr, s);
+    if (e == hipSuccess)
+        e = launch_mx_tokens_quant_t((const uint16_t *)dy, group_lens, group_offs, (int)G, M, N, fmt, base + w.qd,
+                                     w.pitch, (uint32_t *)(base + w.sd), plan, nullptr, s);
+    if (e != hipSuccess) return PT_ERR_HIP;
+    return mx_wgrad_gemm(w, base, dtype, main_grad, group_lens, group_offs, G, M, N, K, trans_out, accumulate,
+                         workspace, workspace_bytes, s);
 }
 
 int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_t cols, int dtype, int axis,

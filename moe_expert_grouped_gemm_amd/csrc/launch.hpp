@@ -163,6 +163,12 @@ int64_t mx_wgrad_stages(int64_t M, int G, int fmt);
 hipError_t launch_mx_tokens_transpose(const uint8_t *q, const uint8_t *scales, const int64_t *lens,
                                       const int64_t *offs, int G, int64_t M, int64_t C, int fmt, uint8_t *qt,
                                       int64_t pitch, uint32_t *st, int *plan, hipStream_t s);
+// The same operands straight from bf16 x [M, C] (quantisation along tokens
+// and the transpose in one pass, bit-identical to launch_mx_quantize_tokens then
+// launch_mx_tokens_transpose); err may be null.
+hipError_t launch_mx_tokens_quant_t(const uint16_t *x, const int64_t *lens, const int64_t *offs, int G, int64_t M,
+                                    int64_t C, int fmt, uint8_t *qt, int64_t pitch, uint32_t *st, int *plan,
+                                    uint32_t *err, hipStream_t s);
 // Expert weight stack: G separate bf16 matrices (a device array of their
 // addresses) -> [G, R, C], or [G, C, R] with trans; and their MX caches
 // along C ([G, R, C(/2)] + [G, R, C/32]) and/or along R of the transpose

@@ -34,8 +34,7 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t x)
 // non-temporal policy; the transposing kernels' codes fill half lines, which
 // the default policy merges in L2 before they reach memory.
 template <int FMT, bool NT = true>
-__device__ __forceinline__ void quantise8(const uintx4 v, uint8_t *__restrict__ q, uint8_t *__restrict__ scales,
-                                          int64_t t)
+__device__ __forceinline__ uint32_t encode8(const uintx4 v, uint8_t *__restrict__ q, int64_t t)
 {
     constexpr int EMAX = FMT == 0 ? 8 : 2;
     constexpr float LIM = FMT == 0 ? 448.0f : 6.0f;
@@ -72,6 +71,15 @@ __device__ __forceinline__ void quantise8(const uintx4 v, uint8_t *__restrict__ 
         else
             *(uint32_t *)(q + t * 4) = w;
     }
+    return E;
+}
+
+// The same, and lane 0 of the quad stores the block's scale byte.
+template <int FMT, bool NT = true>
+__device__ __forceinline__ void quantise8(const uintx4 v, uint8_t *__restrict__ q, uint8_t *__restrict__ scales,
+                                          int64_t t)
+{
+    const uint32_t E = encode8<FMT, NT>(v, q, t);
     if ((t & 3) == 0) scales[t >> 2] = (uint8_t)E;
 }
 
@@ -618,6 +626,141 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_transpose_kernel(
     }
 }
 
+// Quantisation along tokens straight into the weight gradient's operand
+// layout: bf16 x [M, C] -> the channel rows and stage-major scale words that
+// mx_tokens_quant_kernel followed by mx_tokens_transpose_kernel produce, bit
+// for bit, without the [M, C] codes in between.  A work item is one stage of
+// one expert (TS tokens) for 128 channels: its bf16 tokens go to a 128-column
+// LDS tile (16-byte row loads), then 4 lanes per 32-token block of a channel
+// encode it as the row quantiser does along its axis (amax over the block,
+// E8M0 byte, scaled and clamped values, hardware nearest-even conversion):
+// 8 codes (E4M3) or 4 bytes of token pairs (E2M1, even token in the low
+// nibble) per lane, 128 contiguous bytes per channel row and stage.  Tokens
+// past the expert's end read as zeros, so a partial last block is encoded
+// as the token quantiser encodes it and its padding tokens get zero codes;
+// blocks past the expert's last one are not written (they are the next
+// expert's), and their scale bytes in the expert's stage words are zero.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void mx_tokens_quant_t_kernel(
+    const uint16_t *__restrict__ x, const int64_t *lens, const int64_t *offs, int G, int64_t M, int C,
+    uint8_t *__restrict__ qt, int64_t pitch, uint32_t *__restrict__ st, int *plan, uint32_t *err)
+{
+    constexpr int TS = FMT == 0 ? 128 : 256;            // tokens per stage
+    constexpr int NBS = TS / 32;                        // blocks per stage
+    constexpr int LPC = NBS * 4;                        // lanes per channel
+    extern __shared__ __attribute__((aligned(16))) int sm_tok[];
+    GroupTable tab;
+    tokens_table(tab, sm_tok, lens, offs, G, M, err);
+    int *sst = tab.tile0 + G + 1 + 8;                   // each expert's first stage, [G + 1]
+    int *scr = sst + G + 1;
+    uint8_t *tile = (uint8_t *)(((uintptr_t)(scr + 8) + 15) & ~(uintptr_t)15);
+    {
+        const int per = (G + kThreads - 1) / kThreads, g0 = threadIdx.x * per;
+        int sum = 0;
+        for (int i = 0; i < per; ++i)
+            if (g0 + i < G) sum += (tab.rows[g0 + i] + TS - 1) / TS;
+        int all;
+        int pre = block_exclusive_scan<kThreads>(sum, scr, &all);
+        for (int i = 0; i < per; ++i)
+            if (g0 + i < G) {
+                sst[g0 + i] = pre;
+                pre += (tab.rows[g0 + i] + TS - 1) / TS;
+            }
+        if (threadIdx.x == 0) sst[G] = all;
+        __syncthreads();
+    }
+    if (blockIdx.x == 0)
+        for (int g = threadIdx.x; g < G; g += kThreads) {
+            plan[2 * g] = tab.tile0[g];
+            plan[2 * g + 1] = sst[g];
+        }
+    const int nch = (C + kTrCh - 1) / kTrCh;
+    const int64_t items = (int64_t)sst[G] * nch;
+    const int tid = threadIdx.x;
+    // An item's place: expert g, its stage kt, global stage sg, channels c0..
+    struct Item {
+        int g, kt, sg, c0, nvalid, nbk;
+        int64_t r0, ob;
+    };
+    auto place = [&](int64_t w) {
+        Item it;
+        it.sg = (int)(w / nch);
+        it.c0 = (int)(w % nch) * kTrCh;
+        int lo = 0, hi = G;                              // the last expert with sst <= sg
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sst[mid] <= it.sg) lo = mid; else hi = mid;
+        }
+        it.g = lo;
+        it.kt = it.sg - sst[lo];
+        const int rows = tab.rows[lo], nb = (rows + 31) / 32, tok0 = it.kt * TS;
+        it.nvalid = min(TS, rows - tok0);               // real tokens of the stage
+        it.nbk = min(NBS, nb - it.kt * NBS);            // the expert's blocks in the stage
+        it.r0 = (int64_t)tab.row0[lo] + tok0;
+        it.ob = (int64_t)(FMT == 0 ? 32 : 16) * tab.tile0[lo] + (int64_t)it.kt * 128;
+        return it;
+    };
+    // tokens r0 .. r0 + TS - 1, channels c0 .. c0 + 127 into registers (the
+    // next item's loads fly while the current one is encoded), then to LDS
+    // rows of TB_RS bytes
+    constexpr int NL = TS * 16 / kThreads;
+    uintx4 v[NL];
+    auto load = [&](const Item &it) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int k = tid + j * kThreads;
+            const int t = k >> 4, c8 = (k & 15) * 8;
+            v[j] = uintx4{0u, 0u, 0u, 0u};
+            if (t < it.nvalid && it.c0 + c8 < C)
+                v[j] = __builtin_nontemporal_load((const uintx4 *)(x + (it.r0 + t) * C + it.c0 + c8));
+        }
+    };
+    int64_t w = blockIdx.x;
+    Item cur = place(w < items ? w : 0);
+    if (w < items) load(cur);
+    for (; w < items; w += gridDim.x) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int k = tid + j * kThreads;
+            uint32_t *d = (uint32_t *)(tile + (k >> 4) * TB_RS + (k & 15) * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = v[j][e];
+        }
+        __syncthreads();
+        const Item it = cur;
+        if (w + gridDim.x < items) {
+            cur = place(w + gridDim.x);
+            load(cur);
+        }
+        // LPC lanes per channel: lane li takes tokens 8 li .. 8 li + 7 of
+        // block li / 4
+#pragma unroll 2
+        for (int pass = 0; pass < kTrCh * LPC / kThreads; ++pass) {
+            const int u = tid + pass * kThreads;
+            const int col = u / LPC, li = u % LPC, blk = li >> 2, tt = li * 8;
+            if (it.c0 + col >= C) continue;              // whole channels: whole quads
+            uintx4 q8;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo16 = *(const uint16_t *)(tile + (tt + 2 * e) * TB_RS + col * 2);
+                const uint32_t hi16 = *(const uint16_t *)(tile + (tt + 2 * e + 1) * TB_RS + col * 2);
+                q8[e] = lo16 | (hi16 << 16);
+            }
+            uint8_t *qrow = qt + (int64_t)(it.c0 + col) * pitch + it.ob;
+            uint32_t E = 0;
+            if (blk < it.nbk) E = encode8<FMT, false>(q8, qrow, li);   // whole quads: blk is uniform over one
+            // the block's scale byte in the expert's stage word(s): E4M3
+            // byte blk of word (sg, c); E2M1 byte blk / 2 of word 2 (sg, c) + blk % 2
+            if ((li & 3) == 0) {
+                const int64_t wi = (int64_t)it.sg * C + it.c0 + col;
+                uint8_t *sb = (uint8_t *)st + (FMT == 0 ? wi * 4 + blk : (2 * wi + (blk & 1)) * 4 + (blk >> 1));
+                *sb = (uint8_t)E;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------------ expert weight stack
 // Per-expert weights are G separate bf16 matrices W_g [R, C] (row-major),
 // given as a device array of their addresses.  One read of each builds the
@@ -643,18 +786,33 @@ __global__ __launch_bounds__(kThreads) void stack_experts_kernel(const void *con
     __shared__ __attribute__((aligned(16))) uint8_t tile[TRANS ? TB * TB_RS : 16];
     const int64_t g = blockIdx.z;
     const int64_t r0 = (int64_t)blockIdx.y * TB, c0 = (int64_t)blockIdx.x * TB;
-    uintx4 v[8];
-    load_rows_tb(expert_ptr(ptrs, err), R, C, r0, c0, v);
+    const uint16_t *xb = expert_ptr(ptrs, err);
     if (!TRANS) {
+        // a plain copy of the tile's rows: four 16-byte loads in flight per
+        // thread, then their stores, twice
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int k = threadIdx.x + j * kThreads;
-            const int row = k >> 4, c8 = (k & 15) * 8;
-            if (r0 + row < R && c0 + c8 < C)
-                __builtin_nontemporal_store(v[j], (uintx4 *)(out + (g * R + r0 + row) * C + c0 + c8));
+        for (int h = 0; h < 2; ++h) {
+            uintx4 w4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = threadIdx.x + (4 * h + j) * kThreads;
+                const int row = k >> 4, c8 = (k & 15) * 8;
+                w4[j] = uintx4{0u, 0u, 0u, 0u};
+                if (xb && r0 + row < R && c0 + c8 < C)
+                    w4[j] = __builtin_nontemporal_load((const uintx4 *)(xb + (r0 + row) * C + c0 + c8));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = threadIdx.x + (4 * h + j) * kThreads;
+                const int row = k >> 4, c8 = (k & 15) * 8;
+                if (r0 + row < R && c0 + c8 < C)
+                    __builtin_nontemporal_store(w4[j], (uintx4 *)(out + (g * R + r0 + row) * C + c0 + c8));
+            }
         }
         return;
     }
+    uintx4 v[8];
+    load_rows_tb(xb, R, C, r0, c0, v);
     rows_to_lds_tb(v, tile);
     __syncthreads();
     // the tile's 128 columns become 128 output rows of 16 chunks of 8
@@ -827,6 +985,27 @@ hipError_t launch_mx_tokens_transpose(const uint8_t *q, const uint8_t *scales, c
     else
         hipLaunchKernelGGL(mx_tokens_transpose_kernel<1>, dim3((unsigned)grid), dim3(kThreads), lds, s, q, scales,
                            lens, offs, G, M, (int)C, qt, pitch, st, plan);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_tokens_quant_t(const uint16_t *x, const int64_t *lens, const int64_t *offs, int G, int64_t M,
+                                    int64_t C, int fmt, uint8_t *qt, int64_t pitch, uint32_t *st, int *plan,
+                                    uint32_t *err, hipStream_t s)
+{
+    if (G == 0 || C == 0) return hipSuccess;
+    const int ts = fmt == 0 ? 128 : 256;
+    const size_t lds = table_bytes(G) + 4 * (G + 1) + 32 + 16 + (size_t)ts * TB_RS;
+    const int64_t items = mx_wgrad_stages(M, G, fmt) * ((C + kTrCh - 1) / kTrCh);
+    // as many workgroups as fit beside each other (LDS: 45 or 79 KiB each)
+    int64_t grid = (int64_t)device_cus() * (fmt == 0 ? 3 : 2);
+    if (grid > items) grid = items;
+    if (grid < 1) grid = 1;
+    if (fmt == 0)
+        hipLaunchKernelGGL(mx_tokens_quant_t_kernel<0>, dim3((unsigned)grid), dim3(kThreads), lds, s, x, lens, offs,
+                           G, M, (int)C, qt, pitch, st, plan, err);
+    else
+        hipLaunchKernelGGL(mx_tokens_quant_t_kernel<1>, dim3((unsigned)grid), dim3(kThreads), lds, s, x, lens, offs,
+                           G, M, (int)C, qt, pitch, st, plan, err);
     return hipGetLastError();
 }
 

@@ -1,0 +1,134 @@
+"""GPU checks of pt_grouped_gemm_wgrad_quantize, the MX weight gradient
+from bf16 gradients: quantisation along tokens fused into the transpose to
+the weight gradient's operand layout.  main_grad must come out bit-identical
+to pt_mx_quantize_tokens on both gradients followed by pt_grouped_gemm_wgrad
+(itself checked against the oracle), for both formats, both output layouts,
+accumulating and overwriting, with empty, single-row, partial-block and
+multi-stage experts, explicit offsets with unowned rows between experts,
+the split reduction, and channel counts that leave a partial 128-channel
+group.  A workspace filled with 0xA5 beforehand shows that nothing relies on
+its previous contents."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_grouped_gemm_amd as ptm
+from moe_expert_grouped_gemm_amd import synth
+from util import dev_i64
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [ptm.PT_MXFP8_E4M3, ptm.PT_MXFP4_E2M1]
+FMT_IDS = ["e4m3", "e2m1"]
+
+
+def main_grad0(dev, G, N, K, trans_out, seed):
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    shape = (G, N, K) if trans_out else (G, K, N)
+    return (torch.randn(shape, generator=g, device=dev) * 1e-3).float()
+
+
+def workspace(dev, G, M, N, K, fmt, extra=0):
+    n = ptm.pt_grouped_gemm_workspace_size(ptm.PT_OP_WGRAD, G, M, N, K, fmt)
+    return torch.full((n + extra,), 0xA5, dtype=torch.uint8, device=dev)
+
+
+def two_step(dev, a, dy, lens, offs, N, K, fmt, trans_out, accumulate, mg, ws):
+    M, G = a.shape[0], len(lens)
+    lens_d = dev_i64(lens, dev)
+    offs_d = None if offs is None else dev_i64(offs, dev)
+    cols = (lambda c: c) if fmt == ptm.PT_MXFP8_E4M3 else (lambda c: c // 2)
+    aq = torch.zeros((M, cols(K)), dtype=torch.uint8, device=dev)
+    dq = torch.zeros((M, cols(N)), dtype=torch.uint8, device=dev)
+    as_ = torch.zeros((M // 32 + G, K), dtype=torch.uint8, device=dev)
+    ds = torch.zeros((M // 32 + G, N), dtype=torch.uint8, device=dev)
+    ptm.pt_mx_quantize_tokens(a, lens_d, offs_d, aq, as_, G, M, K, fmt)
+    ptm.pt_mx_quantize_tokens(dy, lens_d, offs_d, dq, ds, G, M, N, fmt)
+    ptm.pt_grouped_gemm_wgrad(aq, as_, dq, ds, mg, lens_d, offs_d, G, M, N, K, fmt, trans_out, accumulate,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    return mg
+
+
+def fused(dev, a, dy, lens, offs, N, K, fmt, trans_out, accumulate, mg, ws):
+    M, G = a.shape[0], len(lens)
+    ptm.pt_grouped_gemm_wgrad_quantize(a, dy, mg, dev_i64(lens, dev), None if offs is None else dev_i64(offs, dev),
+                                       G, M, N, K, fmt, trans_out, accumulate, workspace=ws)
+    torch.cuda.synchronize()
+    return mg
+
+
+CASES = [
+    # (name, lens, K, N)
+    ("ragged", [0, 70, 1, 0, 300, 129, 0, 33], 264, 136),
+    ("multi_stage", [600, 5, 257, 1000], 200, 392),
+    ("one_expert", [45], 8, 16),
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("trans_out", [0, 1])
+@pytest.mark.parametrize("accumulate", [1, 0])
+def test_fused_equals_quantize_then_wgrad(dev, fmt, case, trans_out, accumulate):
+    name, lens, K, N = case
+    lens = np.array(lens, np.int64)
+    M, G = int(lens.sum()), len(lens)
+    print(f"wgrad_quantize {name} fmt={fmt} trans_out={trans_out} acc={accumulate}", flush=True)
+    a = synth.randn_bf16((M, K), seed=400, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    dy = synth.randn_bf16((M, N), seed=401, std=1e-2, device=dev)
+    ref = two_step(dev, a, dy, lens, None, N, K, fmt, trans_out, accumulate, main_grad0(dev, G, N, K, trans_out, 402),
+                   workspace(dev, G, M, N, K, fmt))
+    ws = workspace(dev, G, M, N, K, fmt, extra=4096)
+    got = fused(dev, a, dy, lens, None, N, K, fmt, trans_out, accumulate, main_grad0(dev, G, N, K, trans_out, 402),
+                ws)
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    n = ws.numel() - 4096
+    assert (ws[n:].cpu().numpy() == 0xA5).all(), "write past the workspace"
+    # a second call on the same (now dirty) workspace gives the same bits
+    again = fused(dev, a, dy, lens, None, N, K, fmt, trans_out, accumulate,
+                  main_grad0(dev, G, N, K, trans_out, 402), ws)
+    assert torch.equal(again.view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_fused_with_offsets_and_gaps(dev, fmt):
+    # experts at explicit offsets with unowned rows between and after them
+    lens = np.array([40, 0, 97, 3], np.int64)
+    offs = np.array([2, 50, 50, 160, 170], np.int64)
+    M, G, K, N = 180, len(lens), 96, 72
+    a = synth.randn_bf16((M, K), seed=410, device=dev)
+    dy = synth.randn_bf16((M, N), seed=411, std=1e-2, device=dev)
+    ref = two_step(dev, a, dy, lens, offs, N, K, fmt, 0, 1, main_grad0(dev, G, N, K, 0, 412),
+                   workspace(dev, G, M, N, K, fmt))
+    got = fused(dev, a, dy, lens, offs, N, K, fmt, 0, 1, main_grad0(dev, G, N, K, 0, 412),
+                workspace(dev, G, M, N, K, fmt))
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_IDS)
+def test_fused_split_reduction(dev, fmt):
+    # one 12.5k-token expert among short ones, K = N = 256: the split cuts it
+    lens = np.array([12500, 480, 0, 350, 499, 1, 200], np.int64)
+    M, G, K, N = int(lens.sum()), len(lens), 256, 256
+    a = synth.randn_bf16((M, K), seed=420, std=K ** -0.5, device=dev)
+    dy = synth.randn_bf16((M, N), seed=421, std=1e-2, device=dev)
+    ref = two_step(dev, a, dy, lens, None, N, K, fmt, 0, 1, main_grad0(dev, G, N, K, 0, 422),
+                   workspace(dev, G, M, N, K, fmt))
+    got = fused(dev, a, dy, lens, None, N, K, fmt, 0, 1, main_grad0(dev, G, N, K, 0, 422),
+                workspace(dev, G, M, N, K, fmt))
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+
+
+def test_fused_argument_errors(dev):
+    lens = dev_i64([4, 4], dev)
+    a = torch.zeros((8, 16), dtype=torch.bfloat16, device=dev)
+    dy = torch.zeros((8, 16), dtype=torch.bfloat16, device=dev)
+    mg = torch.zeros((2, 16, 16), dtype=torch.float32, device=dev)
+    ws = workspace(dev, 2, 8, 16, 16, ptm.PT_MXFP8_E4M3)
+    with pytest.raises(ptm.PtggError, match="UNSUPPORTED"):
+        ptm.pt_grouped_gemm_wgrad_quantize(a, dy, mg, lens, None, 2, 8, 16, 16, ptm.PT_BF16, 0, 1, workspace=ws)
+    with pytest.raises(ptm.PtggError, match="WORKSPACE"):
+        ptm.pt_grouped_gemm_wgrad_quantize(a, dy, mg, lens, None, 2, 8, 16, 16, ptm.PT_MXFP8_E4M3, 0, 1,
+                                           workspace=ws[:64])
