@@ -145,6 +145,16 @@ def test_argument_checks_host_only():
     assert L.pt_stack_experts(None, None, 0, 64, 64, 0, None, 0, None) == 0          # nothing to do
     assert L.pt_mx_quantize_experts(None, None, None, None, None, 2, 64, 64, 1, None, 0, None) == 1
     assert L.pt_mx_quantize_tokens(None, lp, None, None, None, 4, 10, 64, 0, None, 0, None) == 2   # BF16
+    # the MX weight gradient from bf16 gradients: argument refusals, then the
+    # dtype (MX formats only), then the 8-column alignment
+    mg = (ctypes.c_float * 4)()
+    mp = ctypes.cast(mg, ctypes.c_void_p).value
+    W = L.pt_grouped_gemm_wgrad_quantize
+    assert W(None, None, None, lp, None, 4, 10, 64, 64, 1, 0, 1, None, 0, None) == 1     # no main_grad
+    assert W(mp, mp, mp, lp, None, 4, 10, 64, 64, 1, 2, 1, None, 0, None) == 1          # trans_out
+    assert W(mp, mp, mp, lp, None, 4, 10, 64, 64, 1, 0, 2, None, 0, None) == 1          # accumulate
+    assert W(mp, mp, mp, lp, None, 4, 10, 64, 64, 0, 0, 1, None, 0, None) == 2          # BF16
+    assert W(mp, mp, mp, lp, None, 4, 10, 64, 60, 2, 0, 1, None, 0, None) == 2          # K % 8
 
 
 def test_config_mode_host_only():
