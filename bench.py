@@ -658,9 +658,13 @@ def bench_cfg3_wgrad(dev, stream, iters):
         ptm.pt_grouped_gemm_wgrad(aq, fa, dq, fd, mg, lens_d, None, G, M, N, K, ptm.PT_FP8_E4M3, 0, 1,
                                   workspace=ws8, stream=stream)
     _, per8 = time_launches(step8, iters, 3, stream)
+    _, per8f = time_launches(lambda: ptm.pt_grouped_gemm_wgrad_quantize(
+        a, dy, mg, lens_d, None, G, M, N, K, ptm.PT_FP8_E4M3, 0, 1, workspace=ws8, stream=stream),
+        iters, 3, stream)
     nbytes8 = M * K * 2 * 2 + M * N * 2 * 2 + 2 * (M * K + M * N) + bytes_weights(lens, K * N * 4 * 2)
     w8 = summary("FP8 wgrad with tensor factors (two-pass quantise of A and dY + weight gradient into fp32 "
-                 "main_grad), 32 experts, M=65536, K=2880, N=5760", "fp8", flops, nbytes8, per8)
+                 "main_grad), 32 experts, M=65536, K=2880, N=5760", "fp8", flops, nbytes8, per8,
+                 {"fused_quantize_wgrad_ms_median": round(float(np.median(per8f)), 4)})
     del a, dy, aq, dq, mg, ws8
     torch.cuda.empty_cache()
     return w, w8

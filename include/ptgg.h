@@ -319,8 +319,10 @@ int pt_grouped_gemm_dgrad_swiglu(const void *dy, const uint8_t *dy_scale, const 
  *  with S_g the fp32 sum of the exact code products (the whole expert's:
  *  no split along tokens), one fused multiply-add per element.  The
  *  workspace is required: both operands' codes transposed to channel rows
- *  as for MXFP8 (no scales) and the experts' starts,
- *  pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ..., PT_FP8_E4M3) bytes,
+ *  as for MXFP8 (no scales) and the experts' starts (the size that
+ *  pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ..., PT_FP8_E4M3) gives is
+ *  256 bytes more, for pt_grouped_gemm_wgrad_quantize's amax words and
+ *  factors; this call needs only the bytes before them),
  *  else PT_ERR_WORKSPACE.  (Row factors vary along the reduction, so
  *  PT_FP8_E4M3_ROWWISE has no weight gradient: PT_ERR_UNSUPPORTED.)
  *  Requirements: K % 8 == 0, N % 8 == 0; dtype PT_BF16, PT_MXFP8_E4M3,
@@ -335,17 +337,22 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * The MX weight gradient from the bf16 gradients themselves (Primus-Turbo
- * README, "What's New": MXFP8 grouped MLP backward; PR page "[Megatron-LM]
- * feat: add grouped gemm fp4 support, ...", "Changes": the gradient added
- * into weight.main_grad).  a [M, K] and dy [M, N] are bf16, rows grouped by
- * expert as for pt_grouped_gemm_wgrad; dtype PT_MXFP8_E4M3 or
- * PT_MXFP4_E2M1.  Both are quantised along tokens within each expert
- * (blocks of 32 rows, the rule of pt_mx_quantize_tokens) straight into the
- * workspace's transposed operand layout, then the MX weight gradient runs:
- * main_grad comes out bit-identical to pt_mx_quantize_tokens on a and on dy
- * followed by pt_grouped_gemm_wgrad with that dtype and workspace, but the
- * [M, K] and [M, N] codes are neither written nor read back.  Same
+ * The low-precision weight gradient from the bf16 gradients themselves
+ * (Primus-Turbo README, "What's New": MXFP8 grouped MLP backward and FP8
+ * grouped GEMM; PR page "[Megatron-LM] feat: add grouped gemm fp4 support,
+ * ...", "Changes": the gradient added into weight.main_grad).  a [M, K] and
+ * dy [M, N] are bf16, rows grouped by expert as for pt_grouped_gemm_wgrad.
+ *  PT_MXFP8_E4M3 / PT_MXFP4_E2M1: both are quantised along tokens within
+ *  each expert (blocks of 32 rows, the rule of pt_mx_quantize_tokens)
+ *  straight into the workspace's transposed operand layout, then the MX
+ *  weight gradient runs: main_grad comes out bit-identical to
+ *  pt_mx_quantize_tokens on a and on dy followed by pt_grouped_gemm_wgrad
+ *  with that dtype and workspace.
+ *  PT_FP8_E4M3: each tensor's amax, then its codes with one factor per
+ *  tensor (the rule of pt_fp8_quantize, batch 1, over all M rows) straight
+ *  into the transposed layout: bit-identical to pt_fp8_quantize on a and
+ *  on dy followed by pt_grouped_gemm_wgrad with PT_FP8_E4M3.
+ * The [M, K] and [M, N] codes are neither written nor read back.  Same
  * arguments, layouts (trans_out), accumulate rule, split reduction and
  * errors as pt_grouped_gemm_wgrad; the workspace is required,
  * pt_grouped_gemm_workspace_size(PT_OP_WGRAD, ..., dtype) bytes, else

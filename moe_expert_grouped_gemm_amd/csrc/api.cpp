@@ -780,6 +780,47 @@ static int mx_wgrad_gemm(const MxWgradWs &w, uint8_t *base, int dtype, float *ma
     });
 }
 
+// The FP8 weight gradient with one factor per tensor on operands already in
+// the workspace (both gradients' codes as channel rows, the experts' plan);
+// fa, fd: the two dequantisation factors (device).
+static int fp8_wgrad_gemm(const MxWgradWs &w, uint8_t *base, const float *fa, const float *fd, float *main_grad,
+                          const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M, int64_t N,
+                          int64_t K, int trans_out, int accumulate, void *workspace, size_t workspace_bytes,
+                          hipStream_t s)
+{
+    int *plan = (int *)(base + w.plan);
+    uint8_t *qa = base + w.qa, *qd = base + w.qd;
+    MxParams p = {};
+    p.a = trans_out ? qd : qa;
+    p.b = trans_out ? qa : qd;
+    p.sfa = fa;
+    p.sfb = fd;
+    p.wrows = (int)(trans_out ? N : K);
+    p.wcols = (int)(trans_out ? K : N);
+    p.pitch = w.pitch;
+    p.plan = plan;
+    p.out = main_grad;
+    p.ldo = p.wcols;
+    p.o_gstride = N * K;
+    p.tilesM = (p.wrows + mx_wide_tile() - 1) / mx_wide_tile();
+    p.tilesN = (p.wcols + mx_wide_tile() - 1) / mx_wide_tile();
+    p.accumulate = accumulate;
+    p.lens = group_lens;
+    p.offs = group_offs;
+    p.err = error_word(workspace, workspace_bytes);
+    p.G = (int)G;
+    p.M = M;
+    p.K = 32;
+    p.N = p.wcols;
+    p.swiglu_limit = __builtin_huge_valf();
+    uint32_t *queues = queue_words(workspace, workspace_bytes);
+    const TuneKey key = tune_key(PT_OP_WGRAD, PT_FP8_E4M3, kEpiWgrad, trans_out, G, M, N, K);
+    return configured(key, cfg_mask(queues != nullptr, false), false, s, [&](int cfg) {
+        p.sched = (cfg & kCfgStatic) ? nullptr : queues;
+        return queued(p.sched, s, [&] { return launch_mx_wgrad(p, 2, s); });
+    });
+}
+
 int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy, const uint8_t *dy_scale,
                           float *main_grad, const int64_t *group_lens, const int64_t *group_offs, int64_t G,
                           int64_t M, int64_t N, int64_t K, int dtype, int trans_out, int accumulate,
@@ -849,41 +890,18 @@ int pt_grouped_gemm_wgrad(const void *a, const uint8_t *a_scale, const void *dy,
             e = launch_mx_tokens_transpose((const uint8_t *)dy, nullptr, group_lens, group_offs, (int)G, M, N, 0, qd,
                                            w.pitch, nullptr, plan, s);
         if (e != hipSuccess) return PT_ERR_HIP;
-        MxParams p = {};
-        p.a = trans_out ? qd : qa;
-        p.b = trans_out ? qa : qd;
-        p.sfa = (const float *)a_scale;
-        p.sfb = (const float *)dy_scale;
-        p.wrows = (int)(trans_out ? N : K);
-        p.wcols = (int)(trans_out ? K : N);
-        p.pitch = w.pitch;
-        p.plan = plan;
-        p.out = main_grad;
-        p.ldo = p.wcols;
-        p.o_gstride = N * K;
-        p.tilesM = (p.wrows + mx_wide_tile() - 1) / mx_wide_tile();
-        p.tilesN = (p.wcols + mx_wide_tile() - 1) / mx_wide_tile();
-        p.accumulate = accumulate;
-        p.lens = group_lens;
-        p.offs = group_offs;
-        p.err = error_word(workspace, workspace_bytes);
-        p.G = (int)G;
-        p.M = M;
-        p.K = 32;
-        p.N = p.wcols;
-        p.swiglu_limit = __builtin_huge_valf();
-        uint32_t *queues = queue_words(workspace, workspace_bytes);
-        const TuneKey key = tune_key(PT_OP_WGRAD, dtype, kEpiWgrad, trans_out, G, M, N, K);
-        return configured(key, cfg_mask(queues != nullptr, false), false, s, [&](int cfg) {
-            p.sched = (cfg & kCfgStatic) ? nullptr : queues;
-            return queued(p.sched, s, [&] { return launch_mx_wgrad(p, 2, s); });
-        });
+        return fp8_wgrad_gemm(w, base, (const float *)a_scale, (const float *)dy_scale, main_grad, group_lens,
+                              group_offs, G, M, N, K, trans_out, accumulate, workspace, workspace_bytes, s);
     }
     if (dtype != PT_BF16) return PT_ERR_UNSUPPORTED;
     if (a_scale || dy_scale) return PT_ERR_INVALID_ARG;
     return bf16_wgrad(a, dy, main_grad, group_lens, group_offs, G, M, N, K, trans_out, accumulate, workspace,
                       workspace_bytes, kQueueWsBytes, s);
 }
+
+// Bytes the FP8 weight gradient with tensor factors keeps after its
+// operands: the two amax words and the two dequantisation factors.
+constexpr int64_t kFp8WgradTail = 256;
 
 int pt_grouped_gemm_wgrad_quantize(const void *a, const void *dy, float *main_grad, const int64_t *group_lens,
                                    const int64_t *group_offs, int64_t G, int64_t M, int64_t N, int64_t K, int dtype,
@@ -896,27 +914,48 @@ int pt_grouped_gemm_wgrad_quantize(const void *a, const void *dy, float *main_gr
     if (!main_grad || (M > 0 && (!a || !dy))) return PT_ERR_INVALID_ARG;
     if (trans_out != 0 && trans_out != 1) return PT_ERR_INVALID_ARG;
     if (accumulate != 0 && accumulate != 1) return PT_ERR_INVALID_ARG;
-    if (dtype != PT_MXFP8_E4M3 && dtype != PT_MXFP4_E2M1) return PT_ERR_UNSUPPORTED;
+    if (dtype != PT_MXFP8_E4M3 && dtype != PT_MXFP4_E2M1 && dtype != PT_FP8_E4M3) return PT_ERR_UNSUPPORTED;
     if (N % 8 || K % 8) return PT_ERR_UNSUPPORTED;
     if (!fits31(M * K * 2) || !fits31(M * N * 2)) return PT_ERR_UNSUPPORTED;
     if (!aligned16(a) || !aligned16(dy) || !aligned16(main_grad)) return PT_ERR_MISALIGNED;
     if (M == 0 && accumulate) return PT_OK;
     if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
-    const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
-    const MxWgradWs w = mx_wgrad_ws(G, M, N, K, fmt);
-    if (!fits31(K * w.pitch) || !fits31(N * w.pitch) || !fits31(w.stages * (K + N) * 8)) return PT_ERR_UNSUPPORTED;
-    if (!workspace || !aligned16(workspace) || workspace_bytes < (size_t)w.total) return PT_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
+    const bool fp8 = dtype == PT_FP8_E4M3;
+    if (fp8 && M == 0)
+        return bf16_wgrad(nullptr, nullptr, main_grad, group_lens, group_offs, G, M, N, K, trans_out, accumulate,
+                          workspace, workspace_bytes, kQueueWsBytes, s);
+    const int fmt = dtype == PT_MXFP4_E2M1 ? 1 : 0;
+    const MxWgradWs w = mx_wgrad_ws(G, M, N, K, fmt);
+    if (!fits31(K * w.pitch) || !fits31(N * w.pitch) || (!fp8 && !fits31(w.stages * (K + N) * 8)))
+        return PT_ERR_UNSUPPORTED;
+    const int64_t need = fp8 ? w.sa + kFp8WgradTail : w.total;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < (size_t)need) return PT_ERR_WORKSPACE;
     uint8_t *base = (uint8_t *)workspace;
     int *plan = (int *)(base + w.plan);
     // both gradients quantised along tokens straight into the operand layout
-    // of the MX weight gradient (the GEMM validates the lengths itself)
-    hipError_t e = launch_mx_tokens_quant_t((const uint16_t *)a, group_lens, group_offs, (int)G, M, K, fmt,
-                                            base + w.qa, w.pitch, (uint32_t *)(base + w.sa), plan, nullptr, s);
+    // of the weight gradient (the GEMM validates the lengths itself); FP8:
+    // each tensor's amax first, then its codes with the factor of
+    // pt_fp8_quantize
+    uint32_t *amax = fp8 ? (uint32_t *)(base + w.sa) : nullptr;
+    float *deq = fp8 ? (float *)(base + w.sa + 16) : nullptr;
+    hipError_t e = hipSuccess;
+    if (fp8) {
+        e = launch_fp8_amax((const uint16_t *)a, amax, M * K, s);
+        if (e == hipSuccess) e = launch_fp8_amax((const uint16_t *)dy, amax + 1, M * N, s);
+    }
     if (e == hipSuccess)
-        e = launch_mx_tokens_quant_t((const uint16_t *)dy, group_lens, group_offs, (int)G, M, N, fmt, base + w.qd,
-                                     w.pitch, (uint32_t *)(base + w.sd), plan, nullptr, s);
+        e = launch_mx_tokens_quant_t((const uint16_t *)a, group_lens, group_offs, (int)G, M, K, fp8 ? 2 : fmt,
+                                     base + w.qa, w.pitch, fp8 ? nullptr : (uint32_t *)(base + w.sa), plan, nullptr,
+                                     amax, deq, s);
+    if (e == hipSuccess)
+        e = launch_mx_tokens_quant_t((const uint16_t *)dy, group_lens, group_offs, (int)G, M, N, fp8 ? 2 : fmt,
+                                     base + w.qd, w.pitch, fp8 ? nullptr : (uint32_t *)(base + w.sd), plan, nullptr,
+                                     fp8 ? amax + 1 : nullptr, fp8 ? deq + 1 : nullptr, s);
     if (e != hipSuccess) return PT_ERR_HIP;
+    if (fp8)
+        return fp8_wgrad_gemm(w, base, deq, deq + 1, main_grad, group_lens, group_offs, G, M, N, K, trans_out,
+                              accumulate, workspace, workspace_bytes, s);
     return mx_wgrad_gemm(w, base, dtype, main_grad, group_lens, group_offs, G, M, N, K, trans_out, accumulate,
                          workspace, workspace_bytes, s);
 }
@@ -1052,7 +1091,7 @@ size_t pt_grouped_gemm_workspace_size(int op, int64_t G, int64_t M, int64_t N, i
         return (size_t)(mx_wgrad_ws(G, M, N, K, dtype == PT_MXFP8_E4M3 ? 0 : 1).total + wgrad_split_bytes(M, K, N));
     // FP8 with tensor factors: the plan and both gradients' transposed codes
     if (op == PT_OP_WGRAD && dtype == PT_FP8_E4M3 && M > 0 && N > 0 && K > 0 && G > 0)
-        return (size_t)mx_wgrad_ws(G, M, N, K, 0).sa;
+        return (size_t)(mx_wgrad_ws(G, M, N, K, 0).sa + kFp8WgradTail);
     if (op == PT_OP_WGRAD && M > 0 && N > 0 && K > 0 && G > 0)
         return (size_t)(kQueueWsBytes + wgrad_split_bytes(M, K, N));
     // the MX data gradient: K outputs per row, a reduction over N

@@ -165,10 +165,15 @@ hipError_t launch_mx_tokens_transpose(const uint8_t *q, const uint8_t *scales, c
                                       int64_t pitch, uint32_t *st, int *plan, hipStream_t s);
 // The same operands straight from bf16 x [M, C] (quantisation along tokens
 // and the transpose in one pass, bit-identical to launch_mx_quantize_tokens then
-// launch_mx_tokens_transpose); err may be null.
+// launch_mx_tokens_transpose); err may be null.  fmt 2: E4M3 with one factor
+// per tensor from amax[0] (launch_fp8_amax; bit-identical to
+// launch_fp8_quantize then the transpose without scales), the dequantisation
+// factor written to dequant[0]; st unused.
 hipError_t launch_mx_tokens_quant_t(const uint16_t *x, const int64_t *lens, const int64_t *offs, int G, int64_t M,
                                     int64_t C, int fmt, uint8_t *qt, int64_t pitch, uint32_t *st, int *plan,
-                                    uint32_t *err, hipStream_t s);
+                                    uint32_t *err, const uint32_t *amax, float *dequant, hipStream_t s);
+// max |x| over n bf16 values as fp32 bits into amax[0] (zeroed first).
+hipError_t launch_fp8_amax(const uint16_t *x, uint32_t *amax, int64_t n, hipStream_t s);
 // Expert weight stack: G separate bf16 matrices (a device array of their
 // addresses) -> [G, R, C], or [G, C, R] with trans; and their MX caches
 // along C ([G, R, C(/2)] + [G, R, C/32]) and/or along R of the transpose

@@ -643,9 +643,12 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_transpose_kernel(
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void mx_tokens_quant_t_kernel(
     const uint16_t *__restrict__ x, const int64_t *lens, const int64_t *offs, int G, int64_t M, int C,
-    uint8_t *__restrict__ qt, int64_t pitch, uint32_t *__restrict__ st, int *plan, uint32_t *err)
+    uint8_t *__restrict__ qt, int64_t pitch, uint32_t *__restrict__ st, int *plan, uint32_t *err,
+    const uint32_t *amax, float *dequant)
 {
-    constexpr int TS = FMT == 0 ? 128 : 256;            // tokens per stage
+    // FMT 2: E4M3 with one factor per tensor (the rule of fp8_encode_kernel
+    // from the tensor's amax), the E4M3 layout without scale words
+    constexpr int TS = FMT == 1 ? 256 : 128;            // tokens per stage
     constexpr int NBS = TS / 32;                        // blocks per stage
     constexpr int LPC = NBS * 4;                        // lanes per channel
     extern __shared__ __attribute__((aligned(16))) int sm_tok[];
@@ -674,6 +677,11 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_t_kernel(
             plan[2 * g] = tab.tile0[g];
             plan[2 * g + 1] = sst[g];
         }
+    float fs = 1.0f;                                    // FMT 2: the tensor's scale
+    if constexpr (FMT == 2) {
+        fs = fp8_tensor_scale(__uint_as_float(amax[0]));
+        if (blockIdx.x == 0 && threadIdx.x == 0) dequant[0] = 1.0f / fs;
+    }
     const int nch = (C + kTrCh - 1) / kTrCh;
     const int64_t items = (int64_t)sst[G] * nch;
     const int tid = threadIdx.x;
@@ -697,7 +705,7 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_t_kernel(
         it.nvalid = min(TS, rows - tok0);               // real tokens of the stage
         it.nbk = min(NBS, nb - it.kt * NBS);            // the expert's blocks in the stage
         it.r0 = (int64_t)tab.row0[lo] + tok0;
-        it.ob = (int64_t)(FMT == 0 ? 32 : 16) * tab.tile0[lo] + (int64_t)it.kt * 128;
+        it.ob = (int64_t)(FMT == 1 ? 16 : 32) * tab.tile0[lo] + (int64_t)it.kt * 128;
         return it;
     };
     // tokens r0 .. r0 + TS - 1, channels c0 .. c0 + 127 into registers (the
@@ -747,6 +755,22 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_t_kernel(
                 q8[e] = lo16 | (hi16 << 16);
             }
             uint8_t *qrow = qt + (int64_t)(it.c0 + col) * pitch + it.ob;
+            if constexpr (FMT == 2) {
+                if (blk < it.nbk) {
+                    float f[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        f[2 * e] = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(q8[e] & 0xFFFFu) * fs, -448.0f), 448.0f);
+                        f[2 * e + 1] = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(q8[e] >> 16) * fs, -448.0f), 448.0f);
+                    }
+                    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+                    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
+                    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+                    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
+                    *(uintx2 *)(qrow + li * 8) = uintx2{(uint32_t)w0, (uint32_t)w1};
+                }
+                continue;
+            }
             uint32_t E = 0;
             if (blk < it.nbk) E = encode8<FMT, false>(q8, qrow, li);   // whole quads: blk is uniform over one
             // the block's scale byte in the expert's stage word(s): E4M3
@@ -931,6 +955,18 @@ hipError_t launch_fp8_quantize(const uint16_t *x, uint8_t *q, float *amax, float
     return hipGetLastError();
 }
 
+hipError_t launch_fp8_amax(const uint16_t *x, uint32_t *amax, int64_t n, hipStream_t s)
+{
+    hipLaunchKernelGGL(fp8_amax_zero_kernel, dim3(1), dim3(64), 0, s, amax, (int64_t)1);
+    const int64_t n8 = n / 8;
+    int64_t chunks = (n8 + kThreads - 1) / kThreads;
+    const int64_t cap = (int64_t)device_cus() * 8;
+    if (chunks > cap) chunks = cap;
+    if (chunks < 1) chunks = 1;
+    hipLaunchKernelGGL(fp8_amax_kernel, dim3((unsigned)chunks, 1u), dim3(kThreads), 0, s, x, amax, n8);
+    return hipGetLastError();
+}
+
 hipError_t launch_fp8_quantize_rows(const uint16_t *x, uint8_t *q, float *amax, float *dequant, int64_t rows,
                                     int64_t cols, hipStream_t s)
 {
@@ -990,22 +1026,25 @@ hipError_t launch_mx_tokens_transpose(const uint8_t *q, const uint8_t *scales, c
 
 hipError_t launch_mx_tokens_quant_t(const uint16_t *x, const int64_t *lens, const int64_t *offs, int G, int64_t M,
                                     int64_t C, int fmt, uint8_t *qt, int64_t pitch, uint32_t *st, int *plan,
-                                    uint32_t *err, hipStream_t s)
+                                    uint32_t *err, const uint32_t *amax, float *dequant, hipStream_t s)
 {
     if (G == 0 || C == 0) return hipSuccess;
-    const int ts = fmt == 0 ? 128 : 256;
+    const int ts = fmt == 1 ? 256 : 128;
     const size_t lds = table_bytes(G) + 4 * (G + 1) + 32 + 16 + (size_t)ts * TB_RS;
-    const int64_t items = mx_wgrad_stages(M, G, fmt) * ((C + kTrCh - 1) / kTrCh);
+    const int64_t items = mx_wgrad_stages(M, G, fmt == 1 ? 1 : 0) * ((C + kTrCh - 1) / kTrCh);
     // as many workgroups as fit beside each other (LDS: 45 or 79 KiB each)
-    int64_t grid = (int64_t)device_cus() * (fmt == 0 ? 3 : 2);
+    int64_t grid = (int64_t)device_cus() * (fmt == 1 ? 2 : 3);
     if (grid > items) grid = items;
     if (grid < 1) grid = 1;
     if (fmt == 0)
         hipLaunchKernelGGL(mx_tokens_quant_t_kernel<0>, dim3((unsigned)grid), dim3(kThreads), lds, s, x, lens, offs,
-                           G, M, (int)C, qt, pitch, st, plan, err);
-    else
+                           G, M, (int)C, qt, pitch, st, plan, err, amax, dequant);
+    else if (fmt == 1)
         hipLaunchKernelGGL(mx_tokens_quant_t_kernel<1>, dim3((unsigned)grid), dim3(kThreads), lds, s, x, lens, offs,
-                           G, M, (int)C, qt, pitch, st, plan, err);
+                           G, M, (int)C, qt, pitch, st, plan, err, amax, dequant);
+    else
+        hipLaunchKernelGGL(mx_tokens_quant_t_kernel<2>, dim3((unsigned)grid), dim3(kThreads), lds, s, x, lens, offs,
+                           G, M, (int)C, qt, pitch, st, plan, err, amax, dequant);
     return hipGetLastError();
 }
 

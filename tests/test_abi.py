@@ -113,10 +113,11 @@ def test_workspace_sizes_host_only():
                     r256(stages * n_ * wpr * 4) + split(m_, n_, k_))
             assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, g_, m_, n_, k_, dt) == want, (dt, g_, m_)
     # FP8 with one factor per tensor: the plan and both gradients' transposed
-    # codes as for MXFP8 (no scale words, no split)
+    # codes as for MXFP8 (no scale words, no split), then 256 bytes for the
+    # amax words and factors of pt_grouped_gemm_wgrad_quantize
     pitch8 = -(-32 * (M // 32 + G) // 128) * 128
     assert (pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, G, M, N, K, pt.PT_FP8_E4M3) ==
-            base + r256(8 * G) + r256(K * pitch8) + r256(N * pitch8))
+            base + r256(8 * G) + r256(K * pitch8) + r256(N * pitch8) + 256)
     # one output tile per expert and 14030 rows: 512-token chunks, 27 slots
     assert pt.pt_grouped_gemm_workspace_size(pt.PT_OP_WGRAD, 7, 14030, 256, 256, pt.PT_BF16) == \
         base + 27 * 256 * 256 * 4
@@ -154,6 +155,7 @@ def test_argument_checks_host_only():
     assert W(mp, mp, mp, lp, None, 4, 10, 64, 64, 1, 2, 1, None, 0, None) == 1          # trans_out
     assert W(mp, mp, mp, lp, None, 4, 10, 64, 64, 1, 0, 2, None, 0, None) == 1          # accumulate
     assert W(mp, mp, mp, lp, None, 4, 10, 64, 64, 0, 0, 1, None, 0, None) == 2          # BF16
+    assert W(mp, mp, mp, lp, None, 4, 10, 64, 64, 4, 0, 1, None, 0, None) == 2          # FP8 row factors
     assert W(mp, mp, mp, lp, None, 4, 10, 64, 60, 2, 0, 1, None, 0, None) == 2          # K % 8
 
 

@@ -1,8 +1,9 @@
-"""GPU checks of pt_grouped_gemm_wgrad_quantize, the MX weight gradient
-from bf16 gradients: quantisation along tokens fused into the transpose to
-the weight gradient's operand layout.  main_grad must come out bit-identical
-to pt_mx_quantize_tokens on both gradients followed by pt_grouped_gemm_wgrad
-(itself checked against the oracle), for both formats, both output layouts,
+"""GPU checks of pt_grouped_gemm_wgrad_quantize, the low-precision weight
+gradient from bf16 gradients: quantisation fused into the transpose to the
+weight gradient's operand layout.  main_grad must come out bit-identical to
+pt_mx_quantize_tokens (MXFP8, MXFP4) or pt_fp8_quantize (FP8 with one factor
+per tensor, whose amax covers every row) on both gradients followed by
+pt_grouped_gemm_wgrad (itself checked against the oracle), in both output layouts,
 accumulating and overwriting, with empty, single-row, partial-block and
 multi-stage experts, explicit offsets with unowned rows between experts,
 the split reduction, and channel counts that leave a partial 128-channel
@@ -117,6 +118,60 @@ def test_fused_split_reduction(dev, fmt):
     ref = two_step(dev, a, dy, lens, None, N, K, fmt, 0, 1, main_grad0(dev, G, N, K, 0, 422),
                    workspace(dev, G, M, N, K, fmt))
     got = fused(dev, a, dy, lens, None, N, K, fmt, 0, 1, main_grad0(dev, G, N, K, 0, 422),
+                workspace(dev, G, M, N, K, fmt))
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+
+
+def two_step_fp8(dev, a, dy, lens, offs, N, K, trans_out, accumulate, mg, ws):
+    M, G = a.shape[0], len(lens)
+    aq = torch.zeros((M, K), dtype=torch.uint8, device=dev)
+    dq = torch.zeros((M, N), dtype=torch.uint8, device=dev)
+    ma, fa, md, fd = (torch.zeros((1,), dtype=torch.float32, device=dev) for _ in range(4))
+    ptm.pt_fp8_quantize(a, aq, ma, fa, 1, M, K)
+    ptm.pt_fp8_quantize(dy, dq, md, fd, 1, M, N)
+    ptm.pt_grouped_gemm_wgrad(aq, fa, dq, fd, mg, dev_i64(lens, dev), None if offs is None else dev_i64(offs, dev),
+                              G, M, N, K, ptm.PT_FP8_E4M3, trans_out, accumulate, workspace=ws)
+    torch.cuda.synchronize()
+    return mg
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("trans_out", [0, 1])
+@pytest.mark.parametrize("accumulate", [1, 0])
+def test_fused_fp8_equals_quantize_then_wgrad(dev, case, trans_out, accumulate):
+    # FP8 with one factor per tensor: amax over the whole tensors, codes
+    # straight into the transposed layout
+    name, lens, K, N = case
+    lens = np.array(lens, np.int64)
+    M, G = int(lens.sum()), len(lens)
+    fmt = ptm.PT_FP8_E4M3
+    print(f"wgrad_quantize fp8 {name} trans_out={trans_out} acc={accumulate}", flush=True)
+    a = synth.randn_bf16((M, K), seed=430, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    dy = synth.randn_bf16((M, N), seed=431, std=1e-2, device=dev)
+    ref = two_step_fp8(dev, a, dy, lens, None, N, K, trans_out, accumulate, main_grad0(dev, G, N, K, trans_out, 432),
+                       workspace(dev, G, M, N, K, fmt))
+    ws = workspace(dev, G, M, N, K, fmt, extra=4096)
+    got = fused(dev, a, dy, lens, None, N, K, fmt, trans_out, accumulate, main_grad0(dev, G, N, K, trans_out, 432),
+                ws)
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    n = ws.numel() - 4096
+    assert (ws[n:].cpu().numpy() == 0xA5).all(), "write past the workspace"
+
+
+def test_fused_fp8_amax_covers_unowned_rows(dev):
+    # the tensor factor comes from every row, owned by an expert or not (as
+    # pt_fp8_quantize over the whole tensor): a large value in a row between
+    # experts changes every code
+    lens = np.array([40, 0, 97, 3], np.int64)
+    offs = np.array([2, 50, 50, 160, 170], np.int64)
+    M, G, K, N = 180, len(lens), 96, 72
+    fmt = ptm.PT_FP8_E4M3
+    a = synth.randn_bf16((M, K), seed=440, device=dev)
+    a[45, 7] = 300.0                                  # row 45 belongs to no expert
+    dy = synth.randn_bf16((M, N), seed=441, std=1e-2, device=dev)
+    ref = two_step_fp8(dev, a, dy, lens, offs, N, K, 0, 1, main_grad0(dev, G, N, K, 0, 442),
+                       workspace(dev, G, M, N, K, fmt))
+    got = fused(dev, a, dy, lens, offs, N, K, fmt, 0, 1, main_grad0(dev, G, N, K, 0, 442),
                 workspace(dev, G, M, N, K, fmt))
     assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
 
