@@ -4,7 +4,7 @@ next to each kernel's operand ring, so every kernel family is run: the BF16
 forward (both weight layouts, plain and SwiGLU epilogues, every kernel
 configuration and both tile orders), the dgrad, the weight gradient (with
 and without the split-reduction workspace), and the MXFP8 / MXFP4 forward
-and weight gradient.
+and weight gradient (also from bf16 with the fused quantisation).
 The routing mixes empty experts, single rows, experts under one tile and a
 few over two tiles."""
 import numpy as np
@@ -194,3 +194,9 @@ def test_mx_wgrad_max_groups(orc, dev, fmt, name):
             continue
         D = av[offs[e]:offs[e + 1]].T @ dv[offs[e]:offs[e + 1]]
         assert floored_rel_err(after[e].astype(np.float64) - before[e], D) <= BF16_TOL, e
+    # the same from bf16 in one call (quantisation fused into the transpose):
+    # bit-identical
+    mg2 = torch.as_tensor(before, device=dev)
+    ptm.pt_grouped_gemm_wgrad_quantize(a, dy, mg2, lens_d, None, G, M, N, K, fmt, 0, 1, workspace=ws)
+    torch.cuda.synchronize()
+    assert (mg2.cpu().numpy().view(np.int32) == after.view(np.int32)).all()
