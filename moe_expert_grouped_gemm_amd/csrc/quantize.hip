@@ -177,7 +177,25 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_cols_kernel(const uint16
 // 64 x 64 tiles two workgroups wrote the halves of each run.
 // R % 32 == 0, C % 8 == 0.
 constexpr int TB = 128;                // tile rows and columns
-constexpr int TB_RS = TB * 2 + 4;      // LDS row stride (bytes), padded off the bank period
+constexpr int TB_RS = TB * 2;          // LDS row stride (bytes): 16 chunks of 16
+
+// LDS tiles of bf16 rows, 256 bytes each: 16-byte chunk c of row r sits at
+// chunk position c ^ ((r / 8) % 16).  The readers take one column per 16
+// lanes (lane l: rows 8 l .. 8 l + 7, four columns per wave), so the 16 rows
+// a read instruction touches for one column fall in 16 different chunks:
+// 64 distinct banks, where a padded row stride left rows 8 apart two to a
+// bank (40% of the LDS cycles of the fused token quantiser in conflicts;
+// the kernels' times did not move, they wait on memory).  Rows stay whole
+// 16-byte chunks, so the row-wise 16-byte writes are unchanged.
+__device__ __forceinline__ uint8_t *tb_chunk(uint8_t *tile, int r, int c)
+{
+    return tile + r * TB_RS + 16 * (c ^ ((r >> 3) & 15));
+}
+// bf16 element (r, col) of such a tile
+__device__ __forceinline__ uint32_t tb_elem(const uint8_t *tile, int r, int col)
+{
+    return *(const uint16_t *)(tile + r * TB_RS + 16 * ((col >> 3) ^ ((r >> 3) & 15)) + (col & 7) * 2);
+}
 
 // This thread's eight 16-byte row chunks of a 128 x 128 tile (zeros outside
 // x_b): chunk k = threadIdx.x + j * kThreads is row k / 16, columns
@@ -200,7 +218,7 @@ __device__ __forceinline__ void rows_to_lds_tb(const uintx4 (&v)[8], uint8_t *ti
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int k = threadIdx.x + j * kThreads;
-        uint32_t *d = (uint32_t *)(tile + (k >> 4) * TB_RS + (k & 15) * 16);
+        uint32_t *d = (uint32_t *)tb_chunk(tile, k >> 4, k & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) d[e] = v[j][e];
     }
@@ -223,8 +241,8 @@ __device__ __forceinline__ void quantise_t_tile(const uint8_t *tile, uint8_t *qb
         uintx4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = *(const uint16_t *)(tile + (rr + 2 * e) * TB_RS + col * 2);
-            const uint32_t hi = *(const uint16_t *)(tile + (rr + 2 * e + 1) * TB_RS + col * 2);
+            const uint32_t lo = tb_elem(tile, rr + 2 * e, col);
+            const uint32_t hi = tb_elem(tile, rr + 2 * e + 1, col);
             w[e] = lo | (hi << 16);
         }
         if (c0 + col < C && r0 + (rr & ~31) < R) quantise8<FMT, false>(w, qb, sb, (c0 + col) * RB + (r0 + rr) / 8);
@@ -710,7 +728,7 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_t_kernel(
     };
     // tokens r0 .. r0 + TS - 1, channels c0 .. c0 + 127 into registers (the
     // next item's loads fly while the current one is encoded), then to LDS
-    // rows of TB_RS bytes
+    // rows (tb_chunk)
     constexpr int NL = TS * 16 / kThreads;
     uintx4 v[NL];
     auto load = [&](const Item &it) {
@@ -730,7 +748,7 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_t_kernel(
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             const int k = tid + j * kThreads;
-            uint32_t *d = (uint32_t *)(tile + (k >> 4) * TB_RS + (k & 15) * 16);
+            uint32_t *d = (uint32_t *)tb_chunk(tile, k >> 4, k & 15);
 #pragma unroll
             for (int e = 0; e < 4; ++e) d[e] = v[j][e];
         }
@@ -750,8 +768,8 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_t_kernel(
             uintx4 q8;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t lo16 = *(const uint16_t *)(tile + (tt + 2 * e) * TB_RS + col * 2);
-                const uint32_t hi16 = *(const uint16_t *)(tile + (tt + 2 * e + 1) * TB_RS + col * 2);
+                const uint32_t lo16 = tb_elem(tile, tt + 2 * e, col);
+                const uint32_t hi16 = tb_elem(tile, tt + 2 * e + 1, col);
                 q8[e] = lo16 | (hi16 << 16);
             }
             uint8_t *qrow = qt + (int64_t)(it.c0 + col) * pitch + it.ob;
@@ -850,8 +868,8 @@ __global__ __launch_bounds__(kThreads) void stack_experts_kernel(const void *con
             uintx4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = *(const uint16_t *)(tile + (r8 + 2 * e) * TB_RS + oc * 2);
-                const uint32_t hi = *(const uint16_t *)(tile + (r8 + 2 * e + 1) * TB_RS + oc * 2);
+                const uint32_t lo = tb_elem(tile, r8 + 2 * e, oc);
+                const uint32_t hi = tb_elem(tile, r8 + 2 * e + 1, oc);
                 o[e] = lo | (hi << 16);
             }
             __builtin_nontemporal_store(o, (uintx4 *)(out + (g * C + c0 + oc) * R + r0 + r8));
