@@ -1050,8 +1050,10 @@ hipError_t launch_mx_tokens_quant_t(const uint16_t *x, const int64_t *lens, cons
     const int ts = fmt == 1 ? 256 : 128;
     const size_t lds = table_bytes(G) + 4 * (G + 1) + 32 + 16 + (size_t)ts * TB_RS;
     const int64_t items = mx_wgrad_stages(M, G, fmt == 1 ? 1 : 0) * ((C + kTrCh - 1) / kTrCh);
-    // as many workgroups as fit beside each other (LDS: 45 or 79 KiB each)
-    int64_t grid = (int64_t)device_cus() * (fmt == 1 ? 2 : 3);
+    // as many workgroups per CU as fit beside each other in LDS (160 KiB), at
+    // most four (four waves per SIMD)
+    const int64_t per_cu = std::min<int64_t>(4, (int64_t)(160 * 1024) / (int64_t)lds);
+    int64_t grid = (int64_t)device_cus() * std::max<int64_t>(1, per_cu);
     if (grid > items) grid = items;
     if (grid < 1) grid = 1;
     if (fmt == 0)
