@@ -176,6 +176,23 @@ def test_fused_fp8_amax_covers_unowned_rows(dev):
     assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
 
 
+@pytest.mark.parametrize("fmt", FMTS + [ptm.PT_FP8_E4M3], ids=FMT_IDS + ["fp8"])
+def test_fused_no_tokens(dev, fmt):
+    # every expert empty (M = 0): main_grad untouched when accumulating,
+    # zeroed when not
+    G, K, N = 3, 64, 48
+    lens = np.zeros(G, np.int64)
+    a = torch.empty((0, K), dtype=torch.bfloat16, device=dev)
+    dy = torch.empty((0, N), dtype=torch.bfloat16, device=dev)
+    ws = workspace(dev, G, 0, N, K, fmt)
+    mg = main_grad0(dev, G, N, K, 0, 450)
+    before = mg.clone()
+    fused(dev, a, dy, lens, None, N, K, fmt, 0, 1, mg, ws)
+    assert torch.equal(mg, before)
+    fused(dev, a, dy, lens, None, N, K, fmt, 0, 0, mg, ws)
+    assert (mg == 0).all()
+
+
 def test_fused_argument_errors(dev):
     lens = dev_i64([4, 4], dev)
     a = torch.zeros((8, 16), dtype=torch.bfloat16, device=dev)
