@@ -89,6 +89,17 @@ TRAFFIC_KEYS = {
     "fc2_bf16_dgrad_swiglu_bwd": ["fc2_bf16_dgrad_swiglu_bwd"],
     "fc2_mxfp8_dgrad_swiglu_bwd": ["fc2_mxfp8_dgrad_swiglu_bwd"],
     "fc2_mxfp4_dgrad_swiglu_bwd": ["fc2_mxfp4_dgrad_swiglu_bwd"],
+    "fc1_bf16_swiglu_clamped": ["fc1_bf16_swiglu_clamped"],
+    "fc1_bf16_swiglu_save": ["fc1_bf16_swiglu_save"],
+    "ep8_share_bf16_fc1_swiglu": ["ep8_share_bf16_fc1_swiglu"],
+    # the activation's (or output gradient's) quantise passes, then the GEMM
+    "cfg3_fp8_tensor_fwd": ["cfg3_fp8_amax_A", "cfg3_fp8_encode_A", "cfg3_fp8_tensor_fwd_gemm"],
+    "cfg3_fp8_rowwise_fwd": ["cfg3_fp8_rows_A", "cfg3_fp8_rowwise_fwd_gemm"],
+    "cfg3_fp8_tensor_dgrad": ["cfg3_fp8_amax_dY", "cfg3_fp8_encode_dY", "cfg3_fp8_tensor_dgrad_gemm"],
+    "cfg3_fp8_rowwise_dgrad": ["cfg3_fp8_rows_dY", "cfg3_fp8_rowwise_dgrad_gemm"],
+    "cfg3_mxfp8_dgrad": ["cfg3_mx_quantize_e4m3_dY", "cfg3_mxfp8_dgrad_gemm"],
+    "stack_experts_transpose": ["stack_experts_transpose"],
+    "stack_experts_mxfp8_caches": ["stack_experts_mxfp8_caches"],
 }
 
 
