@@ -344,7 +344,8 @@ __global__ __launch_bounds__(kThreads) void fp8_encode_kernel(const uint16_t *__
 }
 
 // One scale per row: a wave per row, one pass for the amax (a wave
-// reduction, no atomics) and one for the codes (the row is then in L2).
+// reduction, no atomics) and one for the codes, which reads the row again
+// (rows longer than 8192 values; shorter ones take the kernel below).
 __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(const uint16_t *__restrict__ x, uint8_t *__restrict__ q,
                                                             float *amax, float *dequant, int64_t rows, int64_t cols)
 {
@@ -374,6 +375,56 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(const uint16_t *__re
         for (int i = 0; i < 4; ++i) {
             f[2 * i] = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(v[i] & 0xFFFFu) * s, -448.0f), 448.0f);
             f[2 * i + 1] = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(v[i] >> 16) * s, -448.0f), 448.0f);
+        }
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
+        __builtin_nontemporal_store(uintx2{(uint32_t)w0, (uint32_t)w1}, (uintx2 *)(qr + c));
+    }
+}
+
+// The same with the row held in registers between the two passes, for rows
+// of at most R·512 values: x is read from HBM once (rows of 5760 values re-read
+// half their bytes when the second pass went back to L2, with up to 32 rows in
+// flight per CU and an L2 shared by 32 CUs).
+template <int R>
+__global__ __launch_bounds__(kThreads) void fp8_rows_reg_kernel(const uint16_t *__restrict__ x, uint8_t *__restrict__ q,
+                                                                float *amax, float *dequant, int64_t rows, int64_t cols)
+{
+    const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const uint16_t *xr = x + r * cols;
+    uintx4 v[R];
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t c = lane * 8 + j * 512;
+        v[j] = c < cols ? __builtin_nontemporal_load((const uintx4 *)(xr + c)) : uintx4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, max(v[j][i] & 0x7FFFu, (v[j][i] >> 16) & 0x7FFFu));
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+    const float mf = __uint_as_float(m << 16);
+    const float s = fp8_tensor_scale(mf);
+    if (lane == 0) {
+        amax[r] = mf;
+        dequant[r] = 1.0f / s;
+    }
+    uint8_t *qr = q + r * cols;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t c = lane * 8 + j * 512;
+        if (c >= cols) break;
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(v[j][i] & 0xFFFFu) * s, -448.0f), 448.0f);
+            f[2 * i + 1] = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(v[j][i] >> 16) * s, -448.0f), 448.0f);
         }
         int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
@@ -1004,7 +1055,17 @@ hipError_t launch_fp8_quantize_rows(const uint16_t *x, uint8_t *q, float *amax, 
 {
     if (rows == 0 || cols == 0) return hipSuccess;
     const int64_t grid = (rows + kThreads / 64 - 1) / (kThreads / 64);
-    hipLaunchKernelGGL(fp8_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, amax, dequant, rows, cols);
+    const dim3 g((unsigned)grid), b(kThreads);
+    if (cols <= 4 * 512)
+        hipLaunchKernelGGL(fp8_rows_reg_kernel<4>, g, b, 0, s, x, q, amax, dequant, rows, cols);
+    else if (cols <= 8 * 512)
+        hipLaunchKernelGGL(fp8_rows_reg_kernel<8>, g, b, 0, s, x, q, amax, dequant, rows, cols);
+    else if (cols <= 12 * 512)
+        hipLaunchKernelGGL(fp8_rows_reg_kernel<12>, g, b, 0, s, x, q, amax, dequant, rows, cols);
+    else if (cols <= 16 * 512)
+        hipLaunchKernelGGL(fp8_rows_reg_kernel<16>, g, b, 0, s, x, q, amax, dequant, rows, cols);
+    else
+        hipLaunchKernelGGL(fp8_rows_kernel, g, b, 0, s, x, q, amax, dequant, rows, cols);
     return hipGetLastError();
 }
 

@@ -182,7 +182,11 @@ def fp8_quantize_rows(dev, x2d):
     return q, amax, deq
 
 
-@pytest.mark.parametrize("rows,cols", [(1000, 2880), (7, 8), (3, 600)], ids=["rows1000", "tiny", "odd512"])
+# widths for each register-held row length (up to 2048, 4096, 6144 and 8192
+# values) and past them (the two-pass kernel), each with a partial last chunk
+@pytest.mark.parametrize("rows,cols", [(1000, 2880), (7, 8), (3, 600), (9, 2048), (5, 5760), (6, 8192), (5, 8200),
+                                       (3, 12296)],
+                         ids=["rows1000", "tiny", "odd512", "w2048", "w5760", "w8192", "w8200", "w12296"])
 def test_fp8_quantize_rows_bit_exact(orc, dev, rows, cols):
     x = synth.randn_bf16((rows, cols), seed=90, device=dev, outlier_frac=0.01, outlier_mult=50.0)
     x[0] = 0                                                   # an all-zero row
