@@ -308,8 +308,17 @@ __global__ __launch_bounds__(kThreads) void fp8_amax_kernel(const uint16_t *__re
     }
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
-    // bf16 magnitude bits -> fp32 bits of the same value
-    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_max(amax + b, m << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // one atomic per workgroup: the waves' maxima meet in LDS first (the
+    // device-wide atomics on one word serialise, and most waves finish at once)
+    __shared__ uint32_t wave_max[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) m = max(m, wave_max[w]);
+        // bf16 magnitude bits -> fp32 bits of the same value
+        __hip_atomic_fetch_max(amax + b, m << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 __device__ __forceinline__ float fp8_tensor_scale(float amax)
