@@ -748,7 +748,9 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_t_kernel(
     tokens_table(tab, sm_tok, lens, offs, G, M, err);
     int *sst = tab.tile0 + G + 1 + 8;                   // each expert's first stage, [G + 1]
     int *scr = sst + G + 1;
-    uint8_t *tile = (uint8_t *)(((uintptr_t)(scr + 8) + 15) & ~(uintptr_t)15);
+    // the tile at the next 16-byte boundary, as an offset from the aligned base
+    // (so that the compiler can prove the alignment of its 16-byte accesses)
+    uint8_t *tile = (uint8_t *)(sm_tok + ((int)(scr + 8 - sm_tok) + 3 & ~3));
     {
         const int per = (G + kThreads - 1) / kThreads, g0 = threadIdx.x * per;
         int sum = 0;
@@ -821,10 +823,10 @@ __global__ __launch_bounds__(kThreads) void mx_tokens_quant_t_kernel(
     for (; w < items; w += gridDim.x) {
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
+            // one 16-byte LDS write per chunk (the tile is 16-byte aligned; as
+            // four 4-byte writes, the four rows of a wave met on 16 banks)
             const int k = tid + j * kThreads;
-            uint32_t *d = (uint32_t *)tb_chunk(tile, k >> 4, k & 15);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) d[e] = v[j][e];
+            *(uintx4 *)tb_chunk(tile, k >> 4, k & 15) = v[j];
         }
         __syncthreads();
         const Item it = cur;
