@@ -85,6 +85,10 @@ TRAFFIC_KEYS = {
     # A and dY each quantised along tokens and transposed (per-launch means), then the weight gradient
     "cfg3_mxfp8_wgrad": ["cfg3_mx_tokens_quant", "cfg3_mx_tokens_quant", "cfg3_mx_wgrad_transpose",
                          "cfg3_mx_wgrad_transpose", "cfg3_mxfp8_wgrad"],
+    # the two-pass tensor quantise of A and dY, their transposes, the weight gradient
+    "cfg3_fp8_tensor_wgrad": ["cfg3_fp8_wgrad_amax", "cfg3_fp8_wgrad_amax", "cfg3_fp8_wgrad_encode",
+                              "cfg3_fp8_wgrad_encode", "cfg3_mx_wgrad_transpose", "cfg3_mx_wgrad_transpose",
+                              "cfg3_fp8_tensor_wgrad_gemm"],
     "cfg4_mxfp4_mlp": ["cfg4_mx_quantize_e2m1_X", "cfg4_mxfp4_fc1_swiglu_mxfp4", "cfg4_mxfp4_fc2"],
     "fc2_bf16_dgrad_swiglu_bwd": ["fc2_bf16_dgrad_swiglu_bwd"],
     "fc2_mxfp8_dgrad_swiglu_bwd": ["fc2_mxfp8_dgrad_swiglu_bwd"],
