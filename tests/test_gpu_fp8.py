@@ -39,6 +39,29 @@ def test_fp8_quantize_bit_exact(orc, dev, shape, std):
     assert (u8(q).reshape(shape[0], -1) == rq).all()
 
 
+# The tensor amax pass: threads take 16-byte chunks a grid apart, four at a
+# time then one at a time, and a workgroup's four waves meet in LDS before one
+# atomic.  A single spike in batch 1 at positions that land in each of those
+# places (another wave of workgroup 0, the fourth load of a group, the
+# one-at-a-time tail, the last element) must come out as that batch's amax;
+# the other batches keep their own.
+S = 2048 * 256                       # chunks per grid pass (8 workgroups per CU, 256 CUs)
+
+
+@pytest.mark.parametrize("pos", [0, 512 + 3, 3 * 512 + 5, (3 * S + 100) * 8 + 1, (4 * S + 700) * 8 + 7, -1],
+                         ids=["first", "wave1", "wave3", "fourth_load", "tail", "last"])
+@pytest.mark.parametrize("sign", [1.0, -1.0], ids=["pos", "neg"])
+def test_fp8_amax_spike_positions(dev, pos, sign):
+    print(f"fp8 amax spike pos={pos} sign={sign}", flush=True)
+    x = synth.randn_bf16((3, 8192, 2880), seed=92, device=dev)
+    flat = x[1].reshape(-1)
+    flat[pos] = sign * 768.0                           # exact in bf16, far above any N(0, 1) draw
+    q, amax, deq = fp8_quantize(dev, x)
+    assert amax[1].item() == 768.0
+    for b in (0, 2):
+        assert amax[b].item() == x[b].abs().max().float().item()
+
+
 def test_fp8_quantize_zero_matrix_and_repeat(orc, dev):
     x = torch.zeros((2, 64, 64), dtype=torch.bfloat16, device=dev)
     x[1] = synth.randn_bf16((64, 64), seed=81, device=dev)
