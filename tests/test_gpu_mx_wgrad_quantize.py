@@ -204,3 +204,25 @@ def test_fused_argument_errors(dev):
     with pytest.raises(ptm.PtggError, match="WORKSPACE"):
         ptm.pt_grouped_gemm_wgrad_quantize(a, dy, mg, lens, None, 2, 8, 16, 16, ptm.PT_MXFP8_E4M3, 0, 1,
                                            workspace=ws[:64])
+
+
+@pytest.mark.parametrize("fmt", [ptm.PT_MXFP8_E4M3, ptm.PT_FP8_E4M3], ids=["e4m3", "fp8"])
+def test_fused_full_config3_shape(dev, fmt):
+    # the MXFP8 weight-gradient workload at full size (32 experts with Zipf
+    # routing, 65536 tokens, K = 2880, N = 5760, accumulating into [G, K, N]),
+    # as the benchmark times it: every element of main_grad bit-identical to
+    # the two-step path (which the sampled full-size oracle tests pin)
+    lens = synth.lens_zipf_distinct(16384, 32, 4, 1.1, seed=3)
+    M, G, K, N = int(lens.sum()), len(lens), 2880, 5760
+    print(f"wgrad_quantize full config-3 shape fmt={fmt} M={M}", flush=True)
+    a = synth.randn_bf16((M, K), seed=104, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    dy = synth.randn_bf16((M, N), seed=106, std=1e-2, device=dev)
+    ws = workspace(dev, G, M, N, K, fmt)
+    mg_ref = main_grad0(dev, G, N, K, 0, seed=460)
+    mg = mg_ref.clone()
+    if fmt == ptm.PT_FP8_E4M3:
+        two_step_fp8(dev, a, dy, lens, None, N, K, 0, 1, mg_ref, ws)
+    else:
+        two_step(dev, a, dy, lens, None, N, K, fmt, 0, 1, mg_ref, ws)
+    fused(dev, a, dy, lens, None, N, K, fmt, 0, 1, mg, ws)
+    assert torch.equal(mg, mg_ref)
