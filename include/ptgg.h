@@ -151,6 +151,36 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * pt_grouped_gemm_fwd for the MX and FP8 dtypes with code rows of A [M, ...]
+ * and of B [G, N, ...] stored code_pitch bytes apart (as
+ * pt_mx_quantize_pitched writes them) instead of packed; trans_b is 1 (the
+ * weights' codes are reduction-contiguous).  Same operation and passages as
+ * pt_grouped_gemm_fwd, and bit-identical results for the same codes: only
+ * where each code row starts changes.  A row pitch that is a multiple of
+ * 128 bytes starts every row on a cache line, so the kernel's 128-byte
+ * reduction stages read whole lines (a 2880-byte pitch starts every other row
+ * half-way into one).  The bytes past a row's codes are never read.
+ *  dtype      PT_MXFP8_E4M3, PT_MXFP4_E2M1, PT_FP8_E4M3 or PT_FP8_E4M3_ROWWISE;
+ *             PT_BF16 gives PT_ERR_UNSUPPORTED.
+ *  code_pitch bytes between code rows of both A and B: at least K (E4M3) or
+ *             K/2 (E2M1) and a multiple of 16, else PT_ERR_INVALID_ARG.  a
+ *             holds (M - 1) * code_pitch + the row's code bytes, b
+ *             (G * N - 1) * code_pitch + the row's code bytes.  Scales as
+ *             pt_grouped_gemm_fwd (packed).
+ *  Runs on the 256 x 256 kernel only: MXFP4 with K % 256 != 0 also needs
+ *  the workspace's stage-major scale copies (else PT_ERR_UNSUPPORTED), and
+ *  configurations 2 and 3 of pt_set_gemm_config fall back to 0 and 1.
+ *  Other arguments, requirements and errors as pt_grouped_gemm_fwd.
+ */
+int pt_grouped_gemm_fwd_pitched(const void *a, const uint8_t *a_scale,
+                                const void *b, const uint8_t *b_scale,
+                                void *out, uint8_t *out_scale,
+                                const int64_t *group_lens, const int64_t *group_offs,
+                                int64_t G, int64_t M, int64_t N, int64_t K,
+                                int dtype, int epilogue, float swiglu_limit, int64_t code_pitch,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pt_grouped_gemm_fwd without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, results and
@@ -395,6 +425,22 @@ int pt_grouped_gemm_wgrad_quantize(const void *a, const void *dy, float *main_gr
  */
 int pt_mx_quantize(const void *x, void *q, uint8_t *scales,
                    int64_t rows, int64_t cols, int dtype, int axis, void *stream);
+
+/*
+ * pt_mx_quantize along the columns (axis 1) into code rows q_pitch bytes
+ * apart instead of packed: row r's codes are bytes [r * q_pitch, r * q_pitch
+ * + cols) of q (E4M3) or [r * q_pitch, r * q_pitch + cols/2) (E2M1), the
+ * same bytes pt_mx_quantize writes to its row r; the rest of each row is not
+ * written.  scales as pt_mx_quantize (packed [rows, cols/32]).  The operand
+ * layout for pt_grouped_gemm_fwd_pitched (same MX rule and passages as
+ * pt_mx_quantize; the pitch is a storage choice, not part of the method).
+ *  q_pitch  bytes between code rows: at least the row's code bytes and a
+ *           multiple of 16, else PT_ERR_INVALID_ARG.  q holds
+ *           (rows - 1) * q_pitch + the row's code bytes, 16-byte aligned.
+ *  Other requirements and errors as pt_mx_quantize with axis = 1.
+ */
+int pt_mx_quantize_pitched(const void *x, void *q, uint8_t *scales,
+                           int64_t rows, int64_t cols, int dtype, int64_t q_pitch, void *stream);
 
 /*
  * Transposing OCP-MX quantisation, the transposed weight cache of the MX

@@ -24,7 +24,8 @@ __all__ = [
     "load", "lib_path", "PtggError",
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu",
     "pt_grouped_gemm_wgrad", "pt_grouped_gemm_wgrad_quantize", "pt_grouped_gemm_fwd_swiglu_save",
-    "pt_grouped_gemm_fwd_noalloc", "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
+    "pt_grouped_gemm_fwd_noalloc", "pt_grouped_gemm_fwd_pitched", "pt_mx_quantize", "pt_mx_quantize_pitched",
+    "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts", "expert_addresses",
     "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning", "PT_CONFIG_RULES", "PT_CONFIG_TUNE",
     "PT_OP_DGRAD_SWIGLU", "PT_MAX_GROUPS",
@@ -40,7 +41,7 @@ PT_MAX_GROUPS = 1024
 EXPORTS = (
     "pt_grouped_gemm_fwd", "pt_grouped_gemm_dgrad", "pt_grouped_gemm_dgrad_swiglu", "pt_grouped_gemm_wgrad",
     "pt_grouped_gemm_wgrad_quantize", "pt_grouped_gemm_fwd_swiglu_save", "pt_grouped_gemm_fwd_noalloc",
-    "pt_mx_quantize", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
+    "pt_grouped_gemm_fwd_pitched", "pt_mx_quantize", "pt_mx_quantize_pitched", "pt_mx_quantize_t", "pt_mx_quantize_tokens", "pt_fp8_quantize", "pt_fp8_quantize_rows",
     "pt_stack_experts", "pt_mx_quantize_experts",
     "pt_set_gemm_config", "pt_gemm_config_of", "pt_clear_gemm_tuning",
     "pt_grouped_gemm_workspace_size", "pt_read_error_flags", "pt_status_string", "pt_version",
@@ -84,6 +85,10 @@ def load(require_gpu: bool = True):
     L.pt_grouped_gemm_wgrad_quantize.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, i32, i32, p, sz, p]
     L.pt_mx_quantize.restype = i32
     L.pt_mx_quantize.argtypes = [p, p, p, i64, i64, i32, i32, p]
+    L.pt_mx_quantize_pitched.restype = i32
+    L.pt_mx_quantize_pitched.argtypes = [p, p, p, i64, i64, i32, i64, p]
+    L.pt_grouped_gemm_fwd_pitched.restype = i32
+    L.pt_grouped_gemm_fwd_pitched.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, f32, i64, p, sz, p]
     L.pt_mx_quantize_t.restype = i32
     L.pt_mx_quantize_t.argtypes = [p, p, p, i64, i64, i64, i32, p]
     L.pt_fp8_quantize.restype = i32
@@ -211,6 +216,22 @@ def pt_mx_quantize(x, q, scales, rows, cols, dtype, axis=1, stream=None):
     L = load()
     _check("pt_mx_quantize", L.pt_mx_quantize(
         _ptr(x), _ptr(q), _ptr(scales), rows, cols, dtype, axis, _stream(stream)))
+
+
+def pt_mx_quantize_pitched(x, q, scales, rows, cols, dtype, q_pitch, stream=None):
+    L = load()
+    _check("pt_mx_quantize_pitched", L.pt_mx_quantize_pitched(
+        _ptr(x), _ptr(q), _ptr(scales), rows, cols, dtype, q_pitch, _stream(stream)))
+
+
+def pt_grouped_gemm_fwd_pitched(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs,
+                                G, M, N, K, dtype, epilogue, code_pitch, workspace=None, stream=None,
+                                swiglu_limit=0.0):
+    L = load()
+    _check("pt_grouped_gemm_fwd_pitched", L.pt_grouped_gemm_fwd_pitched(
+        _ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), _ptr(out), _ptr(out_scale),
+        _ptr(group_lens), _ptr(group_offs), G, M, N, K, dtype, epilogue, swiglu_limit, code_pitch,
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def pt_mx_quantize_t(x, q, scales, batch, rows, cols, dtype, stream=None):

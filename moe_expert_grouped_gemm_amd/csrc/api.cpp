@@ -273,7 +273,7 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
                    uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
                    int64_t N, int64_t K, int dtype, int ep, int64_t Nc, int64_t ldo, float swiglu_limit,
                    void *workspace, size_t workspace_bytes, hipStream_t s, uint16_t *save = nullptr,
-                   bool timing = true, const uint16_t *aux = nullptr)
+                   bool timing = true, const uint16_t *aux = nullptr, int64_t pitch = 0)
 {
     const bool tensor_scales = dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE;
     if (N % 8) return PT_ERR_UNSUPPORTED;              // outputs leave in 16-byte chunks
@@ -281,8 +281,11 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
     if (M > 0 && (!a_scale || !b_scale)) return PT_ERR_INVALID_ARG;
     if (!aligned4(a_scale) || !aligned4(b_scale)) return PT_ERR_MISALIGNED;
     const int64_t kb = dtype == PT_MXFP4_E2M1 ? K / 2 : K;      // code bytes per row
-    if (!fits31(M * kb) || !fits31(N * kb) || !fits31(G * N * (K / 32) + 4)) return PT_ERR_UNSUPPORTED;
+    if (pitch && (pitch < kb || pitch % 16)) return PT_ERR_INVALID_ARG;
+    const int64_t rb = pitch ? pitch : kb;                      // bytes between code rows
+    if (!fits31(M * rb) || !fits31(N * rb) || !fits31(G * N * (K / 32) + 4)) return PT_ERR_UNSUPPORTED;
     MxParams p = {};
+    p.pitch = pitch;
     p.swiglu_limit = swiglu_clamp(swiglu_limit);
     p.save = save;
     p.ldsave = (int)N;
@@ -320,10 +323,11 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
                                                  mx_swz_b_bytes(G, N, K, fmt));
     // the SwiGLU that keeps its input exists for the 256 x 256 kernel only,
     // which E2M1 with K % 256 != 0 reaches through the scale copies alone
-    const bool wide_only = ep == kEpiSwigluSave || ep == kEpiDSwiglu;
+    // (and so are code rows with their own pitch)
+    const bool wide_only = ep == kEpiSwigluSave || ep == kEpiDSwiglu || pitch != 0;
     if (wide_only && fmt == 1 && K % 256 && !swz) return PT_ERR_UNSUPPORTED;
     uint32_t *queues = p.sched;
-    const TuneKey key = tune_key(op, dtype, ep, 0, G, M, N, K);
+    const TuneKey key = tune_key(op, dtype, ep, pitch ? 2 : 0, G, M, N, K);
     return configured(key, cfg_mask(queues != nullptr, !tensor_scales && !wide_only), timing, s, [&](int cfg) {
         p.narrow = (cfg & kCfgNarrow) != 0;
         p.sched = (cfg & kCfgStatic) ? nullptr : queues;
@@ -347,8 +351,9 @@ static int mx_gemm(int op, const void *a, const uint8_t *a_scale, const void *b,
 static int grouped_fwd(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale, void *out,
                        uint8_t *out_scale, const int64_t *group_lens, const int64_t *group_offs, int64_t G, int64_t M,
                        int64_t N, int64_t K, int dtype, int trans_b, int epilogue, float swiglu_limit,
-                       void *workspace, size_t workspace_bytes, void *stream, bool timing)
+                       void *workspace, size_t workspace_bytes, void *stream, bool timing, int64_t pitch = 0)
 {
+    if (pitch < 0 || (pitch && dtype == PT_BF16)) return pitch < 0 ? PT_ERR_INVALID_ARG : PT_ERR_UNSUPPORTED;
     if (swiglu_limit != swiglu_limit) return PT_ERR_INVALID_ARG;   // NaN
     int st = check_groups(group_lens, G, M);
     if (st) return st;
@@ -404,7 +409,7 @@ static int grouped_fwd(const void *a, const uint8_t *a_scale, const void *b, con
     if (dtype == PT_MXFP8_E4M3 || dtype == PT_MXFP4_E2M1 || dtype == PT_FP8_E4M3 || dtype == PT_FP8_E4M3_ROWWISE) {
         if (!trans_b) return PT_ERR_UNSUPPORTED;           // K-contiguous codes
         return mx_gemm(PT_OP_FWD, a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype,
-                       ep, Nc, ldo, swiglu_limit, workspace, workspace_bytes, s, nullptr, timing);
+                       ep, Nc, ldo, swiglu_limit, workspace, workspace_bytes, s, nullptr, timing, nullptr, pitch);
     }
     return PT_ERR_UNSUPPORTED;
 }
@@ -451,6 +456,17 @@ int pt_grouped_gemm_fwd(const void *a, const uint8_t *a_scale, const void *b, co
 {
     return grouped_fwd(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype, trans_b,
                        epilogue, swiglu_limit, workspace, workspace_bytes, stream, true);
+}
+
+int pt_grouped_gemm_fwd_pitched(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale,
+                                void *out, uint8_t *out_scale, const int64_t *group_lens,
+                                const int64_t *group_offs, int64_t G, int64_t M, int64_t N, int64_t K, int dtype,
+                                int epilogue, float swiglu_limit, int64_t code_pitch, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    if (code_pitch <= 0) return PT_ERR_INVALID_ARG;
+    return grouped_fwd(a, a_scale, b, b_scale, out, out_scale, group_lens, group_offs, G, M, N, K, dtype, 1, epilogue,
+                       swiglu_limit, workspace, workspace_bytes, stream, true, code_pitch);
 }
 
 int pt_grouped_gemm_fwd_noalloc(const void *a, const uint8_t *a_scale, const void *b, const uint8_t *b_scale,
@@ -979,6 +995,22 @@ int pt_mx_quantize(const void *x, void *q, uint8_t *scales, int64_t rows, int64_
                                                (hipStream_t)stream));
     return hip_status(launch_quantize((const uint16_t *)x, (uint8_t *)q, scales, rows, cols, fmt,
                                       (hipStream_t)stream));
+}
+
+int pt_mx_quantize_pitched(const void *x, void *q, uint8_t *scales, int64_t rows, int64_t cols, int dtype,
+                           int64_t q_pitch, void *stream)
+{
+    if (rows < 0 || cols < 0) return PT_ERR_INVALID_ARG;
+    if (dtype != PT_MXFP8_E4M3 && dtype != PT_MXFP4_E2M1) return PT_ERR_UNSUPPORTED;
+    if (cols % 32) return PT_ERR_UNSUPPORTED;
+    const int fmt = dtype == PT_MXFP8_E4M3 ? 0 : 1;
+    if (q_pitch < (fmt == 0 ? cols : cols / 2) || q_pitch % 16) return PT_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return PT_OK;
+    if (!x || !q || !scales) return PT_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q)) return PT_ERR_MISALIGNED;
+    if (!device_is_gfx950()) return PT_ERR_UNSUPPORTED;
+    return hip_status(launch_quantize((const uint16_t *)x, (uint8_t *)q, scales, rows, cols, fmt,
+                                      (hipStream_t)stream, q_pitch));
 }
 
 int pt_fp8_quantize(const void *x, void *q, float *amax, float *dequant, int64_t batch, int64_t rows, int64_t cols,

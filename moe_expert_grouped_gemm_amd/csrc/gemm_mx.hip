@@ -754,12 +754,13 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
         WOps o;
         // row pitch of the operands: the reduction length, or the channel
         // rows' pitch of the weight gradient
-        const uint32_t ap = WG ? (uint32_t)p.pitch : (uint32_t)Kb;
+        // (the forward's codes may also come with a longer, line-aligned pitch)
+        const uint32_t ap = (WG || p.pitch) ? (uint32_t)p.pitch : (uint32_t)Kb;
         o.b_once = !WG && tm == 1;   // an expert within one row block: no other tile reads its weights
-        o.a = WG ? p.a + pb : p.a + (int64_t)row0 * Kb;
-        o.abytes = WG ? (uint32_t)rows * ap - pb : (uint32_t)rows * Kb;
-        o.b = WG ? p.b + pb : p.b + (int64_t)g * p.N * Kb;
-        o.bbytes = WG ? (uint32_t)p.wcols * ap - pb : (uint32_t)p.N * Kb;
+        o.a = WG ? p.a + pb : p.a + (int64_t)row0 * ap;
+        o.abytes = WG ? (uint32_t)rows * ap - pb : (uint32_t)rows * ap;
+        o.b = WG ? p.b + pb : p.b + (int64_t)g * p.N * ap;
+        o.bbytes = WG ? (uint32_t)p.wcols * ap - pb : (uint32_t)p.N * ap;
         o.chunk = (uint32_t)(((tid & 7) ^ ((tid >> 4) & 7)) * 16);
         o.avoff = (uint32_t)(m0 + (tid >> 3)) * ap + o.chunk;
 #pragma unroll
@@ -772,11 +773,11 @@ __global__ __launch_bounds__(WTHREADS, 1) void gg_mx_wide_kernel(MxParams p)
             // tile rows 0-63 / 64-127 / 128-191 / 192-255: gate j, up I + j,
             // gate j + 64, up I + j + 64, with j = nt * 128 + row % 64
             const int I = p.N >> 1;
-            o.bvoff = (uint32_t)(nt * (WBN / 2) + (tid >> 3)) * Kb + o.chunk;
+            o.bvoff = (uint32_t)(nt * (WBN / 2) + (tid >> 3)) * ap + o.chunk;
             o.bdelta[0] = 0u;
-            o.bdelta[1] = (uint32_t)I * Kb;
-            o.bdelta[2] = 64u * Kb;
-            o.bdelta[3] = (uint32_t)(I + 64) * Kb;
+            o.bdelta[1] = (uint32_t)I * ap;
+            o.bdelta[2] = 64u * ap;
+            o.bdelta[3] = (uint32_t)(I + 64) * ap;
         }
         ScRows sr;
         if constexpr (WSC == kWE4M3Swz || WSC == kWE2M1Swz) {

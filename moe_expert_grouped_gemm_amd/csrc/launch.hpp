@@ -88,7 +88,7 @@ struct MxParams {
     // stage starts; out is main_grad, fp32 [G][wrows][ldo] at o_gstride
     // elements
     const int *plan;
-    int64_t pitch;
+    int64_t pitch;           // also the forward's: code bytes between rows of A and of B, or 0 (packed)
     int wrows, wcols;
     int64_t o_gstride;
     int tilesM;
@@ -126,8 +126,9 @@ constexpr int kQueueWsBytes = kQueueWsOffset + kQueues * kQueueStride * 4;
 // a memset node would not be safe to capture in a graph).
 hipError_t launch_queue_reset(uint32_t *sched, hipStream_t s);
 
+// Blocks of 32 along the columns; code rows q_pitch bytes apart (0: packed).
 hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales,
-                           int64_t rows, int64_t cols, int fmt, hipStream_t s);
+                           int64_t rows, int64_t cols, int fmt, hipStream_t s, int64_t q_pitch = 0);
 // Blocks of 32 along the rows (axis 0): x [rows, cols] bf16 -> E4M3
 // [rows, cols] / E2M1 [rows/2, cols] codes (row pairs share a byte, even row
 // low) and [rows/32, cols] scales; rows % 32 == 0, cols % 4 == 0.

@@ -87,20 +87,24 @@ template <int FMT>
 __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const uint16_t *__restrict__ x,
                                                                uint8_t *__restrict__ q,
                                                                uint8_t *__restrict__ scales,
-                                                               int64_t nquads)
+                                                               int64_t nquads, int64_t gpr, int64_t extra)
 {
     // t indexes 8-value groups (a block is 4 consecutive t, in 4 consecutive
     // lanes); two groups per iteration, a whole grid apart, keep two loads
-    // in flight per lane
+    // in flight per lane.  Code rows `extra` bytes longer than the packed
+    // row (gpr groups per row) move group t's codes by `extra` per row before
+    // it.
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     for (; t + stride < nquads; t += 2 * stride) {
         const uintx4 v0 = __builtin_nontemporal_load((const uintx4 *)(x + t * 8));
         const uintx4 v1 = __builtin_nontemporal_load((const uintx4 *)(x + (t + stride) * 8));
-        quantise8<FMT>(v0, q, scales, t);
-        quantise8<FMT>(v1, q, scales, t + stride);
+        quantise8<FMT>(v0, extra ? q + (t / gpr) * extra : q, scales, t);
+        quantise8<FMT>(v1, extra ? q + ((t + stride) / gpr) * extra : q, scales, t + stride);
     }
-    if (t < nquads) quantise8<FMT>(__builtin_nontemporal_load((const uintx4 *)(x + t * 8)), q, scales, t);
+    if (t < nquads)
+        quantise8<FMT>(__builtin_nontemporal_load((const uintx4 *)(x + t * 8)), extra ? q + (t / gpr) * extra : q,
+                       scales, t);
 }
 
 // Quantisation along the columns (axis 0): blocks of 32 consecutive rows of
@@ -992,18 +996,21 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_experts_kernel(const voi
 }  // namespace
 
 hipError_t launch_quantize(const uint16_t *x, uint8_t *q, uint8_t *scales, int64_t rows, int64_t cols,
-                           int fmt, hipStream_t s)
+                           int fmt, hipStream_t s, int64_t q_pitch)
 {
     const int64_t nquads = rows * cols / 8;
+    const int64_t extra = q_pitch ? q_pitch - (fmt == 0 ? cols : cols / 2) : 0;
     if (nquads == 0) return hipSuccess;
     // whole blocks per workgroup (256 lanes = 64 blocks), a few waves per SIMD
     int64_t grid = (nquads + kThreads - 1) / kThreads;
     const int64_t cap = (int64_t)device_cus() * 16;
     if (grid > cap) grid = cap;
     if (fmt == 0)
-        hipLaunchKernelGGL(mx_quantize_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, scales, nquads);
+        hipLaunchKernelGGL(mx_quantize_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, scales, nquads,
+                           cols / 8, extra);
     else
-        hipLaunchKernelGGL(mx_quantize_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, scales, nquads);
+        hipLaunchKernelGGL(mx_quantize_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, x, q, scales, nquads,
+                           cols / 8, extra);
     return hipGetLastError();
 }
 
