@@ -207,6 +207,10 @@ def fc1_inputs(dev):
     return lens, G, M, K, N, a, b
 
 
+def up(x, m):
+    return (x + m - 1) // m * m
+
+
 def bytes_weights(lens, per_expert):
     return int((lens > 0).sum()) * per_expert
 
@@ -364,10 +368,26 @@ def bench_cfg3(dev, stream, iters):
     _, per = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
         aq, as_, bq, bs, out, None, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, 1, ptm.PT_EPI_NONE,
         workspace=WS[0], stream=stream), iters, 3, stream)
+    # the same codes with rows 2944 bytes apart (each row starting on a
+    # 128-byte line), as pt_mx_quantize_pitched writes them, through
+    # pt_grouped_gemm_fwd_pitched
+    P = up(K, 128)
+    ap = torch.empty((M, P), dtype=torch.uint8, device=dev)
+    bp = torch.empty((G * N, P), dtype=torch.uint8, device=dev)
+    ap[:, :K] = aq
+    bp[:, :K] = bq
+    _, per_p = time_launches(lambda: ptm.pt_grouped_gemm_fwd_pitched(
+        ap, as_, bp, bs, out, None, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, ptm.PT_EPI_NONE, P,
+        workspace=WS[0], stream=stream), iters, 3, stream)
+    _, per_qp = time_launches(lambda: ptm.pt_mx_quantize_pitched(x, ap, as_, M, K, ptm.PT_MXFP8_E4M3, P,
+                                                                 stream=stream), iters, 3, stream)
     flops = 2.0 * M * K * N
     nbytes = bytes_weights(lens, N * K + N * K // 32) + M * K + M * K // 32 + M * N * 2
     f = summary("MXFP8 fwd, 32 experts (Zipf 1.1), M=65536, K=2880, N=5760", "mxfp8", flops, nbytes, per,
-                {"group_lens_min_median_max": [int(lens.min()), int(np.median(lens)), int(lens.max())]})
+                {"group_lens_min_median_max": [int(lens.min()), int(np.median(lens)), int(lens.max())],
+                 "line_aligned_codes_pitch": P,
+                 "line_aligned_codes_ms_median": round(float(np.median(per_p)), 4),
+                 "line_aligned_quantise_A_ms_median": round(float(np.median(per_qp)), 4)})
     return f, q
 
 
