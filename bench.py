@@ -82,6 +82,7 @@ TRAFFIC_KEYS = {
     "cfg2_bf16_wgrad": ["cfg2_bf16_wgrad"],
     "cfg3_mxfp8_fwd": ["cfg3_mxfp8_fwd"],
     "cfg3_mxfp8_quantize_A": ["cfg3_mx_quantize_e4m3_A"],
+    "cfg3_mxfp8_fwd_line_aligned": ["cfg3_mxfp8_fwd_line_aligned"],
     # A and dY each quantised along tokens and transposed (per-launch means), then the weight gradient
     "cfg3_mxfp8_wgrad": ["cfg3_mx_tokens_quant", "cfg3_mx_tokens_quant", "cfg3_mx_wgrad_transpose",
                          "cfg3_mx_wgrad_transpose", "cfg3_mxfp8_wgrad"],
@@ -368,27 +369,42 @@ def bench_cfg3(dev, stream, iters):
     _, per = time_launches(lambda: ptm.pt_grouped_gemm_fwd(
         aq, as_, bq, bs, out, None, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, 1, ptm.PT_EPI_NONE,
         workspace=WS[0], stream=stream), iters, 3, stream)
-    # the same codes with rows 2944 bytes apart (each row starting on a
-    # 128-byte line), as pt_mx_quantize_pitched writes them, through
-    # pt_grouped_gemm_fwd_pitched
-    P = up(K, 128)
-    ap = torch.empty((M, P), dtype=torch.uint8, device=dev)
-    bp = torch.empty((G * N, P), dtype=torch.uint8, device=dev)
-    ap[:, :K] = aq
-    bp[:, :K] = bq
-    _, per_p = time_launches(lambda: ptm.pt_grouped_gemm_fwd_pitched(
-        ap, as_, bp, bs, out, None, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, ptm.PT_EPI_NONE, P,
-        workspace=WS[0], stream=stream), iters, 3, stream)
-    _, per_qp = time_launches(lambda: ptm.pt_mx_quantize_pitched(x, ap, as_, M, K, ptm.PT_MXFP8_E4M3, P,
-                                                                 stream=stream), iters, 3, stream)
     flops = 2.0 * M * K * N
     nbytes = bytes_weights(lens, N * K + N * K // 32) + M * K + M * K // 32 + M * N * 2
     f = summary("MXFP8 fwd, 32 experts (Zipf 1.1), M=65536, K=2880, N=5760", "mxfp8", flops, nbytes, per,
-                {"group_lens_min_median_max": [int(lens.min()), int(np.median(lens)), int(lens.max())],
-                 "line_aligned_codes_pitch": P,
-                 "line_aligned_codes_ms_median": round(float(np.median(per_p)), 4),
-                 "line_aligned_quantise_A_ms_median": round(float(np.median(per_qp)), 4)})
+                {"group_lens_min_median_max": [int(lens.min()), int(np.median(lens)), int(lens.max())]})
     return f, q
+
+
+def bench_cfg3_aligned(dev, stream, iters):
+    """The MXFP8 forward of the same workload on line-aligned codes: A and
+    the weights quantised by pt_mx_quantize_pitched with rows 2944 bytes
+    apart (each row starting on a 128-byte line), then
+    pt_grouped_gemm_fwd_pitched; timed as the packed line (GEMM with its
+    scale pre-pass), the pitched quantise of A beside it."""
+    lens = synth.lens_zipf_distinct(16384, 32, 4, 1.1, seed=3)
+    G, M, K, N = 32, int(lens.sum()), 2880, 5760
+    P = up(K, 128)
+    x = synth.randn_bf16((M, K), seed=104, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    w = synth.randn_bf16((G * N, K), seed=104 + 1000, device=dev, outlier_frac=0.01, outlier_mult=50.0)
+    ap = torch.empty((M, P), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    bp = torch.empty((G * N, P), dtype=torch.uint8, device=dev)
+    bs = torch.empty((G * N, K // 32), dtype=torch.uint8, device=dev)
+    ptm.pt_mx_quantize_pitched(w, bp, bs, G * N, K, ptm.PT_MXFP8_E4M3, P, stream=stream)
+    del w
+    _, per_q = time_launches(lambda: ptm.pt_mx_quantize_pitched(x, ap, as_, M, K, ptm.PT_MXFP8_E4M3, P,
+                                                                stream=stream), iters, 3, stream)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    lens_d = torch.as_tensor(lens, device=dev)
+    _, per = time_launches(lambda: ptm.pt_grouped_gemm_fwd_pitched(
+        ap, as_, bp, bs, out, None, lens_d, None, G, M, N, K, ptm.PT_MXFP8_E4M3, ptm.PT_EPI_NONE, P,
+        workspace=WS[0], stream=stream), iters, 3, stream)
+    flops = 2.0 * M * K * N
+    nbytes = bytes_weights(lens, N * K + N * K // 32) + M * K + M * K // 32 + M * N * 2
+    return summary(f"MXFP8 fwd on line-aligned codes (row pitch {P} bytes), 32 experts (Zipf 1.1), M=65536, "
+                   "K=2880, N=5760", "mxfp8", flops, nbytes, per,
+                   {"code_pitch": P, "quantise_A_pitched_ms_median": round(float(np.median(per_q)), 4)})
 
 
 def bench_cfg3_dgrad(dev, stream, iters):
@@ -865,6 +881,10 @@ def main():
         if want is None or "cfg3" in want:
             log("per_config: MXFP8")
             per["cfg3_mxfp8_fwd"], per["cfg3_mxfp8_quantize_A"] = bench_cfg3(dev, stream, iters)
+            torch.cuda.empty_cache()
+        if want is None or "cfg3la" in want:
+            log("per_config: MXFP8 on line-aligned codes")
+            per["cfg3_mxfp8_fwd_line_aligned"] = bench_cfg3_aligned(dev, stream, iters)
             torch.cuda.empty_cache()
         if want is None or "cfg3fp8" in want:
             log("per_config: FP8 with tensor scales")
